@@ -1,0 +1,209 @@
+/*
+ * tokengate.h -- C ABI of the TokenGate pruned-prefill hot path on AMD
+ * Instinct MI355X (gfx950).
+ *
+ * TokenGate prunes the prompt inside the model: the layers below a gate layer
+ * see every token; at the gate a small MLP scores every prunable (document)
+ * token; the best K document tokens plus every non-prunable token
+ * (instruction, question) form the kept set; the layers above the gate run on
+ * the kept rows only, with token-gated attention.  Sources, cited by page and
+ * section:
+ *   [reading] "TokenGate 与 T2Quant：LLM/DLM 推理效率双子星 精读"
+ *             (inkeast.github.io paper reading), sections 3.1 and 4.1;
+ *   [news]    news.farwalk.ai translation of the MarkTechPost article on
+ *             TokenGate, sections "TokenGate 的可学习 token 剪枝如何工作？",
+ *             "什么是 token 门控注意力？" and "如何部署 TokenGate？".
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * - Every function returns a tg_status (0 = TG_OK, negative = error); no
+ *   exception or abort crosses the ABI.  All arguments are validated before
+ *   any kernel is launched; on error nothing is launched.
+ * - Device pointers are plain HIP device addresses owned by the caller.  The
+ *   library never allocates or frees device memory and never synchronises
+ *   the stream: every launch is asynchronous on `stream` (a hipStream_t;
+ *   NULL = the legacy default stream).
+ * - Host pointers (marked "host") are read during the call only.
+ * - bf16 tensors are IEEE bfloat16 bit patterns (uint16), row-major,
+ *   token-major ([tokens, heads, head_dim]).  Scores and parameters are fp32.
+ * - A packed batch of prompts ("segments") is described by a segment table
+ *   built on the host with tg_plan_segments() and copied by the caller to the
+ *   device; the kernels read the device copy and trust it (build it only
+ *   with tg_plan_segments, which validates it).
+ * - Results are deterministic: the same inputs give bit-identical outputs
+ *   (fixed-order reductions, integer-only atomics).
+ */
+#ifndef TOKENGATE_H
+#define TOKENGATE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define TG_ABI_VERSION 1
+
+typedef enum tg_status {
+  TG_OK = 0,
+  TG_ERR_INVALID_ARG = -1, /* null pointer, negative size or budget, bad segment table */
+  TG_ERR_UNSUPPORTED = -2, /* shape the kernels do not implement (see each function) */
+  TG_ERR_WORKSPACE = -3,   /* workspace missing, misaligned or smaller than required */
+  TG_ERR_NO_DEVICE = -4,   /* no HIP device, or the current device is not gfx950 */
+  TG_ERR_HIP = -5          /* a HIP runtime call or kernel launch failed */
+} tg_status;
+
+/* Human-readable text of a status code (static storage). */
+const char* tg_status_string(int status);
+
+/* TG_ABI_VERSION of the library that was loaded. */
+int tg_abi_version(void);
+
+/* ------------------------------------------------------------------------ */
+/* Segment table                                                             */
+/* ------------------------------------------------------------------------ */
+
+/* One prompt of a packed batch.  The prompt is x = [x_R, x_D]: a request and
+ * a document that arrives with it ([reading] section 3.1); only the document
+ * span [doc_begin, doc_end) is prunable, every other token is always kept
+ * ([reading] section 4.1 component one; [news] "TokenGate 的可学习 token 剪枝如何
+ * 工作？": the question is never pruned).  32 bytes, 4-byte aligned. */
+typedef struct tg_segment {
+  int32_t seg_start;  /* first token of the prompt in the packed token arrays */
+  int32_t seg_len;    /* tokens in the prompt */
+  int32_t doc_begin;  /* document span, relative to seg_start, 0 <= b <= e <= seg_len */
+  int32_t doc_end;
+  int32_t k_eff;      /* kept documents = min(K, doc_end - doc_begin) */
+  int32_t kept_start; /* first row of this prompt in the compacted (kept) arrays */
+  int32_t kept_len;   /* k_eff + seg_len - (doc_end - doc_begin) */
+  int32_t reserved;   /* 0 */
+} tg_segment;
+
+/* Totals of a segment table, used on the host to size grids and buffers. */
+typedef struct tg_plan_info {
+  int64_t n_tokens;     /* sum of seg_len */
+  int64_t total_kept;   /* sum of kept_len (= rows of every compacted array) */
+  int32_t n_seg;
+  int32_t max_seg_len;
+  int32_t max_doc_len;
+  int32_t max_kept_len;
+} tg_plan_info;
+
+/* Builds the segment table of a packed batch (host only, no GPU needed).
+ *   seg_start [n_seg + 1] (host): prefix offsets, seg_start[0] = 0, non-decreasing.
+ *   doc_begin, doc_end [n_seg] (host): document span of each prompt, relative.
+ *   k_budget [n_seg] (host): document budget K ("max_kept_prefill_tokens",
+ *     [news] "如何部署 TokenGate？"); K > document length keeps the whole
+ *     document, K = 0 keeps only the non-document tokens, K < 0 is an error.
+ *   table [n_seg] (host, out), info (host, out).
+ * Errors: TG_ERR_INVALID_ARG for n_seg < 1, null pointers, a span outside its
+ * prompt, a negative budget, or more than 2^31 - 1 tokens. */
+int tg_plan_segments(int n_seg, const int32_t* seg_start, const int32_t* doc_begin, const int32_t* doc_end,
+                     const int32_t* k_budget, tg_segment* table, tg_plan_info* info);
+
+/* ------------------------------------------------------------------------ */
+/* (1) Gate score                                                            */
+/* ------------------------------------------------------------------------ */
+
+/* Device workspace (bytes) tg_gate_score needs for this plan (256-byte aligned). */
+size_t tg_gate_workspace_bytes(const tg_plan_info* info);
+
+/* Gate score of every token ([reading] section 4.1 component one): a small MLP
+ * reads the hidden row x_j of every prunable token and outputs one scalar,
+ *   r_j = w2 . GELU(W1 x_j + b1) + b2      (exact erf GELU),
+ * the scores are RMS-normalised along each prompt's document,
+ *   s_j = r_j / sqrt(mean_{j in doc} r_j^2 + rms_eps),
+ * and every non-document token gets s_j = 0 exactly.
+ *   x   bf16 [n_tokens, ld_x] (device): hidden rows; only the first d columns are read.
+ *   w1  bf16 [h, d] (device, row-major); b1 fp32 [h] (device) or NULL (= 0);
+ *   w2  fp32 [h] (device); b2 scalar.
+ *   segs (device) / info (host): tg_plan_segments output.
+ *   rms_eps: >= 0 normalises; < 0 skips the normalisation (s_j = r_j on the document).
+ *   scores fp32 [n_tokens] (device, out): every token of every prompt is written.
+ *   workspace (device, tg_gate_workspace_bytes, 256-byte aligned).
+ * The first layer runs on bf16 MFMA with fp32 accumulation; GELU, the h -> 1
+ * dot and the normalisation are fp32 (the sum of squares is accumulated in
+ * fp64, in a fixed order).
+ * Supported: d % 64 == 0, d <= 65536, h % 64 == 0, 64 <= h <= 256, ld_x >= d,
+ * x and w1 16-byte aligned, ld_x % 8 == 0; otherwise TG_ERR_UNSUPPORTED. */
+int tg_gate_score(const void* x, int64_t ld_x, int d, const void* w1, const float* b1, const float* w2, float b2,
+                  int h, const tg_segment* segs, const tg_plan_info* info, float rms_eps, float* scores,
+                  void* workspace, size_t workspace_bytes, void* stream);
+
+/* ------------------------------------------------------------------------ */
+/* (2) Top-K select                                                          */
+/* ------------------------------------------------------------------------ */
+
+/* Device workspace (bytes) tg_select_topk needs for this plan. */
+size_t tg_select_workspace_bytes(const tg_plan_info* info);
+
+/* Kept set of every prompt, S = top-K(s_j over the document) ∪ (every
+ * non-document token) ([reading] sections 3.1 and 4.1: |S ∩ P| = K).
+ * Order among documents: higher score first; equal scores (IEEE equality, so
+ * -0.0 == +0.0) go to the lower token index; NaN ranks below every number,
+ * NaNs among themselves by index; +-inf are ordinary values.
+ *   scores fp32 [n_tokens] (device).
+ *   kept_idx int32 [info->total_kept] (device, out): global token indices,
+ *     ascending; prompt i fills rows [kept_start, kept_start + kept_len).
+ *   workspace (device, tg_select_workspace_bytes, 256-byte aligned).
+ * Exact integer algorithm (radix select on order-preserving 32-bit keys,
+ * then an index-ordered scan): identical results on every run. */
+int tg_select_topk(const float* scores, const tg_segment* segs, const tg_plan_info* info, int32_t* kept_idx,
+                   void* workspace, size_t workspace_bytes, void* stream);
+
+/* ------------------------------------------------------------------------ */
+/* (3) Compaction                                                            */
+/* ------------------------------------------------------------------------ */
+
+#define TG_COMPACT_MAX_TENSORS 8
+
+/* Row gather of up to TG_COMPACT_MAX_TENSORS tensors in one launch:
+ *   dst_t[r] = src_t[kept_idx[r]] for r < n_kept, row_bytes[t] bytes, bit-exact.
+ * Pruned tokens never reach the layers above the gate, which create no KV
+ * entries for them ([reading] section 4.1; [news] "剪枝前向").
+ *   kept_idx int32 [n_kept] (device), each in [0, n_src_rows).  An index
+ *     outside that range is a caller error; its row is skipped (dst row left
+ *     as it was), never read out of bounds.
+ *   n_src_rows: rows of every src tensor.
+ *   src, dst [n_tensors] (host arrays of device pointers).
+ *   row_bytes, src_stride, dst_stride [n_tensors] (host): bytes per row copied
+ *     and the byte distance between rows; dst_stride >= row_bytes.
+ * Rows are moved 16 bytes at a time when every pointer, stride and row size
+ * of a tensor is a multiple of 16, else 4 bytes, else 1 byte.
+ * src and dst of a tensor must not overlap.
+ * Errors: TG_ERR_INVALID_ARG (null, negative sizes, dst_stride < row_bytes,
+ * n_tensors outside 1..TG_COMPACT_MAX_TENSORS, src == dst). */
+int tg_compact_kept(const int32_t* kept_idx, int64_t n_kept, int64_t n_src_rows, int n_tensors, const void* const* src,
+                    void* const* dst, const int64_t* row_bytes, const int64_t* src_stride,
+                    const int64_t* dst_stride, void* stream);
+
+/* ------------------------------------------------------------------------ */
+/* (4) Token-gated attention, prefill                                       */
+/* ------------------------------------------------------------------------ */
+
+/* Causal token-gated GQA attention over the kept rows of every prompt
+ * ([reading] section 4.1 component two: the kept token's score enters the
+ * attention logits as a bias, scaled by a per-(layer, head) gain, with a
+ * temperature on q.k; [news] "什么是 token 门控注意力？").  For query head h,
+ * key/value head c = h / (hq / hkv), kept rows r and t <= r of one prompt:
+ *   z_rt = tau_h * (q_r . k_t) / sqrt(head_dim) + gain_h * s_t
+ *   out[r, h] = sum_t softmax_t(z_r.) v_t
+ *   q   bf16 [total_kept, hq, head_dim] (device, contiguous)
+ *   k,v bf16 [total_kept, hkv, head_dim] (device, contiguous)
+ *   key_score fp32 [total_kept] (device) or NULL (no bias)
+ *   tau  fp32 [hq] (device) or NULL (= 1); gain fp32 [hq] (device) or NULL (no bias)
+ *   segs (device) / info (host): rows of prompt i are [kept_start, kept_start + kept_len).
+ *   out bf16 [total_kept, hq, head_dim] (device, out).
+ * bf16 MFMA for q.k and p.v, fp32 softmax and accumulation.
+ * Supported: head_dim in {64, 128}; hq % hkv == 0 with hq / hkv in {1, 2, 4};
+ * all pointers 16-byte aligned; otherwise TG_ERR_UNSUPPORTED / INVALID_ARG. */
+int tg_gated_attention_prefill(const void* q, const void* k, const void* v, const float* key_score,
+                               const float* tau, const float* gain, const tg_segment* segs,
+                               const tg_plan_info* info, int hq, int hkv, int head_dim, void* out, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* TOKENGATE_H */

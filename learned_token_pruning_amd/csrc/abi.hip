@@ -1,0 +1,196 @@
+// C ABI of libtokengate: argument validation, device checks and dispatch to
+// the kernel launchers.  Nothing here allocates device memory or synchronises.
+#include <atomic>
+#include <cstring>
+
+#include "common.h"
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::atomic<int> g_arch_state[kMaxDevices];  // 0 unknown, 1 gfx950, -1 other
+
+int check_device() {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) {
+    (void)hipGetLastError();
+    return TG_ERR_NO_DEVICE;
+  }
+  if (dev < kMaxDevices) {
+    const int s = g_arch_state[dev].load(std::memory_order_relaxed);
+    if (s == 1) return TG_OK;
+    if (s == -1) return TG_ERR_NO_DEVICE;
+  }
+  hipDeviceProp_t prop;
+  if (hipGetDeviceProperties(&prop, dev) != hipSuccess) {
+    (void)hipGetLastError();
+    return TG_ERR_NO_DEVICE;
+  }
+  const bool ok = std::strncmp(prop.gcnArchName, "gfx950", 6) == 0;
+  if (dev < kMaxDevices) g_arch_state[dev].store(ok ? 1 : -1, std::memory_order_relaxed);
+  return ok ? TG_OK : TG_ERR_NO_DEVICE;
+}
+
+inline bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+
+inline int hip_status(hipError_t e) { return e == hipSuccess ? TG_OK : TG_ERR_HIP; }
+
+int check_info(const tg_segment* segs, const tg_plan_info* info) {
+  if (segs == nullptr || info == nullptr) return TG_ERR_INVALID_ARG;
+  if (info->n_seg < 1 || info->n_tokens < 0 || info->total_kept < 0 || info->max_seg_len < 0 ||
+      info->max_doc_len < 0 || info->max_kept_len < 0)
+    return TG_ERR_INVALID_ARG;
+  if (info->max_doc_len > info->max_seg_len || info->max_kept_len > info->max_seg_len ||
+      info->n_tokens > 0x7fffffffLL || info->total_kept > info->n_tokens)
+    return TG_ERR_INVALID_ARG;
+  if (!aligned(segs, 4)) return TG_ERR_INVALID_ARG;
+  return TG_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* tg_status_string(int status) {
+  switch (status) {
+    case TG_OK: return "ok";
+    case TG_ERR_INVALID_ARG: return "invalid argument";
+    case TG_ERR_UNSUPPORTED: return "unsupported shape or layout";
+    case TG_ERR_WORKSPACE: return "workspace missing, misaligned or too small";
+    case TG_ERR_NO_DEVICE: return "no gfx950 HIP device";
+    case TG_ERR_HIP: return "HIP runtime or launch error";
+    default: return "unknown status";
+  }
+}
+
+int tg_abi_version(void) { return TG_ABI_VERSION; }
+
+int tg_plan_segments(int n_seg, const int32_t* seg_start, const int32_t* doc_begin, const int32_t* doc_end,
+                     const int32_t* k_budget, tg_segment* table, tg_plan_info* info) {
+  if (n_seg < 1 || !seg_start || !doc_begin || !doc_end || !k_budget || !table || !info) return TG_ERR_INVALID_ARG;
+  if (seg_start[0] != 0) return TG_ERR_INVALID_ARG;
+  int64_t kept = 0;
+  int32_t max_seg = 0, max_doc = 0, max_kept = 0;
+  for (int i = 0; i < n_seg; ++i) {
+    const int64_t a = seg_start[i], b = seg_start[i + 1];
+    if (b < a) return TG_ERR_INVALID_ARG;
+    const int64_t len = b - a;
+    const int64_t db = doc_begin[i], de = doc_end[i];
+    if (db < 0 || de < db || de > len) return TG_ERR_INVALID_ARG;
+    if (k_budget[i] < 0) return TG_ERR_INVALID_ARG;
+    const int64_t n_doc = de - db;
+    const int64_t keff = k_budget[i] < n_doc ? k_budget[i] : n_doc;
+    const int64_t klen = keff + (len - n_doc);
+    tg_segment s;
+    s.seg_start = (int32_t)a;
+    s.seg_len = (int32_t)len;
+    s.doc_begin = (int32_t)db;
+    s.doc_end = (int32_t)de;
+    s.k_eff = (int32_t)keff;
+    s.kept_start = (int32_t)kept;
+    s.kept_len = (int32_t)klen;
+    s.reserved = 0;
+    table[i] = s;
+    kept += klen;
+    if (len > max_seg) max_seg = (int32_t)len;
+    if (n_doc > max_doc) max_doc = (int32_t)n_doc;
+    if (klen > max_kept) max_kept = (int32_t)klen;
+  }
+  info->n_tokens = seg_start[n_seg];
+  info->total_kept = kept;
+  info->n_seg = n_seg;
+  info->max_seg_len = max_seg;
+  info->max_doc_len = max_doc;
+  info->max_kept_len = max_kept;
+  return TG_OK;
+}
+
+size_t tg_gate_workspace_bytes(const tg_plan_info* info) {
+  if (info == nullptr || info->n_seg < 1) return 0;
+  return tg::gate_workspace_bytes(*info);
+}
+
+int tg_gate_score(const void* x, int64_t ld_x, int d, const void* w1, const float* b1, const float* w2, float b2,
+                  int h, const tg_segment* segs, const tg_plan_info* info, float rms_eps, float* scores,
+                  void* workspace, size_t workspace_bytes, void* stream) {
+  int st = check_info(segs, info);
+  if (st != TG_OK) return st;
+  if (!x || !w1 || !w2 || !scores || d <= 0 || h <= 0 || ld_x < d) return TG_ERR_INVALID_ARG;
+  if (rms_eps != rms_eps) return TG_ERR_INVALID_ARG;  // NaN
+  if (d % 64 != 0 || d > 65536 || h % 64 != 0 || h > 256 || ld_x % 8 != 0) return TG_ERR_UNSUPPORTED;
+  if (!aligned(x, 16) || !aligned(w1, 16) || !aligned(w2, 16) || (b1 && !aligned(b1, 16)) || !aligned(scores, 4))
+    return TG_ERR_UNSUPPORTED;
+  if (!workspace || !aligned(workspace, 256) || workspace_bytes < tg::gate_workspace_bytes(*info))
+    return TG_ERR_WORKSPACE;
+  st = check_device();
+  if (st != TG_OK) return st;
+  return hip_status(tg::launch_gate_score(x, ld_x, d, w1, b1, w2, b2, h, segs, *info, rms_eps, scores, workspace,
+                                          reinterpret_cast<hipStream_t>(stream)));
+}
+
+size_t tg_select_workspace_bytes(const tg_plan_info* info) {
+  if (info == nullptr || info->n_seg < 1) return 0;
+  return tg::select_workspace_bytes(*info);
+}
+
+int tg_select_topk(const float* scores, const tg_segment* segs, const tg_plan_info* info, int32_t* kept_idx,
+                   void* workspace, size_t workspace_bytes, void* stream) {
+  int st = check_info(segs, info);
+  if (st != TG_OK) return st;
+  if (!scores || (!kept_idx && info->total_kept > 0)) return TG_ERR_INVALID_ARG;
+  if (!aligned(scores, 4) || (kept_idx && !aligned(kept_idx, 4))) return TG_ERR_INVALID_ARG;
+  if (!workspace || !aligned(workspace, 256) || workspace_bytes < tg::select_workspace_bytes(*info))
+    return TG_ERR_WORKSPACE;
+  st = check_device();
+  if (st != TG_OK) return st;
+  return hip_status(
+      tg::launch_select_topk(scores, segs, *info, kept_idx, workspace, reinterpret_cast<hipStream_t>(stream)));
+}
+
+int tg_compact_kept(const int32_t* kept_idx, int64_t n_kept, int64_t n_src_rows, int n_tensors, const void* const* src,
+                    void* const* dst, const int64_t* row_bytes, const int64_t* src_stride,
+                    const int64_t* dst_stride, void* stream) {
+  if (n_kept < 0 || n_src_rows < 0 || n_tensors < 1 || n_tensors > TG_COMPACT_MAX_TENSORS) return TG_ERR_INVALID_ARG;
+  if (!src || !dst || !row_bytes || !src_stride || !dst_stride) return TG_ERR_INVALID_ARG;
+  if (n_kept > 0 && (!kept_idx || !aligned(kept_idx, 4))) return TG_ERR_INVALID_ARG;
+  tg::CompactDesc desc{};
+  desc.n = n_tensors;
+  for (int t = 0; t < n_tensors; ++t) {
+    if (row_bytes[t] < 0 || src_stride[t] < 0 || dst_stride[t] < row_bytes[t]) return TG_ERR_INVALID_ARG;
+    if (row_bytes[t] > 0 && n_kept > 0) {
+      if (!src[t] || !dst[t]) return TG_ERR_INVALID_ARG;
+      if (src[t] == dst[t]) return TG_ERR_INVALID_ARG;  // an in-place gather would race
+    }
+    desc.src[t] = static_cast<const char*>(src[t]);
+    desc.dst[t] = static_cast<char*>(dst[t]);
+    desc.row_bytes[t] = row_bytes[t];
+    desc.src_stride[t] = src_stride[t];
+    desc.dst_stride[t] = dst_stride[t];
+  }
+  if (n_kept == 0) return TG_OK;
+  int st = check_device();
+  if (st != TG_OK) return st;
+  return hip_status(tg::launch_compact(kept_idx, n_kept, n_src_rows, desc, reinterpret_cast<hipStream_t>(stream)));
+}
+
+int tg_gated_attention_prefill(const void* q, const void* k, const void* v, const float* key_score,
+                               const float* tau, const float* gain, const tg_segment* segs,
+                               const tg_plan_info* info, int hq, int hkv, int head_dim, void* out, void* stream) {
+  int st = check_info(segs, info);
+  if (st != TG_OK) return st;
+  if (hq <= 0 || hkv <= 0 || head_dim <= 0) return TG_ERR_INVALID_ARG;
+  if (info->total_kept > 0 && (!q || !k || !v || !out)) return TG_ERR_INVALID_ARG;
+  if (hq % hkv != 0) return TG_ERR_UNSUPPORTED;
+  const int G = hq / hkv;
+  if (!(head_dim == 64 || head_dim == 128) || !(G == 1 || G == 2 || G == 4)) return TG_ERR_UNSUPPORTED;
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(out, 16)) return TG_ERR_INVALID_ARG;
+  if ((key_score && !aligned(key_score, 4)) || (tau && !aligned(tau, 4)) || (gain && !aligned(gain, 4)))
+    return TG_ERR_INVALID_ARG;
+  if (info->total_kept == 0) return TG_OK;
+  st = check_device();
+  if (st != TG_OK) return st;
+  return hip_status(tg::launch_gated_attention(q, k, v, key_score, tau, gain, segs, *info, hq, hkv, head_dim, out,
+                                               reinterpret_cast<hipStream_t>(stream)));
+}
+
+}  // extern "C"

@@ -1,0 +1,80 @@
+// Internal helpers shared by the gfx950 kernels of libtokengate (not part of the ABI).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "tokengate.h"
+
+namespace tg {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+constexpr int kWave = 64;
+
+// 32x32x16 bf16 MFMA, fp32 accumulate (CDNA4).  Operand layout, lane l, g = l / 32:
+//   A[m][k]: lane holds m = l % 32, k = 8 g .. 8 g + 7
+//   B[k][n]: lane holds n = l % 32, k = 8 g .. 8 g + 7
+//   C[m][n]: register i holds m = 8 (i / 4) + 4 g + (i % 4), n = l % 32
+__device__ __forceinline__ f32x16 mfma32(u32x4 a, u32x4 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b), c,
+                                                 0, 0, 0);
+}
+
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+// fp32 -> bf16, round to nearest even (inputs here are finite or inf; NaN kept quiet).
+__device__ __forceinline__ uint32_t f32_to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return (u >> 16) | 0x40u;
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return u >> 16;
+}
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  return f32_to_bf16(lo) | (f32_to_bf16(hi) << 16);
+}
+
+// Order-preserving key of an fp32 score: larger score -> larger key; -0.0 and
+// +0.0 share a key; NaN maps to 0, below every number (-inf -> 0x007fffff).
+__device__ __forceinline__ uint32_t score_key(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) == 0u) u = 0u;
+  if ((u & 0x7fffffffu) > 0x7f800000u) return 0u;
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+}  // namespace tg
+
+// Launchers (one per kernel family), defined in the kernel sources.  They
+// only launch; arguments are validated by the ABI layer.
+namespace tg {
+hipError_t launch_gate_score(const void* x, int64_t ld_x, int d, const void* w1, const float* b1, const float* w2,
+                             float b2, int h, const tg_segment* segs, const tg_plan_info& info, float rms_eps,
+                             float* scores, void* workspace, hipStream_t stream);
+size_t gate_workspace_bytes(const tg_plan_info& info);
+
+hipError_t launch_select_topk(const float* scores, const tg_segment* segs, const tg_plan_info& info,
+                              int32_t* kept_idx, void* workspace, hipStream_t stream);
+size_t select_workspace_bytes(const tg_plan_info& info);
+
+struct CompactDesc {
+  int n;
+  const char* src[TG_COMPACT_MAX_TENSORS];
+  char* dst[TG_COMPACT_MAX_TENSORS];
+  int64_t row_bytes[TG_COMPACT_MAX_TENSORS];
+  int64_t src_stride[TG_COMPACT_MAX_TENSORS];
+  int64_t dst_stride[TG_COMPACT_MAX_TENSORS];
+};
+hipError_t launch_compact(const int32_t* kept_idx, int64_t n_kept, int64_t n_src, const CompactDesc& desc,
+                          hipStream_t stream);
+
+hipError_t launch_gated_attention(const void* q, const void* k, const void* v, const float* key_score,
+                                  const float* tau, const float* gain, const tg_segment* segs,
+                                  const tg_plan_info& info, int hq, int hkv, int head_dim, void* out,
+                                  hipStream_t stream);
+}  // namespace tg

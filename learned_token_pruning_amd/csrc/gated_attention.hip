@@ -1,0 +1,309 @@
+// Token-gated causal GQA attention over the kept rows, prefill (gfx950).
+//
+// "TokenGate 与 T2Quant ... 精读", section 4.1, component two: the kept token's
+// gate score enters the attention logits as a bias, with a per-(layer, head)
+// gain and a temperature:
+//   z_rt = tau_h (q_r . k_t) / sqrt(D) + g_h s_t,   t <= r (kept rows, original order)
+//
+// Flash-style, one pass over the keys with an online softmax in the exp2
+// domain.  A workgroup (4 waves) owns one key/value head and a 128/G-row
+// query tile of all G query heads sharing it, so every K/V tile staged in LDS
+// serves G heads.  Each wave owns 32 query rows of one head.
+//
+// MFMA mapping (v_mfma_f32_32x32x16_bf16).  Scores are computed transposed,
+// S^T = K . Q^T, so a lane owns one query column (l % 32) and 16 key rows per
+// 32-key half: the softmax row max/sum is a register loop plus one swap with
+// the other half-wave.  The output is accumulated transposed too,
+// O^T += V^T . P^T, which lets P^T be fed from the score registers without
+// any data movement (the key order inside each 16-key MFMA step is permuted
+// identically on both operands) and keeps the per-query rescale lane-local.
+// V is therefore staged transposed in LDS; K row-major.  Both use padded rows
+// so that the 16- and 8-byte LDS reads are bank-conflict free.
+//
+// The gate bias g_h s_t is fused into the same FMA that applies the
+// temperature: x = S * (tau_h log2(e) / sqrt(D)) + (g_h log2(e)) s_t.
+// Tiles are launched longest-first (the last query tile of a prompt first).
+#include "common.h"
+
+namespace tg {
+namespace {
+
+constexpr int kBN = 64;  // keys per tile
+constexpr int kThreads = 256;
+constexpr float kLog2e = 1.4426950408889634f;
+
+template <int D>
+struct AttnSmem {
+  static constexpr int kLd = D + 8;        // K row stride (bf16)
+  static constexpr int vLd = kBN + 4;      // V^T row stride (bf16)
+  uint16_t k[2][kBN * kLd];
+  uint16_t vt[2][D * vLd];
+  float s[2][kBN];
+};
+
+template <int D>
+__device__ __forceinline__ void load_kv_tile(const uint16_t* __restrict__ kb, const uint16_t* __restrict__ vb,
+                                             const float* __restrict__ sb, int64_t kv_stride, int kv0, int n_keys,
+                                             int tid, u32x4 (&kr)[D / 32], u32x4 (&vr)[4], float& sr) {
+  // K: row tid / 4, D/4 columns starting at (tid % 4) * D / 4
+  {
+    const int r = tid >> 2;
+    const int c = (tid & 3) * (D / 4);
+    if (kv0 + r < n_keys) {
+      const u32x4* src = reinterpret_cast<const u32x4*>(kb + (int64_t)(kv0 + r) * kv_stride + c);
+#pragma unroll
+      for (int j = 0; j < D / 32; ++j) kr[j] = src[j];
+    } else {
+#pragma unroll
+      for (int j = 0; j < D / 32; ++j) kr[j] = u32x4{0u, 0u, 0u, 0u};
+    }
+  }
+  // V: 4 consecutive key rows x 8 dims; (dc, kq) chosen so the transposed LDS writes are conflict free
+  if (tid < 2 * D) {
+    const int dc = (tid & 1) + 2 * ((tid >> 4) % (D / 16));
+    const int kq = ((tid >> 1) & 7) + 8 * (tid / D);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int r = kv0 + 4 * kq + i;
+      if (r < n_keys)
+        vr[i] = *reinterpret_cast<const u32x4*>(vb + (int64_t)r * kv_stride + dc * 8);
+      else
+        vr[i] = u32x4{0u, 0u, 0u, 0u};
+    }
+  }
+  if (tid < kBN) sr = (sb != nullptr && kv0 + tid < n_keys) ? sb[kv0 + tid] : 0.0f;
+}
+
+template <int D>
+__device__ __forceinline__ void store_kv_tile(AttnSmem<D>& sm, int buf, int tid, const u32x4 (&kr)[D / 32],
+                                              const u32x4 (&vr)[4], float sr) {
+  {
+    const int r = tid >> 2;
+    const int c = (tid & 3) * (D / 4);
+    u32x4* dst = reinterpret_cast<u32x4*>(&sm.k[buf][r * AttnSmem<D>::kLd + c]);
+#pragma unroll
+    for (int j = 0; j < D / 32; ++j) dst[j] = kr[j];
+  }
+  if (tid < 2 * D) {
+    const int dc = (tid & 1) + 2 * ((tid >> 4) % (D / 16));
+    const int kq = ((tid >> 1) & 7) + 8 * (tid / D);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const int w = e >> 1;
+      const int sh = (e & 1) * 16;
+      const uint32_t a0 = (vr[0][w] >> sh) & 0xffffu, a1 = (vr[1][w] >> sh) & 0xffffu;
+      const uint32_t a2 = (vr[2][w] >> sh) & 0xffffu, a3 = (vr[3][w] >> sh) & 0xffffu;
+      u32x2 pk = u32x2{a0 | (a1 << 16), a2 | (a3 << 16)};
+      *reinterpret_cast<u32x2*>(&sm.vt[buf][(dc * 8 + e) * AttnSmem<D>::vLd + 4 * kq]) = pk;
+    }
+  }
+  if (tid < kBN) sm.s[buf][tid] = sr;
+}
+
+template <int D, int G>
+__global__ __launch_bounds__(kThreads, 2) void gated_attention_kernel(
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
+    const float* __restrict__ key_score, const float* __restrict__ tau, const float* __restrict__ gain,
+    const tg_segment* __restrict__ segs, int hq, int hkv, uint16_t* __restrict__ out) {
+  constexpr int kBM = 128 / G;              // query rows per workgroup
+  constexpr int kWavesPerHead = 4 / G;
+  __shared__ AttnSmem<D> sm;
+
+  const tg_segment seg = segs[blockIdx.z];
+  const int n = seg.kept_len;
+  const int q0 = (gridDim.y - 1 - blockIdx.y) * kBM;
+  if (q0 >= n) return;  // uniform
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int g = lane >> 5;
+  const int l32 = lane & 31;
+  const int c = blockIdx.x;
+  const int h = c * G + wave / kWavesPerHead;
+  const int qw0 = q0 + (wave % kWavesPerHead) * 32;  // first query row of this wave
+  const int qrow = qw0 + l32;                         // the query column this lane owns
+
+  const int64_t q_stride = (int64_t)hq * D;
+  const int64_t kv_stride = (int64_t)hkv * D;
+  const uint16_t* qb = q + (int64_t)seg.kept_start * q_stride + (int64_t)h * D;
+  const uint16_t* kb = k + (int64_t)seg.kept_start * kv_stride + (int64_t)c * D;
+  const uint16_t* vb = v + (int64_t)seg.kept_start * kv_stride + (int64_t)c * D;
+  const float* sb = key_score != nullptr ? key_score + seg.kept_start : nullptr;
+
+  const float th = tau != nullptr ? tau[h] : 1.0f;
+  const float qk_scale = th * kLog2e * (1.0f / __builtin_sqrtf((float)D));
+  const bool use_bias = key_score != nullptr && gain != nullptr;
+  const float bias_scale = use_bias ? gain[h] * kLog2e : 0.0f;
+
+  // Q^T operand: lane holds q[qrow][16 ks + 8 g .. + 7]
+  u32x4 qf[D / 16];
+  {
+    const int r = qrow < n ? qrow : n - 1;
+    const u32x4* src = reinterpret_cast<const u32x4*>(qb + (int64_t)r * q_stride + 8 * g);
+#pragma unroll
+    for (int ks = 0; ks < D / 16; ++ks) qf[ks] = src[2 * ks];
+  }
+
+  f32x16 o[D / 32];
+#pragma unroll
+  for (int dt = 0; dt < D / 32; ++dt) o[dt] = f32x16{};
+  float m_run = -__builtin_inff();
+  float l_run = 0.0f;
+
+  const int q_end = min(q0 + kBM, n);  // keys needed: t < q_end
+  const int ntiles = (q_end + kBN - 1) / kBN;
+
+  u32x4 kr[D / 32];
+  u32x4 vr[4];
+  float sr = 0.0f;
+  load_kv_tile<D>(kb, vb, sb, kv_stride, 0, n, tid, kr, vr, sr);
+  store_kv_tile<D>(sm, 0, tid, kr, vr, sr);
+  __syncthreads();
+
+  for (int jt = 0; jt < ntiles; ++jt) {
+    const int buf = jt & 1;
+    const int kv0 = jt * kBN;
+    const bool more = jt + 1 < ntiles;
+    if (more) load_kv_tile<D>(kb, vb, sb, kv_stride, kv0 + kBN, n, tid, kr, vr, sr);
+
+    if (kv0 <= qw0 + 31) {  // some key of this tile is visible to some row of this wave
+      // S^T = K . Q^T for the two 32-key halves
+      f32x16 st[2];
+#pragma unroll
+      for (int hf = 0; hf < 2; ++hf) {
+        st[hf] = f32x16{};
+        const uint16_t* krow = &sm.k[buf][(hf * 32 + l32) * AttnSmem<D>::kLd + 8 * g];
+#pragma unroll
+        for (int ks = 0; ks < D / 16; ++ks) {
+          const u32x4 a = *reinterpret_cast<const u32x4*>(krow + 16 * ks);
+          st[hf] = mfma32(a, qf[ks], st[hf]);
+        }
+      }
+      // logits in the exp2 domain, masking, tile max
+      const bool need_mask = (kv0 + kBN - 1 > qw0) || (kv0 + kBN > n);
+      float tmax = -__builtin_inff();
+#pragma unroll
+      for (int hf = 0; hf < 2; ++hf) {
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4) {
+          const int kl = hf * 32 + 8 * q4 + 4 * g;  // first of 4 consecutive keys (tile-local)
+          f32x4 bias = f32x4{0.f, 0.f, 0.f, 0.f};
+          if (use_bias) bias = *reinterpret_cast<const f32x4*>(&sm.s[buf][kl]);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            float xv = __builtin_fmaf(st[hf][4 * q4 + e], qk_scale, bias_scale * bias[e]);
+            if (need_mask) {
+              const int kvi = kv0 + kl + e;
+              if (kvi > qrow || kvi >= n) xv = -__builtin_inff();
+            }
+            st[hf][4 * q4 + e] = xv;
+            tmax = __builtin_fmaxf(tmax, xv);
+          }
+        }
+      }
+      tmax = __builtin_fmaxf(tmax, __shfl_xor(tmax, 32));
+      const float m_new = __builtin_fmaxf(m_run, tmax);
+      const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+      m_run = m_new;
+      float psum = 0.0f;
+      u32x4 pf[4];  // P^T operands of the 4 PV steps (16 keys each)
+#pragma unroll
+      for (int hf = 0; hf < 2; ++hf) {
+#pragma unroll
+        for (int sub = 0; sub < 2; ++sub) {
+          float p[8];
+#pragma unroll
+          for (int j = 0; j < 8; ++j) {
+            p[j] = __builtin_amdgcn_exp2f(st[hf][8 * sub + j] - m_new);
+            psum += p[j];
+          }
+          u32x4 w;
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+            typedef float f32x2 __attribute__((ext_vector_type(2)));
+            w[j] = __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2{p[2 * j], p[2 * j + 1]}), bf16x2));
+          }
+          pf[2 * hf + sub] = w;
+        }
+      }
+      l_run = l_run * alpha + psum;
+#pragma unroll
+      for (int dt = 0; dt < D / 32; ++dt) o[dt] *= alpha;
+      // O^T += V^T . P^T
+#pragma unroll
+      for (int s4 = 0; s4 < 4; ++s4) {
+#pragma unroll
+        for (int dt = 0; dt < D / 32; ++dt) {
+          const uint16_t* vrow = &sm.vt[buf][(dt * 32 + l32) * AttnSmem<D>::vLd + 16 * s4 + 4 * g];
+          const u32x2 lo = *reinterpret_cast<const u32x2*>(vrow);
+          const u32x2 hi = *reinterpret_cast<const u32x2*>(vrow + 8);
+          const u32x4 a = u32x4{lo[0], lo[1], hi[0], hi[1]};
+          o[dt] = mfma32(a, pf[s4], o[dt]);
+        }
+      }
+    }
+
+    if (more) store_kv_tile<D>(sm, buf ^ 1, tid, kr, vr, sr);
+    __syncthreads();
+  }
+
+  // normalise and store: lane holds O^T[d][qrow], d = 32 dt + 8 (i / 4) + 4 g + (i % 4)
+  const float l_tot = l_run + __shfl_xor(l_run, 32);
+  const float inv = 1.0f / l_tot;
+  if (qrow < n) {
+    uint16_t* orow = out + ((int64_t)seg.kept_start + qrow) * q_stride + (int64_t)h * D;
+#pragma unroll
+    for (int dt = 0; dt < D / 32; ++dt) {
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4) {
+        typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+        typedef float f32x2 __attribute__((ext_vector_type(2)));
+        const f32x16& a = o[dt];
+        const uint32_t w0 = __builtin_bit_cast(
+            uint32_t, __builtin_convertvector((f32x2{a[4 * q4] * inv, a[4 * q4 + 1] * inv}), bf16x2));
+        const uint32_t w1 = __builtin_bit_cast(
+            uint32_t, __builtin_convertvector((f32x2{a[4 * q4 + 2] * inv, a[4 * q4 + 3] * inv}), bf16x2));
+        *reinterpret_cast<u32x2*>(orow + 32 * dt + 8 * q4 + 4 * g) = u32x2{w0, w1};
+      }
+    }
+  }
+}
+
+template <int D, int G>
+hipError_t launch_dg(const void* q, const void* k, const void* v, const float* ks, const float* tau,
+                     const float* gain, const tg_segment* segs, const tg_plan_info& info, int hq, int hkv, void* out,
+                     hipStream_t stream) {
+  constexpr int kBM = 128 / G;
+  const int ntiles = (info.max_kept_len + kBM - 1) / kBM;
+  if (ntiles == 0) return hipSuccess;
+  dim3 grid(hkv, ntiles, info.n_seg);
+  hipLaunchKernelGGL((gated_attention_kernel<D, G>), grid, dim3(kThreads), 0, stream,
+                     reinterpret_cast<const uint16_t*>(q), reinterpret_cast<const uint16_t*>(k),
+                     reinterpret_cast<const uint16_t*>(v), ks, tau, gain, segs, hq, hkv,
+                     reinterpret_cast<uint16_t*>(out));
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_gated_attention(const void* q, const void* k, const void* v, const float* key_score,
+                                  const float* tau, const float* gain, const tg_segment* segs,
+                                  const tg_plan_info& info, int hq, int hkv, int head_dim, void* out,
+                                  hipStream_t stream) {
+  const int G = hq / hkv;
+#define TG_ATTN_CASE(DD, GG) \
+  if (head_dim == DD && G == GG) \
+    return launch_dg<DD, GG>(q, k, v, key_score, tau, gain, segs, info, hq, hkv, out, stream);
+  TG_ATTN_CASE(128, 1)
+  TG_ATTN_CASE(128, 2)
+  TG_ATTN_CASE(128, 4)
+  TG_ATTN_CASE(64, 1)
+  TG_ATTN_CASE(64, 2)
+  TG_ATTN_CASE(64, 4)
+#undef TG_ATTN_CASE
+  return hipErrorInvalidValue;
+}
+
+}  // namespace tg

@@ -1,0 +1,249 @@
+"""Python binding of libtokengate (ctypes).
+
+Argument marshalling only: every step of the path runs in the HIP kernels of
+``libtokengate.so``.  torch provides device memory and streams.  Importing
+this module loads the library and raises ImportError when it has not been
+built (``python -m learned_token_pruning_amd.build``); there is no other code
+path.
+
+The names mirror the C ABI in include/tokengate.h: plan_segments,
+gate_score, select_topk, compact_kept, gated_attention_prefill.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass
+from typing import List, Optional, Sequence, Tuple
+
+import numpy as np
+import torch  # loads the HIP runtime first, so the library binds to the same one
+
+_LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libtokengate.so")
+
+if not os.path.exists(_LIB_PATH):
+    raise ImportError(f"libtokengate.so is not built ({_LIB_PATH}); run `python -m learned_token_pruning_amd.build`")
+
+_lib = ctypes.CDLL(_LIB_PATH, mode=ctypes.RTLD_GLOBAL)
+
+TG_OK = 0
+STATUS_NAMES = {0: "TG_OK", -1: "TG_ERR_INVALID_ARG", -2: "TG_ERR_UNSUPPORTED", -3: "TG_ERR_WORKSPACE",
+                -4: "TG_ERR_NO_DEVICE", -5: "TG_ERR_HIP"}
+EXPORTS = ("tg_status_string", "tg_abi_version", "tg_plan_segments", "tg_gate_workspace_bytes", "tg_gate_score",
+           "tg_select_workspace_bytes", "tg_select_topk", "tg_compact_kept", "tg_gated_attention_prefill")
+COMPACT_MAX_TENSORS = 8
+
+
+class TokenGateError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: {STATUS_NAMES.get(status, status)} ({status_string(status)})")
+
+
+class Segment(ctypes.Structure):
+    _fields_ = [("seg_start", ctypes.c_int32), ("seg_len", ctypes.c_int32), ("doc_begin", ctypes.c_int32),
+                ("doc_end", ctypes.c_int32), ("k_eff", ctypes.c_int32), ("kept_start", ctypes.c_int32),
+                ("kept_len", ctypes.c_int32), ("reserved", ctypes.c_int32)]
+
+
+class PlanInfo(ctypes.Structure):
+    _fields_ = [("n_tokens", ctypes.c_int64), ("total_kept", ctypes.c_int64), ("n_seg", ctypes.c_int32),
+                ("max_seg_len", ctypes.c_int32), ("max_doc_len", ctypes.c_int32), ("max_kept_len", ctypes.c_int32)]
+
+
+_vp = ctypes.c_void_p
+_i64 = ctypes.c_int64
+_i32 = ctypes.c_int
+_f32 = ctypes.c_float
+_sz = ctypes.c_size_t
+
+_lib.tg_status_string.restype = ctypes.c_char_p
+_lib.tg_status_string.argtypes = [_i32]
+_lib.tg_abi_version.restype = _i32
+_lib.tg_plan_segments.restype = _i32
+_lib.tg_plan_segments.argtypes = [_i32, _vp, _vp, _vp, _vp, ctypes.POINTER(Segment), ctypes.POINTER(PlanInfo)]
+_lib.tg_gate_workspace_bytes.restype = _sz
+_lib.tg_gate_workspace_bytes.argtypes = [ctypes.POINTER(PlanInfo)]
+_lib.tg_gate_score.restype = _i32
+_lib.tg_gate_score.argtypes = [_vp, _i64, _i32, _vp, _vp, _vp, _f32, _i32, _vp, ctypes.POINTER(PlanInfo), _f32, _vp,
+                               _vp, _sz, _vp]
+_lib.tg_select_workspace_bytes.restype = _sz
+_lib.tg_select_workspace_bytes.argtypes = [ctypes.POINTER(PlanInfo)]
+_lib.tg_select_topk.restype = _i32
+_lib.tg_select_topk.argtypes = [_vp, _vp, ctypes.POINTER(PlanInfo), _vp, _vp, _sz, _vp]
+_lib.tg_compact_kept.restype = _i32
+_lib.tg_compact_kept.argtypes = [_vp, _i64, _i64, _i32, ctypes.POINTER(_vp), ctypes.POINTER(_vp), ctypes.POINTER(_i64),
+                                 ctypes.POINTER(_i64), ctypes.POINTER(_i64), _vp]
+_lib.tg_gated_attention_prefill.restype = _i32
+_lib.tg_gated_attention_prefill.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, ctypes.POINTER(PlanInfo), _i32, _i32,
+                                            _i32, _vp, _vp]
+
+
+def library_path() -> str:
+    return _LIB_PATH
+
+
+def status_string(status: int) -> str:
+    return _lib.tg_status_string(int(status)).decode()
+
+
+def abi_version() -> int:
+    return int(_lib.tg_abi_version())
+
+
+def _check(status: int, where: str) -> None:
+    if status != TG_OK:
+        raise TokenGateError(int(status), where)
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream) -> ctypes.c_void_p:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(int(stream.cuda_stream))
+
+
+def hip_runtimes_loaded() -> List[str]:
+    """Distinct libamdhip64 files mapped into this process (there must be one)."""
+    paths = set()
+    with open("/proc/self/maps") as f:
+        for ln in f:
+            parts = ln.split()
+            if len(parts) >= 6 and "libamdhip64" in parts[-1]:
+                paths.add(os.path.realpath(parts[-1]))
+    return sorted(paths)
+
+
+# ----------------------------------------------------------------------------
+# Segment plan
+# ----------------------------------------------------------------------------
+
+
+@dataclass
+class Plan:
+    info: PlanInfo
+    table: np.ndarray  # host copy, int32 [n_seg, 8]
+    table_dev: Optional[torch.Tensor]  # int32 [n_seg, 8] on the device
+
+    @property
+    def n_tokens(self) -> int:
+        return int(self.info.n_tokens)
+
+    @property
+    def total_kept(self) -> int:
+        return int(self.info.total_kept)
+
+    @property
+    def kept_offsets(self) -> np.ndarray:
+        return np.concatenate([self.table[:, 5], [self.total_kept]]).astype(np.int64)
+
+
+def plan_segments(seg_start: Sequence[int], doc_begin: Sequence[int], doc_end: Sequence[int],
+                  k_budget: Sequence[int], device: Optional[torch.device] = None) -> Plan:
+    """tg_plan_segments on host arrays; copies the table to ``device`` (None: host only)."""
+    n_seg = len(doc_begin)
+    ss = np.ascontiguousarray(seg_start, dtype=np.int32)
+    db = np.ascontiguousarray(doc_begin, dtype=np.int32)
+    de = np.ascontiguousarray(doc_end, dtype=np.int32)
+    kb = np.ascontiguousarray(k_budget, dtype=np.int32)
+    if ss.size != n_seg + 1 or de.size != n_seg or kb.size != n_seg:
+        raise TokenGateError(-1, "plan_segments: array lengths")
+    table = (Segment * max(n_seg, 1))()
+    info = PlanInfo()
+    st = _lib.tg_plan_segments(n_seg, ss.ctypes.data, db.ctypes.data, de.ctypes.data, kb.ctypes.data, table,
+                               ctypes.byref(info))
+    _check(st, "tg_plan_segments")
+    host = np.frombuffer(bytearray(table), dtype=np.int32).reshape(-1, 8)[:n_seg].copy()
+    dev = None
+    if device is not None:
+        dev = torch.from_numpy(host).to(device)
+    return Plan(info=info, table=host, table_dev=dev)
+
+
+def plan_from(segments, device=None) -> Plan:
+    """Plan of a workloads.Segments-like object (seg_start, doc_begin, doc_end, k_budget)."""
+    return plan_segments(segments.seg_start, segments.doc_begin, segments.doc_end, segments.k_budget, device)
+
+
+def _dev_table(plan: Plan) -> ctypes.c_void_p:
+    if plan.table_dev is None:
+        raise TokenGateError(-1, "plan has no device copy")
+    return ctypes.c_void_p(plan.table_dev.data_ptr())
+
+
+# ----------------------------------------------------------------------------
+# Entry points
+# ----------------------------------------------------------------------------
+
+
+def gate_workspace_bytes(plan: Plan) -> int:
+    return int(_lib.tg_gate_workspace_bytes(ctypes.byref(plan.info)))
+
+
+def select_workspace_bytes(plan: Plan) -> int:
+    return int(_lib.tg_select_workspace_bytes(ctypes.byref(plan.info)))
+
+
+def _workspace(nbytes: int, device) -> torch.Tensor:
+    return torch.empty(max(nbytes, 256), dtype=torch.uint8, device=device)
+
+
+def gate_score(x: torch.Tensor, w1: torch.Tensor, b1: Optional[torch.Tensor], w2: torch.Tensor, b2: float, plan: Plan,
+               rms_eps: float = 1e-6, scores: Optional[torch.Tensor] = None,
+               workspace: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """tg_gate_score.  x bf16 [n_tokens, >= d] (row stride = x.stride(0)), w1 bf16 [h, d]."""
+    h, d = w1.shape
+    if scores is None:
+        scores = torch.empty(plan.n_tokens, dtype=torch.float32, device=x.device)
+    if workspace is None:
+        workspace = _workspace(gate_workspace_bytes(plan), x.device)
+    st = _lib.tg_gate_score(_ptr(x), x.stride(0), d, _ptr(w1), _ptr(b1), _ptr(w2), float(b2), h, _dev_table(plan),
+                            ctypes.byref(plan.info), float(rms_eps), _ptr(scores), _ptr(workspace),
+                            workspace.numel() * workspace.element_size(), _stream(stream))
+    _check(st, "tg_gate_score")
+    return scores
+
+
+def select_topk(scores: torch.Tensor, plan: Plan, kept_idx: Optional[torch.Tensor] = None,
+                workspace: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """tg_select_topk -> int32 [total_kept] ascending global token indices."""
+    if kept_idx is None:
+        kept_idx = torch.empty(max(plan.total_kept, 1), dtype=torch.int32, device=scores.device)[:plan.total_kept]
+    if workspace is None:
+        workspace = _workspace(select_workspace_bytes(plan), scores.device)
+    st = _lib.tg_select_topk(_ptr(scores), _dev_table(plan), ctypes.byref(plan.info), _ptr(kept_idx),
+                             _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(stream))
+    _check(st, "tg_select_topk")
+    return kept_idx
+
+
+def compact_kept(kept_idx: torch.Tensor, pairs: Sequence[Tuple[torch.Tensor, torch.Tensor]], stream=None) -> None:
+    """tg_compact_kept: for every (src, dst), dst[r] = src[kept_idx[r]] (rows = dim 0)."""
+    n = len(pairs)
+    srcs = (_vp * n)(*[p[0].data_ptr() for p in pairs])
+    dsts = (_vp * n)(*[p[1].data_ptr() for p in pairs])
+    rb = (_i64 * n)(*[p[0][0].numel() * p[0].element_size() if p[0].dim() > 1 else p[0].element_size()
+                      for p in pairs])
+    ss = (_i64 * n)(*[p[0].stride(0) * p[0].element_size() for p in pairs])
+    ds = (_i64 * n)(*[p[1].stride(0) * p[1].element_size() for p in pairs])
+    n_src = min(p[0].shape[0] for p in pairs)
+    st = _lib.tg_compact_kept(_ptr(kept_idx), kept_idx.numel(), n_src, n, srcs, dsts, rb, ss, ds, _stream(stream))
+    _check(st, "tg_compact_kept")
+
+
+def gated_attention_prefill(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, key_score: Optional[torch.Tensor],
+                            tau: Optional[torch.Tensor], gain: Optional[torch.Tensor], plan: Plan,
+                            out: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """tg_gated_attention_prefill.  q [M, hq, D], k/v [M, hkv, D] bf16 contiguous."""
+    m, hq, dh = q.shape
+    hkv = k.shape[1]
+    if out is None:
+        out = torch.empty_like(q)
+    st = _lib.tg_gated_attention_prefill(_ptr(q), _ptr(k), _ptr(v), _ptr(key_score), _ptr(tau), _ptr(gain),
+                                         _dev_table(plan), ctypes.byref(plan.info), hq, hkv, dh, _ptr(out),
+                                         _stream(stream))
+    _check(st, "tg_gated_attention_prefill")
+    return out
