@@ -1,0 +1,265 @@
+"""Benchmark of the TokenGate pruned-prefill hot path on one MI355X.
+
+One step = gate score -> top-K select -> compaction of the kept rows (hidden,
+Q, K, V, scores) -> token-gated attention over the kept rows, on one batch of
+synthetic input already resident in HBM.  The headline workload is the
+16K-token gated layer (16320 document + 64 question tokens, d = 2048, gate
+MLP 2048 -> 256 -> 1, K = 2048, 16 query / 8 key-value heads, head_dim 128).
+The 128K-token layer at K = 2048 is measured too and reported beside it.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+
+Prints one JSON line.  Per-kernel times come from HIP events recorded on the
+stream the kernels run on, inside the timed region.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16
+HBM_PEAK_GBS = 8000.0  # MI355X HBM3E
+METRIC = "gated prefill tokens/s at N=16K/128K, K=2K; attention TFLOP/s as % of MFMA peak"
+
+
+def log(*a):
+    print("[bench]", *a, file=sys.stderr, flush=True)
+
+
+class Pipeline:
+    """Device-resident inputs, outputs and workspaces of one gated layer."""
+
+    def __init__(self, layer, k_budget, torch, tg):
+        self.torch, self.tg = torch, tg
+        dev = torch.device("cuda")
+        seg = layer.segments.with_budget(k_budget)
+        self.layer, self.seg = layer, seg
+
+        def bf(bits):
+            return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).to(dev)
+
+        def f32(a):
+            return torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).to(dev)
+
+        self.plan = tg.plan_from(seg, device=dev)
+        m = self.plan.total_kept
+        self.n, self.m = seg.n_tokens, m
+        self.x, self.w1, self.w2 = bf(layer.x), bf(layer.w1), f32(layer.w2)
+        self.q, self.k, self.v = bf(layer.q), bf(layer.k), bf(layer.v)
+        self.tau, self.gain = f32(layer.tau), f32(layer.gain)
+        self.scores = torch.empty(self.n, dtype=torch.float32, device=dev)
+        self.kept = torch.empty(m, dtype=torch.int32, device=dev)
+        self.gws = torch.empty(max(tg.gate_workspace_bytes(self.plan, layer.d, layer.h), 256), dtype=torch.uint8, device=dev)
+        self.sws = torch.empty(max(tg.select_workspace_bytes(self.plan), 256), dtype=torch.uint8, device=dev)
+        self.hc = torch.empty((m, layer.d), dtype=torch.bfloat16, device=dev)
+        self.qc = torch.empty((m, layer.hq, layer.head_dim), dtype=torch.bfloat16, device=dev)
+        self.kc = torch.empty((m, layer.hkv, layer.head_dim), dtype=torch.bfloat16, device=dev)
+        self.vc = torch.empty_like(self.kc)
+        self.sc = torch.empty(m, dtype=torch.float32, device=dev)
+        self.out = torch.empty_like(self.qc)
+        self.pairs = [(self.x, self.hc), (self.q, self.qc), (self.k, self.kc), (self.v, self.vc),
+                      (self.scores, self.sc)]
+
+    def stages(self):
+        tg = self.tg
+        return [
+            ("gate", lambda: tg.gate_score(self.x, self.w1, None, self.w2, 0.0, self.plan, scores=self.scores,
+                                           workspace=self.gws)),
+            ("select", lambda: tg.select_topk(self.scores, self.plan, kept_idx=self.kept, workspace=self.sws)),
+            ("compact", lambda: tg.compact_kept(self.kept, self.pairs)),
+            ("attention", lambda: tg.gated_attention_prefill(self.qc, self.kc, self.vc, self.sc, self.tau, self.gain,
+                                                             self.plan, out=self.out)),
+        ]
+
+    # algorithmic work (what the method must do), per launch
+    def gate_bytes(self):
+        L = self.layer
+        n_doc = self.seg.n_doc(0)
+        return 2 * n_doc * L.d + 2 * L.d * L.h + 4 * L.h + 4 * self.n
+
+    def gate_flops(self):
+        L = self.layer
+        n_doc = self.seg.n_doc(0)
+        return 2 * n_doc * L.d * L.h + 2 * n_doc * L.h
+
+    def select_compact_bytes(self):
+        L = self.layer
+        row = 2 * L.d + 2 * L.hq * L.head_dim + 2 * 2 * L.hkv * L.head_dim + 4
+        return 4 * self.seg.n_doc(0) + 4 * self.m + 4 * self.m + 2 * self.m * row
+
+    def compact_bytes(self):
+        L = self.layer
+        row = 2 * L.d + 2 * L.hq * L.head_dim + 2 * 2 * L.hkv * L.head_dim + 4
+        return 4 * self.m + 2 * self.m * row
+
+    def attention_flops(self):
+        L = self.layer
+        return 4 * L.hq * L.head_dim * self.m * (self.m + 1) // 2
+
+
+def time_pipeline(pipe, steps, warmup):
+    torch = pipe.torch
+    stages = pipe.stages()
+    stream = torch.cuda.current_stream()
+    for _ in range(warmup):
+        for _, f in stages:
+            f()
+    torch.cuda.synchronize()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(stages) + 1)] for _ in range(steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        ev[i][0].record(stream)
+        for j, (_, f) in enumerate(stages):
+            f()
+            ev[i][j + 1].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    per_stage = {name: float(np.mean([ev[i][j].elapsed_time(ev[i][j + 1]) for i in range(steps)])) * 1e3
+                 for j, (name, _) in enumerate(stages)}
+    gpu_step = float(np.mean([ev[i][0].elapsed_time(ev[i][-1]) for i in range(steps)])) * 1e3
+    return wall / steps * 1e6, gpu_step, per_stage
+
+
+def cpu_baseline(layer, k_budget, budget_s=12.0):
+    """The oracle (as it stands) on the same 16K workload, timed on the host cores."""
+    import oracle
+    from learned_token_pruning_amd import workloads as W
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
+    except Exception:  # pragma: no cover
+        threads = os.cpu_count() or 1
+    seg = layer.segments.with_budget(k_budget)
+    x, w1 = W.bf16_bits_to_f64(layer.x), W.bf16_bits_to_f64(layer.w1)
+    q, k, v = (W.bf16_bits_to_f64(a) for a in (layer.q, layer.k, layer.v))
+    reps, t_total = 0, 0.0
+    while reps < 3 and t_total < budget_s:
+        t0 = time.perf_counter()
+        s = oracle.gate_scores(x, w1, None, layer.w2.astype(np.float64), 0.0, seg.seg_start, seg.doc_begin,
+                               seg.doc_end)
+        idx, offs = oracle.kept_indices(s, seg.seg_start, seg.doc_begin, seg.doc_end, seg.k_budget)
+        hc, qc, kc, vc, sc = (oracle.compact_rows(a, idx) for a in (x, q, k, v, s))
+        oracle.gated_attention(qc, kc, vc, sc, layer.tau.astype(np.float64), layer.gain.astype(np.float64), offs)
+        t_total += time.perf_counter() - t0
+        reps += 1
+    t = t_total / reps
+    return {"value": seg.n_tokens / t, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"full 16K-token gated layer (gate over {seg.n_doc(0)} documents, select, compaction, "
+                      f"attention over {idx.size} kept rows), float64 NumPy, mean of {reps} run(s), "
+                      f"{t:.2f} s each"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-long", action="store_true", help="skip the 128K-token layer")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (the hot path is single-GPU here); got --gpus {args.gpus}",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    if not os.path.exists(os.path.join(ROOT, "learned_token_pruning_amd", "libtokengate.so")):
+        from learned_token_pruning_amd import build as _b
+        _b.build()
+    from learned_token_pruning_amd import tokengate as tg
+    from learned_token_pruning_amd import workloads as W
+
+    log("generating the 16K-token workload")
+    l16 = W.workload(2)
+    p16 = Pipeline(l16, 2048, torch, tg)
+    log("timing 16K", args.steps, "steps")
+    us_wall, us_gpu, st16 = time_pipeline(p16, args.steps, args.warmup)
+    log("16K: wall", f"{us_wall:.1f} us/step, events {us_gpu:.1f} us/step", st16)
+
+    attn_tflops = p16.attention_flops() / (st16["attention"] * 1e-6) / 1e12
+    gate_gbs = p16.gate_bytes() / (st16["gate"] * 1e-6) / 1e9
+    gate_tflops = p16.gate_flops() / (st16["gate"] * 1e-6) / 1e12
+    sc_gbs = p16.select_compact_bytes() / ((st16["select"] + st16["compact"]) * 1e-6) / 1e9
+    compact_gbs = p16.compact_bytes() / (st16["compact"] * 1e-6) / 1e9
+    dominant = max(st16, key=st16.get)
+    if dominant == "attention":
+        roof = {"kernel": "gated_attention_kernel<128,2>", "bound": "mfma", "achieved": attn_tflops,
+                "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": attn_tflops / MFMA_BF16_PEAK_TFLOPS,
+                "traffic": None}
+    elif dominant == "gate":
+        roof = {"kernel": "gate_mlp_kernel<2> + gate_normalize_kernel", "bound": "hbm", "achieved": gate_gbs,
+                "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": gate_gbs / HBM_PEAK_GBS, "traffic": None}
+    elif dominant == "compact":
+        roof = {"kernel": "compact_kernel", "bound": "hbm", "achieved": compact_gbs, "peak": HBM_PEAK_GBS,
+                "unit": "GB/s", "frac": compact_gbs / HBM_PEAK_GBS, "traffic": None}
+    else:
+        b = 4 * p16.seg.n_doc(0) + 4 * p16.m
+        gbs = b / (st16["select"] * 1e-6) / 1e9
+        roof = {"kernel": "select (6 launches)", "bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS,
+                "unit": "GB/s", "frac": gbs / HBM_PEAK_GBS, "traffic": None}
+
+    result = {
+        "metric": METRIC,
+        "value": p16.n / (us_wall * 1e-6),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": us_wall / 1e3,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "gated layer N=16384 (16320 doc + 64 question), d=2048, gate 2048-256-1, K=2048 "
+                               "(M=2112 kept), 16 Q / 8 KV heads, head_dim 128",
+                   "global_batch": 1, "seq_len": p16.n, "k_budget": 2048, "kept_rows": p16.m,
+                   "parallelism": "none", "launch": "eager, one stream"},
+        "roofline": roof,
+        "stages_us": {k: round(v, 2) for k, v in st16.items()},
+        "gpu_us_per_step_events": round(us_gpu, 2),
+        "attention": {"tflops": attn_tflops, "frac_mfma_peak": attn_tflops / MFMA_BF16_PEAK_TFLOPS},
+        "gate": {"gbs": gate_gbs, "frac_hbm_peak": gate_gbs / HBM_PEAK_GBS, "tflops": gate_tflops,
+                 "frac_mfma_peak": gate_tflops / MFMA_BF16_PEAK_TFLOPS},
+        "select_plus_compact": {"gbs": sc_gbs, "frac_hbm_peak": sc_gbs / HBM_PEAK_GBS},
+    }
+    del p16
+    torch.cuda.empty_cache()
+
+    if not args.no_long:
+        log("generating the 128K-token workload")
+        l128 = W.workload(4)
+        torch.cuda.reset_peak_memory_stats()
+        p128 = Pipeline(l128, 2048, torch, tg)
+        steps = max(10, args.steps // 4)
+        us_wall128, us_gpu128, st128 = time_pipeline(p128, steps, max(3, args.warmup // 4))
+        log("128K: wall", f"{us_wall128:.1f} us/step", st128)
+        result["n131072_k2048"] = {
+            "tokens_per_s": p128.n / (us_wall128 * 1e-6), "ms_per_step": us_wall128 / 1e3, "steps": steps,
+            "stages_us": {k: round(v, 2) for k, v in st128.items()},
+            "gate_gbs": p128.gate_bytes() / (st128["gate"] * 1e-6) / 1e9,
+            "peak_device_mem_gib": torch.cuda.max_memory_allocated() / 2 ** 30,
+        }
+        del p128, l128
+        torch.cuda.empty_cache()
+
+    if not args.no_cpu_baseline:
+        log("timing the CPU oracle on the 16K workload")
+        result["cpu_baseline"] = cpu_baseline(l16, 2048)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

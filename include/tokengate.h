@@ -106,8 +106,9 @@ int tg_plan_segments(int n_seg, const int32_t* seg_start, const int32_t* doc_beg
 /* (1) Gate score                                                            */
 /* ------------------------------------------------------------------------ */
 
-/* Device workspace (bytes) tg_gate_score needs for this plan (256-byte aligned). */
-size_t tg_gate_workspace_bytes(const tg_plan_info* info);
+/* Device workspace (bytes) tg_gate_score needs for this plan and MLP shape
+ * (per-tile sums of squares, and W1 re-ordered into MFMA fragment order). */
+size_t tg_gate_workspace_bytes(const tg_plan_info* info, int d, int h);
 
 /* Gate score of every token ([reading] section 4.1 component one): a small MLP
  * reads the hidden row x_j of every prunable token and outputs one scalar,
@@ -121,7 +122,7 @@ size_t tg_gate_workspace_bytes(const tg_plan_info* info);
  *   segs (device) / info (host): tg_plan_segments output.
  *   rms_eps: >= 0 normalises; < 0 skips the normalisation (s_j = r_j on the document).
  *   scores fp32 [n_tokens] (device, out): every token of every prompt is written.
- *   workspace (device, tg_gate_workspace_bytes, 256-byte aligned).
+ *   workspace (device, tg_gate_workspace_bytes(info, d, h), 256-byte aligned).
  * The first layer runs on bf16 MFMA with fp32 accumulation; GELU, the h -> 1
  * dot and the normalisation are fp32 (the sum of squares is accumulated in
  * fp64, in a fixed order).
@@ -135,7 +136,8 @@ int tg_gate_score(const void* x, int64_t ld_x, int d, const void* w1, const floa
 /* (2) Top-K select                                                          */
 /* ------------------------------------------------------------------------ */
 
-/* Device workspace (bytes) tg_select_topk needs for this plan. */
+/* Device workspace (bytes) tg_select_topk needs for this plan (currently 0:
+ * the selector keeps its state on chip; workspace may then be NULL). */
 size_t tg_select_workspace_bytes(const tg_plan_info* info);
 
 /* Kept set of every prompt, S = top-K(s_j over the document) ∪ (every
@@ -146,9 +148,11 @@ size_t tg_select_workspace_bytes(const tg_plan_info* info);
  *   scores fp32 [n_tokens] (device).
  *   kept_idx int32 [info->total_kept] (device, out): global token indices,
  *     ascending; prompt i fills rows [kept_start, kept_start + kept_len).
- *   workspace (device, tg_select_workspace_bytes, 256-byte aligned).
+ *   workspace (device, tg_select_workspace_bytes, 256-byte aligned; may be
+ *     NULL when that size is 0).
  * Exact integer algorithm (radix select on order-preserving 32-bit keys,
- * then an index-ordered scan): identical results on every run. */
+ * then an index-ordered scan): identical results on every run.  One launch,
+ * one workgroup per prompt. */
 int tg_select_topk(const float* scores, const tg_segment* segs, const tg_plan_info* info, int32_t* kept_idx,
                    void* workspace, size_t workspace_bytes, void* stream);
 

@@ -105,9 +105,9 @@ int tg_plan_segments(int n_seg, const int32_t* seg_start, const int32_t* doc_beg
   return TG_OK;
 }
 
-size_t tg_gate_workspace_bytes(const tg_plan_info* info) {
-  if (info == nullptr || info->n_seg < 1) return 0;
-  return tg::gate_workspace_bytes(*info);
+size_t tg_gate_workspace_bytes(const tg_plan_info* info, int d, int h) {
+  if (info == nullptr || info->n_seg < 1 || d <= 0 || h <= 0) return 0;
+  return tg::gate_workspace_bytes(*info, d, h);
 }
 
 int tg_gate_score(const void* x, int64_t ld_x, int d, const void* w1, const float* b1, const float* w2, float b2,
@@ -120,7 +120,7 @@ int tg_gate_score(const void* x, int64_t ld_x, int d, const void* w1, const floa
   if (d % 64 != 0 || d > 65536 || h % 64 != 0 || h > 256 || ld_x % 8 != 0) return TG_ERR_UNSUPPORTED;
   if (!aligned(x, 16) || !aligned(w1, 16) || !aligned(w2, 16) || (b1 && !aligned(b1, 16)) || !aligned(scores, 4))
     return TG_ERR_UNSUPPORTED;
-  if (!workspace || !aligned(workspace, 256) || workspace_bytes < tg::gate_workspace_bytes(*info))
+  if (!workspace || !aligned(workspace, 256) || workspace_bytes < tg::gate_workspace_bytes(*info, d, h))
     return TG_ERR_WORKSPACE;
   st = check_device();
   if (st != TG_OK) return st;
@@ -139,8 +139,8 @@ int tg_select_topk(const float* scores, const tg_segment* segs, const tg_plan_in
   if (st != TG_OK) return st;
   if (!scores || (!kept_idx && info->total_kept > 0)) return TG_ERR_INVALID_ARG;
   if (!aligned(scores, 4) || (kept_idx && !aligned(kept_idx, 4))) return TG_ERR_INVALID_ARG;
-  if (!workspace || !aligned(workspace, 256) || workspace_bytes < tg::select_workspace_bytes(*info))
-    return TG_ERR_WORKSPACE;
+  const size_t ws_need = tg::select_workspace_bytes(*info);
+  if (ws_need > 0 && (!workspace || !aligned(workspace, 256) || workspace_bytes < ws_need)) return TG_ERR_WORKSPACE;
   st = check_device();
   if (st != TG_OK) return st;
   return hip_status(

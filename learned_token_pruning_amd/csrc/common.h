@@ -56,7 +56,7 @@ namespace tg {
 hipError_t launch_gate_score(const void* x, int64_t ld_x, int d, const void* w1, const float* b1, const float* w2,
                              float b2, int h, const tg_segment* segs, const tg_plan_info& info, float rms_eps,
                              float* scores, void* workspace, hipStream_t stream);
-size_t gate_workspace_bytes(const tg_plan_info& info);
+size_t gate_workspace_bytes(const tg_plan_info& info, int d, int h);
 
 hipError_t launch_select_topk(const float* scores, const tg_segment* segs, const tg_plan_info& info,
                               int32_t* kept_idx, void* workspace, hipStream_t stream);

@@ -29,33 +29,34 @@ namespace tg {
 namespace {
 
 constexpr int kBN = 64;  // keys per tile
-constexpr int kThreads = 256;
+constexpr int kThreads = 512;  // two groups of 4 waves
 constexpr float kLog2e = 1.4426950408889634f;
 
 template <int D>
 struct AttnSmem {
   static constexpr int kLd = D + 8;        // K row stride (bf16)
   static constexpr int vLd = kBN + 4;      // V^T row stride (bf16)
-  uint16_t k[2][kBN * kLd];
-  uint16_t vt[2][D * vLd];
-  float s[2][kBN];
+  uint16_t k[1][kBN * kLd];
+  uint16_t vt[1][D * vLd];
+  float s[4][kBN];  // gate bias of every key, pre-multiplied by g_h log2(e), one row per query head of the group
 };
 
 template <int D>
 __device__ __forceinline__ void load_kv_tile(const uint16_t* __restrict__ kb, const uint16_t* __restrict__ vb,
                                              const float* __restrict__ sb, int64_t kv_stride, int kv0, int n_keys,
                                              int tid, u32x4 (&kr)[D / 32], u32x4 (&vr)[4], float& sr) {
-  // K: row tid / 4, D/4 columns starting at (tid % 4) * D / 4
+  // K: D/8 threads per row, 16 bytes each, so every load instruction reads whole rows
   {
-    const int r = tid >> 2;
-    const int c = (tid & 3) * (D / 4);
-    if (kv0 + r < n_keys) {
-      const u32x4* src = reinterpret_cast<const u32x4*>(kb + (int64_t)(kv0 + r) * kv_stride + c);
+    constexpr int kTpr = D / 8;            // threads per row
+    constexpr int kRpi = 256 / kTpr;       // rows per load instruction
+    const int c = (tid % kTpr) * 8;
 #pragma unroll
-      for (int j = 0; j < D / 32; ++j) kr[j] = src[j];
-    } else {
-#pragma unroll
-      for (int j = 0; j < D / 32; ++j) kr[j] = u32x4{0u, 0u, 0u, 0u};
+    for (int j = 0; j < D / 32; ++j) {
+      const int r = tid / kTpr + kRpi * j;
+      if (kv0 + r < n_keys)
+        kr[j] = *reinterpret_cast<const u32x4*>(kb + (int64_t)(kv0 + r) * kv_stride + c);
+      else
+        kr[j] = u32x4{0u, 0u, 0u, 0u};
     }
   }
   // V: 4 consecutive key rows x 8 dims; (dc, kq) chosen so the transposed LDS writes are conflict free
@@ -74,15 +75,16 @@ __device__ __forceinline__ void load_kv_tile(const uint16_t* __restrict__ kb, co
   if (tid < kBN) sr = (sb != nullptr && kv0 + tid < n_keys) ? sb[kv0 + tid] : 0.0f;
 }
 
-template <int D>
+template <int D, int G>
 __device__ __forceinline__ void store_kv_tile(AttnSmem<D>& sm, int buf, int tid, const u32x4 (&kr)[D / 32],
-                                              const u32x4 (&vr)[4], float sr) {
+                                              const u32x4 (&vr)[4], float sr, const float (&bscale)[G]) {
   {
-    const int r = tid >> 2;
-    const int c = (tid & 3) * (D / 4);
-    u32x4* dst = reinterpret_cast<u32x4*>(&sm.k[buf][r * AttnSmem<D>::kLd + c]);
+    constexpr int kTpr = D / 8;
+    constexpr int kRpi = 256 / kTpr;
+    const int c = (tid % kTpr) * 8;
 #pragma unroll
-    for (int j = 0; j < D / 32; ++j) dst[j] = kr[j];
+    for (int j = 0; j < D / 32; ++j)
+      *reinterpret_cast<u32x4*>(&sm.k[buf][(tid / kTpr + kRpi * j) * AttnSmem<D>::kLd + c]) = kr[j];
   }
   if (tid < 2 * D) {
     const int dc = (tid & 1) + 2 * ((tid >> 4) % (D / 16));
@@ -97,17 +99,102 @@ __device__ __forceinline__ void store_kv_tile(AttnSmem<D>& sm, int buf, int tid,
       *reinterpret_cast<u32x2*>(&sm.vt[buf][(dc * 8 + e) * AttnSmem<D>::vLd + 4 * kq]) = pk;
     }
   }
-  if (tid < kBN) sm.s[buf][tid] = sr;
+  if (tid < kBN) {
+#pragma unroll
+    for (int hh = 0; hh < G; ++hh) sm.s[hh][tid] = bscale[hh] * sr;
+  }
+}
+
+// One key tile for one wave: S^T = K . Q^T, masked exp2-domain online softmax
+// with the gate bias, O^T += V^T . P^T.  `lim` (MASK only): the lane's last
+// visible key, tile-local (keys after it are causally masked or past the end).
+template <int D, bool MASK>
+__device__ __forceinline__ void attend_tile(const AttnSmem<D>& s_, int hl, const u32x4 (&qf)[D / 16],
+                                            f32x16 (&o)[D / 32], float& m_run, float& l_run, float qk_scale, int lim,
+                                            int g, int l32) {
+  // S^T for the two 32-key halves; the two accumulation chains are interleaved
+  f32x16 st[2] = {f32x16{}, f32x16{}};
+  const uint16_t* krow0 = &s_.k[0][l32 * AttnSmem<D>::kLd + 8 * g];
+  const uint16_t* krow1 = krow0 + 32 * AttnSmem<D>::kLd;
+#pragma unroll
+  for (int ks = 0; ks < D / 16; ++ks) {
+    const u32x4 a0 = *reinterpret_cast<const u32x4*>(krow0 + 16 * ks);
+    const u32x4 a1 = *reinterpret_cast<const u32x4*>(krow1 + 16 * ks);
+    st[0] = mfma32(a0, qf[ks], st[0]);
+    st[1] = mfma32(a1, qf[ks], st[1]);
+  }
+  // logits in the exp2 domain, tile max
+  float tmax = -__builtin_inff();
+#pragma unroll
+  for (int hf = 0; hf < 2; ++hf) {
+#pragma unroll
+    for (int q4 = 0; q4 < 4; ++q4) {
+      const int kl = hf * 32 + 8 * q4 + 4 * g;  // first of 4 consecutive keys (tile-local)
+      const f32x4 sv = *reinterpret_cast<const f32x4*>(&s_.s[hl][kl]);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        float xv = __builtin_fmaf(st[hf][4 * q4 + e], qk_scale, sv[e]);
+        if (MASK && kl + e > lim) xv = -__builtin_inff();
+        st[hf][4 * q4 + e] = xv;
+        tmax = __builtin_fmaxf(tmax, xv);
+      }
+    }
+  }
+  tmax = __builtin_fmaxf(tmax, __shfl_xor(tmax, 32));
+  // Lazy rescale: the reference point m_run only moves when some row's max
+  // exceeds it by more than 2^8 (or on the first visible tile); softmax does
+  // not depend on the reference point, and exp2(x - m_run) <= 2^8 stays well
+  // inside fp32 and bf16 range.
+  if (__ballot(tmax > m_run + 8.0f) != 0) {
+    const float m_new = __builtin_fmaxf(m_run, tmax);
+    const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+    l_run *= alpha;
+#pragma unroll
+    for (int dt = 0; dt < D / 32; ++dt) o[dt] *= alpha;
+    m_run = m_new;
+  }
+  float psum = 0.0f;
+  u32x4 pf[4];  // P^T operands of the 4 PV steps (16 keys each)
+#pragma unroll
+  for (int hf = 0; hf < 2; ++hf) {
+#pragma unroll
+    for (int sub = 0; sub < 2; ++sub) {
+      u32x4 w;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+        typedef float f32x2 __attribute__((ext_vector_type(2)));
+        const float p0 = __builtin_amdgcn_exp2f(st[hf][8 * sub + 2 * j] - m_run);
+        const float p1 = __builtin_amdgcn_exp2f(st[hf][8 * sub + 2 * j + 1] - m_run);
+        psum += p0 + p1;
+        w[j] = __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2{p0, p1}), bf16x2));
+      }
+      pf[2 * hf + sub] = w;
+    }
+  }
+  l_run += psum;
+  // O^T += V^T . P^T
+#pragma unroll
+  for (int s4 = 0; s4 < 4; ++s4) {
+#pragma unroll
+    for (int dt = 0; dt < D / 32; ++dt) {
+      const uint16_t* vrow = &s_.vt[0][(dt * 32 + l32) * AttnSmem<D>::vLd + 16 * s4 + 4 * g];
+      const u32x2 lo = *reinterpret_cast<const u32x2*>(vrow);
+      const u32x2 hi = *reinterpret_cast<const u32x2*>(vrow + 8);
+      o[dt] = mfma32(u32x4{lo[0], lo[1], hi[0], hi[1]}, pf[s4], o[dt]);
+    }
+  }
 }
 
 template <int D, int G>
-__global__ __launch_bounds__(kThreads, 2) void gated_attention_kernel(
+__global__ __launch_bounds__(kThreads) void gated_attention_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
     const float* __restrict__ key_score, const float* __restrict__ tau, const float* __restrict__ gain,
     const tg_segment* __restrict__ segs, int hq, int hkv, uint16_t* __restrict__ out) {
-  constexpr int kBM = 128 / G;              // query rows per workgroup
+  constexpr int kBM = 128 / G;  // query rows per workgroup
   constexpr int kWavesPerHead = 4 / G;
-  __shared__ AttnSmem<D> sm;
+  // smem[stage][group]: the two wave groups work on alternate key tiles
+  __shared__ AttnSmem<D> sm[2][2];
 
   const tg_segment seg = segs[blockIdx.z];
   const int n = seg.kept_len;
@@ -115,8 +202,10 @@ __global__ __launch_bounds__(kThreads, 2) void gated_attention_kernel(
   if (q0 >= n) return;  // uniform
 
   const int tid = threadIdx.x;
+  const int grp = tid >> 8;      // 0: even key tiles, 1: odd key tiles
+  const int gtid = tid & 255;    // thread index inside the group
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = gtid >> 6;    // wave inside the group
   const int g = lane >> 5;
   const int l32 = lane & 31;
   const int c = blockIdx.x;
@@ -129,12 +218,15 @@ __global__ __launch_bounds__(kThreads, 2) void gated_attention_kernel(
   const uint16_t* qb = q + (int64_t)seg.kept_start * q_stride + (int64_t)h * D;
   const uint16_t* kb = k + (int64_t)seg.kept_start * kv_stride + (int64_t)c * D;
   const uint16_t* vb = v + (int64_t)seg.kept_start * kv_stride + (int64_t)c * D;
-  const float* sb = key_score != nullptr ? key_score + seg.kept_start : nullptr;
+  const bool use_bias = key_score != nullptr && gain != nullptr;
+  const float* sb = use_bias ? key_score + seg.kept_start : nullptr;  // no bias: the LDS score tile holds zeros
 
   const float th = tau != nullptr ? tau[h] : 1.0f;
   const float qk_scale = th * kLog2e * (1.0f / __builtin_sqrtf((float)D));
-  const bool use_bias = key_score != nullptr && gain != nullptr;
-  const float bias_scale = use_bias ? gain[h] * kLog2e : 0.0f;
+  float bscale[G];  // g_h log2(e) of every query head of the group (0 without a bias)
+#pragma unroll
+  for (int hh = 0; hh < G; ++hh) bscale[hh] = use_bias ? gain[c * G + hh] * kLog2e : 0.0f;
+  const int hl = wave / kWavesPerHead;  // this wave's head inside the group
 
   // Q^T operand: lane holds q[qrow][16 ks + 8 g .. + 7]
   u32x4 qf[D / 16];
@@ -143,6 +235,8 @@ __global__ __launch_bounds__(kThreads, 2) void gated_attention_kernel(
     const u32x4* src = reinterpret_cast<const u32x4*>(qb + (int64_t)r * q_stride + 8 * g);
 #pragma unroll
     for (int ks = 0; ks < D / 16; ++ks) qf[ks] = src[2 * ks];
+#pragma unroll
+    for (int ks = 0; ks < D / 16; ++ks) asm volatile("" : "+v"(qf[ks]));  // keep Q resident, never re-read
   }
 
   f32x16 o[D / 32];
@@ -153,119 +247,78 @@ __global__ __launch_bounds__(kThreads, 2) void gated_attention_kernel(
 
   const int q_end = min(q0 + kBM, n);  // keys needed: t < q_end
   const int ntiles = (q_end + kBN - 1) / kBN;
+  const int npairs = (ntiles + 1) / 2;
 
   u32x4 kr[D / 32];
   u32x4 vr[4];
   float sr = 0.0f;
-  load_kv_tile<D>(kb, vb, sb, kv_stride, 0, n, tid, kr, vr, sr);
-  store_kv_tile<D>(sm, 0, tid, kr, vr, sr);
+  // pair 0: group 0 stages tile 0, group 1 tile 1 (if any)
+  if (grp < ntiles) {
+    load_kv_tile<D>(kb, vb, sb, kv_stride, grp * kBN, n, gtid, kr, vr, sr);
+    store_kv_tile<D, G>(sm[0][grp], 0, gtid, kr, vr, sr, bscale);
+  }
   __syncthreads();
 
-  for (int jt = 0; jt < ntiles; ++jt) {
-    const int buf = jt & 1;
+  for (int ip = 0; ip < npairs; ++ip) {
+    const int buf = ip & 1;
+    const int jt = 2 * ip + grp;  // this group's key tile
     const int kv0 = jt * kBN;
-    const bool more = jt + 1 < ntiles;
-    if (more) load_kv_tile<D>(kb, vb, sb, kv_stride, kv0 + kBN, n, tid, kr, vr, sr);
+    const int jn = jt + 2;        // this group's next key tile
+    const bool more = jn < ntiles;
+    if (more) load_kv_tile<D>(kb, vb, sb, kv_stride, jn * kBN, n, gtid, kr, vr, sr);
 
-    if (kv0 <= qw0 + 31) {  // some key of this tile is visible to some row of this wave
-      // S^T = K . Q^T for the two 32-key halves
-      f32x16 st[2];
-#pragma unroll
-      for (int hf = 0; hf < 2; ++hf) {
-        st[hf] = f32x16{};
-        const uint16_t* krow = &sm.k[buf][(hf * 32 + l32) * AttnSmem<D>::kLd + 8 * g];
-#pragma unroll
-        for (int ks = 0; ks < D / 16; ++ks) {
-          const u32x4 a = *reinterpret_cast<const u32x4*>(krow + 16 * ks);
-          st[hf] = mfma32(a, qf[ks], st[hf]);
-        }
-      }
-      // logits in the exp2 domain, masking, tile max
-      const bool need_mask = (kv0 + kBN - 1 > qw0) || (kv0 + kBN > n);
-      float tmax = -__builtin_inff();
-#pragma unroll
-      for (int hf = 0; hf < 2; ++hf) {
-#pragma unroll
-        for (int q4 = 0; q4 < 4; ++q4) {
-          const int kl = hf * 32 + 8 * q4 + 4 * g;  // first of 4 consecutive keys (tile-local)
-          f32x4 bias = f32x4{0.f, 0.f, 0.f, 0.f};
-          if (use_bias) bias = *reinterpret_cast<const f32x4*>(&sm.s[buf][kl]);
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            float xv = __builtin_fmaf(st[hf][4 * q4 + e], qk_scale, bias_scale * bias[e]);
-            if (need_mask) {
-              const int kvi = kv0 + kl + e;
-              if (kvi > qrow || kvi >= n) xv = -__builtin_inff();
-            }
-            st[hf][4 * q4 + e] = xv;
-            tmax = __builtin_fmaxf(tmax, xv);
-          }
-        }
-      }
-      tmax = __builtin_fmaxf(tmax, __shfl_xor(tmax, 32));
-      const float m_new = __builtin_fmaxf(m_run, tmax);
-      const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
-      m_run = m_new;
-      float psum = 0.0f;
-      u32x4 pf[4];  // P^T operands of the 4 PV steps (16 keys each)
-#pragma unroll
-      for (int hf = 0; hf < 2; ++hf) {
-#pragma unroll
-        for (int sub = 0; sub < 2; ++sub) {
-          float p[8];
-#pragma unroll
-          for (int j = 0; j < 8; ++j) {
-            p[j] = __builtin_amdgcn_exp2f(st[hf][8 * sub + j] - m_new);
-            psum += p[j];
-          }
-          u32x4 w;
-#pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-            typedef float f32x2 __attribute__((ext_vector_type(2)));
-            w[j] = __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2{p[2 * j], p[2 * j + 1]}), bf16x2));
-          }
-          pf[2 * hf + sub] = w;
-        }
-      }
-      l_run = l_run * alpha + psum;
-#pragma unroll
-      for (int dt = 0; dt < D / 32; ++dt) o[dt] *= alpha;
-      // O^T += V^T . P^T
-#pragma unroll
-      for (int s4 = 0; s4 < 4; ++s4) {
-#pragma unroll
-        for (int dt = 0; dt < D / 32; ++dt) {
-          const uint16_t* vrow = &sm.vt[buf][(dt * 32 + l32) * AttnSmem<D>::vLd + 16 * s4 + 4 * g];
-          const u32x2 lo = *reinterpret_cast<const u32x2*>(vrow);
-          const u32x2 hi = *reinterpret_cast<const u32x2*>(vrow + 8);
-          const u32x4 a = u32x4{lo[0], lo[1], hi[0], hi[1]};
-          o[dt] = mfma32(a, pf[s4], o[dt]);
-        }
-      }
+    if (jt < ntiles && kv0 <= qw0 + 31) {  // some key of this tile is visible to some row of this wave
+      const AttnSmem<D>& s_ = sm[buf][grp];
+      if ((kv0 + kBN - 1 > qw0) || (kv0 + kBN > n))
+        attend_tile<D, true>(s_, hl, qf, o, m_run, l_run, qk_scale, min(qrow, n - 1) - kv0, g, l32);
+      else
+        attend_tile<D, false>(s_, hl, qf, o, m_run, l_run, qk_scale, 0, g, l32);
     }
 
-    if (more) store_kv_tile<D>(sm, buf ^ 1, tid, kr, vr, sr);
+    if (more) store_kv_tile<D, G>(sm[buf ^ 1][grp], 0, gtid, kr, vr, sr, bscale);
     __syncthreads();
   }
 
-  // normalise and store: lane holds O^T[d][qrow], d = 32 dt + 8 (i / 4) + 4 g + (i % 4)
-  const float l_tot = l_run + __shfl_xor(l_run, 32);
-  const float inv = 1.0f / l_tot;
-  if (qrow < n) {
-    uint16_t* orow = out + ((int64_t)seg.kept_start + qrow) * q_stride + (int64_t)h * D;
+  // Merge the two groups: group 1 hands (m, l, O^T) to group 0 through LDS.
+  float* xo = reinterpret_cast<float*>(&sm[0][0]);  // 4 waves x (D x 32 + 64) floats, fits in the K/V buffers
+  float* mine = xo + wave * (D * 32 + 64);
+  const float l_half = l_run + __shfl_xor(l_run, 32);  // both half-waves: same bits
+  if (grp == 1) {
 #pragma unroll
-    for (int dt = 0; dt < D / 32; ++dt) {
+    for (int dt = 0; dt < D / 32; ++dt)
 #pragma unroll
-      for (int q4 = 0; q4 < 4; ++q4) {
-        typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-        typedef float f32x2 __attribute__((ext_vector_type(2)));
-        const f32x16& a = o[dt];
-        const uint32_t w0 = __builtin_bit_cast(
-            uint32_t, __builtin_convertvector((f32x2{a[4 * q4] * inv, a[4 * q4 + 1] * inv}), bf16x2));
-        const uint32_t w1 = __builtin_bit_cast(
-            uint32_t, __builtin_convertvector((f32x2{a[4 * q4 + 2] * inv, a[4 * q4 + 3] * inv}), bf16x2));
-        *reinterpret_cast<u32x2*>(orow + 32 * dt + 8 * q4 + 4 * g) = u32x2{w0, w1};
+      for (int i = 0; i < 16; ++i) mine[(dt * 16 + i) * 64 + lane] = o[dt][i];
+    if (g == 0) {
+      mine[D * 32 + l32] = m_run;
+      mine[D * 32 + 32 + l32] = l_half;
+    }
+  }
+  __syncthreads();
+  if (grp == 0) {
+    const float m1 = mine[D * 32 + l32];
+    const float l1 = mine[D * 32 + 32 + l32];
+    const float m = __builtin_fmaxf(m_run, m1);
+    const float a0 = m_run == -__builtin_inff() ? 0.0f : __builtin_amdgcn_exp2f(m_run - m);
+    const float a1 = m1 == -__builtin_inff() ? 0.0f : __builtin_amdgcn_exp2f(m1 - m);
+    const float inv = 1.0f / (l_half * a0 + l1 * a1);
+    if (qrow < n) {
+      uint16_t* orow = out + ((int64_t)seg.kept_start + qrow) * q_stride + (int64_t)h * D;
+#pragma unroll
+      for (int dt = 0; dt < D / 32; ++dt) {
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4) {
+          typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+          typedef float f32x2 __attribute__((ext_vector_type(2)));
+          float r[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int i = 4 * q4 + e;
+            r[e] = (o[dt][i] * a0 + mine[(dt * 16 + i) * 64 + lane] * a1) * inv;
+          }
+          const uint32_t w0 = __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2{r[0], r[1]}), bf16x2));
+          const uint32_t w1 = __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2{r[2], r[3]}), bf16x2));
+          *reinterpret_cast<u32x2*>(orow + 32 * dt + 8 * q4 + 4 * g) = u32x2{w0, w1};
+        }
       }
     }
   }

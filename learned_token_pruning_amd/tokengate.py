@@ -63,7 +63,7 @@ _lib.tg_abi_version.restype = _i32
 _lib.tg_plan_segments.restype = _i32
 _lib.tg_plan_segments.argtypes = [_i32, _vp, _vp, _vp, _vp, ctypes.POINTER(Segment), ctypes.POINTER(PlanInfo)]
 _lib.tg_gate_workspace_bytes.restype = _sz
-_lib.tg_gate_workspace_bytes.argtypes = [ctypes.POINTER(PlanInfo)]
+_lib.tg_gate_workspace_bytes.argtypes = [ctypes.POINTER(PlanInfo), _i32, _i32]
 _lib.tg_gate_score.restype = _i32
 _lib.tg_gate_score.argtypes = [_vp, _i64, _i32, _vp, _vp, _vp, _f32, _i32, _vp, ctypes.POINTER(PlanInfo), _f32, _vp,
                                _vp, _sz, _vp]
@@ -179,8 +179,8 @@ def _dev_table(plan: Plan) -> ctypes.c_void_p:
 # ----------------------------------------------------------------------------
 
 
-def gate_workspace_bytes(plan: Plan) -> int:
-    return int(_lib.tg_gate_workspace_bytes(ctypes.byref(plan.info)))
+def gate_workspace_bytes(plan: Plan, d: int, h: int) -> int:
+    return int(_lib.tg_gate_workspace_bytes(ctypes.byref(plan.info), d, h))
 
 
 def select_workspace_bytes(plan: Plan) -> int:
@@ -199,7 +199,7 @@ def gate_score(x: torch.Tensor, w1: torch.Tensor, b1: Optional[torch.Tensor], w2
     if scores is None:
         scores = torch.empty(plan.n_tokens, dtype=torch.float32, device=x.device)
     if workspace is None:
-        workspace = _workspace(gate_workspace_bytes(plan), x.device)
+        workspace = _workspace(gate_workspace_bytes(plan, d, h), x.device)
     st = _lib.tg_gate_score(_ptr(x), x.stride(0), d, _ptr(w1), _ptr(b1), _ptr(w2), float(b2), h, _dev_table(plan),
                             ctypes.byref(plan.info), float(rms_eps), _ptr(scores), _ptr(workspace),
                             workspace.numel() * workspace.element_size(), _stream(stream))

@@ -71,7 +71,7 @@ def test_gate_validation():
     p = _plan()
     info = ctypes.byref(p.info)
     f = L.tg_gate_score
-    ws = tg.gate_workspace_bytes(p)
+    ws = tg.gate_workspace_bytes(p, 2048, 256)
     assert ws >= 8 and ws % 256 == 0
     # null x
     assert f(None, 2048, 2048, FAKE, None, FAKE, 0.0, 256, FAKE, info, 1e-6, FAKE, FAKE, ws, None) == -1
@@ -95,12 +95,13 @@ def test_select_validation():
     p = _plan()
     info = ctypes.byref(p.info)
     ws = tg.select_workspace_bytes(p)
-    assert ws > 0
+    assert ws >= 0
     f = L.tg_select_topk
     assert f(None, FAKE, info, FAKE, FAKE, ws, None) == -1
     assert f(FAKE, FAKE, info, None, FAKE, ws, None) == -1
-    assert f(FAKE, FAKE, info, FAKE, FAKE, ws - 4, None) == -3
-    assert f(FAKE, FAKE, info, FAKE, None, ws, None) == -3
+    if ws > 0:
+        assert f(FAKE, FAKE, info, FAKE, FAKE, ws - 4, None) == -3
+        assert f(FAKE, FAKE, info, FAKE, None, ws, None) == -3
     bad = tg.PlanInfo(n_tokens=10, total_kept=20, n_seg=1, max_seg_len=10, max_doc_len=5, max_kept_len=10)
     assert f(FAKE, FAKE, ctypes.byref(bad), FAKE, FAKE, ws, None) == -1
 
@@ -140,7 +141,7 @@ def test_attention_validation():
 def test_valid_calls_report_no_device_without_gpu():
     p = _plan()
     info = ctypes.byref(p.info)
-    ws = tg.gate_workspace_bytes(p)
+    ws = tg.gate_workspace_bytes(p, 2048, 256)
     assert L.tg_gate_score(FAKE, 2048, 2048, FAKE, None, FAKE, 0.0, 256, FAKE, info, 1e-6, FAKE, FAKE, ws, None) == -4
     assert L.tg_select_topk(FAKE, FAKE, info, FAKE, FAKE, tg.select_workspace_bytes(p), None) == -4
     assert L.tg_gated_attention_prefill(FAKE, FAKE, FAKE, None, None, None, FAKE, info, 16, 8, 128, FAKE, None) == -4
