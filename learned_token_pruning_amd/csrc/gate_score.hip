@@ -211,8 +211,7 @@ __global__ __launch_bounds__(kThreads) void gate_mlp_kernel(const uint16_t* __re
   }
 #pragma unroll
   for (int rt = 0; rt < 2; ++rt) {
-    const float other = __shfl_xor(part[rt], 32);
-    const float both = part[rt] + other;  // commutative: both half-waves hold the same bits
+    const float both = xor32_sum(part[rt]);  // both half-waves hold the same bits
     if (g == 0) red[wave][rt * 32 + l32] = both;
   }
   __syncthreads();

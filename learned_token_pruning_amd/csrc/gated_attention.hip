@@ -41,38 +41,34 @@ struct AttnSmem {
   float s[4][kBN];  // gate bias of every key, pre-multiplied by g_h log2(e), one row per query head of the group
 };
 
+// Per-thread constant parts of the K/V/score tile loads (byte offsets).
 template <int D>
-__device__ __forceinline__ void load_kv_tile(const uint16_t* __restrict__ kb, const uint16_t* __restrict__ vb,
-                                             const float* __restrict__ sb, int64_t kv_stride, int kv0, int n_keys,
-                                             int tid, u32x4 (&kr)[D / 32], u32x4 (&vr)[4], float& sr) {
-  // K: D/8 threads per row, 16 bytes each, so every load instruction reads whole rows
-  {
-    constexpr int kTpr = D / 8;            // threads per row
-    constexpr int kRpi = 256 / kTpr;       // rows per load instruction
-    const int c = (tid % kTpr) * 8;
-#pragma unroll
-    for (int j = 0; j < D / 32; ++j) {
-      const int r = tid / kTpr + kRpi * j;
-      if (kv0 + r < n_keys)
-        kr[j] = *reinterpret_cast<const u32x4*>(kb + (int64_t)(kv0 + r) * kv_stride + c);
-      else
-        kr[j] = u32x4{0u, 0u, 0u, 0u};
-    }
-  }
-  // V: 4 consecutive key rows x 8 dims; (dc, kq) chosen so the transposed LDS writes are conflict free
-  if (tid < 2 * D) {
+struct TileAddr {
+  uint32_t k_off;  // K: D/8 threads per row, 16 bytes each, rows tid / (D/8) + j 256/(D/8)
+  uint32_t v_off;  // V: 4 consecutive rows x 8 dims (see store_kv_tile)
+  uint32_t s_off;  // score: one key per thread (tid < 64)
+  __device__ TileAddr(int tid, uint32_t row_bytes) {
+    k_off = (uint32_t)(tid / (D / 8)) * row_bytes + (uint32_t)(tid % (D / 8)) * 16u;
     const int dc = (tid & 1) + 2 * ((tid >> 4) % (D / 16));
     const int kq = ((tid >> 1) & 7) + 8 * (tid / D);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int r = kv0 + 4 * kq + i;
-      if (r < n_keys)
-        vr[i] = *reinterpret_cast<const u32x4*>(vb + (int64_t)r * kv_stride + dc * 8);
-      else
-        vr[i] = u32x4{0u, 0u, 0u, 0u};
-    }
+    v_off = (uint32_t)(4 * kq) * row_bytes + (uint32_t)dc * 16u;
+    s_off = (uint32_t)tid * 4u;
   }
-  if (tid < kBN) sr = (sb != nullptr && kv0 + tid < n_keys) ? sb[kv0 + tid] : 0.0f;
+};
+
+// Buffer loads of one 64-key tile; keys past the prompt read as zeros.
+template <int D>
+__device__ __forceinline__ void load_kv_tile(__amdgpu_buffer_rsrc_t rk, __amdgpu_buffer_rsrc_t rv,
+                                             __amdgpu_buffer_rsrc_t rs, const TileAddr<D>& ad, uint32_t row_bytes,
+                                             int kv0, int tid, u32x4 (&kr)[D / 32], u32x4 (&vr)[4], float& sr) {
+  constexpr int kRpi = 256 / (D / 8);  // K rows per load instruction
+#pragma unroll
+  for (int j = 0; j < D / 32; ++j) kr[j] = buf_load16(rk, ad.k_off, (uint32_t)(kv0 + kRpi * j) * row_bytes);
+  if (tid < 2 * D) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) vr[i] = buf_load16(rv, ad.v_off, (uint32_t)(kv0 + i) * row_bytes);
+  }
+  if (tid < kBN) sr = buf_load4f(rs, ad.s_off, (uint32_t)kv0 * 4u);
 }
 
 template <int D, int G>
@@ -91,11 +87,11 @@ __device__ __forceinline__ void store_kv_tile(AttnSmem<D>& sm, int buf, int tid,
     const int kq = ((tid >> 1) & 7) + 8 * (tid / D);
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
+      // dim e of the 4 rows: low or high bf16 of word e / 2 of each row, packed pairwise
+      const uint32_t sel = (e & 1) ? 0x07060302u : 0x05040100u;
       const int w = e >> 1;
-      const int sh = (e & 1) * 16;
-      const uint32_t a0 = (vr[0][w] >> sh) & 0xffffu, a1 = (vr[1][w] >> sh) & 0xffffu;
-      const uint32_t a2 = (vr[2][w] >> sh) & 0xffffu, a3 = (vr[3][w] >> sh) & 0xffffu;
-      u32x2 pk = u32x2{a0 | (a1 << 16), a2 | (a3 << 16)};
+      const u32x2 pk = u32x2{__builtin_amdgcn_perm(vr[1][w], vr[0][w], sel),
+                             __builtin_amdgcn_perm(vr[3][w], vr[2][w], sel)};
       *reinterpret_cast<u32x2*>(&sm.vt[buf][(dc * 8 + e) * AttnSmem<D>::vLd + 4 * kq]) = pk;
     }
   }
@@ -140,12 +136,13 @@ __device__ __forceinline__ void attend_tile(const AttnSmem<D>& s_, int hl, const
       }
     }
   }
-  tmax = __builtin_fmaxf(tmax, __shfl_xor(tmax, 32));
+  tmax = xor32_max(tmax);
   // Lazy rescale: the reference point m_run only moves when some row's max
   // exceeds it by more than 2^8 (or on the first visible tile); softmax does
   // not depend on the reference point, and exp2(x - m_run) <= 2^8 stays well
   // inside fp32 and bf16 range.
   if (__ballot(tmax > m_run + 8.0f) != 0) {
+    asm volatile("; rare rescale");  // keeps this a branch rather than a select on every tile
     const float m_new = __builtin_fmaxf(m_run, tmax);
     const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
     l_run *= alpha;
@@ -219,7 +216,13 @@ __global__ __launch_bounds__(kThreads) void gated_attention_kernel(
   const uint16_t* kb = k + (int64_t)seg.kept_start * kv_stride + (int64_t)c * D;
   const uint16_t* vb = v + (int64_t)seg.kept_start * kv_stride + (int64_t)c * D;
   const bool use_bias = key_score != nullptr && gain != nullptr;
-  const float* sb = use_bias ? key_score + seg.kept_start : nullptr;  // no bias: the LDS score tile holds zeros
+  const uint32_t row_bytes = (uint32_t)kv_stride * 2u;
+  const __amdgpu_buffer_rsrc_t rk = make_rsrc(kb, (uint32_t)n * row_bytes - (uint32_t)c * D * 2u);
+  const __amdgpu_buffer_rsrc_t rv = make_rsrc(vb, (uint32_t)n * row_bytes - (uint32_t)c * D * 2u);
+  // no bias: an empty range makes every score load return 0
+  const __amdgpu_buffer_rsrc_t rs = make_rsrc(use_bias ? key_score + seg.kept_start : key_score,
+                                              use_bias ? (uint32_t)n * 4u : 0u);
+  const TileAddr<D> ad(gtid, row_bytes);
 
   const float th = tau != nullptr ? tau[h] : 1.0f;
   const float qk_scale = th * kLog2e * (1.0f / __builtin_sqrtf((float)D));
@@ -254,7 +257,7 @@ __global__ __launch_bounds__(kThreads) void gated_attention_kernel(
   float sr = 0.0f;
   // pair 0: group 0 stages tile 0, group 1 tile 1 (if any)
   if (grp < ntiles) {
-    load_kv_tile<D>(kb, vb, sb, kv_stride, grp * kBN, n, gtid, kr, vr, sr);
+    load_kv_tile<D>(rk, rv, rs, ad, row_bytes, grp * kBN, gtid, kr, vr, sr);
     store_kv_tile<D, G>(sm[0][grp], 0, gtid, kr, vr, sr, bscale);
   }
   __syncthreads();
@@ -265,7 +268,7 @@ __global__ __launch_bounds__(kThreads) void gated_attention_kernel(
     const int kv0 = jt * kBN;
     const int jn = jt + 2;        // this group's next key tile
     const bool more = jn < ntiles;
-    if (more) load_kv_tile<D>(kb, vb, sb, kv_stride, jn * kBN, n, gtid, kr, vr, sr);
+    if (more) load_kv_tile<D>(rk, rv, rs, ad, row_bytes, jn * kBN, gtid, kr, vr, sr);
 
     if (jt < ntiles && kv0 <= qw0 + 31) {  // some key of this tile is visible to some row of this wave
       const AttnSmem<D>& s_ = sm[buf][grp];
@@ -282,7 +285,7 @@ __global__ __launch_bounds__(kThreads) void gated_attention_kernel(
   // Merge the two groups: group 1 hands (m, l, O^T) to group 0 through LDS.
   float* xo = reinterpret_cast<float*>(&sm[0][0]);  // 4 waves x (D x 32 + 64) floats, fits in the K/V buffers
   float* mine = xo + wave * (D * 32 + 64);
-  const float l_half = l_run + __shfl_xor(l_run, 32);  // both half-waves: same bits
+  const float l_half = xor32_sum(l_run);  // both half-waves: same bits
   if (grp == 1) {
 #pragma unroll
     for (int dt = 0; dt < D / 32; ++dt)
