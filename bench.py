@@ -158,6 +158,44 @@ def cpu_baseline(layer, k_budget, budget_s=12.0):
                       f"{t:.2f} s each"}
 
 
+def kernel_traffic(kernel_source):
+    """HBM bytes per launch of a kernel from the committed rocprofv3 counter
+    summary (profiles/traffic.json), or None when the kernel source has
+    changed since the counters were taken."""
+    import hashlib
+    try:
+        with open(os.path.join(ROOT, "profiles", "traffic.json")) as f:
+            rec = json.load(f)[os.path.basename(kernel_source)]
+        with open(kernel_source, "rb") as f:
+            sha = hashlib.sha256(f.read()).hexdigest()
+    except (OSError, KeyError, ValueError):
+        return None
+    return rec["bytes_per_launch"] if rec.get("source_sha256") == sha else None
+
+
+def stage_rooflines(pipe, st, csrc):
+    """Roofline entry of every stage (algorithmic work / measured time)."""
+    attn_tflops = pipe.attention_flops() / (st["attention"] * 1e-6) / 1e12
+    gate_gbs = pipe.gate_bytes() / (st["gate"] * 1e-6) / 1e9
+    compact_gbs = pipe.compact_bytes() / (st["compact"] * 1e-6) / 1e9
+    select_gbs = (4 * pipe.seg.n_tokens + 4 * pipe.m) / (st["select"] * 1e-6) / 1e9
+    return {
+        "attention": {"kernel": "gated_attention_kernel<128,2>", "bound": "mfma", "achieved": attn_tflops,
+                      "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": attn_tflops / MFMA_BF16_PEAK_TFLOPS,
+                      "traffic": kernel_traffic(os.path.join(csrc, "gated_attention.hip"))},
+        "gate": {"kernel": "pack_w1_kernel + gate_mlp_kernel<2,4> + gate_normalize_kernel", "bound": "hbm",
+                 "achieved": gate_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": gate_gbs / HBM_PEAK_GBS,
+                 "traffic": kernel_traffic(os.path.join(csrc, "gate_score.hip")),
+                 "mfma_tflops": pipe.gate_flops() / (st["gate"] * 1e-6) / 1e12},
+        "compact": {"kernel": "compact_kernel", "bound": "hbm", "achieved": compact_gbs, "peak": HBM_PEAK_GBS,
+                    "unit": "GB/s", "frac": compact_gbs / HBM_PEAK_GBS,
+                    "traffic": kernel_traffic(os.path.join(csrc, "compact.hip"))},
+        "select": {"kernel": "select_topk_kernel", "bound": "hbm", "achieved": select_gbs, "peak": HBM_PEAK_GBS,
+                   "unit": "GB/s", "frac": select_gbs / HBM_PEAK_GBS,
+                   "traffic": kernel_traffic(os.path.join(csrc, "select_topk.hip"))},
+    }
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -165,6 +203,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-long", action="store_true", help="skip the 128K-token layer")
+    ap.add_argument("--only-long", action="store_true", help="time only the 128K-token layer (profiling)")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="also run one plain 256 MiB device copy (reference for rocprofv3 FETCH_SIZE / WRITE_SIZE)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (the hot path is single-GPU here); got --gpus {args.gpus}",
@@ -180,82 +221,80 @@ def main():
         _b.build()
     from learned_token_pruning_amd import tokengate as tg
     from learned_token_pruning_amd import workloads as W
+    csrc = os.path.join(ROOT, "learned_token_pruning_amd", "csrc")
 
-    log("generating the 16K-token workload")
-    l16 = W.workload(2)
-    p16 = Pipeline(l16, 2048, torch, tg)
-    log("timing 16K", args.steps, "steps")
-    us_wall, us_gpu, st16 = time_pipeline(p16, args.steps, args.warmup)
-    log("16K: wall", f"{us_wall:.1f} us/step, events {us_gpu:.1f} us/step", st16)
+    if args.calibrate_copy:
+        src = torch.empty(64 * 2 ** 20, dtype=torch.float32, device="cuda").fill_(1.0)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
 
-    attn_tflops = p16.attention_flops() / (st16["attention"] * 1e-6) / 1e12
-    gate_gbs = p16.gate_bytes() / (st16["gate"] * 1e-6) / 1e9
-    gate_tflops = p16.gate_flops() / (st16["gate"] * 1e-6) / 1e12
-    sc_gbs = p16.select_compact_bytes() / ((st16["select"] + st16["compact"]) * 1e-6) / 1e9
-    compact_gbs = p16.compact_bytes() / (st16["compact"] * 1e-6) / 1e9
-    dominant = max(st16, key=st16.get)
-    if dominant == "attention":
-        roof = {"kernel": "gated_attention_kernel<128,2>", "bound": "mfma", "achieved": attn_tflops,
-                "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": attn_tflops / MFMA_BF16_PEAK_TFLOPS,
-                "traffic": None}
-    elif dominant == "gate":
-        roof = {"kernel": "gate_mlp_kernel<2> + gate_normalize_kernel", "bound": "hbm", "achieved": gate_gbs,
-                "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": gate_gbs / HBM_PEAK_GBS, "traffic": None}
-    elif dominant == "compact":
-        roof = {"kernel": "compact_kernel", "bound": "hbm", "achieved": compact_gbs, "peak": HBM_PEAK_GBS,
-                "unit": "GB/s", "frac": compact_gbs / HBM_PEAK_GBS, "traffic": None}
-    else:
-        b = 4 * p16.seg.n_doc(0) + 4 * p16.m
-        gbs = b / (st16["select"] * 1e-6) / 1e9
-        roof = {"kernel": "select (6 launches)", "bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS,
-                "unit": "GB/s", "frac": gbs / HBM_PEAK_GBS, "traffic": None}
-
-    result = {
-        "metric": METRIC,
-        "value": p16.n / (us_wall * 1e-6),
-        "unit": "tokens/s",
-        "n_gpus": 1,
-        "steps": args.steps,
-        "warmup": args.warmup,
-        "ms_per_step": us_wall / 1e3,
-        "higher_is_better": True,
-        "scaling": "weak",
-        "vs_baseline": None,
-        "dtype": "bf16",
-        "data": "synthetic",
-        "config": {"workload": "gated layer N=16384 (16320 doc + 64 question), d=2048, gate 2048-256-1, K=2048 "
-                               "(M=2112 kept), 16 Q / 8 KV heads, head_dim 128",
-                   "global_batch": 1, "seq_len": p16.n, "k_budget": 2048, "kept_rows": p16.m,
-                   "parallelism": "none", "launch": "eager, one stream"},
-        "roofline": roof,
-        "stages_us": {k: round(v, 2) for k, v in st16.items()},
-        "gpu_us_per_step_events": round(us_gpu, 2),
-        "attention": {"tflops": attn_tflops, "frac_mfma_peak": attn_tflops / MFMA_BF16_PEAK_TFLOPS},
-        "gate": {"gbs": gate_gbs, "frac_hbm_peak": gate_gbs / HBM_PEAK_GBS, "tflops": gate_tflops,
-                 "frac_mfma_peak": gate_tflops / MFMA_BF16_PEAK_TFLOPS},
-        "select_plus_compact": {"gbs": sc_gbs, "frac_hbm_peak": sc_gbs / HBM_PEAK_GBS},
-    }
-    del p16
-    torch.cuda.empty_cache()
+    result = None
+    l16 = None
+    if not args.only_long:
+        log("generating the 16K-token workload")
+        l16 = W.workload(2)
+        p16 = Pipeline(l16, 2048, torch, tg)
+        log("timing 16K", args.steps, "steps")
+        us_wall, us_gpu, st16 = time_pipeline(p16, args.steps, args.warmup)
+        log("16K: wall", f"{us_wall:.1f} us/step, events {us_gpu:.1f} us/step", st16)
+        roofs = stage_rooflines(p16, st16, csrc)
+        dominant = max(st16, key=st16.get)
+        sc_gbs = p16.select_compact_bytes() / ((st16["select"] + st16["compact"]) * 1e-6) / 1e9
+        result = {
+            "metric": METRIC,
+            "value": p16.n / (us_wall * 1e-6),
+            "unit": "tokens/s",
+            "n_gpus": 1,
+            "steps": args.steps,
+            "warmup": args.warmup,
+            "ms_per_step": us_wall / 1e3,
+            "higher_is_better": True,
+            "scaling": "weak",
+            "vs_baseline": None,
+            "dtype": "bf16",
+            "data": "synthetic",
+            "config": {"workload": "gated layer N=16384 (16320 doc + 64 question), d=2048, gate 2048-256-1, "
+                                   "K=2048 (M=2112 kept), 16 Q / 8 KV heads, head_dim 128",
+                       "global_batch": 1, "seq_len": p16.n, "k_budget": 2048, "kept_rows": p16.m,
+                       "parallelism": "none", "launch": "eager, one stream"},
+            "roofline": dict(roofs[dominant], stage=dominant),
+            "stages_us": {k: round(v, 2) for k, v in st16.items()},
+            "stage_rooflines": roofs,
+            "gpu_us_per_step_events": round(us_gpu, 2),
+            "attention": {"tflops": roofs["attention"]["achieved"], "frac_mfma_peak": roofs["attention"]["frac"]},
+            "select_plus_compact": {"gbs": sc_gbs, "frac_hbm_peak": sc_gbs / HBM_PEAK_GBS},
+        }
+        del p16
+        torch.cuda.empty_cache()
 
     if not args.no_long:
         log("generating the 128K-token workload")
         l128 = W.workload(4)
         torch.cuda.reset_peak_memory_stats()
         p128 = Pipeline(l128, 2048, torch, tg)
-        steps = max(10, args.steps // 4)
+        steps = args.steps if args.only_long else max(10, args.steps // 4)
         us_wall128, us_gpu128, st128 = time_pipeline(p128, steps, max(3, args.warmup // 4))
         log("128K: wall", f"{us_wall128:.1f} us/step", st128)
-        result["n131072_k2048"] = {
+        long_rec = {
+            "workload": "gated layer N=131072 (131008 doc + 64 question), d=2048, K=2048 (M=2112 kept)",
             "tokens_per_s": p128.n / (us_wall128 * 1e-6), "ms_per_step": us_wall128 / 1e3, "steps": steps,
             "stages_us": {k: round(v, 2) for k, v in st128.items()},
-            "gate_gbs": p128.gate_bytes() / (st128["gate"] * 1e-6) / 1e9,
+            "stage_rooflines": stage_rooflines(p128, st128, csrc),
             "peak_device_mem_gib": torch.cuda.max_memory_allocated() / 2 ** 30,
         }
         del p128, l128
         torch.cuda.empty_cache()
+        if result is None:
+            result = {"metric": METRIC, "value": long_rec["tokens_per_s"], "unit": "tokens/s", "n_gpus": 1,
+                      "steps": steps, "warmup": args.warmup, "ms_per_step": long_rec["ms_per_step"],
+                      "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+                      "data": "synthetic", "config": {"workload": long_rec["workload"]}}
+        result["n131072_k2048"] = long_rec
 
-    if not args.no_cpu_baseline:
+    if not args.no_cpu_baseline and l16 is not None:
         log("timing the CPU oracle on the 16K workload")
         result["cpu_baseline"] = cpu_baseline(l16, 2048)
     print(json.dumps(result), flush=True)
