@@ -25,10 +25,8 @@
 namespace tg {
 namespace {
 
-constexpr int kRows = 64;      // document rows per workgroup
-constexpr int kKB = 64;        // d per pipeline stage
+constexpr int kRows = 64;      // smallest tile height (document rows per workgroup)
 constexpr int kThreads = 256;  // 4 waves
-constexpr int kXLd = kKB + 8;  // LDS row stride in bf16 (144 B: conflict-free 16-byte reads)
 
 // GELU(u) = u Phi(u) = 0.5 u (1 + erf(u / sqrt 2)), with erf from Abramowitz &
 // Stegun, Handbook of Mathematical Functions, formula 7.1.26 (|error| <= 1.5e-7):
@@ -44,26 +42,6 @@ __device__ __forceinline__ float gelu_erf(float u) {
   p *= t;
   const float q = p * __builtin_amdgcn_exp2f(-z * z * 1.4426950408889634f);
   return 0.5f * u * (u >= 0.0f ? 2.0f - q : q);
-}
-
-// Loads this thread's share of an X stage (64 rows x 64 k): 8 threads per
-// 128-byte row, rows tid / 8 and 32 + tid / 8, 16 bytes at column (tid % 8) * 8.
-// Rows past the tile's last document row re-read that row (their results are
-// discarded), so the load is unconditional.
-__device__ __forceinline__ void load_x_stage(const uint16_t* __restrict__ x, int64_t ld_x, int64_t row0, int nrows,
-                                             int k0, int tid, u32x4 (&p)[2]) {
-  const int c = (tid & 7) * 8;
-#pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    const int r = min((tid >> 3) + 32 * i, nrows - 1);
-    p[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(x + (row0 + r) * ld_x + k0 + c));
-  }
-}
-
-__device__ __forceinline__ void store_x_stage(uint16_t* lds, int tid, const u32x4 (&p)[2]) {
-  const int c = (tid & 7) * 8;
-#pragma unroll
-  for (int i = 0; i < 2; ++i) *reinterpret_cast<u32x4*>(lds + ((tid >> 3) + 32 * i) * kXLd + c) = p[i];
 }
 
 // W1 in MFMA-fragment order (built by pack_w1_kernel in the workspace): for
@@ -96,11 +74,19 @@ __global__ __launch_bounds__(256) void pack_w1_kernel(const uint16_t* __restrict
   w1p[i] = *reinterpret_cast<const u32x4*>(w1 + (int64_t)unit * d + k);
 }
 
-// NCT: 32-unit column tiles per wave (1 or 2).  S: k blocks in flight (W1 and
-// X are prefetched S - 1 blocks ahead in registers); d / 64 is a multiple of S,
-// so the pipelined loop has no guards and the compiler can count the loads
-// still in flight exactly.
-template <int NCT, int S>
+// NCT: 32-unit column tiles per wave (1 or 2).  RT: 32-row tiles per workgroup
+// (BM = 32 RT document rows); every wave covers all BM rows for its units, so
+// a W1 fragment feeds RT MFMAs.  XB: 64-wide k blocks per X stage.
+//
+// X goes through LDS in stages of BM rows x 64 XB columns.  Each wave load
+// reads a contiguous 16 x (64 XB / 8)-byte slice of one row (1 KiB at XB = 8):
+// long row bursts instead of 128-byte pieces scattered over thousands of rows
+// is what lets the HBM stream reach bandwidth.  The next stage is loaded into
+// registers in two halves during the current one (issued at blocks 0 and
+// XB/2, written to the other LDS buffer half a stage later), so there is one
+// barrier per stage.  W1 fragments come straight from the fragment-packed copy
+// through a register ring S blocks deep.  d is a multiple of 64 XB.
+template <int NCT, int S, int RT, int XB>
 __global__ __launch_bounds__(kThreads) void gate_mlp_kernel(const uint16_t* __restrict__ x, int64_t ld_x, int d,
                                                             const u32x4* __restrict__ w1p,
                                                             const float* __restrict__ b1,
@@ -108,16 +94,23 @@ __global__ __launch_bounds__(kThreads) void gate_mlp_kernel(const uint16_t* __re
                                                             const tg_segment* __restrict__ segs, int max_tiles,
                                                             float* __restrict__ scores,
                                                             double* __restrict__ tile_sumsq) {
-  __shared__ __attribute__((aligned(16))) uint16_t xs[2][kRows * kXLd];
-  __shared__ float red[4][kRows];
-  __shared__ double red2[kRows];
+  constexpr int BM = 32 * RT;
+  constexpr int KX = 64 * XB;               // k per X stage
+  constexpr int LD = KX + 8;                // LDS row stride (bf16): 16-byte pad keeps fragment reads conflict free
+  constexpr int UPR = KX / 8;               // 16-byte units per row slice
+  constexpr int HALF = BM * UPR / 2 / kThreads;  // 16-byte loads per thread per half stage
+  static_assert((XB % 2 == 0 || XB == 1) && XB % S == 0, "stage shape");
+  static_assert(HALF >= 1 && (BM * UPR / 2) % kThreads == 0, "stage split");
+  __shared__ __attribute__((aligned(16))) uint16_t xs[2][BM * LD];
+  __shared__ float red[4][BM];
+  __shared__ double red2[BM];
 
   const tg_segment seg = segs[blockIdx.y];
   const int n_doc = seg.doc_end - seg.doc_begin;
   const int tile = blockIdx.x;
-  if (tile * kRows >= n_doc) return;  // uniform across the workgroup
-  const int64_t row0 = (int64_t)seg.seg_start + seg.doc_begin + (int64_t)tile * kRows;
-  const int nrows = min(kRows, n_doc - tile * kRows);
+  if (tile * BM >= n_doc) return;  // uniform across the workgroup
+  const int64_t row0 = (int64_t)seg.seg_start + seg.doc_begin + (int64_t)tile * BM;
+  const int nrows = min(BM, n_doc - tile * BM);
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -129,69 +122,98 @@ __global__ __launch_bounds__(kThreads) void gate_mlp_kernel(const uint16_t* __re
   const int ut0 = active ? unit_base / 32 : 0;
   const int n_ut = h / 32;
 
-  f32x16 acc[NCT][2];
+  // X half-stage h (0: rows [0, BM/2), 1: rows [BM/2, BM)): unit u = i kThreads + tid of the half
+  auto x_src = [&](int hf, int i, int k0) -> const u32x4* {
+    const int u = i * kThreads + tid;
+    const int r = min(hf * (BM / 2) + u / UPR, nrows - 1);  // rows past the tile re-read its last row
+    return reinterpret_cast<const u32x4*>(x + (row0 + r) * ld_x + k0 + (u % UPR) * 8);
+  };
+  auto x_dst = [&](uint16_t* buf, int hf, int i) -> u32x4* {
+    const int u = i * kThreads + tid;
+    return reinterpret_cast<u32x4*>(buf + (hf * (BM / 2) + u / UPR) * LD + (u % UPR) * 8);
+  };
+
+  f32x16 acc[NCT][RT];
 #pragma unroll
   for (int ct = 0; ct < NCT; ++ct)
 #pragma unroll
-    for (int rt = 0; rt < 2; ++rt) acc[ct][rt] = f32x16{};
+    for (int rt = 0; rt < RT; ++rt) acc[ct][rt] = f32x16{};
 
-  const int nkb = d / kKB;
-  u32x4 wr[S][NCT][4];  // W1 ring (registers)
-  u32x4 xr[S][2];       // X ring (registers; written to LDS one block ahead of use)
+  const int nkb = d / 64;
+  const int nst = nkb / XB;
+  u32x4 wr[S][NCT][4];  // W1 ring
+  u32x4 xr[HALF];       // X half stage in flight
 
-  // prologue: blocks 0 .. S-2 in flight, block 0 in LDS
+  // prologue: X stage 0 into LDS, W1 blocks 0 .. S-2 in flight
 #pragma unroll
-  for (int s = 0; s < S - 1; ++s) {
-    load_x_stage(x, ld_x, row0, nrows, s * kKB, tid, xr[s]);
+  for (int hf = 0; hf < 2; ++hf) {
+#pragma unroll
+    for (int i = 0; i < HALF; ++i) xr[i] = __builtin_nontemporal_load(x_src(hf, i, 0));
+#pragma unroll
+    for (int i = 0; i < HALF; ++i) *x_dst(xs[0], hf, i) = xr[i];
+  }
+#pragma unroll
+  for (int s = 0; s < S - 1; ++s)
 #pragma unroll
     for (int ct = 0; ct < NCT; ++ct) load_w_frag(w1p, n_ut, ut0 + ct, s, lane, wr[s][ct]);
-  }
-  if (S == 1) {
-    load_x_stage(x, ld_x, row0, nrows, 0, tid, xr[0]);
-#pragma unroll
-    for (int ct = 0; ct < NCT; ++ct) load_w_frag(w1p, n_ut, ut0 + ct, 0, lane, wr[0][ct]);
-  }
-  store_x_stage(xs[0], tid, xr[0]);
   __syncthreads();
 
-  for (int kb0 = 0; kb0 < nkb; kb0 += S) {
+  for (int st = 0; st < nst; ++st) {
+    const uint16_t* xb = xs[st & 1];
+    uint16_t* xn = xs[(st + 1) & 1];
+    const bool next = st + 1 < nst;
+    const int kx_next = (st + 1) * KX;
 #pragma unroll
-    for (int s = 0; s < S; ++s) {
-      const int kb = kb0 + s;
-      // block kb + S - 1 starts loading now (clamped: the tail re-reads the last block)
-      const int kn = min(kb + S - 1, nkb - 1);
-      if (S > 1) {
-        load_x_stage(x, ld_x, row0, nrows, kn * kKB, tid, xr[(s + S - 1) % S]);
+    for (int c = 0; c < XB; ++c) {
+      const int kb = st * XB + c;
+      if (next && c == 0) {
 #pragma unroll
-        for (int ct = 0; ct < NCT; ++ct) load_w_frag(w1p, n_ut, ut0 + ct, kn, lane, wr[(s + S - 1) % S][ct]);
+        for (int i = 0; i < HALF; ++i) xr[i] = __builtin_nontemporal_load(x_src(0, i, kx_next));
       }
-      const uint16_t* xb = xs[kb & 1];
+      if (next && c == XB / 2) {
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        u32x4 xf[2];
+        for (int i = 0; i < HALF; ++i) *x_dst(xn, 0, i) = xr[i];
 #pragma unroll
-        for (int rt = 0; rt < 2; ++rt)
-          xf[rt] = *reinterpret_cast<const u32x4*>(xb + (rt * 32 + l32) * kXLd + 32 * g + 8 * j);
-#pragma unroll
-        for (int ct = 0; ct < NCT; ++ct)
-#pragma unroll
-          for (int rt = 0; rt < 2; ++rt) acc[ct][rt] = mfma32(wr[s][ct][j], xf[rt], acc[ct][rt]);
+        for (int i = 0; i < HALF; ++i) xr[i] = __builtin_nontemporal_load(x_src(1, i, kx_next));
       }
-      if (S == 1) {  // no ring: load the next block now
-        const int k1 = min(kb + 1, nkb - 1);
-        load_x_stage(x, ld_x, row0, nrows, k1 * kKB, tid, xr[0]);
+      {  // W1 block kb + S - 1 starts loading now (clamped: the tail re-reads the last block)
+        const int kn = min(kb + S - 1, nkb - 1);
 #pragma unroll
-        for (int ct = 0; ct < NCT; ++ct) load_w_frag(w1p, n_ut, ut0 + ct, k1, lane, wr[0][ct]);
-        store_x_stage(xs[(kb + 1) & 1], tid, xr[0]);
-      } else {
-        store_x_stage(xs[(kb + 1) & 1], tid, xr[(s + 1) % S]);
+        for (int ct = 0; ct < NCT; ++ct) load_w_frag(w1p, n_ut, ut0 + ct, kn, lane, wr[(c + S - 1) % S][ct]);
       }
-      __syncthreads();
+      // all X fragments of the block are requested before the first MFMA
+      constexpr int JH = RT <= 2 ? 4 : 2;
+#pragma unroll
+      for (int j0 = 0; j0 < 4; j0 += JH) {
+        u32x4 xf[JH][RT];
+#pragma unroll
+        for (int j = 0; j < JH; ++j)
+#pragma unroll
+          for (int rt = 0; rt < RT; ++rt)
+            xf[j][rt] = *reinterpret_cast<const u32x4*>(xb + (rt * 32 + l32) * LD + 64 * c + 32 * g + 8 * (j0 + j));
+#pragma unroll
+        for (int j = 0; j < JH; ++j)
+#pragma unroll
+          for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+            for (int ct = 0; ct < NCT; ++ct) acc[ct][rt] = mfma32(wr[c % S][ct][j0 + j], xf[j][rt], acc[ct][rt]);
+        // keep the order: every LDS read of the batch, then the MFMAs (the
+        // default schedule reuses one register per read and waits before each MFMA pair)
+        __builtin_amdgcn_sched_group_barrier(0x100, JH * RT, 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, JH * RT * NCT, 0);
+      }
     }
+    if (next) {
+#pragma unroll
+      for (int i = 0; i < HALF; ++i) *x_dst(xn, 1, i) = xr[i];
+    }
+    __syncthreads();
   }
 
   // Epilogue: lane holds U^T[unit][row] for unit = unit_base + 32 ct + 8 (i/4) + 4 g + (i%4), row = 32 rt + l32.
-  float part[2] = {0.f, 0.f};
+  float part[RT];
+#pragma unroll
+  for (int rt = 0; rt < RT; ++rt) part[rt] = 0.f;
   if (active) {
 #pragma unroll
     for (int ct = 0; ct < NCT; ++ct) {
@@ -204,30 +226,30 @@ __global__ __launch_bounds__(kThreads) void gate_mlp_kernel(const uint16_t* __re
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
 #pragma unroll
-          for (int rt = 0; rt < 2; ++rt) part[rt] += gelu_erf(acc[ct][rt][4 * q4 + e] + b1v[e]) * w2v[e];
+          for (int rt = 0; rt < RT; ++rt) part[rt] += gelu_erf(acc[ct][rt][4 * q4 + e] + b1v[e]) * w2v[e];
         }
       }
     }
   }
 #pragma unroll
-  for (int rt = 0; rt < 2; ++rt) {
+  for (int rt = 0; rt < RT; ++rt) {
     const float both = xor32_sum(part[rt]);  // both half-waves hold the same bits
     if (g == 0) red[wave][rt * 32 + l32] = both;
   }
   __syncthreads();
-  if (tid < kRows) {
-    const float r = ((red[0][tid] + red[1][tid]) + (red[2][tid] + red[3][tid])) + b2;
+  for (int i = tid; i < BM; i += kThreads) {
+    const float r = ((red[0][i] + red[1][i]) + (red[2][i] + red[3][i])) + b2;
     double sq = 0.0;
-    if (tid < nrows) {
-      scores[row0 + tid] = r;
+    if (i < nrows) {
+      scores[row0 + i] = r;
       sq = (double)r * (double)r;
     }
-    red2[tid] = sq;
+    red2[i] = sq;
   }
   __syncthreads();
   if (tid == 0) {
     double s = 0.0;
-    for (int i = 0; i < kRows; ++i) s += red2[i];
+    for (int i = 0; i < BM; ++i) s += red2[i];
     tile_sumsq[(int64_t)blockIdx.y * max_tiles + tile] = s;
   }
 }
@@ -236,7 +258,7 @@ constexpr int kNormThreads = 256;
 constexpr int kNormTokens = 1024;  // tokens per block
 
 __global__ __launch_bounds__(kNormThreads) void gate_normalize_kernel(const tg_segment* __restrict__ segs,
-                                                                     int max_tiles,
+                                                                     int max_tiles, int rows_per_tile,
                                                                      const double* __restrict__ tile_sumsq,
                                                                      float rms_eps, float* __restrict__ scores) {
   __shared__ double red[kNormThreads];
@@ -248,7 +270,7 @@ __global__ __launch_bounds__(kNormThreads) void gate_normalize_kernel(const tg_s
   float rho = 1.0f;
   const bool norm = rms_eps >= 0.0f && n_doc > 0;
   if (norm) {
-    const int ntiles = (n_doc + kRows - 1) / kRows;
+    const int ntiles = (n_doc + rows_per_tile - 1) / rows_per_tile;
     const double* ts = tile_sumsq + (int64_t)blockIdx.y * max_tiles;
     double s = 0.0;
     for (int i = tid; i < ntiles; i += kNormThreads) s += ts[i];
@@ -287,10 +309,31 @@ size_t gate_workspace_bytes(const tg_plan_info& info, int d, int h) {
   return sumsq_bytes(info) + (size_t)d * (size_t)h * 2;  // tile sums + W1 in fragment order
 }
 
+template <int NCT, int RT, int XB, int S>
+static void launch_mlp(dim3 grid, hipStream_t stream, const uint16_t* xp, int64_t ld_x, int d, const u32x4* wp,
+                       const float* b1, const float* w2, float b2, int h, const tg_segment* segs, int max_tiles,
+                       float* scores, double* ts) {
+  hipLaunchKernelGGL((gate_mlp_kernel<NCT, S, RT, XB>), grid, dim3(kThreads), 0, stream, xp, ld_x, d, wp, b1, w2, b2,
+                     h, segs, max_tiles, scores, ts);
+}
+
+template <int NCT>
+static void launch_mlp_d(dim3 grid, hipStream_t stream, const uint16_t* xp, int64_t ld_x, int d, const u32x4* wp,
+                         const float* b1, const float* w2, float b2, int h, const tg_segment* segs, int max_tiles,
+                         float* scores, double* ts) {
+  // X stage of 256 columns (512-byte row bursts) when d allows; measured best among 128-1024-byte bursts
+  if (d % 256 == 0)
+    launch_mlp<NCT, 2, 4, 4>(grid, stream, xp, ld_x, d, wp, b1, w2, b2, h, segs, max_tiles, scores, ts);
+  else if (d % 128 == 0)
+    launch_mlp<NCT, 2, 2, 2>(grid, stream, xp, ld_x, d, wp, b1, w2, b2, h, segs, max_tiles, scores, ts);
+  else
+    launch_mlp<NCT, 2, 1, 1>(grid, stream, xp, ld_x, d, wp, b1, w2, b2, h, segs, max_tiles, scores, ts);
+}
+
 hipError_t launch_gate_score(const void* x, int64_t ld_x, int d, const void* w1, const float* b1, const float* w2,
                              float b2, int h, const tg_segment* segs, const tg_plan_info& info, float rms_eps,
                              float* scores, void* workspace, hipStream_t stream) {
-  int max_tiles = (info.max_doc_len + kRows - 1) / kRows;
+  int max_tiles = (info.max_doc_len + kRows - 1) / kRows;  // at the smallest tile height: an upper bound
   if (max_tiles < 1) max_tiles = 1;
   double* ts = reinterpret_cast<double*>(workspace);
   u32x4* w1p = reinterpret_cast<u32x4*>(reinterpret_cast<char*>(workspace) + sumsq_bytes(info));
@@ -299,24 +342,17 @@ hipError_t launch_gate_score(const void* x, int64_t ld_x, int d, const void* w1,
     hipLaunchKernelGGL(pack_w1_kernel, dim3((unsigned)((chunks + 255) / 256)), dim3(256), 0, stream,
                        reinterpret_cast<const uint16_t*>(w1), d, h, w1p);
     dim3 grid(max_tiles, info.n_seg);
-    const int nkb = d / kKB;
     const uint16_t* xp = reinterpret_cast<const uint16_t*>(x);
-    const u32x4* wp = w1p;
-#define TG_GATE_LAUNCH(NCT, S)                                                                                 \
-  hipLaunchKernelGGL((gate_mlp_kernel<NCT, S>), grid, dim3(kThreads), 0, stream, xp, ld_x, d, wp, b1, w2, b2, h, \
-                     segs, max_tiles, scores, ts)
-    if (h <= 128) {
-      if (nkb % 4 == 0) TG_GATE_LAUNCH(1, 4); else if (nkb % 2 == 0) TG_GATE_LAUNCH(1, 2); else TG_GATE_LAUNCH(1, 1);
-    } else {
-      if (nkb % 4 == 0) TG_GATE_LAUNCH(2, 4); else if (nkb % 2 == 0) TG_GATE_LAUNCH(2, 2); else TG_GATE_LAUNCH(2, 1);
-    }
-#undef TG_GATE_LAUNCH
+    if (h <= 128)
+      launch_mlp_d<1>(grid, stream, xp, ld_x, d, w1p, b1, w2, b2, h, segs, max_tiles, scores, ts);
+    else
+      launch_mlp_d<2>(grid, stream, xp, ld_x, d, w1p, b1, w2, b2, h, segs, max_tiles, scores, ts);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
   if (info.max_seg_len > 0) {
     dim3 grid((info.max_seg_len + kNormTokens - 1) / kNormTokens, info.n_seg);
-    hipLaunchKernelGGL(gate_normalize_kernel, grid, dim3(kNormThreads), 0, stream, segs, max_tiles, ts, rms_eps,
+    hipLaunchKernelGGL(gate_normalize_kernel, grid, dim3(kNormThreads), 0, stream, segs, max_tiles, kRows, ts, rms_eps,
                        scores);
     return hipGetLastError();
   }
