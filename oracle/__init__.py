@@ -31,3 +31,12 @@ from .tokengate_ref import (  # noqa: F401
     compact_rows,
     gated_attention,
 )
+from .stack_ref import (  # noqa: F401,E402
+    round_bf16,
+    rmsnorm,
+    rope,
+    silu,
+    LayerWeights,
+    decoder_layer,
+    pruned_stack,
+)

@@ -1,0 +1,143 @@
+"""Pins of the oracle's dense decoder stack: the bf16 format definition,
+closed forms and invariances of RMSNorm / RoPE / SiLU, a layer against the
+same layer assembled from torch library routines (float64), and the pruned
+stack reducing to the unpruned stack when nothing is pruned."""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+
+
+def test_round_bf16_definition():
+    v = np.array([1.0, 1 + 2 ** -8, 1 + 3 * 2 ** -8, 1 + 2 ** -7, -2.5, 3.0e38, 1e-40, 0.0])
+    got = oracle.round_bf16(v)
+    # halfway cases go to the even significand; 1 + 2^-7 is exactly representable
+    exp = np.array([1.0, 1.0, 1 + 4 * 2 ** -8, 1 + 2 ** -7, -2.5, got[5], got[6], 0.0])
+    np.testing.assert_array_equal(got[[0, 1, 2, 3, 4, 7]], exp[[0, 1, 2, 3, 4, 7]])
+    assert abs(got[5] - 3.0e38) / 3.0e38 <= 2 ** -8
+    x = np.random.default_rng(0).standard_normal(5000)
+    r = oracle.round_bf16(x)
+    assert np.all(np.abs(r - x) <= 2 ** -8 * np.abs(x))
+    assert np.array_equal(oracle.round_bf16(r), r)  # idempotent
+
+
+def test_rmsnorm_closed_forms():
+    w = np.array([1.0, 2.0, -1.0, 0.5])
+    x = np.full((1, 4), -3.0)
+    np.testing.assert_allclose(oracle.rmsnorm(x, w, 0.0), -w[None, :], rtol=1e-15)
+    rng = np.random.default_rng(1)
+    x = rng.standard_normal((5, 64))
+    np.testing.assert_allclose(oracle.rmsnorm(7.0 * x, np.ones(64), 0.0), oracle.rmsnorm(x, np.ones(64), 0.0),
+                               rtol=1e-13)
+    y = oracle.rmsnorm(x, np.ones(64), 0.0)
+    np.testing.assert_allclose(np.mean(y * y, axis=1), 1.0, rtol=1e-13)
+
+
+def test_rope_rotation_properties():
+    rng = np.random.default_rng(2)
+    q = rng.standard_normal((6, 3, 16))
+    k = rng.standard_normal((6, 3, 16))
+    pos = np.array([0, 1, 5, 100, 4095, 65535])
+    qr = oracle.rope(q, pos, 1e6)
+    np.testing.assert_allclose(qr[0], q[0], rtol=0, atol=0)  # position 0 is the identity
+    # each pair (i, i + D/2) keeps its length
+    half = 8
+    np.testing.assert_allclose(qr[..., :half] ** 2 + qr[..., half:] ** 2, q[..., :half] ** 2 + q[..., half:] ** 2,
+                               rtol=1e-12)
+    # q(p) . k(p') depends only on p - p'
+    a = np.einsum("hd,hd->h", oracle.rope(q[1:2], [7], 1e4)[0], oracle.rope(k[2:3], [3], 1e4)[0])
+    b = np.einsum("hd,hd->h", oracle.rope(q[1:2], [1007], 1e4)[0], oracle.rope(k[2:3], [1003], 1e4)[0])
+    np.testing.assert_allclose(a, b, rtol=1e-9)
+    # the first pair rotates by exactly p radians
+    e = np.zeros((1, 1, 16)); e[0, 0, 0] = 1.0
+    np.testing.assert_allclose(oracle.rope(e, [2], 1e6)[0, 0, [0, 8]], [math.cos(2), math.sin(2)], rtol=1e-15)
+
+
+def test_silu_antisymmetry():
+    x = np.linspace(-20, 20, 101)
+    np.testing.assert_allclose(oracle.silu(x) - oracle.silu(-x), x, rtol=1e-13, atol=1e-13)
+
+
+def _layer(rng, d, hq, hkv, dh, f, gated=False):
+    s = 0.02
+    mk = lambda *shape: rng.standard_normal(shape) * s
+    tau = rng.uniform(0.8, 1.2, hq) if gated else None
+    gain = rng.uniform(0.5, 1.5, hq) if gated else None
+    return oracle.LayerWeights(1.0 + 0.1 * rng.standard_normal(d), mk(hq * dh, d), mk(hkv * dh, d), mk(hkv * dh, d),
+                               mk(d, hq * dh), 1.0 + 0.1 * rng.standard_normal(d), mk(f, d), mk(f, d), mk(d, f),
+                               tau, gain)
+
+
+def _torch_layer(x, pos, w, hq, hkv, dh, eps, theta):
+    """The same layer from torch library routines in float64 (causal, no gate)."""
+    F = torch.nn.functional
+    t = lambda a: torch.from_numpy(np.asarray(a, dtype=np.float64))
+    X = t(x)
+    m, d = X.shape
+    xn = F.rms_norm(X, (d,), t(w.attn_norm), eps)
+    q = (xn @ t(w.wq).T).reshape(m, hq, dh)
+    k = (xn @ t(w.wk).T).reshape(m, hkv, dh)
+    v = (xn @ t(w.wv).T).reshape(m, hkv, dh)
+    half = dh // 2
+    inv = theta ** (-torch.arange(half, dtype=torch.float64) * 2 / dh)
+    ang = t(pos)[:, None] * inv[None, :]
+    cos = torch.cat([ang.cos(), ang.cos()], -1)[:, None, :]
+    sin = torch.cat([ang.sin(), ang.sin()], -1)[:, None, :]
+    rot = lambda z: torch.cat([-z[..., half:], z[..., :half]], -1)
+    q = q * cos + rot(q) * sin
+    k = k * cos + rot(k) * sin
+    rep = hq // hkv
+    a = F.scaled_dot_product_attention(q.permute(1, 0, 2), k.repeat_interleave(rep, 1).permute(1, 0, 2).contiguous(),
+                                       v.repeat_interleave(rep, 1).permute(1, 0, 2).contiguous(), is_causal=True)
+    h = X + a.permute(1, 0, 2).reshape(m, hq * dh) @ t(w.wo).T
+    hn = F.rms_norm(h, (d,), t(w.mlp_norm), eps)
+    y = h + (F.silu(hn @ t(w.w_gate).T) * (hn @ t(w.w_up).T)) @ t(w.w_down).T
+    return y.numpy(), hn.numpy()
+
+
+@pytest.mark.parametrize("hq,hkv", [(4, 2), (2, 2)])
+def test_layer_equals_library_composition(hq, hkv):
+    rng = np.random.default_rng(hq * 10 + hkv)
+    d, dh, f, m = 32, 8, 48, 23
+    w = _layer(rng, d, hq, hkv, dh, f)
+    x = rng.standard_normal((m, d))
+    pos = np.arange(m) + 3
+    y, hn = oracle.decoder_layer(x, pos, None, w, [0, m], hq, hkv, dh, 1e-6, 1e4, bf16=False)
+    yt, hnt = _torch_layer(x, pos, w, hq, hkv, dh, 1e-6, 1e4)
+    np.testing.assert_allclose(y, yt, rtol=1e-11, atol=1e-11)
+    np.testing.assert_allclose(hn, hnt, rtol=1e-11, atol=1e-11)
+
+
+def test_zero_output_projections_give_identity():
+    rng = np.random.default_rng(7)
+    d, hq, hkv, dh, f, m = 32, 2, 1, 16, 64, 9
+    w = _layer(rng, d, hq, hkv, dh, f)
+    w.wo = np.zeros_like(w.wo)
+    w.w_down = np.zeros_like(w.w_down)
+    x = oracle.round_bf16(rng.standard_normal((m, d)))
+    y, _ = oracle.decoder_layer(x, np.arange(m), None, w, [0, m], hq, hkv, dh, 1e-6, 1e6)
+    np.testing.assert_array_equal(y, x)
+
+
+def test_pruned_stack_without_pruning_is_the_full_stack():
+    rng = np.random.default_rng(11)
+    d, hq, hkv, dh, f, n_layers, gl = 32, 4, 2, 8, 64, 5, 1
+    layers = [_layer(rng, d, hq, hkv, dh, f, gated=False) for _ in range(n_layers)]
+    for li in range(gl + 1, n_layers):  # gated layers with g = 0, tau = 1
+        layers[li].gain = np.zeros(hq)
+        layers[li].tau = np.ones(hq)
+    gw1, gw2 = rng.standard_normal((16, d)) * 0.2, rng.standard_normal(16) * 0.3
+    x0 = oracle.round_bf16(rng.standard_normal((40, d)))
+    seg = ([0, 40], [0], [34], [34])  # K = whole document
+    y, idx, offs, s = oracle.pruned_stack(x0, layers, gl, gw1, gw2, *seg, hq, hkv, dh)
+    assert idx.tolist() == list(range(40))
+    x = x0
+    for li in range(n_layers):
+        x, _ = oracle.decoder_layer(x, np.arange(40), None, layers[li], [0, 40], hq, hkv, dh, 1e-6, 1e6)
+    np.testing.assert_array_equal(y, x)
+    # with pruning the kept rows are the selector's and their count is K + question
+    y2, idx2, offs2, _ = oracle.pruned_stack(x0, layers, gl, gw1, gw2, [0, 40], [0], [34], [10], hq, hkv, dh)
+    assert idx2.size == 16 and y2.shape == (16, d) and np.all(idx2[-6:] == np.arange(34, 40))
