@@ -206,6 +206,73 @@ int tg_gated_attention_prefill(const void* q, const void* k, const void* v, cons
                                const float* tau, const float* gain, const tg_segment* segs,
                                const tg_plan_info* info, int hq, int hkv, int head_dim, void* out, void* stream);
 
+/* ------------------------------------------------------------------------ */
+/* (5) Dense decoder-layer support (the layers below and above the gate)    */
+/* ------------------------------------------------------------------------ */
+
+/* The layers below the gate process every token; the layers above it process
+ * only the kept tokens ([reading] section 4.1: three-stage forward).  These
+ * entry points run a Qwen3-shaped pre-norm decoder layer so the whole pruned
+ * prefill can run on this library:
+ *   h = x + Wo . Attn(RoPE(Wqkv . RMSNorm(x)))      (token-gated above the gate)
+ *   y = h + Wdown . (silu(Wgate . RMSNorm(h)) * (Wup . RMSNorm(h)))
+ * bf16 tensors, fp32 accumulation; every tensor between two steps is bf16. */
+
+#define TG_GEMM_STORE 0    /* y = x . w^T */
+#define TG_GEMM_RESIDUAL 1 /* y = x . w^T + residual (residual may be y itself) */
+#define TG_GEMM_SWIGLU 2   /* w rows interleaved in groups of 8: gate 8j..8j+7, then up 8j..8j+7;
+                              y[:, c] = silu(gate_c) * up_c, n / 2 output columns */
+
+/* y [m, n] (or [m, n / 2] for SWIGLU) = x [m, k] . w [n, k]^T with the chosen
+ * epilogue; row strides ldx, ldw, ldr, ldy in elements.  All bf16, device.
+ * Supported: n % 128 == 0, k % 64 == 0, row strides % 8 == 0, 16-byte aligned
+ * pointers; otherwise TG_ERR_UNSUPPORTED.  m may be any size >= 0. */
+int tg_gemm_bf16(int epilogue, const void* x, int64_t ldx, const void* w, int64_t ldw, int64_t m, int n, int k,
+                 const void* residual, int64_t ldr, void* y, int64_t ldy, void* stream);
+
+/* y = x / sqrt(mean(x^2) + eps) * weight per row (fp32 math).  x, y bf16 [m, d]
+ * (row strides ldx, ldy), weight bf16 [d].  d % 8 == 0. */
+int tg_rmsnorm_bf16(const void* x, int64_t ldx, int64_t m, int d, const void* weight, float eps, void* y, int64_t ldy,
+                    void* stream);
+
+/* Splits a fused QKV row [q (hq heads) | k (hkv heads) | v (hkv heads)] x head_dim
+ * into token-major q [m, hq, head_dim], k, v [m, hkv, head_dim], applying the
+ * rotate-half rotary embedding to q and k at position positions[r] (int32,
+ * device): pair (i, i + head_dim/2) rotates by positions[r] * theta^(-2i/head_dim)
+ * (angle and its sine/cosine in fp64).  Above the gate the positions are the
+ * original token positions of the kept rows. */
+int tg_rope_split_bf16(const void* qkv, int64_t ldqkv, int64_t m, int hq, int hkv, int head_dim,
+                       const int32_t* positions, float theta, void* q, void* k, void* v, void* stream);
+
+/* Weights of one decoder layer (device pointers, bf16 unless noted). */
+typedef struct tg_layer_weights {
+  const void* attn_norm; /* [d] */
+  const void* wqkv;      /* [(hq + 2 hkv) head_dim, d] */
+  const void* wo;        /* [d, hq head_dim] */
+  const void* mlp_norm;  /* [d] */
+  const void* w_gate_up; /* [2 f, d], gate/up rows interleaved in groups of 8 (TG_GEMM_SWIGLU) */
+  const void* w_down;    /* [d, f] */
+  const float* tau;      /* fp32 [hq] temperature, or NULL (= 1) */
+  const float* gain;     /* fp32 [hq] gate gain, or NULL (no bias) */
+} tg_layer_weights;
+
+/* Device workspace (bytes) of tg_decoder_layer for m rows. */
+size_t tg_decoder_layer_workspace_bytes(int64_t m, int d, int hq, int hkv, int head_dim, int f);
+
+/* One decoder layer over the rows described by segs / info (kept rows of every
+ * prompt: kept_start, kept_len; below the gate plan with K >= document length
+ * so that every token is a kept row).  hidden bf16 [total_kept, d] is updated
+ * in place.  positions int32 [total_kept] (device): RoPE positions.
+ * key_score fp32 [total_kept] or NULL: the gate scores of the kept rows (the
+ * attention bias, with w->gain).  post_attn_norm bf16 [total_kept, d] or NULL:
+ * if given, receives RMSNorm(h) (the MLP input, the tensor the gate reads).
+ * Supported: d % 128 == 0, f % 64 == 0, head_dim 64 or 128, hq / hkv in
+ * {1, 2, 4}, (hq + 2 hkv) head_dim % 128 == 0, hq head_dim % 64 == 0. */
+int tg_decoder_layer(void* hidden, const int32_t* positions, const float* key_score, const tg_segment* segs,
+                     const tg_plan_info* info, int d, int hq, int hkv, int head_dim, int f, float rms_eps,
+                     float rope_theta, const tg_layer_weights* w, void* post_attn_norm, void* workspace,
+                     size_t workspace_bytes, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -193,4 +193,124 @@ int tg_gated_attention_prefill(const void* q, const void* k, const void* v, cons
                                                reinterpret_cast<hipStream_t>(stream)));
 }
 
+int tg_gemm_bf16(int epilogue, const void* x, int64_t ldx, const void* w, int64_t ldw, int64_t m, int n, int k,
+                 const void* residual, int64_t ldr, void* y, int64_t ldy, void* stream) {
+  if (epilogue < TG_GEMM_STORE || epilogue > TG_GEMM_SWIGLU || m < 0 || n <= 0 || k <= 0) return TG_ERR_INVALID_ARG;
+  if (m > 0 && (!x || !w || !y || (epilogue == TG_GEMM_RESIDUAL && !residual))) return TG_ERR_INVALID_ARG;
+  const int n_out = epilogue == TG_GEMM_SWIGLU ? n / 2 : n;
+  if (ldx < k || ldw < k || ldy < n_out || (epilogue == TG_GEMM_RESIDUAL && ldr < n)) return TG_ERR_INVALID_ARG;
+  if (n % 128 != 0 || k % 64 != 0 || ldx % 8 != 0 || ldw % 8 != 0 || ldy % 8 != 0 ||
+      (epilogue == TG_GEMM_RESIDUAL && ldr % 8 != 0))
+    return TG_ERR_UNSUPPORTED;
+  if (!aligned(x, 16) || !aligned(w, 16) || !aligned(y, 16) || (residual && !aligned(residual, 16)))
+    return TG_ERR_UNSUPPORTED;
+  if (m == 0) return TG_OK;
+  int st = check_device();
+  if (st != TG_OK) return st;
+  return hip_status(tg::launch_gemm(epilogue, x, ldx, w, ldw, m, n, k, residual, ldr, y, ldy,
+                                    reinterpret_cast<hipStream_t>(stream)));
+}
+
+int tg_rmsnorm_bf16(const void* x, int64_t ldx, int64_t m, int d, const void* weight, float eps, void* y, int64_t ldy,
+                    void* stream) {
+  if (m < 0 || d <= 0 || !(eps >= 0.0f)) return TG_ERR_INVALID_ARG;
+  if (m > 0 && (!x || !weight || !y)) return TG_ERR_INVALID_ARG;
+  if (ldx < d || ldy < d) return TG_ERR_INVALID_ARG;
+  if (d % 8 != 0 || ldx % 8 != 0 || ldy % 8 != 0 || !aligned(x, 16) || !aligned(y, 16) || !aligned(weight, 16))
+    return TG_ERR_UNSUPPORTED;
+  if (m == 0) return TG_OK;
+  int st = check_device();
+  if (st != TG_OK) return st;
+  return hip_status(tg::launch_rmsnorm(x, ldx, m, d, weight, eps, y, ldy, reinterpret_cast<hipStream_t>(stream)));
+}
+
+int tg_rope_split_bf16(const void* qkv, int64_t ldqkv, int64_t m, int hq, int hkv, int head_dim,
+                       const int32_t* positions, float theta, void* q, void* k, void* v, void* stream) {
+  if (m < 0 || hq <= 0 || hkv <= 0 || head_dim <= 0 || !(theta > 1.0f)) return TG_ERR_INVALID_ARG;
+  if (m > 0 && (!qkv || !positions || !q || !k || !v)) return TG_ERR_INVALID_ARG;
+  if (ldqkv < (int64_t)(hq + 2 * hkv) * head_dim) return TG_ERR_INVALID_ARG;
+  if (head_dim % 2 != 0 || head_dim > 256) return TG_ERR_UNSUPPORTED;
+  if (m == 0) return TG_OK;
+  int st = check_device();
+  if (st != TG_OK) return st;
+  return hip_status(tg::launch_rope_split(qkv, ldqkv, m, hq, hkv, head_dim, positions, theta, q, k, v,
+                                          reinterpret_cast<hipStream_t>(stream)));
+}
+
+namespace {
+struct LayerWs {
+  size_t xn, qkv, q, k, v, att, mid, total;
+};
+LayerWs layer_ws(int64_t m, int d, int hq, int hkv, int dh, int f) {
+  auto al = [](size_t b) { return (b + 255) / 256 * 256; };
+  LayerWs w{};
+  const size_t r = (size_t)(m > 0 ? m : 1);
+  w.xn = al(r * d * 2);
+  w.qkv = al(r * (size_t)(hq + 2 * hkv) * dh * 2);
+  w.q = al(r * (size_t)hq * dh * 2);
+  w.k = al(r * (size_t)hkv * dh * 2);
+  w.v = w.k;
+  w.att = w.q;
+  w.mid = al(r * (size_t)f * 2);
+  w.total = w.xn + w.qkv + w.q + w.k + w.v + w.att + w.mid;
+  return w;
+}
+}  // namespace
+
+size_t tg_decoder_layer_workspace_bytes(int64_t m, int d, int hq, int hkv, int head_dim, int f) {
+  if (m < 0 || d <= 0 || hq <= 0 || hkv <= 0 || head_dim <= 0 || f <= 0) return 0;
+  return layer_ws(m, d, hq, hkv, head_dim, f).total;
+}
+
+int tg_decoder_layer(void* hidden, const int32_t* positions, const float* key_score, const tg_segment* segs,
+                     const tg_plan_info* info, int d, int hq, int hkv, int head_dim, int f, float rms_eps,
+                     float rope_theta, const tg_layer_weights* w, void* post_attn_norm, void* workspace,
+                     size_t workspace_bytes, void* stream) {
+  int st = check_info(segs, info);
+  if (st != TG_OK) return st;
+  if (!w || d <= 0 || hq <= 0 || hkv <= 0 || head_dim <= 0 || f <= 0 || !(rms_eps >= 0.0f) || !(rope_theta > 1.0f))
+    return TG_ERR_INVALID_ARG;
+  const int64_t m = info->total_kept;
+  if (m > 0 && (!hidden || !positions || !w->attn_norm || !w->wqkv || !w->wo || !w->mlp_norm || !w->w_gate_up ||
+                !w->w_down))
+    return TG_ERR_INVALID_ARG;
+  const int nqkv = (hq + 2 * hkv) * head_dim;
+  if (hq % hkv != 0) return TG_ERR_UNSUPPORTED;
+  const int G = hq / hkv;
+  if (d % 128 != 0 || f % 64 != 0 || nqkv % 128 != 0 || (hq * head_dim) % 64 != 0 || (2 * f) % 128 != 0 ||
+      !(head_dim == 64 || head_dim == 128) || !(G == 1 || G == 2 || G == 4))
+    return TG_ERR_UNSUPPORTED;
+  const LayerWs L = layer_ws(m, d, hq, hkv, head_dim, f);
+  if (!workspace || !aligned(workspace, 256) || workspace_bytes < L.total) return TG_ERR_WORKSPACE;
+  if (!aligned(hidden, 16) || (post_attn_norm && !aligned(post_attn_norm, 16))) return TG_ERR_UNSUPPORTED;
+  if (m == 0) return TG_OK;
+  st = check_device();
+  if (st != TG_OK) return st;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  char* base = static_cast<char*>(workspace);
+  void* xn = base;
+  void* qkv = base + L.xn;
+  void* q = static_cast<char*>(qkv) + L.qkv;
+  void* k = static_cast<char*>(q) + L.q;
+  void* v = static_cast<char*>(k) + L.k;
+  void* att = static_cast<char*>(v) + L.v;
+  void* mid = static_cast<char*>(att) + L.att;
+  void* hn = post_attn_norm ? post_attn_norm : xn;
+  hipError_t e;
+#define TG_TRY(call)            \
+  e = (call);                   \
+  if (e != hipSuccess) return TG_ERR_HIP;
+  TG_TRY(tg::launch_rmsnorm(hidden, d, m, d, w->attn_norm, rms_eps, xn, d, s));
+  TG_TRY(tg::launch_gemm(0, xn, d, w->wqkv, d, m, nqkv, d, nullptr, 0, qkv, nqkv, s));
+  TG_TRY(tg::launch_rope_split(qkv, nqkv, m, hq, hkv, head_dim, positions, rope_theta, q, k, v, s));
+  TG_TRY(tg::launch_gated_attention(q, k, v, key_score, w->tau, w->gain, segs, *info, hq, hkv, head_dim, att, s));
+  TG_TRY(tg::launch_gemm(1, att, (int64_t)hq * head_dim, w->wo, (int64_t)hq * head_dim, m, d, hq * head_dim, hidden,
+                         d, hidden, d, s));
+  TG_TRY(tg::launch_rmsnorm(hidden, d, m, d, w->mlp_norm, rms_eps, hn, d, s));
+  TG_TRY(tg::launch_gemm(2, hn, d, w->w_gate_up, d, m, 2 * f, d, nullptr, 0, mid, f, s));
+  TG_TRY(tg::launch_gemm(1, mid, f, w->w_down, f, m, d, f, hidden, d, hidden, d, s));
+#undef TG_TRY
+  return TG_OK;
+}
+
 }  // extern "C"

@@ -101,4 +101,11 @@ hipError_t launch_gated_attention(const void* q, const void* k, const void* v, c
                                   const float* tau, const float* gain, const tg_segment* segs,
                                   const tg_plan_info& info, int hq, int hkv, int head_dim, void* out,
                                   hipStream_t stream);
+
+hipError_t launch_gemm(int epi, const void* x, int64_t ldx, const void* w, int64_t ldw, int64_t m, int n, int k,
+                       const void* res, int64_t ldr, void* y, int64_t ldy, hipStream_t stream);
+hipError_t launch_rmsnorm(const void* x, int64_t ldx, int64_t m, int d, const void* weight, float eps, void* y,
+                          int64_t ldy, hipStream_t stream);
+hipError_t launch_rope_split(const void* qkv, int64_t ldqkv, int64_t m, int hq, int hkv, int dh,
+                             const int32_t* positions, float theta, void* q, void* k, void* v, hipStream_t stream);
 }  // namespace tg

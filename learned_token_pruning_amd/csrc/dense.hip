@@ -1,0 +1,292 @@
+// Dense decoder-layer support kernels (gfx950): bf16 GEMM with fused
+// epilogues, RMSNorm and rotary embedding.  They run the layers below and
+// above the gate of a Qwen3-1.7B-shaped stack (RMSNorm -> QKV -> RoPE ->
+// attention -> O + residual -> RMSNorm -> SwiGLU MLP + residual); the gate,
+// selector, compaction and token-gated attention are the other kernels of
+// this library ("TokenGate 与 T2Quant ... 精读", section 4.1: the layers above
+// the gate run on the kept tokens only).
+//
+// GEMM: Y[m][n] = sum_k X[m][k] W[n][k] (X activations, W weights, both
+// k-contiguous), fp32 accumulation on v_mfma_f32_32x32x16_bf16.  The product
+// is computed transposed (W rows on the MFMA rows), so each lane owns one
+// activation row and 16 output columns per 32x32 tile: four runs of four
+// consecutive columns (8-byte stores), and with W's gate/up rows interleaved
+// in groups of 8 the SwiGLU pair of an output column sits in the same lane.
+// Workgroup tile 128 (n) x 256 (m), 4 waves of 64 x 128, k step 64, both
+// operands double-buffered in LDS (padded rows: conflict-free 16-byte reads),
+// the next k block prefetched into registers while the current one is
+// multiplied.
+#include "common.h"
+
+namespace tg {
+namespace {
+
+constexpr int kGT = 256;       // threads
+constexpr int kBN = 128;       // weight rows (output columns) per workgroup
+constexpr int kBM = 256;       // activation rows per workgroup
+constexpr int kBK = 64;        // k per stage
+constexpr int kLd = kBK + 8;   // LDS row stride (bf16)
+constexpr int kWN = 64;        // per-wave tile: 64 output columns
+constexpr int kWM = 128;       //                x 128 activation rows
+constexpr int kTN = kWN / 32;  // 2 MFMA tiles along n
+constexpr int kTM = kWM / 32;  // 4 MFMA tiles along m
+// loads of one stage: (128 + 256) rows x 128 bytes = 3072 16-byte units, 12 per thread
+constexpr int kLoadsW = kBN * kBK / 8 / kGT;  // 4
+constexpr int kLoadsX = kBM * kBK / 8 / kGT;  // 8
+
+enum Epi { kEpiStore = 0, kEpiResidual = 1, kEpiSwiGLU = 2 };
+
+__device__ __forceinline__ float silu(float v) { return v / (1.0f + __builtin_amdgcn_exp2f(-v * 1.4426950408889634f)); }
+
+template <int EPI>
+__global__ __launch_bounds__(kGT) void gemm_kernel(const uint16_t* __restrict__ x, int64_t ldx,
+                                                   const uint16_t* __restrict__ w, int64_t ldw, int64_t m, int n, int k,
+                                                   const uint16_t* __restrict__ res, int64_t ldr,
+                                                   uint16_t* __restrict__ y, int64_t ldy) {
+  __shared__ __attribute__((aligned(16))) uint16_t ws[2][kBN * kLd];
+  __shared__ __attribute__((aligned(16))) uint16_t xs[2][kBM * kLd];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int g = lane >> 5;
+  const int l32 = lane & 31;
+  const int n0 = blockIdx.x * kBN;
+  const int64_t m0 = (int64_t)blockIdx.y * kBM;
+  const int wn = (wave & 1) * kWN;  // wave's column offset inside the tile
+  const int wm = (wave >> 1) * kWM;  // wave's row offset inside the tile
+
+  // per-thread load slots: unit u = i * 256 + tid -> row u / 8, 16-byte column (u % 8) * 8
+  const uint16_t* wsrc[kLoadsW];
+  const uint16_t* xsrc[kLoadsX];
+#pragma unroll
+  for (int i = 0; i < kLoadsW; ++i) {
+    const int u = i * kGT + tid;
+    wsrc[i] = w + (int64_t)(n0 + u / 8) * ldw + (u % 8) * 8;
+  }
+#pragma unroll
+  for (int i = 0; i < kLoadsX; ++i) {
+    const int u = i * kGT + tid;
+    int64_t r = m0 + u / 8;
+    if (r >= m) r = m - 1;  // rows past the end re-read the last row; their results are not stored
+    xsrc[i] = x + r * ldx + (u % 8) * 8;
+  }
+  auto load_stage = [&](int kk, u32x4 (&rw)[kLoadsW], u32x4 (&rx)[kLoadsX]) {
+#pragma unroll
+    for (int i = 0; i < kLoadsW; ++i) rw[i] = *reinterpret_cast<const u32x4*>(wsrc[i] + kk);
+#pragma unroll
+    for (int i = 0; i < kLoadsX; ++i) rx[i] = *reinterpret_cast<const u32x4*>(xsrc[i] + kk);
+  };
+  auto store_stage = [&](int buf, const u32x4 (&rw)[kLoadsW], const u32x4 (&rx)[kLoadsX]) {
+#pragma unroll
+    for (int i = 0; i < kLoadsW; ++i) {
+      const int u = i * kGT + tid;
+      *reinterpret_cast<u32x4*>(&ws[buf][(u / 8) * kLd + (u % 8) * 8]) = rw[i];
+    }
+#pragma unroll
+    for (int i = 0; i < kLoadsX; ++i) {
+      const int u = i * kGT + tid;
+      *reinterpret_cast<u32x4*>(&xs[buf][(u / 8) * kLd + (u % 8) * 8]) = rx[i];
+    }
+  };
+
+  f32x16 acc[kTN][kTM];
+#pragma unroll
+  for (int a = 0; a < kTN; ++a)
+#pragma unroll
+    for (int b = 0; b < kTM; ++b) acc[a][b] = f32x16{};
+
+  u32x4 rw[kLoadsW], rx[kLoadsX];
+  load_stage(0, rw, rx);
+  store_stage(0, rw, rx);
+  __syncthreads();
+  const int nk = k / kBK;
+  for (int kb = 0; kb < nk; ++kb) {
+    const int buf = kb & 1;
+    const bool more = kb + 1 < nk;
+    if (more) load_stage((kb + 1) * kBK, rw, rx);
+    const uint16_t* wb = ws[buf];
+    const uint16_t* xb = xs[buf];
+#pragma unroll
+    for (int ks = 0; ks < kBK / 16; ++ks) {
+      u32x4 fa[kTN], fb[kTM];
+#pragma unroll
+      for (int a = 0; a < kTN; ++a)
+        fa[a] = *reinterpret_cast<const u32x4*>(wb + (wn + 32 * a + l32) * kLd + 16 * ks + 8 * g);
+#pragma unroll
+      for (int b = 0; b < kTM; ++b)
+        fb[b] = *reinterpret_cast<const u32x4*>(xb + (wm + 32 * b + l32) * kLd + 16 * ks + 8 * g);
+#pragma unroll
+      for (int a = 0; a < kTN; ++a)
+#pragma unroll
+        for (int b = 0; b < kTM; ++b) acc[a][b] = mfma32(fa[a], fb[b], acc[a][b]);
+      __builtin_amdgcn_sched_group_barrier(0x100, kTN + kTM, 0);  // the step's LDS reads first
+      __builtin_amdgcn_sched_group_barrier(0x008, kTN * kTM, 0);  // then its MFMAs
+    }
+    if (more) store_stage(buf ^ 1, rw, rx);
+    __syncthreads();
+  }
+
+  // Epilogue.  acc[a][b] register i: output column n0 + wn + 32 a + 8 (i / 4) + 4 g + (i % 4),
+  // activation row m0 + wm + 32 b + l32.
+  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+  typedef float f32x2 __attribute__((ext_vector_type(2)));
+#pragma unroll
+  for (int b = 0; b < kTM; ++b) {
+    const int64_t row = m0 + wm + 32 * b + l32;
+    if (row >= m) continue;
+#pragma unroll
+    for (int a = 0; a < kTN; ++a) {
+      if (EPI == kEpiSwiGLU) {
+        // weight rows come in groups of 8: gate j .. j+7 then up j .. j+7, so registers i and i + 4
+        // (i % 8 < 4) hold gate and up of the same intermediate column
+#pragma unroll
+        for (int q = 0; q < 2; ++q) {
+          const int c0 = (n0 + wn + 32 * a) / 2 + 8 * q + 4 * g;  // intermediate column of register 8 q
+          float r[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) r[e] = silu(acc[a][b][8 * q + e]) * acc[a][b][8 * q + 4 + e];
+          const uint32_t w0 = __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2{r[0], r[1]}), bf16x2));
+          const uint32_t w1 = __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2{r[2], r[3]}), bf16x2));
+          *reinterpret_cast<u32x2*>(y + row * ldy + c0) = u32x2{w0, w1};
+        }
+      } else {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int col = n0 + wn + 32 * a + 8 * q + 4 * g;
+          float r[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) r[e] = acc[a][b][4 * q + e];
+          if (EPI == kEpiResidual) {
+            const u32x2 rv = *reinterpret_cast<const u32x2*>(res + row * ldr + col);
+            r[0] += bf16_lo(rv[0]);
+            r[1] += bf16_hi(rv[0]);
+            r[2] += bf16_lo(rv[1]);
+            r[3] += bf16_hi(rv[1]);
+          }
+          const uint32_t w0 = __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2{r[0], r[1]}), bf16x2));
+          const uint32_t w1 = __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2{r[2], r[3]}), bf16x2));
+          *reinterpret_cast<u32x2*>(y + row * ldy + col) = u32x2{w0, w1};
+        }
+      }
+    }
+  }
+}
+
+// RMSNorm of bf16 rows: y = x / sqrt(mean(x^2) + eps) * weight, fp32 math, one wave per row.
+__global__ __launch_bounds__(256) void rmsnorm_kernel(const uint16_t* __restrict__ x, int64_t ldx, int64_t m, int d,
+                                                      const uint16_t* __restrict__ weight, float eps,
+                                                      uint16_t* __restrict__ y, int64_t ldy) {
+  const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (row >= m) return;
+  const int lane = threadIdx.x & 63;
+  const uint16_t* xr = x + row * ldx;
+  float ss = 0.0f;
+  for (int c = lane * 8; c < d; c += 512) {
+    const u32x4 v = *reinterpret_cast<const u32x4*>(xr + c);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const float a = bf16_lo(v[j]), b = bf16_hi(v[j]);
+      ss += a * a + b * b;
+    }
+  }
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) ss += __shfl_xor(ss, o);
+  const float inv = 1.0f / __builtin_sqrtf(ss / (float)d + eps);
+  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+  typedef float f32x2 __attribute__((ext_vector_type(2)));
+  for (int c = lane * 8; c < d; c += 512) {
+    const u32x4 v = *reinterpret_cast<const u32x4*>(xr + c);
+    const u32x4 wv = *reinterpret_cast<const u32x4*>(weight + c);
+    u32x4 o;
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      o[j] = __builtin_bit_cast(uint32_t, __builtin_convertvector(
+                                               (f32x2{bf16_lo(v[j]) * inv * bf16_lo(wv[j]),
+                                                      bf16_hi(v[j]) * inv * bf16_hi(wv[j])}),
+                                               bf16x2));
+    *reinterpret_cast<u32x4*>(y + row * ldy + c) = o;
+  }
+}
+
+// Rotary embedding (rotate-half form) of the Q and K heads of a fused QKV row,
+// written to separate token-major Q, K, V arrays.  Position p of row r is
+// positions[r]; frequency of pair i (i < D/2) is theta^(-2 i / D); the angle
+// is computed in fp32 from the integer position.  One wave per (row, head).
+__global__ __launch_bounds__(256) void rope_split_kernel(const uint16_t* __restrict__ qkv, int64_t ldqkv, int64_t m,
+                                                         int hq, int hkv, int dh, const int32_t* __restrict__ positions,
+                                                         float log2_theta, uint16_t* __restrict__ q,
+                                                         uint16_t* __restrict__ k, uint16_t* __restrict__ v) {
+  const int heads = hq + 2 * hkv;
+  const int64_t item = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (item >= m * heads) return;
+  const int64_t row = item / heads;
+  const int h = (int)(item - row * heads);
+  const int lane = threadIdx.x & 63;
+  const uint16_t* src = qkv + row * ldqkv + (int64_t)h * dh;
+  uint16_t* dst;
+  if (h < hq)
+    dst = q + (row * hq + h) * dh;
+  else if (h < hq + hkv)
+    dst = k + (row * hkv + (h - hq)) * dh;
+  else
+    dst = v + (row * hkv + (h - hq - hkv)) * dh;
+  const int half = dh / 2;
+  if (h >= hq + hkv) {  // V: plain copy
+    for (int c = lane; c < dh; c += 64) dst[c] = src[c];
+    return;
+  }
+  const double p = (double)positions[row];
+  for (int i = lane; i < half; i += 64) {
+    // angle in fp64: at positions up to 2^17 an fp32 angle would carry errors of ~1e-2 rad
+    const double ang = p * exp2(-(double)log2_theta * (2.0 * (double)i / (double)dh));
+    double sd, cd;
+    sincos(ang, &sd, &cd);
+    const float s = (float)sd, c = (float)cd;
+    const float x1 = bf16_lo((uint32_t)src[i]), x2 = bf16_lo((uint32_t)src[i + half]);
+    dst[i] = (uint16_t)f32_to_bf16(x1 * c - x2 * s);
+    dst[i + half] = (uint16_t)f32_to_bf16(x2 * c + x1 * s);
+  }
+}
+
+}  // namespace
+
+hipError_t launch_gemm(int epi, const void* x, int64_t ldx, const void* w, int64_t ldw, int64_t m, int n, int k,
+                       const void* res, int64_t ldr, void* y, int64_t ldy, hipStream_t stream) {
+  if (m == 0) return hipSuccess;
+  dim3 grid(n / kBN, (unsigned)((m + kBM - 1) / kBM));
+  const uint16_t* xp = reinterpret_cast<const uint16_t*>(x);
+  const uint16_t* wp = reinterpret_cast<const uint16_t*>(w);
+  const uint16_t* rp = reinterpret_cast<const uint16_t*>(res);
+  uint16_t* yp = reinterpret_cast<uint16_t*>(y);
+  if (epi == kEpiStore)
+    hipLaunchKernelGGL(gemm_kernel<kEpiStore>, grid, dim3(kGT), 0, stream, xp, ldx, wp, ldw, m, n, k, rp, ldr, yp, ldy);
+  else if (epi == kEpiResidual)
+    hipLaunchKernelGGL(gemm_kernel<kEpiResidual>, grid, dim3(kGT), 0, stream, xp, ldx, wp, ldw, m, n, k, rp, ldr, yp,
+                       ldy);
+  else
+    hipLaunchKernelGGL(gemm_kernel<kEpiSwiGLU>, grid, dim3(kGT), 0, stream, xp, ldx, wp, ldw, m, n, k, rp, ldr, yp,
+                       ldy);
+  return hipGetLastError();
+}
+
+hipError_t launch_rmsnorm(const void* x, int64_t ldx, int64_t m, int d, const void* weight, float eps, void* y,
+                          int64_t ldy, hipStream_t stream) {
+  if (m == 0) return hipSuccess;
+  hipLaunchKernelGGL(rmsnorm_kernel, dim3((unsigned)((m + 3) / 4)), dim3(256), 0, stream,
+                     reinterpret_cast<const uint16_t*>(x), ldx, m, d, reinterpret_cast<const uint16_t*>(weight), eps,
+                     reinterpret_cast<uint16_t*>(y), ldy);
+  return hipGetLastError();
+}
+
+hipError_t launch_rope_split(const void* qkv, int64_t ldqkv, int64_t m, int hq, int hkv, int dh,
+                             const int32_t* positions, float theta, void* q, void* k, void* v, hipStream_t stream) {
+  if (m == 0) return hipSuccess;
+  const int64_t items = m * (hq + 2 * hkv);
+  hipLaunchKernelGGL(rope_split_kernel, dim3((unsigned)((items + 3) / 4)), dim3(256), 0, stream,
+                     reinterpret_cast<const uint16_t*>(qkv), ldqkv, m, hq, hkv, dh, positions, log2f(theta),
+                     reinterpret_cast<uint16_t*>(q), reinterpret_cast<uint16_t*>(k), reinterpret_cast<uint16_t*>(v));
+  return hipGetLastError();
+}
+
+}  // namespace tg
