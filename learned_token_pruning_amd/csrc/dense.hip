@@ -215,7 +215,7 @@ __global__ __launch_bounds__(256) void rmsnorm_kernel(const uint16_t* __restrict
 // is computed in fp32 from the integer position.  One wave per (row, head).
 __global__ __launch_bounds__(256) void rope_split_kernel(const uint16_t* __restrict__ qkv, int64_t ldqkv, int64_t m,
                                                          int hq, int hkv, int dh, const int32_t* __restrict__ positions,
-                                                         float log2_theta, uint16_t* __restrict__ q,
+                                                         double log2_theta, uint16_t* __restrict__ q,
                                                          uint16_t* __restrict__ k, uint16_t* __restrict__ v) {
   const int heads = hq + 2 * hkv;
   const int64_t item = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
@@ -238,8 +238,9 @@ __global__ __launch_bounds__(256) void rope_split_kernel(const uint16_t* __restr
   }
   const double p = (double)positions[row];
   for (int i = lane; i < half; i += 64) {
-    // angle in fp64: at positions up to 2^17 an fp32 angle would carry errors of ~1e-2 rad
-    const double ang = p * exp2(-(double)log2_theta * (2.0 * (double)i / (double)dh));
+    // angle in fp64 (log2 theta too): at positions up to 2^17 an fp32 angle, or an fp32 log2 theta, carries
+    // errors of 1e-3 .. 1e-2 rad
+    const double ang = p * exp2(-log2_theta * (2.0 * (double)i / (double)dh));
     double sd, cd;
     sincos(ang, &sd, &cd);
     const float s = (float)sd, c = (float)cd;
@@ -284,7 +285,7 @@ hipError_t launch_rope_split(const void* qkv, int64_t ldqkv, int64_t m, int hq, 
   if (m == 0) return hipSuccess;
   const int64_t items = m * (hq + 2 * hkv);
   hipLaunchKernelGGL(rope_split_kernel, dim3((unsigned)((items + 3) / 4)), dim3(256), 0, stream,
-                     reinterpret_cast<const uint16_t*>(qkv), ldqkv, m, hq, hkv, dh, positions, log2f(theta),
+                     reinterpret_cast<const uint16_t*>(qkv), ldqkv, m, hq, hkv, dh, positions, log2((double)theta),
                      reinterpret_cast<uint16_t*>(q), reinterpret_cast<uint16_t*>(k), reinterpret_cast<uint16_t*>(v));
   return hipGetLastError();
 }

@@ -1,0 +1,121 @@
+"""Pruned-prefill decoder stack on the HIP library.
+
+Layers 0 .. gate_layer run over every token; the gate scores the documents
+from gate_layer's normalised post-attention residual; the top-K selector and
+the compaction keep the best document rows plus every non-document row; the
+remaining layers run only on the kept rows, with token-gated attention and
+rotary embedding at the original positions ("TokenGate 与 T2Quant ... 精读",
+section 4.1, three-stage forward).  Every step is a libtokengate call; this
+module only sequences them and owns the device buffers.
+"""
+from __future__ import annotations
+
+import ctypes
+from dataclasses import dataclass, field
+from typing import List, Optional
+
+import numpy as np
+import torch
+
+from . import tokengate as tg
+
+
+def interleave_gate_up(w_gate: torch.Tensor, w_up: torch.Tensor) -> torch.Tensor:
+    """[f, d] gate and up rows -> [2f, d] in groups of 8 (gate 8j..8j+7, up 8j..8j+7), the SwiGLU GEMM layout."""
+    f, d = w_gate.shape
+    return torch.stack([w_gate.reshape(f // 8, 8, d), w_up.reshape(f // 8, 8, d)], dim=1).reshape(2 * f, d).contiguous()
+
+
+@dataclass
+class DeviceLayer:
+    attn_norm: torch.Tensor
+    wqkv: torch.Tensor
+    wo: torch.Tensor
+    mlp_norm: torch.Tensor
+    w_gate_up: torch.Tensor
+    w_down: torch.Tensor
+    tau: Optional[torch.Tensor] = None
+    gain: Optional[torch.Tensor] = None
+    c_struct: tg.LayerWeights = field(init=False)
+
+    def __post_init__(self):
+        p = lambda t: None if t is None else t.data_ptr()
+        self.c_struct = tg.LayerWeights(p(self.attn_norm), p(self.wqkv), p(self.wo), p(self.mlp_norm),
+                                        p(self.w_gate_up), p(self.w_down), p(self.tau), p(self.gain))
+
+
+def random_layers(seed: int, n_layers: int, gated_from: int, d: int, hq: int, hkv: int, dh: int, f: int,
+                  device, std: float = 0.02) -> List[DeviceLayer]:
+    """Seeded random-init layers drawn on the device: weights N(0, std^2) in
+    bf16, RMSNorm weights 1, and for layers >= gated_from a temperature
+    U(0.8, 1.2) and gate gain U(0.5, 1.5) per head."""
+    gen = torch.Generator(device=device)
+    gen.manual_seed(seed)
+    out = []
+    nqkv = (hq + 2 * hkv) * dh
+
+    def normal(*shape):
+        return (torch.randn(shape, generator=gen, device=device, dtype=torch.float32) * std).to(torch.bfloat16)
+
+    for li in range(n_layers):
+        gated = li >= gated_from
+        tau = (0.8 + 0.4 * torch.rand(hq, generator=gen, device=device)) if gated else None
+        gain = (0.5 + torch.rand(hq, generator=gen, device=device)) if gated else None
+        out.append(DeviceLayer(torch.ones(d, dtype=torch.bfloat16, device=device), normal(nqkv, d),
+                               normal(d, hq * dh), torch.ones(d, dtype=torch.bfloat16, device=device),
+                               normal(2 * f, d), normal(d, f), tau, gain))
+    return out
+
+
+def positions_of(plan: tg.Plan) -> np.ndarray:
+    """Position of every token inside its prompt (restarting at 0 per prompt)."""
+    pos = np.zeros(plan.n_tokens, dtype=np.int32)
+    for s0, ln in plan.table[:, :2]:
+        pos[s0:s0 + ln] = np.arange(ln, dtype=np.int32)
+    return pos
+
+
+class PrunedStack:
+    def __init__(self, layers: List[DeviceLayer], gate_layer: int, gate_w1: torch.Tensor, gate_w2: torch.Tensor,
+                 d: int, hq: int, hkv: int, dh: int, f: int, eps: float = 1e-6, theta: float = 1e6,
+                 gate_eps: float = 1e-6):
+        self.layers, self.gate_layer = layers, gate_layer
+        self.gate_w1, self.gate_w2 = gate_w1, gate_w2
+        self.d, self.hq, self.hkv, self.dh, self.f = d, hq, hkv, dh, f
+        self.eps, self.theta, self.gate_eps = eps, theta, gate_eps
+        self._ws = None
+
+    def _workspace(self, rows, device):
+        need = max(tg.decoder_layer_workspace_bytes(rows, self.d, self.hq, self.hkv, self.dh, self.f), 256)
+        if self._ws is None or self._ws.numel() < need:
+            self._ws = torch.empty(need, dtype=torch.uint8, device=device)
+        return self._ws
+
+    def _layer(self, li, hidden, pos, score, plan, post=None):
+        tg.decoder_layer(hidden, pos, score, plan, self.layers[li].c_struct, self.d, self.hq, self.hkv, self.dh,
+                         self.f, self._workspace(plan.total_kept, hidden.device), self.eps, self.theta, post)
+
+    def forward(self, x: torch.Tensor, seg_start, doc_begin, doc_end, k_budget, prune: bool = True) -> dict:
+        """x bf16 [N, d] (not modified).  prune=False runs every layer over every token."""
+        dev = x.device
+        full = tg.plan_segments(seg_start, doc_begin, doc_end, [e - b for b, e in zip(doc_begin, doc_end)], dev)
+        pos = torch.from_numpy(positions_of(full)).to(dev)
+        hidden = x.clone()
+        gate_in = torch.empty_like(hidden)
+        for li in range(self.gate_layer + 1):
+            self._layer(li, hidden, pos, None, full, gate_in if li == self.gate_layer else None)
+        if not prune:
+            for li in range(self.gate_layer + 1, len(self.layers)):
+                self._layer(li, hidden, pos, None, full)
+            return {"hidden": hidden, "gate_in": gate_in}
+        plan = tg.plan_segments(seg_start, doc_begin, doc_end, k_budget, dev)
+        scores = tg.gate_score(gate_in, self.gate_w1, None, self.gate_w2, 0.0, plan, rms_eps=self.gate_eps)
+        kept = tg.select_topk(scores, plan)
+        m = plan.total_kept
+        hk = torch.empty((m, self.d), dtype=torch.bfloat16, device=dev)
+        pk = torch.empty(m, dtype=torch.int32, device=dev)
+        sk = torch.empty(m, dtype=torch.float32, device=dev)
+        tg.compact_kept(kept, [(hidden, hk), (pos, pk), (scores, sk)])
+        for li in range(self.gate_layer + 1, len(self.layers)):
+            self._layer(li, hk, pk, sk, plan)
+        return {"hidden": hk, "kept": kept, "scores": scores, "plan": plan, "gate_in": gate_in}

@@ -30,7 +30,10 @@ TG_OK = 0
 STATUS_NAMES = {0: "TG_OK", -1: "TG_ERR_INVALID_ARG", -2: "TG_ERR_UNSUPPORTED", -3: "TG_ERR_WORKSPACE",
                 -4: "TG_ERR_NO_DEVICE", -5: "TG_ERR_HIP"}
 EXPORTS = ("tg_status_string", "tg_abi_version", "tg_plan_segments", "tg_gate_workspace_bytes", "tg_gate_score",
-           "tg_select_workspace_bytes", "tg_select_topk", "tg_compact_kept", "tg_gated_attention_prefill")
+           "tg_select_workspace_bytes", "tg_select_topk", "tg_compact_kept", "tg_gated_attention_prefill",
+           "tg_gemm_bf16", "tg_rmsnorm_bf16", "tg_rope_split_bf16", "tg_decoder_layer_workspace_bytes",
+           "tg_decoder_layer")
+GEMM_STORE, GEMM_RESIDUAL, GEMM_SWIGLU = 0, 1, 2
 COMPACT_MAX_TENSORS = 8
 
 
@@ -49,6 +52,12 @@ class Segment(ctypes.Structure):
 class PlanInfo(ctypes.Structure):
     _fields_ = [("n_tokens", ctypes.c_int64), ("total_kept", ctypes.c_int64), ("n_seg", ctypes.c_int32),
                 ("max_seg_len", ctypes.c_int32), ("max_doc_len", ctypes.c_int32), ("max_kept_len", ctypes.c_int32)]
+
+
+class LayerWeights(ctypes.Structure):
+    _fields_ = [("attn_norm", ctypes.c_void_p), ("wqkv", ctypes.c_void_p), ("wo", ctypes.c_void_p),
+                ("mlp_norm", ctypes.c_void_p), ("w_gate_up", ctypes.c_void_p), ("w_down", ctypes.c_void_p),
+                ("tau", ctypes.c_void_p), ("gain", ctypes.c_void_p)]
 
 
 _vp = ctypes.c_void_p
@@ -77,6 +86,19 @@ _lib.tg_compact_kept.argtypes = [_vp, _i64, _i64, _i32, ctypes.POINTER(_vp), cty
 _lib.tg_gated_attention_prefill.restype = _i32
 _lib.tg_gated_attention_prefill.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, ctypes.POINTER(PlanInfo), _i32, _i32,
                                             _i32, _vp, _vp]
+
+
+_lib.tg_gemm_bf16.restype = _i32
+_lib.tg_gemm_bf16.argtypes = [_i32, _vp, _i64, _vp, _i64, _i64, _i32, _i32, _vp, _i64, _vp, _i64, _vp]
+_lib.tg_rmsnorm_bf16.restype = _i32
+_lib.tg_rmsnorm_bf16.argtypes = [_vp, _i64, _i64, _i32, _vp, _f32, _vp, _i64, _vp]
+_lib.tg_rope_split_bf16.restype = _i32
+_lib.tg_rope_split_bf16.argtypes = [_vp, _i64, _i64, _i32, _i32, _i32, _vp, _f32, _vp, _vp, _vp, _vp]
+_lib.tg_decoder_layer_workspace_bytes.restype = _sz
+_lib.tg_decoder_layer_workspace_bytes.argtypes = [_i64, _i32, _i32, _i32, _i32, _i32]
+_lib.tg_decoder_layer.restype = _i32
+_lib.tg_decoder_layer.argtypes = [_vp, _vp, _vp, _vp, ctypes.POINTER(PlanInfo), _i32, _i32, _i32, _i32, _i32, _f32,
+                                  _f32, ctypes.POINTER(LayerWeights), _vp, _vp, _sz, _vp]
 
 
 def library_path() -> str:
@@ -247,3 +269,63 @@ def gated_attention_prefill(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, k
                                          _stream(stream))
     _check(st, "tg_gated_attention_prefill")
     return out
+
+
+# ----------------------------------------------------------------------------
+# Dense decoder-layer support
+# ----------------------------------------------------------------------------
+
+
+def gemm_bf16(x: torch.Tensor, w: torch.Tensor, epilogue: int = GEMM_STORE, residual: Optional[torch.Tensor] = None,
+              out: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """tg_gemm_bf16: out = x . w^T (+ residual | SwiGLU).  x [m, k], w [n, k] bf16 (row strides honoured)."""
+    m, k = x.shape
+    n = w.shape[0]
+    n_out = n // 2 if epilogue == GEMM_SWIGLU else n
+    if out is None:
+        out = torch.empty((m, n_out), dtype=torch.bfloat16, device=x.device)
+    st = _lib.tg_gemm_bf16(epilogue, _ptr(x), x.stride(0), _ptr(w), w.stride(0), m, n, k, _ptr(residual),
+                           residual.stride(0) if residual is not None else 0, _ptr(out), out.stride(0),
+                           _stream(stream))
+    _check(st, "tg_gemm_bf16")
+    return out
+
+
+def rmsnorm_bf16(x: torch.Tensor, weight: torch.Tensor, eps: float = 1e-6, out: Optional[torch.Tensor] = None,
+                 stream=None) -> torch.Tensor:
+    m, d = x.shape
+    if out is None:
+        out = torch.empty_like(x)
+    st = _lib.tg_rmsnorm_bf16(_ptr(x), x.stride(0), m, d, _ptr(weight), float(eps), _ptr(out), out.stride(0),
+                              _stream(stream))
+    _check(st, "tg_rmsnorm_bf16")
+    return out
+
+
+def rope_split_bf16(qkv: torch.Tensor, hq: int, hkv: int, head_dim: int, positions: torch.Tensor,
+                    theta: float = 1e6, stream=None):
+    m = qkv.shape[0]
+    q = torch.empty((m, hq, head_dim), dtype=torch.bfloat16, device=qkv.device)
+    k = torch.empty((m, hkv, head_dim), dtype=torch.bfloat16, device=qkv.device)
+    v = torch.empty_like(k)
+    st = _lib.tg_rope_split_bf16(_ptr(qkv), qkv.stride(0), m, hq, hkv, head_dim, _ptr(positions), float(theta),
+                                 _ptr(q), _ptr(k), _ptr(v), _stream(stream))
+    _check(st, "tg_rope_split_bf16")
+    return q, k, v
+
+
+def decoder_layer_workspace_bytes(m: int, d: int, hq: int, hkv: int, head_dim: int, f: int) -> int:
+    return int(_lib.tg_decoder_layer_workspace_bytes(m, d, hq, hkv, head_dim, f))
+
+
+def decoder_layer(hidden: torch.Tensor, positions: torch.Tensor, key_score: Optional[torch.Tensor], plan: Plan,
+                  weights: LayerWeights, d: int, hq: int, hkv: int, head_dim: int, f: int,
+                  workspace: torch.Tensor, rms_eps: float = 1e-6, rope_theta: float = 1e6,
+                  post_attn_norm: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """tg_decoder_layer: hidden [total_kept, d] bf16 updated in place."""
+    st = _lib.tg_decoder_layer(_ptr(hidden), _ptr(positions), _ptr(key_score), _dev_table(plan),
+                               ctypes.byref(plan.info), d, hq, hkv, head_dim, f, float(rms_eps), float(rope_theta),
+                               ctypes.byref(weights), _ptr(post_attn_norm), _ptr(workspace),
+                               workspace.numel() * workspace.element_size(), _stream(stream))
+    _check(st, "tg_decoder_layer")
+    return hidden

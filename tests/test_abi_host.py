@@ -18,7 +18,7 @@ FAKE = ctypes.c_void_p(0x10000)  # never dereferenced: every call below fails va
 def declared_functions():
     text = open(os.path.join(ROOT, "include", "tokengate.h")).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(tg_[a-z_]+)\s*\(", text)))
+    return sorted(set(re.findall(r"\b(tg_[a-z0-9_]+)\s*\(", text)))
 
 
 def test_exports_every_declared_function():
@@ -145,3 +145,32 @@ def test_valid_calls_report_no_device_without_gpu():
     assert L.tg_gate_score(FAKE, 2048, 2048, FAKE, None, FAKE, 0.0, 256, FAKE, info, 1e-6, FAKE, FAKE, ws, None) == -4
     assert L.tg_select_topk(FAKE, FAKE, info, FAKE, FAKE, tg.select_workspace_bytes(p), None) == -4
     assert L.tg_gated_attention_prefill(FAKE, FAKE, FAKE, None, None, None, FAKE, info, 16, 8, 128, FAKE, None) == -4
+
+
+def test_dense_validation():
+    V = ctypes.c_void_p
+    g = L.tg_gemm_bf16
+    # bad epilogue, n not a multiple of 128, k not a multiple of 64, ld too small, missing residual
+    assert g(3, FAKE, 256, FAKE, 256, 10, 128, 256, None, 0, FAKE, 128, None) == -1
+    assert g(0, FAKE, 256, FAKE, 256, 10, 100, 256, None, 0, FAKE, 128, None) == -2
+    assert g(0, FAKE, 256, FAKE, 256, 10, 128, 200, None, 0, FAKE, 128, None) == -2
+    assert g(0, FAKE, 100, FAKE, 256, 10, 128, 256, None, 0, FAKE, 128, None) == -1
+    assert g(1, FAKE, 256, FAKE, 256, 10, 128, 256, None, 0, FAKE, 128, None) == -1
+    assert g(0, None, 256, None, 256, 0, 128, 256, None, 0, None, 128, None) == 0  # empty
+    r = L.tg_rmsnorm_bf16
+    assert r(FAKE, 256, 10, 250, FAKE, 1e-6, FAKE, 256, None) == -2
+    assert r(FAKE, 256, 10, 256, FAKE, -1.0, FAKE, 256, None) == -1
+    rp = L.tg_rope_split_bf16
+    assert rp(FAKE, 4096, 10, 16, 8, 128, FAKE, 0.5, FAKE, FAKE, FAKE, None) == -1  # theta <= 1
+    assert rp(FAKE, 1000, 10, 16, 8, 128, FAKE, 1e6, FAKE, FAKE, FAKE, None) == -1  # ld too small
+    p = _plan()
+    info = ctypes.byref(p.info)
+    w = tg.LayerWeights(0x10000, 0x10000, 0x10000, 0x10000, 0x10000, 0x10000, None, None)
+    ws = tg.decoder_layer_workspace_bytes(p.total_kept, 2048, 16, 8, 128, 6144)
+    assert ws > 0
+    dl = L.tg_decoder_layer
+    assert dl(FAKE, FAKE, None, FAKE, info, 2048, 16, 8, 96, 6144, 1e-6, 1e6, ctypes.byref(w), None, FAKE, ws,
+              None) == -2  # head_dim
+    assert dl(FAKE, FAKE, None, FAKE, info, 2048, 16, 8, 128, 6144, 1e-6, 1e6, ctypes.byref(w), None, FAKE, ws - 1,
+              None) == -3
+    assert dl(FAKE, FAKE, None, FAKE, info, 2048, 16, 8, 128, 6144, 1e-6, 1e6, None, None, FAKE, ws, None) == -1
