@@ -5,9 +5,13 @@ Q, K, V, scores) -> token-gated attention over the kept rows, on one batch of
 synthetic input already resident in HBM.  The headline workload is the
 16K-token gated layer (16320 document + 64 question tokens, d = 2048, gate
 MLP 2048 -> 256 -> 1, K = 2048, 16 query / 8 key-value heads, head_dim 128).
-The 128K-token layer at K = 2048 is measured too and reported beside it.
+The 128K-token layer at K = 2048 is measured too and reported beside it, and
+so is the 28-layer pruned-stack prefill over a 65536-token prompt (13 full
+layers, the gate, K = 4096, 15 token-gated layers) next to the same stack
+unpruned.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+                    [--no-long | --only-long] [--no-stack | --only-stack]
 
 Prints one JSON line.  Per-kernel times come from HIP events recorded on the
 stream the kernels run on, inside the timed region.
@@ -196,6 +200,90 @@ def stage_rooflines(pipe, st, csrc):
     }
 
 
+STACK = dict(n=65536, n_q=64, k=4096, layers=28, gate_layer=12, d=2048, hq=16, hkv=8, dh=128, f=6144, h_gate=256)
+
+
+def stack_flops(rows_per_segment, c):
+    """Model flops of one decoder layer over prompts of the given lengths:
+    the four projections (2 flop per multiply-add) plus causal attention
+    (QK and PV over the causal pairs only)."""
+    d, hq, hkv, dh, f = c["d"], c["hq"], c["hkv"], c["dh"], c["f"]
+    m = sum(rows_per_segment)
+    proj = 2 * m * (d * (hq + 2 * hkv) * dh + hq * dh * d + d * 2 * f + f * d)
+    attn = sum(4 * hq * dh * r * (r + 1) // 2 for r in rows_per_segment)
+    return proj, attn
+
+
+def time_stack(torch, tg, steps, warmup):
+    """28-layer random-init stack over a 65536-token prompt: 13 full layers,
+    the gate on layer 13's normalised residual, top-4096 select, compaction,
+    15 token-gated layers over 4096 + 64 kept rows; and the same stack with no
+    pruning.  Returns the record of both."""
+    from learned_token_pruning_amd.stack import PrunedStack, random_layers
+    c = STACK
+    dev = torch.device("cuda")
+    n, nq = c["n"], c["n_q"]
+    layers = random_layers(5, c["layers"], c["gate_layer"] + 1, c["d"], c["hq"], c["hkv"], c["dh"], c["f"], dev)
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(50)
+    w1 = (torch.randn(c["h_gate"], c["d"], generator=gen, device=dev) * 0.02).to(torch.bfloat16)
+    w2 = torch.randn(c["h_gate"], generator=gen, device=dev) * 0.02
+    x = torch.randn(n, c["d"], generator=gen, device=dev).to(torch.bfloat16)
+    st = PrunedStack(layers, c["gate_layer"], w1, w2, c["d"], c["hq"], c["hkv"], c["dh"], c["f"])
+    plan = st.plan([0, n], [0], [n - nq], [c["k"]], dev)
+    stream = torch.cuda.current_stream()
+    rec = {}
+    for prune in (True, False):
+        for _ in range(warmup):
+            st.forward(x, plan=plan, prune=prune)
+        torch.cuda.synchronize()
+        torch.cuda.reset_peak_memory_stats()
+        phases = []
+        t0 = time.perf_counter()
+        for _ in range(steps):
+            ev = {"start": torch.cuda.Event(enable_timing=True)}
+            ev["start"].record(stream)
+
+            def mark(name, ev=ev):
+                ev[name] = torch.cuda.Event(enable_timing=True)
+                ev[name].record(stream)
+
+            st.forward(x, plan=plan, prune=prune, mark=mark)
+            phases.append(ev)
+        torch.cuda.synchronize()
+        wall = (time.perf_counter() - t0) / steps
+        names = ["lower", "prune", "upper"] if prune else ["lower", "upper"]
+        ph = {}
+        prev = "start"
+        for nm in names:
+            ph[nm] = float(np.mean([e[prev].elapsed_time(e[nm]) for e in phases]))
+            prev = nm
+        m_up = plan.pruned.total_kept if prune else n
+        lo = stack_flops([n], c)
+        up = stack_flops([m_up], c)
+        n_lo, n_up = c["gate_layer"] + 1, c["layers"] - c["gate_layer"] - 1
+        flops = n_lo * sum(lo) + n_up * sum(up)
+        attn_flops = n_lo * lo[1] + n_up * up[1]
+        key = "pruned" if prune else "full"
+        rec[key] = {"ms": wall * 1e3, "tokens_per_s": n / wall, "phases_ms": {k: round(v, 3) for k, v in ph.items()},
+                    "model_tflops": flops / wall / 1e12, "model_frac_mfma_peak": flops / wall / 1e12 /
+                    MFMA_BF16_PEAK_TFLOPS, "attention_share_of_flops": attn_flops / flops,
+                    "peak_device_mem_gib": torch.cuda.max_memory_allocated() / 2 ** 30}
+        log(f"stack {key}: {wall * 1e3:.1f} ms/step", ph)
+    rec["prefill_speedup"] = rec["full"]["ms"] / rec["pruned"]["ms"]
+    rec["workload"] = (f"pruned-stack prefill, 28 random-init layers (d 2048, 16 Q / 8 KV heads, head_dim 128, "
+                       f"SwiGLU 6144), N={n} ({n - nq} doc + {nq} question), 13 full layers, gate after layer 13, "
+                       f"K={c['k']} (M={plan.pruned.total_kept}), 15 token-gated layers; and the same stack unpruned")
+    rec["steps"], rec["warmup"] = steps, warmup
+    kv_row = 2 * c["hkv"] * c["dh"] * 2
+    rec["kv_cache_gib_if_kept"] = {
+        "pruned": ((c["gate_layer"] + 1) * n + (c["layers"] - c["gate_layer"] - 1) * plan.pruned.total_kept) * kv_row
+        / 2 ** 30, "full": c["layers"] * n * kv_row / 2 ** 30}
+    del st, layers, x
+    torch.cuda.empty_cache()
+    return rec
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -204,6 +292,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-long", action="store_true", help="skip the 128K-token layer")
     ap.add_argument("--only-long", action="store_true", help="time only the 128K-token layer (profiling)")
+    ap.add_argument("--no-stack", action="store_true", help="skip the 28-layer pruned-stack prefill")
+    ap.add_argument("--only-stack", action="store_true", help="time only the 28-layer pruned-stack prefill")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="also run one plain 256 MiB device copy (reference for rocprofv3 FETCH_SIZE / WRITE_SIZE)")
     args = ap.parse_args()
@@ -233,6 +323,8 @@ def main():
 
     result = None
     l16 = None
+    if args.only_stack:
+        args.only_long, args.no_long = True, True
     if not args.only_long:
         log("generating the 16K-token workload")
         l16 = W.workload(2)
@@ -293,6 +385,16 @@ def main():
                       "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
                       "data": "synthetic", "config": {"workload": long_rec["workload"]}}
         result["n131072_k2048"] = long_rec
+
+    if not args.no_stack:
+        log("timing the 28-layer pruned stack at N=65536")
+        stack = time_stack(torch, tg, max(2, args.steps // 50), 1)
+        if result is None:
+            result = {"metric": METRIC, "value": stack["pruned"]["tokens_per_s"], "unit": "tokens/s", "n_gpus": 1,
+                      "steps": stack["steps"], "warmup": 1, "ms_per_step": stack["pruned"]["ms"],
+                      "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+                      "data": "synthetic", "config": {"workload": stack["workload"]}}
+        result["stack_n65536_k4096"] = stack
 
     if not args.no_cpu_baseline and l16 is not None:
         log("timing the CPU oracle on the 16K workload")

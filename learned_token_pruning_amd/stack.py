@@ -75,6 +75,16 @@ def positions_of(plan: tg.Plan) -> np.ndarray:
     return pos
 
 
+@dataclass
+class StackPlan:
+    """Host-built segment tables of one batch: `full` covers every token (each
+    document kept whole), `pruned` applies the budgets; `pos` holds the
+    in-prompt positions on the device."""
+    full: tg.Plan
+    pruned: tg.Plan
+    pos: torch.Tensor
+
+
 class PrunedStack:
     def __init__(self, layers: List[DeviceLayer], gate_layer: int, gate_w1: torch.Tensor, gate_w2: torch.Tensor,
                  d: int, hq: int, hkv: int, dh: int, f: int, eps: float = 1e-6, theta: float = 1e6,
@@ -84,6 +94,11 @@ class PrunedStack:
         self.d, self.hq, self.hkv, self.dh, self.f = d, hq, hkv, dh, f
         self.eps, self.theta, self.gate_eps = eps, theta, gate_eps
         self._ws = None
+
+    def plan(self, seg_start, doc_begin, doc_end, k_budget, device) -> StackPlan:
+        full = tg.plan_segments(seg_start, doc_begin, doc_end, [e - b for b, e in zip(doc_begin, doc_end)], device)
+        pruned = tg.plan_segments(seg_start, doc_begin, doc_end, k_budget, device)
+        return StackPlan(full, pruned, torch.from_numpy(positions_of(full)).to(device))
 
     def _workspace(self, rows, device):
         need = max(tg.decoder_layer_workspace_bytes(rows, self.d, self.hq, self.hkv, self.dh, self.f), 256)
@@ -95,27 +110,40 @@ class PrunedStack:
         tg.decoder_layer(hidden, pos, score, plan, self.layers[li].c_struct, self.d, self.hq, self.hkv, self.dh,
                          self.f, self._workspace(plan.total_kept, hidden.device), self.eps, self.theta, post)
 
-    def forward(self, x: torch.Tensor, seg_start, doc_begin, doc_end, k_budget, prune: bool = True) -> dict:
-        """x bf16 [N, d] (not modified).  prune=False runs every layer over every token."""
+    def forward(self, x: torch.Tensor, seg_start=None, doc_begin=None, doc_end=None, k_budget=None,
+                prune: bool = True, plan: Optional[StackPlan] = None, mark=None) -> dict:
+        """x bf16 [N, d] (not modified).  prune=False runs every layer over
+        every token.  `plan` (from plan()) saves rebuilding the tables;
+        `mark(name)`, if given, is called on the host after the launches of
+        each phase ("lower", "prune", "upper") have been issued."""
         dev = x.device
-        full = tg.plan_segments(seg_start, doc_begin, doc_end, [e - b for b, e in zip(doc_begin, doc_end)], dev)
-        pos = torch.from_numpy(positions_of(full)).to(dev)
+        if plan is None:
+            plan = self.plan(seg_start, doc_begin, doc_end, k_budget, dev)
+        full, pos = plan.full, plan.pos
         hidden = x.clone()
         gate_in = torch.empty_like(hidden)
         for li in range(self.gate_layer + 1):
             self._layer(li, hidden, pos, None, full, gate_in if li == self.gate_layer else None)
+        if mark:
+            mark("lower")
         if not prune:
             for li in range(self.gate_layer + 1, len(self.layers)):
                 self._layer(li, hidden, pos, None, full)
+            if mark:
+                mark("upper")
             return {"hidden": hidden, "gate_in": gate_in}
-        plan = tg.plan_segments(seg_start, doc_begin, doc_end, k_budget, dev)
-        scores = tg.gate_score(gate_in, self.gate_w1, None, self.gate_w2, 0.0, plan, rms_eps=self.gate_eps)
-        kept = tg.select_topk(scores, plan)
-        m = plan.total_kept
+        pp = plan.pruned
+        scores = tg.gate_score(gate_in, self.gate_w1, None, self.gate_w2, 0.0, pp, rms_eps=self.gate_eps)
+        kept = tg.select_topk(scores, pp)
+        m = pp.total_kept
         hk = torch.empty((m, self.d), dtype=torch.bfloat16, device=dev)
         pk = torch.empty(m, dtype=torch.int32, device=dev)
         sk = torch.empty(m, dtype=torch.float32, device=dev)
         tg.compact_kept(kept, [(hidden, hk), (pos, pk), (scores, sk)])
+        if mark:
+            mark("prune")
         for li in range(self.gate_layer + 1, len(self.layers)):
-            self._layer(li, hk, pk, sk, plan)
-        return {"hidden": hk, "kept": kept, "scores": scores, "plan": plan, "gate_in": gate_in}
+            self._layer(li, hk, pk, sk, pp)
+        if mark:
+            mark("upper")
+        return {"hidden": hk, "kept": kept, "scores": scores, "plan": pp, "gate_in": gate_in}
