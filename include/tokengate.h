@@ -199,7 +199,10 @@ int tg_compact_kept(const int32_t* kept_idx, int64_t n_kept, int64_t n_src_rows,
  *   tau  fp32 [hq] (device) or NULL (= 1); gain fp32 [hq] (device) or NULL (no bias)
  *   segs (device) / info (host): rows of prompt i are [kept_start, kept_start + kept_len).
  *   out bf16 [total_kept, hq, head_dim] (device, out).
- * bf16 MFMA for q.k and p.v, fp32 softmax and accumulation.
+ * bf16 MFMA for q.k and p.v, fp32 softmax and accumulation; the softmax
+ * denominator sums the bf16-rounded probabilities that the p.v product uses.
+ * NaN anywhere in q, k, v, key_score, tau or gain gives unspecified output
+ * values (no error); +-inf scores act as ordinary logit biases.
  * Supported: head_dim in {64, 128}; hq % hkv == 0 with hq / hkv in {1, 2, 4};
  * all pointers 16-byte aligned; otherwise TG_ERR_UNSUPPORTED / INVALID_ARG. */
 int tg_gated_attention_prefill(const void* q, const void* k, const void* v, const float* key_score,

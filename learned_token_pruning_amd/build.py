@@ -29,6 +29,10 @@ HIPCC = os.environ.get("HIPCC", shutil.which("hipcc") or "/opt/rocm/bin/hipcc")
 DEVICE_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
 COMMON = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-I", INCLUDE, "-I", CSRC,
           "-Wall", "-Wno-unused-function"]
+# Per-source extras.  The attention kernel takes row maxima of MFMA results;
+# without NaN semantics fmaxf needs no canonicalising pass over its inputs
+# (NaN inputs to attention give unspecified outputs).
+FILE_FLAGS = {"gated_attention.hip": ["-fno-honor-nans"]}
 
 
 def _run(cmd):
@@ -47,7 +51,7 @@ def build(verbose: bool = False) -> str:
     for src in sources:
         obj = os.path.join(BUILD, os.path.basename(src) + ".o")
         objs.append(obj)
-        cmds.append([HIPCC, *COMMON, *DEVICE_FLAGS, "-c", src, "-o", obj])
+        cmds.append([HIPCC, *COMMON, *DEVICE_FLAGS, *FILE_FLAGS.get(os.path.basename(src), []), "-c", src, "-o", obj])
     workers = min(len(cmds), max(1, min(8, os.cpu_count() or 1)))
     with cf.ThreadPoolExecutor(workers) as ex:
         for out in ex.map(_run, cmds):

@@ -6,9 +6,19 @@
 //   z_rt = tau_h (q_r . k_t) / sqrt(D) + g_h s_t,   t <= r (kept rows, original order)
 //
 // Flash-style, one pass over the keys with an online softmax in the exp2
-// domain.  A workgroup (4 waves) owns one key/value head and a 128/G-row
-// query tile of all G query heads sharing it, so every K/V tile staged in LDS
-// serves G heads.  Each wave owns 32 query rows of one head.
+// domain.  A workgroup owns one key/value head and a 128/G-row query tile of
+// all G query heads sharing it, so every K/V tile staged in LDS serves G
+// heads.  Its 8 waves form two groups of 4 (one wave of each group per SIMD);
+// each wave owns 32 query rows of one head, group 0 takes the even 64-key
+// tiles and group 1 the odd ones, and the two are merged at the end.
+//
+// Ping-pong schedule.  Each wave alternates an MFMA phase (PV of its previous
+// tile, then QK of its next tile) and a softmax phase (VALU), and the two
+// groups are half a step apart, separated by workgroup barriers: while one
+// wave of a SIMD issues MFMAs the other runs its exp2s, so the matrix cores
+// and the VALU work at the same time.  All 512 threads stage the next K tile
+// (threads 0-255, with the scores) and the V tile due next (threads 256-511)
+// through registers during each half-step.
 //
 // MFMA mapping (v_mfma_f32_32x32x16_bf16).  Scores are computed transposed,
 // S^T = K . Q^T, so a lane owns one query column (l % 32) and 16 key rows per
@@ -20,178 +30,134 @@
 // V is therefore staged transposed in LDS; K row-major.  Both use padded rows
 // so that the 16- and 8-byte LDS reads are bank-conflict free.
 //
-// The gate bias g_h s_t is fused into the same FMA that applies the
-// temperature: x = S * (tau_h log2(e) / sqrt(D)) + (g_h log2(e)) s_t.
+// Logit arithmetic.  With c_h = |tau_h| log2(e) / sqrt(D) (floored at 1e-30;
+// a negative temperature flips the sign of Q, which is exact) the score
+// accumulators start from the key's bias divided by c_h, so the MFMA returns
+// a_rt = q.k + g_h log2(e) s_t / c_h and the exp2-domain logit is c_h a_rt:
+// the softmax needs one FMA and one exp2 per element.  The row sum is taken
+// over the bf16-rounded probabilities (the values the PV product uses).
 // Tiles are launched longest-first (the last query tile of a prompt first).
+#include <type_traits>
+
 #include "common.h"
 
 namespace tg {
 namespace {
 
-constexpr int kBN = 64;  // keys per tile
+constexpr int kBN = 64;        // keys per tile
 constexpr int kThreads = 512;  // two groups of 4 waves
 constexpr float kLog2e = 1.4426950408889634f;
 
 template <int D>
-struct AttnSmem {
-  static constexpr int kLd = D + 8;        // K row stride (bf16)
-  static constexpr int vLd = kBN + 4;      // V^T row stride (bf16)
-  uint16_t k[1][kBN * kLd];
-  uint16_t vt[1][D * vLd];
-  float s[4][kBN];  // gate bias of every key, pre-multiplied by g_h log2(e), one row per query head of the group
+struct alignas(16) AttnSmem {
+  static constexpr int kLd = D + 8;    // K row stride (bf16)
+  static constexpr int vLd = kBN + 4;  // V^T row stride (bf16)
+  uint16_t k[2][kBN * kLd];            // two stages (tile parity)
+  uint16_t vt[2][D * vLd];
+  float s[2][4][kBN];                  // [stage][head of the KV group][key]: bias / c_h
 };
 
-// Per-thread constant parts of the K/V/score tile loads (byte offsets).
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ uint32_t pack_bf16(float a, float b) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2{a, b}), bf16x2));
+}
+
+// Threads 0-255 stage K tiles (and the scores), threads 256-511 V tiles.
 template <int D>
-struct TileAddr {
-  uint32_t k_off;  // K: D/8 threads per row, 16 bytes each, rows tid / (D/8) + j 256/(D/8)
-  uint32_t v_off;  // V: 4 consecutive rows x 8 dims (see store_kv_tile)
-  uint32_t s_off;  // score: one key per thread (tid < 64)
-  __device__ TileAddr(int tid, uint32_t row_bytes) {
-    k_off = (uint32_t)(tid / (D / 8)) * row_bytes + (uint32_t)(tid % (D / 8)) * 16u;
-    const int dc = (tid & 1) + 2 * ((tid >> 4) % (D / 16));
-    const int kq = ((tid >> 1) & 7) + 8 * (tid / D);
-    v_off = (uint32_t)(4 * kq) * row_bytes + (uint32_t)dc * 16u;
-    s_off = (uint32_t)tid * 4u;
+struct Stager {
+  static constexpr int kTpr = D / 8;          // K: threads per row (16 bytes each)
+  static constexpr int kRpi = 256 / kTpr;     // K: rows per load instruction
+  static constexpr int kKLoads = kBN / kRpi;  // = D / 32
+  int k_row, k_col;  // K: first row and column of this thread
+  int v_dc, v_kq;    // V: unit of 8 dims (v_dc) x 4 keys (v_kq)
+  bool v_on;
+  __device__ explicit Stager(int t) {  // t = thread index within its half
+    k_row = t / kTpr;
+    k_col = (t % kTpr) * 8;
+    v_dc = (t & 1) + 2 * ((t >> 4) % (D / 16));
+    v_kq = ((t >> 1) & 7) + 8 * (t / D);
+    v_on = t < 2 * D;
+  }
+  __device__ __forceinline__ uint32_t k_off(uint32_t row_bytes) const {
+    return (uint32_t)k_row * row_bytes + (uint32_t)k_col * 2u;
+  }
+  __device__ __forceinline__ uint32_t v_off(uint32_t row_bytes) const {
+    return (uint32_t)(4 * v_kq) * row_bytes + (uint32_t)v_dc * 16u;
   }
 };
 
-// Buffer loads of one 64-key tile; keys past the prompt read as zeros.
 template <int D>
-__device__ __forceinline__ void load_kv_tile(__amdgpu_buffer_rsrc_t rk, __amdgpu_buffer_rsrc_t rv,
-                                             __amdgpu_buffer_rsrc_t rs, const TileAddr<D>& ad, uint32_t row_bytes,
-                                             int kv0, int tid, u32x4 (&kr)[D / 32], u32x4 (&vr)[4], float& sr) {
-  constexpr int kRpi = 256 / (D / 8);  // K rows per load instruction
+__device__ __forceinline__ void load_k(const Stager<D>& st, __amdgpu_buffer_rsrc_t rk, __amdgpu_buffer_rsrc_t rs,
+                                       uint32_t koff, uint32_t row_bytes, int kv0, int t, u32x4 (&r)[4], float& sr) {
 #pragma unroll
-  for (int j = 0; j < D / 32; ++j) kr[j] = buf_load16(rk, ad.k_off, (uint32_t)(kv0 + kRpi * j) * row_bytes);
-  if (tid < 2 * D) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) vr[i] = buf_load16(rv, ad.v_off, (uint32_t)(kv0 + i) * row_bytes);
-  }
-  if (tid < kBN) sr = buf_load4f(rs, ad.s_off, (uint32_t)kv0 * 4u);
+  for (int j = 0; j < Stager<D>::kKLoads; ++j)
+    r[j] = buf_load16(rk, koff, (uint32_t)(kv0 + Stager<D>::kRpi * j) * row_bytes);
+  if (t < kBN) sr = buf_load4f(rs, (uint32_t)t * 4u, (uint32_t)kv0 * 4u);
 }
 
 template <int D, int G>
-__device__ __forceinline__ void store_kv_tile(AttnSmem<D>& sm, int buf, int tid, const u32x4 (&kr)[D / 32],
-                                              const u32x4 (&vr)[4], float sr, const float (&bscale)[G]) {
-  {
-    constexpr int kTpr = D / 8;
-    constexpr int kRpi = 256 / kTpr;
-    const int c = (tid % kTpr) * 8;
+__device__ __forceinline__ void store_k(const Stager<D>& st, AttnSmem<D>& sm, int buf, int t, const u32x4 (&r)[4],
+                                        float sr, const float (&ratio)[G]) {
 #pragma unroll
-    for (int j = 0; j < D / 32; ++j)
-      *reinterpret_cast<u32x4*>(&sm.k[buf][(tid / kTpr + kRpi * j) * AttnSmem<D>::kLd + c]) = kr[j];
+  for (int j = 0; j < Stager<D>::kKLoads; ++j)
+    *reinterpret_cast<u32x4*>(&sm.k[buf][(st.k_row + Stager<D>::kRpi * j) * AttnSmem<D>::kLd + st.k_col]) = r[j];
+  if (t < kBN) {
+#pragma unroll
+    for (int hh = 0; hh < G; ++hh) sm.s[buf][hh][t] = ratio[hh] * sr;
   }
-  if (tid < 2 * D) {
-    const int dc = (tid & 1) + 2 * ((tid >> 4) % (D / 16));
-    const int kq = ((tid >> 1) & 7) + 8 * (tid / D);
+}
+
+template <int D>
+__device__ __forceinline__ void load_v(const Stager<D>& st, __amdgpu_buffer_rsrc_t rv, uint32_t voff,
+                                       uint32_t row_bytes, int kv0, u32x4 (&r)[4]) {
+  if (st.v_on) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) r[i] = buf_load16(rv, voff, (uint32_t)(kv0 + i) * row_bytes);
+  }
+}
+
+template <int D>
+__device__ __forceinline__ void store_v(const Stager<D>& st, AttnSmem<D>& sm, int buf, const u32x4 (&r)[4]) {
+  if (st.v_on) {
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
-      // dim e of the 4 rows: low or high bf16 of word e / 2 of each row, packed pairwise
+      // dim e of the 4 keys: low or high bf16 of word e / 2 of each key row, packed pairwise
       const uint32_t sel = (e & 1) ? 0x07060302u : 0x05040100u;
       const int w = e >> 1;
-      const u32x2 pk = u32x2{__builtin_amdgcn_perm(vr[1][w], vr[0][w], sel),
-                             __builtin_amdgcn_perm(vr[3][w], vr[2][w], sel)};
-      *reinterpret_cast<u32x2*>(&sm.vt[buf][(dc * 8 + e) * AttnSmem<D>::vLd + 4 * kq]) = pk;
+      const u32x2 pk = u32x2{__builtin_amdgcn_perm(r[1][w], r[0][w], sel),
+                             __builtin_amdgcn_perm(r[3][w], r[2][w], sel)};
+      *reinterpret_cast<u32x2*>(&sm.vt[buf][(st.v_dc * 8 + e) * AttnSmem<D>::vLd + 4 * st.v_kq]) = pk;
     }
-  }
-  if (tid < kBN) {
-#pragma unroll
-    for (int hh = 0; hh < G; ++hh) sm.s[hh][tid] = bscale[hh] * sr;
   }
 }
 
-// One key tile for one wave: S^T = K . Q^T, masked exp2-domain online softmax
-// with the gate bias, O^T += V^T . P^T.  `lim` (MASK only): the lane's last
-// visible key, tile-local (keys after it are causally masked or past the end).
-template <int D, bool MASK>
-__device__ __forceinline__ void attend_tile(const AttnSmem<D>& s_, int hl, const u32x4 (&qf)[D / 16],
-                                            f32x16 (&o)[D / 32], float& m_run, float& l_run, float qk_scale, int lim,
-                                            int g, int l32) {
-  // S^T for the two 32-key halves; the two accumulation chains are interleaved
-  f32x16 st[2] = {f32x16{}, f32x16{}};
-  const uint16_t* krow0 = &s_.k[0][l32 * AttnSmem<D>::kLd + 8 * g];
-  const uint16_t* krow1 = krow0 + 32 * AttnSmem<D>::kLd;
+// Instruction order for a block of MFMAS matrix ops fed by READS LDS reads:
+// AHEAD reads first, then alternating MFMA / read, then the remaining MFMAs.
+// Left alone, the compiler waits for each read right before its MFMA.
+template <int MFMAS, int READS, int AHEAD>
+__device__ __forceinline__ void sched_reads_ahead() {
+  static_assert(READS >= AHEAD && MFMAS >= READS - AHEAD, "pattern");
 #pragma unroll
-  for (int ks = 0; ks < D / 16; ++ks) {
-    const u32x4 a0 = *reinterpret_cast<const u32x4*>(krow0 + 16 * ks);
-    const u32x4 a1 = *reinterpret_cast<const u32x4*>(krow1 + 16 * ks);
-    st[0] = mfma32(a0, qf[ks], st[0]);
-    st[1] = mfma32(a1, qf[ks], st[1]);
+  for (int i = 0; i < AHEAD; ++i) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // DS read
+#pragma unroll
+  for (int i = 0; i < READS - AHEAD; ++i) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
   }
-  // logits in the exp2 domain, tile max
-  float tmax = -__builtin_inff();
 #pragma unroll
-  for (int hf = 0; hf < 2; ++hf) {
-#pragma unroll
-    for (int q4 = 0; q4 < 4; ++q4) {
-      const int kl = hf * 32 + 8 * q4 + 4 * g;  // first of 4 consecutive keys (tile-local)
-      const f32x4 sv = *reinterpret_cast<const f32x4*>(&s_.s[hl][kl]);
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        float xv = __builtin_fmaf(st[hf][4 * q4 + e], qk_scale, sv[e]);
-        if (MASK && kl + e > lim) xv = -__builtin_inff();
-        st[hf][4 * q4 + e] = xv;
-        tmax = __builtin_fmaxf(tmax, xv);
-      }
-    }
-  }
-  tmax = xor32_max(tmax);
-  // Lazy rescale: the reference point m_run only moves when some row's max
-  // exceeds it by more than 2^8 (or on the first visible tile); softmax does
-  // not depend on the reference point, and exp2(x - m_run) <= 2^8 stays well
-  // inside fp32 and bf16 range.
-  if (__ballot(tmax > m_run + 8.0f) != 0) {
-    asm volatile("; rare rescale");  // keeps this a branch rather than a select on every tile
-    const float m_new = __builtin_fmaxf(m_run, tmax);
-    const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
-    l_run *= alpha;
-#pragma unroll
-    for (int dt = 0; dt < D / 32; ++dt) o[dt] *= alpha;
-    m_run = m_new;
-  }
-  float psum = 0.0f;
-  u32x4 pf[4];  // P^T operands of the 4 PV steps (16 keys each)
-#pragma unroll
-  for (int hf = 0; hf < 2; ++hf) {
-#pragma unroll
-    for (int sub = 0; sub < 2; ++sub) {
-      u32x4 w;
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-        typedef float f32x2 __attribute__((ext_vector_type(2)));
-        const float p0 = __builtin_amdgcn_exp2f(st[hf][8 * sub + 2 * j] - m_run);
-        const float p1 = __builtin_amdgcn_exp2f(st[hf][8 * sub + 2 * j + 1] - m_run);
-        psum += p0 + p1;
-        w[j] = __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2{p0, p1}), bf16x2));
-      }
-      pf[2 * hf + sub] = w;
-    }
-  }
-  l_run += psum;
-  // O^T += V^T . P^T
-#pragma unroll
-  for (int s4 = 0; s4 < 4; ++s4) {
-#pragma unroll
-    for (int dt = 0; dt < D / 32; ++dt) {
-      const uint16_t* vrow = &s_.vt[0][(dt * 32 + l32) * AttnSmem<D>::vLd + 16 * s4 + 4 * g];
-      const u32x2 lo = *reinterpret_cast<const u32x2*>(vrow);
-      const u32x2 hi = *reinterpret_cast<const u32x2*>(vrow + 8);
-      o[dt] = mfma32(u32x4{lo[0], lo[1], hi[0], hi[1]}, pf[s4], o[dt]);
-    }
-  }
+  for (int i = 0; i < MFMAS - (READS - AHEAD); ++i) __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
 }
 
 template <int D, int G>
-__global__ __launch_bounds__(kThreads) void gated_attention_kernel(
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void gated_attention_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
     const float* __restrict__ key_score, const float* __restrict__ tau, const float* __restrict__ gain,
     const tg_segment* __restrict__ segs, int hq, int hkv, uint16_t* __restrict__ out) {
   constexpr int kBM = 128 / G;  // query rows per workgroup
   constexpr int kWavesPerHead = 4 / G;
-  // smem[stage][group]: the two wave groups work on alternate key tiles
-  __shared__ AttnSmem<D> sm[2][2];
+  __shared__ AttnSmem<D> sm;
 
   const tg_segment seg = segs[blockIdx.z];
   const int n = seg.kept_len;
@@ -200,19 +166,19 @@ __global__ __launch_bounds__(kThreads) void gated_attention_kernel(
 
   const int tid = threadIdx.x;
   const int grp = tid >> 8;      // 0: even key tiles, 1: odd key tiles
-  const int gtid = tid & 255;    // thread index inside the group
+  const int gtid = tid & 255;    // thread index inside the group (and inside its staging half)
   const int lane = tid & 63;
   const int wave = gtid >> 6;    // wave inside the group
   const int g = lane >> 5;
   const int l32 = lane & 31;
   const int c = blockIdx.x;
-  const int h = c * G + wave / kWavesPerHead;
+  const int hl = wave / kWavesPerHead;  // this wave's head inside the KV group
+  const int h = c * G + hl;
   const int qw0 = q0 + (wave % kWavesPerHead) * 32;  // first query row of this wave
   const int qrow = qw0 + l32;                         // the query column this lane owns
 
   const int64_t q_stride = (int64_t)hq * D;
   const int64_t kv_stride = (int64_t)hkv * D;
-  const uint16_t* qb = q + (int64_t)seg.kept_start * q_stride + (int64_t)h * D;
   const uint16_t* kb = k + (int64_t)seg.kept_start * kv_stride + (int64_t)c * D;
   const uint16_t* vb = v + (int64_t)seg.kept_start * kv_stride + (int64_t)c * D;
   const bool use_bias = key_score != nullptr && gain != nullptr;
@@ -222,22 +188,30 @@ __global__ __launch_bounds__(kThreads) void gated_attention_kernel(
   // no bias: an empty range makes every score load return 0
   const __amdgpu_buffer_rsrc_t rs = make_rsrc(use_bias ? key_score + seg.kept_start : key_score,
                                               use_bias ? (uint32_t)n * 4u : 0u);
-  const TileAddr<D> ad(gtid, row_bytes);
+  const Stager<D> stg(gtid);
+  const bool stage_k = grp == 0;  // threads 0-255 stage K, 256-511 V
+  const uint32_t koff = stg.k_off(row_bytes), voff = stg.v_off(row_bytes);
 
-  const float th = tau != nullptr ? tau[h] : 1.0f;
-  const float qk_scale = th * kLog2e * (1.0f / __builtin_sqrtf((float)D));
-  float bscale[G];  // g_h log2(e) of every query head of the group (0 without a bias)
+  // logit scale c_h of this wave's head, and g_h log2(e) / c_h of every head of the group (for the staged bias)
+  const float base = kLog2e / __builtin_sqrtf((float)D);
+  float ratio[G];
 #pragma unroll
-  for (int hh = 0; hh < G; ++hh) bscale[hh] = use_bias ? gain[c * G + hh] * kLog2e : 0.0f;
-  const int hl = wave / kWavesPerHead;  // this wave's head inside the group
+  for (int hh = 0; hh < G; ++hh) {
+    const float th = tau != nullptr ? tau[c * G + hh] : 1.0f;
+    ratio[hh] = use_bias ? gain[c * G + hh] * kLog2e / __builtin_fmaxf(__builtin_fabsf(th) * base, 1e-30f) : 0.0f;
+  }
+  const float th = tau != nullptr ? tau[h] : 1.0f;
+  const float cs = __builtin_fmaxf(__builtin_fabsf(th) * base, 1e-30f);
 
   // Q^T operand: lane holds q[qrow][16 ks + 8 g .. + 7]
   u32x4 qf[D / 16];
   {
     const int r = qrow < n ? qrow : n - 1;
-    const u32x4* src = reinterpret_cast<const u32x4*>(qb + (int64_t)r * q_stride + 8 * g);
+    const u32x4* src = reinterpret_cast<const u32x4*>(q + ((int64_t)seg.kept_start + r) * q_stride +
+                                                      (int64_t)h * D + 8 * g);
+    const uint32_t flip = th < 0.0f ? 0x80008000u : 0u;
 #pragma unroll
-    for (int ks = 0; ks < D / 16; ++ks) qf[ks] = src[2 * ks];
+    for (int ks = 0; ks < D / 16; ++ks) qf[ks] = src[2 * ks] ^ flip;
 #pragma unroll
     for (int ks = 0; ks < D / 16; ++ks) asm volatile("" : "+v"(qf[ks]));  // keep Q resident, never re-read
   }
@@ -247,43 +221,150 @@ __global__ __launch_bounds__(kThreads) void gated_attention_kernel(
   for (int dt = 0; dt < D / 32; ++dt) o[dt] = f32x16{};
   float m_run = -__builtin_inff();
   float l_run = 0.0f;
+  f32x16 sa[2];  // S^T accumulators of the two 32-key halves
+  u32x4 pf[4];   // P^T operands of the 4 PV steps (16 keys each)
 
   const int q_end = min(q0 + kBM, n);  // keys needed: t < q_end
   const int ntiles = (q_end + kBN - 1) / kBN;
-  const int npairs = (ntiles + 1) / 2;
+  const int wlast = qw0 + 31;  // this wave's last query row
 
-  u32x4 kr[D / 32];
-  u32x4 vr[4];
-  float sr = 0.0f;
-  // pair 0: group 0 stages tile 0, group 1 tile 1 (if any)
-  if (grp < ntiles) {
-    load_kv_tile<D>(rk, rv, rs, ad, row_bytes, grp * kBN, gtid, kr, vr, sr);
-    store_kv_tile<D, G>(sm[0][grp], 0, gtid, kr, vr, sr, bscale);
+  // Staging registers, two sets (set = tile parity): a tile's global loads are
+  // issued two half-steps before the tile is read from LDS and stored to LDS
+  // at the start of the half-step in between.
+  u32x4 sreg[2][4];
+  float sr[2] = {0.0f, 0.0f};
+  if (stage_k) {
+    if (ntiles > 0) {
+      load_k<D>(stg, rk, rs, koff, row_bytes, 0, gtid, sreg[0], sr[0]);
+      store_k<D, G>(stg, sm, 0, gtid, sreg[0], sr[0], ratio);
+    }
+    if (ntiles > 1) load_k<D>(stg, rk, rs, koff, row_bytes, kBN, gtid, sreg[1], sr[1]);
   }
   __syncthreads();
 
-  for (int ip = 0; ip < npairs; ++ip) {
-    const int buf = ip & 1;
-    const int jt = 2 * ip + grp;  // this group's key tile
-    const int kv0 = jt * kBN;
-    const int jn = jt + 2;        // this group's next key tile
-    const bool more = jn < ntiles;
-    if (more) load_kv_tile<D>(rk, rv, rs, ad, row_bytes, jn * kBN, gtid, kr, vr, sr);
-
-    if (jt < ntiles && kv0 <= qw0 + 31) {  // some key of this tile is visible to some row of this wave
-      const AttnSmem<D>& s_ = sm[buf][grp];
-      if ((kv0 + kBN - 1 > qw0) || (kv0 + kBN > n))
-        attend_tile<D, true>(s_, hl, qf, o, m_run, l_run, qk_scale, min(qrow, n - 1) - kv0, g, l32);
-      else
-        attend_tile<D, false>(s_, hl, qf, o, m_run, l_run, qk_scale, 0, g, l32);
+  // One half-step; P = hs & 1 (compile time, so the register sets are static).
+  auto half_step = [&](int hs, auto p_) {
+    constexpr int P = decltype(p_)::value;
+    // stores first, so that the LDS writes overlap this half-step's work instead
+    // of delaying its barrier: K tile hs + 1 and V tile hs - 1 from set P ^ 1
+    // (loaded one half-step ago) into the buffers last read in the previous half-step
+    if (stage_k) {
+      if (hs + 1 < ntiles) store_k<D, G>(stg, sm, P ^ 1, gtid, sreg[P ^ 1], sr[P ^ 1], ratio);
+    } else {
+      if (hs >= 1 && hs - 1 < ntiles) store_v<D>(stg, sm, P ^ 1, sreg[P ^ 1]);
+    }
+    // loads: K tile hs + 2 (threads 0-255) and V tile hs (threads 256-511) into set P
+    if (stage_k) {
+      if (hs + 2 < ntiles) load_k<D>(stg, rk, rs, koff, row_bytes, (hs + 2) * kBN, gtid, sreg[P], sr[P]);
+    } else {
+      if (hs < ntiles) load_v<D>(stg, rv, voff, row_bytes, hs * kBN, sreg[P]);
     }
 
-    if (more) store_kv_tile<D, G>(sm[buf ^ 1][grp], 0, gtid, kr, vr, sr, bscale);
+    if (P == grp) {
+      // MFMA phase: PV of tile hs - 2, then QK of tile hs
+      const int jp = hs - 2;
+      if (jp >= 0 && jp * kBN <= wlast) {
+        const uint16_t* vt = sm.vt[jp & 1];
+#pragma unroll
+        for (int s4 = 0; s4 < 4; ++s4) {
+#pragma unroll
+          for (int dt = 0; dt < D / 32; ++dt) {
+            const uint16_t* vrow = vt + (dt * 32 + l32) * AttnSmem<D>::vLd + 16 * s4 + 4 * g;
+            const u32x2 lo = *reinterpret_cast<const u32x2*>(vrow);
+            const u32x2 hi = *reinterpret_cast<const u32x2*>(vrow + 8);
+            o[dt] = mfma32(u32x4{lo[0], lo[1], hi[0], hi[1]}, pf[s4], o[dt]);
+          }
+        }
+        // keep 4 V fragment reads in flight ahead of the MFMAs (left alone, the
+        // compiler waits for each read right before its MFMA)
+        sched_reads_ahead<4 * (D / 32), 4 * (D / 32), 8>();
+      }
+      const int jq = hs;
+      if (jq < ntiles && jq * kBN <= wlast) {
+        const float* bias = sm.s[jq & 1][hl];
+#pragma unroll
+        for (int hf = 0; hf < 2; ++hf)
+#pragma unroll
+          for (int q4 = 0; q4 < 4; ++q4) {
+            const f32x4 bv = *reinterpret_cast<const f32x4*>(&bias[hf * 32 + 8 * q4 + 4 * g]);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) sa[hf][4 * q4 + e] = bv[e];
+          }
+        const uint16_t* krow0 = &sm.k[jq & 1][l32 * AttnSmem<D>::kLd + 8 * g];
+        const uint16_t* krow1 = krow0 + 32 * AttnSmem<D>::kLd;
+#pragma unroll
+        for (int ks = 0; ks < D / 16; ++ks) {
+          const u32x4 a0 = *reinterpret_cast<const u32x4*>(krow0 + 16 * ks);
+          const u32x4 a1 = *reinterpret_cast<const u32x4*>(krow1 + 16 * ks);
+          sa[0] = mfma32(a0, qf[ks], sa[0]);
+          sa[1] = mfma32(a1, qf[ks], sa[1]);
+        }
+        sched_reads_ahead<D / 8, 8 + D / 8, 8 + 8>();  // the 8 bias reads and 8 K fragments ahead
+      }
+    } else {
+      // softmax phase of tile hs - 1
+      const int js = hs - 1;
+      if (js >= 0 && js < ntiles && js * kBN <= wlast) {
+        const int kv0 = js * kBN;
+        if (kv0 + kBN - 1 > qw0 || kv0 + kBN > n) {
+          // the lane's last visible key (tile-local), less its 4 g row offset, so that
+          // every comparison below is against a constant
+          const int lim = min(qrow, n - 1) - kv0 - 4 * g;
+#pragma unroll
+          for (int hf = 0; hf < 2; ++hf)
+#pragma unroll
+            for (int i = 0; i < 16; ++i)
+              if (hf * 32 + 8 * (i / 4) + (i % 4) > lim) sa[hf][i] = -__builtin_inff();
+        }
+        float m0 = -__builtin_inff(), m1 = -__builtin_inff();
+#pragma unroll
+        for (int i = 0; i < 16; i += 2) {
+          m0 = __builtin_fmaxf(m0, __builtin_fmaxf(sa[0][i], sa[0][i + 1]));
+          m1 = __builtin_fmaxf(m1, __builtin_fmaxf(sa[1][i], sa[1][i + 1]));
+        }
+        const float x = cs * xor32_max(__builtin_fmaxf(m0, m1));
+        // Lazy rescale: the reference point m_run only moves when some row's
+        // max exceeds it by more than 2^8 (or on the first visible tile);
+        // softmax does not depend on the reference point, and
+        // exp2(x - m_run) <= 2^8 stays well inside fp32 and bf16 range.
+        if (__ballot(x > m_run + 8.0f) != 0) {
+          asm volatile("; rare rescale");  // keeps this a branch rather than a select on every tile
+          const float m_new = __builtin_fmaxf(m_run, x);
+          const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+          l_run *= alpha;
+#pragma unroll
+          for (int dt = 0; dt < D / 32; ++dt) o[dt] *= alpha;
+          m_run = m_new;
+        }
+        const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
+#pragma unroll
+        for (int hf = 0; hf < 2; ++hf)
+#pragma unroll
+          for (int sub = 0; sub < 2; ++sub) {
+            u32x4 w;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+              const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(sa[hf][8 * sub + 2 * j], cs, -m_run));
+              const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(sa[hf][8 * sub + 2 * j + 1], cs, -m_run));
+              // (bit-cast a scalar: a bit-cast of the vector element w[j] reads element 0 with this compiler)
+              const uint32_t pk = pack_bf16(p0, p1);
+              w[j] = pk;
+              l_run = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pk), ones, l_run, false);
+            }
+            pf[2 * hf + sub] = w;
+          }
+      }
+    }
+
     __syncthreads();
+  };
+  for (int hs = 0; hs < ntiles + 2; hs += 2) {
+    half_step(hs, std::integral_constant<int, 0>());
+    if (hs + 1 < ntiles + 2) half_step(hs + 1, std::integral_constant<int, 1>());
   }
 
   // Merge the two groups: group 1 hands (m, l, O^T) to group 0 through LDS.
-  float* xo = reinterpret_cast<float*>(&sm[0][0]);  // 4 waves x (D x 32 + 64) floats, fits in the K/V buffers
+  float* xo = reinterpret_cast<float*>(&sm);  // 4 waves x (D x 32 + 64) floats, fits in the K/V buffers
   float* mine = xo + wave * (D * 32 + 64);
   const float l_half = xor32_sum(l_run);  // both half-waves: same bits
   if (grp == 1) {
@@ -310,17 +391,14 @@ __global__ __launch_bounds__(kThreads) void gated_attention_kernel(
       for (int dt = 0; dt < D / 32; ++dt) {
 #pragma unroll
         for (int q4 = 0; q4 < 4; ++q4) {
-          typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-          typedef float f32x2 __attribute__((ext_vector_type(2)));
           float r[4];
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
             const int i = 4 * q4 + e;
             r[e] = (o[dt][i] * a0 + mine[(dt * 16 + i) * 64 + lane] * a1) * inv;
           }
-          const uint32_t w0 = __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2{r[0], r[1]}), bf16x2));
-          const uint32_t w1 = __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2{r[2], r[3]}), bf16x2));
-          *reinterpret_cast<u32x2*>(orow + 32 * dt + 8 * q4 + 4 * g) = u32x2{w0, w1};
+          *reinterpret_cast<u32x2*>(orow + 32 * dt + 8 * q4 + 4 * g) = u32x2{pack_bf16(r[0], r[1]),
+                                                                             pack_bf16(r[2], r[3])};
         }
       }
     }
