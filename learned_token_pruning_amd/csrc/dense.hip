@@ -209,45 +209,50 @@ __global__ __launch_bounds__(256) void rmsnorm_kernel(const uint16_t* __restrict
   }
 }
 
-// Rotary embedding (rotate-half form) of the Q and K heads of a fused QKV row,
-// written to separate token-major Q, K, V arrays.  Position p of row r is
-// positions[r]; frequency of pair i (i < D/2) is theta^(-2 i / D); the angle
-// is computed in fp32 from the integer position.  One wave per (row, head).
+// RoPE (rotate-half) of Q and K and the Q/K/V split: the fused projection
+// output [m, (hq + 2 hkv) D] is written to separate token-major Q, K, V
+// arrays.  Position p of row r is positions[r]; pair i (i < D/2) of every Q
+// and K head turns by p * theta^(-2 i / D), the angle and its sin / cos taken
+// in fp64 (at positions up to 2^17 an fp32 angle, or an fp32 log2 theta,
+// carries errors of 1e-3 .. 1e-2 rad) and rounded to fp32 once per row: one
+// wave per row computes the row's D/2 angles into LDS, then rotates all
+// hq + hkv heads with them and copies V.
 __global__ __launch_bounds__(256) void rope_split_kernel(const uint16_t* __restrict__ qkv, int64_t ldqkv, int64_t m,
                                                          int hq, int hkv, int dh, const int32_t* __restrict__ positions,
                                                          double log2_theta, uint16_t* __restrict__ q,
                                                          uint16_t* __restrict__ k, uint16_t* __restrict__ v) {
-  const int heads = hq + 2 * hkv;
-  const int64_t item = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (item >= m * heads) return;
-  const int64_t row = item / heads;
-  const int h = (int)(item - row * heads);
+  __shared__ float tab[4][2][128];  // per wave: cos, sin of the row's angles (dh <= 256)
+  const int wave = threadIdx.x >> 6;
   const int lane = threadIdx.x & 63;
-  const uint16_t* src = qkv + row * ldqkv + (int64_t)h * dh;
-  uint16_t* dst;
-  if (h < hq)
-    dst = q + (row * hq + h) * dh;
-  else if (h < hq + hkv)
-    dst = k + (row * hkv + (h - hq)) * dh;
-  else
-    dst = v + (row * hkv + (h - hq - hkv)) * dh;
+  const int64_t row = (int64_t)blockIdx.x * 4 + wave;
+  const bool on = row < m;
   const int half = dh / 2;
-  if (h >= hq + hkv) {  // V: plain copy
-    for (int c = lane; c < dh; c += 64) dst[c] = src[c];
-    return;
+  if (on) {
+    const double p = (double)positions[row];
+    for (int i = lane; i < half; i += 64) {
+      const double ang = p * exp2(-log2_theta * (2.0 * (double)i / (double)dh));
+      double sd, cd;
+      sincos(ang, &sd, &cd);
+      tab[wave][0][i] = (float)cd;
+      tab[wave][1][i] = (float)sd;
+    }
   }
-  const double p = (double)positions[row];
-  for (int i = lane; i < half; i += 64) {
-    // angle in fp64 (log2 theta too): at positions up to 2^17 an fp32 angle, or an fp32 log2 theta, carries
-    // errors of 1e-3 .. 1e-2 rad
-    const double ang = p * exp2(-log2_theta * (2.0 * (double)i / (double)dh));
-    double sd, cd;
-    sincos(ang, &sd, &cd);
-    const float s = (float)sd, c = (float)cd;
-    const float x1 = bf16_lo((uint32_t)src[i]), x2 = bf16_lo((uint32_t)src[i + half]);
-    dst[i] = (uint16_t)f32_to_bf16(x1 * c - x2 * s);
-    dst[i + half] = (uint16_t)f32_to_bf16(x2 * c + x1 * s);
+  __syncthreads();
+  if (!on) return;
+  const uint16_t* src = qkv + row * ldqkv;
+  for (int h = 0; h < hq + hkv; ++h) {
+    const uint16_t* sh = src + (int64_t)h * dh;
+    uint16_t* dst = h < hq ? q + (row * hq + h) * dh : k + (row * hkv + (h - hq)) * dh;
+    for (int i = lane; i < half; i += 64) {
+      const float c = tab[wave][0][i], s = tab[wave][1][i];
+      const float x1 = bf16_lo((uint32_t)sh[i]), x2 = bf16_lo((uint32_t)sh[i + half]);
+      dst[i] = (uint16_t)f32_to_bf16(x1 * c - x2 * s);
+      dst[i + half] = (uint16_t)f32_to_bf16(x2 * c + x1 * s);
+    }
   }
+  const uint16_t* sv = src + (int64_t)(hq + hkv) * dh;
+  uint16_t* dv = v + row * hkv * dh;
+  for (int e = lane; e < hkv * dh; e += 64) dv[e] = sv[e];
 }
 
 }  // namespace
@@ -283,8 +288,7 @@ hipError_t launch_rmsnorm(const void* x, int64_t ldx, int64_t m, int d, const vo
 hipError_t launch_rope_split(const void* qkv, int64_t ldqkv, int64_t m, int hq, int hkv, int dh,
                              const int32_t* positions, float theta, void* q, void* k, void* v, hipStream_t stream) {
   if (m == 0) return hipSuccess;
-  const int64_t items = m * (hq + 2 * hkv);
-  hipLaunchKernelGGL(rope_split_kernel, dim3((unsigned)((items + 3) / 4)), dim3(256), 0, stream,
+  hipLaunchKernelGGL(rope_split_kernel, dim3((unsigned)((m + 3) / 4)), dim3(256), 0, stream,
                      reinterpret_cast<const uint16_t*>(qkv), ldqkv, m, hq, hkv, dh, positions, log2((double)theta),
                      reinterpret_cast<uint16_t*>(q), reinterpret_cast<uint16_t*>(k), reinterpret_cast<uint16_t*>(v));
   return hipGetLastError();
