@@ -136,8 +136,11 @@ int tg_gate_score(const void* x, int64_t ld_x, int d, const void* w1, const floa
 /* (2) Top-K select                                                          */
 /* ------------------------------------------------------------------------ */
 
-/* Device workspace (bytes) tg_select_topk needs for this plan (currently 0:
- * the selector keeps its state on chip; workspace may then be NULL). */
+/* Device workspace (bytes) tg_select_topk needs for this plan: 0 when every
+ * prompt has at most 32768 tokens (one workgroup per prompt keeps its state
+ * on chip; workspace may then be NULL); otherwise room for the radix
+ * histograms and per-slice counts of the multi-workgroup path (no initial
+ * contents required). */
 size_t tg_select_workspace_bytes(const tg_plan_info* info);
 
 /* Kept set of every prompt, S = top-K(s_j over the document) ∪ (every
@@ -151,8 +154,9 @@ size_t tg_select_workspace_bytes(const tg_plan_info* info);
  *   workspace (device, tg_select_workspace_bytes, 256-byte aligned; may be
  *     NULL when that size is 0).
  * Exact integer algorithm (radix select on order-preserving 32-bit keys,
- * then an index-ordered scan): identical results on every run.  One launch,
- * one workgroup per prompt. */
+ * then an index-ordered scan): identical results on every run.  One launch
+ * with one workgroup per prompt up to 32768 tokens; longer prompts use six
+ * launches over 4096-token slices (integer atomics only). */
 int tg_select_topk(const float* scores, const tg_segment* segs, const tg_plan_info* info, int32_t* kept_idx,
                    void* workspace, size_t workspace_bytes, void* stream);
 

@@ -4,11 +4,11 @@
 // ("TokenGate 与 T2Quant ... 精读", sections 3.1 and 4.1).  Order among document
 // tokens: higher score, then lower index.
 //
-// One launch, one 1024-thread workgroup per prompt.  At batch 1 the scores
-// are 64-512 KiB: the cost is latency, not bandwidth, so everything a
-// multi-block design would spend on launches, global atomics and fences is
-// avoided.  Thread t owns R consecutive tokens of every 1024 R-token chunk;
-// when the prompt fits one chunk the keys stay in registers for all passes.
+// Prompts of up to 32K tokens: one launch, one 1024-thread workgroup per
+// prompt, keys in registers for all passes (thread t owns R = 16 or 32
+// consecutive tokens).  At that size the cost is latency, so launches, global
+// atomics and fences are avoided.  Longer prompts use the multi-workgroup
+// path below.
 //
 // Scores become order-preserving 32-bit keys (score_key); the K-th largest
 // document key T is found exactly by a three-digit MSB radix select
@@ -226,22 +226,305 @@ __global__ __launch_bounds__(kThreads) void select_topk_kernel(const float* __re
   }
 }
 
+
+// ---------------------------------------------------------------------------
+// Long prompts (more than 32K tokens): the same algorithm spread over many
+// workgroups.  Every prompt is cut into 4096-token slices, one 256-thread
+// workgroup each.  A radix pass accumulates each slice's LDS histogram into a
+// global one with integer atomics (exact, so the result does not depend on
+// the order); the next pass's workgroups all re-derive the chosen digit from
+// it with the same integer scan, so they agree without exchanging anything.
+// After three passes a count kernel records, per slice, how many tokens are
+// kept for sure and how many tie the threshold; the emission kernel turns
+// the counts of the earlier slices into its output offset and the tie quota
+// left for it, then writes its kept indices in index order.
+// Workspace: hist [3][n_seg][2048] u32 | cnt [n_seg][n_slices][2] u32.
+
+constexpr int kSlice = 4096;
+constexpr int kMT = 256;
+constexpr int kMPer = kSlice / kMT;  // tokens per thread
+
+struct MultiSmem {
+  uint32_t hist[kBins];
+  uint32_t wtot[2][4];
+  uint32_t digit, rem;
+};
+
+// exclusive prefixes of two counters over the 256 threads; block totals out
+__device__ __forceinline__ void scan256(uint32_t a, uint32_t b, uint32_t& ea, uint32_t& eb, uint32_t& ta,
+                                        uint32_t& tb, MultiSmem& sm) {
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  uint32_t xa = a, xb = b;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const uint32_t ya = __shfl_up(xa, o), yb = __shfl_up(xb, o);
+    if (lane >= o) {
+      xa += ya;
+      xb += yb;
+    }
+  }
+  if (lane == 63) {
+    sm.wtot[0][wave] = xa;
+    sm.wtot[1][wave] = xb;
+  }
+  __syncthreads();
+  uint32_t pa = 0, pb = 0;
+  ta = tb = 0;
+#pragma unroll
+  for (int w = 0; w < 4; ++w) {
+    const uint32_t va = sm.wtot[0][w], vb = sm.wtot[1][w];
+    if (w < wave) {
+      pa += va;
+      pb += vb;
+    }
+    ta += va;
+    tb += vb;
+  }
+  __syncthreads();
+  ea = pa + xa - a;
+  eb = pb + xb - b;
+}
+
+// Digit (counted from the top) of the global histogram h that holds the
+// rem-th largest key, and the rank left inside it.
+__device__ void multi_find(const uint32_t* __restrict__ h, uint32_t bins, uint32_t& rem, uint32_t& digit,
+                           MultiSmem& sm) {
+  const int tid = threadIdx.x;
+  const uint32_t per = bins / kMT;  // 8 or 4 bins per thread, highest first
+  uint32_t c[8];
+  uint32_t sum = 0u;
+  for (uint32_t j = 0; j < per; ++j) {
+    c[j] = h[bins - 1u - (tid * per + j)];
+    sum += c[j];
+  }
+  uint32_t before, u0, t0, t1;
+  scan256(sum, 0u, before, u0, t0, t1, sm);
+  if (before < rem && rem <= before + sum) {
+    uint32_t acc = before;
+    for (uint32_t j = 0; j < per; ++j) {
+      if (acc + c[j] >= rem) {
+        sm.digit = bins - 1u - (tid * per + j);
+        sm.rem = rem - acc;
+        break;
+      }
+      acc += c[j];
+    }
+  }
+  __syncthreads();
+  digit = sm.digit;
+  rem = sm.rem;
+  __syncthreads();
+}
+
+__device__ __forceinline__ void pass_shape(int pass, int& shift, uint32_t& bins, uint32_t& mask) {
+  shift = pass == 0 ? 21 : (pass == 1 ? 10 : 0);
+  bins = pass == 2 ? 1024u : 2048u;
+  mask = pass == 0 ? 0u : (pass == 1 ? 0xffe00000u : 0xfffffc00u);
+}
+
+__global__ __launch_bounds__(256) void select_zero_kernel(uint32_t* __restrict__ w, int64_t n) {
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256) w[i] = 0u;
+}
+
+template <int PASS>
+__global__ __launch_bounds__(kMT) void select_hist_kernel(const float* __restrict__ scores,
+                                                          const tg_segment* __restrict__ segs, int n_seg,
+                                                          uint32_t* __restrict__ ws) {
+  __shared__ MultiSmem sm;
+  const tg_segment seg = segs[blockIdx.y];
+  const int n_doc = seg.doc_end - seg.doc_begin;
+  if (seg.k_eff <= 0 || seg.k_eff >= n_doc) return;  // no selection to make
+  const int t0 = blockIdx.x * kSlice;
+  if (t0 >= seg.seg_len) return;
+  const int tid = threadIdx.x;
+  uint32_t* hs = ws + (int64_t)blockIdx.y * kBins;  // + p * n_seg * kBins for pass p
+  uint32_t prefix = 0u, rem = (uint32_t)seg.k_eff;
+  for (int p = 0; p < PASS; ++p) {
+    int shift;
+    uint32_t bins, mask, digit;
+    pass_shape(p, shift, bins, mask);
+    multi_find(hs + (int64_t)p * n_seg * kBins, bins, rem, digit, sm);
+    prefix |= digit << shift;
+  }
+  int shift;
+  uint32_t bins, mask;
+  pass_shape(PASS, shift, bins, mask);
+  for (int i = tid; i < kBins; i += kMT) sm.hist[i] = 0u;
+  __syncthreads();
+  const float* ss = scores + seg.seg_start;
+#pragma unroll
+  for (int i = 0; i < kMPer; ++i) {
+    const int t = t0 + i * kMT + tid;  // coalesced
+    if (t < seg.seg_len && t >= seg.doc_begin && t < seg.doc_end) {
+      const uint32_t key = score_key(ss[t]);
+      if ((key & mask) == prefix) atomicAdd(&sm.hist[(key >> shift) & (bins - 1u)], 1u);
+    }
+  }
+  __syncthreads();
+  uint32_t* hg = hs + (int64_t)PASS * n_seg * kBins;
+  for (int b = tid; b < (int)bins; b += kMT) {
+    const uint32_t v = sm.hist[b];
+    if (v != 0u) atomicAdd(&hg[b], v);
+  }
+}
+
+// Threshold key T and tie quota `need` of a prompt (as in the one-workgroup kernel).
+__device__ void multi_threshold(const tg_segment& seg, int n_seg, const uint32_t* __restrict__ ws, MultiSmem& sm,
+                                uint32_t& thresh, uint32_t& need) {
+  const int n_doc = seg.doc_end - seg.doc_begin;
+  if (seg.k_eff <= 0) {
+    thresh = 0xffffffffu;
+    need = 0u;
+  } else if (seg.k_eff >= n_doc) {
+    thresh = 0u;
+    need = 0xffffffffu;
+  } else {
+    const uint32_t* hs = ws + (int64_t)blockIdx.y * kBins;
+    uint32_t prefix = 0u, rem = (uint32_t)seg.k_eff;
+    for (int p = 0; p < 3; ++p) {
+      int shift;
+      uint32_t bins, mask, digit;
+      pass_shape(p, shift, bins, mask);
+      multi_find(hs + (int64_t)p * n_seg * kBins, bins, rem, digit, sm);
+      prefix |= digit << shift;
+    }
+    thresh = prefix;
+    need = rem;
+  }
+}
+
+// Per slice: tokens kept for sure (non-document or key > T) and ties at T.
+__global__ __launch_bounds__(kMT) void select_count_kernel(const float* __restrict__ scores,
+                                                           const tg_segment* __restrict__ segs, int n_seg,
+                                                           int n_slices, uint32_t* __restrict__ ws) {
+  __shared__ MultiSmem sm;
+  const tg_segment seg = segs[blockIdx.y];
+  const int t0 = blockIdx.x * kSlice;
+  if (t0 >= seg.seg_len) return;
+  uint32_t thresh, need;
+  multi_threshold(seg, n_seg, ws, sm, thresh, need);
+  const float* ss = scores + seg.seg_start;
+  uint32_t nd = 0u, nt = 0u;
+#pragma unroll
+  for (int i = 0; i < kMPer; ++i) {
+    const int t = t0 + i * kMT + (int)threadIdx.x;
+    if (t < seg.seg_len) {
+      if (t < seg.doc_begin || t >= seg.doc_end) {
+        ++nd;
+      } else {
+        const uint32_t key = score_key(ss[t]);
+        nd += key > thresh;
+        nt += key == thresh;
+      }
+    }
+  }
+  uint32_t e0, e1, td, tt;
+  scan256(nd, nt, e0, e1, td, tt, sm);
+  if (threadIdx.x == 0) {
+    uint32_t* cnt = ws + (int64_t)3 * n_seg * kBins + ((int64_t)blockIdx.y * n_slices + blockIdx.x) * 2;
+    cnt[0] = td;
+    cnt[1] = tt;
+  }
+}
+
+__global__ __launch_bounds__(kMT) void select_emit_kernel(const float* __restrict__ scores,
+                                                          const tg_segment* __restrict__ segs, int n_seg,
+                                                          int n_slices, const uint32_t* __restrict__ ws,
+                                                          int32_t* __restrict__ kept_idx) {
+  __shared__ MultiSmem sm;
+  const tg_segment seg = segs[blockIdx.y];
+  const int s0 = blockIdx.x * kSlice;
+  if (s0 >= seg.seg_len) return;
+  uint32_t thresh, need;
+  multi_threshold(seg, n_seg, ws, sm, thresh, need);
+  // offsets from the earlier slices of this prompt
+  const uint32_t* cnt = ws + (int64_t)3 * n_seg * kBins + (int64_t)blockIdx.y * n_slices * 2;
+  uint32_t bd = 0u, bt = 0u;
+  {
+    const int j = threadIdx.x;  // one earlier slice per thread (n_slices <= 256 per 1M tokens; looped beyond)
+    uint32_t d = 0u, t = 0u;
+    for (int jj = j; jj < (int)blockIdx.x; jj += kMT) {
+      d += cnt[2 * jj];
+      t += cnt[2 * jj + 1];
+    }
+    uint32_t e0, e1;
+    scan256(d, t, e0, e1, bd, bt, sm);
+  }
+  // thread-contiguous ownership for the index-ordered emission
+  const float* ss = scores + seg.seg_start;
+  const int t0 = s0 + (int)threadIdx.x * kMPer;
+  uint32_t fd = 0u, ft = 0u;
+#pragma unroll
+  for (int i = 0; i < kMPer; ++i) {
+    const int t = t0 + i;
+    if (t < seg.seg_len && t < s0 + kSlice) {
+      if (t < seg.doc_begin || t >= seg.doc_end) {
+        fd |= 1u << i;
+      } else {
+        const uint32_t key = score_key(ss[t]);
+        if (key > thresh)
+          fd |= 1u << i;
+        else if (key == thresh)
+          ft |= 1u << i;
+      }
+    }
+  }
+  uint32_t ed, et, td, tt;
+  scan256((uint32_t)__builtin_popcount(fd), (uint32_t)__builtin_popcount(ft), ed, et, td, tt, sm);
+  uint32_t rdf = bd + ed;
+  uint32_t rtie = bt + et;
+  int32_t* out = kept_idx + seg.kept_start;
+#pragma unroll
+  for (int i = 0; i < kMPer; ++i) {
+    const bool d = (fd >> i) & 1u;
+    const bool tie = (ft >> i) & 1u;
+    const uint32_t taken = rtie < need ? rtie : need;
+    if (d || (tie && rtie < need)) {
+      const uint32_t pos = rdf + taken;
+      if (pos < (uint32_t)seg.kept_len) out[pos] = seg.seg_start + t0 + i;
+    }
+    rdf += d;
+    rtie += tie;
+  }
+}
+
 }  // namespace
 
+// One workgroup per prompt up to 32K tokens (keys resident in registers);
+// past that the six-launch multi-workgroup path is faster.
+static bool use_multi(const tg_plan_info& info) { return info.max_seg_len > kThreads * 32; }
+
+static int n_slices(const tg_plan_info& info) { return (int)((info.max_seg_len + kSlice - 1) / kSlice); }
+
 size_t select_workspace_bytes(const tg_plan_info& info) {
-  (void)info;
-  return 0;
+  if (!use_multi(info)) return 0;  // the one-workgroup kernel keeps its state on chip
+  const size_t words = (size_t)3 * info.n_seg * kBins + (size_t)info.n_seg * n_slices(info) * 2;
+  return (words * 4 + 255) / 256 * 256;
 }
 
 hipError_t launch_select_topk(const float* scores, const tg_segment* segs, const tg_plan_info& info,
                               int32_t* kept_idx, void* workspace, hipStream_t stream) {
-  (void)workspace;
   if (info.max_seg_len <= 0) return hipSuccess;
-  dim3 grid(info.n_seg);
-  if (info.max_seg_len <= kThreads * 16)
-    hipLaunchKernelGGL(select_topk_kernel<16>, grid, dim3(kThreads), 0, stream, scores, segs, kept_idx);
-  else
-    hipLaunchKernelGGL(select_topk_kernel<32>, grid, dim3(kThreads), 0, stream, scores, segs, kept_idx);
+  if (!use_multi(info)) {
+    if (info.max_seg_len <= kThreads * 16)
+      hipLaunchKernelGGL(select_topk_kernel<16>, dim3(info.n_seg), dim3(kThreads), 0, stream, scores, segs, kept_idx);
+    else
+      hipLaunchKernelGGL(select_topk_kernel<32>, dim3(info.n_seg), dim3(kThreads), 0, stream, scores, segs, kept_idx);
+    return hipGetLastError();
+  }
+  uint32_t* ws = static_cast<uint32_t*>(workspace);
+  const int ns = n_slices(info);
+  const int n_seg = (int)info.n_seg;
+  const int64_t hist_words = (int64_t)3 * n_seg * kBins;
+  hipLaunchKernelGGL(select_zero_kernel, dim3((unsigned)((hist_words + 255) / 256 < 1024 ? (hist_words + 255) / 256 : 1024)),
+                     dim3(256), 0, stream, ws, hist_words);
+  const dim3 grid(ns, n_seg);
+  hipLaunchKernelGGL(select_hist_kernel<0>, grid, dim3(kMT), 0, stream, scores, segs, n_seg, ws);
+  hipLaunchKernelGGL(select_hist_kernel<1>, grid, dim3(kMT), 0, stream, scores, segs, n_seg, ws);
+  hipLaunchKernelGGL(select_hist_kernel<2>, grid, dim3(kMT), 0, stream, scores, segs, n_seg, ws);
+  hipLaunchKernelGGL(select_count_kernel, grid, dim3(kMT), 0, stream, scores, segs, n_seg, ns, ws);
+  hipLaunchKernelGGL(select_emit_kernel, grid, dim3(kMT), 0, stream, scores, segs, n_seg, ns, ws, kept_idx);
   return hipGetLastError();
 }
 

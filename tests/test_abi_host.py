@@ -102,6 +102,14 @@ def test_select_validation():
     if ws > 0:
         assert f(FAKE, FAKE, info, FAKE, FAKE, ws - 4, None) == -3
         assert f(FAKE, FAKE, info, FAKE, None, ws, None) == -3
+    # prompts past 32768 tokens take the multi-workgroup path, which needs a workspace
+    assert ws == 0
+    long = tg.plan_segments([0, 40000, 40100], [0, 0], [39000, 90], [4096, 10])  # 10 slices of 4096
+    wl = tg.select_workspace_bytes(long)
+    assert wl >= 4 * (3 * 2 * 2048 + 2 * 10 * 2) and wl % 256 == 0
+    il = ctypes.byref(long.info)
+    assert f(FAKE, FAKE, il, FAKE, None, wl, None) == -3
+    assert f(FAKE, FAKE, il, FAKE, FAKE, wl - 256, None) == -3
     bad = tg.PlanInfo(n_tokens=10, total_kept=20, n_seg=1, max_seg_len=10, max_doc_len=5, max_kept_len=10)
     assert f(FAKE, FAKE, ctypes.byref(bad), FAKE, FAKE, ws, None) == -1
 

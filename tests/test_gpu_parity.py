@@ -189,15 +189,26 @@ def test_select_all_equal():
     check_select(s, W.Segments([0, 10000], [0], [10000], [4321]))
 
 
-@pytest.mark.parametrize("seed", [0, 1, 2, 3])
+@pytest.mark.parametrize("seed", [0, 1, 2, 3, 4, 5])
 def test_select_ragged_segments(seed):
+    """Batches of 40 prompts; seeds 4 and 5 have prompts past 32K tokens, so they
+    run the multi-workgroup path (4096-token slices) next to short prompts."""
     _say("select ragged", seed)
     rng = np.random.default_rng(100 + seed)
-    seg = W.random_segments(rng, 40, [50, 500, 5000, 20000][seed])
+    seg = W.random_segments(rng, 40, [50, 500, 5000, 20000, 70000, 70000][seed])
     s = W.mixture_scores(seed, seg)
-    if seed == 3:  # coarse values: many ties everywhere
+    if seed in (3, 5):  # coarse values: many ties everywhere
         s = np.round(s * 2) / 2
     check_select(s.astype(np.float32), seg)
+
+
+@pytest.mark.parametrize("k", [0, 1, 4095, 4096, 40000, 40003, 50000])
+def test_select_budget_edges_long(k):
+    """Budget edges on the multi-workgroup path (one 40003-token document)."""
+    _say("select budget long", k)
+    seg = W.single_segment(40003, 5, k)
+    s = W.mixture_scores(11, seg, k_marks=(4096,))
+    check_select(s, seg)
 
 
 def test_select_deterministic():
