@@ -57,21 +57,24 @@ __device__ __forceinline__ void load_w_frag(const u32x4* __restrict__ w1p, int n
   for (int j = 0; j < 4; ++j) w[j] = src[j * 64];
 }
 
+// One workgroup per (k block kb, 32-unit tile ut): the 32 x 64 block of W1 is
+// read row by row (8 lanes x 16 bytes per 128-byte row slice), staged in LDS
+// and written out in fragment order as 4 contiguous KiB.
 __global__ __launch_bounds__(256) void pack_w1_kernel(const uint16_t* __restrict__ w1, int d, int h,
                                                       u32x4* __restrict__ w1p) {
-  // one thread per packed 16-byte chunk: chunk = ((kb * n_ut + ut) * 4 + j) * 64 + lane
-  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  const int64_t total = (int64_t)d * h / 8;
-  if (i >= total) return;
-  const int lane = (int)(i & 63);
-  const int j = (int)((i >> 6) & 3);
-  const int64_t rest = i >> 8;
+  __shared__ u32x4 blk[32][8 + 1];  // [unit][16-byte k chunk], padded
   const int n_ut = h / 32;
-  const int ut = (int)(rest % n_ut);
-  const int kb = (int)(rest / n_ut);
-  const int unit = 32 * ut + (lane & 31);
-  const int k = 64 * kb + 32 * (lane >> 5) + 8 * j;
-  w1p[i] = *reinterpret_cast<const u32x4*>(w1 + (int64_t)unit * d + k);
+  const int ut = blockIdx.x % n_ut;
+  const int kb = blockIdx.x / n_ut;
+  const int tid = threadIdx.x;
+  {
+    const int u = tid >> 3, c = tid & 7;  // unit row, 16-byte chunk of its 64 k values
+    blk[u][c] = *reinterpret_cast<const u32x4*>(w1 + (int64_t)(32 * ut + u) * d + 64 * kb + 8 * c);
+  }
+  __syncthreads();
+  // fragment chunk i = j * 64 + lane holds W1[32 ut + lane % 32][64 kb + 32 (lane / 32) + 8 j .. + 7]
+  const int lane = tid & 63, j = tid >> 6;
+  w1p[((int64_t)(kb * n_ut + ut) * 4 + j) * 64 + lane] = blk[lane & 31][4 * (lane >> 5) + j];
 }
 
 // NCT: 32-unit column tiles per wave (1 or 2).  RT: 32-row tiles per workgroup
@@ -338,8 +341,7 @@ hipError_t launch_gate_score(const void* x, int64_t ld_x, int d, const void* w1,
   double* ts = reinterpret_cast<double*>(workspace);
   u32x4* w1p = reinterpret_cast<u32x4*>(reinterpret_cast<char*>(workspace) + sumsq_bytes(info));
   if (info.max_doc_len > 0) {
-    const int64_t chunks = (int64_t)d * h / 8;
-    hipLaunchKernelGGL(pack_w1_kernel, dim3((unsigned)((chunks + 255) / 256)), dim3(256), 0, stream,
+    hipLaunchKernelGGL(pack_w1_kernel, dim3((unsigned)((d / 64) * (h / 32))), dim3(256), 0, stream,
                        reinterpret_cast<const uint16_t*>(w1), d, h, w1p);
     dim3 grid(max_tiles, info.n_seg);
     const uint16_t* xp = reinterpret_cast<const uint16_t*>(x);
