@@ -133,6 +133,40 @@ def time_pipeline(pipe, steps, warmup):
     return wall / steps * 1e6, gpu_step, per_stage
 
 
+def capture_step(pipe):
+    """One step (all stages) captured as a HIP graph on a side stream; every
+    buffer is preallocated, and no stage allocates, synchronises or memsets."""
+    torch = pipe.torch
+    stages = pipe.stages()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):  # warm the stream before capture
+        for _, f in stages:
+            f()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for _, f in stages:
+            f()
+    torch.cuda.synchronize()
+    return g
+
+
+def time_graph(pipe, steps, warmup):
+    """Wall time per step of graph replays, bracketed by device synchronisation."""
+    torch = pipe.torch
+    g = capture_step(pipe)
+    for _ in range(warmup):
+        g.replay()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        g.replay()
+    torch.cuda.synchronize()
+    return (time.perf_counter() - t0) / steps * 1e6
+
+
 def cpu_baseline(layer, k_budget, budget_s=12.0):
     """The oracle (as it stands) on the same 16K workload, timed on the host cores."""
     import oracle
@@ -330,8 +364,10 @@ def main():
         l16 = W.workload(2)
         p16 = Pipeline(l16, 2048, torch, tg)
         log("timing 16K", args.steps, "steps")
-        us_wall, us_gpu, st16 = time_pipeline(p16, args.steps, args.warmup)
-        log("16K: wall", f"{us_wall:.1f} us/step, events {us_gpu:.1f} us/step", st16)
+        us_eager, us_gpu, st16 = time_pipeline(p16, args.steps, args.warmup)
+        log("16K: eager", f"{us_eager:.1f} us/step, events {us_gpu:.1f} us/step", st16)
+        us_wall = time_graph(p16, args.steps, args.warmup)
+        log("16K: graph replay", f"{us_wall:.1f} us/step")
         roofs = stage_rooflines(p16, st16, csrc)
         dominant = max(st16, key=st16.get)
         sc_gbs = p16.select_compact_bytes() / ((st16["select"] + st16["compact"]) * 1e-6) / 1e9
@@ -351,11 +387,12 @@ def main():
             "config": {"workload": "gated layer N=16384 (16320 doc + 64 question), d=2048, gate 2048-256-1, "
                                    "K=2048 (M=2112 kept), 16 Q / 8 KV heads, head_dim 128",
                        "global_batch": 1, "seq_len": p16.n, "k_budget": 2048, "kept_rows": p16.m,
-                       "parallelism": "none", "launch": "eager, one stream"},
+                       "parallelism": "none", "launch": "one HIP graph per step (per-stage times: eager launches)"},
             "roofline": dict(roofs[dominant], stage=dominant),
             "stages_us": {k: round(v, 2) for k, v in st16.items()},
             "stage_rooflines": roofs,
             "gpu_us_per_step_events": round(us_gpu, 2),
+            "eager_us_per_step": round(us_eager, 2),
             "attention": {"tflops": roofs["attention"]["achieved"], "frac_mfma_peak": roofs["attention"]["frac"]},
             "select_plus_compact": {"gbs": sc_gbs, "frac_hbm_peak": sc_gbs / HBM_PEAK_GBS},
         }
@@ -368,11 +405,13 @@ def main():
         torch.cuda.reset_peak_memory_stats()
         p128 = Pipeline(l128, 2048, torch, tg)
         steps = args.steps if args.only_long else max(10, args.steps // 4)
-        us_wall128, us_gpu128, st128 = time_pipeline(p128, steps, max(3, args.warmup // 4))
-        log("128K: wall", f"{us_wall128:.1f} us/step", st128)
+        us_eager128, us_gpu128, st128 = time_pipeline(p128, steps, max(3, args.warmup // 4))
+        us_wall128 = time_graph(p128, steps, max(3, args.warmup // 4))
+        log("128K: eager", f"{us_eager128:.1f} us/step, graph replay {us_wall128:.1f} us/step", st128)
         long_rec = {
             "workload": "gated layer N=131072 (131008 doc + 64 question), d=2048, K=2048 (M=2112 kept)",
             "tokens_per_s": p128.n / (us_wall128 * 1e-6), "ms_per_step": us_wall128 / 1e3, "steps": steps,
+            "eager_us_per_step": round(us_eager128, 2), "launch": "one HIP graph per step",
             "stages_us": {k: round(v, 2) for k, v in st128.items()},
             "stage_rooflines": stage_rooflines(p128, st128, csrc),
             "peak_device_mem_gib": torch.cuda.max_memory_allocated() / 2 ** 30,

@@ -393,3 +393,33 @@ def test_pipeline(idx):
     q, k, v = (oracle.compact_rows(a, ref_idx) for a in (L.q, L.k, L.v))
     # the oracle's own scores drive its attention: gate error feeds through the bias (|g| <= 1.5)
     check_attention(got, q, k, v, oracle.compact_rows(s_ref, ref_idx), L.tau, L.gain, offs)
+
+
+def test_pipeline_graph_replays_match_eager():
+    """The step captured as a HIP graph (as bench.py times it): every replay,
+    with eager launches and synchronisations in between, gives the eager
+    results bit for bit."""
+    _say("pipeline graph replay")
+    import torch
+    import bench
+    tg = _tg()
+    L = layer(1)
+    pipe = bench.Pipeline(L, 128, torch, tg)
+    for _, f in pipe.stages():
+        f()
+    torch.cuda.synchronize()
+    ref = [t.clone() for t in (pipe.scores, pipe.kept, pipe.out, pipe.hc)]
+    g = bench.capture_step(pipe)
+    for rep in range(4):
+        for t in (pipe.scores, pipe.out, pipe.hc):
+            t.zero_()
+        pipe.kept.fill_(-1)
+        g.replay()
+        torch.cuda.synchronize()
+        got = (pipe.scores, pipe.kept, pipe.out, pipe.hc)
+        for a, b in zip(got, ref):
+            assert torch.equal(a.view(torch.uint8) if a.dtype != torch.int32 else a,
+                               b.view(torch.uint8) if b.dtype != torch.int32 else b), f"replay {rep}"
+        for _, f in pipe.stages():  # eager work between replays
+            f()
+        torch.cuda.synchronize()
