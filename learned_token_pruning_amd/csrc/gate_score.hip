@@ -323,12 +323,9 @@ static void launch_mlp(dim3 grid, hipStream_t stream, const uint16_t* xp, int64_
 template <int NCT>
 static void launch_mlp_d(dim3 grid, hipStream_t stream, const uint16_t* xp, int64_t ld_x, int d, const u32x4* wp,
                          const float* b1, const float* w2, float b2, int h, const tg_segment* segs, int max_tiles,
-                         float* scores, double* ts, bool tall) {
-  // X stage of 256 columns (512-byte row bursts) when d allows; measured best among 128-1024-byte bursts.
-  // Tall tiles (128 rows) halve the W1 fragment traffic per MFMA; used when they still fill the device.
-  if (tall && d % 256 == 0)
-    launch_mlp<NCT, 4, 4, 4>(grid, stream, xp, ld_x, d, wp, b1, w2, b2, h, segs, max_tiles, scores, ts);
-  else if (d % 256 == 0)
+                         float* scores, double* ts) {
+  // X stage of 256 columns (512-byte row bursts) when d allows; measured best among 128-1024-byte bursts
+  if (d % 256 == 0)
     launch_mlp<NCT, 2, 4, 4>(grid, stream, xp, ld_x, d, wp, b1, w2, b2, h, segs, max_tiles, scores, ts);
   else if (d % 128 == 0)
     launch_mlp<NCT, 2, 2, 2>(grid, stream, xp, ld_x, d, wp, b1, w2, b2, h, segs, max_tiles, scores, ts);
@@ -341,28 +338,24 @@ hipError_t launch_gate_score(const void* x, int64_t ld_x, int d, const void* w1,
                              float* scores, void* workspace, hipStream_t stream) {
   int max_tiles = (info.max_doc_len + kRows - 1) / kRows;  // at the smallest tile height: an upper bound
   if (max_tiles < 1) max_tiles = 1;
-  // 128-row tiles when there are at least two per CU (document rows of all prompts), else 64
-  const bool tall = d % 256 == 0 && (int64_t)info.n_seg * info.max_doc_len >= 2LL * 256 * 2 * kRows;
-  int rows_per_tile = kRows;
   double* ts = reinterpret_cast<double*>(workspace);
   u32x4* w1p = reinterpret_cast<u32x4*>(reinterpret_cast<char*>(workspace) + sumsq_bytes(info));
   if (info.max_doc_len > 0) {
     hipLaunchKernelGGL(pack_w1_kernel, dim3((unsigned)((d / 64) * (h / 32))), dim3(256), 0, stream,
                        reinterpret_cast<const uint16_t*>(w1), d, h, w1p);
+    dim3 grid(max_tiles, info.n_seg);
     const uint16_t* xp = reinterpret_cast<const uint16_t*>(x);
-    rows_per_tile = tall ? 2 * kRows : kRows;
-    dim3 grid((info.max_doc_len + rows_per_tile - 1) / rows_per_tile, info.n_seg);
     if (h <= 128)
-      launch_mlp_d<1>(grid, stream, xp, ld_x, d, w1p, b1, w2, b2, h, segs, max_tiles, scores, ts, tall);
+      launch_mlp_d<1>(grid, stream, xp, ld_x, d, w1p, b1, w2, b2, h, segs, max_tiles, scores, ts);
     else
-      launch_mlp_d<2>(grid, stream, xp, ld_x, d, w1p, b1, w2, b2, h, segs, max_tiles, scores, ts, tall);
+      launch_mlp_d<2>(grid, stream, xp, ld_x, d, w1p, b1, w2, b2, h, segs, max_tiles, scores, ts);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
   if (info.max_seg_len > 0) {
     dim3 grid((info.max_seg_len + kNormTokens - 1) / kNormTokens, info.n_seg);
-    hipLaunchKernelGGL(gate_normalize_kernel, grid, dim3(kNormThreads), 0, stream, segs, max_tiles, rows_per_tile, ts,
-                       rms_eps, scores);
+    hipLaunchKernelGGL(gate_normalize_kernel, grid, dim3(kNormThreads), 0, stream, segs, max_tiles, kRows, ts, rms_eps,
+                       scores);
     return hipGetLastError();
   }
   return hipSuccess;
