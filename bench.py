@@ -2,7 +2,9 @@
 
 One step = gate score -> top-K select -> compaction of the kept rows (hidden,
 Q, K, V, scores) -> token-gated attention over the kept rows, on one batch of
-synthetic input already resident in HBM.  The headline workload is the
+synthetic input already resident in HBM, launched as one HIP graph.  The
+variant whose attention reads Q, K, V and the scores through the kept indices
+(gather on load, compacting only hidden rows and scores) is timed beside it.  The headline workload is the
 16K-token gated layer (16320 document + 64 question tokens, d = 2048, gate
 MLP 2048 -> 256 -> 1, K = 2048, 16 query / 8 key-value heads, head_dim 128).
 The 128K-token layer at K = 2048 is measured too and reported beside it, and
@@ -41,8 +43,8 @@ def log(*a):
 class Pipeline:
     """Device-resident inputs, outputs and workspaces of one gated layer."""
 
-    def __init__(self, layer, k_budget, torch, tg):
-        self.torch, self.tg = torch, tg
+    def __init__(self, layer, k_budget, torch, tg, gather=False):
+        self.torch, self.tg, self.gather = torch, tg, gather
         dev = torch.device("cuda")
         seg = layer.segments.with_budget(k_budget)
         self.layer, self.seg = layer, seg
@@ -69,8 +71,11 @@ class Pipeline:
         self.vc = torch.empty_like(self.kc)
         self.sc = torch.empty(m, dtype=torch.float32, device=dev)
         self.out = torch.empty_like(self.qc)
-        self.pairs = [(self.x, self.hc), (self.q, self.qc), (self.k, self.kc), (self.v, self.vc),
-                      (self.scores, self.sc)]
+        # gather on load: attention reads Q, K, V and the scores through the kept indices, so only the
+        # rows the next layer needs (hidden state, scores) are compacted
+        self.pairs = ([(self.x, self.hc), (self.scores, self.sc)] if gather else
+                      [(self.x, self.hc), (self.q, self.qc), (self.k, self.kc), (self.v, self.vc),
+                       (self.scores, self.sc)])
 
     def stages(self):
         tg = self.tg
@@ -79,8 +84,11 @@ class Pipeline:
                                            workspace=self.gws)),
             ("select", lambda: tg.select_topk(self.scores, self.plan, kept_idx=self.kept, workspace=self.sws)),
             ("compact", lambda: tg.compact_kept(self.kept, self.pairs)),
-            ("attention", lambda: tg.gated_attention_prefill(self.qc, self.kc, self.vc, self.sc, self.tau, self.gain,
-                                                             self.plan, out=self.out)),
+            ("attention", (lambda: tg.gated_attention_prefill_gather(
+                self.q, self.k, self.v, self.scores, self.tau, self.gain, self.plan, self.kept, out=self.out))
+             if self.gather else
+             (lambda: tg.gated_attention_prefill(self.qc, self.kc, self.vc, self.sc, self.tau, self.gain, self.plan,
+                                                 out=self.out))),
         ]
 
     # algorithmic work (what the method must do), per launch
@@ -94,15 +102,15 @@ class Pipeline:
         n_doc = self.seg.n_doc(0)
         return 2 * n_doc * L.d * L.h + 2 * n_doc * L.h
 
-    def select_compact_bytes(self):
+    def compact_row_bytes(self):
         L = self.layer
-        row = 2 * L.d + 2 * L.hq * L.head_dim + 2 * 2 * L.hkv * L.head_dim + 4
-        return 4 * self.seg.n_doc(0) + 4 * self.m + 4 * self.m + 2 * self.m * row
+        return 2 * L.d + 4 + (0 if self.gather else 2 * L.hq * L.head_dim + 2 * 2 * L.hkv * L.head_dim)
+
+    def select_compact_bytes(self):
+        return 4 * self.seg.n_doc(0) + 4 * self.m + 4 * self.m + 2 * self.m * self.compact_row_bytes()
 
     def compact_bytes(self):
-        L = self.layer
-        row = 2 * L.d + 2 * L.hq * L.head_dim + 2 * 2 * L.hkv * L.head_dim + 4
-        return 4 * self.m + 2 * self.m * row
+        return 4 * self.m + 2 * self.m * self.compact_row_bytes()
 
     def attention_flops(self):
         L = self.layer
@@ -368,6 +376,10 @@ def main():
         log("16K: eager", f"{us_eager:.1f} us/step, events {us_gpu:.1f} us/step", st16)
         us_wall = time_graph(p16, args.steps, args.warmup)
         log("16K: graph replay", f"{us_wall:.1f} us/step")
+        p16g = Pipeline(l16, 2048, torch, tg, gather=True)
+        us_gather = time_graph(p16g, args.steps, args.warmup)
+        log("16K: graph replay, attention gathering Q/K/V", f"{us_gather:.1f} us/step")
+        del p16g
         roofs = stage_rooflines(p16, st16, csrc)
         dominant = max(st16, key=st16.get)
         sc_gbs = p16.select_compact_bytes() / ((st16["select"] + st16["compact"]) * 1e-6) / 1e9
@@ -393,6 +405,7 @@ def main():
             "stage_rooflines": roofs,
             "gpu_us_per_step_events": round(us_gpu, 2),
             "eager_us_per_step": round(us_eager, 2),
+            "gather_on_load_us_per_step": round(us_gather, 2),
             "attention": {"tflops": roofs["attention"]["achieved"], "frac_mfma_peak": roofs["attention"]["frac"]},
             "select_plus_compact": {"gbs": sc_gbs, "frac_hbm_peak": sc_gbs / HBM_PEAK_GBS},
         }
@@ -408,10 +421,15 @@ def main():
         us_eager128, us_gpu128, st128 = time_pipeline(p128, steps, max(3, args.warmup // 4))
         us_wall128 = time_graph(p128, steps, max(3, args.warmup // 4))
         log("128K: eager", f"{us_eager128:.1f} us/step, graph replay {us_wall128:.1f} us/step", st128)
+        p128g = Pipeline(l128, 2048, torch, tg, gather=True)
+        us_gather128 = time_graph(p128g, steps, max(3, args.warmup // 4))
+        log("128K: graph replay, attention gathering Q/K/V", f"{us_gather128:.1f} us/step")
+        del p128g
         long_rec = {
             "workload": "gated layer N=131072 (131008 doc + 64 question), d=2048, K=2048 (M=2112 kept)",
             "tokens_per_s": p128.n / (us_wall128 * 1e-6), "ms_per_step": us_wall128 / 1e3, "steps": steps,
             "eager_us_per_step": round(us_eager128, 2), "launch": "one HIP graph per step",
+            "gather_on_load_us_per_step": round(us_gather128, 2),
             "stages_us": {k: round(v, 2) for k, v in st128.items()},
             "stage_rooflines": stage_rooflines(p128, st128, csrc),
             "peak_device_mem_gib": torch.cuda.max_memory_allocated() / 2 ** 30,

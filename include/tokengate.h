@@ -213,6 +213,23 @@ int tg_gated_attention_prefill(const void* q, const void* k, const void* v, cons
                                const float* tau, const float* gain, const tg_segment* segs,
                                const tg_plan_info* info, int hq, int hkv, int head_dim, void* out, void* stream);
 
+/* The same attention reading the kept rows where they are (gather on load)
+ * instead of from compacted copies: q [n_src_rows, hq, head_dim], k and v
+ * [n_src_rows, hkv, head_dim] (bf16, device) and key_score [n_src_rows]
+ * (fp32, device, or NULL) hold every token, and kept row r of prompt i is
+ * source row kept_idx[kept_start_i + r] (int32 [info->total_kept], device,
+ * as tg_select_topk writes it).  The output is compacted exactly as above:
+ * out [info->total_kept, hq, head_dim].  The compaction step then only has to
+ * move the rows the next layer needs (hidden state, scores), not Q, K and V.
+ * An index outside [0, n_src_rows) is a caller error: its K/V row and score
+ * read as zeros and its Q row as row 0 (no access outside the arrays).
+ * Supported in addition: at most 16384 kept rows per prompt and
+ * n_src_rows * hkv * head_dim * 2 < 2^32 (else TG_ERR_UNSUPPORTED). */
+int tg_gated_attention_prefill_gather(const void* q, const void* k, const void* v, const float* key_score,
+                                      const float* tau, const float* gain, const tg_segment* segs,
+                                      const tg_plan_info* info, int hq, int hkv, int head_dim,
+                                      const int32_t* kept_idx, int64_t n_src_rows, void* out, void* stream);
+
 /* ------------------------------------------------------------------------ */
 /* (5) Dense decoder-layer support (the layers below and above the gate)    */
 /* ------------------------------------------------------------------------ */

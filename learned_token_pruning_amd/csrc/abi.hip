@@ -189,8 +189,34 @@ int tg_gated_attention_prefill(const void* q, const void* k, const void* v, cons
   if (info->total_kept == 0) return TG_OK;
   st = check_device();
   if (st != TG_OK) return st;
-  return hip_status(tg::launch_gated_attention(q, k, v, key_score, tau, gain, segs, *info, hq, hkv, head_dim, out,
-                                               reinterpret_cast<hipStream_t>(stream)));
+  return hip_status(tg::launch_gated_attention(q, k, v, key_score, tau, gain, segs, *info, hq, hkv, head_dim,
+                                               nullptr, 0, out, reinterpret_cast<hipStream_t>(stream)));
+}
+
+int tg_gated_attention_prefill_gather(const void* q, const void* k, const void* v, const float* key_score,
+                                      const float* tau, const float* gain, const tg_segment* segs,
+                                      const tg_plan_info* info, int hq, int hkv, int head_dim,
+                                      const int32_t* kept_idx, int64_t n_src_rows, void* out, void* stream) {
+  int st = check_info(segs, info);
+  if (st != TG_OK) return st;
+  if (hq <= 0 || hkv <= 0 || head_dim <= 0 || n_src_rows < 0) return TG_ERR_INVALID_ARG;
+  if (info->total_kept > 0 && (!q || !k || !v || !out || !kept_idx || n_src_rows == 0)) return TG_ERR_INVALID_ARG;
+  if (hq % hkv != 0) return TG_ERR_UNSUPPORTED;
+  const int G = hq / hkv;
+  if (!(head_dim == 64 || head_dim == 128) || !(G == 1 || G == 2 || G == 4)) return TG_ERR_UNSUPPORTED;
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(out, 16)) return TG_ERR_INVALID_ARG;
+  if ((key_score && !aligned(key_score, 4)) || (tau && !aligned(tau, 4)) || (gain && !aligned(gain, 4)) ||
+      (kept_idx && !aligned(kept_idx, 4)))
+    return TG_ERR_INVALID_ARG;
+  // indices of a prompt's kept rows live in LDS; K/V rows are addressed with 32-bit byte offsets
+  if (info->max_kept_len > tg::kAttnMaxGatherRows) return TG_ERR_UNSUPPORTED;
+  if (n_src_rows * (int64_t)hkv * head_dim * 2 >= 0xffffff00LL || n_src_rows * 4 >= 0xffffff00LL)
+    return TG_ERR_UNSUPPORTED;
+  if (info->total_kept == 0) return TG_OK;
+  st = check_device();
+  if (st != TG_OK) return st;
+  return hip_status(tg::launch_gated_attention(q, k, v, key_score, tau, gain, segs, *info, hq, hkv, head_dim,
+                                               kept_idx, n_src_rows, out, reinterpret_cast<hipStream_t>(stream)));
 }
 
 int tg_gemm_bf16(int epilogue, const void* x, int64_t ldx, const void* w, int64_t ldw, int64_t m, int n, int k,
@@ -303,7 +329,8 @@ int tg_decoder_layer(void* hidden, const int32_t* positions, const float* key_sc
   TG_TRY(tg::launch_rmsnorm(hidden, d, m, d, w->attn_norm, rms_eps, xn, d, s));
   TG_TRY(tg::launch_gemm(0, xn, d, w->wqkv, d, m, nqkv, d, nullptr, 0, qkv, nqkv, s));
   TG_TRY(tg::launch_rope_split(qkv, nqkv, m, hq, hkv, head_dim, positions, rope_theta, q, k, v, s));
-  TG_TRY(tg::launch_gated_attention(q, k, v, key_score, w->tau, w->gain, segs, *info, hq, hkv, head_dim, att, s));
+  TG_TRY(tg::launch_gated_attention(q, k, v, key_score, w->tau, w->gain, segs, *info, hq, hkv, head_dim, nullptr, 0,
+                                    att, s));
   TG_TRY(tg::launch_gemm(1, att, (int64_t)hq * head_dim, w->wo, (int64_t)hq * head_dim, m, d, hq * head_dim, hidden,
                          d, hidden, d, s));
   TG_TRY(tg::launch_rmsnorm(hidden, d, m, d, w->mlp_norm, rms_eps, hn, d, s));

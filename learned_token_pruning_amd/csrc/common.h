@@ -97,10 +97,13 @@ struct CompactDesc {
 hipError_t launch_compact(const int32_t* kept_idx, int64_t n_kept, int64_t n_src, const CompactDesc& desc,
                           hipStream_t stream);
 
+// kept_idx == nullptr: q, k, v, key_score are the compacted kept rows.  Otherwise
+// they hold n_src rows and kept row r of a prompt is row kept_idx[kept_start + r].
 hipError_t launch_gated_attention(const void* q, const void* k, const void* v, const float* key_score,
                                   const float* tau, const float* gain, const tg_segment* segs,
-                                  const tg_plan_info& info, int hq, int hkv, int head_dim, void* out,
-                                  hipStream_t stream);
+                                  const tg_plan_info& info, int hq, int hkv, int head_dim, const int32_t* kept_idx,
+                                  int64_t n_src, void* out, hipStream_t stream);
+constexpr int64_t kAttnMaxGatherRows = 16384;
 
 hipError_t launch_gemm(int epi, const void* x, int64_t ldx, const void* w, int64_t ldw, int64_t m, int n, int k,
                        const void* res, int64_t ldr, void* y, int64_t ldy, hipStream_t stream);

@@ -46,6 +46,7 @@ namespace {
 
 constexpr int kBN = 64;        // keys per tile
 constexpr int kThreads = 512;  // two groups of 4 waves
+constexpr int kMaxGatherRows = 16384;  // kept rows per prompt the gathering variant supports (indices in LDS)
 constexpr float kLog2e = 1.4426950408889634f;
 
 template <int D>
@@ -88,13 +89,31 @@ struct Stager {
   }
 };
 
-template <int D>
+// Gathered rows: kept row r of the prompt is source row sidx[r]; rows at or
+// past `nvalid` get an offset past every buffer range, so they read as zeros.
+constexpr uint32_t kPastRange = 0xfffffff0u;
+
+template <int D, bool GATHER>
 __device__ __forceinline__ void load_k(const Stager<D>& st, __amdgpu_buffer_rsrc_t rk, __amdgpu_buffer_rsrc_t rs,
-                                       uint32_t koff, uint32_t row_bytes, int kv0, int t, u32x4 (&r)[4], float& sr) {
+                                       uint32_t koff, uint32_t row_bytes, int kv0, int t, u32x4 (&r)[4], float& sr,
+                                       const int32_t* sidx, int nvalid) {
+  if (!GATHER) {
 #pragma unroll
-  for (int j = 0; j < Stager<D>::kKLoads; ++j)
-    r[j] = buf_load16(rk, koff, (uint32_t)(kv0 + Stager<D>::kRpi * j) * row_bytes);
-  if (t < kBN) sr = buf_load4f(rs, (uint32_t)t * 4u, (uint32_t)kv0 * 4u);
+    for (int j = 0; j < Stager<D>::kKLoads; ++j)
+      r[j] = buf_load16(rk, koff, (uint32_t)(kv0 + Stager<D>::kRpi * j) * row_bytes);
+    if (t < kBN) sr = buf_load4f(rs, (uint32_t)t * 4u, (uint32_t)kv0 * 4u);
+  } else {
+#pragma unroll
+    for (int j = 0; j < Stager<D>::kKLoads; ++j) {
+      const int row = kv0 + st.k_row + Stager<D>::kRpi * j;
+      const uint32_t off = row < nvalid ? (uint32_t)sidx[row] * row_bytes + (uint32_t)st.k_col * 2u : kPastRange;
+      r[j] = buf_load16(rk, off, 0u);
+    }
+    if (t < kBN) {
+      const int row = kv0 + t;
+      sr = buf_load4f(rs, row < nvalid ? (uint32_t)sidx[row] * 4u : kPastRange, 0u);
+    }
+  }
 }
 
 template <int D, int G>
@@ -109,12 +128,21 @@ __device__ __forceinline__ void store_k(const Stager<D>& st, AttnSmem<D>& sm, in
   }
 }
 
-template <int D>
+template <int D, bool GATHER>
 __device__ __forceinline__ void load_v(const Stager<D>& st, __amdgpu_buffer_rsrc_t rv, uint32_t voff,
-                                       uint32_t row_bytes, int kv0, u32x4 (&r)[4]) {
+                                       uint32_t row_bytes, int kv0, u32x4 (&r)[4], const int32_t* sidx, int nvalid) {
   if (st.v_on) {
+    if (!GATHER) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) r[i] = buf_load16(rv, voff, (uint32_t)(kv0 + i) * row_bytes);
+      for (int i = 0; i < 4; ++i) r[i] = buf_load16(rv, voff, (uint32_t)(kv0 + i) * row_bytes);
+    } else {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int row = kv0 + 4 * st.v_kq + i;
+        const uint32_t off = row < nvalid ? (uint32_t)sidx[row] * row_bytes + (uint32_t)st.v_dc * 16u : kPastRange;
+        r[i] = buf_load16(rv, off, 0u);
+      }
+    }
   }
 }
 
@@ -150,19 +178,29 @@ __device__ __forceinline__ void sched_reads_ahead() {
   for (int i = 0; i < MFMAS - (READS - AHEAD); ++i) __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
 }
 
-template <int D, int G>
+// GATHER: q, k, v and key_score hold every token (n_src rows); kept row r of
+// a prompt is read from source row kept_idx[kept_start + r] (gather on load,
+// no compacted copies).  The output is always compacted.
+template <int D, int G, bool GATHER>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void gated_attention_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
     const float* __restrict__ key_score, const float* __restrict__ tau, const float* __restrict__ gain,
-    const tg_segment* __restrict__ segs, int hq, int hkv, uint16_t* __restrict__ out) {
+    const tg_segment* __restrict__ segs, int hq, int hkv, const int32_t* __restrict__ kept_idx, int64_t n_src,
+    uint16_t* __restrict__ out) {
   constexpr int kBM = 128 / G;  // query rows per workgroup
   constexpr int kWavesPerHead = 4 / G;
   __shared__ AttnSmem<D> sm;
+  __shared__ int32_t sidx[GATHER ? kMaxGatherRows : 1];  // source rows of the kept rows [0, q_end)
 
   const tg_segment seg = segs[blockIdx.z];
   const int n = seg.kept_len;
   const int q0 = (gridDim.y - 1 - blockIdx.y) * kBM;
   if (q0 >= n) return;  // uniform
+  const int q_end = min(q0 + kBM, n);  // keys needed: t < q_end
+  if (GATHER) {
+    for (int i = threadIdx.x; i < q_end; i += kThreads) sidx[i] = kept_idx[seg.kept_start + i];
+    __syncthreads();
+  }
 
   const int tid = threadIdx.x;
   const int grp = tid >> 8;      // 0: even key tiles, 1: odd key tiles
@@ -179,15 +217,16 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
 
   const int64_t q_stride = (int64_t)hq * D;
   const int64_t kv_stride = (int64_t)hkv * D;
-  const uint16_t* kb = k + (int64_t)seg.kept_start * kv_stride + (int64_t)c * D;
-  const uint16_t* vb = v + (int64_t)seg.kept_start * kv_stride + (int64_t)c * D;
+  const int64_t row0 = GATHER ? 0 : seg.kept_start;                  // first row of the K/V/score buffers
+  const uint32_t nrows = GATHER ? (uint32_t)n_src : (uint32_t)n;     // rows the buffers cover
+  const uint16_t* kb = k + row0 * kv_stride + (int64_t)c * D;
+  const uint16_t* vb = v + row0 * kv_stride + (int64_t)c * D;
   const bool use_bias = key_score != nullptr && gain != nullptr;
   const uint32_t row_bytes = (uint32_t)kv_stride * 2u;
-  const __amdgpu_buffer_rsrc_t rk = make_rsrc(kb, (uint32_t)n * row_bytes - (uint32_t)c * D * 2u);
-  const __amdgpu_buffer_rsrc_t rv = make_rsrc(vb, (uint32_t)n * row_bytes - (uint32_t)c * D * 2u);
+  const __amdgpu_buffer_rsrc_t rk = make_rsrc(kb, nrows * row_bytes - (uint32_t)c * D * 2u);
+  const __amdgpu_buffer_rsrc_t rv = make_rsrc(vb, nrows * row_bytes - (uint32_t)c * D * 2u);
   // no bias: an empty range makes every score load return 0
-  const __amdgpu_buffer_rsrc_t rs = make_rsrc(use_bias ? key_score + seg.kept_start : key_score,
-                                              use_bias ? (uint32_t)n * 4u : 0u);
+  const __amdgpu_buffer_rsrc_t rs = make_rsrc(use_bias ? key_score + row0 : key_score, use_bias ? nrows * 4u : 0u);
   const Stager<D> stg(gtid);
   const bool stage_k = grp == 0;  // threads 0-255 stage K, 256-511 V
   const uint32_t koff = stg.k_off(row_bytes), voff = stg.v_off(row_bytes);
@@ -207,8 +246,12 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
   u32x4 qf[D / 16];
   {
     const int r = qrow < n ? qrow : n - 1;
-    const u32x4* src = reinterpret_cast<const u32x4*>(q + ((int64_t)seg.kept_start + r) * q_stride +
-                                                      (int64_t)h * D + 8 * g);
+    int64_t qsrc = (int64_t)seg.kept_start + r;
+    if (GATHER) {
+      qsrc = sidx[r];
+      if (qsrc < 0 || qsrc >= n_src) qsrc = 0;  // a bad index never reads outside q
+    }
+    const u32x4* src = reinterpret_cast<const u32x4*>(q + qsrc * q_stride + (int64_t)h * D + 8 * g);
     const uint32_t flip = th < 0.0f ? 0x80008000u : 0u;
 #pragma unroll
     for (int ks = 0; ks < D / 16; ++ks) qf[ks] = src[2 * ks] ^ flip;
@@ -224,7 +267,6 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
   f32x16 sa[2];  // S^T accumulators of the two 32-key halves
   u32x4 pf[4];   // P^T operands of the 4 PV steps (16 keys each)
 
-  const int q_end = min(q0 + kBM, n);  // keys needed: t < q_end
   const int ntiles = (q_end + kBN - 1) / kBN;
   const int wlast = qw0 + 31;  // this wave's last query row
 
@@ -235,10 +277,10 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
   float sr[2] = {0.0f, 0.0f};
   if (stage_k) {
     if (ntiles > 0) {
-      load_k<D>(stg, rk, rs, koff, row_bytes, 0, gtid, sreg[0], sr[0]);
+      load_k<D, GATHER>(stg, rk, rs, koff, row_bytes, 0, gtid, sreg[0], sr[0], sidx, q_end);
       store_k<D, G>(stg, sm, 0, gtid, sreg[0], sr[0], ratio);
     }
-    if (ntiles > 1) load_k<D>(stg, rk, rs, koff, row_bytes, kBN, gtid, sreg[1], sr[1]);
+    if (ntiles > 1) load_k<D, GATHER>(stg, rk, rs, koff, row_bytes, kBN, gtid, sreg[1], sr[1], sidx, q_end);
   }
   __syncthreads();
 
@@ -255,9 +297,10 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
     }
     // loads: K tile hs + 2 (threads 0-255) and V tile hs (threads 256-511) into set P
     if (stage_k) {
-      if (hs + 2 < ntiles) load_k<D>(stg, rk, rs, koff, row_bytes, (hs + 2) * kBN, gtid, sreg[P], sr[P]);
+      if (hs + 2 < ntiles)
+        load_k<D, GATHER>(stg, rk, rs, koff, row_bytes, (hs + 2) * kBN, gtid, sreg[P], sr[P], sidx, q_end);
     } else {
-      if (hs < ntiles) load_v<D>(stg, rv, voff, row_bytes, hs * kBN, sreg[P]);
+      if (hs < ntiles) load_v<D, GATHER>(stg, rv, voff, row_bytes, hs * kBN, sreg[P], sidx, q_end);
     }
 
     if (P == grp) {
@@ -407,16 +450,22 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
 
 template <int D, int G>
 hipError_t launch_dg(const void* q, const void* k, const void* v, const float* ks, const float* tau,
-                     const float* gain, const tg_segment* segs, const tg_plan_info& info, int hq, int hkv, void* out,
-                     hipStream_t stream) {
+                     const float* gain, const tg_segment* segs, const tg_plan_info& info, int hq, int hkv,
+                     const int32_t* kept_idx, int64_t n_src, void* out, hipStream_t stream) {
   constexpr int kBM = 128 / G;
   const int ntiles = (info.max_kept_len + kBM - 1) / kBM;
   if (ntiles == 0) return hipSuccess;
   dim3 grid(hkv, ntiles, info.n_seg);
-  hipLaunchKernelGGL((gated_attention_kernel<D, G>), grid, dim3(kThreads), 0, stream,
-                     reinterpret_cast<const uint16_t*>(q), reinterpret_cast<const uint16_t*>(k),
-                     reinterpret_cast<const uint16_t*>(v), ks, tau, gain, segs, hq, hkv,
-                     reinterpret_cast<uint16_t*>(out));
+  if (kept_idx != nullptr)
+    hipLaunchKernelGGL((gated_attention_kernel<D, G, true>), grid, dim3(kThreads), 0, stream,
+                       reinterpret_cast<const uint16_t*>(q), reinterpret_cast<const uint16_t*>(k),
+                       reinterpret_cast<const uint16_t*>(v), ks, tau, gain, segs, hq, hkv, kept_idx, n_src,
+                       reinterpret_cast<uint16_t*>(out));
+  else
+    hipLaunchKernelGGL((gated_attention_kernel<D, G, false>), grid, dim3(kThreads), 0, stream,
+                       reinterpret_cast<const uint16_t*>(q), reinterpret_cast<const uint16_t*>(k),
+                       reinterpret_cast<const uint16_t*>(v), ks, tau, gain, segs, hq, hkv, nullptr, (int64_t)0,
+                       reinterpret_cast<uint16_t*>(out));
   return hipGetLastError();
 }
 
@@ -424,12 +473,12 @@ hipError_t launch_dg(const void* q, const void* k, const void* v, const float* k
 
 hipError_t launch_gated_attention(const void* q, const void* k, const void* v, const float* key_score,
                                   const float* tau, const float* gain, const tg_segment* segs,
-                                  const tg_plan_info& info, int hq, int hkv, int head_dim, void* out,
-                                  hipStream_t stream) {
+                                  const tg_plan_info& info, int hq, int hkv, int head_dim, const int32_t* kept_idx,
+                                  int64_t n_src, void* out, hipStream_t stream) {
   const int G = hq / hkv;
 #define TG_ATTN_CASE(DD, GG) \
   if (head_dim == DD && G == GG) \
-    return launch_dg<DD, GG>(q, k, v, key_score, tau, gain, segs, info, hq, hkv, out, stream);
+    return launch_dg<DD, GG>(q, k, v, key_score, tau, gain, segs, info, hq, hkv, kept_idx, n_src, out, stream);
   TG_ATTN_CASE(128, 1)
   TG_ATTN_CASE(128, 2)
   TG_ATTN_CASE(128, 4)

@@ -31,6 +31,7 @@ STATUS_NAMES = {0: "TG_OK", -1: "TG_ERR_INVALID_ARG", -2: "TG_ERR_UNSUPPORTED", 
                 -4: "TG_ERR_NO_DEVICE", -5: "TG_ERR_HIP"}
 EXPORTS = ("tg_status_string", "tg_abi_version", "tg_plan_segments", "tg_gate_workspace_bytes", "tg_gate_score",
            "tg_select_workspace_bytes", "tg_select_topk", "tg_compact_kept", "tg_gated_attention_prefill",
+           "tg_gated_attention_prefill_gather",
            "tg_gemm_bf16", "tg_rmsnorm_bf16", "tg_rope_split_bf16", "tg_decoder_layer_workspace_bytes",
            "tg_decoder_layer")
 GEMM_STORE, GEMM_RESIDUAL, GEMM_SWIGLU = 0, 1, 2
@@ -83,6 +84,9 @@ _lib.tg_select_topk.argtypes = [_vp, _vp, ctypes.POINTER(PlanInfo), _vp, _vp, _s
 _lib.tg_compact_kept.restype = _i32
 _lib.tg_compact_kept.argtypes = [_vp, _i64, _i64, _i32, ctypes.POINTER(_vp), ctypes.POINTER(_vp), ctypes.POINTER(_i64),
                                  ctypes.POINTER(_i64), ctypes.POINTER(_i64), _vp]
+_lib.tg_gated_attention_prefill_gather.restype = _i32
+_lib.tg_gated_attention_prefill_gather.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, ctypes.POINTER(PlanInfo), _i32,
+                                                   _i32, _i32, _vp, _i64, _vp, _vp]
 _lib.tg_gated_attention_prefill.restype = _i32
 _lib.tg_gated_attention_prefill.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, ctypes.POINTER(PlanInfo), _i32, _i32,
                                             _i32, _vp, _vp]
@@ -268,6 +272,23 @@ def gated_attention_prefill(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, k
                                          _dev_table(plan), ctypes.byref(plan.info), hq, hkv, dh, _ptr(out),
                                          _stream(stream))
     _check(st, "tg_gated_attention_prefill")
+    return out
+
+
+def gated_attention_prefill_gather(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
+                                   key_score: Optional[torch.Tensor], tau: Optional[torch.Tensor],
+                                   gain: Optional[torch.Tensor], plan: Plan, kept_idx: torch.Tensor,
+                                   out: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """tg_gated_attention_prefill_gather.  q [N, hq, D], k/v [N, hkv, D] bf16
+    contiguous over every token; kept_idx int32 [M]; returns out [M, hq, D]."""
+    n_src, hq, dh = q.shape
+    hkv = k.shape[1]
+    if out is None:
+        out = torch.empty((plan.total_kept, hq, dh), dtype=q.dtype, device=q.device)
+    st = _lib.tg_gated_attention_prefill_gather(_ptr(q), _ptr(k), _ptr(v), _ptr(key_score), _ptr(tau), _ptr(gain),
+                                                _dev_table(plan), ctypes.byref(plan.info), hq, hkv, dh,
+                                                _ptr(kept_idx), n_src, _ptr(out), _stream(stream))
+    _check(st, "tg_gated_attention_prefill_gather")
     return out
 
 

@@ -145,6 +145,19 @@ def test_attention_validation():
     assert f(FAKE, FAKE, FAKE, None, None, None, FAKE, info, 0, 8, 128, FAKE, None) == -1
 
 
+def test_attention_gather_validation():
+    p = _plan()
+    info = ctypes.byref(p.info)
+    f = L.tg_gated_attention_prefill_gather
+    assert f(FAKE, FAKE, FAKE, None, None, None, FAKE, info, 16, 8, 128, None, 100, FAKE, None) == -1  # no indices
+    assert f(FAKE, FAKE, FAKE, None, None, None, FAKE, info, 16, 8, 128, FAKE, 0, FAKE, None) == -1  # no rows
+    assert f(FAKE, FAKE, FAKE, None, None, None, FAKE, info, 16, 8, 96, FAKE, 100, FAKE, None) == -2
+    assert f(FAKE, FAKE, FAKE, None, None, None, FAKE, info, 16, 8, 128, FAKE, 1 << 22, FAKE, None) == -2  # 32-bit offsets
+    big = tg.plan_segments([0, 40000], [0], [39000], [20000])  # more kept rows than the gather path holds
+    assert f(FAKE, FAKE, FAKE, None, None, None, FAKE, ctypes.byref(big.info), 16, 8, 128, FAKE, 40000, FAKE,
+             None) == -2
+
+
 @pytest.mark.skipif(gpu_available(), reason="only meaningful without a GPU: valid calls must report no device")
 def test_valid_calls_report_no_device_without_gpu():
     p = _plan()

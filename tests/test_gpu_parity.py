@@ -342,6 +342,45 @@ def test_attention_workload_3_sampled(kb):
     check_attention(got, q, k, v, sc, L.tau, L.gain, offs, rows=rows)
 
 
+@pytest.mark.parametrize("d,hq,hkv,lens", [(128, 16, 8, [16384]), (64, 4, 2, [512, 3, 1000]),
+                                           (128, 8, 8, [700, 65]), (128, 16, 4, [2000, 1])])
+def test_attention_gather_equals_compacted(d, hq, hkv, lens):
+    """Gather on load (Q/K/V/scores read through the kept indices) gives the
+    compacted path's outputs bit for bit, and both match the oracle."""
+    import torch
+    _say("attention gather", d, hq, hkv, lens)
+    tg = _tg()
+    rng = np.random.default_rng(d + hq + len(lens))
+    offs = np.concatenate([[0], np.cumsum(lens)])
+    n = int(offs[-1])
+    q = W.f32_to_bf16_bits(rng.standard_normal((n, hq, d)).astype(np.float32))
+    k = W.f32_to_bf16_bits(rng.standard_normal((n, hkv, d)).astype(np.float32))
+    v = W.f32_to_bf16_bits(rng.standard_normal((n, hkv, d)).astype(np.float32))
+    s = rng.standard_normal(n).astype(np.float32)
+    tau = rng.uniform(0.8, 1.2, hq).astype(np.float32)
+    gain = rng.uniform(0.5, 1.5, hq).astype(np.float32)
+    # prompts whose documents are all but the last few tokens; budgets keep about a quarter
+    n_seg = len(lens)
+    db = [0] * n_seg
+    de = [max(0, L - 3) for L in lens]
+    kb = [max(0, (L - 3) // 4) for L in lens]
+    plan = tg.plan_segments(list(offs), db, de, kb, device="cuda")
+    kept = tg.select_topk(dev_f32(s), plan)
+    idx = kept.cpu().numpy().astype(np.int64)
+    qd, kd, vd, sd = dev_bf16(q), dev_bf16(k), dev_bf16(v), dev_f32(s)
+    tt, gg = dev_f32(tau), dev_f32(gain)
+    got_g = tg.gated_attention_prefill_gather(qd, kd, vd, sd, tt, gg, plan, kept)
+    qc, kc, vc, sc = (torch.index_select(t, 0, kept.long()) for t in (qd, kd, vd, sd))
+    got_c = tg.gated_attention_prefill(qc.contiguous(), kc.contiguous(), vc.contiguous(), sc.contiguous(), tt, gg,
+                                       plan)
+    torch.cuda.synchronize()
+    assert torch.equal(got_g.view(torch.int16), got_c.view(torch.int16))
+    koffs = plan.kept_offsets
+    ref_rows = np.linspace(0, idx.size - 1, min(idx.size, 300)).astype(np.int64)
+    check_attention(W.bf16_bits_to_f64(host_bf16(got_g)), q[idx], k[idx], v[idx], s[idx], tau, gain, koffs,
+                    rows=np.unique(ref_rows))
+
+
 def test_attention_deterministic():
     _say("attention determinism")
     L = layer(1)
@@ -395,7 +434,8 @@ def test_pipeline(idx):
     check_attention(got, q, k, v, oracle.compact_rows(s_ref, ref_idx), L.tau, L.gain, offs)
 
 
-def test_pipeline_graph_replays_match_eager():
+@pytest.mark.parametrize("gather", [False, True])
+def test_pipeline_graph_replays_match_eager(gather):
     """The step captured as a HIP graph (as bench.py times it): every replay,
     with eager launches and synchronisations in between, gives the eager
     results bit for bit."""
@@ -404,7 +444,7 @@ def test_pipeline_graph_replays_match_eager():
     import bench
     tg = _tg()
     L = layer(1)
-    pipe = bench.Pipeline(L, 128, torch, tg)
+    pipe = bench.Pipeline(L, 128, torch, tg, gather=gather)
     for _, f in pipe.stages():
         f()
     torch.cuda.synchronize()
