@@ -30,6 +30,8 @@ from .tokengate_ref import (  # noqa: F401
     kept_indices,
     compact_rows,
     gated_attention,
+    softplus,
+    query_temperature,
 )
 from .stack_ref import (  # noqa: F401,E402
     round_bf16,

@@ -221,8 +221,9 @@ def gated_attention(q: np.ndarray, k: np.ndarray, v: np.ndarray, s: Optional[np.
     g_j = softmax(b_j) ([reading] §4.1 component two), i.e. the score enters
     as an additive logit bias; the per-(layer, head) gain multiplies it and the
     temperature rescales q.k (refinements one and two).  The per-head
-    constant tau_h is the reading used here (the per-query temperature is a
-    later extension).  tau None -> 1, gain None or s None -> no bias.
+    constant tau_h is the reading used here; a [M, Hq] array instead gives
+    every kept row its own temperature (see query_temperature).  tau None
+    -> 1, gain None or s None -> no bias.
 
     q [M, Hq, D], k/v [M, Hkv, D], s [M]; float64.  ``rows`` optionally
     restricts the computation to those global kept-row indices (returned in
@@ -239,6 +240,8 @@ def gated_attention(q: np.ndarray, k: np.ndarray, v: np.ndarray, s: Optional[np.
         raise ValueError("Hq must be a multiple of Hkv")
     group = hq // hkv
     tau = np.ones(hq) if tau is None else np.asarray(tau, dtype=np.float64)
+    if tau.ndim == 1:
+        tau = np.broadcast_to(tau[None, :], (m_total, hq))
     use_bias = s is not None and gain is not None
     if use_bias:
         s = np.asarray(s, dtype=np.float64)
@@ -258,7 +261,7 @@ def gated_attention(q: np.ndarray, k: np.ndarray, v: np.ndarray, s: Optional[np.
         causal = np.arange(nk)[None, :] <= r_loc[:, None]
         for h in range(hq):
             c = h // group
-            z = tau[h] * (q[a + r_loc, h, :] @ k[a:a + nk, c, :].T) * scale
+            z = tau[a + r_loc, h][:, None] * (q[a + r_loc, h, :] @ k[a:a + nk, c, :].T) * scale
             if use_bias:
                 z = z + gain[h] * s[a:a + nk][None, :]
             z = np.where(causal, z, -np.inf)
@@ -267,3 +270,37 @@ def gated_attention(q: np.ndarray, k: np.ndarray, v: np.ndarray, s: Optional[np.
             p = p / p.sum(axis=1, keepdims=True)
             out[sel, h, :] = p @ v[a:a + nk, c, :]
     return out
+
+
+def softplus(x: np.ndarray) -> np.ndarray:
+    """log(1 + e^x), evaluated as max(x, 0) + log1p(e^-|x|) (no overflow)."""
+    x = np.asarray(x, dtype=np.float64)
+    return np.maximum(x, 0.0) + np.log1p(np.exp(-np.abs(x)))
+
+
+def query_temperature(sigma: np.ndarray, positions: np.ndarray, kept_offsets: Sequence[int]) -> np.ndarray:
+    """Per-query temperature of the kept rows ([reading] §4.1, component two,
+    second refinement): pruning shrinks the keys a query sees from its
+    original position p_i to its rank m_i among the kept tokens, which
+    sharpens the softmax; the temperature
+        tau_ih = softplus(sigma_h) * log(m_i) / log(max(2, p_i))
+    recalibrates it.  Readings: p_i = 1 + the row's original 0-based position
+    inside its prompt (the number of keys it sees unpruned) and m_i = 1 + its
+    0-based kept row inside the prompt (the number of kept keys it sees);
+    sigma is one value per (layer, head).  With nothing pruned m_i = p_i and
+    the factor is 1 (0 for the first row, whose single key makes any
+    temperature equivalent).
+
+    sigma [Hq]; positions [M] int (original positions of the kept rows, in
+    kept order); returns tau [M, Hq] float64.
+    Pinned by the no-pruning reduction, a two-key closed form and the
+    vanishing-temperature limit (tests/test_oracle_attention.py).
+    """
+    sigma = np.asarray(sigma, dtype=np.float64)
+    positions = np.asarray(positions, dtype=np.int64)
+    offs = [int(o) for o in kept_offsets]
+    m_rank = np.zeros(positions.size, dtype=np.float64)
+    for a, b in zip(offs[:-1], offs[1:]):
+        m_rank[a:b] = np.arange(1, b - a + 1)
+    p = np.maximum(2.0, positions.astype(np.float64) + 1.0)
+    return softplus(sigma)[None, :] * (np.log(m_rank) / np.log(p))[:, None]

@@ -106,3 +106,87 @@ def test_large_gain_selects_highest_score_key():
     for r in range(m):
         best = int(np.argmax(s[:r + 1]))
         np.testing.assert_allclose(o[r, 0], v[best, 0], atol=1e-9)
+
+
+# ----------------------------------------------------------------------------- per-query temperature
+
+
+def test_softplus_closed_forms():
+    assert oracle.softplus(np.array([0.0]))[0] == pytest.approx(LN2, abs=1e-15)
+    x = np.array([-30.0, -2.5, -0.1, 0.3, 4.0, 40.0, 800.0])
+    # softplus(x) - softplus(-x) = x, softplus(x) > max(x, 0), and e^softplus(x) - 1 = e^x
+    np.testing.assert_allclose(oracle.softplus(x) - oracle.softplus(-x), x, rtol=1e-14, atol=1e-14)
+    assert np.all(oracle.softplus(x[:5]) > np.maximum(x[:5], 0.0)) and oracle.softplus(x[-1:])[0] == 800.0
+    small = x[x < 5]
+    np.testing.assert_allclose(np.expm1(oracle.softplus(small)), np.exp(small), rtol=1e-13)
+
+
+def test_query_temperature_ranks_restart_per_prompt():
+    sig = np.array([0.0, 2.0])
+    pos = np.array([0, 4, 9, 2, 3])  # prompt 0 keeps positions 0, 4, 9; prompt 1 keeps 2, 3
+    t = oracle.query_temperature(sig, pos, [0, 3, 3, 5])
+    sp = np.log1p(np.exp(sig))
+    ranks = np.array([1, 2, 3, 1, 2])
+    orig = np.array([1, 5, 10, 3, 4])
+    for r in range(5):
+        want = 0.0 if ranks[r] == 1 else math.log(ranks[r]) / math.log(orig[r])
+        np.testing.assert_allclose(t[r], sp * want, rtol=1e-14, atol=0)
+    # kept rows in original order: rank <= position, so 0 <= tau <= softplus(sigma)
+    assert np.all(t >= 0) and np.all(t <= sp[None, :] + 1e-15)
+
+
+def test_query_temperature_is_identity_without_pruning():
+    """Nothing pruned: every query keeps all its keys (m_i = p_i), the
+    recalibration factor is 1, and the attention equals the per-head form
+    with tau_h = softplus(sigma_h)."""
+    rng = np.random.default_rng(11)
+    offs = [0, 9, 10, 31]
+    m, hq, hkv, d = 31, 4, 2, 8
+    q, k, v = (rng.standard_normal((m, h, d)) for h in (hq, hkv, hkv))
+    s = rng.standard_normal(m)
+    sigma = rng.uniform(-1.0, 1.5, hq)
+    gain = rng.uniform(0.5, 1.5, hq)
+    pos = np.concatenate([np.arange(b - a) for a, b in zip(offs[:-1], offs[1:])])
+    t = oracle.query_temperature(sigma, pos, offs)
+    first = np.isin(np.arange(m), offs[:-1])
+    np.testing.assert_allclose(t[~first], np.broadcast_to(oracle.softplus(sigma), (m - 3, hq)), rtol=1e-14)
+    o = oracle.gated_attention(q, k, v, s, t, gain, offs)
+    np.testing.assert_allclose(o, oracle.gated_attention(q, k, v, s, oracle.softplus(sigma), gain, offs),
+                               rtol=1e-13, atol=1e-13)
+
+
+@pytest.mark.parametrize("g", [0.0, 1.0])
+def test_query_temperature_worked_example(g):
+    """Three kept tokens at original positions 0, 3, 7 (1 head, D = 1), with
+    softplus(sigma) = 2, q = 1, k = [0, ln2, 0], v = [6, 0, 3], s = [0, 0, ln2].
+    Worked by hand: tau = [0, 2 ln2/ln4, 2 ln3/ln8] = [0, 1, (2/3) log2 3], so
+    row 1 weighs exp([0, ln2]) = [1, 2]; row 2 weighs [1, 2^tau_2, 2^g] with
+    2^tau_2 = 3^(2/3) (the bias is not scaled by the temperature)."""
+    sigma = np.array([math.log(math.expm1(2.0))])
+    pos = np.array([0, 3, 7])
+    t = oracle.query_temperature(sigma, pos, [0, 3])
+    np.testing.assert_allclose(t[:, 0], [0.0, 1.0, 2.0 * math.log(3.0) / math.log(8.0)], rtol=1e-14)
+    q = np.ones((3, 1, 1))
+    k = np.array([0.0, LN2, 0.0]).reshape(3, 1, 1)
+    v = np.array([6.0, 0.0, 3.0]).reshape(3, 1, 1)
+    s = np.array([0.0, 0.0, LN2])
+    o = oracle.gated_attention(q, k, v, s, t, np.array([g]), [0, 3])[:, 0, 0]
+    c = 3.0 ** (2.0 / 3.0)
+    w2 = 2.0 ** g
+    np.testing.assert_allclose(o, [6.0, 2.0, (6.0 + 3.0 * w2) / (1.0 + c + w2)], rtol=1e-13)
+
+
+def test_query_temperature_vanishing_leaves_the_bias_softmax():
+    """softplus(sigma) -> 0: the logits reduce to the gate bias, so each row is
+    the causal softmax(g s)-weighted mean of v, whatever q and k are."""
+    rng = np.random.default_rng(12)
+    m, d = 14, 4
+    q, k, v = (rng.standard_normal((m, 1, d)) * 5 for _ in range(3))
+    s = rng.standard_normal(m)
+    pos = np.sort(rng.choice(100, m, replace=False))
+    t = oracle.query_temperature(np.array([-80.0]), pos, [0, m])
+    o = oracle.gated_attention(q, k, v, s, t, np.array([1.3]), [0, m])
+    for r in range(m):
+        w = [math.exp(1.3 * s[j]) for j in range(r + 1)]
+        want = sum(w[j] * v[j, 0] for j in range(r + 1)) / sum(w)
+        np.testing.assert_allclose(o[r, 0], want, rtol=1e-12)
