@@ -43,8 +43,9 @@ def log(*a):
 class Pipeline:
     """Device-resident inputs, outputs and workspaces of one gated layer."""
 
-    def __init__(self, layer, k_budget, torch, tg, gather=False):
-        self.torch, self.tg, self.gather = torch, tg, gather
+    def __init__(self, layer, k_budget, torch, tg, gather=False, query_tau=False):
+        assert not (gather and query_tau)
+        self.torch, self.tg, self.gather, self.query_tau = torch, tg, gather, query_tau
         dev = torch.device("cuda")
         seg = layer.segments.with_budget(k_budget)
         self.layer, self.seg = layer, seg
@@ -76,6 +77,14 @@ class Pipeline:
         self.pairs = ([(self.x, self.hc), (self.scores, self.sc)] if gather else
                       [(self.x, self.hc), (self.q, self.qc), (self.k, self.kc), (self.v, self.vc),
                        (self.scores, self.sc)])
+        if query_tau:
+            # per-query temperature with softplus(sigma_h) = tau_h; the original positions of the kept
+            # rows are compacted with the other rows
+            self.sigma = f32(np.log(np.expm1(layer.tau.astype(np.float64))))
+            self.pos = torch.from_numpy(np.concatenate(
+                [np.arange(seg.seg_len(i), dtype=np.int32) for i in range(seg.n_seg)])).to(dev)
+            self.pc = torch.empty(m, dtype=torch.int32, device=dev)
+            self.pairs.append((self.pos, self.pc))
 
     def stages(self):
         tg = self.tg
@@ -87,6 +96,9 @@ class Pipeline:
             ("attention", (lambda: tg.gated_attention_prefill_gather(
                 self.q, self.k, self.v, self.scores, self.tau, self.gain, self.plan, self.kept, out=self.out))
              if self.gather else
+             (lambda: tg.gated_attention_prefill_query_tau(self.qc, self.kc, self.vc, self.sc, self.sigma, self.gain,
+                                                           self.pc, self.plan, out=self.out))
+             if self.query_tau else
              (lambda: tg.gated_attention_prefill(self.qc, self.kc, self.vc, self.sc, self.tau, self.gain, self.plan,
                                                  out=self.out))),
         ]
@@ -104,7 +116,8 @@ class Pipeline:
 
     def compact_row_bytes(self):
         L = self.layer
-        return 2 * L.d + 4 + (0 if self.gather else 2 * L.hq * L.head_dim + 2 * 2 * L.hkv * L.head_dim)
+        return (2 * L.d + 4 + (0 if self.gather else 2 * L.hq * L.head_dim + 2 * 2 * L.hkv * L.head_dim)
+                + (4 if self.query_tau else 0))
 
     def select_compact_bytes(self):
         return 4 * self.seg.n_doc(0) + 4 * self.m + 4 * self.m + 2 * self.m * self.compact_row_bytes()
@@ -380,6 +393,11 @@ def main():
         us_gather = time_graph(p16g, args.steps, args.warmup)
         log("16K: graph replay, attention gathering Q/K/V", f"{us_gather:.1f} us/step")
         del p16g
+        p16t = Pipeline(l16, 2048, torch, tg, query_tau=True)
+        us_qtau = time_graph(p16t, args.steps, args.warmup)
+        _, _, st16t = time_pipeline(p16t, args.steps, args.warmup)
+        log("16K: graph replay, per-query temperature", f"{us_qtau:.1f} us/step", st16t)
+        del p16t
         roofs = stage_rooflines(p16, st16, csrc)
         dominant = max(st16, key=st16.get)
         sc_gbs = p16.select_compact_bytes() / ((st16["select"] + st16["compact"]) * 1e-6) / 1e9
@@ -406,6 +424,8 @@ def main():
             "gpu_us_per_step_events": round(us_gpu, 2),
             "eager_us_per_step": round(us_eager, 2),
             "gather_on_load_us_per_step": round(us_gather, 2),
+            "query_tau": {"us_per_step": round(us_qtau, 2), "attention_us": round(st16t["attention"], 2),
+                          "note": "tau_rh = softplus(sigma_h) log(rank) / log(max(2, position)), graph replay"},
             "attention": {"tflops": roofs["attention"]["achieved"], "frac_mfma_peak": roofs["attention"]["frac"]},
             "select_plus_compact": {"gbs": sc_gbs, "frac_hbm_peak": sc_gbs / HBM_PEAK_GBS},
         }
@@ -434,7 +454,23 @@ def main():
             "stage_rooflines": stage_rooflines(p128, st128, csrc),
             "peak_device_mem_gib": torch.cuda.max_memory_allocated() / 2 ** 30,
         }
-        del p128, l128
+        del p128
+        torch.cuda.empty_cache()
+        # the long-context configuration's own budget, K = 4096 (M = 4160 kept)
+        torch.cuda.reset_peak_memory_stats()
+        p128k = Pipeline(l128, 4096, torch, tg)
+        us_eager4k, _, st4k = time_pipeline(p128k, steps, max(3, args.warmup // 4))
+        us_wall4k = time_graph(p128k, steps, max(3, args.warmup // 4))
+        log("128K, K=4096: eager", f"{us_eager4k:.1f} us/step, graph replay {us_wall4k:.1f} us/step", st4k)
+        long_rec4k = {
+            "workload": "gated layer N=131072 (131008 doc + 64 question), d=2048, K=4096 (M=4160 kept)",
+            "tokens_per_s": p128k.n / (us_wall4k * 1e-6), "ms_per_step": us_wall4k / 1e3, "steps": steps,
+            "eager_us_per_step": round(us_eager4k, 2), "launch": "one HIP graph per step",
+            "stages_us": {k: round(v, 2) for k, v in st4k.items()},
+            "stage_rooflines": stage_rooflines(p128k, st4k, csrc),
+            "peak_device_mem_gib": torch.cuda.max_memory_allocated() / 2 ** 30,
+        }
+        del p128k, l128
         torch.cuda.empty_cache()
         if result is None:
             result = {"metric": METRIC, "value": long_rec["tokens_per_s"], "unit": "tokens/s", "n_gpus": 1,
@@ -442,6 +478,7 @@ def main():
                       "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
                       "data": "synthetic", "config": {"workload": long_rec["workload"]}}
         result["n131072_k2048"] = long_rec
+        result["n131072_k4096"] = long_rec4k
 
     if not args.no_stack:
         log("timing the 28-layer pruned stack at N=65536")

@@ -230,6 +230,26 @@ int tg_gated_attention_prefill_gather(const void* q, const void* k, const void* 
                                       const tg_plan_info* info, int hq, int hkv, int head_dim,
                                       const int32_t* kept_idx, int64_t n_src_rows, void* out, void* stream);
 
+/* The same attention with a temperature per query row ([reading] section 4.1
+ * component two, second refinement: pruning shrinks the keys a query sees
+ * from its original position to its rank among the kept tokens, and a
+ * learnable temperature recalibrates the sharpened softmax).  For kept row r
+ * (0-based inside its prompt) with original 0-based position positions[r]:
+ *   tau_rh = softplus(sigma_h) * log(r + 1) / log(max(2, positions[r] + 1))
+ *   z_rt = tau_rh * (q_r . k_t) / sqrt(head_dim) + gain_h * s_t
+ * (the bias is not scaled by the temperature).
+ *   sigma     fp32 [hq] (device, required): softplus(sigma_h) is the head's scale
+ *   positions int32 [total_kept] (device): original position of every kept row
+ *             inside its prompt, in kept order (what tg_compact_kept makes of
+ *             the per-token positions); a value below 1 counts as 1
+ * Everything else, the precision and the supported shapes are as for
+ * tg_gated_attention_prefill.  NULL sigma, or NULL positions with kept rows,
+ * is TG_ERR_INVALID_ARG. */
+int tg_gated_attention_prefill_query_tau(const void* q, const void* k, const void* v, const float* key_score,
+                                         const float* sigma, const float* gain, const int32_t* positions,
+                                         const tg_segment* segs, const tg_plan_info* info, int hq, int hkv,
+                                         int head_dim, void* out, void* stream);
+
 /* ------------------------------------------------------------------------ */
 /* (5) Dense decoder-layer support (the layers below and above the gate)    */
 /* ------------------------------------------------------------------------ */

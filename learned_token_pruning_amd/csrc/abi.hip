@@ -190,7 +190,29 @@ int tg_gated_attention_prefill(const void* q, const void* k, const void* v, cons
   st = check_device();
   if (st != TG_OK) return st;
   return hip_status(tg::launch_gated_attention(q, k, v, key_score, tau, gain, segs, *info, hq, hkv, head_dim,
-                                               nullptr, 0, out, reinterpret_cast<hipStream_t>(stream)));
+                                               nullptr, 0, nullptr, out, reinterpret_cast<hipStream_t>(stream)));
+}
+
+int tg_gated_attention_prefill_query_tau(const void* q, const void* k, const void* v, const float* key_score,
+                                         const float* sigma, const float* gain, const int32_t* positions,
+                                         const tg_segment* segs, const tg_plan_info* info, int hq, int hkv,
+                                         int head_dim, void* out, void* stream) {
+  int st = check_info(segs, info);
+  if (st != TG_OK) return st;
+  if (hq <= 0 || hkv <= 0 || head_dim <= 0 || !sigma) return TG_ERR_INVALID_ARG;
+  if (info->total_kept > 0 && (!q || !k || !v || !out || !positions)) return TG_ERR_INVALID_ARG;
+  if (hq % hkv != 0) return TG_ERR_UNSUPPORTED;
+  const int G = hq / hkv;
+  if (!(head_dim == 64 || head_dim == 128) || !(G == 1 || G == 2 || G == 4)) return TG_ERR_UNSUPPORTED;
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(out, 16)) return TG_ERR_INVALID_ARG;
+  if ((key_score && !aligned(key_score, 4)) || !aligned(sigma, 4) || (gain && !aligned(gain, 4)) ||
+      (positions && !aligned(positions, 4)))
+    return TG_ERR_INVALID_ARG;
+  if (info->total_kept == 0) return TG_OK;
+  st = check_device();
+  if (st != TG_OK) return st;
+  return hip_status(tg::launch_gated_attention(q, k, v, key_score, sigma, gain, segs, *info, hq, hkv, head_dim,
+                                               nullptr, 0, positions, out, reinterpret_cast<hipStream_t>(stream)));
 }
 
 int tg_gated_attention_prefill_gather(const void* q, const void* k, const void* v, const float* key_score,
@@ -216,7 +238,8 @@ int tg_gated_attention_prefill_gather(const void* q, const void* k, const void* 
   st = check_device();
   if (st != TG_OK) return st;
   return hip_status(tg::launch_gated_attention(q, k, v, key_score, tau, gain, segs, *info, hq, hkv, head_dim,
-                                               kept_idx, n_src_rows, out, reinterpret_cast<hipStream_t>(stream)));
+                                               kept_idx, n_src_rows, nullptr, out,
+                                               reinterpret_cast<hipStream_t>(stream)));
 }
 
 int tg_gemm_bf16(int epilogue, const void* x, int64_t ldx, const void* w, int64_t ldw, int64_t m, int n, int k,
@@ -330,7 +353,7 @@ int tg_decoder_layer(void* hidden, const int32_t* positions, const float* key_sc
   TG_TRY(tg::launch_gemm(0, xn, d, w->wqkv, d, m, nqkv, d, nullptr, 0, qkv, nqkv, s));
   TG_TRY(tg::launch_rope_split(qkv, nqkv, m, hq, hkv, head_dim, positions, rope_theta, q, k, v, s));
   TG_TRY(tg::launch_gated_attention(q, k, v, key_score, w->tau, w->gain, segs, *info, hq, hkv, head_dim, nullptr, 0,
-                                    att, s));
+                                    nullptr, att, s));
   TG_TRY(tg::launch_gemm(1, att, (int64_t)hq * head_dim, w->wo, (int64_t)hq * head_dim, m, d, hq * head_dim, hidden,
                          d, hidden, d, s));
   TG_TRY(tg::launch_rmsnorm(hidden, d, m, d, w->mlp_norm, rms_eps, hn, d, s));

@@ -102,7 +102,7 @@ hipError_t launch_compact(const int32_t* kept_idx, int64_t n_kept, int64_t n_src
 hipError_t launch_gated_attention(const void* q, const void* k, const void* v, const float* key_score,
                                   const float* tau, const float* gain, const tg_segment* segs,
                                   const tg_plan_info& info, int hq, int hkv, int head_dim, const int32_t* kept_idx,
-                                  int64_t n_src, void* out, hipStream_t stream);
+                                  int64_t n_src, const int32_t* qpos, void* out, hipStream_t stream);
 constexpr int64_t kAttnMaxGatherRows = 16384;
 
 hipError_t launch_gemm(int epi, const void* x, int64_t ldx, const void* w, int64_t ldw, int64_t m, int n, int k,

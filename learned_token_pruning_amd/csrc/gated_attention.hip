@@ -37,6 +37,12 @@
 // the softmax needs one FMA and one exp2 per element.  The row sum is taken
 // over the bf16-rounded probabilities (the values the PV product uses).
 // Tiles are launched longest-first (the last query tile of a prompt first).
+//
+// Per-query temperature (same section, second refinement): the temperature of
+// kept row r can instead be softplus(sigma_h) log(m_r) / log(max(2, p_r)),
+// with m_r = r + 1 its rank among the prompt's kept rows and p_r = 1 + its
+// original position.  The lane owning row r then has its own c_r, the staged
+// bias is g_h log2(e) s_t, and the accumulator seed is that times 1 / c_r.
 #include <type_traits>
 
 #include "common.h"
@@ -92,6 +98,10 @@ struct Stager {
 // Gathered rows: kept row r of the prompt is source row sidx[r]; rows at or
 // past `nvalid` get an offset past every buffer range, so they read as zeros.
 constexpr uint32_t kPastRange = 0xfffffff0u;
+
+// Kernel variants: compacted rows (per-head temperature), gather on load, and
+// compacted rows with the per-query temperature.
+enum AttnMode { kCompacted = 0, kGather = 1, kQueryTau = 2 };
 
 template <int D, bool GATHER>
 __device__ __forceinline__ void load_k(const Stager<D>& st, __amdgpu_buffer_rsrc_t rk, __amdgpu_buffer_rsrc_t rs,
@@ -178,15 +188,18 @@ __device__ __forceinline__ void sched_reads_ahead() {
   for (int i = 0; i < MFMAS - (READS - AHEAD); ++i) __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
 }
 
-// GATHER: q, k, v and key_score hold every token (n_src rows); kept row r of
+// kGather: q, k, v and key_score hold every token (n_src rows); kept row r of
 // a prompt is read from source row kept_idx[kept_start + r] (gather on load,
 // no compacted copies).  The output is always compacted.
-template <int D, int G, bool GATHER>
+// kQueryTau: tau holds sigma_h and qpos the original positions of the kept rows.
+template <int D, int G, int MODE>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void gated_attention_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
     const float* __restrict__ key_score, const float* __restrict__ tau, const float* __restrict__ gain,
     const tg_segment* __restrict__ segs, int hq, int hkv, const int32_t* __restrict__ kept_idx, int64_t n_src,
-    uint16_t* __restrict__ out) {
+    const int32_t* __restrict__ qpos, uint16_t* __restrict__ out) {
+  constexpr bool GATHER = MODE == kGather;
+  constexpr bool QTAU = MODE == kQueryTau;
   constexpr int kBM = 128 / G;  // query rows per workgroup
   constexpr int kWavesPerHead = 4 / G;
   __shared__ AttnSmem<D> sm;
@@ -237,10 +250,20 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
 #pragma unroll
   for (int hh = 0; hh < G; ++hh) {
     const float th = tau != nullptr ? tau[c * G + hh] : 1.0f;
-    ratio[hh] = use_bias ? gain[c * G + hh] * kLog2e / __builtin_fmaxf(__builtin_fabsf(th) * base, 1e-30f) : 0.0f;
+    ratio[hh] = !use_bias ? 0.0f
+                : QTAU    ? gain[c * G + hh] * kLog2e
+                          : gain[c * G + hh] * kLog2e / __builtin_fmaxf(__builtin_fabsf(th) * base, 1e-30f);
   }
-  const float th = tau != nullptr ? tau[h] : 1.0f;
+  float th = tau != nullptr ? tau[h] : 1.0f;
+  if (QTAU) {
+    // tau_r = softplus(sigma_h) log(r + 1) / log(max(2, p_r + 1)) for this lane's row r (>= 0)
+    const int r = qrow < n ? qrow : n - 1;
+    const float sp = th > 20.0f ? th : log1pf(expf(th));
+    const float pr = (float)max(2, qpos[seg.kept_start + r] + 1);
+    th = sp * (logf((float)(r + 1)) / logf(pr));
+  }
   const float cs = __builtin_fmaxf(__builtin_fabsf(th) * base, 1e-30f);
+  const float inv_cs = QTAU ? 1.0f / cs : 1.0f;
 
   // Q^T operand: lane holds q[qrow][16 ks + 8 g .. + 7]
   u32x4 qf[D / 16];
@@ -331,7 +354,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
           for (int q4 = 0; q4 < 4; ++q4) {
             const f32x4 bv = *reinterpret_cast<const f32x4*>(&bias[hf * 32 + 8 * q4 + 4 * g]);
 #pragma unroll
-            for (int e = 0; e < 4; ++e) sa[hf][4 * q4 + e] = bv[e];
+            for (int e = 0; e < 4; ++e) sa[hf][4 * q4 + e] = QTAU ? bv[e] * inv_cs : bv[e];
           }
         const uint16_t* krow0 = &sm.k[jq & 1][l32 * AttnSmem<D>::kLd + 8 * g];
         const uint16_t* krow1 = krow0 + 32 * AttnSmem<D>::kLd;
@@ -451,21 +474,24 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
 template <int D, int G>
 hipError_t launch_dg(const void* q, const void* k, const void* v, const float* ks, const float* tau,
                      const float* gain, const tg_segment* segs, const tg_plan_info& info, int hq, int hkv,
-                     const int32_t* kept_idx, int64_t n_src, void* out, hipStream_t stream) {
+                     const int32_t* kept_idx, int64_t n_src, const int32_t* qpos, void* out, hipStream_t stream) {
   constexpr int kBM = 128 / G;
   const int ntiles = (info.max_kept_len + kBM - 1) / kBM;
   if (ntiles == 0) return hipSuccess;
   dim3 grid(hkv, ntiles, info.n_seg);
+  auto* qb = reinterpret_cast<const uint16_t*>(q);
+  auto* kb = reinterpret_cast<const uint16_t*>(k);
+  auto* vb = reinterpret_cast<const uint16_t*>(v);
+  auto* ob = reinterpret_cast<uint16_t*>(out);
   if (kept_idx != nullptr)
-    hipLaunchKernelGGL((gated_attention_kernel<D, G, true>), grid, dim3(kThreads), 0, stream,
-                       reinterpret_cast<const uint16_t*>(q), reinterpret_cast<const uint16_t*>(k),
-                       reinterpret_cast<const uint16_t*>(v), ks, tau, gain, segs, hq, hkv, kept_idx, n_src,
-                       reinterpret_cast<uint16_t*>(out));
+    hipLaunchKernelGGL((gated_attention_kernel<D, G, kGather>), grid, dim3(kThreads), 0, stream, qb, kb, vb, ks, tau,
+                       gain, segs, hq, hkv, kept_idx, n_src, nullptr, ob);
+  else if (qpos != nullptr)
+    hipLaunchKernelGGL((gated_attention_kernel<D, G, kQueryTau>), grid, dim3(kThreads), 0, stream, qb, kb, vb, ks,
+                       tau, gain, segs, hq, hkv, nullptr, (int64_t)0, qpos, ob);
   else
-    hipLaunchKernelGGL((gated_attention_kernel<D, G, false>), grid, dim3(kThreads), 0, stream,
-                       reinterpret_cast<const uint16_t*>(q), reinterpret_cast<const uint16_t*>(k),
-                       reinterpret_cast<const uint16_t*>(v), ks, tau, gain, segs, hq, hkv, nullptr, (int64_t)0,
-                       reinterpret_cast<uint16_t*>(out));
+    hipLaunchKernelGGL((gated_attention_kernel<D, G, kCompacted>), grid, dim3(kThreads), 0, stream, qb, kb, vb, ks,
+                       tau, gain, segs, hq, hkv, nullptr, (int64_t)0, nullptr, ob);
   return hipGetLastError();
 }
 
@@ -474,11 +500,11 @@ hipError_t launch_dg(const void* q, const void* k, const void* v, const float* k
 hipError_t launch_gated_attention(const void* q, const void* k, const void* v, const float* key_score,
                                   const float* tau, const float* gain, const tg_segment* segs,
                                   const tg_plan_info& info, int hq, int hkv, int head_dim, const int32_t* kept_idx,
-                                  int64_t n_src, void* out, hipStream_t stream) {
+                                  int64_t n_src, const int32_t* qpos, void* out, hipStream_t stream) {
   const int G = hq / hkv;
 #define TG_ATTN_CASE(DD, GG) \
   if (head_dim == DD && G == GG) \
-    return launch_dg<DD, GG>(q, k, v, key_score, tau, gain, segs, info, hq, hkv, kept_idx, n_src, out, stream);
+    return launch_dg<DD, GG>(q, k, v, key_score, tau, gain, segs, info, hq, hkv, kept_idx, n_src, qpos, out, stream);
   TG_ATTN_CASE(128, 1)
   TG_ATTN_CASE(128, 2)
   TG_ATTN_CASE(128, 4)

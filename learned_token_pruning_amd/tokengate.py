@@ -31,7 +31,7 @@ STATUS_NAMES = {0: "TG_OK", -1: "TG_ERR_INVALID_ARG", -2: "TG_ERR_UNSUPPORTED", 
                 -4: "TG_ERR_NO_DEVICE", -5: "TG_ERR_HIP"}
 EXPORTS = ("tg_status_string", "tg_abi_version", "tg_plan_segments", "tg_gate_workspace_bytes", "tg_gate_score",
            "tg_select_workspace_bytes", "tg_select_topk", "tg_compact_kept", "tg_gated_attention_prefill",
-           "tg_gated_attention_prefill_gather",
+           "tg_gated_attention_prefill_gather", "tg_gated_attention_prefill_query_tau",
            "tg_gemm_bf16", "tg_rmsnorm_bf16", "tg_rope_split_bf16", "tg_decoder_layer_workspace_bytes",
            "tg_decoder_layer")
 GEMM_STORE, GEMM_RESIDUAL, GEMM_SWIGLU = 0, 1, 2
@@ -87,6 +87,9 @@ _lib.tg_compact_kept.argtypes = [_vp, _i64, _i64, _i32, ctypes.POINTER(_vp), cty
 _lib.tg_gated_attention_prefill_gather.restype = _i32
 _lib.tg_gated_attention_prefill_gather.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, ctypes.POINTER(PlanInfo), _i32,
                                                    _i32, _i32, _vp, _i64, _vp, _vp]
+_lib.tg_gated_attention_prefill_query_tau.restype = _i32
+_lib.tg_gated_attention_prefill_query_tau.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, ctypes.POINTER(PlanInfo),
+                                                      _i32, _i32, _i32, _vp, _vp]
 _lib.tg_gated_attention_prefill.restype = _i32
 _lib.tg_gated_attention_prefill.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, ctypes.POINTER(PlanInfo), _i32, _i32,
                                             _i32, _vp, _vp]
@@ -289,6 +292,23 @@ def gated_attention_prefill_gather(q: torch.Tensor, k: torch.Tensor, v: torch.Te
                                                 _dev_table(plan), ctypes.byref(plan.info), hq, hkv, dh,
                                                 _ptr(kept_idx), n_src, _ptr(out), _stream(stream))
     _check(st, "tg_gated_attention_prefill_gather")
+    return out
+
+
+def gated_attention_prefill_query_tau(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
+                                      key_score: Optional[torch.Tensor], sigma: torch.Tensor,
+                                      gain: Optional[torch.Tensor], positions: torch.Tensor, plan: Plan,
+                                      out: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """tg_gated_attention_prefill_query_tau.  As gated_attention_prefill, with
+    sigma fp32 [hq] and positions int32 [M] (original positions of the kept rows)."""
+    m, hq, dh = q.shape
+    hkv = k.shape[1]
+    if out is None:
+        out = torch.empty_like(q)
+    st = _lib.tg_gated_attention_prefill_query_tau(_ptr(q), _ptr(k), _ptr(v), _ptr(key_score), _ptr(sigma),
+                                                   _ptr(gain), _ptr(positions), _dev_table(plan),
+                                                   ctypes.byref(plan.info), hq, hkv, dh, _ptr(out), _stream(stream))
+    _check(st, "tg_gated_attention_prefill_query_tau")
     return out
 
 

@@ -158,6 +158,20 @@ def test_attention_gather_validation():
              None) == -2
 
 
+def test_attention_query_tau_validation():
+    p = _plan()
+    info = ctypes.byref(p.info)
+    f = L.tg_gated_attention_prefill_query_tau
+    assert f(FAKE, FAKE, FAKE, None, None, None, FAKE, FAKE, info, 16, 8, 128, FAKE, None) == -1  # no sigma
+    assert f(FAKE, FAKE, FAKE, None, FAKE, None, None, FAKE, info, 16, 8, 128, FAKE, None) == -1  # no positions
+    assert f(FAKE, FAKE, FAKE, None, FAKE, None, ctypes.c_void_p(0x10002), FAKE, info, 16, 8, 128, FAKE,
+             None) == -1  # misaligned positions
+    assert f(FAKE, FAKE, FAKE, None, FAKE, None, FAKE, FAKE, info, 16, 8, 96, FAKE, None) == -2
+    assert f(FAKE, FAKE, FAKE, None, FAKE, None, FAKE, FAKE, info, 16, 2, 128, FAKE, None) == -2
+    empty = tg.plan_segments([0, 0], [0], [0], [0])
+    assert f(None, None, None, None, FAKE, None, None, FAKE, ctypes.byref(empty.info), 16, 8, 128, None, None) == 0
+
+
 @pytest.mark.skipif(gpu_available(), reason="only meaningful without a GPU: valid calls must report no device")
 def test_valid_calls_report_no_device_without_gpu():
     p = _plan()
@@ -166,6 +180,8 @@ def test_valid_calls_report_no_device_without_gpu():
     assert L.tg_gate_score(FAKE, 2048, 2048, FAKE, None, FAKE, 0.0, 256, FAKE, info, 1e-6, FAKE, FAKE, ws, None) == -4
     assert L.tg_select_topk(FAKE, FAKE, info, FAKE, FAKE, tg.select_workspace_bytes(p), None) == -4
     assert L.tg_gated_attention_prefill(FAKE, FAKE, FAKE, None, None, None, FAKE, info, 16, 8, 128, FAKE, None) == -4
+    assert L.tg_gated_attention_prefill_query_tau(FAKE, FAKE, FAKE, None, FAKE, None, FAKE, FAKE, info, 16, 8, 128,
+                                                  FAKE, None) == -4
 
 
 def test_dense_validation():

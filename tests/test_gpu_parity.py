@@ -381,6 +381,87 @@ def test_attention_gather_equals_compacted(d, hq, hkv, lens):
                     rows=np.unique(ref_rows))
 
 
+def run_attention_query_tau(q, k, v, s, sigma, gain, pos, offs, use_bias=True):
+    import torch
+    tg = _tg()
+    n_seg = len(offs) - 1
+    plan = tg.plan_segments(list(offs), [0] * n_seg, [0] * n_seg, [0] * n_seg, device="cuda")
+    out = tg.gated_attention_prefill_query_tau(dev_bf16(q), dev_bf16(k), dev_bf16(v),
+                                               dev_f32(s) if use_bias else None, dev_f32(sigma),
+                                               dev_f32(gain) if use_bias else None,
+                                               torch.from_numpy(np.asarray(pos, dtype=np.int32)).cuda(), plan)
+    return W.bf16_bits_to_f64(host_bf16(out))
+
+
+def check_attention_query_tau(got, q, k, v, s, sigma, gain, pos, offs, rows=None, use_bias=True):
+    tau = oracle.query_temperature(np.asarray(sigma, dtype=np.float64), pos, offs)
+    ref = oracle.gated_attention(f64(q), f64(k), f64(v), s.astype(np.float64) if use_bias else None, tau,
+                                 gain.astype(np.float64) if use_bias else None, offs, rows=rows)
+    g = got if rows is None else got[rows]
+    err = np.abs(g - ref).max()
+    assert err <= ATTN_ATOL, f"max abs err {err:.3e}"
+    return err
+
+
+def kept_positions(rng, lens, keep_all=()):
+    """Original positions of the kept rows of each prompt: a sorted random
+    subset of a prompt about four times longer (all of it for prompts listed
+    in keep_all)."""
+    out = []
+    for i, n in enumerate(lens):
+        if i in keep_all:
+            out.append(np.arange(n))
+        else:
+            out.append(np.sort(rng.choice(4 * n + 3, n, replace=False)))
+    return np.concatenate(out).astype(np.int64) if out else np.zeros(0, np.int64)
+
+
+@pytest.mark.parametrize("d,hq,hkv", [(64, 4, 2), (64, 8, 2), (128, 2, 2), (128, 16, 8), (128, 16, 4)])
+def test_attention_query_tau_ragged(d, hq, hkv):
+    _say("attention query tau ragged", d, hq, hkv)
+    rng = np.random.default_rng(d + 7 * hq + hkv)
+    lens = [1, 63, 64, 65, 130, 0, 257]
+    offs = np.concatenate([[0], np.cumsum(lens)])
+    m = int(offs[-1])
+    q = W.f32_to_bf16_bits(rng.standard_normal((m, hq, d)).astype(np.float32))
+    k = W.f32_to_bf16_bits(rng.standard_normal((m, hkv, d)).astype(np.float32))
+    v = W.f32_to_bf16_bits(rng.standard_normal((m, hkv, d)).astype(np.float32))
+    s = rng.standard_normal(m).astype(np.float32)
+    sigma = rng.uniform(-1.0, 1.5, hq).astype(np.float32)
+    sigma[0] = -40.0  # softplus ~ 4e-18: the bias alone
+    if hq > 2:
+        sigma[1] = 25.0  # the large-sigma branch of softplus
+    gain = rng.uniform(0.5, 1.5, hq).astype(np.float32)
+    pos = kept_positions(rng, lens, keep_all=(4,))
+    got = run_attention_query_tau(q, k, v, s, sigma, gain, pos, offs)
+    check_attention_query_tau(got, q, k, v, s, sigma, gain, pos, offs)
+    got = run_attention_query_tau(q, k, v, s, sigma, gain, pos, offs, use_bias=False)
+    check_attention_query_tau(got, q, k, v, s, sigma, gain, pos, offs, use_bias=False)
+
+
+@pytest.mark.parametrize("idx,kb", [(2, 2048), (3, 8192)])
+def test_attention_query_tau_workloads(idx, kb):
+    """The kept rows of workloads 2 and 3 with their true original positions;
+    every row of workload 2 (M = 2112), sampled rows of workload 3 (M = 8256)."""
+    _say("attention query tau workload", idx, kb)
+    L = layer(idx)
+    s = W.mixture_scores(idx, L.segments, k_marks=(1024, 2048, 4096, 8192))
+    seg = L.segments.with_budget(kb)
+    kept, offs = oracle.kept_indices(s, seg.seg_start, seg.doc_begin, seg.doc_end, seg.k_budget)
+    starts = np.repeat(np.asarray(seg.seg_start[:-1]), np.diff(offs))
+    pos = kept - starts
+    q, k, v = (oracle.compact_rows(t, kept) for t in (L.q, L.k, L.v))
+    sc = oracle.compact_rows(s, kept).astype(np.float32)
+    m = q.shape[0]
+    rng = np.random.default_rng(kb)
+    sigma = rng.uniform(-0.5, 1.0, L.tau.size).astype(np.float32)
+    got = run_attention_query_tau(q, k, v, sc, sigma, L.gain, pos, offs)
+    rows = None
+    if m > 4000:
+        rows = np.unique(np.concatenate([[0, 1, 63, 64, m - 65, m - 64, m - 2, m - 1], rng.integers(0, m, 120)]))
+    check_attention_query_tau(got, q, k, v, sc, sigma, L.gain, pos, offs, rows=rows)
+
+
 def test_attention_deterministic():
     _say("attention determinism")
     L = layer(1)
