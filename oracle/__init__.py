@@ -32,6 +32,7 @@ from .tokengate_ref import (  # noqa: F401
     gated_attention,
     softplus,
     query_temperature,
+    gated_attention_decode,
 )
 from .stack_ref import (  # noqa: F401,E402
     round_bf16,

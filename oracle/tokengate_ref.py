@@ -304,3 +304,46 @@ def query_temperature(sigma: np.ndarray, positions: np.ndarray, kept_offsets: Se
         m_rank[a:b] = np.arange(1, b - a + 1)
     p = np.maximum(2.0, positions.astype(np.float64) + 1.0)
     return softplus(sigma)[None, :] * (np.log(m_rank) / np.log(p))[:, None]
+
+
+def gated_attention_decode(q: np.ndarray, k_cache: np.ndarray, v_cache: np.ndarray, s: Optional[np.ndarray],
+                           tau: Optional[np.ndarray], gain: Optional[np.ndarray], lens: Sequence[int]) -> np.ndarray:
+    """One decode step of token-gated attention over a pruned KV cache
+    ([reading] §4.1 component one: pruned tokens leave no KV entry and the
+    tokens being decoded are not prunable, score 0; engineering notes: at
+    decode time the gate term becomes an additive attention mask).
+
+    Sequence b's new query q[b] (its own K/V already appended) attends to the
+    cache rows j < lens[b]:
+        z_j = tau_h (q_h . k_j) / sqrt(D) + g_h s_j,   out[b, h] = sum_j softmax_j(z) v_j
+    i.e. the additive mask is g_h s_j.  q [B, Hq, D]; k_cache / v_cache
+    [B, cap, Hkv, D]; s [B, cap] (0 for generated or question tokens) or None;
+    tau [Hq], [B, Hq] (a temperature per query) or None (= 1); gain [Hq] or
+    None.  An empty cache (lens[b] = 0) gives a zero output.
+    Pinned by row-by-row equality with the prefill oracle (causal attention is
+    decode applied to every prefix), a two-key closed form and the empty and
+    single-key cases.
+    """
+    q = np.asarray(q, dtype=np.float64)
+    k_cache = np.asarray(k_cache, dtype=np.float64)
+    v_cache = np.asarray(v_cache, dtype=np.float64)
+    bsz, hq, dh = q.shape
+    hkv = k_cache.shape[2]
+    group = hq // hkv
+    tau = np.ones(hq) if tau is None else np.asarray(tau, dtype=np.float64)
+    if tau.ndim == 1:
+        tau = np.broadcast_to(tau[None, :], (bsz, hq))
+    use_bias = s is not None and gain is not None
+    out = np.zeros((bsz, hq, dh), dtype=np.float64)
+    for b in range(bsz):
+        n = int(lens[b])
+        if n == 0:
+            continue
+        for h in range(hq):
+            c = h // group
+            z = tau[b, h] * (k_cache[b, :n, c, :] @ q[b, h, :]) / math.sqrt(dh)
+            if use_bias:
+                z = z + float(gain[h]) * np.asarray(s[b, :n], dtype=np.float64)
+            p = np.exp(z - z.max())
+            out[b, h, :] = (p / p.sum()) @ v_cache[b, :n, c, :]
+    return out

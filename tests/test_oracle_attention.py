@@ -190,3 +190,52 @@ def test_query_temperature_vanishing_leaves_the_bias_softmax():
         w = [math.exp(1.3 * s[j]) for j in range(r + 1)]
         want = sum(w[j] * v[j, 0] for j in range(r + 1)) / sum(w)
         np.testing.assert_allclose(o[r, 0], want, rtol=1e-12)
+
+
+# ----------------------------------------------------------------------------- decode
+
+
+def test_decode_equals_prefill_row_by_row():
+    """Causal prefill is decode applied to every prefix: row r of the prefill
+    oracle equals a decode step of q_r over the cache rows 0 .. r."""
+    rng = np.random.default_rng(21)
+    m, hq, hkv, d = 23, 4, 2, 8
+    q, k, v = (rng.standard_normal((m, h, d)) for h in (hq, hkv, hkv))
+    s = rng.standard_normal(m)
+    tau = rng.uniform(0.8, 1.2, hq)
+    gain = rng.uniform(0.5, 1.5, hq)
+    pre = oracle.gated_attention(q, k, v, s, tau, gain, [0, m])
+    cap = m + 5
+    kc = np.zeros((m, cap, hkv, d))
+    vc = np.zeros((m, cap, hkv, d))
+    sc = np.zeros((m, cap))
+    kc[:, :m], vc[:, :m], sc[:, :m] = k[None], v[None], s[None]
+    kc[:, m:] = 1e3  # rows past a sequence's length never count
+    dec = oracle.gated_attention_decode(q, kc, vc, sc, tau, gain, np.arange(1, m + 1))
+    np.testing.assert_allclose(dec, pre, rtol=1e-13, atol=1e-13)
+    # a per-query temperature row gives the same as the per-head form when it repeats tau
+    dec2 = oracle.gated_attention_decode(q, kc, vc, sc, np.tile(tau, (m, 1)), gain, np.arange(1, m + 1))
+    np.testing.assert_allclose(dec2, dec, rtol=1e-15)
+
+
+@pytest.mark.parametrize("g,want", [(0.0, (8.0 + 3 * 4.0) / 4), (1.0, (2 * 8.0 + 3 * 4.0) / 5)])
+def test_decode_two_key_closed_form(g, want):
+    """q = 1, D = 1, k = [0, ln 3], v = [8, 4], s = [ln 2, 0], tau = 1: by hand
+    the weights are [1, 3] / 4 without the gate and [2, 3] / 5 with g = 1."""
+    q = np.ones((1, 1, 1))
+    kc = np.array([0.0, math.log(3.0)]).reshape(1, 2, 1, 1)
+    vc = np.array([8.0, 4.0]).reshape(1, 2, 1, 1)
+    s = np.array([[LN2, 0.0]])
+    o = oracle.gated_attention_decode(q, kc, vc, s, np.array([1.0]), np.array([g]), [2])
+    assert o[0, 0, 0] == pytest.approx(want, rel=1e-14)
+
+
+def test_decode_empty_and_single_key():
+    rng = np.random.default_rng(22)
+    q = rng.standard_normal((3, 4, 8))
+    kc, vc = rng.standard_normal((2, 3, 5, 2, 8))
+    s = rng.standard_normal((3, 5))
+    o = oracle.gated_attention_decode(q, kc, vc, s, None, np.ones(4), [0, 1, 5])
+    assert np.all(o[0] == 0.0)
+    np.testing.assert_allclose(o[1], np.repeat(vc[1, 0], 2, axis=0), rtol=1e-15)
+    assert np.all(np.isfinite(o[2]))
