@@ -255,6 +255,51 @@ def stage_rooflines(pipe, st, csrc):
     }
 
 
+def time_decode(torch, tg, reps=200):
+    """One decode step of token-gated attention for 32 sequences whose 16K-token
+    prompts were pruned to K = 2048 (2112 kept rows + 1 generated row in the
+    cache), against the same step over the unpruned caches (16385 rows): 16 Q /
+    8 KV heads, head_dim 128, random bf16 caches, fp32 scores (0 on the
+    generated row).  Kernel time from events around `reps` back-to-back steps."""
+    dev = torch.device("cuda")
+    gen = torch.Generator(device=dev).manual_seed(77)
+    bsz, hq, hkv, dh = 32, 16, 8, 128
+    tau = 0.8 + 0.4 * torch.rand(hq, generator=gen, device=dev)
+    gain = 0.5 + torch.rand(hq, generator=gen, device=dev)
+    rec = {"workload": "decode step, 32 sequences, 16 Q / 8 KV heads, head_dim 128: pruned caches "
+                       "(16K prompt, K=2048: 2112 kept + 1 generated rows) vs unpruned caches (16385 rows)"}
+    for name, cap in (("pruned", 2113), ("full", 16385)):
+        q = torch.randn(bsz, hq, dh, generator=gen, device=dev).to(torch.bfloat16)
+        kc = torch.randn(bsz, cap, hkv, dh, generator=gen, device=dev).to(torch.bfloat16)
+        vc = torch.randn(bsz, cap, hkv, dh, generator=gen, device=dev).to(torch.bfloat16)
+        sc = torch.randn(bsz, cap, generator=gen, device=dev)
+        sc[:, -1] = 0.0
+        lens = torch.full((bsz,), cap, dtype=torch.int32, device=dev)
+        out = torch.empty_like(q)
+        ws = torch.empty(tg.decode_workspace_bytes(bsz, hq, dh, cap), dtype=torch.uint8, device=dev)
+        step = lambda: tg.gated_attention_decode(q, kc, vc, sc, tau, gain, lens, out=out, workspace=ws)
+        for _ in range(10):
+            step()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            step()
+        e1.record()
+        torch.cuda.synchronize()
+        us = e0.elapsed_time(e1) / reps * 1e3
+        nbytes = bsz * cap * (2 * hkv * dh * 2 + 4) + 2 * bsz * hq * dh * 2  # K, V, scores once; q and out
+        gbs = nbytes / (us * 1e-6) / 1e9
+        rec[name] = {"cache_rows": cap, "us_per_step": round(us, 2), "kv_gib": bsz * cap * 2 * hkv * dh * 2 / 2 ** 30,
+                     "roofline": {"kernel": "decode_partial_kernel<128,2> + decode_combine_kernel<128>",
+                                  "bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                                  "frac": gbs / HBM_PEAK_GBS, "traffic": None}}
+        del q, kc, vc, sc, ws
+        torch.cuda.empty_cache()
+    rec["speedup_pruned_vs_full"] = rec["full"]["us_per_step"] / rec["pruned"]["us_per_step"]
+    return rec
+
+
 STACK = dict(n=65536, n_q=64, k=4096, layers=28, gate_layer=12, d=2048, hq=16, hkv=8, dh=128, f=6144, h_gate=256)
 
 
@@ -349,6 +394,7 @@ def main():
     ap.add_argument("--only-long", action="store_true", help="time only the 128K-token layer (profiling)")
     ap.add_argument("--no-stack", action="store_true", help="skip the 28-layer pruned-stack prefill")
     ap.add_argument("--only-stack", action="store_true", help="time only the 28-layer pruned-stack prefill")
+    ap.add_argument("--no-decode", action="store_true", help="skip the decode-step timing")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="also run one plain 256 MiB device copy (reference for rocprofv3 FETCH_SIZE / WRITE_SIZE)")
     args = ap.parse_args()
@@ -380,6 +426,8 @@ def main():
     l16 = None
     if args.only_stack:
         args.only_long, args.no_long = True, True
+    if args.only_long:
+        args.no_decode = True
     if not args.only_long:
         log("generating the 16K-token workload")
         l16 = W.workload(2)
@@ -489,6 +537,11 @@ def main():
                       "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
                       "data": "synthetic", "config": {"workload": stack["workload"]}}
         result["stack_n65536_k4096"] = stack
+
+    if not args.no_decode and result is not None:
+        log("timing the decode step over pruned and unpruned caches")
+        result["decode_b32"] = time_decode(torch, tg)
+        log("decode", {k: v["us_per_step"] for k, v in result["decode_b32"].items() if isinstance(v, dict)})
 
     if not args.no_cpu_baseline and l16 is not None:
         log("timing the CPU oracle on the 16K workload")

@@ -251,6 +251,39 @@ int tg_gated_attention_prefill_query_tau(const void* q, const void* k, const voi
                                          int head_dim, void* out, void* stream);
 
 /* ------------------------------------------------------------------------ */
+/* (4b) Token-gated attention, one decode step over a pruned KV cache        */
+/* ------------------------------------------------------------------------ */
+
+/* [reading] section 4.1: pruned tokens leave no KV entry, and the tokens
+ * being generated are not prunable (score 0); the engineering notes of the
+ * same section fold the gate term into an additive attention mask at decode
+ * time.  Sequence b's new query attends to its cache rows j < lens[b] (its
+ * own K/V row appended by the caller beforehand):
+ *   z_j = tau_h * (q_h . k_j) / sqrt(head_dim) + gain_h * s_j
+ *   out[b, h] = sum_j softmax_j(z) v_j          (0 when lens[b] == 0)
+ *   q        bf16 [batch, hq, head_dim] (device)
+ *   k_cache, v_cache bf16 [batch, cache_rows, hkv, head_dim] (device, contiguous)
+ *   key_score fp32 [batch, cache_rows] (device) or NULL (no mask); 0 for
+ *             generated and question rows
+ *   tau      fp32 [hq] (tau_per_query = 0), [batch, hq] (tau_per_query = 1:
+ *            a temperature per query, e.g. the per-query form of
+ *            tg_gated_attention_prefill_query_tau evaluated on the host) or NULL (= 1)
+ *   gain     fp32 [hq] (device) or NULL (no mask)
+ *   lens     int32 [batch] (device): valid rows; values outside [0, cache_rows]
+ *            are clamped into it (no access outside the caches)
+ *   out      bf16 [batch, hq, head_dim] (device, out)
+ *   workspace: device, 16-byte aligned, >= tg_decode_workspace_bytes(...)
+ *            (split-KV partials; no state is kept between calls)
+ * fp32 arithmetic on bf16 inputs; the key scores must be finite.
+ * Supported: head_dim in {64, 128}, hq / hkv in {1, 2, 4}, batch and hkv at
+ * most 65535, cache_rows at most 65535 * 256 (else TG_ERR_UNSUPPORTED). */
+size_t tg_decode_workspace_bytes(int batch, int hq, int head_dim, int64_t cache_rows);
+int tg_gated_attention_decode(const void* q, const void* k_cache, const void* v_cache, const float* key_score,
+                              const float* tau, int tau_per_query, const float* gain, const int32_t* lens,
+                              int batch, int64_t cache_rows, int hq, int hkv, int head_dim, void* out,
+                              void* workspace, size_t workspace_bytes, void* stream);
+
+/* ------------------------------------------------------------------------ */
 /* (5) Dense decoder-layer support (the layers below and above the gate)    */
 /* ------------------------------------------------------------------------ */
 

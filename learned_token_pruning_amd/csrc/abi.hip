@@ -242,6 +242,37 @@ int tg_gated_attention_prefill_gather(const void* q, const void* k, const void* 
                                                reinterpret_cast<hipStream_t>(stream)));
 }
 
+size_t tg_decode_workspace_bytes(int batch, int hq, int head_dim, int64_t cache_rows) {
+  if (batch <= 0 || hq <= 0 || head_dim <= 0 || cache_rows < 0) return 0;
+  return tg::decode_workspace_bytes(batch, hq, head_dim, cache_rows);
+}
+
+int tg_gated_attention_decode(const void* q, const void* k_cache, const void* v_cache, const float* key_score,
+                              const float* tau, int tau_per_query, const float* gain, const int32_t* lens,
+                              int batch, int64_t cache_rows, int hq, int hkv, int head_dim, void* out,
+                              void* workspace, size_t workspace_bytes, void* stream) {
+  if (batch < 0 || hq <= 0 || hkv <= 0 || head_dim <= 0 || cache_rows < 0) return TG_ERR_INVALID_ARG;
+  if (tau_per_query != 0 && tau_per_query != 1) return TG_ERR_INVALID_ARG;
+  if (batch == 0) return TG_OK;
+  if (!q || !out || !lens || (cache_rows > 0 && (!k_cache || !v_cache))) return TG_ERR_INVALID_ARG;
+  if (hq % hkv != 0) return TG_ERR_UNSUPPORTED;
+  const int G = hq / hkv;
+  if (!(head_dim == 64 || head_dim == 128) || !(G == 1 || G == 2 || G == 4)) return TG_ERR_UNSUPPORTED;
+  if (batch > 65535 || hkv > 65535 || cache_rows > 65535LL * 256) return TG_ERR_UNSUPPORTED;
+  if (!aligned(q, 16) || !aligned(k_cache, 16) || !aligned(v_cache, 16) || !aligned(out, 16) ||
+      !aligned(lens, 4) || (key_score && !aligned(key_score, 4)) || (tau && !aligned(tau, 4)) ||
+      (gain && !aligned(gain, 4)))
+    return TG_ERR_INVALID_ARG;
+  if (!workspace || !aligned(workspace, 16) ||
+      workspace_bytes < tg::decode_workspace_bytes(batch, hq, head_dim, cache_rows))
+    return TG_ERR_WORKSPACE;
+  const int st = check_device();
+  if (st != TG_OK) return st;
+  return hip_status(tg::launch_gated_decode(q, k_cache, v_cache, key_score, tau, tau_per_query, gain, lens, batch,
+                                            cache_rows, hq, hkv, head_dim, out, workspace,
+                                            reinterpret_cast<hipStream_t>(stream)));
+}
+
 int tg_gemm_bf16(int epilogue, const void* x, int64_t ldx, const void* w, int64_t ldw, int64_t m, int n, int k,
                  const void* residual, int64_t ldr, void* y, int64_t ldy, void* stream) {
   if (epilogue < TG_GEMM_STORE || epilogue > TG_GEMM_SWIGLU || m < 0 || n <= 0 || k <= 0) return TG_ERR_INVALID_ARG;

@@ -105,6 +105,14 @@ hipError_t launch_gated_attention(const void* q, const void* k, const void* v, c
                                   int64_t n_src, const int32_t* qpos, void* out, hipStream_t stream);
 constexpr int64_t kAttnMaxGatherRows = 16384;
 
+// One decode step over per-sequence KV caches [batch, cap, hkv, head_dim];
+// the workspace holds the split-KV partials.
+size_t decode_workspace_bytes(int batch, int hq, int head_dim, int64_t cap);
+hipError_t launch_gated_decode(const void* q, const void* kc, const void* vc, const float* key_score,
+                               const float* tau, int tau_per_query, const float* gain, const int32_t* lens,
+                               int batch, int64_t cap, int hq, int hkv, int head_dim, void* out, void* workspace,
+                               hipStream_t stream);
+
 hipError_t launch_gemm(int epi, const void* x, int64_t ldx, const void* w, int64_t ldw, int64_t m, int n, int k,
                        const void* res, int64_t ldr, void* y, int64_t ldy, hipStream_t stream);
 hipError_t launch_rmsnorm(const void* x, int64_t ldx, int64_t m, int d, const void* weight, float eps, void* y,

@@ -32,6 +32,7 @@ STATUS_NAMES = {0: "TG_OK", -1: "TG_ERR_INVALID_ARG", -2: "TG_ERR_UNSUPPORTED", 
 EXPORTS = ("tg_status_string", "tg_abi_version", "tg_plan_segments", "tg_gate_workspace_bytes", "tg_gate_score",
            "tg_select_workspace_bytes", "tg_select_topk", "tg_compact_kept", "tg_gated_attention_prefill",
            "tg_gated_attention_prefill_gather", "tg_gated_attention_prefill_query_tau",
+           "tg_decode_workspace_bytes", "tg_gated_attention_decode",
            "tg_gemm_bf16", "tg_rmsnorm_bf16", "tg_rope_split_bf16", "tg_decoder_layer_workspace_bytes",
            "tg_decoder_layer")
 GEMM_STORE, GEMM_RESIDUAL, GEMM_SWIGLU = 0, 1, 2
@@ -90,6 +91,11 @@ _lib.tg_gated_attention_prefill_gather.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp,
 _lib.tg_gated_attention_prefill_query_tau.restype = _i32
 _lib.tg_gated_attention_prefill_query_tau.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, ctypes.POINTER(PlanInfo),
                                                       _i32, _i32, _i32, _vp, _vp]
+_lib.tg_decode_workspace_bytes.restype = _sz
+_lib.tg_decode_workspace_bytes.argtypes = [_i32, _i32, _i32, _i64]
+_lib.tg_gated_attention_decode.restype = _i32
+_lib.tg_gated_attention_decode.argtypes = [_vp, _vp, _vp, _vp, _vp, _i32, _vp, _vp, _i32, _i64, _i32, _i32, _i32, _vp,
+                                           _vp, _sz, _vp]
 _lib.tg_gated_attention_prefill.restype = _i32
 _lib.tg_gated_attention_prefill.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, ctypes.POINTER(PlanInfo), _i32, _i32,
                                             _i32, _vp, _vp]
@@ -309,6 +315,31 @@ def gated_attention_prefill_query_tau(q: torch.Tensor, k: torch.Tensor, v: torch
                                                    _ptr(gain), _ptr(positions), _dev_table(plan),
                                                    ctypes.byref(plan.info), hq, hkv, dh, _ptr(out), _stream(stream))
     _check(st, "tg_gated_attention_prefill_query_tau")
+    return out
+
+
+def decode_workspace_bytes(batch: int, hq: int, head_dim: int, cache_rows: int) -> int:
+    return int(_lib.tg_decode_workspace_bytes(batch, hq, head_dim, cache_rows))
+
+
+def gated_attention_decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
+                           key_score: Optional[torch.Tensor], tau: Optional[torch.Tensor],
+                           gain: Optional[torch.Tensor], lens: torch.Tensor, out: Optional[torch.Tensor] = None,
+                           workspace: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """tg_gated_attention_decode.  q [B, hq, D]; k_cache / v_cache [B, cap, hkv, D]
+    bf16 contiguous; key_score [B, cap] fp32; tau [hq] or [B, hq] (per query);
+    lens int32 [B]; returns out [B, hq, D]."""
+    bsz, hq, dh = q.shape
+    cap, hkv = k_cache.shape[1], k_cache.shape[2]
+    if out is None:
+        out = torch.empty_like(q)
+    if workspace is None:
+        workspace = _workspace(decode_workspace_bytes(bsz, hq, dh, cap), q.device)
+    per_query = 1 if tau is not None and tau.dim() == 2 else 0
+    st = _lib.tg_gated_attention_decode(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(key_score), _ptr(tau), per_query,
+                                        _ptr(gain), _ptr(lens), bsz, cap, hq, hkv, dh, _ptr(out), _ptr(workspace),
+                                        workspace.numel() * workspace.element_size(), _stream(stream))
+    _check(st, "tg_gated_attention_decode")
     return out
 
 

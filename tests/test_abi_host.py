@@ -172,6 +172,30 @@ def test_attention_query_tau_validation():
     assert f(None, None, None, None, FAKE, None, None, FAKE, ctypes.byref(empty.info), 16, 8, 128, None, None) == 0
 
 
+def test_decode_validation():
+    f = L.tg_gated_attention_decode
+    ws = tg.decode_workspace_bytes(2, 16, 128, 1000)
+    assert ws == 2 * 16 * 4 * 130 * 4  # 4 chunks of 256 rows, D + 2 floats per head and chunk
+    assert tg.decode_workspace_bytes(0, 16, 128, 10) == 0
+    args = lambda **kw: dict(dict(q=FAKE, k=FAKE, v=FAKE, s=None, tau=None, tpq=0, gain=None, lens=FAKE, b=2, cap=1000,
+                                  hq=16, hkv=8, d=128, out=FAKE, ws=FAKE, wsb=ws), **kw)
+    call = lambda a: f(a["q"], a["k"], a["v"], a["s"], a["tau"], a["tpq"], a["gain"], a["lens"], a["b"], a["cap"],
+                       a["hq"], a["hkv"], a["d"], a["out"], a["ws"], a["wsb"], None)
+    assert call(args(b=0, q=None, lens=None)) == 0  # nothing to do
+    assert call(args(lens=None)) == -1
+    assert call(args(k=None)) == -1
+    assert call(args(tpq=2)) == -1
+    assert call(args(cap=-1)) == -1
+    assert call(args(q=ctypes.c_void_p(0x10008))) == -1
+    assert call(args(hkv=6)) == -2
+    assert call(args(hkv=2)) == -2   # group of 8
+    assert call(args(d=96)) == -2
+    assert call(args(b=70000, wsb=1 << 40)) == -2
+    assert call(args(cap=65535 * 256 + 1, wsb=1 << 40)) == -2
+    assert call(args(wsb=ws - 1)) == -3
+    assert call(args(ws=None)) == -3
+
+
 @pytest.mark.skipif(gpu_available(), reason="only meaningful without a GPU: valid calls must report no device")
 def test_valid_calls_report_no_device_without_gpu():
     p = _plan()
@@ -182,6 +206,8 @@ def test_valid_calls_report_no_device_without_gpu():
     assert L.tg_gated_attention_prefill(FAKE, FAKE, FAKE, None, None, None, FAKE, info, 16, 8, 128, FAKE, None) == -4
     assert L.tg_gated_attention_prefill_query_tau(FAKE, FAKE, FAKE, None, FAKE, None, FAKE, FAKE, info, 16, 8, 128,
                                                   FAKE, None) == -4
+    assert L.tg_gated_attention_decode(FAKE, FAKE, FAKE, None, None, 0, None, FAKE, 2, 1000, 16, 8, 128, FAKE, FAKE,
+                                       tg.decode_workspace_bytes(2, 16, 128, 1000), None) == -4
 
 
 def test_dense_validation():
