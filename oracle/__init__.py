@@ -33,6 +33,7 @@ from .tokengate_ref import (  # noqa: F401
     softplus,
     query_temperature,
     gated_attention_decode,
+    gated_attention_backward,
 )
 from .stack_ref import (  # noqa: F401,E402
     round_bf16,

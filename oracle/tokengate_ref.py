@@ -347,3 +347,63 @@ def gated_attention_decode(q: np.ndarray, k_cache: np.ndarray, v_cache: np.ndarr
             p = np.exp(z - z.max())
             out[b, h, :] = (p / p.sum()) @ v_cache[b, :n, c, :]
     return out
+
+
+def gated_attention_backward(q: np.ndarray, k: np.ndarray, v: np.ndarray, s: Optional[np.ndarray],
+                             tau: Optional[np.ndarray], gain: Optional[np.ndarray], kept_offsets: Sequence[int],
+                             dout: np.ndarray) -> dict:
+    """Gradients of the token-gated attention (the forward of gated_attention)
+    with respect to q, k, v, the key scores s, the gains g_h and the
+    temperatures tau_h, for an upstream gradient dout [M, Hq, D]
+    ([reading] §4.1 engineering notes: the same attention kernel accumulates
+    the bias gradient back into the scorer in the backward pass).
+
+    Per prompt and head, with z = tau q.k/sqrt(D) + g s (causal), P = softmax(z):
+        dV   = P^T dO                       (summed over the heads sharing a KV head)
+        dZ   = P o (dO V^T - rowsum(dO o O))
+        dQ   = tau/sqrt(D) dZ K,   dK = tau/sqrt(D) dZ^T Q  (dK summed like dV)
+        ds_t = sum_h g_h sum_r dZ_rt,   dg_h = sum_rt dZ_rt s_t,   dtau_h = sum_rt dZ_rt q_r.k_t/sqrt(D)
+    Returns a dict of float64 arrays: dq [M, Hq, D], dk, dv [M, Hkv, D],
+    ds [M], dgain [Hq], dtau [Hq] (the last three zero without a bias / with
+    tau None, where they are not inputs).
+    Pinned by central finite differences of gated_attention and by torch
+    autograd on the same forward (tests/test_oracle_attention.py).
+    """
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    dout = np.asarray(dout, dtype=np.float64)
+    m_total, hq, dh = q.shape
+    hkv = k.shape[1]
+    group = hq // hkv
+    tau_v = np.ones(hq) if tau is None else np.asarray(tau, dtype=np.float64)
+    use_bias = s is not None and gain is not None
+    s_v = np.asarray(s, dtype=np.float64) if use_bias else np.zeros(m_total)
+    g_v = np.asarray(gain, dtype=np.float64) if use_bias else np.zeros(hq)
+    scale = 1.0 / math.sqrt(dh)
+    res = {"dq": np.zeros_like(q), "dk": np.zeros_like(k), "dv": np.zeros_like(v), "ds": np.zeros(m_total),
+           "dgain": np.zeros(hq), "dtau": np.zeros(hq)}
+    offs = [int(o) for o in kept_offsets]
+    for a, b in zip(offs[:-1], offs[1:]):
+        n = b - a
+        if n == 0:
+            continue
+        causal = np.tril(np.ones((n, n), dtype=bool))
+        for h in range(hq):
+            c = h // group
+            qh, kc, vc, do = q[a:b, h], k[a:b, c], v[a:b, c], dout[a:b, h]
+            qk = (qh @ kc.T) * scale
+            z = np.where(causal, tau_v[h] * qk + g_v[h] * s_v[a:b][None, :], -np.inf)
+            z = z - z.max(axis=1, keepdims=True)
+            p = np.exp(z)
+            p = p / p.sum(axis=1, keepdims=True)
+            o = p @ vc
+            dp = do @ vc.T
+            dz = p * (dp - (do * o).sum(axis=1, keepdims=True))
+            res["dv"][a:b, c] += p.T @ do
+            res["dq"][a:b, h] += tau_v[h] * scale * (dz @ kc)
+            res["dk"][a:b, c] += tau_v[h] * scale * (dz.T @ qh)
+            res["ds"][a:b] += g_v[h] * dz.sum(axis=0)
+            res["dgain"][h] += (dz.sum(axis=0) * s_v[a:b]).sum()
+            res["dtau"][h] += (dz * qk).sum()
+    return res

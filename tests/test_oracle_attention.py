@@ -239,3 +239,65 @@ def test_decode_empty_and_single_key():
     assert np.all(o[0] == 0.0)
     np.testing.assert_allclose(o[1], np.repeat(vc[1, 0], 2, axis=0), rtol=1e-15)
     assert np.all(np.isfinite(o[2]))
+
+
+# ----------------------------------------------------------------------------- backward
+
+
+def _loss(q, k, v, s, tau, gain, offs, w):
+    return float((oracle.gated_attention(q, k, v, s, tau, gain, offs) * w).sum())
+
+
+def test_backward_matches_finite_differences():
+    """Every gradient against central differences of the forward (step 1e-6,
+    float64) on a two-prompt GQA case: the loss is sum(O * W) for a fixed W,
+    so dout = W."""
+    rng = np.random.default_rng(31)
+    offs = [0, 5, 9]
+    m, hq, hkv, d = 9, 4, 2, 3
+    q, k, v = (rng.standard_normal((m, h, d)) for h in (hq, hkv, hkv))
+    s = rng.standard_normal(m)
+    tau = rng.uniform(0.6, 1.4, hq)
+    gain = rng.uniform(0.5, 1.5, hq)
+    w = rng.standard_normal((m, hq, d))
+    g = oracle.gated_attention_backward(q, k, v, s, tau, gain, offs, w)
+    eps = 1e-6
+    args = {"q": q, "k": k, "v": v, "s": s, "gain": gain, "tau": tau}
+    names = {"q": "dq", "k": "dk", "v": "dv", "s": "ds", "gain": "dgain", "tau": "dtau"}
+    for name, arr in args.items():
+        num = np.zeros_like(arr)
+        for idx in np.ndindex(arr.shape):
+            plus, minus = dict(args), dict(args)
+            plus[name] = arr.copy()
+            minus[name] = arr.copy()
+            plus[name][idx] += eps
+            minus[name][idx] -= eps
+            num[idx] = (_loss(plus["q"], plus["k"], plus["v"], plus["s"], plus["tau"], plus["gain"], offs, w)
+                        - _loss(minus["q"], minus["k"], minus["v"], minus["s"], minus["tau"], minus["gain"], offs,
+                                w)) / (2 * eps)
+        np.testing.assert_allclose(g[names[name]], num, rtol=1e-6, atol=1e-7, err_msg=name)
+
+
+def test_backward_matches_torch_autograd():
+    """Against torch autograd (float64, CPU) through a forward written with
+    torch ops: logits tau q k^T / sqrt(D) + g s plus a causal -inf mask."""
+    rng = np.random.default_rng(32)
+    m, hq, hkv, d = 21, 4, 2, 8
+    group = hq // hkv
+    q, k, v = (rng.standard_normal((m, h, d)) for h in (hq, hkv, hkv))
+    s = rng.standard_normal(m)
+    tau = rng.uniform(0.6, 1.4, hq)
+    gain = rng.uniform(0.5, 1.5, hq)
+    dout = rng.standard_normal((m, hq, d))
+    tq, tk, tv, ts, tt, tg = (torch.tensor(a, requires_grad=True) for a in (q, k, v, s, tau, gain))
+    kk = tk.repeat_interleave(group, dim=1).permute(1, 0, 2)
+    vv = tv.repeat_interleave(group, dim=1).permute(1, 0, 2)
+    z = tt[:, None, None] * (tq.permute(1, 0, 2) @ kk.transpose(1, 2)) / math.sqrt(d) + tg[:, None, None] * ts[None,
+                                                                                                               None, :]
+    mask = torch.triu(torch.ones(m, m, dtype=torch.bool), diagonal=1)
+    z = z.masked_fill(mask, float("-inf"))
+    o = (torch.softmax(z, dim=-1) @ vv).permute(1, 0, 2)
+    (o * torch.from_numpy(dout)).sum().backward()
+    g = oracle.gated_attention_backward(q, k, v, s, tau, gain, [0, m], dout)
+    for name, t in (("dq", tq), ("dk", tk), ("dv", tv), ("ds", ts), ("dtau", tt), ("dgain", tg)):
+        np.testing.assert_allclose(g[name], t.grad.numpy(), rtol=1e-10, atol=1e-11, err_msg=name)
