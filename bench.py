@@ -300,6 +300,54 @@ def time_decode(torch, tg, reps=200):
     return rec
 
 
+def time_backward(torch, tg, reps=20):
+    """Forward with the saved log-sum-exp, then the backward (dq, dk, dv and
+    the key-score / gain / temperature gradients) of token-gated attention over
+    M kept rows of one prompt: 16 Q / 8 KV heads, head_dim 128, random bf16
+    inputs.  Algorithmic work: forward 4 hq D M(M+1)/2 flop (QK and PV over
+    the causal pairs), backward 2.5x that (QK recompute, dP, dV, dK, dQ)."""
+    dev = torch.device("cuda")
+    gen = torch.Generator(device=dev).manual_seed(78)
+    hq, hkv, dh = 16, 8, 128
+    rec = {"workload": "token-gated attention backward, one prompt of M kept rows, 16 Q / 8 KV heads, head_dim 128"}
+    for m in (2112, 4160):
+        q = torch.randn(m, hq, dh, generator=gen, device=dev).to(torch.bfloat16)
+        k = torch.randn(m, hkv, dh, generator=gen, device=dev).to(torch.bfloat16)
+        v = torch.randn(m, hkv, dh, generator=gen, device=dev).to(torch.bfloat16)
+        do = torch.randn(m, hq, dh, generator=gen, device=dev).to(torch.bfloat16)
+        sc = torch.randn(m, generator=gen, device=dev)
+        tau = 0.8 + 0.4 * torch.rand(hq, generator=gen, device=dev)
+        gain = 0.5 + torch.rand(hq, generator=gen, device=dev)
+        plan = tg.plan_segments([0, m], [0], [0], [0], device=dev)
+        out, lse = tg.gated_attention_prefill_lse(q, k, v, sc, tau, gain, plan)
+        ws = torch.empty(max(tg.attention_backward_workspace_bytes(plan, hq, hkv), 256), dtype=torch.uint8, device=dev)
+
+        def timed(f):
+            for _ in range(3):
+                f()
+            torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for _ in range(reps):
+                f()
+            e1.record()
+            torch.cuda.synchronize()
+            return e0.elapsed_time(e1) / reps * 1e3
+
+        us_f = timed(lambda: tg.gated_attention_prefill_lse(q, k, v, sc, tau, gain, plan, out=out, lse=lse))
+        us_b = timed(lambda: tg.gated_attention_backward(q, k, v, sc, tau, gain, plan, out, do, lse, workspace=ws))
+        fwd = 4 * hq * dh * m * (m + 1) // 2
+        tf_b = 2.5 * fwd / (us_b * 1e-6) / 1e12
+        rec[f"m{m}"] = {"forward_lse_us": round(us_f, 2), "backward_us": round(us_b, 2),
+                        "forward_tflops": fwd / (us_f * 1e-6) / 1e12,
+                        "roofline": {"kernel": "bwd_rowdot + bwd_dkdv<128,2> + bwd_dq<128,2> + bwd_reduce",
+                                     "bound": "mfma", "achieved": tf_b, "peak": MFMA_BF16_PEAK_TFLOPS,
+                                     "unit": "TFLOP/s", "frac": tf_b / MFMA_BF16_PEAK_TFLOPS, "traffic": None}}
+        del q, k, v, do, out, lse, ws
+        torch.cuda.empty_cache()
+    return rec
+
+
 STACK = dict(n=65536, n_q=64, k=4096, layers=28, gate_layer=12, d=2048, hq=16, hkv=8, dh=128, f=6144, h_gate=256)
 
 
@@ -542,6 +590,11 @@ def main():
         log("timing the decode step over pruned and unpruned caches")
         result["decode_b32"] = time_decode(torch, tg)
         log("decode", {k: v["us_per_step"] for k, v in result["decode_b32"].items() if isinstance(v, dict)})
+
+    if not args.no_decode and result is not None:
+        log("timing the attention backward")
+        result["attention_backward"] = time_backward(torch, tg)
+        log("backward", {k: v["backward_us"] for k, v in result["attention_backward"].items() if isinstance(v, dict)})
 
     if not args.no_cpu_baseline and l16 is not None:
         log("timing the CPU oracle on the 16K workload")

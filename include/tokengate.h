@@ -251,6 +251,43 @@ int tg_gated_attention_prefill_query_tau(const void* q, const void* k, const voi
                                          int head_dim, void* out, void* stream);
 
 /* ------------------------------------------------------------------------ */
+/* (4a) Token-gated attention, backward                                     */
+/* ------------------------------------------------------------------------ */
+
+/* The forward of tg_gated_attention_prefill that also writes the natural-log
+ * log-sum-exp of every row's logits, lse[r * hq + h] = ln sum_t exp(z_rt)
+ * (fp32 [total_kept, hq], device), which the backward needs. */
+int tg_gated_attention_prefill_lse(const void* q, const void* k, const void* v, const float* key_score,
+                                   const float* tau, const float* gain, const tg_segment* segs,
+                                   const tg_plan_info* info, int hq, int hkv, int head_dim, void* out, float* lse,
+                                   void* stream);
+
+/* Gradients of tg_gated_attention_prefill ([reading] section 4.1,
+ * engineering notes: the biased attention kernel runs backwards too and
+ * carries the bias gradient back into the gate's scorer).  With P the
+ * attention weights and dout [total_kept, hq, head_dim] (bf16) the upstream
+ * gradient of out:
+ *   dv = P^T dout, dZ = P o (dout v^T - rowsum(dout o out)),
+ *   dq = tau_h / sqrt(D) dZ k,  dk = tau_h / sqrt(D) dZ^T q  (dk, dv summed over
+ *   the hq / hkv heads sharing a KV head),
+ *   ds_t = sum_h gain_h sum_r dZ_rt  (the key-score gradient, to the scorer),
+ *   dgain_h = sum dZ_rt s_t,  dtau_h = sum dZ_rt (q_r . k_t) / sqrt(D).
+ * Inputs as for the forward, plus out (its bf16 output) and lse (from
+ * tg_gated_attention_prefill_lse).  Outputs, all fp32 and overwritten:
+ *   dq [total_kept, hq, head_dim], dk and dv [total_kept, hkv, head_dim] (16-byte aligned);
+ *   ds [total_kept], dgain [hq], dtau [hq]: each may be NULL (not written);
+ *   without a bias (key_score or gain NULL) ds and dgain come out 0.
+ * workspace: device, 16-byte aligned, >= tg_attention_backward_workspace_bytes.
+ * bf16 MFMA products (P and the scaled dZ rounded to bf16), fp32
+ * accumulation; results are deterministic.  Shapes as for the forward. */
+size_t tg_attention_backward_workspace_bytes(const tg_plan_info* info, int hq, int hkv);
+int tg_gated_attention_backward(const void* q, const void* k, const void* v, const float* key_score,
+                                const float* tau, const float* gain, const tg_segment* segs,
+                                const tg_plan_info* info, int hq, int hkv, int head_dim, const void* out,
+                                const void* dout, const float* lse, float* dq, float* dk, float* dv, float* ds,
+                                float* dgain, float* dtau, void* workspace, size_t workspace_bytes, void* stream);
+
+/* ------------------------------------------------------------------------ */
 /* (4b) Token-gated attention, one decode step over a pruned KV cache        */
 /* ------------------------------------------------------------------------ */
 

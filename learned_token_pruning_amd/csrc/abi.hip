@@ -190,7 +190,8 @@ int tg_gated_attention_prefill(const void* q, const void* k, const void* v, cons
   st = check_device();
   if (st != TG_OK) return st;
   return hip_status(tg::launch_gated_attention(q, k, v, key_score, tau, gain, segs, *info, hq, hkv, head_dim,
-                                               nullptr, 0, nullptr, out, reinterpret_cast<hipStream_t>(stream)));
+                                               nullptr, 0, nullptr, nullptr, out,
+                                               reinterpret_cast<hipStream_t>(stream)));
 }
 
 int tg_gated_attention_prefill_query_tau(const void* q, const void* k, const void* v, const float* key_score,
@@ -212,7 +213,8 @@ int tg_gated_attention_prefill_query_tau(const void* q, const void* k, const voi
   st = check_device();
   if (st != TG_OK) return st;
   return hip_status(tg::launch_gated_attention(q, k, v, key_score, sigma, gain, segs, *info, hq, hkv, head_dim,
-                                               nullptr, 0, positions, out, reinterpret_cast<hipStream_t>(stream)));
+                                               nullptr, 0, positions, nullptr, out,
+                                               reinterpret_cast<hipStream_t>(stream)));
 }
 
 int tg_gated_attention_prefill_gather(const void* q, const void* k, const void* v, const float* key_score,
@@ -238,8 +240,67 @@ int tg_gated_attention_prefill_gather(const void* q, const void* k, const void* 
   st = check_device();
   if (st != TG_OK) return st;
   return hip_status(tg::launch_gated_attention(q, k, v, key_score, tau, gain, segs, *info, hq, hkv, head_dim,
-                                               kept_idx, n_src_rows, nullptr, out,
+                                               kept_idx, n_src_rows, nullptr, nullptr, out,
                                                reinterpret_cast<hipStream_t>(stream)));
+}
+
+namespace {
+int check_attention_shapes(const tg_segment* segs, const tg_plan_info* info, int hq, int hkv, int head_dim) {
+  int st = check_info(segs, info);
+  if (st != TG_OK) return st;
+  if (hq <= 0 || hkv <= 0 || head_dim <= 0) return TG_ERR_INVALID_ARG;
+  if (hq % hkv != 0) return TG_ERR_UNSUPPORTED;
+  const int G = hq / hkv;
+  if (!(head_dim == 64 || head_dim == 128) || !(G == 1 || G == 2 || G == 4)) return TG_ERR_UNSUPPORTED;
+  return TG_OK;
+}
+}  // namespace
+
+int tg_gated_attention_prefill_lse(const void* q, const void* k, const void* v, const float* key_score,
+                                   const float* tau, const float* gain, const tg_segment* segs,
+                                   const tg_plan_info* info, int hq, int hkv, int head_dim, void* out, float* lse,
+                                   void* stream) {
+  int st = check_attention_shapes(segs, info, hq, hkv, head_dim);
+  if (st != TG_OK) return st;
+  if (info->total_kept > 0 && (!q || !k || !v || !out || !lse)) return TG_ERR_INVALID_ARG;
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(out, 16) || !aligned(lse, 4) ||
+      (key_score && !aligned(key_score, 4)) || (tau && !aligned(tau, 4)) || (gain && !aligned(gain, 4)))
+    return TG_ERR_INVALID_ARG;
+  if (info->total_kept == 0) return TG_OK;
+  st = check_device();
+  if (st != TG_OK) return st;
+  return hip_status(tg::launch_gated_attention(q, k, v, key_score, tau, gain, segs, *info, hq, hkv, head_dim,
+                                               nullptr, 0, nullptr, lse, out,
+                                               reinterpret_cast<hipStream_t>(stream)));
+}
+
+size_t tg_attention_backward_workspace_bytes(const tg_plan_info* info, int hq, int hkv) {
+  if (!info || hq <= 0 || hkv <= 0 || info->n_seg < 1 || info->total_kept < 0) return 0;
+  return tg::attention_backward_workspace_bytes(*info, hq, hkv);
+}
+
+int tg_gated_attention_backward(const void* q, const void* k, const void* v, const float* key_score,
+                                const float* tau, const float* gain, const tg_segment* segs,
+                                const tg_plan_info* info, int hq, int hkv, int head_dim, const void* out,
+                                const void* dout, const float* lse, float* dq, float* dk, float* dv, float* ds,
+                                float* dgain, float* dtau, void* workspace, size_t workspace_bytes, void* stream) {
+  int st = check_attention_shapes(segs, info, hq, hkv, head_dim);
+  if (st != TG_OK) return st;
+  if (info->total_kept > 0 && (!q || !k || !v || !out || !dout || !lse || !dq || !dk || !dv))
+    return TG_ERR_INVALID_ARG;
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(out, 16) || !aligned(dout, 16) ||
+      !aligned(dq, 16) || !aligned(dk, 16) || !aligned(dv, 16) || !aligned(lse, 4) || !aligned(ds, 4) ||
+      !aligned(dgain, 4) || !aligned(dtau, 4) || (key_score && !aligned(key_score, 4)) ||
+      (tau && !aligned(tau, 4)) || (gain && !aligned(gain, 4)))
+    return TG_ERR_INVALID_ARG;
+  if (!workspace || !aligned(workspace, 16) ||
+      workspace_bytes < tg::attention_backward_workspace_bytes(*info, hq, hkv))
+    return TG_ERR_WORKSPACE;
+  st = check_device();
+  if (st != TG_OK) return st;
+  return hip_status(tg::launch_gated_attention_backward(q, k, v, key_score, tau, gain, segs, *info, hq, hkv, head_dim,
+                                                        out, dout, lse, dq, dk, dv, ds, dgain, dtau, workspace,
+                                                        reinterpret_cast<hipStream_t>(stream)));
 }
 
 size_t tg_decode_workspace_bytes(int batch, int hq, int head_dim, int64_t cache_rows) {
@@ -384,7 +445,7 @@ int tg_decoder_layer(void* hidden, const int32_t* positions, const float* key_sc
   TG_TRY(tg::launch_gemm(0, xn, d, w->wqkv, d, m, nqkv, d, nullptr, 0, qkv, nqkv, s));
   TG_TRY(tg::launch_rope_split(qkv, nqkv, m, hq, hkv, head_dim, positions, rope_theta, q, k, v, s));
   TG_TRY(tg::launch_gated_attention(q, k, v, key_score, w->tau, w->gain, segs, *info, hq, hkv, head_dim, nullptr, 0,
-                                    nullptr, att, s));
+                                    nullptr, nullptr, att, s));
   TG_TRY(tg::launch_gemm(1, att, (int64_t)hq * head_dim, w->wo, (int64_t)hq * head_dim, m, d, hq * head_dim, hidden,
                          d, hidden, d, s));
   TG_TRY(tg::launch_rmsnorm(hidden, d, m, d, w->mlp_norm, rms_eps, hn, d, s));

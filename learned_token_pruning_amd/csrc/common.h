@@ -49,6 +49,48 @@ __device__ __forceinline__ float xor32_sum(float x) {
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
+// Lane reductions on DPP row operations and the gfx950 row swaps (no LDS
+// round trip).  Every step combines a lane with its partner in an order-free
+// way (a + b and b + a, max), so all lanes of a group end with the same bits.
+template <int CTRL>
+__device__ __forceinline__ float dpp(float x) {
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), CTRL, 0xf, 0xf, false));
+}
+constexpr int kQuadXor1 = 0xb1, kQuadXor2 = 0x4e, kRowHalfMirror = 0x141, kRowMirror = 0x140, kRowRor8 = 0x128;
+
+__device__ __forceinline__ float swap16_sum(float x) {  // x + x of lane ^ 16
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ __forceinline__ float swap16_max(float x) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __builtin_fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+
+// sum over aligned groups of N lanes (N = 8 or 16)
+template <int N>
+__device__ __forceinline__ float group_sum(float x) {
+  x += dpp<kQuadXor1>(x);
+  x += dpp<kQuadXor2>(x);
+  x += dpp<kRowHalfMirror>(x);
+  if (N == 16) x += dpp<kRowMirror>(x);
+  return x;
+}
+__device__ __forceinline__ float wave_sum(float x) { return xor32_sum(swap16_sum(group_sum<16>(x))); }
+__device__ __forceinline__ float wave_max(float x) {
+  x = __builtin_fmaxf(x, dpp<kQuadXor1>(x));
+  x = __builtin_fmaxf(x, dpp<kQuadXor2>(x));
+  x = __builtin_fmaxf(x, dpp<kRowHalfMirror>(x));
+  x = __builtin_fmaxf(x, dpp<kRowMirror>(x));
+  return xor32_max(swap16_max(x));
+}
+// sum over the lanes sharing lane % N (N = 8 or 16)
+template <int N>
+__device__ __forceinline__ float stride_sum(float x) {
+  if (N == 8) x += dpp<kRowRor8>(x);
+  return xor32_sum(swap16_sum(x));
+}
+
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
 
@@ -102,8 +144,17 @@ hipError_t launch_compact(const int32_t* kept_idx, int64_t n_kept, int64_t n_src
 hipError_t launch_gated_attention(const void* q, const void* k, const void* v, const float* key_score,
                                   const float* tau, const float* gain, const tg_segment* segs,
                                   const tg_plan_info& info, int hq, int hkv, int head_dim, const int32_t* kept_idx,
-                                  int64_t n_src, const int32_t* qpos, void* out, hipStream_t stream);
+                                  int64_t n_src, const int32_t* qpos, float* lse, void* out, hipStream_t stream);
 constexpr int64_t kAttnMaxGatherRows = 16384;
+
+// Backward of the compacted-row attention; lse from the forward (natural log).
+size_t attention_backward_workspace_bytes(const tg_plan_info& info, int hq, int hkv);
+hipError_t launch_gated_attention_backward(const void* q, const void* k, const void* v, const float* key_score,
+                                           const float* tau, const float* gain, const tg_segment* segs,
+                                           const tg_plan_info& info, int hq, int hkv, int head_dim, const void* out,
+                                           const void* dout, const float* lse, float* dq, float* dk, float* dv,
+                                           float* ds, float* dgain, float* dtau, void* workspace,
+                                           hipStream_t stream);
 
 // One decode step over per-sequence KV caches [batch, cap, hkv, head_dim];
 // the workspace holds the split-KV partials.

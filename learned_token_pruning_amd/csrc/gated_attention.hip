@@ -197,7 +197,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
     const float* __restrict__ key_score, const float* __restrict__ tau, const float* __restrict__ gain,
     const tg_segment* __restrict__ segs, int hq, int hkv, const int32_t* __restrict__ kept_idx, int64_t n_src,
-    const int32_t* __restrict__ qpos, uint16_t* __restrict__ out) {
+    const int32_t* __restrict__ qpos, float* __restrict__ lse, uint16_t* __restrict__ out) {
   constexpr bool GATHER = MODE == kGather;
   constexpr bool QTAU = MODE == kQueryTau;
   constexpr int kBM = 128 / G;  // query rows per workgroup
@@ -450,7 +450,11 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
     const float m = __builtin_fmaxf(m_run, m1);
     const float a0 = m_run == -__builtin_inff() ? 0.0f : __builtin_amdgcn_exp2f(m_run - m);
     const float a1 = m1 == -__builtin_inff() ? 0.0f : __builtin_amdgcn_exp2f(m1 - m);
-    const float inv = 1.0f / (l_half * a0 + l1 * a1);
+    const float l_all = l_half * a0 + l1 * a1;
+    const float inv = 1.0f / l_all;
+    // natural-log log-sum-exp of the row's logits (kept for the backward pass)
+    if (lse != nullptr && qrow < n && g == 0)
+      lse[((int64_t)seg.kept_start + qrow) * hq + h] = (m + __log2f(l_all)) * 0.6931471805599453f;
     if (qrow < n) {
       uint16_t* orow = out + ((int64_t)seg.kept_start + qrow) * q_stride + (int64_t)h * D;
 #pragma unroll
@@ -474,7 +478,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
 template <int D, int G>
 hipError_t launch_dg(const void* q, const void* k, const void* v, const float* ks, const float* tau,
                      const float* gain, const tg_segment* segs, const tg_plan_info& info, int hq, int hkv,
-                     const int32_t* kept_idx, int64_t n_src, const int32_t* qpos, void* out, hipStream_t stream) {
+                     const int32_t* kept_idx, int64_t n_src, const int32_t* qpos, float* lse, void* out,
+                     hipStream_t stream) {
   constexpr int kBM = 128 / G;
   const int ntiles = (info.max_kept_len + kBM - 1) / kBM;
   if (ntiles == 0) return hipSuccess;
@@ -485,13 +490,13 @@ hipError_t launch_dg(const void* q, const void* k, const void* v, const float* k
   auto* ob = reinterpret_cast<uint16_t*>(out);
   if (kept_idx != nullptr)
     hipLaunchKernelGGL((gated_attention_kernel<D, G, kGather>), grid, dim3(kThreads), 0, stream, qb, kb, vb, ks, tau,
-                       gain, segs, hq, hkv, kept_idx, n_src, nullptr, ob);
+                       gain, segs, hq, hkv, kept_idx, n_src, nullptr, lse, ob);
   else if (qpos != nullptr)
     hipLaunchKernelGGL((gated_attention_kernel<D, G, kQueryTau>), grid, dim3(kThreads), 0, stream, qb, kb, vb, ks,
-                       tau, gain, segs, hq, hkv, nullptr, (int64_t)0, qpos, ob);
+                       tau, gain, segs, hq, hkv, nullptr, (int64_t)0, qpos, lse, ob);
   else
     hipLaunchKernelGGL((gated_attention_kernel<D, G, kCompacted>), grid, dim3(kThreads), 0, stream, qb, kb, vb, ks,
-                       tau, gain, segs, hq, hkv, nullptr, (int64_t)0, nullptr, ob);
+                       tau, gain, segs, hq, hkv, nullptr, (int64_t)0, nullptr, lse, ob);
   return hipGetLastError();
 }
 
@@ -500,11 +505,12 @@ hipError_t launch_dg(const void* q, const void* k, const void* v, const float* k
 hipError_t launch_gated_attention(const void* q, const void* k, const void* v, const float* key_score,
                                   const float* tau, const float* gain, const tg_segment* segs,
                                   const tg_plan_info& info, int hq, int hkv, int head_dim, const int32_t* kept_idx,
-                                  int64_t n_src, const int32_t* qpos, void* out, hipStream_t stream) {
+                                  int64_t n_src, const int32_t* qpos, float* lse, void* out, hipStream_t stream) {
   const int G = hq / hkv;
 #define TG_ATTN_CASE(DD, GG) \
   if (head_dim == DD && G == GG) \
-    return launch_dg<DD, GG>(q, k, v, key_score, tau, gain, segs, info, hq, hkv, kept_idx, n_src, qpos, out, stream);
+    return launch_dg<DD, GG>(q, k, v, key_score, tau, gain, segs, info, hq, hkv, kept_idx, n_src, qpos, lse, out, \
+                             stream);
   TG_ATTN_CASE(128, 1)
   TG_ATTN_CASE(128, 2)
   TG_ATTN_CASE(128, 4)

@@ -1,0 +1,529 @@
+// Backward pass of token-gated causal GQA attention (gfx950).
+//
+// "TokenGate 与 T2Quant ... 精读", section 4.1, engineering notes: the biased
+// attention kernel is also run backwards, and the gradient of the per-key bias
+// flows back into the gate's scorer.  With z = tau_h q.k / sqrt(D) + g_h s_t,
+// P = softmax(z) (causal, over the kept rows of a prompt) and upstream dO:
+//   dV = P^T dO,  dZ = P o (dO V^T - rowsum(dO o O)),
+//   dQ = tau_h/sqrt(D) dZ K,  dK = tau_h/sqrt(D) dZ^T Q,
+//   ds_t = sum_h g_h sum_r dZ_rt,  dg_h = sum dZ_rt s_t,  dtau_h = sum dZ_rt q_r.k_t / sqrt(D).
+// P is recomputed from the log-sum-exp the forward saved (flash-style: no
+// M x M matrix is stored), in the exp2 domain.
+//
+// Kernels:
+//  bwd_rowdot   Dt[r, h] = dO[r, h] . O[r, h]  (fp32; one row piece per lane group)
+//  bwd_dkdv     one workgroup per (KV head, 128-key block, prompt), wave w owning
+//               32 keys.  S = Q K^T is computed with the keys on the MFMA
+//               columns, so a lane owns one key and its registers hold 16 query
+//               rows: P and dZ are then, without any data movement, the B
+//               operand of dV^T += dO^T P and dK^T += Q^T dZ (the query order
+//               inside each 16-row MFMA step is permuted identically on both
+//               operands).  Q and dO blocks of 32 rows are staged in LDS both
+//               row-major (A operands of S and dP = dO V^T) and transposed.  The
+//               lane-local key sums give ds, dg and dtau partials.
+//  bwd_dq       the forward's transposed layout (a lane owns one query):
+//               S^T = K Q^T, dP^T = V dO^T, dQ^T += K^T dZ^T, with K, V and K^T
+//               tiles of 64 keys staged in LDS.
+//  bwd_reduce   sums the per-KV-head ds partials and the per-workgroup dg /
+//               dtau partials in a fixed order (deterministic results).
+// bf16 MFMA operands (P and the scaled dZ are rounded to bf16 for the
+// products), fp32 accumulation and fp32 gradient outputs.
+#include "common.h"
+
+namespace tg {
+namespace {
+
+constexpr float kL2e = 1.4426950408889634f;
+constexpr int kBwdThreads = 256;
+constexpr int kKeyBlock = 128;  // keys per bwd_dkdv workgroup (4 waves x 32)
+constexpr int kTile = 64;       // keys per bwd_dq tile
+
+__device__ __forceinline__ uint32_t pack2(float a, float b) {
+  typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+  typedef float f32x2_t __attribute__((ext_vector_type(2)));
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2_t{a, b}), bf16x2_t));
+}
+
+// Row r (0-based) of register i of a 32x32 MFMA result for half-wave g.
+__device__ __forceinline__ int c_row(int i, int g) { return 8 * (i / 4) + 4 * g + (i % 4); }
+
+template <int D>
+__global__ __launch_bounds__(kBwdThreads) void bwd_rowdot_kernel(const uint16_t* __restrict__ dout,
+                                                                 const uint16_t* __restrict__ out, int64_t n_rows,
+                                                                 float* __restrict__ dt) {
+  constexpr int LPK = D / 8;
+  const int64_t idx = (int64_t)blockIdx.x * (kBwdThreads / LPK) + threadIdx.x / LPK;  // (row, head)
+  const int sub = threadIdx.x % LPK;
+  float a = 0.0f;
+  if (idx < n_rows) {
+    const u32x4 x = *reinterpret_cast<const u32x4*>(dout + idx * D + 8 * sub);
+    const u32x4 y = *reinterpret_cast<const u32x4*>(out + idx * D + 8 * sub);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      a = __builtin_fmaf(bf16_lo(x[e]), bf16_lo(y[e]), a);
+      a = __builtin_fmaf(bf16_hi(x[e]), bf16_hi(y[e]), a);
+    }
+  }
+  a = group_sum<LPK>(a);
+  if (idx < n_rows && sub == 0) dt[idx] = a;
+}
+
+// Staging of a block of 32 rows x D of one head: units of 4 rows x 8 dims,
+// written row-major (stride D + 8) and transposed (stride 36: dim-major, rows
+// contiguous).  Rows at or past `nvalid` are staged as zeros.
+template <int D>
+struct RowBlock {
+  static constexpr int kLd = D + 8;
+  static constexpr int tLd = 32 + 4;
+  static constexpr int kUnits = 8 * (D / 8);
+};
+
+template <int D>
+__device__ __forceinline__ void stage_rows(const uint16_t* __restrict__ src, int64_t row_stride, int r0, int nvalid,
+                                           int u, uint16_t* rm, uint16_t* tr) {
+  const int rq = u % 8, dc = u / 8;  // rows 4 rq .. 4 rq + 3, dims 8 dc .. 8 dc + 7
+  u32x4 r[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int row = r0 + 4 * rq + i;
+    r[i] = row < nvalid ? *reinterpret_cast<const u32x4*>(src + (int64_t)row * row_stride + 8 * dc) : u32x4{0, 0, 0, 0};
+    *reinterpret_cast<u32x4*>(&rm[(4 * rq + i) * RowBlock<D>::kLd + 8 * dc]) = r[i];
+  }
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    const uint32_t sel = (e & 1) ? 0x07060302u : 0x05040100u;
+    const int w = e >> 1;
+    const u32x2 pk = u32x2{__builtin_amdgcn_perm(r[1][w], r[0][w], sel), __builtin_amdgcn_perm(r[3][w], r[2][w], sel)};
+    *reinterpret_cast<u32x2*>(&tr[(8 * dc + e) * RowBlock<D>::tLd + 4 * rq]) = pk;
+  }
+}
+
+template <int D, int G>
+__global__ __launch_bounds__(kBwdThreads) void bwd_dkdv_kernel(
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
+    const float* __restrict__ key_score, const float* __restrict__ tau, const float* __restrict__ gain,
+    const tg_segment* __restrict__ segs, int hq, int hkv, const uint16_t* __restrict__ dout,
+    const float* __restrict__ lse, const float* __restrict__ dt, float* __restrict__ dk, float* __restrict__ dv,
+    float* __restrict__ ds_part, int64_t total_kept, float* __restrict__ part_g, float* __restrict__ part_t) {
+  using RB = RowBlock<D>;
+  __shared__ __attribute__((aligned(16))) uint16_t qs[32 * RB::kLd], qt[D * RB::tLd];
+  __shared__ __attribute__((aligned(16))) uint16_t os[32 * RB::kLd], ot[D * RB::tLd];
+  __shared__ float lse2[32], dts[32];
+  __shared__ float red[4][G][2];
+
+  const tg_segment seg = segs[blockIdx.z];
+  const int n = seg.kept_len;
+  const int kb0 = blockIdx.y * kKeyBlock;
+  if (kb0 >= n) return;  // uniform
+  const int c = blockIdx.x;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int g = lane >> 5, l32 = lane & 31;
+  const int kw0 = kb0 + 32 * wave;  // first key of this wave
+  const int kj = kw0 + l32;         // the key this lane owns
+  const bool key_ok = kj < n;
+  const int64_t base = seg.kept_start;
+  const int64_t q_stride = (int64_t)hq * D, kv_stride = (int64_t)hkv * D;
+
+  // K and V row fragments of the lane's key (B operands: k = 16 ks + 8 g .. + 7)
+  u32x4 kf[D / 16], vf[D / 16];
+#pragma unroll
+  for (int ks = 0; ks < D / 16; ++ks) {
+    kf[ks] = key_ok ? *reinterpret_cast<const u32x4*>(k + (base + kj) * kv_stride + (int64_t)c * D + 16 * ks + 8 * g)
+                    : u32x4{0, 0, 0, 0};
+    vf[ks] = key_ok ? *reinterpret_cast<const u32x4*>(v + (base + kj) * kv_stride + (int64_t)c * D + 16 * ks + 8 * g)
+                    : u32x4{0, 0, 0, 0};
+  }
+  const bool use_bias = key_score != nullptr && gain != nullptr;
+  const float s_key = use_bias && key_ok ? key_score[base + kj] : 0.0f;
+
+  f32x16 dkt[D / 32], dvt[D / 32];
+#pragma unroll
+  for (int dtile = 0; dtile < D / 32; ++dtile) {
+    dkt[dtile] = f32x16{};
+    dvt[dtile] = f32x16{};
+  }
+  float ds_acc = 0.0f;
+  const float inv_sqrt_d = 1.0f / __builtin_sqrtf((float)D);
+
+  for (int gg = 0; gg < G; ++gg) {
+    const int h = c * G + gg;
+    const float th = tau != nullptr ? tau[h] : 1.0f;
+    const float scale2 = th * kL2e * inv_sqrt_d;      // exp2-domain logit per unit q.k
+    const float dscale = th * inv_sqrt_d;             // dZ -> dQ, dK factor
+    const float gh = use_bias ? gain[h] : 0.0f;
+    const float bias2 = gh * kL2e * s_key;            // exp2-domain bias of the lane's key
+    float dg_acc = 0.0f, dtau_acc = 0.0f;
+
+    for (int q0 = kb0; q0 < n; q0 += 32) {  // query blocks that can see the workgroup's keys
+      __syncthreads();                     // previous block's LDS reads are done
+      if (tid < RB::kUnits) {
+        stage_rows<D>(q + base * q_stride + (int64_t)h * D, q_stride, q0, n, tid, qs, qt);
+      } else if (tid < 2 * RB::kUnits) {
+        stage_rows<D>(dout + base * q_stride + (int64_t)h * D, q_stride, q0, n, tid - RB::kUnits, os, ot);
+      }
+      if (tid < 32) {
+        const int row = q0 + tid;
+        lse2[tid] = row < n ? lse[(base + row) * hq + h] * kL2e : __builtin_inff();
+        dts[tid] = row < n ? dt[(base + row) * hq + h] : 0.0f;
+      }
+      __syncthreads();
+      if (kw0 > q0 + 31) continue;  // every key of the wave is after every query of the block (uniform per wave)
+
+      f32x16 sacc = f32x16{}, dpacc = f32x16{};
+      const uint16_t* qrow = &qs[l32 * RB::kLd + 8 * g];
+      const uint16_t* orow = &os[l32 * RB::kLd + 8 * g];
+#pragma unroll
+      for (int ks = 0; ks < D / 16; ++ks) {
+        sacc = mfma32(*reinterpret_cast<const u32x4*>(qrow + 16 * ks), kf[ks], sacc);
+        dpacc = mfma32(*reinterpret_cast<const u32x4*>(orow + 16 * ks), vf[ks], dpacc);
+      }
+      // register i holds query row q0 + c_row(i, g), key kj
+      float pz[16], dz[16];
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4) {
+        const f32x4 l4 = *reinterpret_cast<const f32x4*>(&lse2[8 * q4 + 4 * g]);
+        const f32x4 d4 = *reinterpret_cast<const f32x4*>(&dts[8 * q4 + 4 * g]);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int i = 4 * q4 + e;
+          const int row = q0 + c_row(i, g);
+          const bool ok = key_ok && kj <= row && row < n;
+          const float p = ok ? __builtin_amdgcn_exp2f(__builtin_fmaf(scale2, sacc[i], bias2) - l4[e]) : 0.0f;
+          const float z = p * (dpacc[i] - d4[e]);
+          pz[i] = p;
+          dz[i] = z;
+          ds_acc = __builtin_fmaf(gh, z, ds_acc);
+          dg_acc = __builtin_fmaf(z, s_key, dg_acc);
+          dtau_acc = __builtin_fmaf(z, sacc[i] * inv_sqrt_d, dtau_acc);
+        }
+      }
+      // B operands of the two 16-query MFMA steps: register 8 st + e
+      u32x4 pb[2], zb[2];
+#pragma unroll
+      for (int st = 0; st < 2; ++st)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int i = 8 * st + 2 * j;
+          const uint32_t pp = pack2(pz[i], pz[i + 1]);
+          const uint32_t zz = pack2(dz[i] * dscale, dz[i + 1] * dscale);
+          pb[st][j] = pp;
+          zb[st][j] = zz;
+        }
+#pragma unroll
+      for (int st = 0; st < 2; ++st) {
+#pragma unroll
+        for (int dtile = 0; dtile < D / 32; ++dtile) {
+          const uint16_t* ro = &ot[(dtile * 32 + l32) * RB::tLd + 16 * st + 4 * g];
+          const uint16_t* rq = &qt[(dtile * 32 + l32) * RB::tLd + 16 * st + 4 * g];
+          const u32x2 olo = *reinterpret_cast<const u32x2*>(ro), ohi = *reinterpret_cast<const u32x2*>(ro + 8);
+          const u32x2 qlo = *reinterpret_cast<const u32x2*>(rq), qhi = *reinterpret_cast<const u32x2*>(rq + 8);
+          dvt[dtile] = mfma32(u32x4{olo[0], olo[1], ohi[0], ohi[1]}, pb[st], dvt[dtile]);
+          dkt[dtile] = mfma32(u32x4{qlo[0], qlo[1], qhi[0], qhi[1]}, zb[st], dkt[dtile]);
+        }
+      }
+    }
+    const float dgw = wave_sum(dg_acc), dtw = wave_sum(dtau_acc);
+    if (lane == 0) {
+      red[wave][gg][0] = dgw;
+      red[wave][gg][1] = dtw;
+    }
+  }
+  // dK, dV of the lane's key: register i of tile t holds dim 32 t + c_row(i, g)
+  if (key_ok) {
+    float* dkr = dk + (base + kj) * kv_stride + (int64_t)c * D;
+    float* dvr = dv + (base + kj) * kv_stride + (int64_t)c * D;
+#pragma unroll
+    for (int dtile = 0; dtile < D / 32; ++dtile)
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4) {
+        const int d0 = 32 * dtile + 8 * q4 + 4 * g;
+        *reinterpret_cast<f32x4*>(dkr + d0) =
+            f32x4{dkt[dtile][4 * q4], dkt[dtile][4 * q4 + 1], dkt[dtile][4 * q4 + 2], dkt[dtile][4 * q4 + 3]};
+        *reinterpret_cast<f32x4*>(dvr + d0) =
+            f32x4{dvt[dtile][4 * q4], dvt[dtile][4 * q4 + 1], dvt[dtile][4 * q4 + 2], dvt[dtile][4 * q4 + 3]};
+      }
+  }
+  const float ds_key = xor32_sum(ds_acc);  // the two half-waves hold different query rows
+  if (key_ok && g == 0) ds_part[(int64_t)c * total_kept + base + kj] = ds_key;
+  __syncthreads();
+  if (tid < G) {
+    const int64_t slot = (int64_t)blockIdx.z * gridDim.y + blockIdx.y;
+    float sg = 0.0f, st = 0.0f;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      sg += red[w][tid][0];
+      st += red[w][tid][1];
+    }
+    part_g[slot * hq + c * G + tid] = sg;
+    part_t[slot * hq + c * G + tid] = st;
+  }
+}
+
+template <int D>
+struct KeyTile {
+  static constexpr int kLd = D + 8;       // K, V row-major
+  static constexpr int tLd = kTile + 4;   // K^T
+};
+
+template <int D, int G>
+__global__ __launch_bounds__(kBwdThreads) void bwd_dq_kernel(
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
+    const float* __restrict__ key_score, const float* __restrict__ tau, const float* __restrict__ gain,
+    const tg_segment* __restrict__ segs, int hq, int hkv, const uint16_t* __restrict__ dout,
+    const float* __restrict__ lse, const float* __restrict__ dt, float* __restrict__ dq) {
+  using KT = KeyTile<D>;
+  constexpr int kBM = 128 / G;
+  constexpr int kWavesPerHead = 4 / G;
+  __shared__ __attribute__((aligned(16))) uint16_t ks_[kTile * KT::kLd], vs[kTile * KT::kLd], kt[D * KT::tLd];
+  __shared__ float sc[kTile];
+
+  const tg_segment seg = segs[blockIdx.z];
+  const int n = seg.kept_len;
+  const int q0 = (gridDim.y - 1 - blockIdx.y) * kBM;
+  if (q0 >= n) return;
+  const int q_end = min(q0 + kBM, n);
+  const int c = blockIdx.x;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int g = lane >> 5, l32 = lane & 31;
+  const int hl = wave / kWavesPerHead, h = c * G + hl;
+  const int qw0 = q0 + (wave % kWavesPerHead) * 32;
+  const int qrow = qw0 + l32;
+  const bool row_ok = qrow < n;
+  const int64_t base = seg.kept_start;
+  const int64_t q_stride = (int64_t)hq * D, kv_stride = (int64_t)hkv * D;
+
+  u32x4 qf[D / 16], of[D / 16];
+#pragma unroll
+  for (int ks = 0; ks < D / 16; ++ks) {
+    const int64_t off = (base + qrow) * q_stride + (int64_t)h * D + 16 * ks + 8 * g;
+    qf[ks] = row_ok ? *reinterpret_cast<const u32x4*>(q + off) : u32x4{0, 0, 0, 0};
+    of[ks] = row_ok ? *reinterpret_cast<const u32x4*>(dout + off) : u32x4{0, 0, 0, 0};
+  }
+  const float th = tau != nullptr ? tau[h] : 1.0f;
+  const float inv_sqrt_d = 1.0f / __builtin_sqrtf((float)D);
+  const float scale2 = th * kL2e * inv_sqrt_d, dscale = th * inv_sqrt_d;
+  const bool use_bias = key_score != nullptr && gain != nullptr;
+  const float gb2 = use_bias ? gain[h] * kL2e : 0.0f;
+  const float lse_row = row_ok ? lse[(base + qrow) * hq + h] * kL2e : __builtin_inff();
+  const float dt_row = row_ok ? dt[(base + qrow) * hq + h] : 0.0f;
+
+  f32x16 dqt[D / 32];
+#pragma unroll
+  for (int dtile = 0; dtile < D / 32; ++dtile) dqt[dtile] = f32x16{};
+  const int wlast = qw0 + 31;
+  const int ntiles = (q_end + kTile - 1) / kTile;
+
+  for (int jt = 0; jt < ntiles; ++jt) {
+    const int kv0 = jt * kTile;
+    __syncthreads();
+    {  // K: one unit of 4 keys x 8 dims per thread (row-major and transposed); V: row-major
+      const int units = (kTile / 4) * (D / 8);
+      for (int u = tid; u < units; u += kBwdThreads) {
+        const int kq = u % (kTile / 4), dc = u / (kTile / 4);
+        u32x4 r[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int key = kv0 + 4 * kq + i;
+          const int64_t off = (base + key) * kv_stride + (int64_t)c * D + 8 * dc;
+          r[i] = key < n ? *reinterpret_cast<const u32x4*>(k + off) : u32x4{0, 0, 0, 0};
+          *reinterpret_cast<u32x4*>(&ks_[(4 * kq + i) * KT::kLd + 8 * dc]) = r[i];
+          *reinterpret_cast<u32x4*>(&vs[(4 * kq + i) * KT::kLd + 8 * dc]) =
+              key < n ? *reinterpret_cast<const u32x4*>(v + off) : u32x4{0, 0, 0, 0};
+        }
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const uint32_t sel = (e & 1) ? 0x07060302u : 0x05040100u;
+          const int w = e >> 1;
+          const u32x2 pk = u32x2{__builtin_amdgcn_perm(r[1][w], r[0][w], sel),
+                                 __builtin_amdgcn_perm(r[3][w], r[2][w], sel)};
+          *reinterpret_cast<u32x2*>(&kt[(8 * dc + e) * KT::tLd + 4 * kq]) = pk;
+        }
+      }
+      if (tid < kTile) sc[tid] = use_bias && kv0 + tid < n ? key_score[base + kv0 + tid] : 0.0f;
+    }
+    __syncthreads();
+    if (kv0 > wlast) continue;  // uniform per wave
+
+    u32x4 zb[4];  // scaled dZ^T, B operands of the 4 16-key MFMA steps
+#pragma unroll
+    for (int hf = 0; hf < 2; ++hf) {
+      f32x16 sacc = f32x16{}, dpacc = f32x16{};
+      const uint16_t* krow = &ks_[(hf * 32 + l32) * KT::kLd + 8 * g];
+      const uint16_t* vrow = &vs[(hf * 32 + l32) * KT::kLd + 8 * g];
+#pragma unroll
+      for (int ks = 0; ks < D / 16; ++ks) {
+        sacc = mfma32(*reinterpret_cast<const u32x4*>(krow + 16 * ks), qf[ks], sacc);
+        dpacc = mfma32(*reinterpret_cast<const u32x4*>(vrow + 16 * ks), of[ks], dpacc);
+      }
+      // register i holds key kv0 + 32 hf + c_row(i, g), query qrow
+      float z[16];
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4) {
+        const f32x4 s4 = *reinterpret_cast<const f32x4*>(&sc[hf * 32 + 8 * q4 + 4 * g]);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int i = 4 * q4 + e;
+          const int key = kv0 + hf * 32 + c_row(i, g);
+          const bool ok = row_ok && key <= qrow && key < n;
+          const float p =
+              ok ? __builtin_amdgcn_exp2f(__builtin_fmaf(scale2, sacc[i], gb2 * s4[e]) - lse_row) : 0.0f;
+          z[i] = p * (dpacc[i] - dt_row) * dscale;
+        }
+      }
+#pragma unroll
+      for (int st = 0; st < 2; ++st)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const uint32_t zz = pack2(z[8 * st + 2 * j], z[8 * st + 2 * j + 1]);
+          zb[2 * hf + st][j] = zz;
+        }
+    }
+#pragma unroll
+    for (int s4 = 0; s4 < 4; ++s4)
+#pragma unroll
+      for (int dtile = 0; dtile < D / 32; ++dtile) {
+        const uint16_t* kr = &kt[(dtile * 32 + l32) * KT::tLd + 16 * s4 + 4 * g];
+        const u32x2 lo = *reinterpret_cast<const u32x2*>(kr), hi = *reinterpret_cast<const u32x2*>(kr + 8);
+        dqt[dtile] = mfma32(u32x4{lo[0], lo[1], hi[0], hi[1]}, zb[s4], dqt[dtile]);
+      }
+  }
+  if (row_ok) {
+    float* dqr = dq + (base + qrow) * q_stride + (int64_t)h * D;
+#pragma unroll
+    for (int dtile = 0; dtile < D / 32; ++dtile)
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4)
+        *reinterpret_cast<f32x4*>(dqr + 32 * dtile + 8 * q4 + 4 * g) =
+            f32x4{dqt[dtile][4 * q4], dqt[dtile][4 * q4 + 1], dqt[dtile][4 * q4 + 2], dqt[dtile][4 * q4 + 3]};
+  }
+}
+
+// ds[t] = sum_c ds_part[c][t]; dgain / dtau = sum over the workgroup slots that ran
+__global__ __launch_bounds__(kBwdThreads) void bwd_reduce_kernel(const tg_segment* __restrict__ segs, int n_seg,
+                                                                 int key_blocks, int hq, int hkv, int64_t total_kept,
+                                                                 const float* __restrict__ ds_part,
+                                                                 const float* __restrict__ part_g,
+                                                                 const float* __restrict__ part_t,
+                                                                 float* __restrict__ ds, float* __restrict__ dgain,
+                                                                 float* __restrict__ dtau, int64_t ds_blocks) {
+  __shared__ float red[2][kBwdThreads];
+  const int tid = threadIdx.x;
+  if ((int64_t)blockIdx.x < ds_blocks) {
+    const int64_t t = (int64_t)blockIdx.x * kBwdThreads + tid;
+    if (ds != nullptr && t < total_kept) {
+      float a = 0.0f;
+      for (int c = 0; c < hkv; ++c) a += ds_part[(int64_t)c * total_kept + t];
+      ds[t] = a;
+    }
+    return;
+  }
+  const int h = (int)(blockIdx.x - ds_blocks);  // one block per head
+  float sg = 0.0f, st = 0.0f;
+  const int64_t n_slots = (int64_t)n_seg * key_blocks;
+  for (int64_t s = tid; s < n_slots; s += kBwdThreads) {
+    const int seg_i = (int)(s / key_blocks), y = (int)(s % key_blocks);
+    if (y * kKeyBlock < segs[seg_i].kept_len) {
+      sg += part_g[s * hq + h];
+      st += part_t[s * hq + h];
+    }
+  }
+  red[0][tid] = sg;
+  red[1][tid] = st;
+  __syncthreads();
+  for (int w = kBwdThreads / 2; w > 0; w >>= 1) {
+    if (tid < w) {
+      red[0][tid] += red[0][tid + w];
+      red[1][tid] += red[1][tid + w];
+    }
+    __syncthreads();
+  }
+  if (tid == 0) {
+    if (dgain != nullptr) dgain[h] = red[0][0];
+    if (dtau != nullptr) dtau[h] = red[1][0];
+  }
+}
+
+struct BwdWs {
+  float* dt;
+  float* ds_part;
+  float* part_g;
+  float* part_t;
+};
+
+BwdWs carve(void* ws, const tg_plan_info& info, int hq, int hkv) {
+  const int key_blocks = (int)((info.max_kept_len + kKeyBlock - 1) / kKeyBlock);
+  const int64_t n_slots = (int64_t)info.n_seg * (key_blocks > 0 ? key_blocks : 1);
+  BwdWs w;
+  w.dt = reinterpret_cast<float*>(ws);
+  w.ds_part = w.dt + ((info.total_kept * hq + 63) / 64) * 64;
+  w.part_g = w.ds_part + ((info.total_kept * hkv + 63) / 64) * 64;
+  w.part_t = w.part_g + n_slots * hq;
+  return w;
+}
+
+template <int D, int G>
+hipError_t launch_bwd_dg(const void* q, const void* k, const void* v, const float* ks, const float* tau,
+                         const float* gain, const tg_segment* segs, const tg_plan_info& info, int hq, int hkv,
+                         const void* out, const void* dout, const float* lse, float* dq, float* dk, float* dv,
+                         float* ds, float* dgain, float* dtau, void* workspace, hipStream_t stream) {
+  const BwdWs w = carve(workspace, info, hq, hkv);
+  auto* qb = reinterpret_cast<const uint16_t*>(q);
+  auto* kb = reinterpret_cast<const uint16_t*>(k);
+  auto* vb = reinterpret_cast<const uint16_t*>(v);
+  auto* ob = reinterpret_cast<const uint16_t*>(out);
+  auto* dob = reinterpret_cast<const uint16_t*>(dout);
+  const int key_blocks = (int)((info.max_kept_len + kKeyBlock - 1) / kKeyBlock);
+  if (info.total_kept > 0) {  // with no kept rows only the reduction runs (zero dgain / dtau)
+    const int64_t rows = info.total_kept * hq;
+    const int per_block = kBwdThreads / (D / 8);
+    hipLaunchKernelGGL((bwd_rowdot_kernel<D>), dim3((unsigned)((rows + per_block - 1) / per_block)),
+                       dim3(kBwdThreads), 0, stream, dob, ob, rows, w.dt);
+    hipLaunchKernelGGL((bwd_dkdv_kernel<D, G>), dim3(hkv, key_blocks, info.n_seg), dim3(kBwdThreads), 0, stream, qb,
+                       kb, vb, ks, tau, gain, segs, hq, hkv, dob, lse, w.dt, dk, dv, w.ds_part, info.total_kept,
+                       w.part_g, w.part_t);
+    constexpr int kBM = 128 / G;
+    const int q_tiles = (int)((info.max_kept_len + kBM - 1) / kBM);
+    hipLaunchKernelGGL((bwd_dq_kernel<D, G>), dim3(hkv, q_tiles, info.n_seg), dim3(kBwdThreads), 0, stream, qb, kb,
+                       vb, ks, tau, gain, segs, hq, hkv, dob, lse, w.dt, dq);
+  }
+  const int64_t ds_blocks = (info.total_kept + kBwdThreads - 1) / kBwdThreads;
+  hipLaunchKernelGGL(bwd_reduce_kernel, dim3((unsigned)(ds_blocks + hq)), dim3(kBwdThreads), 0, stream, segs,
+                     info.n_seg, key_blocks, hq, hkv, info.total_kept, w.ds_part, w.part_g, w.part_t, ds, dgain, dtau,
+                     ds_blocks);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+size_t attention_backward_workspace_bytes(const tg_plan_info& info, int hq, int hkv) {
+  const int key_blocks = (int)((info.max_kept_len + kKeyBlock - 1) / kKeyBlock);
+  const int64_t n_slots = (int64_t)info.n_seg * (key_blocks > 0 ? key_blocks : 1);
+  const int64_t floats = ((info.total_kept * hq + 63) / 64) * 64 + ((info.total_kept * hkv + 63) / 64) * 64 +
+                         2 * n_slots * hq;
+  return (size_t)(floats * 4);
+}
+
+hipError_t launch_gated_attention_backward(const void* q, const void* k, const void* v, const float* key_score,
+                                           const float* tau, const float* gain, const tg_segment* segs,
+                                           const tg_plan_info& info, int hq, int hkv, int head_dim, const void* out,
+                                           const void* dout, const float* lse, float* dq, float* dk, float* dv,
+                                           float* ds, float* dgain, float* dtau, void* workspace,
+                                           hipStream_t stream) {
+  const int G = hq / hkv;
+#define TG_BWD_CASE(DD, GG) \
+  if (head_dim == DD && G == GG) \
+    return launch_bwd_dg<DD, GG>(q, k, v, key_score, tau, gain, segs, info, hq, hkv, out, dout, lse, dq, dk, dv, ds, \
+                                 dgain, dtau, workspace, stream);
+  TG_BWD_CASE(128, 1)
+  TG_BWD_CASE(128, 2)
+  TG_BWD_CASE(128, 4)
+  TG_BWD_CASE(64, 1)
+  TG_BWD_CASE(64, 2)
+  TG_BWD_CASE(64, 4)
+#undef TG_BWD_CASE
+  return hipErrorInvalidValue;
+}
+
+}  // namespace tg

@@ -32,48 +32,6 @@ constexpr int kChunk = 256;        // cache rows per workgroup
 constexpr int kDecThreads = 256;   // 4 waves x 64 rows
 constexpr float kLog2eD = 1.4426950408889634f;
 
-// Lane reductions on DPP row operations and the gfx950 row swaps (no LDS
-// round trip).  Every step combines a lane with its partner in an order-free
-// way (a + b and b + a, max), so all lanes of a group end with the same bits.
-template <int CTRL>
-__device__ __forceinline__ float dpp(float x) {
-  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), CTRL, 0xf, 0xf, false));
-}
-constexpr int kQuadXor1 = 0xb1, kQuadXor2 = 0x4e, kRowHalfMirror = 0x141, kRowMirror = 0x140, kRowRor8 = 0x128;
-
-__device__ __forceinline__ float swap16_sum(float x) {  // x + x of lane ^ 16
-  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
-}
-__device__ __forceinline__ float swap16_max(float x) {
-  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return __builtin_fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
-}
-
-// sum over aligned groups of N lanes (N = 8 or 16)
-template <int N>
-__device__ __forceinline__ float group_sum(float x) {
-  x += dpp<kQuadXor1>(x);
-  x += dpp<kQuadXor2>(x);
-  x += dpp<kRowHalfMirror>(x);
-  if (N == 16) x += dpp<kRowMirror>(x);
-  return x;
-}
-__device__ __forceinline__ float wave_sum(float x) { return xor32_sum(swap16_sum(group_sum<16>(x))); }
-__device__ __forceinline__ float wave_max(float x) {
-  x = __builtin_fmaxf(x, dpp<kQuadXor1>(x));
-  x = __builtin_fmaxf(x, dpp<kQuadXor2>(x));
-  x = __builtin_fmaxf(x, dpp<kRowHalfMirror>(x));
-  x = __builtin_fmaxf(x, dpp<kRowMirror>(x));
-  return xor32_max(swap16_max(x));
-}
-// sum over the lanes sharing lane % N (N = 8 or 16)
-template <int N>
-__device__ __forceinline__ float stride_sum(float x) {
-  if (N == 8) x += dpp<kRowRor8>(x);
-  return xor32_sum(swap16_sum(x));
-}
-
 template <int D, int G>
 __global__ __launch_bounds__(kDecThreads) void decode_partial_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ kc, const uint16_t* __restrict__ vc,

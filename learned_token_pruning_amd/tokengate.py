@@ -32,7 +32,8 @@ STATUS_NAMES = {0: "TG_OK", -1: "TG_ERR_INVALID_ARG", -2: "TG_ERR_UNSUPPORTED", 
 EXPORTS = ("tg_status_string", "tg_abi_version", "tg_plan_segments", "tg_gate_workspace_bytes", "tg_gate_score",
            "tg_select_workspace_bytes", "tg_select_topk", "tg_compact_kept", "tg_gated_attention_prefill",
            "tg_gated_attention_prefill_gather", "tg_gated_attention_prefill_query_tau",
-           "tg_decode_workspace_bytes", "tg_gated_attention_decode",
+           "tg_decode_workspace_bytes", "tg_gated_attention_decode", "tg_gated_attention_prefill_lse",
+           "tg_attention_backward_workspace_bytes", "tg_gated_attention_backward",
            "tg_gemm_bf16", "tg_rmsnorm_bf16", "tg_rope_split_bf16", "tg_decoder_layer_workspace_bytes",
            "tg_decoder_layer")
 GEMM_STORE, GEMM_RESIDUAL, GEMM_SWIGLU = 0, 1, 2
@@ -91,6 +92,14 @@ _lib.tg_gated_attention_prefill_gather.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp,
 _lib.tg_gated_attention_prefill_query_tau.restype = _i32
 _lib.tg_gated_attention_prefill_query_tau.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, ctypes.POINTER(PlanInfo),
                                                       _i32, _i32, _i32, _vp, _vp]
+_lib.tg_gated_attention_prefill_lse.restype = _i32
+_lib.tg_gated_attention_prefill_lse.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, ctypes.POINTER(PlanInfo), _i32, _i32,
+                                                _i32, _vp, _vp, _vp]
+_lib.tg_attention_backward_workspace_bytes.restype = _sz
+_lib.tg_attention_backward_workspace_bytes.argtypes = [ctypes.POINTER(PlanInfo), _i32, _i32]
+_lib.tg_gated_attention_backward.restype = _i32
+_lib.tg_gated_attention_backward.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, ctypes.POINTER(PlanInfo), _i32, _i32,
+                                             _i32, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]
 _lib.tg_decode_workspace_bytes.restype = _sz
 _lib.tg_decode_workspace_bytes.argtypes = [_i32, _i32, _i32, _i64]
 _lib.tg_gated_attention_decode.restype = _i32
@@ -316,6 +325,53 @@ def gated_attention_prefill_query_tau(q: torch.Tensor, k: torch.Tensor, v: torch
                                                    ctypes.byref(plan.info), hq, hkv, dh, _ptr(out), _stream(stream))
     _check(st, "tg_gated_attention_prefill_query_tau")
     return out
+
+
+def gated_attention_prefill_lse(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
+                                key_score: Optional[torch.Tensor], tau: Optional[torch.Tensor],
+                                gain: Optional[torch.Tensor], plan: Plan, out: Optional[torch.Tensor] = None,
+                                lse: Optional[torch.Tensor] = None, stream=None):
+    """tg_gated_attention_prefill_lse: returns (out [M, hq, D] bf16, lse [M, hq] fp32)."""
+    m, hq, dh = q.shape
+    hkv = k.shape[1]
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None:
+        lse = torch.empty((m, hq), dtype=torch.float32, device=q.device)
+    st = _lib.tg_gated_attention_prefill_lse(_ptr(q), _ptr(k), _ptr(v), _ptr(key_score), _ptr(tau), _ptr(gain),
+                                             _dev_table(plan), ctypes.byref(plan.info), hq, hkv, dh, _ptr(out),
+                                             _ptr(lse), _stream(stream))
+    _check(st, "tg_gated_attention_prefill_lse")
+    return out, lse
+
+
+def attention_backward_workspace_bytes(plan: Plan, hq: int, hkv: int) -> int:
+    return int(_lib.tg_attention_backward_workspace_bytes(ctypes.byref(plan.info), hq, hkv))
+
+
+def gated_attention_backward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, key_score: Optional[torch.Tensor],
+                             tau: Optional[torch.Tensor], gain: Optional[torch.Tensor], plan: Plan,
+                             out: torch.Tensor, dout: torch.Tensor, lse: torch.Tensor,
+                             workspace: Optional[torch.Tensor] = None, stream=None) -> dict:
+    """tg_gated_attention_backward: returns fp32 dq, dk, dv, ds, dgain, dtau."""
+    m, hq, dh = q.shape
+    hkv = k.shape[1]
+    dev = q.device
+    g = {"dq": torch.empty((m, hq, dh), dtype=torch.float32, device=dev),
+         "dk": torch.empty((m, hkv, dh), dtype=torch.float32, device=dev),
+         "dv": torch.empty((m, hkv, dh), dtype=torch.float32, device=dev),
+         "ds": torch.empty(m, dtype=torch.float32, device=dev),
+         "dgain": torch.empty(hq, dtype=torch.float32, device=dev),
+         "dtau": torch.empty(hq, dtype=torch.float32, device=dev)}
+    if workspace is None:
+        workspace = _workspace(attention_backward_workspace_bytes(plan, hq, hkv), dev)
+    st = _lib.tg_gated_attention_backward(_ptr(q), _ptr(k), _ptr(v), _ptr(key_score), _ptr(tau), _ptr(gain),
+                                          _dev_table(plan), ctypes.byref(plan.info), hq, hkv, dh, _ptr(out),
+                                          _ptr(dout), _ptr(lse), _ptr(g["dq"]), _ptr(g["dk"]), _ptr(g["dv"]),
+                                          _ptr(g["ds"]), _ptr(g["dgain"]), _ptr(g["dtau"]), _ptr(workspace),
+                                          workspace.numel() * workspace.element_size(), _stream(stream))
+    _check(st, "tg_gated_attention_backward")
+    return g
 
 
 def decode_workspace_bytes(batch: int, hq: int, head_dim: int, cache_rows: int) -> int:

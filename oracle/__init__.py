@@ -34,6 +34,7 @@ from .tokengate_ref import (  # noqa: F401
     query_temperature,
     gated_attention_decode,
     gated_attention_backward,
+    attention_logsumexp,
 )
 from .stack_ref import (  # noqa: F401,E402
     round_bf16,

@@ -407,3 +407,33 @@ def gated_attention_backward(q: np.ndarray, k: np.ndarray, v: np.ndarray, s: Opt
             res["dgain"][h] += (dz.sum(axis=0) * s_v[a:b]).sum()
             res["dtau"][h] += (dz * qk).sum()
     return res
+
+
+def attention_logsumexp(q: np.ndarray, k: np.ndarray, s: Optional[np.ndarray], tau: Optional[np.ndarray],
+                        gain: Optional[np.ndarray], kept_offsets: Sequence[int]) -> np.ndarray:
+    """ln sum_{t <= r} exp(z_rt) for every kept row r and query head h, with
+    the logits of gated_attention: the normaliser of the row's softmax, which
+    a flash-style backward keeps from the forward.  Returns [M, Hq] float64.
+    Pinned by the uniform-logit closed form ln(r + 1) and by the weights
+    exp(z - lse) summing to 1 (tests/test_oracle_attention.py)."""
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    m_total, hq, dh = q.shape
+    group = hq // k.shape[1]
+    tau = np.ones(hq) if tau is None else np.asarray(tau, dtype=np.float64)
+    use_bias = s is not None and gain is not None
+    out = np.zeros((m_total, hq))
+    offs = [int(o) for o in kept_offsets]
+    for a, b in zip(offs[:-1], offs[1:]):
+        n = b - a
+        if n == 0:
+            continue
+        causal = np.tril(np.ones((n, n), dtype=bool))
+        for h in range(hq):
+            z = tau[h] * (q[a:b, h] @ k[a:b, h // group].T) / math.sqrt(dh)
+            if use_bias:
+                z = z + float(gain[h]) * np.asarray(s[a:b], dtype=np.float64)[None, :]
+            z = np.where(causal, z, -np.inf)
+            mx = z.max(axis=1)
+            out[a:b, h] = mx + np.log(np.exp(z - mx[:, None]).sum(axis=1))
+    return out

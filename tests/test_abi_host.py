@@ -196,6 +196,28 @@ def test_decode_validation():
     assert call(args(ws=None)) == -3
 
 
+def test_backward_validation():
+    p = _plan()
+    info = ctypes.byref(p.info)
+    ws = tg.attention_backward_workspace_bytes(p, 16, 8)
+    assert ws >= (10 * 16 + 10 * 8) * 4
+    f = L.tg_gated_attention_backward
+    call = lambda **kw: f(*[kw.get(n, FAKE) for n in ("q", "k", "v")], None, None, None, FAKE, info, 16,
+                          kw.get("hkv", 8), kw.get("d", 128), *[kw.get(n, FAKE) for n in ("out", "dout", "lse", "dq",
+                                                                                           "dk", "dv")],
+                          None, None, None, kw.get("ws", FAKE), kw.get("wsb", ws), None)
+    assert call(dout=None) == -1
+    assert call(lse=None) == -1
+    assert call(dq=ctypes.c_void_p(0x10004)) == -1
+    assert call(hkv=6) == -2
+    assert call(d=96) == -2
+    assert call(wsb=ws - 4) == -3
+    assert call(ws=None) == -3
+    g = L.tg_gated_attention_prefill_lse
+    assert g(FAKE, FAKE, FAKE, None, None, None, FAKE, info, 16, 8, 128, FAKE, None, None) == -1  # no lse
+    assert g(FAKE, FAKE, FAKE, None, None, None, FAKE, info, 16, 8, 96, FAKE, FAKE, None) == -2
+
+
 @pytest.mark.skipif(gpu_available(), reason="only meaningful without a GPU: valid calls must report no device")
 def test_valid_calls_report_no_device_without_gpu():
     p = _plan()
@@ -208,6 +230,11 @@ def test_valid_calls_report_no_device_without_gpu():
                                                   FAKE, None) == -4
     assert L.tg_gated_attention_decode(FAKE, FAKE, FAKE, None, None, 0, None, FAKE, 2, 1000, 16, 8, 128, FAKE, FAKE,
                                        tg.decode_workspace_bytes(2, 16, 128, 1000), None) == -4
+    assert L.tg_gated_attention_prefill_lse(FAKE, FAKE, FAKE, None, None, None, FAKE, info, 16, 8, 128, FAKE, FAKE,
+                                            None) == -4
+    assert L.tg_gated_attention_backward(FAKE, FAKE, FAKE, None, None, None, FAKE, info, 16, 8, 128, FAKE, FAKE, FAKE,
+                                         FAKE, FAKE, FAKE, None, None, None, FAKE,
+                                         tg.attention_backward_workspace_bytes(p, 16, 8), None) == -4
 
 
 def test_dense_validation():

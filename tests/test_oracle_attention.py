@@ -301,3 +301,23 @@ def test_backward_matches_torch_autograd():
     g = oracle.gated_attention_backward(q, k, v, s, tau, gain, [0, m], dout)
     for name, t in (("dq", tq), ("dk", tk), ("dv", tv), ("ds", ts), ("dtau", tt), ("dgain", tg)):
         np.testing.assert_allclose(g[name], t.grad.numpy(), rtol=1e-10, atol=1e-11, err_msg=name)
+
+
+def test_logsumexp_closed_form_and_normalisation():
+    rng = np.random.default_rng(33)
+    offs = [0, 6, 17]
+    m, hq, hkv, d = 17, 2, 1, 4
+    q, k = rng.standard_normal((m, hq, d)), rng.standard_normal((m, hkv, d))
+    # uniform logits (tau = 0, no bias): ln(number of visible keys)
+    lse0 = oracle.attention_logsumexp(q, k, None, np.zeros(hq), None, offs)
+    r = np.concatenate([np.arange(6), np.arange(11)]) + 1
+    np.testing.assert_allclose(lse0, np.log(r)[:, None].repeat(hq, 1), rtol=1e-14)
+    # with temperature and bias: exp(z - lse) sums to 1 over the visible keys
+    s = rng.standard_normal(m)
+    tau, gain = np.array([1.3, 0.7]), np.array([0.9, 1.4])
+    lse = oracle.attention_logsumexp(q, k, s, tau, gain, offs)
+    for a, b in zip(offs[:-1], offs[1:]):
+        for row in range(a, b):
+            for h in range(hq):
+                z = [tau[h] * float(q[row, h] @ k[t, 0]) / 2.0 + gain[h] * s[t] for t in range(a, row + 1)]
+                assert sum(math.exp(x - lse[row, h]) for x in z) == pytest.approx(1.0, rel=1e-13)
