@@ -320,7 +320,7 @@ def time_backward(torch, tg, reps=20):
         gain = 0.5 + torch.rand(hq, generator=gen, device=dev)
         plan = tg.plan_segments([0, m], [0], [0], [0], device=dev)
         out, lse = tg.gated_attention_prefill_lse(q, k, v, sc, tau, gain, plan)
-        ws = torch.empty(max(tg.attention_backward_workspace_bytes(plan, hq, hkv), 256), dtype=torch.uint8, device=dev)
+        ws = torch.empty(max(tg.attention_backward_workspace_bytes(plan, hq, hkv, dh), 256), dtype=torch.uint8, device=dev)
 
         def timed(f):
             for _ in range(3):

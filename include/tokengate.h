@@ -277,10 +277,11 @@ int tg_gated_attention_prefill_lse(const void* q, const void* k, const void* v, 
  *   dq [total_kept, hq, head_dim], dk and dv [total_kept, hkv, head_dim] (16-byte aligned);
  *   ds [total_kept], dgain [hq], dtau [hq]: each may be NULL (not written);
  *   without a bias (key_score or gain NULL) ds and dgain come out 0.
- * workspace: device, 16-byte aligned, >= tg_attention_backward_workspace_bytes.
+ * workspace: device, 16-byte aligned, >= tg_attention_backward_workspace_bytes
+ *   (row terms, and fp32 dk / dv / ds partials of up to five query chunks).
  * bf16 MFMA products (P and the scaled dZ rounded to bf16), fp32
  * accumulation; results are deterministic.  Shapes as for the forward. */
-size_t tg_attention_backward_workspace_bytes(const tg_plan_info* info, int hq, int hkv);
+size_t tg_attention_backward_workspace_bytes(const tg_plan_info* info, int hq, int hkv, int head_dim);
 int tg_gated_attention_backward(const void* q, const void* k, const void* v, const float* key_score,
                                 const float* tau, const float* gain, const tg_segment* segs,
                                 const tg_plan_info* info, int hq, int hkv, int head_dim, const void* out,

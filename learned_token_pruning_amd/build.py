@@ -32,7 +32,11 @@ COMMON = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-I", INCLUDE,
 # Per-source extras.  The attention kernel takes row maxima of MFMA results;
 # without NaN semantics fmaxf needs no canonicalising pass over its inputs
 # (NaN inputs to attention give unspecified outputs).
-FILE_FLAGS = {"gated_attention.hip": ["-fno-honor-nans"]}
+# The backward kernels hold more live values than the 256 architectural VGPRs
+# of one wave: keeping MFMA results in VGPRs (AGPRs only as spill space) avoids
+# copying accumulators between the two register files around every product.
+FILE_FLAGS = {"gated_attention.hip": ["-fno-honor-nans"],
+              "gated_attention_bwd.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]}
 
 
 def _run(cmd):

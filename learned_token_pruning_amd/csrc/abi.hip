@@ -274,9 +274,9 @@ int tg_gated_attention_prefill_lse(const void* q, const void* k, const void* v, 
                                                reinterpret_cast<hipStream_t>(stream)));
 }
 
-size_t tg_attention_backward_workspace_bytes(const tg_plan_info* info, int hq, int hkv) {
-  if (!info || hq <= 0 || hkv <= 0 || info->n_seg < 1 || info->total_kept < 0) return 0;
-  return tg::attention_backward_workspace_bytes(*info, hq, hkv);
+size_t tg_attention_backward_workspace_bytes(const tg_plan_info* info, int hq, int hkv, int head_dim) {
+  if (!info || hq <= 0 || hkv <= 0 || head_dim <= 0 || info->n_seg < 1 || info->total_kept < 0) return 0;
+  return tg::attention_backward_workspace_bytes(*info, hq, hkv, head_dim);
 }
 
 int tg_gated_attention_backward(const void* q, const void* k, const void* v, const float* key_score,
@@ -294,7 +294,7 @@ int tg_gated_attention_backward(const void* q, const void* k, const void* v, con
       (tau && !aligned(tau, 4)) || (gain && !aligned(gain, 4)))
     return TG_ERR_INVALID_ARG;
   if (!workspace || !aligned(workspace, 16) ||
-      workspace_bytes < tg::attention_backward_workspace_bytes(*info, hq, hkv))
+      workspace_bytes < tg::attention_backward_workspace_bytes(*info, hq, hkv, head_dim))
     return TG_ERR_WORKSPACE;
   st = check_device();
   if (st != TG_OK) return st;

@@ -148,7 +148,7 @@ hipError_t launch_gated_attention(const void* q, const void* k, const void* v, c
 constexpr int64_t kAttnMaxGatherRows = 16384;
 
 // Backward of the compacted-row attention; lse from the forward (natural log).
-size_t attention_backward_workspace_bytes(const tg_plan_info& info, int hq, int hkv);
+size_t attention_backward_workspace_bytes(const tg_plan_info& info, int hq, int hkv, int head_dim);
 hipError_t launch_gated_attention_backward(const void* q, const void* k, const void* v, const float* key_score,
                                            const float* tau, const float* gain, const tg_segment* segs,
                                            const tg_plan_info& info, int hq, int hkv, int head_dim, const void* out,

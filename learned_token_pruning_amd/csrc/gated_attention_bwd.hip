@@ -79,16 +79,21 @@ struct RowBlock {
 };
 
 template <int D>
-__device__ __forceinline__ void stage_rows(const uint16_t* __restrict__ src, int64_t row_stride, int r0, int nvalid,
-                                           int u, uint16_t* rm, uint16_t* tr) {
+__device__ __forceinline__ void load_rows(const uint16_t* __restrict__ src, int64_t row_stride, int r0, int nvalid,
+                                          int u, u32x4 (&r)[4]) {
   const int rq = u % 8, dc = u / 8;  // rows 4 rq .. 4 rq + 3, dims 8 dc .. 8 dc + 7
-  u32x4 r[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int row = r0 + 4 * rq + i;
     r[i] = row < nvalid ? *reinterpret_cast<const u32x4*>(src + (int64_t)row * row_stride + 8 * dc) : u32x4{0, 0, 0, 0};
-    *reinterpret_cast<u32x4*>(&rm[(4 * rq + i) * RowBlock<D>::kLd + 8 * dc]) = r[i];
   }
+}
+
+template <int D>
+__device__ __forceinline__ void store_rows(int u, const u32x4 (&r)[4], uint16_t* rm, uint16_t* tr) {
+  const int rq = u % 8, dc = u / 8;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) *reinterpret_cast<u32x4*>(&rm[(4 * rq + i) * RowBlock<D>::kLd + 8 * dc]) = r[i];
 #pragma unroll
   for (int e = 0; e < 8; ++e) {
     const uint32_t sel = (e & 1) ? 0x07060302u : 0x05040100u;
@@ -103,17 +108,22 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_dkdv_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
     const float* __restrict__ key_score, const float* __restrict__ tau, const float* __restrict__ gain,
     const tg_segment* __restrict__ segs, int hq, int hkv, const uint16_t* __restrict__ dout,
-    const float* __restrict__ lse, const float* __restrict__ dt, float* __restrict__ dk, float* __restrict__ dv,
-    float* __restrict__ ds_part, int64_t total_kept, float* __restrict__ part_g, float* __restrict__ part_t) {
+    const float* __restrict__ lse, const float* __restrict__ dt, int n_chunks, int qc, float* __restrict__ dk_part,
+    float* __restrict__ dv_part, float* __restrict__ ds_part, int64_t total_kept, float* __restrict__ part_g,
+    float* __restrict__ part_t) {
   using RB = RowBlock<D>;
   __shared__ __attribute__((aligned(16))) uint16_t qs[32 * RB::kLd], qt[D * RB::tLd];
   __shared__ __attribute__((aligned(16))) uint16_t os[32 * RB::kLd], ot[D * RB::tLd];
+  __shared__ __attribute__((aligned(16))) uint16_t kvk[kKeyBlock * RB::kLd], kvv[kKeyBlock * RB::kLd];
   __shared__ float lse2[32], dts[32];
   __shared__ float red[4][G][2];
 
   const tg_segment seg = segs[blockIdx.z];
   const int n = seg.kept_len;
-  const int kb0 = blockIdx.y * kKeyBlock;
+  // blockIdx.y = key block x query chunk: the chunk covers query blocks
+  // [kb0 / 32 + ci qc, + qc) of the prompt (possibly none: then zero partials)
+  const int ci = blockIdx.y % n_chunks;
+  const int kb0 = (blockIdx.y / n_chunks) * kKeyBlock;
   if (kb0 >= n) return;  // uniform
   const int c = blockIdx.x;
   const int tid = threadIdx.x, lane = tid & 63;
@@ -125,15 +135,19 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_dkdv_kernel(
   const int64_t base = seg.kept_start;
   const int64_t q_stride = (int64_t)hq * D, kv_stride = (int64_t)hkv * D;
 
-  // K and V row fragments of the lane's key (B operands: k = 16 ks + 8 g .. + 7)
-  u32x4 kf[D / 16], vf[D / 16];
-#pragma unroll
-  for (int ks = 0; ks < D / 16; ++ks) {
-    kf[ks] = key_ok ? *reinterpret_cast<const u32x4*>(k + (base + kj) * kv_stride + (int64_t)c * D + 16 * ks + 8 * g)
-                    : u32x4{0, 0, 0, 0};
-    vf[ks] = key_ok ? *reinterpret_cast<const u32x4*>(v + (base + kj) * kv_stride + (int64_t)c * D + 16 * ks + 8 * g)
-                    : u32x4{0, 0, 0, 0};
+  // the workgroup's K and V rows, staged once (row-major; B operands of S and
+  // dP read the lane's key row at k = 16 ks + 8 g .. + 7)
+  for (int u = tid; u < kKeyBlock * (D / 8); u += kBwdThreads) {
+    const int r = u / (D / 8), col = 8 * (u % (D / 8));
+    const int key = kb0 + r;
+    const int64_t off = (base + key) * kv_stride + (int64_t)c * D + col;
+    *reinterpret_cast<u32x4*>(&kvk[r * RB::kLd + col]) =
+        key < n ? *reinterpret_cast<const u32x4*>(k + off) : u32x4{0, 0, 0, 0};
+    *reinterpret_cast<u32x4*>(&kvv[r * RB::kLd + col]) =
+        key < n ? *reinterpret_cast<const u32x4*>(v + off) : u32x4{0, 0, 0, 0};
   }
+  const uint16_t* krow_l = &kvk[(32 * wave + l32) * RB::kLd + 8 * g];
+  const uint16_t* vrow_l = &kvv[(32 * wave + l32) * RB::kLd + 8 * g];
   const bool use_bias = key_score != nullptr && gain != nullptr;
   const float s_key = use_bias && key_ok ? key_score[base + kj] : 0.0f;
 
@@ -146,37 +160,59 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_dkdv_kernel(
   float ds_acc = 0.0f;
   const float inv_sqrt_d = 1.0f / __builtin_sqrtf((float)D);
 
-  for (int gg = 0; gg < G; ++gg) {
+  // (head, query block) pairs in order; the next pair's rows are loaded into
+  // registers while the current one computes
+  const int qb_begin = kb0 / 32 + ci * qc;
+  const int nqb = max(0, min(qb_begin + qc, (n + 31) / 32) - qb_begin);  // query blocks of this chunk
+  const int total = G * nqb;
+  u32x4 sreg[4];
+  float slse = 0.0f, sdt = 0.0f;
+  auto load_block = [&](int it) {
+    const int h = c * G + it / nqb, q0 = 32 * (qb_begin + it % nqb);
+    if (tid < RB::kUnits)
+      load_rows<D>(q + base * q_stride + (int64_t)h * D, q_stride, q0, n, tid, sreg);
+    else if (tid < 2 * RB::kUnits)
+      load_rows<D>(dout + base * q_stride + (int64_t)h * D, q_stride, q0, n, tid - RB::kUnits, sreg);
+    if (tid < 32) {
+      const int row = q0 + tid;
+      slse = row < n ? lse[(base + row) * hq + h] * kL2e : __builtin_inff();
+      sdt = row < n ? dt[(base + row) * hq + h] : 0.0f;
+    }
+  };
+  if (total > 0) load_block(0);
+  float dg_acc = 0.0f, dtau_acc = 0.0f;
+  if (tid < 4 * G) red[tid / G][tid % G][0] = red[tid / G][tid % G][1] = 0.0f;  // heads with no block here
+  for (int it = 0; it < total; ++it) {
+    const int gg = it / nqb, q0 = 32 * (qb_begin + it % nqb);
     const int h = c * G + gg;
     const float th = tau != nullptr ? tau[h] : 1.0f;
-    const float scale2 = th * kL2e * inv_sqrt_d;      // exp2-domain logit per unit q.k
-    const float dscale = th * inv_sqrt_d;             // dZ -> dQ, dK factor
+    const float scale2 = th * kL2e * inv_sqrt_d;  // exp2-domain logit per unit q.k
+    const float dscale = th * inv_sqrt_d;         // dZ -> dQ, dK factor
     const float gh = use_bias ? gain[h] : 0.0f;
-    const float bias2 = gh * kL2e * s_key;            // exp2-domain bias of the lane's key
-    float dg_acc = 0.0f, dtau_acc = 0.0f;
+    const float bias2 = gh * kL2e * s_key;        // exp2-domain bias of the lane's key
 
-    for (int q0 = kb0; q0 < n; q0 += 32) {  // query blocks that can see the workgroup's keys
-      __syncthreads();                     // previous block's LDS reads are done
-      if (tid < RB::kUnits) {
-        stage_rows<D>(q + base * q_stride + (int64_t)h * D, q_stride, q0, n, tid, qs, qt);
-      } else if (tid < 2 * RB::kUnits) {
-        stage_rows<D>(dout + base * q_stride + (int64_t)h * D, q_stride, q0, n, tid - RB::kUnits, os, ot);
-      }
-      if (tid < 32) {
-        const int row = q0 + tid;
-        lse2[tid] = row < n ? lse[(base + row) * hq + h] * kL2e : __builtin_inff();
-        dts[tid] = row < n ? dt[(base + row) * hq + h] : 0.0f;
-      }
-      __syncthreads();
-      if (kw0 > q0 + 31) continue;  // every key of the wave is after every query of the block (uniform per wave)
+    __syncthreads();  // the previous block's LDS reads are done
+    if (tid < RB::kUnits)
+      store_rows<D>(tid, sreg, qs, qt);
+    else if (tid < 2 * RB::kUnits)
+      store_rows<D>(tid - RB::kUnits, sreg, os, ot);
+    if (tid < 32) {
+      lse2[tid] = slse;
+      dts[tid] = sdt;
+    }
+    if (it + 1 < total) load_block(it + 1);
+    __syncthreads();
 
+    if (kw0 <= q0 + 31) {  // some key of the wave is visible to some query of the block (uniform per wave)
       f32x16 sacc = f32x16{}, dpacc = f32x16{};
       const uint16_t* qrow = &qs[l32 * RB::kLd + 8 * g];
       const uint16_t* orow = &os[l32 * RB::kLd + 8 * g];
 #pragma unroll
       for (int ks = 0; ks < D / 16; ++ks) {
-        sacc = mfma32(*reinterpret_cast<const u32x4*>(qrow + 16 * ks), kf[ks], sacc);
-        dpacc = mfma32(*reinterpret_cast<const u32x4*>(orow + 16 * ks), vf[ks], dpacc);
+        sacc = mfma32(*reinterpret_cast<const u32x4*>(qrow + 16 * ks), *reinterpret_cast<const u32x4*>(krow_l + 16 * ks),
+                      sacc);
+        dpacc = mfma32(*reinterpret_cast<const u32x4*>(orow + 16 * ks),
+                       *reinterpret_cast<const u32x4*>(vrow_l + 16 * ks), dpacc);
       }
       // register i holds query row q0 + c_row(i, g), key kj
       float pz[16], dz[16];
@@ -223,16 +259,21 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_dkdv_kernel(
         }
       }
     }
-    const float dgw = wave_sum(dg_acc), dtw = wave_sum(dtau_acc);
-    if (lane == 0) {
-      red[wave][gg][0] = dgw;
-      red[wave][gg][1] = dtw;
+    if (it % nqb == nqb - 1) {  // the head's last block: publish its dg / dtau partial
+      const float dgw = wave_sum(dg_acc), dtw = wave_sum(dtau_acc);
+      if (lane == 0) {
+        red[wave][gg][0] = dgw;
+        red[wave][gg][1] = dtw;
+      }
+      dg_acc = 0.0f;
+      dtau_acc = 0.0f;
     }
   }
   // dK, dV of the lane's key: register i of tile t holds dim 32 t + c_row(i, g)
   if (key_ok) {
-    float* dkr = dk + (base + kj) * kv_stride + (int64_t)c * D;
-    float* dvr = dv + (base + kj) * kv_stride + (int64_t)c * D;
+    const int64_t prow = ((int64_t)ci * total_kept + base + kj) * kv_stride + (int64_t)c * D;
+    float* dkr = dk_part + prow;
+    float* dvr = dv_part + prow;
 #pragma unroll
     for (int dtile = 0; dtile < D / 32; ++dtile)
 #pragma unroll
@@ -245,7 +286,7 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_dkdv_kernel(
       }
   }
   const float ds_key = xor32_sum(ds_acc);  // the two half-waves hold different query rows
-  if (key_ok && g == 0) ds_part[(int64_t)c * total_kept + base + kj] = ds_key;
+  if (key_ok && g == 0) ds_part[((int64_t)ci * hkv + c) * total_kept + base + kj] = ds_key;
   __syncthreads();
   if (tid < G) {
     const int64_t slot = (int64_t)blockIdx.z * gridDim.y + blockIdx.y;
@@ -315,34 +356,47 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_dq_kernel(
   const int wlast = qw0 + 31;
   const int ntiles = (q_end + kTile - 1) / kTile;
 
+  // K / V units of 4 keys x 8 dims: the next tile's are loaded into registers
+  // while the current tile computes
+  constexpr int kUnitsK = (kTile / 4) * (D / 8);  // <= kBwdThreads
+  u32x4 kr[4], vr[4];
+  float scr = 0.0f;
+  auto load_tile = [&](int jt) {
+    const int kv0 = jt * kTile;
+    if (tid < kUnitsK) {
+      const int kq = tid % (kTile / 4), dc = tid / (kTile / 4);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int key = kv0 + 4 * kq + i;
+        const int64_t off = (base + key) * kv_stride + (int64_t)c * D + 8 * dc;
+        kr[i] = key < n ? *reinterpret_cast<const u32x4*>(k + off) : u32x4{0, 0, 0, 0};
+        vr[i] = key < n ? *reinterpret_cast<const u32x4*>(v + off) : u32x4{0, 0, 0, 0};
+      }
+    }
+    if (tid < kTile) scr = use_bias && kv0 + tid < n ? key_score[base + kv0 + tid] : 0.0f;
+  };
+  load_tile(0);
   for (int jt = 0; jt < ntiles; ++jt) {
     const int kv0 = jt * kTile;
-    __syncthreads();
-    {  // K: one unit of 4 keys x 8 dims per thread (row-major and transposed); V: row-major
-      const int units = (kTile / 4) * (D / 8);
-      for (int u = tid; u < units; u += kBwdThreads) {
-        const int kq = u % (kTile / 4), dc = u / (kTile / 4);
-        u32x4 r[4];
+    __syncthreads();  // the previous tile's LDS reads are done
+    if (tid < kUnitsK) {  // K row-major and transposed, V row-major
+      const int kq = tid % (kTile / 4), dc = tid / (kTile / 4);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int key = kv0 + 4 * kq + i;
-          const int64_t off = (base + key) * kv_stride + (int64_t)c * D + 8 * dc;
-          r[i] = key < n ? *reinterpret_cast<const u32x4*>(k + off) : u32x4{0, 0, 0, 0};
-          *reinterpret_cast<u32x4*>(&ks_[(4 * kq + i) * KT::kLd + 8 * dc]) = r[i];
-          *reinterpret_cast<u32x4*>(&vs[(4 * kq + i) * KT::kLd + 8 * dc]) =
-              key < n ? *reinterpret_cast<const u32x4*>(v + off) : u32x4{0, 0, 0, 0};
-        }
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const uint32_t sel = (e & 1) ? 0x07060302u : 0x05040100u;
-          const int w = e >> 1;
-          const u32x2 pk = u32x2{__builtin_amdgcn_perm(r[1][w], r[0][w], sel),
-                                 __builtin_amdgcn_perm(r[3][w], r[2][w], sel)};
-          *reinterpret_cast<u32x2*>(&kt[(8 * dc + e) * KT::tLd + 4 * kq]) = pk;
-        }
+      for (int i = 0; i < 4; ++i) {
+        *reinterpret_cast<u32x4*>(&ks_[(4 * kq + i) * KT::kLd + 8 * dc]) = kr[i];
+        *reinterpret_cast<u32x4*>(&vs[(4 * kq + i) * KT::kLd + 8 * dc]) = vr[i];
       }
-      if (tid < kTile) sc[tid] = use_bias && kv0 + tid < n ? key_score[base + kv0 + tid] : 0.0f;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const uint32_t sel = (e & 1) ? 0x07060302u : 0x05040100u;
+        const int w = e >> 1;
+        const u32x2 pk = u32x2{__builtin_amdgcn_perm(kr[1][w], kr[0][w], sel),
+                               __builtin_amdgcn_perm(kr[3][w], kr[2][w], sel)};
+        *reinterpret_cast<u32x2*>(&kt[(8 * dc + e) * KT::tLd + 4 * kq]) = pk;
+      }
     }
+    if (tid < kTile) sc[tid] = scr;
+    if (jt + 1 < ntiles) load_tile(jt + 1);
     __syncthreads();
     if (kv0 > wlast) continue;  // uniform per wave
 
@@ -400,31 +454,48 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_dq_kernel(
   }
 }
 
-// ds[t] = sum_c ds_part[c][t]; dgain / dtau = sum over the workgroup slots that ran
-__global__ __launch_bounds__(kBwdThreads) void bwd_reduce_kernel(const tg_segment* __restrict__ segs, int n_seg,
-                                                                 int key_blocks, int hq, int hkv, int64_t total_kept,
-                                                                 const float* __restrict__ ds_part,
-                                                                 const float* __restrict__ part_g,
-                                                                 const float* __restrict__ part_t,
-                                                                 float* __restrict__ ds, float* __restrict__ dgain,
-                                                                 float* __restrict__ dtau, int64_t ds_blocks) {
-  __shared__ float red[2][kBwdThreads];
-  const int tid = threadIdx.x;
-  if ((int64_t)blockIdx.x < ds_blocks) {
-    const int64_t t = (int64_t)blockIdx.x * kBwdThreads + tid;
-    if (ds != nullptr && t < total_kept) {
-      float a = 0.0f;
-      for (int c = 0; c < hkv; ++c) a += ds_part[(int64_t)c * total_kept + t];
-      ds[t] = a;
+// dk, dv: sum of the chunk partials; ds[t] = sum over chunks and KV heads
+// (fixed order, so results are deterministic)
+__global__ __launch_bounds__(kBwdThreads) void bwd_reduce_rows_kernel(int n_chunks, int hkv, int64_t total_kept,
+                                                                      int64_t kv_elems, const float* __restrict__ dk_part,
+                                                                      const float* __restrict__ dv_part,
+                                                                      const float* __restrict__ ds_part,
+                                                                      float* __restrict__ dk, float* __restrict__ dv,
+                                                                      float* __restrict__ ds) {
+  const int64_t i = (int64_t)blockIdx.x * kBwdThreads + threadIdx.x;  // 4-float group of dk / dv, or a ds row
+  const int64_t n4 = kv_elems / 4;
+  if (i < n4) {
+    f32x4 a = *reinterpret_cast<const f32x4*>(dk_part + 4 * i);
+    f32x4 b = *reinterpret_cast<const f32x4*>(dv_part + 4 * i);
+    for (int c = 1; c < n_chunks; ++c) {
+      a += *reinterpret_cast<const f32x4*>(dk_part + c * kv_elems + 4 * i);
+      b += *reinterpret_cast<const f32x4*>(dv_part + c * kv_elems + 4 * i);
     }
-    return;
+    *reinterpret_cast<f32x4*>(dk + 4 * i) = a;
+    *reinterpret_cast<f32x4*>(dv + 4 * i) = b;
+  } else if (ds != nullptr && i - n4 < total_kept) {
+    const int64_t t = i - n4;
+    float a = 0.0f;
+    for (int c = 0; c < n_chunks; ++c)
+      for (int h = 0; h < hkv; ++h) a += ds_part[((int64_t)c * hkv + h) * total_kept + t];
+    ds[t] = a;
   }
-  const int h = (int)(blockIdx.x - ds_blocks);  // one block per head
+}
+
+// dgain / dtau = sum over the workgroup slots that ran, one block per head
+__global__ __launch_bounds__(kBwdThreads) void bwd_reduce_params_kernel(const tg_segment* __restrict__ segs, int n_seg,
+                                                                        int slots_per_seg, int n_chunks, int hq,
+                                                                        const float* __restrict__ part_g,
+                                                                        const float* __restrict__ part_t,
+                                                                        float* __restrict__ dgain,
+                                                                        float* __restrict__ dtau) {
+  __shared__ float red[2][kBwdThreads];
+  const int tid = threadIdx.x, h = blockIdx.x;
   float sg = 0.0f, st = 0.0f;
-  const int64_t n_slots = (int64_t)n_seg * key_blocks;
+  const int64_t n_slots = (int64_t)n_seg * slots_per_seg;
   for (int64_t s = tid; s < n_slots; s += kBwdThreads) {
-    const int seg_i = (int)(s / key_blocks), y = (int)(s % key_blocks);
-    if (y * kKeyBlock < segs[seg_i].kept_len) {
+    const int seg_i = (int)(s / slots_per_seg), y = (int)(s % slots_per_seg);
+    if ((y / n_chunks) * kKeyBlock < segs[seg_i].kept_len) {
       sg += part_g[s * hq + h];
       st += part_t[s * hq + h];
     }
@@ -445,21 +516,52 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_reduce_kernel(const tg_segmen
   }
 }
 
+// Work split of bwd_dkdv: 128-key blocks x query chunks of qc 32-row blocks
+// (at most about four chunks per key block, so the longest workgroup walks
+// about a quarter of the prompt).
+struct BwdGeom {
+  int key_blocks, qc, n_chunks;
+  int64_t n_slots;
+};
+BwdGeom bwd_geom(const tg_plan_info& info) {
+  BwdGeom g;
+  const int max_len = (int)info.max_kept_len;
+  g.key_blocks = max(1, (max_len + kKeyBlock - 1) / kKeyBlock);
+  const int max_qb = max(1, (max_len + 31) / 32);
+  g.qc = max(8, (max_qb + 3) / 4);
+  g.n_chunks = (max_qb + g.qc - 1) / g.qc;
+  g.n_slots = (int64_t)info.n_seg * g.key_blocks * g.n_chunks;
+  return g;
+}
+
 struct BwdWs {
   float* dt;
   float* ds_part;
+  float* dk_part;
+  float* dv_part;
   float* part_g;
   float* part_t;
 };
 
-BwdWs carve(void* ws, const tg_plan_info& info, int hq, int hkv) {
-  const int key_blocks = (int)((info.max_kept_len + kKeyBlock - 1) / kKeyBlock);
-  const int64_t n_slots = (int64_t)info.n_seg * (key_blocks > 0 ? key_blocks : 1);
+int64_t round64(int64_t x) { return (x + 63) / 64 * 64; }
+
+int64_t bwd_ws_floats(const tg_plan_info& info, int hq, int hkv, int head_dim) {
+  const BwdGeom g = bwd_geom(info);
+  const int64_t kv = info.total_kept * hkv * head_dim;
+  return round64(info.total_kept * hq) + round64((int64_t)g.n_chunks * hkv * info.total_kept) +
+         2 * round64(g.n_chunks * kv) + 2 * g.n_slots * hq;
+}
+
+BwdWs carve(void* ws, const tg_plan_info& info, int hq, int hkv, int head_dim) {
+  const BwdGeom g = bwd_geom(info);
+  const int64_t kv = info.total_kept * hkv * head_dim;
   BwdWs w;
   w.dt = reinterpret_cast<float*>(ws);
-  w.ds_part = w.dt + ((info.total_kept * hq + 63) / 64) * 64;
-  w.part_g = w.ds_part + ((info.total_kept * hkv + 63) / 64) * 64;
-  w.part_t = w.part_g + n_slots * hq;
+  w.ds_part = w.dt + round64(info.total_kept * hq);
+  w.dk_part = w.ds_part + round64((int64_t)g.n_chunks * hkv * info.total_kept);
+  w.dv_part = w.dk_part + round64(g.n_chunks * kv);
+  w.part_g = w.dv_part + round64(g.n_chunks * kv);
+  w.part_t = w.part_g + g.n_slots * hq;
   return w;
 }
 
@@ -468,41 +570,40 @@ hipError_t launch_bwd_dg(const void* q, const void* k, const void* v, const floa
                          const float* gain, const tg_segment* segs, const tg_plan_info& info, int hq, int hkv,
                          const void* out, const void* dout, const float* lse, float* dq, float* dk, float* dv,
                          float* ds, float* dgain, float* dtau, void* workspace, hipStream_t stream) {
-  const BwdWs w = carve(workspace, info, hq, hkv);
+  const BwdWs w = carve(workspace, info, hq, hkv, D);
+  const BwdGeom geo = bwd_geom(info);
   auto* qb = reinterpret_cast<const uint16_t*>(q);
   auto* kb = reinterpret_cast<const uint16_t*>(k);
   auto* vb = reinterpret_cast<const uint16_t*>(v);
   auto* ob = reinterpret_cast<const uint16_t*>(out);
   auto* dob = reinterpret_cast<const uint16_t*>(dout);
-  const int key_blocks = (int)((info.max_kept_len + kKeyBlock - 1) / kKeyBlock);
-  if (info.total_kept > 0) {  // with no kept rows only the reduction runs (zero dgain / dtau)
+  if (info.total_kept > 0) {  // with no kept rows only the parameter reduction runs (zero dgain / dtau)
     const int64_t rows = info.total_kept * hq;
     const int per_block = kBwdThreads / (D / 8);
     hipLaunchKernelGGL((bwd_rowdot_kernel<D>), dim3((unsigned)((rows + per_block - 1) / per_block)),
                        dim3(kBwdThreads), 0, stream, dob, ob, rows, w.dt);
-    hipLaunchKernelGGL((bwd_dkdv_kernel<D, G>), dim3(hkv, key_blocks, info.n_seg), dim3(kBwdThreads), 0, stream, qb,
-                       kb, vb, ks, tau, gain, segs, hq, hkv, dob, lse, w.dt, dk, dv, w.ds_part, info.total_kept,
-                       w.part_g, w.part_t);
+    hipLaunchKernelGGL((bwd_dkdv_kernel<D, G>), dim3(hkv, geo.key_blocks * geo.n_chunks, info.n_seg),
+                       dim3(kBwdThreads), 0, stream, qb, kb, vb, ks, tau, gain, segs, hq, hkv, dob, lse, w.dt,
+                       geo.n_chunks, geo.qc, w.dk_part, w.dv_part, w.ds_part, info.total_kept, w.part_g, w.part_t);
     constexpr int kBM = 128 / G;
     const int q_tiles = (int)((info.max_kept_len + kBM - 1) / kBM);
     hipLaunchKernelGGL((bwd_dq_kernel<D, G>), dim3(hkv, q_tiles, info.n_seg), dim3(kBwdThreads), 0, stream, qb, kb,
                        vb, ks, tau, gain, segs, hq, hkv, dob, lse, w.dt, dq);
+    const int64_t kv_elems = info.total_kept * hkv * D;
+    const int64_t items = kv_elems / 4 + info.total_kept;
+    hipLaunchKernelGGL(bwd_reduce_rows_kernel, dim3((unsigned)((items + kBwdThreads - 1) / kBwdThreads)),
+                       dim3(kBwdThreads), 0, stream, geo.n_chunks, hkv, info.total_kept, kv_elems, w.dk_part,
+                       w.dv_part, w.ds_part, dk, dv, ds);
   }
-  const int64_t ds_blocks = (info.total_kept + kBwdThreads - 1) / kBwdThreads;
-  hipLaunchKernelGGL(bwd_reduce_kernel, dim3((unsigned)(ds_blocks + hq)), dim3(kBwdThreads), 0, stream, segs,
-                     info.n_seg, key_blocks, hq, hkv, info.total_kept, w.ds_part, w.part_g, w.part_t, ds, dgain, dtau,
-                     ds_blocks);
+  hipLaunchKernelGGL(bwd_reduce_params_kernel, dim3(hq), dim3(kBwdThreads), 0, stream, segs, info.n_seg,
+                     geo.key_blocks * geo.n_chunks, geo.n_chunks, hq, w.part_g, w.part_t, dgain, dtau);
   return hipGetLastError();
 }
 
 }  // namespace
 
-size_t attention_backward_workspace_bytes(const tg_plan_info& info, int hq, int hkv) {
-  const int key_blocks = (int)((info.max_kept_len + kKeyBlock - 1) / kKeyBlock);
-  const int64_t n_slots = (int64_t)info.n_seg * (key_blocks > 0 ? key_blocks : 1);
-  const int64_t floats = ((info.total_kept * hq + 63) / 64) * 64 + ((info.total_kept * hkv + 63) / 64) * 64 +
-                         2 * n_slots * hq;
-  return (size_t)(floats * 4);
+size_t attention_backward_workspace_bytes(const tg_plan_info& info, int hq, int hkv, int head_dim) {
+  return (size_t)(bwd_ws_floats(info, hq, hkv, head_dim) * 4);
 }
 
 hipError_t launch_gated_attention_backward(const void* q, const void* k, const void* v, const float* key_score,

@@ -96,7 +96,7 @@ _lib.tg_gated_attention_prefill_lse.restype = _i32
 _lib.tg_gated_attention_prefill_lse.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, ctypes.POINTER(PlanInfo), _i32, _i32,
                                                 _i32, _vp, _vp, _vp]
 _lib.tg_attention_backward_workspace_bytes.restype = _sz
-_lib.tg_attention_backward_workspace_bytes.argtypes = [ctypes.POINTER(PlanInfo), _i32, _i32]
+_lib.tg_attention_backward_workspace_bytes.argtypes = [ctypes.POINTER(PlanInfo), _i32, _i32, _i32]
 _lib.tg_gated_attention_backward.restype = _i32
 _lib.tg_gated_attention_backward.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, ctypes.POINTER(PlanInfo), _i32, _i32,
                                              _i32, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]
@@ -345,8 +345,8 @@ def gated_attention_prefill_lse(q: torch.Tensor, k: torch.Tensor, v: torch.Tenso
     return out, lse
 
 
-def attention_backward_workspace_bytes(plan: Plan, hq: int, hkv: int) -> int:
-    return int(_lib.tg_attention_backward_workspace_bytes(ctypes.byref(plan.info), hq, hkv))
+def attention_backward_workspace_bytes(plan: Plan, hq: int, hkv: int, head_dim: int) -> int:
+    return int(_lib.tg_attention_backward_workspace_bytes(ctypes.byref(plan.info), hq, hkv, head_dim))
 
 
 def gated_attention_backward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, key_score: Optional[torch.Tensor],
@@ -364,7 +364,7 @@ def gated_attention_backward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, 
          "dgain": torch.empty(hq, dtype=torch.float32, device=dev),
          "dtau": torch.empty(hq, dtype=torch.float32, device=dev)}
     if workspace is None:
-        workspace = _workspace(attention_backward_workspace_bytes(plan, hq, hkv), dev)
+        workspace = _workspace(attention_backward_workspace_bytes(plan, hq, hkv, dh), dev)
     st = _lib.tg_gated_attention_backward(_ptr(q), _ptr(k), _ptr(v), _ptr(key_score), _ptr(tau), _ptr(gain),
                                           _dev_table(plan), ctypes.byref(plan.info), hq, hkv, dh, _ptr(out),
                                           _ptr(dout), _ptr(lse), _ptr(g["dq"]), _ptr(g["dk"]), _ptr(g["dv"]),

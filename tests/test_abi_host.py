@@ -199,7 +199,7 @@ def test_decode_validation():
 def test_backward_validation():
     p = _plan()
     info = ctypes.byref(p.info)
-    ws = tg.attention_backward_workspace_bytes(p, 16, 8)
+    ws = tg.attention_backward_workspace_bytes(p, 16, 8, 128)
     assert ws >= (10 * 16 + 10 * 8) * 4
     f = L.tg_gated_attention_backward
     call = lambda **kw: f(*[kw.get(n, FAKE) for n in ("q", "k", "v")], None, None, None, FAKE, info, 16,
@@ -234,7 +234,7 @@ def test_valid_calls_report_no_device_without_gpu():
                                             None) == -4
     assert L.tg_gated_attention_backward(FAKE, FAKE, FAKE, None, None, None, FAKE, info, 16, 8, 128, FAKE, FAKE, FAKE,
                                          FAKE, FAKE, FAKE, None, None, None, FAKE,
-                                         tg.attention_backward_workspace_bytes(p, 16, 8), None) == -4
+                                         tg.attention_backward_workspace_bytes(p, 16, 8, 128), None) == -4
 
 
 def test_dense_validation():
