@@ -442,7 +442,9 @@ def main():
     ap.add_argument("--only-long", action="store_true", help="time only the 128K-token layer (profiling)")
     ap.add_argument("--no-stack", action="store_true", help="skip the 28-layer pruned-stack prefill")
     ap.add_argument("--only-stack", action="store_true", help="time only the 28-layer pruned-stack prefill")
-    ap.add_argument("--no-decode", action="store_true", help="skip the decode-step timing")
+    ap.add_argument("--no-decode", action="store_true", help="skip the decode-step and backward timings")
+    ap.add_argument("--only-decode", action="store_true",
+                    help="time only the decode step and the attention backward (profiling)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="also run one plain 256 MiB device copy (reference for rocprofv3 FETCH_SIZE / WRITE_SIZE)")
     args = ap.parse_args()
@@ -472,9 +474,11 @@ def main():
 
     result = None
     l16 = None
-    if args.only_stack:
+    if args.only_decode:
+        args.only_long, args.no_long, args.no_stack, args.no_cpu_baseline = True, True, True, True
+    elif args.only_stack:
         args.only_long, args.no_long = True, True
-    if args.only_long:
+    if args.only_long and not args.only_decode:
         args.no_decode = True
     if not args.only_long:
         log("generating the 16K-token workload")
@@ -586,6 +590,11 @@ def main():
                       "data": "synthetic", "config": {"workload": stack["workload"]}}
         result["stack_n65536_k4096"] = stack
 
+    if args.only_decode:
+        result = {"metric": METRIC, "value": None, "unit": "tokens/s", "n_gpus": 1, "steps": 0,
+                  "warmup": 0, "ms_per_step": None, "higher_is_better": True, "scaling": "weak",
+                  "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+                  "config": {"workload": "decode step and attention backward only (profiling mode)"}}
     if not args.no_decode and result is not None:
         log("timing the decode step over pruned and unpruned caches")
         result["decode_b32"] = time_decode(torch, tg)
