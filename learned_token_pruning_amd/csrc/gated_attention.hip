@@ -310,14 +310,6 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
   // One half-step; P = hs & 1 (compile time, so the register sets are static).
   auto half_step = [&](int hs, auto p_) {
     constexpr int P = decltype(p_)::value;
-    // stores first, so that the LDS writes overlap this half-step's work instead
-    // of delaying its barrier: K tile hs + 1 and V tile hs - 1 from set P ^ 1
-    // (loaded one half-step ago) into the buffers last read in the previous half-step
-    if (stage_k) {
-      if (hs + 1 < ntiles) store_k<D, G>(stg, sm, P ^ 1, gtid, sreg[P ^ 1], sr[P ^ 1], ratio);
-    } else {
-      if (hs >= 1 && hs - 1 < ntiles) store_v<D>(stg, sm, P ^ 1, sreg[P ^ 1]);
-    }
     // loads: K tile hs + 2 (threads 0-255) and V tile hs (threads 256-511) into set P
     if (stage_k) {
       if (hs + 2 < ntiles)
@@ -422,6 +414,14 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
       }
     }
 
+    // stores last: K tile hs + 1 and V tile hs - 1 from set P ^ 1 (loaded one
+    // half-step ago, so each global load has two half-steps to land) into the
+    // buffers nobody reads during this half-step
+    if (stage_k) {
+      if (hs + 1 < ntiles) store_k<D, G>(stg, sm, P ^ 1, gtid, sreg[P ^ 1], sr[P ^ 1], ratio);
+    } else {
+      if (hs >= 1 && hs - 1 < ntiles) store_v<D>(stg, sm, P ^ 1, sreg[P ^ 1]);
+    }
     __syncthreads();
   };
   for (int hs = 0; hs < ntiles + 2; hs += 2) {
