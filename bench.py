@@ -43,9 +43,10 @@ def log(*a):
 class Pipeline:
     """Device-resident inputs, outputs and workspaces of one gated layer."""
 
-    def __init__(self, layer, k_budget, torch, tg, gather=False, query_tau=False):
+    def __init__(self, layer, k_budget, torch, tg, gather=False, query_tau=False, prepacked=True):
         assert not (gather and query_tau)
         self.torch, self.tg, self.gather, self.query_tau = torch, tg, gather, query_tau
+        self.prepacked = prepacked
         dev = torch.device("cuda")
         seg = layer.segments.with_budget(k_budget)
         self.layer, self.seg = layer, seg
@@ -60,6 +61,8 @@ class Pipeline:
         m = self.plan.total_kept
         self.n, self.m = seg.n_tokens, m
         self.x, self.w1, self.w2 = bf(layer.x), bf(layer.w1), f32(layer.w2)
+        # the gate's W1 in MFMA fragment order, packed once (weights are constant across steps)
+        self.w1p = tg.gate_pack_w1(self.w1) if prepacked else None
         self.q, self.k, self.v = bf(layer.q), bf(layer.k), bf(layer.v)
         self.tau, self.gain = f32(layer.tau), f32(layer.gain)
         self.scores = torch.empty(self.n, dtype=torch.float32, device=dev)
@@ -89,8 +92,11 @@ class Pipeline:
     def stages(self):
         tg = self.tg
         return [
-            ("gate", lambda: tg.gate_score(self.x, self.w1, None, self.w2, 0.0, self.plan, scores=self.scores,
-                                           workspace=self.gws)),
+            ("gate", (lambda: tg.gate_score_prepacked(self.x, self.w1p, self.layer.h, None, self.w2, 0.0, self.plan,
+                                                      scores=self.scores, workspace=self.gws))
+             if self.prepacked else
+             (lambda: tg.gate_score(self.x, self.w1, None, self.w2, 0.0, self.plan, scores=self.scores,
+                                    workspace=self.gws))),
             ("select", lambda: tg.select_topk(self.scores, self.plan, kept_idx=self.kept, workspace=self.sws)),
             ("compact", lambda: tg.compact_kept(self.kept, self.pairs)),
             ("attention", (lambda: tg.gated_attention_prefill_gather(
@@ -242,7 +248,8 @@ def stage_rooflines(pipe, st, csrc):
         "attention": {"kernel": "gated_attention_kernel<128,2>", "bound": "mfma", "achieved": attn_tflops,
                       "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": attn_tflops / MFMA_BF16_PEAK_TFLOPS,
                       "traffic": kernel_traffic(os.path.join(csrc, "gated_attention.hip"))},
-        "gate": {"kernel": "pack_w1_kernel + gate_mlp_kernel<2,4> + gate_normalize_kernel", "bound": "hbm",
+        "gate": {"kernel": ("" if pipe.prepacked else "pack_w1_kernel + ") + "gate_mlp_kernel<2,4> + gate_normalize_kernel",
+                 "bound": "hbm",
                  "achieved": gate_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": gate_gbs / HBM_PEAK_GBS,
                  "traffic": kernel_traffic(os.path.join(csrc, "gate_score.hip")),
                  "mfma_tflops": pipe.gate_flops() / (st["gate"] * 1e-6) / 1e12},
@@ -493,6 +500,10 @@ def main():
         us_gather = time_graph(p16g, args.steps, args.warmup)
         log("16K: graph replay, attention gathering Q/K/V", f"{us_gather:.1f} us/step")
         del p16g
+        p16r = Pipeline(l16, 2048, torch, tg, prepacked=False)
+        us_repack = time_graph(p16r, args.steps, args.warmup)
+        log("16K: graph replay, W1 re-packed inside every step", f"{us_repack:.1f} us/step")
+        del p16r
         p16t = Pipeline(l16, 2048, torch, tg, query_tau=True)
         us_qtau = time_graph(p16t, args.steps, args.warmup)
         _, _, st16t = time_pipeline(p16t, args.steps, args.warmup)
@@ -517,13 +528,15 @@ def main():
             "config": {"workload": "gated layer N=16384 (16320 doc + 64 question), d=2048, gate 2048-256-1, "
                                    "K=2048 (M=2112 kept), 16 Q / 8 KV heads, head_dim 128",
                        "global_batch": 1, "seq_len": p16.n, "k_budget": 2048, "kept_rows": p16.m,
-                       "parallelism": "none", "launch": "one HIP graph per step (per-stage times: eager launches)"},
+                       "parallelism": "none", "launch": "one HIP graph per step (per-stage times: eager launches)",
+                       "gate_weights": "W1 packed into MFMA fragment order once at load"},
             "roofline": dict(roofs[dominant], stage=dominant),
             "stages_us": {k: round(v, 2) for k, v in st16.items()},
             "stage_rooflines": roofs,
             "gpu_us_per_step_events": round(us_gpu, 2),
             "eager_us_per_step": round(us_eager, 2),
             "gather_on_load_us_per_step": round(us_gather, 2),
+            "w1_repacked_every_step_us_per_step": round(us_repack, 2),
             "query_tau": {"us_per_step": round(us_qtau, 2), "attention_us": round(st16t["attention"], 2),
                           "note": "tau_rh = softplus(sigma_h) log(rank) / log(max(2, position)), graph replay"},
             "attention": {"tflops": roofs["attention"]["achieved"], "frac_mfma_peak": roofs["attention"]["frac"]},

@@ -132,6 +132,21 @@ int tg_gate_score(const void* x, int64_t ld_x, int d, const void* w1, const floa
                   int h, const tg_segment* segs, const tg_plan_info* info, float rms_eps, float* scores,
                   void* workspace, size_t workspace_bytes, void* stream);
 
+/* The gate's first-layer weights are constant across calls, so their
+ * re-ordering into MFMA fragment order (done inside every tg_gate_score call)
+ * can be done once at load time instead:
+ *   tg_gate_pack_w1: w1 bf16 [h, d] (device) -> w1_packed (device,
+ *     tg_gate_packed_w1_bytes(d, h) bytes, 16-byte aligned), an opaque layout
+ *     valid only for tg_gate_score_prepacked with the same d and h;
+ *   tg_gate_score_prepacked: tg_gate_score with the packed weights (same
+ *     results bit for bit, one launch fewer).  Same arguments, shapes and
+ *     workspace otherwise. */
+size_t tg_gate_packed_w1_bytes(int d, int h);
+int tg_gate_pack_w1(const void* w1, int d, int h, void* w1_packed, void* stream);
+int tg_gate_score_prepacked(const void* x, int64_t ld_x, int d, const void* w1_packed, const float* b1,
+                            const float* w2, float b2, int h, const tg_segment* segs, const tg_plan_info* info,
+                            float rms_eps, float* scores, void* workspace, size_t workspace_bytes, void* stream);
+
 /* ------------------------------------------------------------------------ */
 /* (2) Top-K select                                                          */
 /* ------------------------------------------------------------------------ */

@@ -124,8 +124,41 @@ int tg_gate_score(const void* x, int64_t ld_x, int d, const void* w1, const floa
     return TG_ERR_WORKSPACE;
   st = check_device();
   if (st != TG_OK) return st;
-  return hip_status(tg::launch_gate_score(x, ld_x, d, w1, b1, w2, b2, h, segs, *info, rms_eps, scores, workspace,
-                                          reinterpret_cast<hipStream_t>(stream)));
+  return hip_status(tg::launch_gate_score(x, ld_x, d, w1, false, b1, w2, b2, h, segs, *info, rms_eps, scores,
+                                          workspace, reinterpret_cast<hipStream_t>(stream)));
+}
+
+size_t tg_gate_packed_w1_bytes(int d, int h) {
+  if (d <= 0 || h <= 0) return 0;
+  return (size_t)d * (size_t)h * 2;
+}
+
+int tg_gate_pack_w1(const void* w1, int d, int h, void* w1_packed, void* stream) {
+  if (!w1 || !w1_packed || d <= 0 || h <= 0) return TG_ERR_INVALID_ARG;
+  if (d % 64 != 0 || d > 65536 || h % 64 != 0 || h > 256) return TG_ERR_UNSUPPORTED;
+  if (!aligned(w1, 16) || !aligned(w1_packed, 16)) return TG_ERR_UNSUPPORTED;
+  const int st = check_device();
+  if (st != TG_OK) return st;
+  return hip_status(tg::launch_gate_pack_w1(w1, d, h, w1_packed, reinterpret_cast<hipStream_t>(stream)));
+}
+
+int tg_gate_score_prepacked(const void* x, int64_t ld_x, int d, const void* w1_packed, const float* b1,
+                            const float* w2, float b2, int h, const tg_segment* segs, const tg_plan_info* info,
+                            float rms_eps, float* scores, void* workspace, size_t workspace_bytes, void* stream) {
+  int st = check_info(segs, info);
+  if (st != TG_OK) return st;
+  if (!x || !w1_packed || !w2 || !scores || d <= 0 || h <= 0 || ld_x < d) return TG_ERR_INVALID_ARG;
+  if (rms_eps != rms_eps) return TG_ERR_INVALID_ARG;  // NaN
+  if (d % 64 != 0 || d > 65536 || h % 64 != 0 || h > 256 || ld_x % 8 != 0) return TG_ERR_UNSUPPORTED;
+  if (!aligned(x, 16) || !aligned(w1_packed, 16) || !aligned(w2, 16) || (b1 && !aligned(b1, 16)) ||
+      !aligned(scores, 4))
+    return TG_ERR_UNSUPPORTED;
+  if (!workspace || !aligned(workspace, 256) || workspace_bytes < tg::gate_workspace_bytes(*info, d, h))
+    return TG_ERR_WORKSPACE;
+  st = check_device();
+  if (st != TG_OK) return st;
+  return hip_status(tg::launch_gate_score(x, ld_x, d, w1_packed, true, b1, w2, b2, h, segs, *info, rms_eps, scores,
+                                          workspace, reinterpret_cast<hipStream_t>(stream)));
 }
 
 size_t tg_select_workspace_bytes(const tg_plan_info* info) {

@@ -119,9 +119,11 @@ __device__ __forceinline__ uint32_t score_key(float f) {
 // Launchers (one per kernel family), defined in the kernel sources.  They
 // only launch; arguments are validated by the ABI layer.
 namespace tg {
-hipError_t launch_gate_score(const void* x, int64_t ld_x, int d, const void* w1, const float* b1, const float* w2,
-                             float b2, int h, const tg_segment* segs, const tg_plan_info& info, float rms_eps,
-                             float* scores, void* workspace, hipStream_t stream);
+// w1_prepacked: w1 is already in fragment order (launch_gate_pack_w1), not [h, d].
+hipError_t launch_gate_score(const void* x, int64_t ld_x, int d, const void* w1, bool w1_prepacked, const float* b1,
+                             const float* w2, float b2, int h, const tg_segment* segs, const tg_plan_info& info,
+                             float rms_eps, float* scores, void* workspace, hipStream_t stream);
+hipError_t launch_gate_pack_w1(const void* w1, int d, int h, void* w1_packed, hipStream_t stream);
 size_t gate_workspace_bytes(const tg_plan_info& info, int d, int h);
 
 hipError_t launch_select_topk(const float* scores, const tg_segment* segs, const tg_plan_info& info,

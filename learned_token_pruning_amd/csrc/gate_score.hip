@@ -333,16 +333,26 @@ static void launch_mlp_d(dim3 grid, hipStream_t stream, const uint16_t* xp, int6
     launch_mlp<NCT, 2, 1, 1>(grid, stream, xp, ld_x, d, wp, b1, w2, b2, h, segs, max_tiles, scores, ts);
 }
 
-hipError_t launch_gate_score(const void* x, int64_t ld_x, int d, const void* w1, const float* b1, const float* w2,
-                             float b2, int h, const tg_segment* segs, const tg_plan_info& info, float rms_eps,
-                             float* scores, void* workspace, hipStream_t stream) {
+hipError_t launch_gate_pack_w1(const void* w1, int d, int h, void* w1_packed, hipStream_t stream) {
+  hipLaunchKernelGGL(pack_w1_kernel, dim3((unsigned)((d / 64) * (h / 32))), dim3(256), 0, stream,
+                     reinterpret_cast<const uint16_t*>(w1), d, h, reinterpret_cast<u32x4*>(w1_packed));
+  return hipGetLastError();
+}
+
+hipError_t launch_gate_score(const void* x, int64_t ld_x, int d, const void* w1, bool w1_prepacked, const float* b1,
+                             const float* w2, float b2, int h, const tg_segment* segs, const tg_plan_info& info,
+                             float rms_eps, float* scores, void* workspace, hipStream_t stream) {
   int max_tiles = (info.max_doc_len + kRows - 1) / kRows;  // at the smallest tile height: an upper bound
   if (max_tiles < 1) max_tiles = 1;
   double* ts = reinterpret_cast<double*>(workspace);
-  u32x4* w1p = reinterpret_cast<u32x4*>(reinterpret_cast<char*>(workspace) + sumsq_bytes(info));
+  const u32x4* w1p = w1_prepacked
+                         ? reinterpret_cast<const u32x4*>(w1)
+                         : reinterpret_cast<const u32x4*>(reinterpret_cast<char*>(workspace) + sumsq_bytes(info));
   if (info.max_doc_len > 0) {
-    hipLaunchKernelGGL(pack_w1_kernel, dim3((unsigned)((d / 64) * (h / 32))), dim3(256), 0, stream,
-                       reinterpret_cast<const uint16_t*>(w1), d, h, w1p);
+    if (!w1_prepacked) {
+      const hipError_t e = launch_gate_pack_w1(w1, d, h, const_cast<u32x4*>(w1p), stream);
+      if (e != hipSuccess) return e;
+    }
     dim3 grid(max_tiles, info.n_seg);
     const uint16_t* xp = reinterpret_cast<const uint16_t*>(x);
     if (h <= 128)

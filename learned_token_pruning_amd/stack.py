@@ -94,6 +94,7 @@ class PrunedStack:
         self.d, self.hq, self.hkv, self.dh, self.f = d, hq, hkv, dh, f
         self.eps, self.theta, self.gate_eps = eps, theta, gate_eps
         self._ws = None
+        self.gate_w1_packed = tg.gate_pack_w1(gate_w1)  # fragment order, packed once
 
     def plan(self, seg_start, doc_begin, doc_end, k_budget, device) -> StackPlan:
         full = tg.plan_segments(seg_start, doc_begin, doc_end, [e - b for b, e in zip(doc_begin, doc_end)], device)
@@ -133,7 +134,8 @@ class PrunedStack:
                 mark("upper")
             return {"hidden": hidden, "gate_in": gate_in}
         pp = plan.pruned
-        scores = tg.gate_score(gate_in, self.gate_w1, None, self.gate_w2, 0.0, pp, rms_eps=self.gate_eps)
+        scores = tg.gate_score_prepacked(gate_in, self.gate_w1_packed, self.gate_w1.shape[0], None, self.gate_w2, 0.0,
+                                         pp, rms_eps=self.gate_eps)
         kept = tg.select_topk(scores, pp)
         m = pp.total_kept
         hk = torch.empty((m, self.d), dtype=torch.bfloat16, device=dev)

@@ -30,6 +30,7 @@ TG_OK = 0
 STATUS_NAMES = {0: "TG_OK", -1: "TG_ERR_INVALID_ARG", -2: "TG_ERR_UNSUPPORTED", -3: "TG_ERR_WORKSPACE",
                 -4: "TG_ERR_NO_DEVICE", -5: "TG_ERR_HIP"}
 EXPORTS = ("tg_status_string", "tg_abi_version", "tg_plan_segments", "tg_gate_workspace_bytes", "tg_gate_score",
+           "tg_gate_packed_w1_bytes", "tg_gate_pack_w1", "tg_gate_score_prepacked",
            "tg_select_workspace_bytes", "tg_select_topk", "tg_compact_kept", "tg_gated_attention_prefill",
            "tg_gated_attention_prefill_gather", "tg_gated_attention_prefill_query_tau",
            "tg_decode_workspace_bytes", "tg_gated_attention_decode", "tg_gated_attention_prefill_lse",
@@ -79,6 +80,13 @@ _lib.tg_gate_workspace_bytes.argtypes = [ctypes.POINTER(PlanInfo), _i32, _i32]
 _lib.tg_gate_score.restype = _i32
 _lib.tg_gate_score.argtypes = [_vp, _i64, _i32, _vp, _vp, _vp, _f32, _i32, _vp, ctypes.POINTER(PlanInfo), _f32, _vp,
                                _vp, _sz, _vp]
+_lib.tg_gate_packed_w1_bytes.restype = _sz
+_lib.tg_gate_packed_w1_bytes.argtypes = [_i32, _i32]
+_lib.tg_gate_pack_w1.restype = _i32
+_lib.tg_gate_pack_w1.argtypes = [_vp, _i32, _i32, _vp, _vp]
+_lib.tg_gate_score_prepacked.restype = _i32
+_lib.tg_gate_score_prepacked.argtypes = [_vp, _i64, _i32, _vp, _vp, _vp, _f32, _i32, _vp, ctypes.POINTER(PlanInfo), _f32,
+                                         _vp, _vp, _sz, _vp]
 _lib.tg_select_workspace_bytes.restype = _sz
 _lib.tg_select_workspace_bytes.argtypes = [ctypes.POINTER(PlanInfo)]
 _lib.tg_select_topk.restype = _i32
@@ -248,6 +256,31 @@ def gate_score(x: torch.Tensor, w1: torch.Tensor, b1: Optional[torch.Tensor], w2
                             ctypes.byref(plan.info), float(rms_eps), _ptr(scores), _ptr(workspace),
                             workspace.numel() * workspace.element_size(), _stream(stream))
     _check(st, "tg_gate_score")
+    return scores
+
+
+def gate_pack_w1(w1: torch.Tensor, stream=None) -> torch.Tensor:
+    """tg_gate_pack_w1: W1 bf16 [h, d] -> its fragment-ordered copy (opaque, for gate_score_prepacked)."""
+    h, d = w1.shape
+    out = torch.empty(int(_lib.tg_gate_packed_w1_bytes(d, h)), dtype=torch.uint8, device=w1.device)
+    _check(_lib.tg_gate_pack_w1(_ptr(w1), d, h, _ptr(out), _stream(stream)), "tg_gate_pack_w1")
+    return out
+
+
+def gate_score_prepacked(x: torch.Tensor, w1_packed: torch.Tensor, h: int, b1: Optional[torch.Tensor],
+                         w2: torch.Tensor, b2: float, plan: Plan, rms_eps: float = 1e-6,
+                         scores: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
+                         stream=None) -> torch.Tensor:
+    """tg_gate_score_prepacked: gate_score with W1 packed by gate_pack_w1."""
+    d = int(w1_packed.numel() * w1_packed.element_size()) // (2 * h)
+    if scores is None:
+        scores = torch.empty(plan.n_tokens, dtype=torch.float32, device=x.device)
+    if workspace is None:
+        workspace = _workspace(gate_workspace_bytes(plan, d, h), x.device)
+    st = _lib.tg_gate_score_prepacked(_ptr(x), x.stride(0), d, _ptr(w1_packed), _ptr(b1), _ptr(w2), float(b2), h,
+                                      _dev_table(plan), ctypes.byref(plan.info), float(rms_eps), _ptr(scores),
+                                      _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(stream))
+    _check(st, "tg_gate_score_prepacked")
     return scores
 
 

@@ -91,6 +91,21 @@ def test_gate_validation():
     assert f(FAKE, 2048, 2048, FAKE, None, FAKE, 0.0, 256, None, info, 1e-6, FAKE, FAKE, ws, None) == -1
 
 
+def test_gate_prepacked_validation():
+    p = _plan()
+    info = ctypes.byref(p.info)
+    assert tg.gate_workspace_bytes(p, 2048, 256) > 0 and L.tg_gate_packed_w1_bytes(2048, 256) == 2048 * 256 * 2
+    assert L.tg_gate_packed_w1_bytes(0, 256) == 0
+    assert L.tg_gate_pack_w1(None, 2048, 256, FAKE, None) == -1
+    assert L.tg_gate_pack_w1(FAKE, 2048, 96, FAKE, None) == -2
+    assert L.tg_gate_pack_w1(FAKE, 2050, 256, FAKE, None) == -2
+    ws = tg.gate_workspace_bytes(p, 2048, 256)
+    f = L.tg_gate_score_prepacked
+    assert f(FAKE, 2048, 2048, None, None, FAKE, 0.0, 256, FAKE, info, 1e-6, FAKE, FAKE, ws, None) == -1
+    assert f(FAKE, 2048, 2048, FAKE, None, FAKE, 0.0, 320, FAKE, info, 1e-6, FAKE, FAKE, ws, None) == -2
+    assert f(FAKE, 2048, 2048, FAKE, None, FAKE, 0.0, 256, FAKE, info, 1e-6, FAKE, FAKE, ws - 1, None) == -3
+
+
 def test_select_validation():
     p = _plan()
     info = ctypes.byref(p.info)
@@ -225,6 +240,9 @@ def test_valid_calls_report_no_device_without_gpu():
     ws = tg.gate_workspace_bytes(p, 2048, 256)
     assert L.tg_gate_score(FAKE, 2048, 2048, FAKE, None, FAKE, 0.0, 256, FAKE, info, 1e-6, FAKE, FAKE, ws, None) == -4
     assert L.tg_select_topk(FAKE, FAKE, info, FAKE, FAKE, tg.select_workspace_bytes(p), None) == -4
+    assert L.tg_gate_pack_w1(FAKE, 2048, 256, FAKE, None) == -4
+    assert L.tg_gate_score_prepacked(FAKE, 2048, 2048, FAKE, None, FAKE, 0.0, 256, FAKE, info, 1e-6, FAKE, FAKE, ws,
+                                     None) == -4
     assert L.tg_gated_attention_prefill(FAKE, FAKE, FAKE, None, None, None, FAKE, info, 16, 8, 128, FAKE, None) == -4
     assert L.tg_gated_attention_prefill_query_tau(FAKE, FAKE, FAKE, None, FAKE, None, FAKE, FAKE, info, 16, 8, 128,
                                                   FAKE, None) == -4

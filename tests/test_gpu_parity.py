@@ -119,6 +119,21 @@ def test_gate_ragged_segments(h, d):
     check_scores(got_raw, oracle_gate(L, eps=-1.0, b1=b1, b2=0.3), doc_mask_of(seg))
 
 
+@pytest.mark.parametrize("idx", [1, 2])
+def test_gate_prepacked_equals_gate(idx):
+    """W1 packed once (tg_gate_pack_w1) gives tg_gate_score's scores bit for bit."""
+    import torch
+    _say("gate prepacked", idx)
+    tg = _tg()
+    L = layer(idx, with_qkv=False)
+    plan = tg.plan_from(L.segments, device="cuda")
+    x, w1, w2 = dev_bf16(L.x), dev_bf16(L.w1), dev_f32(L.w2)
+    a = tg.gate_score(x, w1, None, w2, 0.0, plan)
+    b = tg.gate_score_prepacked(x, tg.gate_pack_w1(w1), w1.shape[0], None, w2, 0.0, plan)
+    torch.cuda.synchronize()
+    assert torch.equal(a.view(torch.int32), b.view(torch.int32))
+
+
 def test_gate_deterministic():
     _say("gate determinism")
     L = layer(2, with_qkv=False)
