@@ -91,6 +91,23 @@ __device__ __forceinline__ float stride_sum(float x) {
   return xor32_sum(swap16_sum(x));
 }
 
+// Inclusive prefix sum over the 64 lanes of a wave on DPP: Hillis-Steele
+// shifts inside each 16-lane row (shifted-in lanes read 0), then row 15's and
+// row 31's totals broadcast into the later rows.  Compiles to six v_add_u32_dpp.
+template <int CTRL, int ROWS>
+__device__ __forceinline__ uint32_t dpp_shift_u32(uint32_t x) {
+  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, CTRL, ROWS, 0xf, true);
+}
+__device__ __forceinline__ uint32_t wave_incl_scan(uint32_t x) {
+  x += dpp_shift_u32<0x111, 0xf>(x);  // row_shr:1
+  x += dpp_shift_u32<0x112, 0xf>(x);  // row_shr:2
+  x += dpp_shift_u32<0x114, 0xf>(x);  // row_shr:4
+  x += dpp_shift_u32<0x118, 0xf>(x);  // row_shr:8
+  x += dpp_shift_u32<0x142, 0xa>(x);  // row_bcast:15 into rows 1 and 3
+  x += dpp_shift_u32<0x143, 0xc>(x);  // row_bcast:31 into rows 2 and 3
+  return x;
+}
+
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
 

@@ -40,16 +40,7 @@ __device__ __forceinline__ void block_scan2(uint32_t a, uint32_t b, uint32_t& ea
                                             uint32_t& tot1, SelSmem& sm) {
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
-  uint32_t xa = a, xb = b;
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const uint32_t ya = __shfl_up(xa, o);
-    const uint32_t yb = __shfl_up(xb, o);
-    if (lane >= o) {
-      xa += ya;
-      xb += yb;
-    }
-  }
+  const uint32_t xa = wave_incl_scan(a), xb = wave_incl_scan(b);
   if (lane == 63) {
     sm.wave_tot[0][wave] = xa;
     sm.wave_tot[1][wave] = xb;
@@ -255,15 +246,7 @@ __device__ __forceinline__ void scan256(uint32_t a, uint32_t b, uint32_t& ea, ui
                                         uint32_t& tb, MultiSmem& sm) {
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
-  uint32_t xa = a, xb = b;
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const uint32_t ya = __shfl_up(xa, o), yb = __shfl_up(xb, o);
-    if (lane >= o) {
-      xa += ya;
-      xb += yb;
-    }
-  }
+  const uint32_t xa = wave_incl_scan(a), xb = wave_incl_scan(b);
   if (lane == 63) {
     sm.wtot[0][wave] = xa;
     sm.wtot[1][wave] = xb;
