@@ -103,8 +103,15 @@ __device__ __forceinline__ void store_rows(int u, const u32x4 (&r)[4], uint16_t*
   }
 }
 
+// 512 threads: two streams of 4 waves (waves w and w + 4 share a SIMD), wave
+// w & 3 owning keys kb0 + 32 (w & 3) .. + 31 in both streams.  Stream s takes
+// the (head, query block) items s, s + 2, s + 4, ... of the chunk with LDS
+// staging of its own; the K/V rows of the workgroup are shared.  The streams'
+// dK, dV and ds are summed in a fixed order at the end.
+constexpr int kDkdvThreads = 512;
+
 template <int D, int G>
-__global__ __launch_bounds__(kBwdThreads) void bwd_dkdv_kernel(
+__global__ __launch_bounds__(kDkdvThreads) void bwd_dkdv_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
     const float* __restrict__ key_score, const float* __restrict__ tau, const float* __restrict__ gain,
     const tg_segment* __restrict__ segs, int hq, int hkv, const uint16_t* __restrict__ dout,
@@ -112,11 +119,16 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_dkdv_kernel(
     float* __restrict__ dv_part, float* __restrict__ ds_part, int64_t total_kept, float* __restrict__ part_g,
     float* __restrict__ part_t) {
   using RB = RowBlock<D>;
-  __shared__ __attribute__((aligned(16))) uint16_t qs[32 * RB::kLd], qt[D * RB::tLd];
-  __shared__ __attribute__((aligned(16))) uint16_t os[32 * RB::kLd], ot[D * RB::tLd];
-  __shared__ __attribute__((aligned(16))) uint16_t kvk[kKeyBlock * RB::kLd], kvv[kKeyBlock * RB::kLd];
-  __shared__ float lse2[32], dts[32];
-  __shared__ float red[4][G][2];
+  struct alignas(16) Stage {
+    uint16_t qs[32 * RB::kLd], qt[D * RB::tLd], os[32 * RB::kLd], ot[D * RB::tLd];
+    float lse2[32], dts[32];
+  };
+  struct alignas(16) Smem {
+    uint16_t kvk[kKeyBlock * RB::kLd], kvv[kKeyBlock * RB::kLd];
+    Stage st[2];
+  };
+  __shared__ Smem sm;
+  __shared__ float red[8][G][2];
 
   const tg_segment seg = segs[blockIdx.z];
   const int n = seg.kept_len;
@@ -128,26 +140,29 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_dkdv_kernel(
   const int c = blockIdx.x;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int strm = wave >> 2, kslot = wave & 3;
+  const int t = tid & 255;  // thread index inside the stream
   const int g = lane >> 5, l32 = lane & 31;
-  const int kw0 = kb0 + 32 * wave;  // first key of this wave
-  const int kj = kw0 + l32;         // the key this lane owns
+  const int kw0 = kb0 + 32 * kslot;  // first key of this wave
+  const int kj = kw0 + l32;          // the key this lane owns
   const bool key_ok = kj < n;
   const int64_t base = seg.kept_start;
   const int64_t q_stride = (int64_t)hq * D, kv_stride = (int64_t)hkv * D;
+  Stage& my = sm.st[strm];
 
   // the workgroup's K and V rows, staged once (row-major; B operands of S and
   // dP read the lane's key row at k = 16 ks + 8 g .. + 7)
-  for (int u = tid; u < kKeyBlock * (D / 8); u += kBwdThreads) {
+  for (int u = tid; u < kKeyBlock * (D / 8); u += kDkdvThreads) {
     const int r = u / (D / 8), col = 8 * (u % (D / 8));
     const int key = kb0 + r;
     const int64_t off = (base + key) * kv_stride + (int64_t)c * D + col;
-    *reinterpret_cast<u32x4*>(&kvk[r * RB::kLd + col]) =
+    *reinterpret_cast<u32x4*>(&sm.kvk[r * RB::kLd + col]) =
         key < n ? *reinterpret_cast<const u32x4*>(k + off) : u32x4{0, 0, 0, 0};
-    *reinterpret_cast<u32x4*>(&kvv[r * RB::kLd + col]) =
+    *reinterpret_cast<u32x4*>(&sm.kvv[r * RB::kLd + col]) =
         key < n ? *reinterpret_cast<const u32x4*>(v + off) : u32x4{0, 0, 0, 0};
   }
-  const uint16_t* krow_l = &kvk[(32 * wave + l32) * RB::kLd + 8 * g];
-  const uint16_t* vrow_l = &kvv[(32 * wave + l32) * RB::kLd + 8 * g];
+  const uint16_t* krow_l = &sm.kvk[(32 * kslot + l32) * RB::kLd + 8 * g];
+  const uint16_t* vrow_l = &sm.kvv[(32 * kslot + l32) * RB::kLd + 8 * g];
   const bool use_bias = key_score != nullptr && gain != nullptr;
   const float s_key = use_bias && key_ok ? key_score[base + kj] : 0.0f;
 
@@ -158,32 +173,50 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_dkdv_kernel(
     dvt[dtile] = f32x16{};
   }
   float ds_acc = 0.0f;
+  float dg_acc[G], dtau_acc[G];
+#pragma unroll
+  for (int gg = 0; gg < G; ++gg) dg_acc[gg] = dtau_acc[gg] = 0.0f;
   const float inv_sqrt_d = 1.0f / __builtin_sqrtf((float)D);
 
-  // (head, query block) pairs in order; the next pair's rows are loaded into
-  // registers while the current one computes
+  // items (head, query block) of the chunk: it -> head it / nqb, block qb_begin + it % nqb
   const int qb_begin = kb0 / 32 + ci * qc;
-  const int nqb = max(0, min(qb_begin + qc, (n + 31) / 32) - qb_begin);  // query blocks of this chunk
+  const int nqb = max(0, min(qb_begin + qc, (n + 31) / 32) - qb_begin);
   const int total = G * nqb;
+  const int iters = (total + 1) / 2;
   u32x4 sreg[4];
   float slse = 0.0f, sdt = 0.0f;
-  auto load_block = [&](int it) {
+  auto load_item = [&](int it) {  // it < total
     const int h = c * G + it / nqb, q0 = 32 * (qb_begin + it % nqb);
-    if (tid < RB::kUnits)
-      load_rows<D>(q + base * q_stride + (int64_t)h * D, q_stride, q0, n, tid, sreg);
-    else if (tid < 2 * RB::kUnits)
-      load_rows<D>(dout + base * q_stride + (int64_t)h * D, q_stride, q0, n, tid - RB::kUnits, sreg);
-    if (tid < 32) {
-      const int row = q0 + tid;
+    if (t < RB::kUnits)
+      load_rows<D>(q + base * q_stride + (int64_t)h * D, q_stride, q0, n, t, sreg);
+    else if (t < 2 * RB::kUnits)
+      load_rows<D>(dout + base * q_stride + (int64_t)h * D, q_stride, q0, n, t - RB::kUnits, sreg);
+    if (t < 32) {
+      const int row = q0 + t;
       slse = row < n ? lse[(base + row) * hq + h] * kL2e : __builtin_inff();
       sdt = row < n ? dt[(base + row) * hq + h] : 0.0f;
     }
   };
-  if (total > 0) load_block(0);
-  float dg_acc = 0.0f, dtau_acc = 0.0f;
-  if (tid < 4 * G) red[tid / G][tid % G][0] = red[tid / G][tid % G][1] = 0.0f;  // heads with no block here
-  for (int it = 0; it < total; ++it) {
-    const int gg = it / nqb, q0 = 32 * (qb_begin + it % nqb);
+  if (strm < total) load_item(strm);
+  for (int j = 0; j < iters; ++j) {
+    const int it = 2 * j + strm;  // this stream's item (none when it >= total)
+    const bool have = it < total;
+    __syncthreads();  // the previous items' LDS reads are done
+    if (have) {
+      if (t < RB::kUnits)
+        store_rows<D>(t, sreg, my.qs, my.qt);
+      else if (t < 2 * RB::kUnits)
+        store_rows<D>(t - RB::kUnits, sreg, my.os, my.ot);
+      if (t < 32) {
+        my.lse2[t] = slse;
+        my.dts[t] = sdt;
+      }
+      if (it + 2 < total) load_item(it + 2);
+    }
+    __syncthreads();
+    const int gg = have ? it / nqb : 0, q0 = have ? 32 * (qb_begin + it % nqb) : 0;
+    if (!have || kw0 > q0 + 31) continue;  // no item, or every key after every query (uniform per wave)
+
     const int h = c * G + gg;
     const float th = tau != nullptr ? tau[h] : 1.0f;
     const float scale2 = th * kL2e * inv_sqrt_d;  // exp2-domain logit per unit q.k
@@ -191,108 +224,129 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_dkdv_kernel(
     const float gh = use_bias ? gain[h] : 0.0f;
     const float bias2 = gh * kL2e * s_key;        // exp2-domain bias of the lane's key
 
-    __syncthreads();  // the previous block's LDS reads are done
-    if (tid < RB::kUnits)
-      store_rows<D>(tid, sreg, qs, qt);
-    else if (tid < 2 * RB::kUnits)
-      store_rows<D>(tid - RB::kUnits, sreg, os, ot);
-    if (tid < 32) {
-      lse2[tid] = slse;
-      dts[tid] = sdt;
+    f32x16 sacc = f32x16{}, dpacc = f32x16{};
+    const uint16_t* qrow = &my.qs[l32 * RB::kLd + 8 * g];
+    const uint16_t* orow = &my.os[l32 * RB::kLd + 8 * g];
+#pragma unroll
+    for (int ks = 0; ks < D / 16; ++ks) {
+      sacc = mfma32(*reinterpret_cast<const u32x4*>(qrow + 16 * ks), *reinterpret_cast<const u32x4*>(krow_l + 16 * ks),
+                    sacc);
+      dpacc = mfma32(*reinterpret_cast<const u32x4*>(orow + 16 * ks),
+                     *reinterpret_cast<const u32x4*>(vrow_l + 16 * ks), dpacc);
     }
-    if (it + 1 < total) load_block(it + 1);
-    __syncthreads();
-
-    if (kw0 <= q0 + 31) {  // some key of the wave is visible to some query of the block (uniform per wave)
-      f32x16 sacc = f32x16{}, dpacc = f32x16{};
-      const uint16_t* qrow = &qs[l32 * RB::kLd + 8 * g];
-      const uint16_t* orow = &os[l32 * RB::kLd + 8 * g];
+    // register i holds query row q0 + c_row(i, g), key kj
+    float pz[16], dz[16];
+    float dg_i = 0.0f, dtau_i = 0.0f;
 #pragma unroll
-      for (int ks = 0; ks < D / 16; ++ks) {
-        sacc = mfma32(*reinterpret_cast<const u32x4*>(qrow + 16 * ks), *reinterpret_cast<const u32x4*>(krow_l + 16 * ks),
-                      sacc);
-        dpacc = mfma32(*reinterpret_cast<const u32x4*>(orow + 16 * ks),
-                       *reinterpret_cast<const u32x4*>(vrow_l + 16 * ks), dpacc);
-      }
-      // register i holds query row q0 + c_row(i, g), key kj
-      float pz[16], dz[16];
+    for (int q4 = 0; q4 < 4; ++q4) {
+      const f32x4 l4 = *reinterpret_cast<const f32x4*>(&my.lse2[8 * q4 + 4 * g]);
+      const f32x4 d4 = *reinterpret_cast<const f32x4*>(&my.dts[8 * q4 + 4 * g]);
 #pragma unroll
-      for (int q4 = 0; q4 < 4; ++q4) {
-        const f32x4 l4 = *reinterpret_cast<const f32x4*>(&lse2[8 * q4 + 4 * g]);
-        const f32x4 d4 = *reinterpret_cast<const f32x4*>(&dts[8 * q4 + 4 * g]);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int i = 4 * q4 + e;
-          const int row = q0 + c_row(i, g);
-          const bool ok = key_ok && kj <= row && row < n;
-          const float p = ok ? __builtin_amdgcn_exp2f(__builtin_fmaf(scale2, sacc[i], bias2) - l4[e]) : 0.0f;
-          const float z = p * (dpacc[i] - d4[e]);
-          pz[i] = p;
-          dz[i] = z;
-          ds_acc = __builtin_fmaf(gh, z, ds_acc);
-          dg_acc = __builtin_fmaf(z, s_key, dg_acc);
-          dtau_acc = __builtin_fmaf(z, sacc[i] * inv_sqrt_d, dtau_acc);
-        }
-      }
-      // B operands of the two 16-query MFMA steps: register 8 st + e
-      u32x4 pb[2], zb[2];
-#pragma unroll
-      for (int st = 0; st < 2; ++st)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const int i = 8 * st + 2 * j;
-          const uint32_t pp = pack2(pz[i], pz[i + 1]);
-          const uint32_t zz = pack2(dz[i] * dscale, dz[i + 1] * dscale);
-          pb[st][j] = pp;
-          zb[st][j] = zz;
-        }
-#pragma unroll
-      for (int st = 0; st < 2; ++st) {
-#pragma unroll
-        for (int dtile = 0; dtile < D / 32; ++dtile) {
-          const uint16_t* ro = &ot[(dtile * 32 + l32) * RB::tLd + 16 * st + 4 * g];
-          const uint16_t* rq = &qt[(dtile * 32 + l32) * RB::tLd + 16 * st + 4 * g];
-          const u32x2 olo = *reinterpret_cast<const u32x2*>(ro), ohi = *reinterpret_cast<const u32x2*>(ro + 8);
-          const u32x2 qlo = *reinterpret_cast<const u32x2*>(rq), qhi = *reinterpret_cast<const u32x2*>(rq + 8);
-          dvt[dtile] = mfma32(u32x4{olo[0], olo[1], ohi[0], ohi[1]}, pb[st], dvt[dtile]);
-          dkt[dtile] = mfma32(u32x4{qlo[0], qlo[1], qhi[0], qhi[1]}, zb[st], dkt[dtile]);
-        }
+      for (int e = 0; e < 4; ++e) {
+        const int i = 4 * q4 + e;
+        const int row = q0 + c_row(i, g);
+        const bool ok = key_ok && kj <= row && row < n;
+        const float p = ok ? __builtin_amdgcn_exp2f(__builtin_fmaf(scale2, sacc[i], bias2) - l4[e]) : 0.0f;
+        const float z = p * (dpacc[i] - d4[e]);
+        pz[i] = p;
+        dz[i] = z;
+        ds_acc = __builtin_fmaf(gh, z, ds_acc);
+        dg_i = __builtin_fmaf(z, s_key, dg_i);
+        dtau_i = __builtin_fmaf(z, sacc[i] * inv_sqrt_d, dtau_i);
       }
     }
-    if (it % nqb == nqb - 1) {  // the head's last block: publish its dg / dtau partial
-      const float dgw = wave_sum(dg_acc), dtw = wave_sum(dtau_acc);
-      if (lane == 0) {
-        red[wave][gg][0] = dgw;
-        red[wave][gg][1] = dtw;
+#pragma unroll
+    for (int hh = 0; hh < G; ++hh) {
+      if (hh == gg) {
+        dg_acc[hh] += dg_i;
+        dtau_acc[hh] += dtau_i;
       }
-      dg_acc = 0.0f;
-      dtau_acc = 0.0f;
+    }
+    // B operands of the two 16-query MFMA steps: register 8 st + e
+    u32x4 pb[2], zb[2];
+#pragma unroll
+    for (int st = 0; st < 2; ++st)
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj) {
+        const int i = 8 * st + 2 * jj;
+        const uint32_t pp = pack2(pz[i], pz[i + 1]);
+        const uint32_t zz = pack2(dz[i] * dscale, dz[i + 1] * dscale);
+        pb[st][jj] = pp;
+        zb[st][jj] = zz;
+      }
+#pragma unroll
+    for (int st = 0; st < 2; ++st) {
+#pragma unroll
+      for (int dtile = 0; dtile < D / 32; ++dtile) {
+        const uint16_t* ro = &my.ot[(dtile * 32 + l32) * RB::tLd + 16 * st + 4 * g];
+        const uint16_t* rq = &my.qt[(dtile * 32 + l32) * RB::tLd + 16 * st + 4 * g];
+        const u32x2 olo = *reinterpret_cast<const u32x2*>(ro), ohi = *reinterpret_cast<const u32x2*>(ro + 8);
+        const u32x2 qlo = *reinterpret_cast<const u32x2*>(rq), qhi = *reinterpret_cast<const u32x2*>(rq + 8);
+        dvt[dtile] = mfma32(u32x4{olo[0], olo[1], ohi[0], ohi[1]}, pb[st], dvt[dtile]);
+        dkt[dtile] = mfma32(u32x4{qlo[0], qlo[1], qhi[0], qhi[1]}, zb[st], dkt[dtile]);
+      }
     }
   }
-  // dK, dV of the lane's key: register i of tile t holds dim 32 t + c_row(i, g)
-  if (key_ok) {
-    const int64_t prow = ((int64_t)ci * total_kept + base + kj) * kv_stride + (int64_t)c * D;
-    float* dkr = dk_part + prow;
-    float* dvr = dv_part + prow;
+  // per-head dg / dtau of the wave
+#pragma unroll
+  for (int gg = 0; gg < G; ++gg) {
+    const float a = wave_sum(dg_acc[gg]), b = wave_sum(dtau_acc[gg]);
+    if (lane == 0) {
+      red[wave][gg][0] = a;
+      red[wave][gg][1] = b;
+    }
+  }
+  // stream 1 hands its dK, dV and ds to stream 0 through LDS (the staging
+  // buffers are free now), which adds them in a fixed order
+  __syncthreads();
+  constexpr int kRec = D * 32 * 2 + 64;  // floats per wave: dK^T, dV^T, ds
+  float* xo = reinterpret_cast<float*>(&sm);
+  static_assert(4 * kRec * 4 <= sizeof(Smem), "stream exchange fits in LDS");
+  float* rec = xo + kslot * kRec;
+  if (strm == 1) {
 #pragma unroll
     for (int dtile = 0; dtile < D / 32; ++dtile)
 #pragma unroll
-      for (int q4 = 0; q4 < 4; ++q4) {
-        const int d0 = 32 * dtile + 8 * q4 + 4 * g;
-        *reinterpret_cast<f32x4*>(dkr + d0) =
-            f32x4{dkt[dtile][4 * q4], dkt[dtile][4 * q4 + 1], dkt[dtile][4 * q4 + 2], dkt[dtile][4 * q4 + 3]};
-        *reinterpret_cast<f32x4*>(dvr + d0) =
-            f32x4{dvt[dtile][4 * q4], dvt[dtile][4 * q4 + 1], dvt[dtile][4 * q4 + 2], dvt[dtile][4 * q4 + 3]};
+      for (int i = 0; i < 16; ++i) {
+        rec[((2 * dtile) * 16 + i) * 64 + lane] = dkt[dtile][i];
+        rec[((2 * dtile + 1) * 16 + i) * 64 + lane] = dvt[dtile][i];
       }
+    rec[D * 32 * 2 + lane] = ds_acc;
   }
-  const float ds_key = xor32_sum(ds_acc);  // the two half-waves hold different query rows
-  if (key_ok && g == 0) ds_part[((int64_t)ci * hkv + c) * total_kept + base + kj] = ds_key;
   __syncthreads();
+  if (strm == 0) {
+#pragma unroll
+    for (int dtile = 0; dtile < D / 32; ++dtile)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        dkt[dtile][i] += rec[((2 * dtile) * 16 + i) * 64 + lane];
+        dvt[dtile][i] += rec[((2 * dtile + 1) * 16 + i) * 64 + lane];
+      }
+    ds_acc += rec[D * 32 * 2 + lane];
+    // dK, dV of the lane's key: register i of tile t holds dim 32 t + c_row(i, g)
+    if (key_ok) {
+      const int64_t prow = ((int64_t)ci * total_kept + base + kj) * kv_stride + (int64_t)c * D;
+      float* dkr = dk_part + prow;
+      float* dvr = dv_part + prow;
+#pragma unroll
+      for (int dtile = 0; dtile < D / 32; ++dtile)
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4) {
+          const int d0 = 32 * dtile + 8 * q4 + 4 * g;
+          *reinterpret_cast<f32x4*>(dkr + d0) =
+              f32x4{dkt[dtile][4 * q4], dkt[dtile][4 * q4 + 1], dkt[dtile][4 * q4 + 2], dkt[dtile][4 * q4 + 3]};
+          *reinterpret_cast<f32x4*>(dvr + d0) =
+              f32x4{dvt[dtile][4 * q4], dvt[dtile][4 * q4 + 1], dvt[dtile][4 * q4 + 2], dvt[dtile][4 * q4 + 3]};
+        }
+    }
+    const float ds_key = xor32_sum(ds_acc);  // the two half-waves hold different query rows
+    if (key_ok && g == 0) ds_part[((int64_t)ci * hkv + c) * total_kept + base + kj] = ds_key;
+  }
   if (tid < G) {
     const int64_t slot = (int64_t)blockIdx.z * gridDim.y + blockIdx.y;
     float sg = 0.0f, st = 0.0f;
 #pragma unroll
-    for (int w = 0; w < 4; ++w) {
+    for (int w = 0; w < 8; ++w) {
       sg += red[w][tid][0];
       st += red[w][tid][1];
     }
@@ -583,7 +637,7 @@ hipError_t launch_bwd_dg(const void* q, const void* k, const void* v, const floa
     hipLaunchKernelGGL((bwd_rowdot_kernel<D>), dim3((unsigned)((rows + per_block - 1) / per_block)),
                        dim3(kBwdThreads), 0, stream, dob, ob, rows, w.dt);
     hipLaunchKernelGGL((bwd_dkdv_kernel<D, G>), dim3(hkv, geo.key_blocks * geo.n_chunks, info.n_seg),
-                       dim3(kBwdThreads), 0, stream, qb, kb, vb, ks, tau, gain, segs, hq, hkv, dob, lse, w.dt,
+                       dim3(kDkdvThreads), 0, stream, qb, kb, vb, ks, tau, gain, segs, hq, hkv, dob, lse, w.dt,
                        geo.n_chunks, geo.qc, w.dk_part, w.dv_part, w.ds_part, info.total_kept, w.part_g, w.part_t);
     constexpr int kBM = 128 / G;
     const int q_tiles = (int)((info.max_kept_len + kBM - 1) / kBM);
