@@ -184,24 +184,51 @@ __global__ __launch_bounds__(kDecThreads) void decode_partial_kernel(
   }
 }
 
+// One workgroup of D threads per (query head, sequence).  The chunk maxima
+// and sums are read in parallel (thread i takes chunks i, i + D, ...), the
+// maximum and the chunk weights go through LDS, then every thread sums its
+// output dimension over the chunks in chunk order (four loads in flight).
 template <int D>
 __global__ __launch_bounds__(D) void decode_combine_kernel(const int32_t* __restrict__ lens, int64_t cap, int hq,
                                                            int hkv, int n_chunks, const float* __restrict__ part_o,
                                                            const float* __restrict__ part_ml,
                                                            uint16_t* __restrict__ out) {
-  const int h = blockIdx.x, b = blockIdx.y, d = threadIdx.x;
+  constexpr int kW = D / 64;
+  __shared__ float wred[kW];
+  __shared__ float wts[D];
+  const int h = blockIdx.x, b = blockIdx.y, d = threadIdx.x, lane = d & 63, wv = d >> 6;
   const int G = hq / hkv, c = h / G, gg = h % G;
   const int len = min(max(lens[b], 0), (int)min(cap, (int64_t)0x7fffffff));
   const int nc = (len + kChunk - 1) / kChunk;
   const int64_t slot0 = ((int64_t)b * hkv + c) * n_chunks;
   float m = -__builtin_inff();
-  for (int i = 0; i < nc; ++i) m = __builtin_fmaxf(m, part_ml[((slot0 + i) * G + gg) * 2]);
+  for (int i = d; i < nc; i += D) m = __builtin_fmaxf(m, part_ml[((slot0 + i) * G + gg) * 2]);
+  m = wave_max(m);
+  if (lane == 0) wred[wv] = m;
+  __syncthreads();
+#pragma unroll
+  for (int w = 0; w < kW; ++w) m = __builtin_fmaxf(m, wred[w]);
   float acc = 0.0f, l = 0.0f;
-  for (int i = 0; i < nc; ++i) {
-    const int64_t s = (slot0 + i) * G + gg;
-    const float a = __builtin_amdgcn_exp2f(part_ml[s * 2] - m);
-    acc = __builtin_fmaf(a, part_o[s * D + d], acc);
-    l = __builtin_fmaf(a, part_ml[s * 2 + 1], l);
+  for (int i0 = 0; i0 < nc; i0 += D) {
+    const int cnt = min(D, nc - i0);
+    __syncthreads();  // the previous group's weights are consumed
+    if (d < cnt) wts[d] = __builtin_amdgcn_exp2f(part_ml[((slot0 + i0 + d) * G + gg) * 2] - m);
+    __syncthreads();
+    int i = 0;
+    for (; i + 4 <= cnt; i += 4) {
+      float o[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) o[u] = part_o[((slot0 + i0 + i + u) * G + gg) * D + d];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        acc = __builtin_fmaf(wts[i + u], o[u], acc);
+        l = __builtin_fmaf(wts[i + u], part_ml[((slot0 + i0 + i + u) * G + gg) * 2 + 1], l);
+      }
+    }
+    for (; i < cnt; ++i) {
+      acc = __builtin_fmaf(wts[i], part_o[((slot0 + i0 + i) * G + gg) * D + d], acc);
+      l = __builtin_fmaf(wts[i], part_ml[((slot0 + i0 + i) * G + gg) * 2 + 1], l);
+    }
   }
   const float r = nc == 0 ? 0.0f : acc / l;
   out[((int64_t)b * hq + h) * D + d] = (uint16_t)f32_to_bf16(r);
