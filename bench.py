@@ -238,13 +238,36 @@ def kernel_traffic(kernel_source):
     return rec["bytes_per_launch"] if rec.get("source_sha256") == sha else None
 
 
+def copy_rate_gbs(torch, reps=20):
+    """Read + write bytes per second of a plain 1 GiB device-to-device copy on
+    this GPU: the practical HBM rate that the published peak overstates."""
+    x = torch.empty(2 ** 29, dtype=torch.bfloat16, device="cuda").fill_(1.0)
+    y = torch.empty_like(x)
+    for _ in range(3):
+        y.copy_(x)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        y.copy_(x)
+    e1.record()
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) / reps * 1e3
+    del x, y
+    torch.cuda.empty_cache()
+    return 2 * 2 ** 30 / (us * 1e-6) / 1e9
+
+
+COPY_GBS = None  # set in main()
+
+
 def stage_rooflines(pipe, st, csrc):
     """Roofline entry of every stage (algorithmic work / measured time)."""
     attn_tflops = pipe.attention_flops() / (st["attention"] * 1e-6) / 1e12
     gate_gbs = pipe.gate_bytes() / (st["gate"] * 1e-6) / 1e9
     compact_gbs = pipe.compact_bytes() / (st["compact"] * 1e-6) / 1e9
     select_gbs = (4 * pipe.seg.n_tokens + 4 * pipe.m) / (st["select"] * 1e-6) / 1e9
-    return {
+    roofs = {
         "attention": {"kernel": "gated_attention_kernel<128,2>", "bound": "mfma", "achieved": attn_tflops,
                       "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": attn_tflops / MFMA_BF16_PEAK_TFLOPS,
                       "traffic": kernel_traffic(os.path.join(csrc, "gated_attention.hip"))},
@@ -260,6 +283,11 @@ def stage_rooflines(pipe, st, csrc):
                    "unit": "GB/s", "frac": select_gbs / HBM_PEAK_GBS,
                    "traffic": kernel_traffic(os.path.join(csrc, "select_topk.hip"))},
     }
+    if COPY_GBS:
+        for r in roofs.values():
+            if r["bound"] == "hbm":
+                r["frac_of_copy_rate"] = r["achieved"] / COPY_GBS
+    return roofs
 
 
 def time_decode(torch, tg, reps=200):
@@ -300,7 +328,8 @@ def time_decode(torch, tg, reps=200):
         rec[name] = {"cache_rows": cap, "us_per_step": round(us, 2), "kv_gib": bsz * cap * 2 * hkv * dh * 2 / 2 ** 30,
                      "roofline": {"kernel": "decode_partial_kernel<128,2> + decode_combine_kernel<128>",
                                   "bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                                  "frac": gbs / HBM_PEAK_GBS, "traffic": None}}
+                                  "frac": gbs / HBM_PEAK_GBS, "traffic": None,
+                                  "frac_of_copy_rate": gbs / COPY_GBS if COPY_GBS else None}}
         del q, kc, vc, sc, ws
         torch.cuda.empty_cache()
     rec["speedup_pruned_vs_full"] = rec["full"]["us_per_step"] / rec["pruned"]["us_per_step"]
@@ -470,6 +499,9 @@ def main():
     from learned_token_pruning_amd import tokengate as tg
     from learned_token_pruning_amd import workloads as W
     csrc = os.path.join(ROOT, "learned_token_pruning_amd", "csrc")
+    global COPY_GBS
+    COPY_GBS = copy_rate_gbs(torch)
+    log(f"device copy rate {COPY_GBS:.0f} GB/s (read + write)")
 
     if args.calibrate_copy:
         src = torch.empty(64 * 2 ** 20, dtype=torch.float32, device="cuda").fill_(1.0)
@@ -540,7 +572,8 @@ def main():
             "query_tau": {"us_per_step": round(us_qtau, 2), "attention_us": round(st16t["attention"], 2),
                           "note": "tau_rh = softplus(sigma_h) log(rank) / log(max(2, position)), graph replay"},
             "attention": {"tflops": roofs["attention"]["achieved"], "frac_mfma_peak": roofs["attention"]["frac"]},
-            "select_plus_compact": {"gbs": sc_gbs, "frac_hbm_peak": sc_gbs / HBM_PEAK_GBS},
+            "select_plus_compact": {"gbs": sc_gbs, "frac_hbm_peak": sc_gbs / HBM_PEAK_GBS,
+                                    "frac_of_copy_rate": sc_gbs / COPY_GBS},
         }
         del p16
         torch.cuda.empty_cache()
@@ -621,6 +654,7 @@ def main():
     if not args.no_cpu_baseline and l16 is not None:
         log("timing the CPU oracle on the 16K workload")
         result["cpu_baseline"] = cpu_baseline(l16, 2048)
+    result["hbm_copy_rate_gbs"] = COPY_GBS
     print(json.dumps(result), flush=True)
 
 
