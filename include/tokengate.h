@@ -223,7 +223,9 @@ int tg_compact_kept(const int32_t* kept_idx, int64_t n_kept, int64_t n_src_rows,
  * NaN anywhere in q, k, v, key_score, tau or gain gives unspecified output
  * values (no error); +-inf scores act as ordinary logit biases.
  * Supported: head_dim in {64, 128}; hq % hkv == 0 with hq / hkv in {1, 2, 4};
- * all pointers 16-byte aligned; otherwise TG_ERR_UNSUPPORTED / INVALID_ARG. */
+ * kept_len * hkv * head_dim * 2 < 2^32 - 256 for every prompt (32-bit buffer
+ * ranges); all pointers 16-byte aligned; otherwise TG_ERR_UNSUPPORTED /
+ * INVALID_ARG. */
 int tg_gated_attention_prefill(const void* q, const void* k, const void* v, const float* key_score,
                                const float* tau, const float* gain, const tg_segment* segs,
                                const tg_plan_info* info, int hq, int hkv, int head_dim, void* out, void* stream);

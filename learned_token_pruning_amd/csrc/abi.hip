@@ -206,16 +206,29 @@ int tg_compact_kept(const int32_t* kept_idx, int64_t n_kept, int64_t n_src_rows,
   return hip_status(tg::launch_compact(kept_idx, n_kept, n_src_rows, desc, reinterpret_cast<hipStream_t>(stream)));
 }
 
-int tg_gated_attention_prefill(const void* q, const void* k, const void* v, const float* key_score,
-                               const float* tau, const float* gain, const tg_segment* segs,
-                               const tg_plan_info* info, int hq, int hkv, int head_dim, void* out, void* stream) {
+namespace {
+// Shapes every attention kernel supports.  `buffer_ranges`: the kernel
+// addresses one prompt's K/V rows through buffer descriptors, whose byte
+// ranges are 32-bit.
+int check_attention_shapes(const tg_segment* segs, const tg_plan_info* info, int hq, int hkv, int head_dim,
+                           bool buffer_ranges) {
   int st = check_info(segs, info);
   if (st != TG_OK) return st;
   if (hq <= 0 || hkv <= 0 || head_dim <= 0) return TG_ERR_INVALID_ARG;
-  if (info->total_kept > 0 && (!q || !k || !v || !out)) return TG_ERR_INVALID_ARG;
   if (hq % hkv != 0) return TG_ERR_UNSUPPORTED;
   const int G = hq / hkv;
   if (!(head_dim == 64 || head_dim == 128) || !(G == 1 || G == 2 || G == 4)) return TG_ERR_UNSUPPORTED;
+  if (buffer_ranges && (int64_t)info->max_kept_len * hkv * head_dim * 2 >= 0xffffff00LL) return TG_ERR_UNSUPPORTED;
+  return TG_OK;
+}
+}  // namespace
+
+int tg_gated_attention_prefill(const void* q, const void* k, const void* v, const float* key_score,
+                               const float* tau, const float* gain, const tg_segment* segs,
+                               const tg_plan_info* info, int hq, int hkv, int head_dim, void* out, void* stream) {
+  int st = check_attention_shapes(segs, info, hq, hkv, head_dim, true);
+  if (st != TG_OK) return st;
+  if (info->total_kept > 0 && (!q || !k || !v || !out)) return TG_ERR_INVALID_ARG;
   if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(out, 16)) return TG_ERR_INVALID_ARG;
   if ((key_score && !aligned(key_score, 4)) || (tau && !aligned(tau, 4)) || (gain && !aligned(gain, 4)))
     return TG_ERR_INVALID_ARG;
@@ -231,13 +244,10 @@ int tg_gated_attention_prefill_query_tau(const void* q, const void* k, const voi
                                          const float* sigma, const float* gain, const int32_t* positions,
                                          const tg_segment* segs, const tg_plan_info* info, int hq, int hkv,
                                          int head_dim, void* out, void* stream) {
-  int st = check_info(segs, info);
+  if (!sigma) return TG_ERR_INVALID_ARG;
+  int st = check_attention_shapes(segs, info, hq, hkv, head_dim, true);
   if (st != TG_OK) return st;
-  if (hq <= 0 || hkv <= 0 || head_dim <= 0 || !sigma) return TG_ERR_INVALID_ARG;
   if (info->total_kept > 0 && (!q || !k || !v || !out || !positions)) return TG_ERR_INVALID_ARG;
-  if (hq % hkv != 0) return TG_ERR_UNSUPPORTED;
-  const int G = hq / hkv;
-  if (!(head_dim == 64 || head_dim == 128) || !(G == 1 || G == 2 || G == 4)) return TG_ERR_UNSUPPORTED;
   if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(out, 16)) return TG_ERR_INVALID_ARG;
   if ((key_score && !aligned(key_score, 4)) || !aligned(sigma, 4) || (gain && !aligned(gain, 4)) ||
       (positions && !aligned(positions, 4)))
@@ -277,23 +287,12 @@ int tg_gated_attention_prefill_gather(const void* q, const void* k, const void* 
                                                reinterpret_cast<hipStream_t>(stream)));
 }
 
-namespace {
-int check_attention_shapes(const tg_segment* segs, const tg_plan_info* info, int hq, int hkv, int head_dim) {
-  int st = check_info(segs, info);
-  if (st != TG_OK) return st;
-  if (hq <= 0 || hkv <= 0 || head_dim <= 0) return TG_ERR_INVALID_ARG;
-  if (hq % hkv != 0) return TG_ERR_UNSUPPORTED;
-  const int G = hq / hkv;
-  if (!(head_dim == 64 || head_dim == 128) || !(G == 1 || G == 2 || G == 4)) return TG_ERR_UNSUPPORTED;
-  return TG_OK;
-}
-}  // namespace
 
 int tg_gated_attention_prefill_lse(const void* q, const void* k, const void* v, const float* key_score,
                                    const float* tau, const float* gain, const tg_segment* segs,
                                    const tg_plan_info* info, int hq, int hkv, int head_dim, void* out, float* lse,
                                    void* stream) {
-  int st = check_attention_shapes(segs, info, hq, hkv, head_dim);
+  int st = check_attention_shapes(segs, info, hq, hkv, head_dim, true);
   if (st != TG_OK) return st;
   if (info->total_kept > 0 && (!q || !k || !v || !out || !lse)) return TG_ERR_INVALID_ARG;
   if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(out, 16) || !aligned(lse, 4) ||
@@ -317,7 +316,7 @@ int tg_gated_attention_backward(const void* q, const void* k, const void* v, con
                                 const tg_plan_info* info, int hq, int hkv, int head_dim, const void* out,
                                 const void* dout, const float* lse, float* dq, float* dk, float* dv, float* ds,
                                 float* dgain, float* dtau, void* workspace, size_t workspace_bytes, void* stream) {
-  int st = check_attention_shapes(segs, info, hq, hkv, head_dim);
+  int st = check_attention_shapes(segs, info, hq, hkv, head_dim, false);
   if (st != TG_OK) return st;
   if (info->total_kept > 0 && (!q || !k || !v || !out || !dout || !lse || !dq || !dk || !dv))
     return TG_ERR_INVALID_ARG;
@@ -454,6 +453,7 @@ int tg_decoder_layer(void* hidden, const int32_t* positions, const float* key_sc
   if (d % 128 != 0 || f % 64 != 0 || nqkv % 128 != 0 || (hq * head_dim) % 64 != 0 || (2 * f) % 128 != 0 ||
       !(head_dim == 64 || head_dim == 128) || !(G == 1 || G == 2 || G == 4))
     return TG_ERR_UNSUPPORTED;
+  if ((int64_t)info->max_kept_len * hkv * head_dim * 2 >= 0xffffff00LL) return TG_ERR_UNSUPPORTED;  // attention ranges
   const LayerWs L = layer_ws(m, d, hq, hkv, head_dim, f);
   if (!workspace || !aligned(workspace, 256) || workspace_bytes < L.total) return TG_ERR_WORKSPACE;
   if (!aligned(hidden, 16) || (post_attn_norm && !aligned(post_attn_norm, 16))) return TG_ERR_UNSUPPORTED;

@@ -160,6 +160,17 @@ def test_attention_validation():
     assert f(FAKE, FAKE, FAKE, None, None, None, FAKE, info, 0, 8, 128, FAKE, None) == -1
 
 
+def test_attention_rejects_prompts_past_32bit_ranges():
+    # 2^21 kept rows x 8 KV heads x 128 dims x 2 bytes = 2^32 bytes of K per prompt
+    big = tg.plan_segments([0, 1 << 21], [0], [0], [0])
+    info = ctypes.byref(big.info)
+    assert L.tg_gated_attention_prefill(FAKE, FAKE, FAKE, None, None, None, FAKE, info, 16, 8, 128, FAKE, None) == -2
+    assert L.tg_gated_attention_prefill_query_tau(FAKE, FAKE, FAKE, None, FAKE, None, FAKE, FAKE, info, 16, 8, 128,
+                                                  FAKE, None) == -2
+    assert L.tg_gated_attention_prefill_lse(FAKE, FAKE, FAKE, None, None, None, FAKE, info, 16, 8, 128, FAKE, FAKE,
+                                            None) == -2
+
+
 def test_attention_gather_validation():
     p = _plan()
     info = ctypes.byref(p.info)
