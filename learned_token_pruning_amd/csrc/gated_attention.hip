@@ -18,7 +18,8 @@
 // wave of a SIMD issues MFMAs the other runs its exp2s, so the matrix cores
 // and the VALU work at the same time.  All 512 threads stage the next K tile
 // (threads 0-255, with the scores) and the V tile due next (threads 256-511)
-// through registers during each half-step.
+// through registers: loaded during one half-step, written to LDS at the end of
+// the next.
 //
 // MFMA mapping (v_mfma_f32_32x32x16_bf16).  Scores are computed transposed,
 // S^T = K . Q^T, so a lane owns one query column (l % 32) and 16 key rows per
@@ -294,8 +295,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
   const int wlast = qw0 + 31;  // this wave's last query row
 
   // Staging registers, two sets (set = tile parity): a tile's global loads are
-  // issued two half-steps before the tile is read from LDS and stored to LDS
-  // at the start of the half-step in between.
+  // issued at the start of one half-step and stored to LDS at the end of the
+  // next, so they have two half-steps to land.
   u32x4 sreg[2][4];
   float sr[2] = {0.0f, 0.0f};
   if (stage_k) {

@@ -570,19 +570,22 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_reduce_params_kernel(const tg
   }
 }
 
-// Work split of bwd_dkdv: 128-key blocks x query chunks of qc 32-row blocks
-// (at most about four chunks per key block, so the longest workgroup walks
-// about a quarter of the prompt).
+// Work split of bwd_dkdv: 128-key blocks x query chunks of qc 32-row blocks.
+// Up to four chunks per key block (then the longest workgroup walks a quarter
+// of the prompt), but only as many as needed for about two workgroups per CU:
+// every chunk costs a pass over fp32 dK / dV partials.
 struct BwdGeom {
   int key_blocks, qc, n_chunks;
   int64_t n_slots;
 };
-BwdGeom bwd_geom(const tg_plan_info& info) {
+BwdGeom bwd_geom(const tg_plan_info& info, int hkv) {
   BwdGeom g;
   const int max_len = (int)info.max_kept_len;
   g.key_blocks = max(1, (max_len + kKeyBlock - 1) / kKeyBlock);
   const int max_qb = max(1, (max_len + 31) / 32);
-  g.qc = max(8, (max_qb + 3) / 4);
+  const int64_t wgs = (int64_t)hkv * g.key_blocks * info.n_seg;
+  const int want = (int)min((int64_t)4, max((int64_t)1, (512 + wgs - 1) / wgs));
+  g.qc = max(8, (max_qb + want - 1) / want);
   g.n_chunks = (max_qb + g.qc - 1) / g.qc;
   g.n_slots = (int64_t)info.n_seg * g.key_blocks * g.n_chunks;
   return g;
@@ -600,14 +603,14 @@ struct BwdWs {
 int64_t round64(int64_t x) { return (x + 63) / 64 * 64; }
 
 int64_t bwd_ws_floats(const tg_plan_info& info, int hq, int hkv, int head_dim) {
-  const BwdGeom g = bwd_geom(info);
+  const BwdGeom g = bwd_geom(info, hkv);
   const int64_t kv = info.total_kept * hkv * head_dim;
   return round64(info.total_kept * hq) + round64((int64_t)g.n_chunks * hkv * info.total_kept) +
          2 * round64(g.n_chunks * kv) + 2 * g.n_slots * hq;
 }
 
 BwdWs carve(void* ws, const tg_plan_info& info, int hq, int hkv, int head_dim) {
-  const BwdGeom g = bwd_geom(info);
+  const BwdGeom g = bwd_geom(info, hkv);
   const int64_t kv = info.total_kept * hkv * head_dim;
   BwdWs w;
   w.dt = reinterpret_cast<float*>(ws);
@@ -625,7 +628,7 @@ hipError_t launch_bwd_dg(const void* q, const void* k, const void* v, const floa
                          const void* out, const void* dout, const float* lse, float* dq, float* dk, float* dv,
                          float* ds, float* dgain, float* dtau, void* workspace, hipStream_t stream) {
   const BwdWs w = carve(workspace, info, hq, hkv, D);
-  const BwdGeom geo = bwd_geom(info);
+  const BwdGeom geo = bwd_geom(info, hkv);
   auto* qb = reinterpret_cast<const uint16_t*>(q);
   auto* kb = reinterpret_cast<const uint16_t*>(k);
   auto* vb = reinterpret_cast<const uint16_t*>(v);
