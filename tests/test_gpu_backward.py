@@ -94,7 +94,8 @@ def _inputs(rng, m, hq, hkv, d):
     return q, k, v, dout, s, tau, gain
 
 
-@pytest.mark.parametrize("d,hq,hkv", [(64, 4, 2), (64, 4, 4), (64, 8, 2), (128, 2, 2), (128, 8, 4), (128, 16, 8)])
+@pytest.mark.parametrize("d,hq,hkv", [(64, 4, 2), (64, 4, 4), (64, 8, 2), (128, 2, 2), (128, 8, 4), (128, 16, 8),
+                                     (128, 16, 4)])
 def test_backward_ragged(d, hq, hkv):
     _say("backward ragged", d, hq, hkv)
     rng = np.random.default_rng(d + 5 * hq + hkv)
