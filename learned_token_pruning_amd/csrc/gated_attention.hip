@@ -17,9 +17,10 @@
 // groups are half a step apart, separated by workgroup barriers: while one
 // wave of a SIMD issues MFMAs the other runs its exp2s, so the matrix cores
 // and the VALU work at the same time.  All 512 threads stage the next K tile
-// (threads 0-255, with the scores) and the V tile due next (threads 256-511)
-// through registers: loaded during one half-step, written to LDS at the end of
-// the next.
+// (threads 0-255, with the scores) and the V tile due next (threads 256-511):
+// for compacted rows by direct-to-LDS loads into three LDS stages (the kernel
+// at the end of this file), for gathered rows through registers, loaded during
+// one half-step and written to LDS at the end of the next.
 //
 // MFMA mapping (v_mfma_f32_32x32x16_bf16).  Scores are computed transposed,
 // S^T = K . Q^T, so a lane owns one query column (l % 32) and 16 key rows per
@@ -28,8 +29,10 @@
 // O^T += V^T . P^T, which lets P^T be fed from the score registers without
 // any data movement (the key order inside each 16-key MFMA step is permuted
 // identically on both operands) and keeps the per-query rescale lane-local.
-// V is therefore staged transposed in LDS; K row-major.  Both use padded rows
-// so that the 16- and 8-byte LDS reads are bank-conflict free.
+// The register-staged kernel stores V transposed in LDS and K row-major, both
+// with padded rows, so the 16- and 8-byte LDS reads are bank-conflict free;
+// the direct-to-LDS kernel keeps both row-major and reads V^T with transposing
+// LDS reads.
 //
 // Logit arithmetic.  With c_h = |tau_h| log2(e) / sqrt(D) (floored at 1e-30;
 // a negative temperature flips the sign of Q, which is exact) the score
@@ -189,6 +192,116 @@ __device__ __forceinline__ void sched_reads_ahead() {
   for (int i = 0; i < MFMAS - (READS - AHEAD); ++i) __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
 }
 
+// Softmax phase of one 64-key tile starting at key kv0: causal mask on the
+// diagonal tiles, running max with the lazy rescale, exp2 of the logits, row
+// sums over the bf16-rounded probabilities, and the P^T operands of the 4 PV
+// steps.
+template <int D>
+__device__ __forceinline__ void softmax_tile(int kv0, int qrow, int qw0, int n, int g, float cs, f32x16 (&sa)[2],
+                                             float& m_run, float& l_run, f32x16 (&o)[D / 32], u32x4 (&pf)[4]) {
+  if (kv0 + kBN - 1 > qw0 || kv0 + kBN > n) {
+    // the lane's last visible key (tile-local), less its 4 g row offset, so that
+    // every comparison below is against a constant
+    const int lim = min(qrow, n - 1) - kv0 - 4 * g;
+#pragma unroll
+    for (int hf = 0; hf < 2; ++hf)
+#pragma unroll
+      for (int i = 0; i < 16; ++i)
+        if (hf * 32 + 8 * (i / 4) + (i % 4) > lim) sa[hf][i] = -__builtin_inff();
+  }
+  float m0 = -__builtin_inff(), m1 = -__builtin_inff();
+#pragma unroll
+  for (int i = 0; i < 16; i += 2) {
+    m0 = __builtin_fmaxf(m0, __builtin_fmaxf(sa[0][i], sa[0][i + 1]));
+    m1 = __builtin_fmaxf(m1, __builtin_fmaxf(sa[1][i], sa[1][i + 1]));
+  }
+  const float x = cs * xor32_max(__builtin_fmaxf(m0, m1));
+  // Lazy rescale: the reference point m_run only moves when some row's
+  // max exceeds it by more than 2^8 (or on the first visible tile);
+  // softmax does not depend on the reference point, and
+  // exp2(x - m_run) <= 2^8 stays well inside fp32 and bf16 range.
+  if (__ballot(x > m_run + 8.0f) != 0) {
+    asm volatile("; rare rescale");  // keeps this a branch rather than a select on every tile
+    const float m_new = __builtin_fmaxf(m_run, x);
+    const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+    l_run *= alpha;
+#pragma unroll
+    for (int dt = 0; dt < D / 32; ++dt) o[dt] *= alpha;
+    m_run = m_new;
+  }
+  const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
+#pragma unroll
+  for (int hf = 0; hf < 2; ++hf)
+#pragma unroll
+    for (int sub = 0; sub < 2; ++sub) {
+      u32x4 w;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(sa[hf][8 * sub + 2 * j], cs, -m_run));
+        const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(sa[hf][8 * sub + 2 * j + 1], cs, -m_run));
+        // (bit-cast a scalar: a bit-cast of the vector element w[j] reads element 0 with this compiler)
+        const uint32_t pk = pack_bf16(p0, p1);
+        w[j] = pk;
+        l_run = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pk), ones, l_run, false);
+      }
+      pf[2 * hf + sub] = w;
+    }
+}
+
+// Merges the two wave groups (group 1 hands m, l and O^T to group 0 through
+// LDS at xo: 4 waves x (D x 32 + 64) floats), normalises, and stores the bf16
+// output rows (and the natural-log log-sum-exp when lse is given).
+template <int D>
+__device__ __forceinline__ void merge_and_store(float* xo, int grp, int wave, int lane, int g, int l32,
+                                                const f32x16 (&o)[D / 32], float m_run, float l_run, int qrow, int n,
+                                                const tg_segment& seg, int64_t q_stride, int h, int hq,
+                                                float* __restrict__ lse, uint16_t* __restrict__ out) {
+  float* mine = xo + wave * (D * 32 + 64);
+  const float l_half = xor32_sum(l_run);  // both half-waves: same bits
+  if (grp == 1) {
+#pragma unroll
+    for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) mine[(dt * 16 + i) * 64 + lane] = o[dt][i];
+    if (g == 0) {
+      mine[D * 32 + l32] = m_run;
+      mine[D * 32 + 32 + l32] = l_half;
+    }
+  }
+  __syncthreads();
+  if (grp == 0) {
+    const float m1 = mine[D * 32 + l32];
+    const float l1 = mine[D * 32 + 32 + l32];
+    const float m = __builtin_fmaxf(m_run, m1);
+    const float a0 = m_run == -__builtin_inff() ? 0.0f : __builtin_amdgcn_exp2f(m_run - m);
+    const float a1 = m1 == -__builtin_inff() ? 0.0f : __builtin_amdgcn_exp2f(m1 - m);
+    const float l_all = l_half * a0 + l1 * a1;
+    const float inv = 1.0f / l_all;
+    // natural-log log-sum-exp of the row's logits (kept for the backward pass)
+    if (lse != nullptr && qrow < n && g == 0)
+      lse[((int64_t)seg.kept_start + qrow) * hq + h] = (m + __log2f(l_all)) * 0.6931471805599453f;
+    if (qrow < n) {
+      uint16_t* orow = out + ((int64_t)seg.kept_start + qrow) * q_stride + (int64_t)h * D;
+#pragma unroll
+      for (int dt = 0; dt < D / 32; ++dt) {
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4) {
+          float r[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int i = 4 * q4 + e;
+            r[e] = (o[dt][i] * a0 + mine[(dt * 16 + i) * 64 + lane] * a1) * inv;
+          }
+          *reinterpret_cast<u32x2*>(orow + 32 * dt + 8 * q4 + 4 * g) = u32x2{pack_bf16(r[0], r[1]),
+                                                                             pack_bf16(r[2], r[3])};
+        }
+      }
+    }
+  }
+}
+
+// Register-staged kernel, launched for gathering reads (the kept-row indices
+// take 64 KiB of LDS, which leaves no room for three direct-to-LDS stages).
 // kGather: q, k, v and key_score hold every token (n_src rows); kept row r of
 // a prompt is read from source row kept_idx[kept_start + r] (gather on load,
 // no compacted copies).  The output is always compacted.
@@ -363,56 +476,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
     } else {
       // softmax phase of tile hs - 1
       const int js = hs - 1;
-      if (js >= 0 && js < ntiles && js * kBN <= wlast) {
-        const int kv0 = js * kBN;
-        if (kv0 + kBN - 1 > qw0 || kv0 + kBN > n) {
-          // the lane's last visible key (tile-local), less its 4 g row offset, so that
-          // every comparison below is against a constant
-          const int lim = min(qrow, n - 1) - kv0 - 4 * g;
-#pragma unroll
-          for (int hf = 0; hf < 2; ++hf)
-#pragma unroll
-            for (int i = 0; i < 16; ++i)
-              if (hf * 32 + 8 * (i / 4) + (i % 4) > lim) sa[hf][i] = -__builtin_inff();
-        }
-        float m0 = -__builtin_inff(), m1 = -__builtin_inff();
-#pragma unroll
-        for (int i = 0; i < 16; i += 2) {
-          m0 = __builtin_fmaxf(m0, __builtin_fmaxf(sa[0][i], sa[0][i + 1]));
-          m1 = __builtin_fmaxf(m1, __builtin_fmaxf(sa[1][i], sa[1][i + 1]));
-        }
-        const float x = cs * xor32_max(__builtin_fmaxf(m0, m1));
-        // Lazy rescale: the reference point m_run only moves when some row's
-        // max exceeds it by more than 2^8 (or on the first visible tile);
-        // softmax does not depend on the reference point, and
-        // exp2(x - m_run) <= 2^8 stays well inside fp32 and bf16 range.
-        if (__ballot(x > m_run + 8.0f) != 0) {
-          asm volatile("; rare rescale");  // keeps this a branch rather than a select on every tile
-          const float m_new = __builtin_fmaxf(m_run, x);
-          const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
-          l_run *= alpha;
-#pragma unroll
-          for (int dt = 0; dt < D / 32; ++dt) o[dt] *= alpha;
-          m_run = m_new;
-        }
-        const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
-#pragma unroll
-        for (int hf = 0; hf < 2; ++hf)
-#pragma unroll
-          for (int sub = 0; sub < 2; ++sub) {
-            u32x4 w;
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-              const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(sa[hf][8 * sub + 2 * j], cs, -m_run));
-              const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(sa[hf][8 * sub + 2 * j + 1], cs, -m_run));
-              // (bit-cast a scalar: a bit-cast of the vector element w[j] reads element 0 with this compiler)
-              const uint32_t pk = pack_bf16(p0, p1);
-              w[j] = pk;
-              l_run = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pk), ones, l_run, false);
-            }
-            pf[2 * hf + sub] = w;
-          }
-      }
+      if (js >= 0 && js < ntiles && js * kBN <= wlast)
+        softmax_tile<D>(js * kBN, qrow, qw0, n, g, cs, sa, m_run, l_run, o, pf);
     }
 
     // stores last: K tile hs + 1 and V tile hs - 1 from set P ^ 1 (loaded one
@@ -431,49 +496,305 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
   }
 
   // Merge the two groups: group 1 hands (m, l, O^T) to group 0 through LDS.
-  float* xo = reinterpret_cast<float*>(&sm);  // 4 waves x (D x 32 + 64) floats, fits in the K/V buffers
-  float* mine = xo + wave * (D * 32 + 64);
-  const float l_half = xor32_sum(l_run);  // both half-waves: same bits
-  if (grp == 1) {
+  merge_and_store<D>(reinterpret_cast<float*>(&sm), grp, wave, lane, g, l32, o, m_run, l_run, qrow, n, seg, q_stride, h,
+                     hq, lse, out);
+}
+
+// ---------------------------------------------------------------------------
+// Direct-to-LDS staging (compacted rows, per-head or per-query temperature).
+//
+// The same schedule, but K, V and the key scores go from global memory straight
+// into LDS (buffer loads with the LDS destination), so no staging registers and
+// no LDS store instructions.  Three LDS stages per operand: the DMA of K tile
+// hs + 2 and V tile hs is issued at the start of half-step hs into the stage
+// nobody reads during it, and every wave waits (vmcnt) for its previous
+// half-step's DMAs before the barrier that ends the half-step, so each DMA has
+// two half-steps to land.  The barriers are plain s_barrier with explicit
+// waits: a workgroup fence would also wait for the DMAs just issued.
+//
+// Both tiles are row-major with their 16-byte chunks swizzled per row, for
+// the 256-byte (64-bank) LDS cycle of gfx950.  K: chunk c of row r sits at
+// c ^ (r & 15) (D = 128) or c ^ ((r >> 1) & 7) (D = 64), so the 16 rows a
+// cycle of QK fragment reads touches land on 16 distinct chunk slots.  V:
+// chunk c of row r sits at c ^ 4 (r & 3) (D = 128) or c ^ 4 ((r >> 1) & 1)
+// (D = 64); the PV operand V^T is read with ds_read_b64_tr_b16, where 16 lanes
+// fetch a 4-key x 16-dim block and each lane receives the 4 keys of one dim,
+// and the 4 rows x 64 bytes of a cycle land on distinct banks.  Out-of-range
+// rows read as zeros (the buffer range check also covers the DMA).
+
+template <int D>
+struct alignas(16) DmaSmem {
+  uint16_t k[3][kBN * D];
+  uint16_t v[3][kBN * D];
+  float s[3][kBN];  // raw key scores
+};
+
+template <int D>
+__device__ __forceinline__ int kswz(int r) {
+  return D == 128 ? (r & 15) : ((r >> 1) & 7);
+}
+template <int D>
+__device__ __forceinline__ int vswz(int r) {
+  return D == 128 ? 4 * (r & 3) : 4 * ((r >> 1) & 1);
+}
+
+#define TG_LDS(p) ((__attribute__((address_space(3))) void*)(p))
+
+// One DMA instruction: every active lane copies 16 (or 4) bytes from the buffer
+// at voff + soff into LDS at lds_dst + 16 (or 4) x lane.  Issued in asm so the
+// compiler does not order later LDS reads after it; every consumer waits with
+// an explicit vmcnt (the instruction has no destination registers).
+__device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, const void* lds_dst, uint32_t voff, uint32_t soff) {
+  const uint32_t m0v = (uint32_t)(uintptr_t)TG_LDS(lds_dst);
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds" ::"s"(m0v), "v"(voff), "s"(r), "s"(soff)
+               : "memory");
+}
+__device__ __forceinline__ void dma4(__amdgpu_buffer_rsrc_t r, const void* lds_dst, uint32_t voff, uint32_t soff) {
+  const uint32_t m0v = (uint32_t)(uintptr_t)TG_LDS(lds_dst);
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dword %1, %2, %3 offen lds" ::"s"(m0v), "v"(voff), "s"(r), "s"(soff)
+               : "memory");
+}
+
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
+// Instruction order for MFMAS matrix ops fed by two LDS reads each: AHEAD
+// reads first, then MFMA / read / read, then the remaining MFMAs.
+template <int MFMAS, int AHEAD>
+__device__ __forceinline__ void sched_two_reads_ahead() {
+  constexpr int READS = 2 * MFMAS;
+  constexpr int PAIRS = (READS - AHEAD) / 2;
 #pragma unroll
-    for (int dt = 0; dt < D / 32; ++dt)
+  for (int i = 0; i < AHEAD; ++i) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
 #pragma unroll
-      for (int i = 0; i < 16; ++i) mine[(dt * 16 + i) * 64 + lane] = o[dt][i];
-    if (g == 0) {
-      mine[D * 32 + l32] = m_run;
-      mine[D * 32 + 32 + l32] = l_half;
+  for (int i = 0; i < PAIRS; ++i) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+  }
+#pragma unroll
+  for (int i = 0; i < MFMAS - PAIRS; ++i) __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+}
+
+template <int D, int G, int MODE>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void gated_attention_dma_kernel(
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
+    const float* __restrict__ key_score, const float* __restrict__ tau, const float* __restrict__ gain,
+    const tg_segment* __restrict__ segs, int hq, int hkv, const int32_t* __restrict__ qpos, float* __restrict__ lse,
+    uint16_t* __restrict__ out) {
+  static_assert(MODE != kGather, "gathering reads keep register staging");
+  constexpr bool QTAU = MODE == kQueryTau;
+  constexpr int kBM = 128 / G;
+  constexpr int kWavesPerHead = 4 / G;
+  constexpr int NC = D / 8;   // 16-byte chunks per row
+  constexpr int NJ = NC / 4;  // DMA instructions per staging wave per tile (64 NC chunks over 4 waves)
+  __shared__ DmaSmem<D> sm;
+
+  const tg_segment seg = segs[blockIdx.z];
+  const int n = seg.kept_len;
+  const int q0 = (gridDim.y - 1 - blockIdx.y) * kBM;
+  if (q0 >= n) return;  // uniform
+  const int q_end = min(q0 + kBM, n);
+
+  const int tid = threadIdx.x;
+  const int grp = tid >> 8;
+  const int gtid = tid & 255;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(gtid >> 6);
+  const int g = lane >> 5;
+  const int l32 = lane & 31;
+  const int c = blockIdx.x;
+  const int hl = wave / kWavesPerHead;
+  const int h = c * G + hl;
+  const int qw0 = q0 + (wave % kWavesPerHead) * 32;
+  const int qrow = qw0 + l32;
+
+  const int64_t q_stride = (int64_t)hq * D;
+  const int64_t kv_stride = (int64_t)hkv * D;
+  const int64_t row0 = seg.kept_start;
+  const uint32_t nrows = (uint32_t)n;
+  const uint16_t* kb = k + row0 * kv_stride + (int64_t)c * D;
+  const uint16_t* vb = v + row0 * kv_stride + (int64_t)c * D;
+  const bool use_bias = key_score != nullptr && gain != nullptr;
+  const uint32_t row_bytes = (uint32_t)kv_stride * 2u;
+  const __amdgpu_buffer_rsrc_t rk = make_rsrc(kb, nrows * row_bytes - (uint32_t)c * D * 2u);
+  const __amdgpu_buffer_rsrc_t rv = make_rsrc(vb, nrows * row_bytes - (uint32_t)c * D * 2u);
+  const __amdgpu_buffer_rsrc_t rs = make_rsrc(use_bias ? key_score + row0 : key_score, use_bias ? nrows * 4u : 0u);
+  const bool stage_k = grp == 0;  // threads 0-255 stage K and the scores, 256-511 V
+
+  // DMA source offsets inside a tile: chunk slot (j 4 + wave) 64 + lane
+  uint32_t doff[NJ];
+#pragma unroll
+  for (int j = 0; j < NJ; ++j) {
+    const int p = (j * 4 + wave) * 64 + lane;
+    const int r = p / NC;
+    const int cc = (p % NC) ^ (stage_k ? kswz<D>(r) : vswz<D>(r));
+    doff[j] = (uint32_t)r * row_bytes + (uint32_t)cc * 16u;
+  }
+  auto dma_k = [&](int tile, int buf) {
+    const uint32_t soff = (uint32_t)(tile * kBN) * row_bytes;
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) dma16(rk, &sm.k[buf][(j * 4 + wave) * 64 * 8], doff[j], soff);
+    if (lane < 16) dma4(rs, &sm.s[buf][16 * wave], (uint32_t)(16 * wave + lane) * 4u, (uint32_t)(tile * kBN) * 4u);
+  };
+  auto dma_v = [&](int tile, int buf) {
+    const uint32_t soff = (uint32_t)(tile * kBN) * row_bytes;
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) dma16(rv, &sm.v[buf][(j * 4 + wave) * 64 * 8], doff[j], soff);
+  };
+
+  const float base = kLog2e / __builtin_sqrtf((float)D);
+  float th = tau != nullptr ? tau[h] : 1.0f;
+  const float rat = !use_bias ? 0.0f
+                    : QTAU    ? gain[h] * kLog2e
+                              : gain[h] * kLog2e / __builtin_fmaxf(__builtin_fabsf(th) * base, 1e-30f);
+  if (QTAU) {
+    const int r = qrow < n ? qrow : n - 1;
+    const float sp = th > 20.0f ? th : log1pf(expf(th));
+    const float pr = (float)max(2, qpos[seg.kept_start + r] + 1);
+    th = sp * (logf((float)(r + 1)) / logf(pr));
+  }
+  const float cs = __builtin_fmaxf(__builtin_fabsf(th) * base, 1e-30f);
+  const float inv_cs = QTAU ? 1.0f / cs : 1.0f;
+
+  const int ntiles = (q_end + kBN - 1) / kBN;
+  const int wlast = qw0 + 31;
+
+  u32x4 qf[D / 16];
+  {
+    const int r = qrow < n ? qrow : n - 1;
+    const u32x4* src =
+        reinterpret_cast<const u32x4*>(q + ((int64_t)seg.kept_start + r) * q_stride + (int64_t)h * D + 8 * g);
+#pragma unroll
+    for (int ks = 0; ks < D / 16; ++ks) qf[ks] = src[2 * ks];
+  }
+  if (stage_k) {
+    dma_k(0, 0);
+    if (ntiles > 1) dma_k(1, 1);
+  }
+  {
+    const uint32_t flip = th < 0.0f ? 0x80008000u : 0u;
+#pragma unroll
+    for (int ks = 0; ks < D / 16; ++ks) qf[ks] ^= flip;
+#pragma unroll
+    for (int ks = 0; ks < D / 16; ++ks) asm volatile("" : "+v"(qf[ks]));
+  }
+
+  // LDS element offsets of this lane's fragment reads inside a tile.
+  // K (QK A operand): row l32 (+32 for the second half), chunk 2 ks + g.
+  uint32_t kaddr[D / 16];
+#pragma unroll
+  for (int ks = 0; ks < D / 16; ++ks) kaddr[ks] = (uint32_t)(l32 * D + (((2 * ks + g) ^ kswz<D>(l32)) * 8));
+  // V (PV A operand, transposing read): 16-lane group qg = lane / 16 covers dims 32 dt + 16 (qg % 2) + 0..15
+  // and keys 4 (qg / 2) + 0..3 of a 16-key step; source lane s points at row 4 g + s / 4, dims + 4 (s % 4).
+  uint32_t vaddr[D / 32];
+  {
+    const int s = lane & 15, qg = lane >> 4;
+    const int r = 4 * g + (s >> 2);
+#pragma unroll
+    for (int dt = 0; dt < D / 32; ++dt) {
+      const int cc = 4 * dt + 2 * (qg & 1) + ((s & 3) >> 1);
+      vaddr[dt] = (uint32_t)(r * D + ((cc ^ vswz<D>(r)) * 8) + 4 * (s & 1));
     }
   }
-  __syncthreads();
-  if (grp == 0) {
-    const float m1 = mine[D * 32 + l32];
-    const float l1 = mine[D * 32 + 32 + l32];
-    const float m = __builtin_fmaxf(m_run, m1);
-    const float a0 = m_run == -__builtin_inff() ? 0.0f : __builtin_amdgcn_exp2f(m_run - m);
-    const float a1 = m1 == -__builtin_inff() ? 0.0f : __builtin_amdgcn_exp2f(m1 - m);
-    const float l_all = l_half * a0 + l1 * a1;
-    const float inv = 1.0f / l_all;
-    // natural-log log-sum-exp of the row's logits (kept for the backward pass)
-    if (lse != nullptr && qrow < n && g == 0)
-      lse[((int64_t)seg.kept_start + qrow) * hq + h] = (m + __log2f(l_all)) * 0.6931471805599453f;
-    if (qrow < n) {
-      uint16_t* orow = out + ((int64_t)seg.kept_start + qrow) * q_stride + (int64_t)h * D;
+
+  f32x16 o[D / 32];
 #pragma unroll
-      for (int dt = 0; dt < D / 32; ++dt) {
+  for (int dt = 0; dt < D / 32; ++dt) o[dt] = f32x16{};
+  float m_run = -__builtin_inff();
+  float l_run = 0.0f;
+  f32x16 sa[2];
+  u32x4 pf[4];
+
+  if (stage_k && ntiles > 1)
+    wait_vm<NJ + 1>();  // K tile 0 landed; tile 1 may still be in flight
+  else
+    wait_vm<0>();
+  lds_barrier();
+
+  int b_cur = 0;  // hs % 3
+  auto half_step = [&](int hs, auto p_) {
+    constexpr int P = decltype(p_)::value;
+    const int b1 = b_cur == 2 ? 0 : b_cur + 1;  // (hs + 1) % 3 == (hs - 2) % 3
+    const int b2 = b1 == 2 ? 0 : b1 + 1;        // (hs + 2) % 3
+    const bool dma_now = stage_k ? hs + 2 < ntiles : hs < ntiles;
+    if (dma_now) {
+      if (stage_k)
+        dma_k(hs + 2, b2);
+      else
+        dma_v(hs, b_cur);
+    }
+
+    if (P == grp) {
+      const int jp = hs - 2;
+      if (jp >= 0 && jp * kBN <= wlast) {
+        const uint16_t* vt = sm.v[b1];
 #pragma unroll
-        for (int q4 = 0; q4 < 4; ++q4) {
-          float r[4];
+        for (int s4 = 0; s4 < 4; ++s4) {
 #pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const int i = 4 * q4 + e;
-            r[e] = (o[dt][i] * a0 + mine[(dt * 16 + i) * 64 + lane] * a1) * inv;
+          for (int dt = 0; dt < D / 32; ++dt) {
+            typedef short short4v __attribute__((ext_vector_type(4)));
+            const short4v lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                (__attribute__((address_space(3))) short4v*)(vt + vaddr[dt] + 16 * s4 * D));
+            const short4v hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                (__attribute__((address_space(3))) short4v*)(vt + vaddr[dt] + (16 * s4 + 8) * D));
+            const u32x2 l2 = __builtin_bit_cast(u32x2, lo), h2 = __builtin_bit_cast(u32x2, hi);
+            o[dt] = mfma32(u32x4{l2[0], l2[1], h2[0], h2[1]}, pf[s4], o[dt]);
           }
-          *reinterpret_cast<u32x2*>(orow + 32 * dt + 8 * q4 + 4 * g) = u32x2{pack_bf16(r[0], r[1]),
-                                                                             pack_bf16(r[2], r[3])};
         }
+        sched_two_reads_ahead<4 * (D / 32), 8>();
       }
+      const int jq = hs;
+      if (jq < ntiles && jq * kBN <= wlast) {
+        const float* bias = sm.s[b_cur];
+#pragma unroll
+        for (int hf = 0; hf < 2; ++hf)
+#pragma unroll
+          for (int q4 = 0; q4 < 4; ++q4) {
+            const f32x4 bv = *reinterpret_cast<const f32x4*>(&bias[hf * 32 + 8 * q4 + 4 * g]);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) sa[hf][4 * q4 + e] = QTAU ? (bv[e] * rat) * inv_cs : bv[e] * rat;
+          }
+        const uint16_t* kt = sm.k[b_cur];
+#pragma unroll
+        for (int ks = 0; ks < D / 16; ++ks) {
+          const u32x4 a0 = *reinterpret_cast<const u32x4*>(kt + kaddr[ks]);
+          const u32x4 a1 = *reinterpret_cast<const u32x4*>(kt + kaddr[ks] + 32 * D);
+          sa[0] = mfma32(a0, qf[ks], sa[0]);
+          sa[1] = mfma32(a1, qf[ks], sa[1]);
+        }
+        sched_reads_ahead<D / 8, 8 + D / 8, 8 + 8>();
+      }
+    } else {
+      // softmax phase of tile hs - 1
+      const int js = hs - 1;
+      if (js >= 0 && js < ntiles && js * kBN <= wlast)
+        softmax_tile<D>(js * kBN, qrow, qw0, n, g, cs, sa, m_run, l_run, o, pf);
     }
+
+    // K tile hs + 1 and V tile hs - 1 (issued one half-step ago) must have landed;
+    // this half-step's DMAs may stay in flight
+    if (dma_now) {
+      if (stage_k)
+        wait_vm<NJ + 1>();
+      else
+        wait_vm<NJ>();
+    } else {
+      wait_vm<0>();
+    }
+    lds_barrier();
+    b_cur = b1;
+  };
+  for (int hs = 0; hs < ntiles + 2; hs += 2) {
+    half_step(hs, std::integral_constant<int, 0>());
+    if (hs + 1 < ntiles + 2) half_step(hs + 1, std::integral_constant<int, 1>());
   }
+
+  // Merge the two groups: group 1 hands (m, l, O^T) to group 0 through LDS.
+  merge_and_store<D>(reinterpret_cast<float*>(&sm), grp, wave, lane, g, l32, o, m_run, l_run, qrow, n, seg, q_stride, h,
+                     hq, lse, out);
 }
 
 template <int D, int G>
@@ -493,11 +814,11 @@ hipError_t launch_dg(const void* q, const void* k, const void* v, const float* k
     hipLaunchKernelGGL((gated_attention_kernel<D, G, kGather>), grid, dim3(kThreads), 0, stream, qb, kb, vb, ks, tau,
                        gain, segs, hq, hkv, kept_idx, n_src, nullptr, lse, ob);
   else if (qpos != nullptr)
-    hipLaunchKernelGGL((gated_attention_kernel<D, G, kQueryTau>), grid, dim3(kThreads), 0, stream, qb, kb, vb, ks,
-                       tau, gain, segs, hq, hkv, nullptr, (int64_t)0, qpos, lse, ob);
+    hipLaunchKernelGGL((gated_attention_dma_kernel<D, G, kQueryTau>), grid, dim3(kThreads), 0, stream, qb, kb, vb, ks,
+                       tau, gain, segs, hq, hkv, qpos, lse, ob);
   else
-    hipLaunchKernelGGL((gated_attention_kernel<D, G, kCompacted>), grid, dim3(kThreads), 0, stream, qb, kb, vb, ks,
-                       tau, gain, segs, hq, hkv, nullptr, (int64_t)0, nullptr, lse, ob);
+    hipLaunchKernelGGL((gated_attention_dma_kernel<D, G, kCompacted>), grid, dim3(kThreads), 0, stream, qb, kb, vb,
+                       ks, tau, gain, segs, hq, hkv, nullptr, lse, ob);
   return hipGetLastError();
 }
 
