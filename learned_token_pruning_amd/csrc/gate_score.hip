@@ -257,19 +257,31 @@ __global__ __launch_bounds__(kThreads) void gate_mlp_kernel(const uint16_t* __re
   }
 }
 
-constexpr int kNormThreads = 256;
-constexpr int kNormTokens = 1024;  // tokens per block
+constexpr int kNormThreads = 256;  // one token per thread
 
+// Per-prompt RMS of the document scores from the per-tile sums of squares,
+// then every token's score divided by it (0 outside the document span).  The
+// fp64 sum has a fixed order: thread i sums tiles i, i + 256, ..., then the
+// 256 partial sums are added pairwise, halving the count each step (the last
+// six steps inside one wave by lane shifts).  Each thread's score load is
+// issued before the reduction, so its latency overlaps it.
 __global__ __launch_bounds__(kNormThreads) void gate_normalize_kernel(const tg_segment* __restrict__ segs,
                                                                      int max_tiles, int rows_per_tile,
                                                                      const double* __restrict__ tile_sumsq,
                                                                      float rms_eps, float* __restrict__ scores) {
-  __shared__ double red[kNormThreads];
+  __shared__ double red128[128];
+  __shared__ double red64[64];
+  __shared__ float rho_s;
   const tg_segment seg = segs[blockIdx.y];
-  const int t0 = blockIdx.x * kNormTokens;
-  if (t0 >= seg.seg_len) return;
+  const int t0 = blockIdx.x * kNormThreads;
+  if (t0 >= seg.seg_len) return;  // uniform
   const int n_doc = seg.doc_end - seg.doc_begin;
   const int tid = threadIdx.x;
+  const int t = t0 + tid;
+  const int64_t gi = (int64_t)seg.seg_start + t;
+  const bool mine = t < seg.seg_len;
+  const bool doc = mine && t >= seg.doc_begin && t < seg.doc_end;
+  const float v = doc ? scores[gi] : 0.0f;
   float rho = 1.0f;
   const bool norm = rms_eps >= 0.0f && n_doc > 0;
   if (norm) {
@@ -277,27 +289,23 @@ __global__ __launch_bounds__(kNormThreads) void gate_normalize_kernel(const tg_s
     const double* ts = tile_sumsq + (int64_t)blockIdx.y * max_tiles;
     double s = 0.0;
     for (int i = tid; i < ntiles; i += kNormThreads) s += ts[i];
-    red[tid] = s;
+    if (tid >= 128) red128[tid - 128] = s;
     __syncthreads();
+    if (tid < 128) {
+      s += red128[tid];
+      if (tid >= 64) red64[tid - 64] = s;
+    }
+    __syncthreads();
+    if (tid < 64) {
+      s += red64[tid];
 #pragma unroll
-    for (int w = kNormThreads / 2; w > 0; w >>= 1) {
-      if (tid < w) red[tid] += red[tid + w];
-      __syncthreads();
+      for (int w = 32; w > 0; w >>= 1) s += __shfl_down(s, w);
+      if (tid == 0) rho_s = (float)sqrt(s / (double)n_doc + (double)rms_eps);
     }
-    const double ms = red[0] / (double)n_doc;
-    rho = (float)sqrt(ms + (double)rms_eps);
+    __syncthreads();
+    rho = rho_s;
   }
-  for (int i = tid; i < kNormTokens; i += kNormThreads) {
-    const int t = t0 + i;
-    if (t >= seg.seg_len) break;
-    const int64_t gi = (int64_t)seg.seg_start + t;
-    float v = 0.0f;
-    if (t >= seg.doc_begin && t < seg.doc_end) {
-      v = scores[gi];
-      if (norm) v = v / rho;
-    }
-    scores[gi] = v;
-  }
+  if (mine) scores[gi] = norm ? v / rho : v;
 }
 
 }  // namespace
@@ -363,7 +371,7 @@ hipError_t launch_gate_score(const void* x, int64_t ld_x, int d, const void* w1,
     if (e != hipSuccess) return e;
   }
   if (info.max_seg_len > 0) {
-    dim3 grid((info.max_seg_len + kNormTokens - 1) / kNormTokens, info.n_seg);
+    dim3 grid((info.max_seg_len + kNormThreads - 1) / kNormThreads, info.n_seg);
     hipLaunchKernelGGL(gate_normalize_kernel, grid, dim3(kNormThreads), 0, stream, segs, max_tiles, kRows, ts, rms_eps,
                        scores);
     return hipGetLastError();

@@ -12,7 +12,9 @@
 //
 // Scores become order-preserving 32-bit keys (score_key); the K-th largest
 // document key T is found exactly by a three-digit MSB radix select
-// (11 + 11 + 10 bits) with LDS histograms (integer atomics: exact).  Then
+// (11 + 11 + 10 bits) with LDS histograms (integer atomics: exact); when a
+// pass's chosen bin holds exactly the keys still needed, every key of that bin
+// is kept and the later passes are skipped (the same set).  Then
 // every token is classified in index order: non-document or key > T is kept,
 // key == T is kept while fewer than need = K_eff - #{key > T} ties have been
 // kept before it.  A block-wide exclusive scan gives every kept token its
@@ -32,6 +34,7 @@ struct SelSmem {
   uint32_t wave_tot[2][kWaves];
   uint32_t found_digit;
   uint32_t found_rem;
+  uint32_t found_cnt;  // keys in the found bin
 };
 
 // Inclusive scan of two counters across the workgroup; returns the exclusive
@@ -87,6 +90,7 @@ __device__ __forceinline__ void find_digit(SelSmem& sm, uint32_t bins, uint32_t 
       if (acc + c[j] >= rem) {
         sm.found_digit = bins - 1u - (tid * per + j);
         sm.found_rem = rem - acc;
+        sm.found_cnt = c[j];
         break;
       }
       acc += c[j];
@@ -172,7 +176,15 @@ __global__ __launch_bounds__(kThreads) void select_topk_kernel(const float* __re
       find_digit(sm, bins, rem);
       prefix |= sm.found_digit << shift;
       rem = sm.found_rem;
+      const bool whole_bin = sm.found_cnt == rem && prefix != 0u;
       __syncthreads();
+      if (whole_bin) {
+        // every key of the found bin is kept: the same set as the exact
+        // threshold (its smallest key) with all its ties, so stop here
+        prefix -= 1u;
+        rem = 0u;
+        break;
+      }
     }
     thresh = prefix;
     need = rem;
