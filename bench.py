@@ -268,7 +268,7 @@ def stage_rooflines(pipe, st, csrc):
     compact_gbs = pipe.compact_bytes() / (st["compact"] * 1e-6) / 1e9
     select_gbs = (4 * pipe.seg.n_tokens + 4 * pipe.m) / (st["select"] * 1e-6) / 1e9
     roofs = {
-        "attention": {"kernel": "gated_attention_kernel<128,2>", "bound": "mfma", "achieved": attn_tflops,
+        "attention": {"kernel": "gated_attention_dma_kernel<128,2>", "bound": "mfma", "achieved": attn_tflops,
                       "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": attn_tflops / MFMA_BF16_PEAK_TFLOPS,
                       "traffic": kernel_traffic(os.path.join(csrc, "gated_attention.hip"))},
         "gate": {"kernel": ("" if pipe.prepacked else "pack_w1_kernel + ") + "gate_mlp_kernel<2,4> + gate_normalize_kernel",
