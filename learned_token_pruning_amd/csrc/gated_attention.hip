@@ -18,9 +18,10 @@
 // wave of a SIMD issues MFMAs the other runs its exp2s, so the matrix cores
 // and the VALU work at the same time.  All 512 threads stage the next K tile
 // (threads 0-255, with the scores) and the V tile due next (threads 256-511):
-// for compacted rows by direct-to-LDS loads into three LDS stages (the kernel
-// at the end of this file), for gathered rows through registers, loaded during
-// one half-step and written to LDS at the end of the next.
+// by direct-to-LDS loads into three LDS stages (the kernel at the end of this
+// file), or, for gathered rows of prompts past 8192 kept rows, through
+// registers, loaded during one half-step and written to LDS at the end of the
+// next.
 //
 // MFMA mapping (v_mfma_f32_32x32x16_bf16).  Scores are computed transposed,
 // S^T = K . Q^T, so a lane owns one query column (l % 32) and 16 key rows per
@@ -57,6 +58,7 @@ namespace {
 constexpr int kBN = 64;        // keys per tile
 constexpr int kThreads = 512;  // two groups of 4 waves
 constexpr int kMaxGatherRows = 16384;  // kept rows per prompt the gathering variant supports (indices in LDS)
+constexpr int kDmaGatherRows = 8192;   // up to this many, gathering reads use direct-to-LDS staging
 constexpr float kLog2e = 1.4426950408889634f;
 
 template <int D>
@@ -300,8 +302,9 @@ __device__ __forceinline__ void merge_and_store(float* xo, int grp, int wave, in
   }
 }
 
-// Register-staged kernel, launched for gathering reads (the kept-row indices
-// take 64 KiB of LDS, which leaves no room for three direct-to-LDS stages).
+// Register-staged kernel, launched for gathering reads of prompts with more
+// than 8192 kept rows (their indices take up to 64 KiB of LDS, which leaves no
+// room for three direct-to-LDS stages).
 // kGather: q, k, v and key_score hold every token (n_src rows); kept row r of
 // a prompt is read from source row kept_idx[kept_start + r] (gather on load,
 // no compacted copies).  The output is always compacted.
@@ -501,7 +504,10 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
 }
 
 // ---------------------------------------------------------------------------
-// Direct-to-LDS staging (compacted rows, per-head or per-query temperature).
+// Direct-to-LDS staging (compacted rows with a per-head or per-query
+// temperature, and gathered rows for prompts of up to 8192 kept rows, whose
+// source-row indices are kept in LDS: each DMA lane then reads its 16 bytes
+// from the kept row's source row).
 //
 // The same schedule, but K, V and the key scores go from global memory straight
 // into LDS (buffer loads with the LDS destination), so no staging registers and
@@ -585,21 +591,26 @@ template <int D, int G, int MODE>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void gated_attention_dma_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
     const float* __restrict__ key_score, const float* __restrict__ tau, const float* __restrict__ gain,
-    const tg_segment* __restrict__ segs, int hq, int hkv, const int32_t* __restrict__ qpos, float* __restrict__ lse,
-    uint16_t* __restrict__ out) {
-  static_assert(MODE != kGather, "gathering reads keep register staging");
+    const tg_segment* __restrict__ segs, int hq, int hkv, const int32_t* __restrict__ kept_idx, int64_t n_src,
+    const int32_t* __restrict__ qpos, float* __restrict__ lse, uint16_t* __restrict__ out) {
+  constexpr bool GATHER = MODE == kGather;
   constexpr bool QTAU = MODE == kQueryTau;
   constexpr int kBM = 128 / G;
   constexpr int kWavesPerHead = 4 / G;
   constexpr int NC = D / 8;   // 16-byte chunks per row
   constexpr int NJ = NC / 4;  // DMA instructions per staging wave per tile (64 NC chunks over 4 waves)
   __shared__ DmaSmem<D> sm;
+  __shared__ int32_t sidx[GATHER ? kDmaGatherRows : 1];  // source rows of the kept rows [0, q_end)
 
   const tg_segment seg = segs[blockIdx.z];
   const int n = seg.kept_len;
   const int q0 = (gridDim.y - 1 - blockIdx.y) * kBM;
   if (q0 >= n) return;  // uniform
   const int q_end = min(q0 + kBM, n);
+  if (GATHER) {
+    for (int i = threadIdx.x; i < q_end; i += kThreads) sidx[i] = kept_idx[seg.kept_start + i];
+    __syncthreads();
+  }
 
   const int tid = threadIdx.x;
   const int grp = tid >> 8;
@@ -616,8 +627,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
 
   const int64_t q_stride = (int64_t)hq * D;
   const int64_t kv_stride = (int64_t)hkv * D;
-  const int64_t row0 = seg.kept_start;
-  const uint32_t nrows = (uint32_t)n;
+  const int64_t row0 = GATHER ? 0 : seg.kept_start;               // first row of the K/V/score buffers
+  const uint32_t nrows = GATHER ? (uint32_t)n_src : (uint32_t)n;  // rows the buffers cover
   const uint16_t* kb = k + row0 * kv_stride + (int64_t)c * D;
   const uint16_t* vb = v + row0 * kv_stride + (int64_t)c * D;
   const bool use_bias = key_score != nullptr && gain != nullptr;
@@ -627,25 +638,53 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
   const __amdgpu_buffer_rsrc_t rs = make_rsrc(use_bias ? key_score + row0 : key_score, use_bias ? nrows * 4u : 0u);
   const bool stage_k = grp == 0;  // threads 0-255 stage K and the scores, 256-511 V
 
-  // DMA source offsets inside a tile: chunk slot (j 4 + wave) 64 + lane
-  uint32_t doff[NJ];
+  // DMA source offsets inside a tile: chunk slot (j 4 + wave) 64 + lane holds row drow[j], chunk dcol[j]
+  int drow[NJ];
+  uint32_t dcol[NJ];
 #pragma unroll
   for (int j = 0; j < NJ; ++j) {
     const int p = (j * 4 + wave) * 64 + lane;
     const int r = p / NC;
-    const int cc = (p % NC) ^ (stage_k ? kswz<D>(r) : vswz<D>(r));
-    doff[j] = (uint32_t)r * row_bytes + (uint32_t)cc * 16u;
+    drow[j] = r;
+    dcol[j] = (uint32_t)((p % NC) ^ (stage_k ? kswz<D>(r) : vswz<D>(r))) * 16u;
   }
+  // byte offset of a tile row in the K/V buffers (gathered: its source row; rows at or past q_end read as zeros)
+  auto row_off = [&](int row) -> uint32_t {
+    if (!GATHER) return (uint32_t)row * row_bytes;
+    return row < q_end ? (uint32_t)sidx[row] * row_bytes : kPastRange;
+  };
   auto dma_k = [&](int tile, int buf) {
-    const uint32_t soff = (uint32_t)(tile * kBN) * row_bytes;
+    if (!GATHER) {
+      const uint32_t soff = (uint32_t)(tile * kBN) * row_bytes;
 #pragma unroll
-    for (int j = 0; j < NJ; ++j) dma16(rk, &sm.k[buf][(j * 4 + wave) * 64 * 8], doff[j], soff);
-    if (lane < 16) dma4(rs, &sm.s[buf][16 * wave], (uint32_t)(16 * wave + lane) * 4u, (uint32_t)(tile * kBN) * 4u);
+      for (int j = 0; j < NJ; ++j)
+        dma16(rk, &sm.k[buf][(j * 4 + wave) * 64 * 8], (uint32_t)drow[j] * row_bytes + dcol[j], soff);
+      if (lane < 16) dma4(rs, &sm.s[buf][16 * wave], (uint32_t)(16 * wave + lane) * 4u, (uint32_t)(tile * kBN) * 4u);
+    } else {
+#pragma unroll
+      for (int j = 0; j < NJ; ++j) {
+        const uint32_t ro = row_off(tile * kBN + drow[j]);
+        dma16(rk, &sm.k[buf][(j * 4 + wave) * 64 * 8], ro == kPastRange ? ro : ro + dcol[j], 0u);
+      }
+      if (lane < 16) {
+        const int row = tile * kBN + 16 * wave + lane;
+        dma4(rs, &sm.s[buf][16 * wave], row < q_end ? (uint32_t)sidx[row] * 4u : kPastRange, 0u);
+      }
+    }
   };
   auto dma_v = [&](int tile, int buf) {
-    const uint32_t soff = (uint32_t)(tile * kBN) * row_bytes;
+    if (!GATHER) {
+      const uint32_t soff = (uint32_t)(tile * kBN) * row_bytes;
 #pragma unroll
-    for (int j = 0; j < NJ; ++j) dma16(rv, &sm.v[buf][(j * 4 + wave) * 64 * 8], doff[j], soff);
+      for (int j = 0; j < NJ; ++j)
+        dma16(rv, &sm.v[buf][(j * 4 + wave) * 64 * 8], (uint32_t)drow[j] * row_bytes + dcol[j], soff);
+    } else {
+#pragma unroll
+      for (int j = 0; j < NJ; ++j) {
+        const uint32_t ro = row_off(tile * kBN + drow[j]);
+        dma16(rv, &sm.v[buf][(j * 4 + wave) * 64 * 8], ro == kPastRange ? ro : ro + dcol[j], 0u);
+      }
+    }
   };
 
   const float base = kLog2e / __builtin_sqrtf((float)D);
@@ -668,8 +707,12 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
   u32x4 qf[D / 16];
   {
     const int r = qrow < n ? qrow : n - 1;
-    const u32x4* src =
-        reinterpret_cast<const u32x4*>(q + ((int64_t)seg.kept_start + r) * q_stride + (int64_t)h * D + 8 * g);
+    int64_t qsrc = (int64_t)seg.kept_start + r;
+    if (GATHER) {
+      qsrc = sidx[r];
+      if (qsrc < 0 || qsrc >= n_src) qsrc = 0;  // a bad index never reads outside q
+    }
+    const u32x4* src = reinterpret_cast<const u32x4*>(q + qsrc * q_stride + (int64_t)h * D + 8 * g);
 #pragma unroll
     for (int ks = 0; ks < D / 16; ++ks) qf[ks] = src[2 * ks];
   }
@@ -810,15 +853,18 @@ hipError_t launch_dg(const void* q, const void* k, const void* v, const float* k
   auto* kb = reinterpret_cast<const uint16_t*>(k);
   auto* vb = reinterpret_cast<const uint16_t*>(v);
   auto* ob = reinterpret_cast<uint16_t*>(out);
-  if (kept_idx != nullptr)
+  if (kept_idx != nullptr && info.max_kept_len <= kDmaGatherRows)
+    hipLaunchKernelGGL((gated_attention_dma_kernel<D, G, kGather>), grid, dim3(kThreads), 0, stream, qb, kb, vb, ks,
+                       tau, gain, segs, hq, hkv, kept_idx, n_src, nullptr, lse, ob);
+  else if (kept_idx != nullptr)
     hipLaunchKernelGGL((gated_attention_kernel<D, G, kGather>), grid, dim3(kThreads), 0, stream, qb, kb, vb, ks, tau,
                        gain, segs, hq, hkv, kept_idx, n_src, nullptr, lse, ob);
   else if (qpos != nullptr)
     hipLaunchKernelGGL((gated_attention_dma_kernel<D, G, kQueryTau>), grid, dim3(kThreads), 0, stream, qb, kb, vb, ks,
-                       tau, gain, segs, hq, hkv, qpos, lse, ob);
+                       tau, gain, segs, hq, hkv, nullptr, (int64_t)0, qpos, lse, ob);
   else
     hipLaunchKernelGGL((gated_attention_dma_kernel<D, G, kCompacted>), grid, dim3(kThreads), 0, stream, qb, kb, vb,
-                       ks, tau, gain, segs, hq, hkv, nullptr, lse, ob);
+                       ks, tau, gain, segs, hq, hkv, nullptr, (int64_t)0, nullptr, lse, ob);
   return hipGetLastError();
 }
 
