@@ -119,6 +119,25 @@ def test_gate_ragged_segments(h, d):
     check_scores(got_raw, oracle_gate(L, eps=-1.0, b1=b1, b2=0.3), doc_mask_of(seg))
 
 
+def test_gate_ragged_128_row_tiles():
+    """A packed batch large enough for the 128-row gate tiles (at least two
+    rounds of them on a 256-CU device): ragged document spans, partial last
+    tiles, an empty document."""
+    _say("gate ragged, 128-row tiles")
+    rng = np.random.default_rng(77)
+    lens = [17000, 16500, 9000, 30000, 600]
+    starts = [0]
+    for n in lens:
+        starts.append(starts[-1] + n)
+    db = [3, 0, 100, 0, 50]
+    de = [16990, 16500, 8977, 29937, 50]  # the last prompt has an empty document
+    seg = W.Segments(starts, db, de, [10, 20, 30, 40, 0])
+    L = W.make_gated_layer(78, seg, 256, 128, 2, 1, 64, with_qkv=False)
+    b1 = rng.standard_normal(128).astype(np.float32) * 0.1
+    got = run_gate(L, b1=b1, b2=0.1)
+    check_scores(got, oracle_gate(L, b1=b1, b2=0.1), doc_mask_of(seg))
+
+
 @pytest.mark.parametrize("idx", [1, 2])
 def test_gate_prepacked_equals_gate(idx):
     """W1 packed once (tg_gate_pack_w1) gives tg_gate_score's scores bit for bit."""
