@@ -237,7 +237,9 @@ __global__ __launch_bounds__(kThreads) void select_topk_kernel(const float* __re
 // global one with integer atomics (exact, so the result does not depend on
 // the order); the next pass's workgroups all re-derive the chosen digit from
 // it with the same integer scan, so they agree without exchanging anything.
-// After three passes a count kernel records, per slice, how many tokens are
+// A pass whose chosen bin holds exactly the keys still needed ends the search
+// early, as in the one-workgroup kernel (the later histogram launches exit at
+// once).  After the passes a count kernel records, per slice, how many tokens are
 // kept for sure and how many tie the threshold; the emission kernel turns
 // the counts of the earlier slices into its output offset and the tie quota
 // left for it, then writes its kept indices in index order.
@@ -250,7 +252,7 @@ constexpr int kMPer = kSlice / kMT;  // tokens per thread
 struct MultiSmem {
   uint32_t hist[kBins];
   uint32_t wtot[2][4];
-  uint32_t digit, rem;
+  uint32_t digit, rem, cnt;
 };
 
 // exclusive prefixes of two counters over the 256 threads; block totals out
@@ -282,9 +284,9 @@ __device__ __forceinline__ void scan256(uint32_t a, uint32_t b, uint32_t& ea, ui
 }
 
 // Digit (counted from the top) of the global histogram h that holds the
-// rem-th largest key, and the rank left inside it.
+// rem-th largest key, the rank left inside it, and the bin's key count.
 __device__ void multi_find(const uint32_t* __restrict__ h, uint32_t bins, uint32_t& rem, uint32_t& digit,
-                           MultiSmem& sm) {
+                           uint32_t& count, MultiSmem& sm) {
   const int tid = threadIdx.x;
   const uint32_t per = bins / kMT;  // 8 or 4 bins per thread, highest first
   uint32_t c[8];
@@ -301,6 +303,7 @@ __device__ void multi_find(const uint32_t* __restrict__ h, uint32_t bins, uint32
       if (acc + c[j] >= rem) {
         sm.digit = bins - 1u - (tid * per + j);
         sm.rem = rem - acc;
+        sm.cnt = c[j];
         break;
       }
       acc += c[j];
@@ -309,6 +312,7 @@ __device__ void multi_find(const uint32_t* __restrict__ h, uint32_t bins, uint32
   __syncthreads();
   digit = sm.digit;
   rem = sm.rem;
+  count = sm.cnt;
   __syncthreads();
 }
 
@@ -337,10 +341,11 @@ __global__ __launch_bounds__(kMT) void select_hist_kernel(const float* __restric
   uint32_t prefix = 0u, rem = (uint32_t)seg.k_eff;
   for (int p = 0; p < PASS; ++p) {
     int shift;
-    uint32_t bins, mask, digit;
+    uint32_t bins, mask, digit, count;
     pass_shape(p, shift, bins, mask);
-    multi_find(hs + (int64_t)p * n_seg * kBins, bins, rem, digit, sm);
+    multi_find(hs + (int64_t)p * n_seg * kBins, bins, rem, digit, count, sm);
     prefix |= digit << shift;
+    if (count == rem && prefix != 0u) return;  // that bin is kept whole: no later pass needed (uniform)
   }
   int shift;
   uint32_t bins, mask;
@@ -379,10 +384,16 @@ __device__ void multi_threshold(const tg_segment& seg, int n_seg, const uint32_t
     uint32_t prefix = 0u, rem = (uint32_t)seg.k_eff;
     for (int p = 0; p < 3; ++p) {
       int shift;
-      uint32_t bins, mask, digit;
+      uint32_t bins, mask, digit, count;
       pass_shape(p, shift, bins, mask);
-      multi_find(hs + (int64_t)p * n_seg * kBins, bins, rem, digit, sm);
+      multi_find(hs + (int64_t)p * n_seg * kBins, bins, rem, digit, count, sm);
       prefix |= digit << shift;
+      if (count == rem && prefix != 0u) {
+        // the found bin is kept whole: the same set as the exact threshold with all its ties
+        prefix -= 1u;
+        rem = 0u;
+        break;
+      }
     }
     thresh = prefix;
     need = rem;
