@@ -133,21 +133,6 @@ __device__ __forceinline__ uint32_t score_key(float f) {
 
 }  // namespace tg
 
-// Compute units of the current device (queried once per device; 256 if the
-// query fails).  Launch shapes that depend on how many rounds of workgroups
-// the device runs use it.
-inline int device_cu_count() {
-  static int cache[64] = {};
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
-  if (cache[dev] == 0) {
-    int n = 0;
-    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
-    cache[dev] = n;
-  }
-  return cache[dev];
-}
-
 // Launchers (one per kernel family), defined in the kernel sources.  They
 // only launch; arguments are validated by the ABI layer.
 namespace tg {

@@ -328,24 +328,12 @@ static void launch_mlp(dim3 grid, hipStream_t stream, const uint16_t* xp, int64_
                      h, segs, max_tiles, scores, ts);
 }
 
-// Document rows per gate workgroup: 128 (each W1 fragment feeds twice the
-// MFMAs, halving the W1 re-reads from L2, but one wave per SIMD) when the
-// prompts hold at least two rounds of such tiles for the device and d allows
-// 256-column X stages; else 64.  Measured per gate call: 179 vs 209 us at
-// 128K tokens, 91 vs 93 at 64K; at 16K-49K the 64-row tiles win.
-static int gate_tile_rows(const tg_plan_info& info, int d) {
-  const int64_t t128 = (int64_t)info.n_seg * ((info.max_doc_len + 127) / 128);
-  return (d % 256 == 0 && t128 >= 2 * (int64_t)device_cu_count()) ? 128 : kRows;
-}
-
 template <int NCT>
 static void launch_mlp_d(dim3 grid, hipStream_t stream, const uint16_t* xp, int64_t ld_x, int d, const u32x4* wp,
                          const float* b1, const float* w2, float b2, int h, const tg_segment* segs, int max_tiles,
-                         float* scores, double* ts, int rows) {
+                         float* scores, double* ts) {
   // X stage of 256 columns (512-byte row bursts) when d allows; measured best among 128-1024-byte bursts
-  if (rows == 128)
-    launch_mlp<NCT, 4, 4, 4>(grid, stream, xp, ld_x, d, wp, b1, w2, b2, h, segs, max_tiles, scores, ts);
-  else if (d % 256 == 0)
+  if (d % 256 == 0)
     launch_mlp<NCT, 2, 4, 4>(grid, stream, xp, ld_x, d, wp, b1, w2, b2, h, segs, max_tiles, scores, ts);
   else if (d % 128 == 0)
     launch_mlp<NCT, 2, 2, 2>(grid, stream, xp, ld_x, d, wp, b1, w2, b2, h, segs, max_tiles, scores, ts);
@@ -364,7 +352,6 @@ hipError_t launch_gate_score(const void* x, int64_t ld_x, int d, const void* w1,
                              float rms_eps, float* scores, void* workspace, hipStream_t stream) {
   int max_tiles = (info.max_doc_len + kRows - 1) / kRows;  // at the smallest tile height: an upper bound
   if (max_tiles < 1) max_tiles = 1;
-  const int rows = gate_tile_rows(info, d);
   double* ts = reinterpret_cast<double*>(workspace);
   const u32x4* w1p = w1_prepacked
                          ? reinterpret_cast<const u32x4*>(w1)
@@ -374,18 +361,18 @@ hipError_t launch_gate_score(const void* x, int64_t ld_x, int d, const void* w1,
       const hipError_t e = launch_gate_pack_w1(w1, d, h, const_cast<u32x4*>(w1p), stream);
       if (e != hipSuccess) return e;
     }
-    dim3 grid((unsigned)((info.max_doc_len + rows - 1) / rows), info.n_seg);
+    dim3 grid(max_tiles, info.n_seg);
     const uint16_t* xp = reinterpret_cast<const uint16_t*>(x);
     if (h <= 128)
-      launch_mlp_d<1>(grid, stream, xp, ld_x, d, w1p, b1, w2, b2, h, segs, max_tiles, scores, ts, rows);
+      launch_mlp_d<1>(grid, stream, xp, ld_x, d, w1p, b1, w2, b2, h, segs, max_tiles, scores, ts);
     else
-      launch_mlp_d<2>(grid, stream, xp, ld_x, d, w1p, b1, w2, b2, h, segs, max_tiles, scores, ts, rows);
+      launch_mlp_d<2>(grid, stream, xp, ld_x, d, w1p, b1, w2, b2, h, segs, max_tiles, scores, ts);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
   if (info.max_seg_len > 0) {
     dim3 grid((info.max_seg_len + kNormThreads - 1) / kNormThreads, info.n_seg);
-    hipLaunchKernelGGL(gate_normalize_kernel, grid, dim3(kNormThreads), 0, stream, segs, max_tiles, rows, ts, rms_eps,
+    hipLaunchKernelGGL(gate_normalize_kernel, grid, dim3(kNormThreads), 0, stream, segs, max_tiles, kRows, ts, rms_eps,
                        scores);
     return hipGetLastError();
   }

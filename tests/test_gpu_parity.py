@@ -119,11 +119,10 @@ def test_gate_ragged_segments(h, d):
     check_scores(got_raw, oracle_gate(L, eps=-1.0, b1=b1, b2=0.3), doc_mask_of(seg))
 
 
-def test_gate_ragged_128_row_tiles():
-    """A packed batch large enough for the 128-row gate tiles (at least two
-    rounds of them on a 256-CU device): ragged document spans, partial last
-    tiles, an empty document."""
-    _say("gate ragged, 128-row tiles")
+def test_gate_ragged_large_batch():
+    """A packed batch of five prompts (73K tokens): ragged document spans,
+    partial last tiles, an empty document."""
+    _say("gate ragged, large batch")
     rng = np.random.default_rng(77)
     lens = [17000, 16500, 9000, 30000, 600]
     starts = [0]
