@@ -177,23 +177,6 @@ __device__ __forceinline__ void store_v(const Stager<D>& st, AttnSmem<D>& sm, in
   }
 }
 
-// Instruction order for a block of MFMAS matrix ops fed by READS LDS reads:
-// AHEAD reads first, then alternating MFMA / read, then the remaining MFMAs.
-// Left alone, the compiler waits for each read right before its MFMA.
-template <int MFMAS, int READS, int AHEAD>
-__device__ __forceinline__ void sched_reads_ahead() {
-  static_assert(READS >= AHEAD && MFMAS >= READS - AHEAD, "pattern");
-#pragma unroll
-  for (int i = 0; i < AHEAD; ++i) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // DS read
-#pragma unroll
-  for (int i = 0; i < READS - AHEAD; ++i) {
-    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
-    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-  }
-#pragma unroll
-  for (int i = 0; i < MFMAS - (READS - AHEAD); ++i) __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-}
-
 // Softmax phase of one 64-key tile starting at key kv0: causal mask on the
 // diagonal tiles, running max with the lazy rescale, exp2 of the logits, row
 // sums over the bf16-rounded probabilities, and the P^T operands of the 4 PV
@@ -545,46 +528,6 @@ __device__ __forceinline__ int kswz(int r) {
 template <int D>
 __device__ __forceinline__ int vswz(int r) {
   return D == 128 ? 4 * (r & 3) : 4 * ((r >> 1) & 1);
-}
-
-#define TG_LDS(p) ((__attribute__((address_space(3))) void*)(p))
-
-// One DMA instruction: every active lane copies 16 (or 4) bytes from the buffer
-// at voff + soff into LDS at lds_dst + 16 (or 4) x lane.  Issued in asm so the
-// compiler does not order later LDS reads after it; every consumer waits with
-// an explicit vmcnt (the instruction has no destination registers).
-__device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, const void* lds_dst, uint32_t voff, uint32_t soff) {
-  const uint32_t m0v = (uint32_t)(uintptr_t)TG_LDS(lds_dst);
-  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds" ::"s"(m0v), "v"(voff), "s"(r), "s"(soff)
-               : "memory");
-}
-__device__ __forceinline__ void dma4(__amdgpu_buffer_rsrc_t r, const void* lds_dst, uint32_t voff, uint32_t soff) {
-  const uint32_t m0v = (uint32_t)(uintptr_t)TG_LDS(lds_dst);
-  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dword %1, %2, %3 offen lds" ::"s"(m0v), "v"(voff), "s"(r), "s"(soff)
-               : "memory");
-}
-
-template <int N>
-__device__ __forceinline__ void wait_vm() {
-  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
-}
-__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
-
-// Instruction order for MFMAS matrix ops fed by two LDS reads each: AHEAD
-// reads first, then MFMA / read / read, then the remaining MFMAs.
-template <int MFMAS, int AHEAD>
-__device__ __forceinline__ void sched_two_reads_ahead() {
-  constexpr int READS = 2 * MFMAS;
-  constexpr int PAIRS = (READS - AHEAD) / 2;
-#pragma unroll
-  for (int i = 0; i < AHEAD; ++i) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-#pragma unroll
-  for (int i = 0; i < PAIRS; ++i) {
-    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-    __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
-  }
-#pragma unroll
-  for (int i = 0; i < MFMAS - PAIRS; ++i) __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
 }
 
 template <int D, int G, int MODE>

@@ -28,6 +28,8 @@
 //               dtau partials in a fixed order (deterministic results).
 // bf16 MFMA operands (P and the scaled dZ are rounded to bf16 for the
 // products), fp32 accumulation and fp32 gradient outputs.
+#include <type_traits>
+
 #include "common.h"
 
 namespace tg {
@@ -508,6 +510,284 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_dq_kernel(
   }
 }
 
+// dQ with direct-to-LDS staging and the forward's ping-pong schedule (D = 128).
+// A workgroup owns one KV head and a 128/G-row query tile of its G heads; its
+// 8 waves form two groups of 4 (one wave of each per SIMD), group 0 taking the
+// even 64-key tiles and group 1 the odd ones.  In its MFMA phase a wave runs
+// dQ^T += K^T dZ^T for its previous tile and S^T = K Q^T, dP^T = V dO^T for its
+// next one; in its other phase it turns S^T and dP^T into dZ^T (P from the
+// saved log-sum-exp, so no running maximum).  K and V come in by DMA: a K tile
+// is read twice (for S at its own half-step, for dQ two half-steps later), so K
+// has five LDS stages and V three.  K^T is read from the row-major K tile with
+// transposing LDS reads; K and V chunks are swizzled so that both read patterns
+// are conflict free (chunk c of row r at c ^ (((r & 3) << 2) | ((r >> 2) & 3)):
+// the 16 rows of a row-read cycle hit 16 distinct chunks, the 4 rows of a
+// transposing read 4 distinct 64-byte groups).  The two groups' dQ^T are added
+// through LDS at the end.
+constexpr int kDqThreads = 512;
+constexpr int kDqK = 5;  // K stages
+constexpr int kDqV = 3;  // V stages
+
+struct alignas(16) DqSmem {
+  uint16_t k[kDqK][kTile * 128];
+  uint16_t v[kDqV][kTile * 128];
+  float s[kDqK][kTile];  // key scores, with their K tile
+};
+
+__device__ __forceinline__ int dq_swz(int r) { return ((r & 3) << 2) | ((r >> 2) & 3); }
+
+template <int G>
+__global__ __launch_bounds__(kDqThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void bwd_dq_dma_kernel(
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
+    const float* __restrict__ key_score, const float* __restrict__ tau, const float* __restrict__ gain,
+    const tg_segment* __restrict__ segs, int hq, int hkv, const uint16_t* __restrict__ dout,
+    const float* __restrict__ lse, const float* __restrict__ dt, float* __restrict__ dq) {
+  constexpr int D = 128;
+  constexpr int kBM = 128 / G;
+  constexpr int kWavesPerHead = 4 / G;
+  constexpr int NC = D / 8;   // 16-byte chunks per row
+  constexpr int NJ = NC / 4;  // DMA instructions per staging wave per tile
+  __shared__ DqSmem sm;
+
+  const tg_segment seg = segs[blockIdx.z];
+  const int n = seg.kept_len;
+  const int q0 = (gridDim.y - 1 - blockIdx.y) * kBM;
+  if (q0 >= n) return;  // uniform
+  const int q_end = min(q0 + kBM, n);
+  const int tid = threadIdx.x;
+  const int grp = tid >> 8;
+  const int gtid = tid & 255;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(gtid >> 6);
+  const int g = lane >> 5, l32 = lane & 31;
+  const int c = blockIdx.x;
+  const int hl = wave / kWavesPerHead, h = c * G + hl;
+  const int qw0 = q0 + (wave % kWavesPerHead) * 32;
+  const int qrow = qw0 + l32;
+  const bool row_ok = qrow < n;
+  const int64_t base = seg.kept_start;
+  const int64_t q_stride = (int64_t)hq * D, kv_stride = (int64_t)hkv * D;
+  const uint32_t row_bytes = (uint32_t)kv_stride * 2u;
+  const uint32_t nrows = (uint32_t)n;
+  const bool use_bias = key_score != nullptr && gain != nullptr;
+  const __amdgpu_buffer_rsrc_t rk = make_rsrc(k + base * kv_stride + (int64_t)c * D, nrows * row_bytes - (uint32_t)c * D * 2u);
+  const __amdgpu_buffer_rsrc_t rv = make_rsrc(v + base * kv_stride + (int64_t)c * D, nrows * row_bytes - (uint32_t)c * D * 2u);
+  const __amdgpu_buffer_rsrc_t rs = make_rsrc(use_bias ? key_score + base : key_score, use_bias ? nrows * 4u : 0u);
+  const bool stage_k = grp == 0;  // threads 0-255 stage K and the scores, 256-511 V
+
+  // DMA source offsets inside a tile: chunk slot (j 4 + wave) 64 + lane
+  uint32_t doff[NJ];
+#pragma unroll
+  for (int j = 0; j < NJ; ++j) {
+    const int p = (j * 4 + wave) * 64 + lane;
+    const int r = p / NC;
+    doff[j] = (uint32_t)r * row_bytes + (uint32_t)((p % NC) ^ dq_swz(r)) * 16u;
+  }
+  auto dma_k = [&](int tile, int buf) {
+    const uint32_t soff = (uint32_t)(tile * kTile) * row_bytes;
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) dma16(rk, &sm.k[buf][(j * 4 + wave) * 64 * 8], doff[j], soff);
+    if (lane < 16) dma4(rs, &sm.s[buf][16 * wave], (uint32_t)(16 * wave + lane) * 4u, (uint32_t)(tile * kTile) * 4u);
+  };
+  auto dma_v = [&](int tile, int buf) {
+    const uint32_t soff = (uint32_t)(tile * kTile) * row_bytes;
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) dma16(rv, &sm.v[buf][(j * 4 + wave) * 64 * 8], doff[j], soff);
+  };
+
+  const float th = tau != nullptr ? tau[h] : 1.0f;
+  const float inv_sqrt_d = 1.0f / __builtin_sqrtf((float)D);
+  const float scale2 = th * kL2e * inv_sqrt_d, dscale = th * inv_sqrt_d;
+  const float gb2 = use_bias ? gain[h] * kL2e : 0.0f;
+  const float lse_row = row_ok ? lse[(base + qrow) * hq + h] * kL2e : __builtin_inff();
+  const float dt_row = row_ok ? dt[(base + qrow) * hq + h] : 0.0f;
+  const int ntiles = (q_end + kTile - 1) / kTile;
+  const int wlast = qw0 + 31;
+
+  if (stage_k) {
+    dma_k(0, 0);
+    if (ntiles > 1) dma_k(1, 1);
+  } else {
+    dma_v(0, 0);
+    if (ntiles > 1) dma_v(1, 1);
+  }
+  // Q^T and dO^T operands: lane holds row qrow, dims 16 ks + 8 g .. + 7
+  u32x4 qf[D / 16], of[D / 16];
+#pragma unroll
+  for (int ks = 0; ks < D / 16; ++ks) {
+    const int64_t off = (base + qrow) * q_stride + (int64_t)h * D + 16 * ks + 8 * g;
+    qf[ks] = row_ok ? *reinterpret_cast<const u32x4*>(q + off) : u32x4{0, 0, 0, 0};
+    of[ks] = row_ok ? *reinterpret_cast<const u32x4*>(dout + off) : u32x4{0, 0, 0, 0};
+  }
+#pragma unroll
+  for (int ks = 0; ks < D / 16; ++ks) {
+    asm volatile("" : "+v"(qf[ks]));  // keep them resident, never re-read
+    asm volatile("" : "+v"(of[ks]));
+  }
+
+  // LDS element offsets of this lane's fragment reads inside a tile.
+  // K and V rows (A operands of S^T and dP^T): row l32 (+32 for the second half), chunk 2 ks + g.
+  uint32_t raddr[D / 16];
+#pragma unroll
+  for (int ks = 0; ks < D / 16; ++ks) raddr[ks] = (uint32_t)(l32 * D + (((2 * ks + g) ^ dq_swz(l32)) * 8));
+  // K^T (A operand of dQ^T, transposing read): 16-lane group qg covers dims 32 dt + 16 (qg % 2) + 0..15 and
+  // keys 4 g + 0..3 (+8 for the upper half of a 16-key step); source lane s points at row 4 g + s / 4 (+8).
+  uint32_t taddr[2][D / 32];
+  {
+    const int s = lane & 15, qg = lane >> 4;
+#pragma unroll
+    for (int hi = 0; hi < 2; ++hi) {
+      const int r = 8 * hi + 4 * g + (s >> 2);
+#pragma unroll
+      for (int dtile = 0; dtile < D / 32; ++dtile) {
+        const int cc = 4 * dtile + 2 * (qg & 1) + ((s & 3) >> 1);
+        taddr[hi][dtile] = (uint32_t)(r * D + ((cc ^ dq_swz(r)) * 8) + 4 * (s & 1));
+      }
+    }
+  }
+
+  f32x16 dqt[D / 32];
+#pragma unroll
+  for (int dtile = 0; dtile < D / 32; ++dtile) dqt[dtile] = f32x16{};
+  f32x16 sa[2], dpa[2];
+  u32x4 zb[4];  // scaled dZ^T, B operands of the 4 16-key steps of the dQ product
+
+  if (stage_k) {
+    if (ntiles > 1)
+      wait_vm<NJ + 1>();
+    else
+      wait_vm<0>();
+  } else {
+    if (ntiles > 1)
+      wait_vm<NJ>();
+    else
+      wait_vm<0>();
+  }
+  lds_barrier();
+
+  int kc = 0, vc = 0;  // hs % kDqK, hs % kDqV
+  auto half_step = [&](int hs, auto p_) {
+    constexpr int P = decltype(p_)::value;
+    const int k_m2 = kc >= 2 ? kc - 2 : kc + kDqK - 2;  // stage of K tile hs - 2
+    const int k_m1 = kc >= 1 ? kc - 1 : kc + kDqK - 1;  // stage of K tile hs - 1
+    const int k_p2 = kc + 2 < kDqK ? kc + 2 : kc + 2 - kDqK;
+    const int v_p2 = vc + 2 < kDqV ? vc + 2 : vc + 2 - kDqV;
+    const bool dma_now = hs + 2 < ntiles;
+    if (dma_now && !stage_k) dma_v(hs + 2, v_p2);  // V tile hs + 2 at the start
+
+    if (P == grp) {
+      const int jp = hs - 2;
+      if (jp >= 0 && jp * kTile <= wlast) {
+        const uint16_t* kt = sm.k[k_m2];
+#pragma unroll
+        for (int s4 = 0; s4 < 4; ++s4) {
+#pragma unroll
+          for (int dtile = 0; dtile < D / 32; ++dtile) {
+            typedef short short4v __attribute__((ext_vector_type(4)));
+            const short4v lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                (__attribute__((address_space(3))) short4v*)(kt + taddr[0][dtile] + 16 * s4 * D));
+            const short4v hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                (__attribute__((address_space(3))) short4v*)(kt + taddr[1][dtile] + 16 * s4 * D));
+            const u32x2 l2 = __builtin_bit_cast(u32x2, lo), h2 = __builtin_bit_cast(u32x2, hi);
+            dqt[dtile] = mfma32(u32x4{l2[0], l2[1], h2[0], h2[1]}, zb[s4], dqt[dtile]);
+          }
+        }
+        sched_two_reads_ahead<4 * (D / 32), 8>();
+      }
+      if (hs < ntiles && hs * kTile <= wlast) {
+        const uint16_t* kt = sm.k[kc];
+        const uint16_t* vt = sm.v[vc];
+        sa[0] = sa[1] = dpa[0] = dpa[1] = f32x16{};
+#pragma unroll
+        for (int ks = 0; ks < D / 16; ++ks) {
+          const u32x4 a0 = *reinterpret_cast<const u32x4*>(kt + raddr[ks]);
+          const u32x4 a1 = *reinterpret_cast<const u32x4*>(kt + raddr[ks] + 32 * D);
+          const u32x4 b0 = *reinterpret_cast<const u32x4*>(vt + raddr[ks]);
+          const u32x4 b1 = *reinterpret_cast<const u32x4*>(vt + raddr[ks] + 32 * D);
+          sa[0] = mfma32(a0, qf[ks], sa[0]);
+          sa[1] = mfma32(a1, qf[ks], sa[1]);
+          dpa[0] = mfma32(b0, of[ks], dpa[0]);
+          dpa[1] = mfma32(b1, of[ks], dpa[1]);
+        }
+        sched_reads_ahead<4 * (D / 16), 4 * (D / 16), 16>();
+      }
+    } else {
+      // dZ^T of tile hs - 1 from this wave's S^T and dP^T
+      const int js = hs - 1;
+      if (js >= 0 && js < ntiles && js * kTile <= wlast) {
+        const int kv0 = js * kTile;
+        const float* scs = sm.s[k_m1];
+#pragma unroll
+        for (int hf = 0; hf < 2; ++hf) {
+          float z[16];
+#pragma unroll
+          for (int q4 = 0; q4 < 4; ++q4) {
+            const f32x4 s4v = *reinterpret_cast<const f32x4*>(&scs[hf * 32 + 8 * q4 + 4 * g]);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              const int i = 4 * q4 + e;
+              const int key = kv0 + hf * 32 + c_row(i, g);
+              const bool ok = row_ok && key <= qrow && key < n;
+              const float p =
+                  ok ? __builtin_amdgcn_exp2f(__builtin_fmaf(scale2, sa[hf][i], gb2 * s4v[e]) - lse_row) : 0.0f;
+              z[i] = p * (dpa[hf][i] - dt_row) * dscale;
+            }
+          }
+#pragma unroll
+          for (int st = 0; st < 2; ++st)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) zb[2 * hf + st][j] = pack2(z[8 * st + 2 * j], z[8 * st + 2 * j + 1]);
+        }
+      }
+    }
+
+    if (dma_now && stage_k) {
+      // K tile hs + 2 at the end; its stage last held tile hs - 3, whose last read (dQ) was at hs - 1
+      dma_k(hs + 2, k_p2);
+    }
+    // K and V tiles hs + 1 (issued one half-step ago) must have landed; this half-step's DMAs may stay in flight
+    if (dma_now) {
+      if (stage_k)
+        wait_vm<NJ + 1>();
+      else
+        wait_vm<NJ>();
+    } else {
+      wait_vm<0>();
+    }
+    lds_barrier();
+    kc = kc + 1 < kDqK ? kc + 1 : 0;
+    vc = vc + 1 < kDqV ? vc + 1 : 0;
+  };
+  for (int hs = 0; hs < ntiles + 2; hs += 2) {
+    half_step(hs, std::integral_constant<int, 0>());
+    if (hs + 1 < ntiles + 2) half_step(hs + 1, std::integral_constant<int, 1>());
+  }
+
+  // dQ = group 0's dQ^T + group 1's: group 1 hands its fragments over through LDS
+  float* mine = reinterpret_cast<float*>(&sm) + wave * (D * 32);
+  if (grp == 1) {
+#pragma unroll
+    for (int dtile = 0; dtile < D / 32; ++dtile)
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4)
+        *reinterpret_cast<f32x4*>(&mine[((dtile * 4 + q4) * 64 + lane) * 4]) =
+            f32x4{dqt[dtile][4 * q4], dqt[dtile][4 * q4 + 1], dqt[dtile][4 * q4 + 2], dqt[dtile][4 * q4 + 3]};
+  }
+  __syncthreads();
+  if (grp == 0 && row_ok) {
+    float* dqr = dq + (base + qrow) * q_stride + (int64_t)h * D;
+#pragma unroll
+    for (int dtile = 0; dtile < D / 32; ++dtile)
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4) {
+        const f32x4 o1 = *reinterpret_cast<const f32x4*>(&mine[((dtile * 4 + q4) * 64 + lane) * 4]);
+        *reinterpret_cast<f32x4*>(dqr + 32 * dtile + 8 * q4 + 4 * g) =
+            f32x4{dqt[dtile][4 * q4] + o1[0], dqt[dtile][4 * q4 + 1] + o1[1], dqt[dtile][4 * q4 + 2] + o1[2],
+                  dqt[dtile][4 * q4 + 3] + o1[3]};
+      }
+  }
+}
+
 // dk, dv: sum of the chunk partials; ds[t] = sum over chunks and KV heads
 // (fixed order, so results are deterministic)
 __global__ __launch_bounds__(kBwdThreads) void bwd_reduce_rows_kernel(int n_chunks, int hkv, int64_t total_kept,
@@ -644,8 +924,14 @@ hipError_t launch_bwd_dg(const void* q, const void* k, const void* v, const floa
                        geo.n_chunks, geo.qc, w.dk_part, w.dv_part, w.ds_part, info.total_kept, w.part_g, w.part_t);
     constexpr int kBM = 128 / G;
     const int q_tiles = (int)((info.max_kept_len + kBM - 1) / kBM);
-    hipLaunchKernelGGL((bwd_dq_kernel<D, G>), dim3(hkv, q_tiles, info.n_seg), dim3(kBwdThreads), 0, stream, qb, kb,
-                       vb, ks, tau, gain, segs, hq, hkv, dob, lse, w.dt, dq);
+    // the DMA kernel addresses a prompt's K / V rows with 32-bit buffer ranges
+    const bool dq_dma = D == 128 && (int64_t)info.max_kept_len * hkv * D * 2 < 0xffffff00LL;
+    if (dq_dma)
+      hipLaunchKernelGGL((bwd_dq_dma_kernel<G>), dim3(hkv, q_tiles, info.n_seg), dim3(kDqThreads), 0, stream, qb, kb,
+                         vb, ks, tau, gain, segs, hq, hkv, dob, lse, w.dt, dq);
+    else
+      hipLaunchKernelGGL((bwd_dq_kernel<D, G>), dim3(hkv, q_tiles, info.n_seg), dim3(kBwdThreads), 0, stream, qb,
+                         kb, vb, ks, tau, gain, segs, hq, hkv, dob, lse, w.dt, dq);
     const int64_t kv_elems = info.total_kept * hkv * D;
     const int64_t items = kv_elems / 4 + info.total_kept;
     hipLaunchKernelGGL(bwd_reduce_rows_kernel, dim3((unsigned)((items + kBwdThreads - 1) / kBwdThreads)),
