@@ -106,6 +106,7 @@ __global__ __launch_bounds__(kThreads) void gate_mlp_kernel(const uint16_t* __re
   static_assert(HALF >= 1 && (BM * UPR / 2) % kThreads == 0, "stage split");
   __shared__ __attribute__((aligned(16))) uint16_t xs[2][BM * LD];
   __shared__ float red[4][BM];
+  __shared__ __attribute__((aligned(16))) float w2s[4 * 32 * NCT], b1s[4 * 32 * NCT];  // read in the epilogue
   __shared__ double red2[BM];
 
   const tg_segment seg = segs[blockIdx.y];
@@ -147,7 +148,11 @@ __global__ __launch_bounds__(kThreads) void gate_mlp_kernel(const uint16_t* __re
   u32x4 wr[S][NCT][4];  // W1 ring
   u32x4 xr[HALF];       // X half stage in flight
 
-  // prologue: X stage 0 into LDS, W1 blocks 0 .. S-2 in flight
+  // prologue: X stage 0 into LDS, W1 blocks 0 .. S-2 in flight, w2 and b1 into LDS
+  for (int u = threadIdx.x; u < 4 * 32 * NCT; u += blockDim.x) {
+    w2s[u] = u < h ? w2[u] : 0.0f;
+    b1s[u] = u < h && b1 != nullptr ? b1[u] : 0.0f;
+  }
 #pragma unroll
   for (int hf = 0; hf < 2; ++hf) {
 #pragma unroll
@@ -166,6 +171,15 @@ __global__ __launch_bounds__(kThreads) void gate_mlp_kernel(const uint16_t* __re
     uint16_t* xn = xs[(st + 1) & 1];
     const bool next = st + 1 < nst;
     const int kx_next = (st + 1) * KX;
+    // X fragments of the current block and the next one: block c + 1's LDS reads
+    // go out during block c's MFMAs (within a stage; the next stage's buffer is
+    // complete only after the stage barrier)
+    u32x4 xfb[2][4][RT];
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int rt = 0; rt < RT; ++rt)
+        xfb[0][j][rt] = *reinterpret_cast<const u32x4*>(xb + (rt * 32 + l32) * LD + 32 * g + 8 * j);
 #pragma unroll
     for (int c = 0; c < XB; ++c) {
       const int kb = st * XB + c;
@@ -184,26 +198,26 @@ __global__ __launch_bounds__(kThreads) void gate_mlp_kernel(const uint16_t* __re
 #pragma unroll
         for (int ct = 0; ct < NCT; ++ct) load_w_frag(w1p, n_ut, ut0 + ct, kn, lane, wr[(c + S - 1) % S][ct]);
       }
-      // all X fragments of the block are requested before the first MFMA
-      constexpr int JH = RT <= 2 ? 4 : 2;
+      if (c + 1 < XB) {
 #pragma unroll
-      for (int j0 = 0; j0 < 4; j0 += JH) {
-        u32x4 xf[JH][RT];
-#pragma unroll
-        for (int j = 0; j < JH; ++j)
+        for (int j = 0; j < 4; ++j)
 #pragma unroll
           for (int rt = 0; rt < RT; ++rt)
-            xf[j][rt] = *reinterpret_cast<const u32x4*>(xb + (rt * 32 + l32) * LD + 64 * c + 32 * g + 8 * (j0 + j));
+            xfb[(c + 1) & 1][j][rt] =
+                *reinterpret_cast<const u32x4*>(xb + (rt * 32 + l32) * LD + 64 * (c + 1) + 32 * g + 8 * j);
+      }
 #pragma unroll
-        for (int j = 0; j < JH; ++j)
+      for (int j = 0; j < 4; ++j)
 #pragma unroll
-          for (int rt = 0; rt < RT; ++rt)
+        for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
-            for (int ct = 0; ct < NCT; ++ct) acc[ct][rt] = mfma32(wr[c % S][ct][j0 + j], xf[j][rt], acc[ct][rt]);
-        // keep the order: every LDS read of the batch, then the MFMAs (the
-        // default schedule reuses one register per read and waits before each MFMA pair)
-        __builtin_amdgcn_sched_group_barrier(0x100, JH * RT, 0);
-        __builtin_amdgcn_sched_group_barrier(0x008, JH * RT * NCT, 0);
+          for (int ct = 0; ct < NCT; ++ct) acc[ct][rt] = mfma32(wr[c % S][ct][j], xfb[c & 1][j][rt], acc[ct][rt]);
+      if (c + 1 < XB) {  // the next block's reads spread over this block's MFMAs
+#pragma unroll
+        for (int i = 0; i < 4 * RT; ++i) {
+          __builtin_amdgcn_sched_group_barrier(0x008, NCT, 0);
+          __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        }
       }
     }
     if (next) {
@@ -223,9 +237,8 @@ __global__ __launch_bounds__(kThreads) void gate_mlp_kernel(const uint16_t* __re
 #pragma unroll
       for (int q4 = 0; q4 < 4; ++q4) {
         const int u0 = unit_base + 32 * ct + 8 * q4 + 4 * g;
-        const f32x4 w2v = *reinterpret_cast<const f32x4*>(w2 + u0);
-        f32x4 b1v = f32x4{0.f, 0.f, 0.f, 0.f};
-        if (b1 != nullptr) b1v = *reinterpret_cast<const f32x4*>(b1 + u0);
+        const f32x4 w2v = *reinterpret_cast<const f32x4*>(&w2s[u0]);
+        const f32x4 b1v = *reinterpret_cast<const f32x4*>(&b1s[u0]);
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
 #pragma unroll
