@@ -28,20 +28,23 @@ namespace {
 constexpr int kRows = 64;      // smallest tile height (document rows per workgroup)
 constexpr int kThreads = 256;  // 4 waves
 
-// GELU(u) = u Phi(u) = 0.5 u (1 + erf(u / sqrt 2)), with erf from Abramowitz &
-// Stegun, Handbook of Mathematical Functions, formula 7.1.26 (|error| <= 1.5e-7):
-//   erf(z) = 1 - (a1 t + a2 t^2 + a3 t^3 + a4 t^4 + a5 t^5) exp(-z^2),  t = 1 / (1 + p z),  z >= 0.
-// With q = erfc(|z|) from that formula, 1 + erf(z) is 2 - q for z >= 0 and q otherwise.
+// GELU(u) = u Phi(u) = max(u, 0) - |u| erfc(|u| / sqrt 2) / 2, with erfc from
+// Abramowitz & Stegun, Handbook of Mathematical Functions, formula 7.1.26
+// (|error| <= 1.5e-7):
+//   erfc(z) = (a1 t + a2 t^2 + a3 t^3 + a4 t^4 + a5 t^5) exp(-z^2),  t = 1 / (1 + p z),  z >= 0.
+// The halving is folded into the a_i (exactly: a power of two), 1 / sqrt 2
+// into p, and exp(-z^2) is exp2(-u^2 log2(e) / 2): 13 vector operations and
+// two transcendentals per unit.
 __device__ __forceinline__ float gelu_erf(float u) {
-  const float z = fabsf(u) * 0.70710678118654752f;
-  const float t = __builtin_amdgcn_rcpf(__builtin_fmaf(0.3275911f, z, 1.0f));
-  float p = __builtin_fmaf(1.061405429f, t, -1.453152027f);
-  p = __builtin_fmaf(p, t, 1.421413741f);
-  p = __builtin_fmaf(p, t, -0.284496736f);
-  p = __builtin_fmaf(p, t, 0.254829592f);
+  const float au = fabsf(u);
+  const float t = __builtin_amdgcn_rcpf(__builtin_fmaf(0.3275911f * 0.70710678118654752f, au, 1.0f));
+  float p = __builtin_fmaf(0.5f * 1.061405429f, t, 0.5f * -1.453152027f);
+  p = __builtin_fmaf(p, t, 0.5f * 1.421413741f);
+  p = __builtin_fmaf(p, t, 0.5f * -0.284496736f);
+  p = __builtin_fmaf(p, t, 0.5f * 0.254829592f);
   p *= t;
-  const float q = p * __builtin_amdgcn_exp2f(-z * z * 1.4426950408889634f);
-  return 0.5f * u * (u >= 0.0f ? 2.0f - q : q);
+  const float e = __builtin_amdgcn_exp2f(u * u * -0.72134752044448170f);
+  return __builtin_fmaf(-au, p * e, fmaxf(u, 0.0f));
 }
 
 // W1 in MFMA-fragment order (built by pack_w1_kernel in the workspace): for
