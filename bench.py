@@ -75,6 +75,8 @@ class Pipeline:
         self.vc = torch.empty_like(self.kc)
         self.sc = torch.empty(m, dtype=torch.float32, device=dev)
         self.out = torch.empty_like(self.qc)
+        # zero-filled once; the attention leaves its merge counters at zero (size 0: no query tile is split)
+        self.aws = tg.attention_prefill_workspace(self.plan, layer.hq, layer.hkv, layer.head_dim, dev)
         # gather on load: attention reads Q, K, V and the scores through the kept indices, so only the
         # rows the next layer needs (hidden state, scores) are compacted
         self.pairs = ([(self.x, self.hc), (self.scores, self.sc)] if gather else
@@ -106,7 +108,7 @@ class Pipeline:
                                                            self.pc, self.plan, out=self.out))
              if self.query_tau else
              (lambda: tg.gated_attention_prefill(self.qc, self.kc, self.vc, self.sc, self.tau, self.gain, self.plan,
-                                                 out=self.out))),
+                                                 out=self.out, workspace=self.aws))),
         ]
 
     # algorithmic work (what the method must do), per launch

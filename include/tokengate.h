@@ -230,6 +230,27 @@ int tg_gated_attention_prefill(const void* q, const void* k, const void* v, cons
                                const float* tau, const float* gain, const tg_segment* segs,
                                const tg_plan_info* info, int hq, int hkv, int head_dim, void* out, void* stream);
 
+/* tg_gated_attention_prefill with a workspace that lets the library split
+ * the longest query tiles of a prompt over two workgroups when the prompt is
+ * too short to fill the GPU (one prompt whose query tiles are few against the
+ * CUs per KV head).  Each half publishes its partial softmax state (running
+ * maximum, denominator, unnormalised output) to the workspace and the second
+ * half to finish merges both; the merge is symmetric, so results are
+ * deterministic.  Output: as tg_gated_attention_prefill up to fp32 rounding
+ * of the merge (within the same tolerance against exact arithmetic).
+ *   workspace: device, 256-byte aligned, at least
+ *     tg_attention_prefill_workspace_bytes(info, hq, hkv, head_dim) bytes,
+ *     zero-filled before its first use; every call leaves it reusable (its
+ *     counters back at zero).  Calls sharing a workspace must not overlap (use
+ *     one stream).  When the size is 0 no tile is split and workspace may be NULL.
+ * Errors as tg_gated_attention_prefill, and TG_ERR_WORKSPACE when the
+ * workspace is missing, misaligned or too small. */
+size_t tg_attention_prefill_workspace_bytes(const tg_plan_info* info, int hq, int hkv, int head_dim);
+int tg_gated_attention_prefill_ws(const void* q, const void* k, const void* v, const float* key_score,
+                                  const float* tau, const float* gain, const tg_segment* segs,
+                                  const tg_plan_info* info, int hq, int hkv, int head_dim, void* out, void* workspace,
+                                  size_t workspace_bytes, void* stream);
+
 /* The same attention reading the kept rows where they are (gather on load)
  * instead of from compacted copies: q [n_src_rows, hq, head_dim], k and v
  * [n_src_rows, hkv, head_dim] (bf16, device) and key_score [n_src_rows]

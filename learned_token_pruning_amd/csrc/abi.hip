@@ -240,6 +240,31 @@ int tg_gated_attention_prefill(const void* q, const void* k, const void* v, cons
                                                reinterpret_cast<hipStream_t>(stream)));
 }
 
+size_t tg_attention_prefill_workspace_bytes(const tg_plan_info* info, int hq, int hkv, int head_dim) {
+  if (!info || hq <= 0 || hkv <= 0 || head_dim <= 0 || info->n_seg < 1 || info->total_kept < 0) return 0;
+  return tg::attention_prefill_workspace_bytes(*info, hq, hkv, head_dim);
+}
+
+int tg_gated_attention_prefill_ws(const void* q, const void* k, const void* v, const float* key_score,
+                                  const float* tau, const float* gain, const tg_segment* segs,
+                                  const tg_plan_info* info, int hq, int hkv, int head_dim, void* out, void* workspace,
+                                  size_t workspace_bytes, void* stream) {
+  int st = check_attention_shapes(segs, info, hq, hkv, head_dim, true);
+  if (st != TG_OK) return st;
+  if (info->total_kept > 0 && (!q || !k || !v || !out)) return TG_ERR_INVALID_ARG;
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(out, 16)) return TG_ERR_INVALID_ARG;
+  if ((key_score && !aligned(key_score, 4)) || (tau && !aligned(tau, 4)) || (gain && !aligned(gain, 4)))
+    return TG_ERR_INVALID_ARG;
+  if (info->total_kept == 0) return TG_OK;
+  st = check_device();
+  if (st != TG_OK) return st;
+  const size_t need = tg::attention_prefill_workspace_bytes(*info, hq, hkv, head_dim);
+  if (need > 0 && (!workspace || !aligned(workspace, 256) || workspace_bytes < need)) return TG_ERR_WORKSPACE;
+  return hip_status(tg::launch_gated_attention(q, k, v, key_score, tau, gain, segs, *info, hq, hkv, head_dim,
+                                               nullptr, 0, nullptr, nullptr, out,
+                                               reinterpret_cast<hipStream_t>(stream), need > 0 ? workspace : nullptr));
+}
+
 int tg_gated_attention_prefill_query_tau(const void* q, const void* k, const void* v, const float* key_score,
                                          const float* sigma, const float* gain, const int32_t* positions,
                                          const tg_segment* segs, const tg_plan_info* info, int hq, int hkv,

@@ -220,10 +220,16 @@ hipError_t launch_compact(const int32_t* kept_idx, int64_t n_kept, int64_t n_src
 
 // kept_idx == nullptr: q, k, v, key_score are the compacted kept rows.  Otherwise
 // they hold n_src rows and kept row r of a prompt is row kept_idx[kept_start + r].
+// split_ws: nullptr, or a zero-initialised workspace of attention_prefill_workspace_bytes
+// (the counters are left at zero): long query tiles of a prompt too short to fill the
+// GPU are then split over two workgroups.
 hipError_t launch_gated_attention(const void* q, const void* k, const void* v, const float* key_score,
                                   const float* tau, const float* gain, const tg_segment* segs,
                                   const tg_plan_info& info, int hq, int hkv, int head_dim, const int32_t* kept_idx,
-                                  int64_t n_src, const int32_t* qpos, float* lse, void* out, hipStream_t stream);
+                                  int64_t n_src, const int32_t* qpos, float* lse, void* out, hipStream_t stream,
+                                  void* split_ws = nullptr);
+// Bytes of split_ws for these shapes on the current device; 0 when no query tile is split.
+size_t attention_prefill_workspace_bytes(const tg_plan_info& info, int hq, int hkv, int head_dim);
 constexpr int64_t kAttnMaxGatherRows = 16384;
 
 // Backward of the compacted-row attention; lse from the forward (natural log).

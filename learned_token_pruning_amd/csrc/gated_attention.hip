@@ -48,7 +48,15 @@
 // with m_r = r + 1 its rank among the prompt's kept rows and p_r = 1 + its
 // original position.  The lane owning row r then has its own c_r, the staged
 // bias is g_h log2(e) s_t, and the accumulator seed is that times 1 / c_r.
+#include <algorithm>
+#include <atomic>
+#include <functional>
+#include <map>
+#include <mutex>
+#include <queue>
+#include <tuple>
 #include <type_traits>
+#include <vector>
 
 #include "common.h"
 
@@ -282,6 +290,124 @@ __device__ __forceinline__ void merge_and_store(float* xo, int grp, int wave, in
         }
       }
     }
+  }
+}
+
+// Epilogue of a split query tile.  The groups merge as in merge_and_store
+// (unnormalised, in group 0), then the workgroup counts itself in at
+// flags[0].  The first half to arrive publishes (O^T, m, l) of its rows to
+// `mine` (4 waves x (D x 32 + 64) floats, in the register layout), then sets
+// flags[1]; the second waits for flags[1] (the first is already past its count
+// and waits on nothing, so the wait ends; it is also bounded), reads the
+// record from `other`, merges, normalises, stores, and resets both flags for
+// the next launch.  The merge is symmetric (both products rounded before the
+// sum), so the result does not depend on the arrival order.  The record and
+// the flags use device-coherent (agent-scope) accesses, and the record writes
+// complete (vmcnt 0) before the flag: a device-scope fence would instead write
+// back and invalidate the whole L2 of the XCD, evicting the K/V tiles the other
+// workgroups there are reading.
+constexpr int kSplitMaxSpins = 1 << 22;
+
+template <int D>
+__device__ __forceinline__ void merge_split(float* xo, int grp, int wave, int lane, int g, int l32,
+                                            f32x16 (&o)[D / 32], float m_run, float l_run, int qrow, int n,
+                                            const tg_segment& seg, int64_t q_stride, int h, int hq,
+                                            float* __restrict__ lse, uint16_t* __restrict__ out, float* mine_rec,
+                                            float* other_rec, int* flags) {
+  constexpr int kRec = D * 32 + 64;
+  float* mine = xo + wave * kRec;
+  int* arrival = reinterpret_cast<int*>(xo + 4 * kRec);
+  const float l_half = xor32_sum(l_run);  // both half-waves: same bits
+  if (grp == 1) {
+#pragma unroll
+    for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) mine[(dt * 16 + i) * 64 + lane] = o[dt][i];
+    if (g == 0) {
+      mine[D * 32 + l32] = m_run;
+      mine[D * 32 + 32 + l32] = l_half;
+    }
+  }
+  __syncthreads();
+  float m = m_run, l = l_half;
+  if (grp == 0) {
+    const float m1 = mine[D * 32 + l32];
+    const float l1 = mine[D * 32 + 32 + l32];
+    m = __builtin_fmaxf(m_run, m1);
+    const float a0 = m_run == -__builtin_inff() ? 0.0f : __builtin_amdgcn_exp2f(m_run - m);
+    const float a1 = m1 == -__builtin_inff() ? 0.0f : __builtin_amdgcn_exp2f(m1 - m);
+    l = l_half * a0 + l1 * a1;
+#pragma unroll
+    for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) o[dt][i] = o[dt][i] * a0 + mine[(dt * 16 + i) * 64 + lane] * a1;
+  }
+  if (threadIdx.x == 0) arrival[0] = atomicAdd(&flags[0], 1);
+  __syncthreads();
+  if (arrival[0] == 0) {  // uniform: first half in publishes its record
+    if (grp == 0) {
+      float* rec = mine_rec + wave * kRec;
+#pragma unroll
+      for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+        for (int i = 0; i < 16; ++i)
+          __hip_atomic_store(&rec[(dt * 16 + i) * 64 + lane], o[dt][i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      if (g == 0) {
+        __hip_atomic_store(&rec[D * 32 + l32], m, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_store(&rec[D * 32 + 32 + l32], l, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      }
+      wait_vm<0>();  // the record writes have completed before the flag below
+    }
+    __syncthreads();
+    if (threadIdx.x == 0) __hip_atomic_store(&flags[1], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    return;
+  }
+  if (threadIdx.x == 0) {
+    int spins = 0;
+    while (__hip_atomic_load(&flags[1], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == 0 && ++spins < kSplitMaxSpins)
+      __builtin_amdgcn_s_sleep(1);
+  }
+  __syncthreads();
+  if (grp == 0) {
+    // both products rounded before the sum (no fused multiply-add), so the two arrival orders give the same bits
+#pragma clang fp contract(off)
+    const float* rec = other_rec + wave * kRec;
+    float ob[D / 32][16];  // the whole record is requested before any of it is used
+#pragma unroll
+    for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+      for (int i = 0; i < 16; ++i)
+        ob[dt][i] = __hip_atomic_load(&rec[(dt * 16 + i) * 64 + lane], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const float mb = __hip_atomic_load(&rec[D * 32 + l32], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const float lb = __hip_atomic_load(&rec[D * 32 + 32 + l32], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const float mm = __builtin_fmaxf(m, mb);
+    const float aa = m == -__builtin_inff() ? 0.0f : __builtin_amdgcn_exp2f(m - mm);
+    const float ab = mb == -__builtin_inff() ? 0.0f : __builtin_amdgcn_exp2f(mb - mm);
+    const float l_all = l * aa + lb * ab;
+    const float inv = 1.0f / l_all;
+    if (lse != nullptr && qrow < n && g == 0)
+      lse[((int64_t)seg.kept_start + qrow) * hq + h] = (mm + __log2f(l_all)) * 0.6931471805599453f;
+    if (qrow < n) {
+      uint16_t* orow = out + ((int64_t)seg.kept_start + qrow) * q_stride + (int64_t)h * D;
+#pragma unroll
+      for (int dt = 0; dt < D / 32; ++dt) {
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4) {
+          float r[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int i = 4 * q4 + e;
+            r[e] = (o[dt][i] * aa + ob[dt][i] * ab) * inv;
+          }
+          *reinterpret_cast<u32x2*>(orow + 32 * dt + 8 * q4 + 4 * g) = u32x2{pack_bf16(r[0], r[1]),
+                                                                             pack_bf16(r[2], r[3])};
+        }
+      }
+    }
+  }
+  if (threadIdx.x == 0) {
+    __hip_atomic_store(&flags[0], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_store(&flags[1], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
 }
 
@@ -535,7 +661,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
     const float* __restrict__ key_score, const float* __restrict__ tau, const float* __restrict__ gain,
     const tg_segment* __restrict__ segs, int hq, int hkv, const int32_t* __restrict__ kept_idx, int64_t n_src,
-    const int32_t* __restrict__ qpos, float* __restrict__ lse, uint16_t* __restrict__ out) {
+    const int32_t* __restrict__ qpos, float* __restrict__ lse, uint16_t* __restrict__ out, int split_t, int ns_max,
+    int* __restrict__ split_cnt, float* __restrict__ split_part) {
   constexpr bool GATHER = MODE == kGather;
   constexpr bool QTAU = MODE == kQueryTau;
   constexpr int kBM = 128 / G;
@@ -547,9 +674,31 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
 
   const tg_segment seg = segs[blockIdx.z];
   const int n = seg.kept_len;
-  const int q0 = (gridDim.y - 1 - blockIdx.y) * kBM;
-  if (q0 >= n) return;  // uniform
+  // Work item: query tile qi (kBM rows) and key tiles [t0, t1) of it.  With split_t > 0 every query tile with
+  // more than split_t key tiles is split in two items, an owner (key tiles [0, split_t)) and a helper (the rest);
+  // each publishes its partial result and the second to finish merges both.  blockIdx.y runs over the owners,
+  // then the helpers, then the whole tiles, each longest first.
+  const int nq = (n + kBM - 1) / kBM;
+  const int qs = (split_t > 0 && n > kBN * split_t) ? min(nq, (kBN * split_t) / kBM) : nq;  // first split tile
+  const int ns = nq - qs;
+  const int y = blockIdx.y;
+  int qi, role;  // role 0: whole tile, 1: owner, 2: helper
+  if (y < ns) {
+    qi = nq - 1 - y;
+    role = 1;
+  } else if (y < 2 * ns) {
+    qi = nq - 1 - (y - ns);
+    role = 2;
+  } else if (y < 2 * ns + qs) {
+    qi = qs - 1 - (y - 2 * ns);
+    role = 0;
+  } else {
+    return;  // uniform: past this prompt's items
+  }
+  const int q0 = qi * kBM;
   const int q_end = min(q0 + kBM, n);
+  const int t0 = role == 2 ? split_t : 0;
+  const int t1 = role == 1 ? split_t : (q_end + kBN - 1) / kBN;
   if (GATHER) {
     for (int i = threadIdx.x; i < q_end; i += kThreads) sidx[i] = kept_idx[seg.kept_start + i];
     __syncthreads();
@@ -596,7 +745,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
     if (!GATHER) return (uint32_t)row * row_bytes;
     return row < q_end ? (uint32_t)sidx[row] * row_bytes : kPastRange;
   };
-  auto dma_k = [&](int tile, int buf) {
+  auto dma_k = [&](int lt, int buf) {  // lt: tile index inside the item
+    const int tile = t0 + lt;
     if (!GATHER) {
       const uint32_t soff = (uint32_t)(tile * kBN) * row_bytes;
 #pragma unroll
@@ -615,7 +765,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
       }
     }
   };
-  auto dma_v = [&](int tile, int buf) {
+  auto dma_v = [&](int lt, int buf) {
+    const int tile = t0 + lt;
     if (!GATHER) {
       const uint32_t soff = (uint32_t)(tile * kBN) * row_bytes;
 #pragma unroll
@@ -644,7 +795,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
   const float cs = __builtin_fmaxf(__builtin_fabsf(th) * base, 1e-30f);
   const float inv_cs = QTAU ? 1.0f / cs : 1.0f;
 
-  const int ntiles = (q_end + kBN - 1) / kBN;
+  const int ntiles = t1 - t0;  // key tiles of the item; local tile j is key tile t0 + j
   const int wlast = qw0 + 31;
 
   u32x4 qf[D / 16];
@@ -713,7 +864,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
 
     if (P == grp) {
       const int jp = hs - 2;
-      if (jp >= 0 && jp * kBN <= wlast) {
+      if (jp >= 0 && (t0 + jp) * kBN <= wlast) {
         const uint16_t* vt = sm.v[b1];
 #pragma unroll
         for (int s4 = 0; s4 < 4; ++s4) {
@@ -731,7 +882,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
         sched_two_reads_ahead<4 * (D / 32), 8>();
       }
       const int jq = hs;
-      if (jq < ntiles && jq * kBN <= wlast) {
+      if (jq < ntiles && (t0 + jq) * kBN <= wlast) {
         const float* bias = sm.s[b_cur];
 #pragma unroll
         for (int hf = 0; hf < 2; ++hf)
@@ -754,8 +905,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
     } else {
       // softmax phase of tile hs - 1
       const int js = hs - 1;
-      if (js >= 0 && js < ntiles && js * kBN <= wlast)
-        softmax_tile<D>(js * kBN, qrow, qw0, n, g, cs, sa, m_run, l_run, o, pf);
+      if (js >= 0 && js < ntiles && (t0 + js) * kBN <= wlast)
+        softmax_tile<D>((t0 + js) * kBN, qrow, qw0, n, g, cs, sa, m_run, l_run, o, pf);
     }
 
     if (dma_now && stage_k) dma_k(hs + 2, b2);  // K tile hs + 2 (and its scores) at the end
@@ -779,18 +930,135 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
   }
 
   // Merge the two groups: group 1 hands (m, l, O^T) to group 0 through LDS.
-  merge_and_store<D>(reinterpret_cast<float*>(&sm), grp, wave, lane, g, l32, o, m_run, l_run, qrow, n, seg, q_stride, h,
-                     hq, lse, out);
+  if (role == 0) {
+    merge_and_store<D>(reinterpret_cast<float*>(&sm), grp, wave, lane, g, l32, o, m_run, l_run, qrow, n, seg, q_stride,
+                       h, hq, lse, out);
+  } else {
+    const int slot = (blockIdx.z * hkv + c) * ns_max + (nq - 1 - qi);
+    constexpr int kPart = 4 * (D * 32 + 64);  // floats per half: 4 waves x (O^T, m, l)
+    merge_split<D>(reinterpret_cast<float*>(&sm), grp, wave, lane, g, l32, o, m_run, l_run, qrow, n, seg, q_stride, h,
+                   hq, lse, out, split_part + ((int64_t)slot * 2 + (role - 1)) * kPart,
+                   split_part + ((int64_t)slot * 2 + (2 - role)) * kPart, split_cnt + 2 * slot);
+  }
+}
+
+// Splitting the long query tiles of one prompt.  Items are scheduled in
+// blockIdx order on the CUs that serve a KV head (blockIdx.x is the head, so a
+// head's workgroups share an XCD); an item of k 64-key tiles costs about
+// k + 2 half-steps plus kItemFixed for its prologue and output (measured on
+// MI355X at head_dim 128: ~1.04 us per half-step, ~5 us fixed), and a split
+// half kItemMerge more (fitted to measured split times at 500-3000 kept
+// rows).  The split point T (owner: key tiles [0, T), helper: the rest)
+// minimises the modelled makespan of list scheduling in the kernel's item
+// order; splitting is used only for a single prompt whose modelled time drops
+// below kSplitGain of the unsplit one.
+constexpr double kItemFixed = 4.8, kItemMerge = 3.5, kSplitGain = 0.93;
+
+int device_cu_count() {
+  static std::atomic<int> cached{0};
+  int n = cached.load(std::memory_order_relaxed);
+  if (n > 0) return n;
+  int dev = 0;
+  n = 0;
+  if (hipGetDevice(&dev) != hipSuccess || hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+      n <= 0)
+    n = 256;
+  cached.store(n, std::memory_order_relaxed);
+  return n;
+}
+
+double list_makespan(const std::vector<double>& items, int ncu) {
+  std::priority_queue<double, std::vector<double>, std::greater<double>> free_at;
+  for (int i = 0; i < ncu; ++i) free_at.push(0.0);
+  double end = 0.0;
+  for (double c : items) {
+    const double t = free_at.top() + c;
+    free_at.pop();
+    free_at.push(t);
+    end = std::max(end, t);
+  }
+  return end;
+}
+
+struct SplitPlan {
+  int t = 0;       // split point in 64-key tiles; 0: no split
+  int ns_max = 0;  // split query tiles of the longest prompt
+};
+
+SplitPlan choose_split(const tg_plan_info& info, int G, int hkv) {
+  SplitPlan sp;
+  const int n = (int)info.max_kept_len;
+  if (info.n_seg != 1 || n <= 0 || hkv <= 0) return sp;
+  const int kBM = 128 / G;
+  const int nq = (n + kBM - 1) / kBM;
+  const int per_head = std::max(1, device_cu_count() / hkv);
+  if (nq > 2 * per_head) return sp;  // enough whole tiles to balance the CUs
+  static std::mutex mu;
+  static std::map<std::tuple<int, int, int>, SplitPlan> cache;
+  const auto key = std::make_tuple(n, G, per_head);
+  {
+    std::lock_guard<std::mutex> lock(mu);
+    const auto it = cache.find(key);
+    if (it != cache.end()) return it->second;
+  }
+  auto nk = [&](int qi) { return (std::min((qi + 1) * kBM, n) + kBN - 1) / kBN; };
+  std::vector<double> items;
+  auto model = [&](int T) {
+    items.clear();
+    for (int qi = nq - 1; qi >= 0; --qi)
+      if (T > 0 && nk(qi) > T) items.push_back(kItemFixed + kItemMerge + T + 2);
+    for (int qi = nq - 1; qi >= 0; --qi)
+      if (T > 0 && nk(qi) > T) items.push_back(kItemFixed + kItemMerge + (nk(qi) - T) + 2);
+    for (int qi = nq - 1; qi >= 0; --qi)
+      if (T == 0 || nk(qi) <= T) items.push_back(kItemFixed + nk(qi) + 2);
+    return list_makespan(items, per_head);
+  };
+  const double whole = model(0);
+  double best = whole;
+  int best_t = 0;
+  for (int T = 1; T < nk(nq - 1); ++T) {
+    const double ms = model(T);
+    if (ms < best) {
+      best = ms;
+      best_t = T;
+    }
+  }
+  if (best_t > 0 && best < kSplitGain * whole) {
+    sp.t = best_t;
+    sp.ns_max = nq - std::min(nq, (kBN * best_t) / kBM);
+  }
+  std::lock_guard<std::mutex> lock(mu);
+  cache[key] = sp;
+  return sp;
+}
+
+// workspace: int flags [n_seg x hkv x ns_max][2] (arrivals, record ready), padded
+// to 256 bytes, then the fp32 records [slot][half][4 waves][D x 32 + 64]
+size_t split_flag_bytes(size_t slots) { return (slots * 8 + 255) / 256 * 256; }
+size_t split_bytes(const SplitPlan& sp, const tg_plan_info& info, int hkv, int D) {
+  if (sp.t == 0) return 0;
+  const size_t slots = (size_t)info.n_seg * hkv * sp.ns_max;
+  return split_flag_bytes(slots) + slots * 2 * 4 * ((size_t)D * 32 + 64) * 4;
 }
 
 template <int D, int G>
 hipError_t launch_dg(const void* q, const void* k, const void* v, const float* ks, const float* tau,
                      const float* gain, const tg_segment* segs, const tg_plan_info& info, int hq, int hkv,
                      const int32_t* kept_idx, int64_t n_src, const int32_t* qpos, float* lse, void* out,
-                     hipStream_t stream) {
+                     hipStream_t stream, void* split_ws) {
   constexpr int kBM = 128 / G;
-  const int ntiles = (info.max_kept_len + kBM - 1) / kBM;
+  int ntiles = (info.max_kept_len + kBM - 1) / kBM;
   if (ntiles == 0) return hipSuccess;
+  SplitPlan sp;
+  if (split_ws != nullptr && !(kept_idx != nullptr && info.max_kept_len > kDmaGatherRows)) sp = choose_split(info, G, hkv);
+  int* split_cnt = nullptr;
+  float* split_part = nullptr;
+  if (sp.t > 0) {
+    const size_t slots = (size_t)info.n_seg * hkv * sp.ns_max;
+    split_cnt = reinterpret_cast<int*>(split_ws);
+    split_part = reinterpret_cast<float*>(reinterpret_cast<char*>(split_ws) + split_flag_bytes(slots));
+    ntiles += sp.ns_max;
+  }
   dim3 grid(hkv, ntiles, info.n_seg);
   auto* qb = reinterpret_cast<const uint16_t*>(q);
   auto* kb = reinterpret_cast<const uint16_t*>(k);
@@ -798,30 +1066,41 @@ hipError_t launch_dg(const void* q, const void* k, const void* v, const float* k
   auto* ob = reinterpret_cast<uint16_t*>(out);
   if (kept_idx != nullptr && info.max_kept_len <= kDmaGatherRows)
     hipLaunchKernelGGL((gated_attention_dma_kernel<D, G, kGather>), grid, dim3(kThreads), 0, stream, qb, kb, vb, ks,
-                       tau, gain, segs, hq, hkv, kept_idx, n_src, nullptr, lse, ob);
+                       tau, gain, segs, hq, hkv, kept_idx, n_src, nullptr, lse, ob, sp.t, sp.ns_max, split_cnt,
+                       split_part);
   else if (kept_idx != nullptr)
     hipLaunchKernelGGL((gated_attention_kernel<D, G, kGather>), grid, dim3(kThreads), 0, stream, qb, kb, vb, ks, tau,
                        gain, segs, hq, hkv, kept_idx, n_src, nullptr, lse, ob);
   else if (qpos != nullptr)
     hipLaunchKernelGGL((gated_attention_dma_kernel<D, G, kQueryTau>), grid, dim3(kThreads), 0, stream, qb, kb, vb, ks,
-                       tau, gain, segs, hq, hkv, nullptr, (int64_t)0, qpos, lse, ob);
+                       tau, gain, segs, hq, hkv, nullptr, (int64_t)0, qpos, lse, ob, sp.t, sp.ns_max, split_cnt,
+                       split_part);
   else
     hipLaunchKernelGGL((gated_attention_dma_kernel<D, G, kCompacted>), grid, dim3(kThreads), 0, stream, qb, kb, vb,
-                       ks, tau, gain, segs, hq, hkv, nullptr, (int64_t)0, nullptr, lse, ob);
+                       ks, tau, gain, segs, hq, hkv, nullptr, (int64_t)0, nullptr, lse, ob, sp.t, sp.ns_max, split_cnt,
+                       split_part);
   return hipGetLastError();
 }
 
 }  // namespace
 
+size_t attention_prefill_workspace_bytes(const tg_plan_info& info, int hq, int hkv, int head_dim) {
+  if (hkv <= 0 || hq % hkv != 0) return 0;
+  const int G = hq / hkv;
+  if (!(G == 1 || G == 2 || G == 4)) return 0;
+  return split_bytes(choose_split(info, G, hkv), info, hkv, head_dim);
+}
+
 hipError_t launch_gated_attention(const void* q, const void* k, const void* v, const float* key_score,
                                   const float* tau, const float* gain, const tg_segment* segs,
                                   const tg_plan_info& info, int hq, int hkv, int head_dim, const int32_t* kept_idx,
-                                  int64_t n_src, const int32_t* qpos, float* lse, void* out, hipStream_t stream) {
+                                  int64_t n_src, const int32_t* qpos, float* lse, void* out, hipStream_t stream,
+                                  void* split_ws) {
   const int G = hq / hkv;
 #define TG_ATTN_CASE(DD, GG) \
   if (head_dim == DD && G == GG) \
     return launch_dg<DD, GG>(q, k, v, key_score, tau, gain, segs, info, hq, hkv, kept_idx, n_src, qpos, lse, out, \
-                             stream);
+                             stream, split_ws);
   TG_ATTN_CASE(128, 1)
   TG_ATTN_CASE(128, 2)
   TG_ATTN_CASE(128, 4)

@@ -32,6 +32,7 @@ STATUS_NAMES = {0: "TG_OK", -1: "TG_ERR_INVALID_ARG", -2: "TG_ERR_UNSUPPORTED", 
 EXPORTS = ("tg_status_string", "tg_abi_version", "tg_plan_segments", "tg_gate_workspace_bytes", "tg_gate_score",
            "tg_gate_packed_w1_bytes", "tg_gate_pack_w1", "tg_gate_score_prepacked",
            "tg_select_workspace_bytes", "tg_select_topk", "tg_compact_kept", "tg_gated_attention_prefill",
+           "tg_attention_prefill_workspace_bytes", "tg_gated_attention_prefill_ws",
            "tg_gated_attention_prefill_gather", "tg_gated_attention_prefill_query_tau",
            "tg_decode_workspace_bytes", "tg_gated_attention_decode", "tg_gated_attention_prefill_lse",
            "tg_attention_backward_workspace_bytes", "tg_gated_attention_backward",
@@ -116,6 +117,11 @@ _lib.tg_gated_attention_decode.argtypes = [_vp, _vp, _vp, _vp, _vp, _i32, _vp, _
 _lib.tg_gated_attention_prefill.restype = _i32
 _lib.tg_gated_attention_prefill.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, ctypes.POINTER(PlanInfo), _i32, _i32,
                                             _i32, _vp, _vp]
+_lib.tg_attention_prefill_workspace_bytes.restype = _sz
+_lib.tg_attention_prefill_workspace_bytes.argtypes = [ctypes.POINTER(PlanInfo), _i32, _i32, _i32]
+_lib.tg_gated_attention_prefill_ws.restype = _i32
+_lib.tg_gated_attention_prefill_ws.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, ctypes.POINTER(PlanInfo), _i32,
+                                               _i32, _i32, _vp, _vp, _sz, _vp]
 
 
 _lib.tg_gemm_bf16.restype = _i32
@@ -311,14 +317,34 @@ def compact_kept(kept_idx: torch.Tensor, pairs: Sequence[Tuple[torch.Tensor, tor
     _check(st, "tg_compact_kept")
 
 
+def attention_prefill_workspace_bytes(plan: Plan, hq: int, hkv: int, head_dim: int) -> int:
+    """tg_attention_prefill_workspace_bytes: 0 when no query tile is split."""
+    return int(_lib.tg_attention_prefill_workspace_bytes(ctypes.byref(plan.info), hq, hkv, head_dim))
+
+
+def attention_prefill_workspace(plan: Plan, hq: int, hkv: int, head_dim: int, device) -> torch.Tensor:
+    """A zero-filled workspace for gated_attention_prefill(..., workspace=)."""
+    return torch.zeros(max(attention_prefill_workspace_bytes(plan, hq, hkv, head_dim), 256), dtype=torch.uint8,
+                       device=device)
+
+
 def gated_attention_prefill(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, key_score: Optional[torch.Tensor],
                             tau: Optional[torch.Tensor], gain: Optional[torch.Tensor], plan: Plan,
-                            out: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
-    """tg_gated_attention_prefill.  q [M, hq, D], k/v [M, hkv, D] bf16 contiguous."""
+                            out: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
+                            stream=None) -> torch.Tensor:
+    """tg_gated_attention_prefill.  q [M, hq, D], k/v [M, hkv, D] bf16 contiguous.  With a workspace (from
+    attention_prefill_workspace) it calls tg_gated_attention_prefill_ws, which may split long query tiles."""
     m, hq, dh = q.shape
     hkv = k.shape[1]
     if out is None:
         out = torch.empty_like(q)
+    if workspace is not None:
+        st = _lib.tg_gated_attention_prefill_ws(_ptr(q), _ptr(k), _ptr(v), _ptr(key_score), _ptr(tau), _ptr(gain),
+                                                _dev_table(plan), ctypes.byref(plan.info), hq, hkv, dh, _ptr(out),
+                                                _ptr(workspace), workspace.numel() * workspace.element_size(),
+                                                _stream(stream))
+        _check(st, "tg_gated_attention_prefill_ws")
+        return out
     st = _lib.tg_gated_attention_prefill(_ptr(q), _ptr(k), _ptr(v), _ptr(key_score), _ptr(tau), _ptr(gain),
                                          _dev_table(plan), ctypes.byref(plan.info), hq, hkv, dh, _ptr(out),
                                          _stream(stream))

@@ -160,6 +160,29 @@ def test_attention_validation():
     assert f(FAKE, FAKE, FAKE, None, None, None, FAKE, info, 0, 8, 128, FAKE, None) == -1
 
 
+def test_attention_split_workspace():
+    """Workspace of the split-tile attention: sized only for a single prompt too short to fill the GPU (the
+    device's CU count, 256 on MI355X and when no device is present), zero for batches and for prompts long enough
+    to fill it; the entry point validates shapes and arguments like the plain one."""
+    def nbytes(lens, hq=16, hkv=8, d=128):
+        p = tg.plan_segments([0] + list(np.cumsum(lens)), [0] * len(lens), [0] * len(lens), [0] * len(lens))
+        return tg.attention_prefill_workspace_bytes(p, hq, hkv, d)
+    if not gpu_available():
+        rec = 2 * 4 * (32 * 128 + 64) * 4  # two records of 4 waves x (O^T, m, l) per split tile
+        b = nbytes([2112])
+        assert b > 0 and (b - 256 * ((b // rec * 8 + 255) // 256)) % rec == 0
+        assert nbytes([1000]) > 0
+    assert nbytes([300, 700]) == 0 and nbytes([64]) == 0 and nbytes([8192]) == 0
+    assert nbytes([2112], hq=16, hkv=6) == 0 and L.tg_attention_prefill_workspace_bytes(None, 16, 8, 128) == 0
+    p = _plan()
+    info = ctypes.byref(p.info)
+    f = L.tg_gated_attention_prefill_ws
+    assert f(FAKE, FAKE, FAKE, None, None, None, FAKE, info, 16, 6, 128, FAKE, None, 0, None) == -2
+    assert f(None, FAKE, FAKE, None, None, None, FAKE, info, 16, 8, 128, FAKE, None, 0, None) == -1
+    empty = tg.plan_segments([0, 0], [0], [0], [0])
+    assert f(None, None, None, None, None, None, FAKE, ctypes.byref(empty.info), 16, 8, 128, None, None, 0, None) == 0
+
+
 def test_attention_rejects_prompts_past_32bit_ranges():
     # 2^21 kept rows x 8 KV heads x 128 dims x 2 bytes = 2^32 bytes of K per prompt
     big = tg.plan_segments([0, 1 << 21], [0], [0], [0])

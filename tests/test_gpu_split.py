@@ -1,0 +1,199 @@
+"""Attention with split query tiles (tg_gated_attention_prefill_ws), through
+the C ABI, against the CPU oracle and against the unsplit entry point.
+
+A prompt too short to fill the GPU has its longest query tiles split over two
+workgroups, whose partial softmax states are merged by the second to finish.
+Bar: the oracle tolerance of the unsplit path (max |d| <= 2e-2 on the bf16
+outputs); repeated calls bit-identical (the merge is symmetric, so arrival
+order does not matter) and the workspace counters back at zero after every
+call, also under graph replay.
+"""
+import functools
+import sys
+
+import numpy as np
+import pytest
+
+import oracle
+from _lib import binding
+from learned_token_pruning_amd import workloads as W
+
+pytestmark = pytest.mark.gpu
+
+ATTN_ATOL = 2e-2
+
+
+def _say(*a):
+    print("[case]", *a, file=sys.stderr, flush=True)
+
+
+@functools.lru_cache(maxsize=None)
+def _tg():
+    import torch
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    return binding()
+
+
+def dev_bf16(bits):
+    import torch
+    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).cuda()
+
+
+def dev_f32(a):
+    import torch
+    return torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).cuda()
+
+
+def host_bf16(t):
+    import torch
+    return t.view(torch.int16).cpu().numpy().view(np.uint16)
+
+
+def random_inputs(seed, m, hq, hkv, d):
+    rng = np.random.default_rng(seed)
+    q = W.f32_to_bf16_bits(rng.standard_normal((m, hq, d)).astype(np.float32))
+    k = W.f32_to_bf16_bits(rng.standard_normal((m, hkv, d)).astype(np.float32))
+    v = W.f32_to_bf16_bits(rng.standard_normal((m, hkv, d)).astype(np.float32))
+    s = rng.standard_normal(m).astype(np.float32)
+    tau = rng.uniform(0.8, 1.2, hq).astype(np.float32)
+    gain = rng.uniform(0.5, 1.5, hq).astype(np.float32)
+    return q, k, v, s, tau, gain
+
+
+def plan_of(tg, lens):
+    n = len(lens)
+    offs = np.concatenate([[0], np.cumsum(lens)]).astype(np.int64)
+    return tg.plan_segments(list(offs), [0] * n, [0] * n, [0] * n, device="cuda"), offs
+
+
+def oracle_check(got_bits, q, k, v, s, tau, gain, offs, rows=None):
+    ref = oracle.gated_attention(W.bf16_bits_to_f64(q), W.bf16_bits_to_f64(k), W.bf16_bits_to_f64(v),
+                                 None if s is None else s.astype(np.float64),
+                                 None if tau is None else tau.astype(np.float64),
+                                 None if gain is None else gain.astype(np.float64), offs, rows=rows)
+    got = W.bf16_bits_to_f64(got_bits)
+    g = got if rows is None else got[rows]
+    err = np.abs(g - ref).max()
+    assert err <= ATTN_ATOL, f"max abs err {err:.3e}"
+    return err
+
+
+def counters_zero(ws, nbytes, d):
+    """The int32 merge flags at the start of the workspace: two per split tile (arrivals, record ready), then
+    two fp32 records of 4 x (32 d + 64) floats per split tile."""
+    import torch
+    torch.cuda.synchronize()
+    slots = nbytes // (2 * 4 * (32 * d + 64) * 4)
+    return bool((ws[: 8 * slots].view(torch.int32) == 0).all().item())
+
+
+def test_split_workload_2_full():
+    """The 16K-token layer's attention (2112 kept rows, 16 Q / 8 KV heads, D = 128)."""
+    import torch
+    _say("split attention, workload 2 (M=2112)")
+    tg = _tg()
+    L = W.workload(2)
+    s = W.mixture_scores(2, L.segments)
+    seg = L.segments.with_budget(2048)
+    idx, offs = oracle.kept_indices(s, seg.seg_start, seg.doc_begin, seg.doc_end, seg.k_budget)
+    q, k, v = (oracle.compact_rows(a, idx) for a in (L.q, L.k, L.v))
+    sc = oracle.compact_rows(s, idx).astype(np.float32)
+    plan, _ = plan_of(tg, [q.shape[0]])
+    hq, hkv, d = q.shape[1], k.shape[1], q.shape[2]
+    nbytes = tg.attention_prefill_workspace_bytes(plan, hq, hkv, d)
+    _say("workspace bytes", nbytes)
+    assert nbytes > 0, "a single 2112-row prompt should split its longest query tiles"
+    ws = tg.attention_prefill_workspace(plan, hq, hkv, d, "cuda")
+    args = (dev_bf16(q), dev_bf16(k), dev_bf16(v), dev_f32(sc), dev_f32(L.tau), dev_f32(L.gain), plan)
+    outs = [tg.gated_attention_prefill(*args, workspace=ws) for _ in range(3)]
+    plain = tg.gated_attention_prefill(*args)
+    torch.cuda.synchronize()
+    for o in outs[1:]:
+        assert torch.equal(o.view(torch.int16), outs[0].view(torch.int16)), "split results differ between calls"
+    assert counters_zero(ws, nbytes, d), "merge counters not reset"
+    diff = (outs[0].float() - plain.float()).abs().max().item()
+    _say("max |split - unsplit|", diff)
+    assert diff <= ATTN_ATOL
+    oracle_check(host_bf16(outs[0]), q, k, v, sc, L.tau, L.gain, offs)
+
+
+@pytest.mark.parametrize("d,hq,hkv,n,bias", [(128, 16, 8, 700, True), (128, 8, 8, 1500, True),
+                                             (128, 16, 4, 1200, False), (64, 8, 2, 1000, True),
+                                             (128, 2, 2, 3000, True), (64, 4, 4, 129, False)])
+def test_split_shapes(d, hq, hkv, n, bias):
+    import torch
+    _say("split attention", d, hq, hkv, n, bias)
+    tg = _tg()
+    q, k, v, s, tau, gain = random_inputs(d + hq + hkv + n, n, hq, hkv, d)
+    if not bias:
+        s, gain = None, None
+    plan, offs = plan_of(tg, [n])
+    nbytes = tg.attention_prefill_workspace_bytes(plan, hq, hkv, d)
+    _say("workspace bytes", nbytes)
+    ws = tg.attention_prefill_workspace(plan, hq, hkv, d, "cuda")
+    args = (dev_bf16(q), dev_bf16(k), dev_bf16(v), None if s is None else dev_f32(s), dev_f32(tau),
+            None if gain is None else dev_f32(gain), plan)
+    outs = [tg.gated_attention_prefill(*args, workspace=ws) for _ in range(6)]
+    torch.cuda.synchronize()
+    a = outs[0]
+    for o in outs[1:]:  # whichever half of a split tile finishes second, the bits are the same
+        assert torch.equal(o.view(torch.int16), a.view(torch.int16))
+    assert counters_zero(ws, nbytes, d)
+    rows = None
+    if n > 1200:
+        rng = np.random.default_rng(n)
+        rows = np.unique(np.concatenate([[0, 1, 63, 64, n - 65, n - 64, n - 2, n - 1], rng.integers(0, n, 200)]))
+    oracle_check(host_bf16(a), q, k, v, s, tau, gain, offs, rows=rows)
+
+
+def test_split_graph_replay():
+    """The split attention captured in a HIP graph: every replay equals the eager result (the counters the
+    merge uses are reset by the kernel itself, no memset node)."""
+    import torch
+    _say("split attention, graph replay")
+    tg = _tg()
+    n, hq, hkv, d = 2112, 16, 8, 128
+    q, k, v, s, tau, gain = random_inputs(5, n, hq, hkv, d)
+    plan, _ = plan_of(tg, [n])
+    nbytes = tg.attention_prefill_workspace_bytes(plan, hq, hkv, d)
+    assert nbytes > 0
+    ws = tg.attention_prefill_workspace(plan, hq, hkv, d, "cuda")
+    args = (dev_bf16(q), dev_bf16(k), dev_bf16(v), dev_f32(s), dev_f32(tau), dev_f32(gain), plan)
+    eager = tg.gated_attention_prefill(*args, workspace=ws)
+    out = torch.empty_like(eager)
+    stream = torch.cuda.Stream()
+    stream.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(stream):
+        tg.gated_attention_prefill(*args, out=out, workspace=ws, stream=stream)  # warm-up outside the capture
+    torch.cuda.current_stream().wait_stream(stream)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, stream=stream):
+        tg.gated_attention_prefill(*args, out=out, workspace=ws, stream=stream)
+    for r in range(3):
+        out.zero_()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out.view(torch.int16), eager.view(torch.int16)), f"replay {r}"
+        tg.gated_attention_prefill(*args, workspace=ws)  # eager work between replays
+        torch.cuda.synchronize()
+    assert counters_zero(ws, nbytes, d)
+
+
+def test_split_batch_not_split():
+    """Several prompts: no split (workspace size 0), and the workspace entry point equals the plain one."""
+    import torch
+    _say("split attention, batch")
+    tg = _tg()
+    lens = [300, 1, 700, 64]
+    n, hq, hkv, d = sum(lens), 16, 8, 128
+    q, k, v, s, tau, gain = random_inputs(9, n, hq, hkv, d)
+    plan, _ = plan_of(tg, lens)
+    assert tg.attention_prefill_workspace_bytes(plan, hq, hkv, d) == 0
+    ws = tg.attention_prefill_workspace(plan, hq, hkv, d, "cuda")
+    args = (dev_bf16(q), dev_bf16(k), dev_bf16(v), dev_f32(s), dev_f32(tau), dev_f32(gain), plan)
+    a = tg.gated_attention_prefill(*args, workspace=ws)
+    b = tg.gated_attention_prefill(*args)
+    torch.cuda.synchronize()
+    assert torch.equal(a.view(torch.int16), b.view(torch.int16))
