@@ -357,6 +357,339 @@ __global__ __launch_bounds__(kDkdvThreads) void bwd_dkdv_kernel(
   }
 }
 
+// dK, dV (head dim 128) with direct-to-LDS staging and the forward's ping-pong
+// schedule.  Same work split as bwd_dkdv_kernel: a workgroup owns one KV head,
+// 128 keys (wave w & 3 owns 32 of them in both groups) and a chunk of the
+// prompt's 32-row query blocks; its two groups of four waves take alternate
+// (head, query block) items.  In its MFMA phase a wave runs dV^T += dO^T P and
+// dK^T += Q^T dZ for its previous item, then S = Q K^T and dP = dO V^T for its
+// next one; in its other phase it forms P and dZ of the item in between.  The
+// workgroup's K and V rows are staged once; each item's Q and dO rows, lse and
+// row terms come in by DMA into five stages (an item's rows are read for S
+// and dP at its half-step and, transposed, for dK and dV two half-steps
+// later).  Q and dO chunks are swizzled as in bwd_dq_dma_kernel's K, K and V
+// rows as c ^ (r & 15).  The arithmetic, and its order, is that of
+// bwd_dkdv_kernel, so the results are the same bits.
+__device__ __forceinline__ int dq_swz(int r) { return ((r & 3) << 2) | ((r >> 2) & 3); }
+
+constexpr int kDkStages = 5;
+
+struct alignas(16) DkdvSmem {
+  uint16_t kv[2][kKeyBlock * 128];   // K, V rows of the workgroup
+  uint16_t qs[kDkStages][32 * 128];  // Q rows of an item
+  uint16_t os[kDkStages][32 * 128];  // dO rows of an item
+  float lse[kDkStages][32];          // natural-log lse of the item's rows
+  float dts[kDkStages][32];          // row terms dO . O
+};
+
+template <int G>
+__global__ __launch_bounds__(kDkdvThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void bwd_dkdv_dma_kernel(
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
+    const float* __restrict__ key_score, const float* __restrict__ tau, const float* __restrict__ gain,
+    const tg_segment* __restrict__ segs, int hq, int hkv, const uint16_t* __restrict__ dout,
+    const float* __restrict__ lse, const float* __restrict__ dt, int n_chunks, int qc, float* __restrict__ dk_part,
+    float* __restrict__ dv_part, float* __restrict__ ds_part, int64_t total_kept, float* __restrict__ part_g,
+    float* __restrict__ part_t) {
+  constexpr int D = 128;
+  __shared__ DkdvSmem sm;
+  __shared__ float red[8][G][2];
+
+  const tg_segment seg = segs[blockIdx.z];
+  const int n = seg.kept_len;
+  const int ci = blockIdx.y % n_chunks;
+  const int kb0 = (blockIdx.y / n_chunks) * kKeyBlock;
+  if (kb0 >= n) return;  // uniform
+  const int c = blockIdx.x;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave8 = __builtin_amdgcn_readfirstlane(tid >> 6);  // 0..7
+  const int grp = tid >> 8;
+  const int wave = __builtin_amdgcn_readfirstlane((tid & 255) >> 6);  // wave inside its group = key slot
+  const int g = lane >> 5, l32 = lane & 31;
+  const int kw0 = kb0 + 32 * wave;  // first key of this wave
+  const int kj = kw0 + l32;         // the key this lane owns
+  const bool key_ok = kj < n;
+  const int64_t base = seg.kept_start;
+  const int64_t q_stride = (int64_t)hq * D, kv_stride = (int64_t)hkv * D;
+  const uint32_t q_row_bytes = (uint32_t)q_stride * 2u, kv_row_bytes = (uint32_t)kv_stride * 2u;
+  const bool use_bias = key_score != nullptr && gain != nullptr;
+  // threads 0-255 stage Q and lse, 256-511 dO and the row terms (a wave-uniform value: the DMA operands are scalar)
+  const bool stage_q = __builtin_amdgcn_readfirstlane(tid >> 8) == 0;
+
+  // buffers: the workgroup's K / V rows of head c; the prompt's Q / dO rows and lse / row terms
+  const uint32_t kv_rows = (uint32_t)(n - kb0);
+  const __amdgpu_buffer_rsrc_t rk =
+      make_rsrc(k + (base + kb0) * kv_stride + (int64_t)c * D, kv_rows * kv_row_bytes - (uint32_t)c * D * 2u);
+  const __amdgpu_buffer_rsrc_t rv =
+      make_rsrc(v + (base + kb0) * kv_stride + (int64_t)c * D, kv_rows * kv_row_bytes - (uint32_t)c * D * 2u);
+  const __amdgpu_buffer_rsrc_t rq = make_rsrc(stage_q ? q + base * q_stride : dout + base * q_stride,
+                                              (uint32_t)n * q_row_bytes);
+  const __amdgpu_buffer_rsrc_t rl = make_rsrc(stage_q ? lse + base * hq : dt + base * hq, (uint32_t)n * (uint32_t)hq * 4u);
+
+  // K and V rows: 128 rows x 16 chunks each, 4 chunks per thread and tensor
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int p = (j * 8 + wave8) * 64 + lane;
+    const int r = p / 16, cc = p % 16;
+    const uint32_t off = (uint32_t)r * kv_row_bytes + (uint32_t)(cc ^ (r & 15)) * 16u;
+    dma16(rk, &sm.kv[0][(j * 8 + wave8) * 64 * 8], off, 0u);
+    dma16(rv, &sm.kv[1][(j * 8 + wave8) * 64 * 8], off, 0u);
+  }
+
+  // items (head, query block) of the chunk: it -> head it / nqb, block qb_begin + it % nqb
+  const int qb_begin = kb0 / 32 + ci * qc;
+  const int nqb = max(0, min(qb_begin + qc, (n + 31) / 32) - qb_begin);
+  const int total = G * nqb;
+  // Q (or dO) rows of item it into stage buf: 32 rows x 16 chunks, 2 chunks per staging lane; lse (or row terms)
+  // of its 32 rows from lanes 0-7 of each staging wave
+  uint32_t doff[2];
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const int p = (j * 4 + wave) * 64 + lane;
+    const int r = p / 16;
+    doff[j] = (uint32_t)r * q_row_bytes + (uint32_t)((p % 16) ^ dq_swz(r)) * 16u;
+  }
+  auto stage_item = [&](int it, int buf) {
+    const int h = c * G + it / nqb, q0 = 32 * (qb_begin + it % nqb);
+    uint16_t* dst = stage_q ? sm.qs[buf] : sm.os[buf];
+    const uint32_t soff = (uint32_t)q0 * q_row_bytes + (uint32_t)h * D * 2u;
+#pragma unroll
+    for (int j = 0; j < 2; ++j) dma16(rq, &dst[(j * 4 + wave) * 64 * 8], doff[j], soff);
+    float* ldst = stage_q ? sm.lse[buf] : sm.dts[buf];
+    if (lane < 8)
+      dma4(rl, &ldst[8 * wave], (uint32_t)(8 * wave + lane) * (uint32_t)hq * 4u, ((uint32_t)q0 * hq + h) * 4u);
+  };
+  if (total > 0) stage_item(0, 0);
+  if (total > 1) stage_item(1, 1);
+
+  // LDS element offsets of this lane's fragment reads.
+  // K / V rows (B operands of S and dP): key row 32 wave + l32, chunk 2 ks + g.
+  uint32_t kaddr[D / 16];
+#pragma unroll
+  for (int ks = 0; ks < D / 16; ++ks) {
+    const int r = 32 * wave + l32;
+    kaddr[ks] = (uint32_t)(r * D + (((2 * ks + g) ^ (r & 15)) * 8));
+  }
+  // Q / dO rows (A operands of S and dP): row l32, chunk 2 ks + g.
+  uint32_t raddr[D / 16];
+#pragma unroll
+  for (int ks = 0; ks < D / 16; ++ks) raddr[ks] = (uint32_t)(l32 * D + (((2 * ks + g) ^ dq_swz(l32)) * 8));
+  // Q^T / dO^T (A operands of dK and dV, transposing reads): as bwd_dq_dma_kernel's K^T, rows of a 16-query step.
+  uint32_t taddr[2][D / 32];
+  {
+    const int s2 = lane & 15, qg = lane >> 4;
+#pragma unroll
+    for (int hi = 0; hi < 2; ++hi) {
+      const int r = 8 * hi + 4 * g + (s2 >> 2);
+#pragma unroll
+      for (int dtile = 0; dtile < D / 32; ++dtile) {
+        const int cc = 4 * dtile + 2 * (qg & 1) + ((s2 & 3) >> 1);
+        taddr[hi][dtile] = (uint32_t)(r * D + ((cc ^ dq_swz(r)) * 8) + 4 * (s2 & 1));
+      }
+    }
+  }
+
+  const float s_key = use_bias && key_ok ? key_score[base + kj] : 0.0f;
+  f32x16 dkt[D / 32], dvt[D / 32];
+#pragma unroll
+  for (int dtile = 0; dtile < D / 32; ++dtile) {
+    dkt[dtile] = f32x16{};
+    dvt[dtile] = f32x16{};
+  }
+  float ds_acc = 0.0f;
+  float dg_acc[G], dtau_acc[G];
+#pragma unroll
+  for (int gg = 0; gg < G; ++gg) dg_acc[gg] = dtau_acc[gg] = 0.0f;
+  const float inv_sqrt_d = 1.0f / __builtin_sqrtf((float)D);
+  f32x16 sacc, dpacc;
+  u32x4 pb[2], zb[2];
+
+  if (total > 1)
+    wait_vm<3>();  // K, V and item 0 landed; item 1 may be in flight
+  else
+    wait_vm<0>();
+  lds_barrier();
+
+  auto item_q0 = [&](int it) { return 32 * (qb_begin + it % nqb); };
+  auto half_step = [&](int hs, auto p_) {
+    constexpr int P = decltype(p_)::value;
+    const bool dma_now = hs + 2 < total;
+    if (dma_now && !stage_q) stage_item(hs + 2, (hs + 2) % kDkStages);  // dO of item hs + 2 at the start
+    if (P == grp) {
+      const int jp = hs - 2;  // dV, dK of item jp
+      if (jp >= 0 && kw0 <= item_q0(jp) + 31) {
+        const int b = jp % kDkStages;
+        const uint16_t* ot = sm.os[b];
+        const uint16_t* qt = sm.qs[b];
+        typedef short short4v __attribute__((ext_vector_type(4)));
+#pragma unroll
+        for (int st = 0; st < 2; ++st) {
+#pragma unroll
+          for (int dtile = 0; dtile < D / 32; ++dtile) {
+            const short4v olo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                (__attribute__((address_space(3))) short4v*)(ot + taddr[0][dtile] + 16 * st * D));
+            const short4v ohi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                (__attribute__((address_space(3))) short4v*)(ot + taddr[1][dtile] + 16 * st * D));
+            const short4v qlo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                (__attribute__((address_space(3))) short4v*)(qt + taddr[0][dtile] + 16 * st * D));
+            const short4v qhi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                (__attribute__((address_space(3))) short4v*)(qt + taddr[1][dtile] + 16 * st * D));
+            const u32x2 o2l = __builtin_bit_cast(u32x2, olo), o2h = __builtin_bit_cast(u32x2, ohi);
+            const u32x2 q2l = __builtin_bit_cast(u32x2, qlo), q2h = __builtin_bit_cast(u32x2, qhi);
+            dvt[dtile] = mfma32(u32x4{o2l[0], o2l[1], o2h[0], o2h[1]}, pb[st], dvt[dtile]);
+            dkt[dtile] = mfma32(u32x4{q2l[0], q2l[1], q2h[0], q2h[1]}, zb[st], dkt[dtile]);
+          }
+        }
+        sched_two_reads_ahead<2 * 2 * (D / 32), 8>();
+      }
+      const int jq = hs;  // S, dP of item jq
+      if (jq < total && kw0 <= item_q0(jq) + 31) {
+        const int b = jq % kDkStages;
+        const uint16_t* qr = sm.qs[b];
+        const uint16_t* orr = sm.os[b];
+        const uint16_t* kt = sm.kv[0];
+        const uint16_t* vt = sm.kv[1];
+        sacc = f32x16{};
+        dpacc = f32x16{};
+#pragma unroll
+        for (int ks = 0; ks < D / 16; ++ks) {
+          sacc = mfma32(*reinterpret_cast<const u32x4*>(qr + raddr[ks]), *reinterpret_cast<const u32x4*>(kt + kaddr[ks]),
+                        sacc);
+          dpacc = mfma32(*reinterpret_cast<const u32x4*>(orr + raddr[ks]),
+                         *reinterpret_cast<const u32x4*>(vt + kaddr[ks]), dpacc);
+        }
+        sched_two_reads_ahead<2 * (D / 16), 8>();
+      }
+    } else {
+      const int js = hs - 1;  // P and dZ of item js
+      if (js >= 0 && js < total && kw0 <= item_q0(js) + 31) {
+        const int b = js % kDkStages;
+        const int gg = js / nqb, q0 = item_q0(js);
+        const int h = c * G + gg;
+        const float th = tau != nullptr ? tau[h] : 1.0f;
+        const float scale2 = th * kL2e * inv_sqrt_d;  // exp2-domain logit per unit q.k
+        const float dscale = th * inv_sqrt_d;         // dZ -> dQ, dK factor
+        const float gh = use_bias ? gain[h] : 0.0f;
+        const float bias2 = gh * kL2e * s_key;        // exp2-domain bias of the lane's key
+        // register i holds query row q0 + c_row(i, g), key kj
+        float pz[16], dz[16];
+        float dg_i = 0.0f, dtau_i = 0.0f;
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4) {
+          const f32x4 l4r = *reinterpret_cast<const f32x4*>(&sm.lse[b][8 * q4 + 4 * g]);
+          const f32x4 d4r = *reinterpret_cast<const f32x4*>(&sm.dts[b][8 * q4 + 4 * g]);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int i = 4 * q4 + e;
+            const int row = q0 + c_row(i, g);
+            const bool ok = key_ok && kj <= row && row < n;
+            const float l4 = row < n ? l4r[e] * kL2e : __builtin_inff();
+            const float d4 = row < n ? d4r[e] : 0.0f;
+            const float p = ok ? __builtin_amdgcn_exp2f(__builtin_fmaf(scale2, sacc[i], bias2) - l4) : 0.0f;
+            const float z = p * (dpacc[i] - d4);
+            pz[i] = p;
+            dz[i] = z;
+            ds_acc = __builtin_fmaf(gh, z, ds_acc);
+            dg_i = __builtin_fmaf(z, s_key, dg_i);
+            dtau_i = __builtin_fmaf(z, sacc[i] * inv_sqrt_d, dtau_i);
+          }
+        }
+#pragma unroll
+        for (int hh = 0; hh < G; ++hh) {
+          if (hh == gg) {
+            dg_acc[hh] += dg_i;
+            dtau_acc[hh] += dtau_i;
+          }
+        }
+#pragma unroll
+        for (int st = 0; st < 2; ++st)
+#pragma unroll
+          for (int jj = 0; jj < 4; ++jj) {
+            const int i = 8 * st + 2 * jj;
+            pb[st][jj] = pack2(pz[i], pz[i + 1]);
+            zb[st][jj] = pack2(dz[i] * dscale, dz[i + 1] * dscale);
+          }
+      }
+    }
+    if (dma_now && stage_q) stage_item(hs + 2, (hs + 2) % kDkStages);  // Q of item hs + 2 at the end
+    // item hs + 1 (issued one half-step ago) must have landed; this half-step's DMAs may stay in flight
+    if (dma_now)
+      wait_vm<3>();
+    else
+      wait_vm<0>();
+    lds_barrier();
+  };
+  for (int hs = 0; hs < total + 2; hs += 2) {
+    half_step(hs, std::integral_constant<int, 0>());
+    if (hs + 1 < total + 2) half_step(hs + 1, std::integral_constant<int, 1>());
+  }
+
+  // per-head dg / dtau of the wave
+#pragma unroll
+  for (int gg = 0; gg < G; ++gg) {
+    const float a = wave_sum(dg_acc[gg]), b = wave_sum(dtau_acc[gg]);
+    if (lane == 0) {
+      red[wave8][gg][0] = a;
+      red[wave8][gg][1] = b;
+    }
+  }
+  // group 1 hands its dK, dV and ds to group 0 through LDS (the stages are free now: the last half-step ended
+  // with a barrier), which adds them in a fixed order
+  constexpr int kRec = D * 32 * 2 + 64;  // floats per wave: dK^T, dV^T, ds
+  float* xo = reinterpret_cast<float*>(&sm);
+  static_assert(4 * kRec * 4 <= sizeof(DkdvSmem), "group exchange fits in LDS");
+  float* rec = xo + wave * kRec;
+  if (grp == 1) {
+#pragma unroll
+    for (int dtile = 0; dtile < D / 32; ++dtile)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        rec[((2 * dtile) * 16 + i) * 64 + lane] = dkt[dtile][i];
+        rec[((2 * dtile + 1) * 16 + i) * 64 + lane] = dvt[dtile][i];
+      }
+    rec[D * 32 * 2 + lane] = ds_acc;
+  }
+  __syncthreads();
+  if (grp == 0) {
+#pragma unroll
+    for (int dtile = 0; dtile < D / 32; ++dtile)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        dkt[dtile][i] += rec[((2 * dtile) * 16 + i) * 64 + lane];
+        dvt[dtile][i] += rec[((2 * dtile + 1) * 16 + i) * 64 + lane];
+      }
+    ds_acc += rec[D * 32 * 2 + lane];
+    // dK, dV of the lane's key: register i of tile t holds dim 32 t + c_row(i, g)
+    if (key_ok) {
+      const int64_t prow = ((int64_t)ci * total_kept + base + kj) * kv_stride + (int64_t)c * D;
+      float* dkr = dk_part + prow;
+      float* dvr = dv_part + prow;
+#pragma unroll
+      for (int dtile = 0; dtile < D / 32; ++dtile)
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4) {
+          const int d0 = 32 * dtile + 8 * q4 + 4 * g;
+          *reinterpret_cast<f32x4*>(dkr + d0) =
+              f32x4{dkt[dtile][4 * q4], dkt[dtile][4 * q4 + 1], dkt[dtile][4 * q4 + 2], dkt[dtile][4 * q4 + 3]};
+          *reinterpret_cast<f32x4*>(dvr + d0) =
+              f32x4{dvt[dtile][4 * q4], dvt[dtile][4 * q4 + 1], dvt[dtile][4 * q4 + 2], dvt[dtile][4 * q4 + 3]};
+        }
+    }
+    const float ds_key = xor32_sum(ds_acc);  // the two half-waves hold different query rows
+    if (key_ok && g == 0) ds_part[((int64_t)ci * hkv + c) * total_kept + base + kj] = ds_key;
+  }
+  if (tid < G) {
+    const int64_t slot = (int64_t)blockIdx.z * gridDim.y + blockIdx.y;
+    float sg = 0.0f, st = 0.0f;
+#pragma unroll
+    for (int w = 0; w < 8; ++w) {
+      sg += red[w][tid][0];
+      st += red[w][tid][1];
+    }
+    part_g[slot * hq + c * G + tid] = sg;
+    part_t[slot * hq + c * G + tid] = st;
+  }
+}
+
 template <int D>
 struct KeyTile {
   static constexpr int kLd = D + 8;       // K, V row-major
@@ -534,7 +867,6 @@ struct alignas(16) DqSmem {
   float s[kDqK][kTile];  // key scores, with their K tile
 };
 
-__device__ __forceinline__ int dq_swz(int r) { return ((r & 3) << 2) | ((r >> 2) & 3); }
 
 template <int G>
 __global__ __launch_bounds__(kDqThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void bwd_dq_dma_kernel(
@@ -919,13 +1251,21 @@ hipError_t launch_bwd_dg(const void* q, const void* k, const void* v, const floa
     const int per_block = kBwdThreads / (D / 8);
     hipLaunchKernelGGL((bwd_rowdot_kernel<D>), dim3((unsigned)((rows + per_block - 1) / per_block)),
                        dim3(kBwdThreads), 0, stream, dob, ob, rows, w.dt);
-    hipLaunchKernelGGL((bwd_dkdv_kernel<D, G>), dim3(hkv, geo.key_blocks * geo.n_chunks, info.n_seg),
-                       dim3(kDkdvThreads), 0, stream, qb, kb, vb, ks, tau, gain, segs, hq, hkv, dob, lse, w.dt,
-                       geo.n_chunks, geo.qc, w.dk_part, w.dv_part, w.ds_part, info.total_kept, w.part_g, w.part_t);
+    // the DMA kernels address a prompt's rows with 32-bit buffer ranges (Q / dO: hq heads per row)
+    const bool kv_fits = (int64_t)info.max_kept_len * hkv * D * 2 < 0xffffff00LL;
+    const bool q_fits = (int64_t)info.max_kept_len * hq * D * 4 < 0xffffff00LL;
+    if (D == 128 && kv_fits && q_fits)
+      hipLaunchKernelGGL((bwd_dkdv_dma_kernel<G>), dim3(hkv, geo.key_blocks * geo.n_chunks, info.n_seg),
+                         dim3(kDkdvThreads), 0, stream, qb, kb, vb, ks, tau, gain, segs, hq, hkv, dob, lse, w.dt,
+                         geo.n_chunks, geo.qc, w.dk_part, w.dv_part, w.ds_part, info.total_kept, w.part_g, w.part_t);
+    else
+      hipLaunchKernelGGL((bwd_dkdv_kernel<D, G>), dim3(hkv, geo.key_blocks * geo.n_chunks, info.n_seg),
+                         dim3(kDkdvThreads), 0, stream, qb, kb, vb, ks, tau, gain, segs, hq, hkv, dob, lse, w.dt,
+                         geo.n_chunks, geo.qc, w.dk_part, w.dv_part, w.ds_part, info.total_kept, w.part_g, w.part_t);
     constexpr int kBM = 128 / G;
     const int q_tiles = (int)((info.max_kept_len + kBM - 1) / kBM);
     // the DMA kernel addresses a prompt's K / V rows with 32-bit buffer ranges
-    const bool dq_dma = D == 128 && (int64_t)info.max_kept_len * hkv * D * 2 < 0xffffff00LL;
+    const bool dq_dma = D == 128 && kv_fits;
     if (dq_dma)
       hipLaunchKernelGGL((bwd_dq_dma_kernel<G>), dim3(hkv, q_tiles, info.n_seg), dim3(kDqThreads), 0, stream, qb, kb,
                          vb, ks, tau, gain, segs, hq, hkv, dob, lse, w.dt, dq);
