@@ -102,10 +102,11 @@ class Pipeline:
             ("select", lambda: tg.select_topk(self.scores, self.plan, kept_idx=self.kept, workspace=self.sws)),
             ("compact", lambda: tg.compact_kept(self.kept, self.pairs)),
             ("attention", (lambda: tg.gated_attention_prefill_gather(
-                self.q, self.k, self.v, self.scores, self.tau, self.gain, self.plan, self.kept, out=self.out))
+                self.q, self.k, self.v, self.scores, self.tau, self.gain, self.plan, self.kept, out=self.out,
+                workspace=self.aws))
              if self.gather else
              (lambda: tg.gated_attention_prefill_query_tau(self.qc, self.kc, self.vc, self.sc, self.sigma, self.gain,
-                                                           self.pc, self.plan, out=self.out))
+                                                           self.pc, self.plan, out=self.out, workspace=self.aws))
              if self.query_tau else
              (lambda: tg.gated_attention_prefill(self.qc, self.kc, self.vc, self.sc, self.tau, self.gain, self.plan,
                                                  out=self.out, workspace=self.aws))),

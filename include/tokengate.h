@@ -267,6 +267,14 @@ int tg_gated_attention_prefill_gather(const void* q, const void* k, const void* 
                                       const float* tau, const float* gain, const tg_segment* segs,
                                       const tg_plan_info* info, int hq, int hkv, int head_dim,
                                       const int32_t* kept_idx, int64_t n_src_rows, void* out, void* stream);
+/* tg_gated_attention_prefill_gather with the split-tile workspace of
+ * tg_gated_attention_prefill_ws (same sizing, zero-fill, reuse and error
+ * rules; outputs equal to the gather call up to fp32 rounding of the merge). */
+int tg_gated_attention_prefill_gather_ws(const void* q, const void* k, const void* v, const float* key_score,
+                                         const float* tau, const float* gain, const tg_segment* segs,
+                                         const tg_plan_info* info, int hq, int hkv, int head_dim,
+                                         const int32_t* kept_idx, int64_t n_src_rows, void* out, void* workspace,
+                                         size_t workspace_bytes, void* stream);
 
 /* The same attention with a temperature per query row ([reading] section 4.1
  * component two, second refinement: pruning shrinks the keys a query sees
@@ -287,6 +295,14 @@ int tg_gated_attention_prefill_query_tau(const void* q, const void* k, const voi
                                          const float* sigma, const float* gain, const int32_t* positions,
                                          const tg_segment* segs, const tg_plan_info* info, int hq, int hkv,
                                          int head_dim, void* out, void* stream);
+/* tg_gated_attention_prefill_query_tau with the split-tile workspace of
+ * tg_gated_attention_prefill_ws (same sizing, zero-fill, reuse and error
+ * rules). */
+int tg_gated_attention_prefill_query_tau_ws(const void* q, const void* k, const void* v, const float* key_score,
+                                            const float* sigma, const float* gain, const int32_t* positions,
+                                            const tg_segment* segs, const tg_plan_info* info, int hq, int hkv,
+                                            int head_dim, void* out, void* workspace, size_t workspace_bytes,
+                                            void* stream);
 
 /* ------------------------------------------------------------------------ */
 /* (4a) Token-gated attention, backward                                     */

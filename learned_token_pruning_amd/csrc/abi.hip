@@ -240,6 +240,18 @@ int tg_gated_attention_prefill(const void* q, const void* k, const void* v, cons
                                                reinterpret_cast<hipStream_t>(stream)));
 }
 
+namespace {
+// The split-tile workspace of an attention call: TG_ERR_WORKSPACE when one is needed and missing, misaligned or
+// short; *use = the workspace, or nullptr when no tile is split.
+int split_workspace(const tg_plan_info* info, int hq, int hkv, int head_dim, void* workspace, size_t workspace_bytes,
+                    void** use) {
+  const size_t need = tg::attention_prefill_workspace_bytes(*info, hq, hkv, head_dim);
+  if (need > 0 && (!workspace || !aligned(workspace, 256) || workspace_bytes < need)) return TG_ERR_WORKSPACE;
+  *use = need > 0 ? workspace : nullptr;
+  return TG_OK;
+}
+}  // namespace
+
 size_t tg_attention_prefill_workspace_bytes(const tg_plan_info* info, int hq, int hkv, int head_dim) {
   if (!info || hq <= 0 || hkv <= 0 || head_dim <= 0 || info->n_seg < 1 || info->total_kept < 0) return 0;
   return tg::attention_prefill_workspace_bytes(*info, hq, hkv, head_dim);
@@ -258,17 +270,20 @@ int tg_gated_attention_prefill_ws(const void* q, const void* k, const void* v, c
   if (info->total_kept == 0) return TG_OK;
   st = check_device();
   if (st != TG_OK) return st;
-  const size_t need = tg::attention_prefill_workspace_bytes(*info, hq, hkv, head_dim);
-  if (need > 0 && (!workspace || !aligned(workspace, 256) || workspace_bytes < need)) return TG_ERR_WORKSPACE;
+  void* split_ws = nullptr;
+  if ((st = split_workspace(info, hq, hkv, head_dim, workspace, workspace_bytes, &split_ws)) != TG_OK) return st;
   return hip_status(tg::launch_gated_attention(q, k, v, key_score, tau, gain, segs, *info, hq, hkv, head_dim,
                                                nullptr, 0, nullptr, nullptr, out,
-                                               reinterpret_cast<hipStream_t>(stream), need > 0 ? workspace : nullptr));
+                                               reinterpret_cast<hipStream_t>(stream), split_ws));
 }
 
-int tg_gated_attention_prefill_query_tau(const void* q, const void* k, const void* v, const float* key_score,
+namespace {
+// with_ws: the _ws entry point (workspace checked and passed on; split query tiles allowed)
+int query_tau_impl(const void* q, const void* k, const void* v, const float* key_score,
                                          const float* sigma, const float* gain, const int32_t* positions,
                                          const tg_segment* segs, const tg_plan_info* info, int hq, int hkv,
-                                         int head_dim, void* out, void* stream) {
+                                         int head_dim, void* out, bool with_ws, void* workspace, size_t workspace_bytes,
+                                         void* stream) {
   if (!sigma) return TG_ERR_INVALID_ARG;
   int st = check_attention_shapes(segs, info, hq, hkv, head_dim, true);
   if (st != TG_OK) return st;
@@ -280,15 +295,38 @@ int tg_gated_attention_prefill_query_tau(const void* q, const void* k, const voi
   if (info->total_kept == 0) return TG_OK;
   st = check_device();
   if (st != TG_OK) return st;
+  void* split_ws = nullptr;
+  if (with_ws && (st = split_workspace(info, hq, hkv, head_dim, workspace, workspace_bytes, &split_ws)) != TG_OK)
+    return st;
   return hip_status(tg::launch_gated_attention(q, k, v, key_score, sigma, gain, segs, *info, hq, hkv, head_dim,
                                                nullptr, 0, positions, nullptr, out,
-                                               reinterpret_cast<hipStream_t>(stream)));
+                                               reinterpret_cast<hipStream_t>(stream), split_ws));
+}
+}  // namespace
+
+int tg_gated_attention_prefill_query_tau(const void* q, const void* k, const void* v, const float* key_score,
+                                         const float* sigma, const float* gain, const int32_t* positions,
+                                         const tg_segment* segs, const tg_plan_info* info, int hq, int hkv,
+                                         int head_dim, void* out, void* stream) {
+  return query_tau_impl(q, k, v, key_score, sigma, gain, positions, segs, info, hq, hkv, head_dim, out, false,
+                        nullptr, 0, stream);
 }
 
-int tg_gated_attention_prefill_gather(const void* q, const void* k, const void* v, const float* key_score,
+int tg_gated_attention_prefill_query_tau_ws(const void* q, const void* k, const void* v, const float* key_score,
+                                            const float* sigma, const float* gain, const int32_t* positions,
+                                            const tg_segment* segs, const tg_plan_info* info, int hq, int hkv,
+                                            int head_dim, void* out, void* workspace, size_t workspace_bytes,
+                                            void* stream) {
+  return query_tau_impl(q, k, v, key_score, sigma, gain, positions, segs, info, hq, hkv, head_dim, out, true,
+                        workspace, workspace_bytes, stream);
+}
+
+namespace {
+int gather_impl(const void* q, const void* k, const void* v, const float* key_score,
                                       const float* tau, const float* gain, const tg_segment* segs,
                                       const tg_plan_info* info, int hq, int hkv, int head_dim,
-                                      const int32_t* kept_idx, int64_t n_src_rows, void* out, void* stream) {
+                                      const int32_t* kept_idx, int64_t n_src_rows, void* out, bool with_ws,
+                                      void* workspace, size_t workspace_bytes, void* stream) {
   int st = check_info(segs, info);
   if (st != TG_OK) return st;
   if (hq <= 0 || hkv <= 0 || head_dim <= 0 || n_src_rows < 0) return TG_ERR_INVALID_ARG;
@@ -307,9 +345,30 @@ int tg_gated_attention_prefill_gather(const void* q, const void* k, const void* 
   if (info->total_kept == 0) return TG_OK;
   st = check_device();
   if (st != TG_OK) return st;
+  void* split_ws = nullptr;
+  if (with_ws && (st = split_workspace(info, hq, hkv, head_dim, workspace, workspace_bytes, &split_ws)) != TG_OK)
+    return st;
   return hip_status(tg::launch_gated_attention(q, k, v, key_score, tau, gain, segs, *info, hq, hkv, head_dim,
                                                kept_idx, n_src_rows, nullptr, nullptr, out,
-                                               reinterpret_cast<hipStream_t>(stream)));
+                                               reinterpret_cast<hipStream_t>(stream), split_ws));
+}
+}  // namespace
+
+int tg_gated_attention_prefill_gather(const void* q, const void* k, const void* v, const float* key_score,
+                                      const float* tau, const float* gain, const tg_segment* segs,
+                                      const tg_plan_info* info, int hq, int hkv, int head_dim,
+                                      const int32_t* kept_idx, int64_t n_src_rows, void* out, void* stream) {
+  return gather_impl(q, k, v, key_score, tau, gain, segs, info, hq, hkv, head_dim, kept_idx, n_src_rows, out, false,
+                     nullptr, 0, stream);
+}
+
+int tg_gated_attention_prefill_gather_ws(const void* q, const void* k, const void* v, const float* key_score,
+                                         const float* tau, const float* gain, const tg_segment* segs,
+                                         const tg_plan_info* info, int hq, int hkv, int head_dim,
+                                         const int32_t* kept_idx, int64_t n_src_rows, void* out, void* workspace,
+                                         size_t workspace_bytes, void* stream) {
+  return gather_impl(q, k, v, key_score, tau, gain, segs, info, hq, hkv, head_dim, kept_idx, n_src_rows, out, true,
+                     workspace, workspace_bytes, stream);
 }
 
 

@@ -33,6 +33,7 @@ EXPORTS = ("tg_status_string", "tg_abi_version", "tg_plan_segments", "tg_gate_wo
            "tg_gate_packed_w1_bytes", "tg_gate_pack_w1", "tg_gate_score_prepacked",
            "tg_select_workspace_bytes", "tg_select_topk", "tg_compact_kept", "tg_gated_attention_prefill",
            "tg_attention_prefill_workspace_bytes", "tg_gated_attention_prefill_ws",
+           "tg_gated_attention_prefill_gather_ws", "tg_gated_attention_prefill_query_tau_ws",
            "tg_gated_attention_prefill_gather", "tg_gated_attention_prefill_query_tau",
            "tg_decode_workspace_bytes", "tg_gated_attention_decode", "tg_gated_attention_prefill_lse",
            "tg_attention_backward_workspace_bytes", "tg_gated_attention_backward",
@@ -98,6 +99,13 @@ _lib.tg_compact_kept.argtypes = [_vp, _i64, _i64, _i32, ctypes.POINTER(_vp), cty
 _lib.tg_gated_attention_prefill_gather.restype = _i32
 _lib.tg_gated_attention_prefill_gather.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, ctypes.POINTER(PlanInfo), _i32,
                                                    _i32, _i32, _vp, _i64, _vp, _vp]
+_lib.tg_gated_attention_prefill_gather_ws.restype = _i32
+_lib.tg_gated_attention_prefill_gather_ws.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, ctypes.POINTER(PlanInfo),
+                                                      _i32, _i32, _i32, _vp, _i64, _vp, _vp, _sz, _vp]
+_lib.tg_gated_attention_prefill_query_tau_ws.restype = _i32
+_lib.tg_gated_attention_prefill_query_tau_ws.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
+                                                         ctypes.POINTER(PlanInfo), _i32, _i32, _i32, _vp, _vp, _sz,
+                                                         _vp]
 _lib.tg_gated_attention_prefill_query_tau.restype = _i32
 _lib.tg_gated_attention_prefill_query_tau.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, ctypes.POINTER(PlanInfo),
                                                       _i32, _i32, _i32, _vp, _vp]
@@ -355,13 +363,22 @@ def gated_attention_prefill(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, k
 def gated_attention_prefill_gather(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
                                    key_score: Optional[torch.Tensor], tau: Optional[torch.Tensor],
                                    gain: Optional[torch.Tensor], plan: Plan, kept_idx: torch.Tensor,
-                                   out: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+                                   out: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
+                                   stream=None) -> torch.Tensor:
     """tg_gated_attention_prefill_gather.  q [N, hq, D], k/v [N, hkv, D] bf16
-    contiguous over every token; kept_idx int32 [M]; returns out [M, hq, D]."""
+    contiguous over every token; kept_idx int32 [M]; returns out [M, hq, D].  With a
+    workspace (attention_prefill_workspace) it calls tg_gated_attention_prefill_gather_ws."""
     n_src, hq, dh = q.shape
     hkv = k.shape[1]
     if out is None:
         out = torch.empty((plan.total_kept, hq, dh), dtype=q.dtype, device=q.device)
+    if workspace is not None:
+        st = _lib.tg_gated_attention_prefill_gather_ws(_ptr(q), _ptr(k), _ptr(v), _ptr(key_score), _ptr(tau),
+                                                       _ptr(gain), _dev_table(plan), ctypes.byref(plan.info), hq,
+                                                       hkv, dh, _ptr(kept_idx), n_src, _ptr(out), _ptr(workspace),
+                                                       workspace.numel() * workspace.element_size(), _stream(stream))
+        _check(st, "tg_gated_attention_prefill_gather_ws")
+        return out
     st = _lib.tg_gated_attention_prefill_gather(_ptr(q), _ptr(k), _ptr(v), _ptr(key_score), _ptr(tau), _ptr(gain),
                                                 _dev_table(plan), ctypes.byref(plan.info), hq, hkv, dh,
                                                 _ptr(kept_idx), n_src, _ptr(out), _stream(stream))
@@ -372,13 +389,24 @@ def gated_attention_prefill_gather(q: torch.Tensor, k: torch.Tensor, v: torch.Te
 def gated_attention_prefill_query_tau(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
                                       key_score: Optional[torch.Tensor], sigma: torch.Tensor,
                                       gain: Optional[torch.Tensor], positions: torch.Tensor, plan: Plan,
-                                      out: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+                                      out: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
+                                      stream=None) -> torch.Tensor:
     """tg_gated_attention_prefill_query_tau.  As gated_attention_prefill, with
-    sigma fp32 [hq] and positions int32 [M] (original positions of the kept rows)."""
+    sigma fp32 [hq] and positions int32 [M] (original positions of the kept rows).  With a
+    workspace (attention_prefill_workspace) it calls tg_gated_attention_prefill_query_tau_ws."""
     m, hq, dh = q.shape
     hkv = k.shape[1]
     if out is None:
         out = torch.empty_like(q)
+    if workspace is not None:
+        st = _lib.tg_gated_attention_prefill_query_tau_ws(_ptr(q), _ptr(k), _ptr(v), _ptr(key_score), _ptr(sigma),
+                                                          _ptr(gain), _ptr(positions), _dev_table(plan),
+                                                          ctypes.byref(plan.info), hq, hkv, dh, _ptr(out),
+                                                          _ptr(workspace),
+                                                          workspace.numel() * workspace.element_size(),
+                                                          _stream(stream))
+        _check(st, "tg_gated_attention_prefill_query_tau_ws")
+        return out
     st = _lib.tg_gated_attention_prefill_query_tau(_ptr(q), _ptr(k), _ptr(v), _ptr(key_score), _ptr(sigma),
                                                    _ptr(gain), _ptr(positions), _dev_table(plan),
                                                    ctypes.byref(plan.info), hq, hkv, dh, _ptr(out), _stream(stream))

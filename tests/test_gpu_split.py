@@ -197,3 +197,45 @@ def test_split_batch_not_split():
     b = tg.gated_attention_prefill(*args)
     torch.cuda.synchronize()
     assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+
+
+@pytest.mark.parametrize("d,hq,hkv,n", [(128, 16, 8, 2112), (64, 8, 2, 1000)])
+def test_split_gather_and_query_tau(d, hq, hkv, n):
+    """Gather on load with split tiles equals the compacted split path bit for bit (as without splitting); the
+    per-query temperature with split tiles is deterministic and matches the oracle."""
+    import torch
+    _say("split gather / query tau", d, hq, hkv, n)
+    tg = _tg()
+    rng = np.random.default_rng(d + n)
+    n_src = n + 500
+    q, k, v, s, tau, gain = random_inputs(d + hq + n, n_src, hq, hkv, d)
+    idx = np.sort(rng.choice(n_src, n, replace=False)).astype(np.int32)
+    plan, offs = plan_of(tg, [n])
+    assert tg.attention_prefill_workspace_bytes(plan, hq, hkv, d) > 0
+    ws = tg.attention_prefill_workspace(plan, hq, hkv, d, "cuda")
+    qd, kd, vd, sd = dev_bf16(q), dev_bf16(k), dev_bf16(v), dev_f32(s)
+    tt, gg = dev_f32(tau), dev_f32(gain)
+    kept = torch.from_numpy(idx).cuda()
+    got_g = tg.gated_attention_prefill_gather(qd, kd, vd, sd, tt, gg, plan, kept, workspace=ws)
+    qc, kc, vc, sc = (torch.index_select(t, 0, kept.long()).contiguous() for t in (qd, kd, vd, sd))
+    got_c = tg.gated_attention_prefill(qc, kc, vc, sc, tt, gg, plan, workspace=ws)
+    torch.cuda.synchronize()
+    assert torch.equal(got_g.view(torch.int16), got_c.view(torch.int16))
+    assert counters_zero(ws, tg.attention_prefill_workspace_bytes(plan, hq, hkv, d), d)
+    # per-query temperature: original positions spread over a prompt about four times longer
+    pos = np.sort(rng.choice(4 * n, n, replace=False)).astype(np.int32)
+    sigma = rng.uniform(0.5, 1.5, hq).astype(np.float32)
+    pd = torch.from_numpy(pos).cuda()
+    outs = [tg.gated_attention_prefill_query_tau(qc, kc, vc, sc, dev_f32(sigma), gg, pd, plan, workspace=ws)
+            for _ in range(4)]
+    plain = tg.gated_attention_prefill_query_tau(qc, kc, vc, sc, dev_f32(sigma), gg, pd, plan)
+    torch.cuda.synchronize()
+    for o in outs[1:]:
+        assert torch.equal(o.view(torch.int16), outs[0].view(torch.int16))
+    assert (outs[0].float() - plain.float()).abs().max().item() <= ATTN_ATOL
+    rows = np.unique(np.concatenate([[0, 1, 63, 64, n - 2, n - 1], rng.integers(0, n, 150)]))
+    tq = oracle.query_temperature(sigma.astype(np.float64), pos.astype(np.int64), offs)
+    ref = oracle.gated_attention(W.bf16_bits_to_f64(q[idx]), W.bf16_bits_to_f64(k[idx]), W.bf16_bits_to_f64(v[idx]),
+                                 s[idx].astype(np.float64), tq, gain.astype(np.float64), offs, rows=rows)
+    got = W.bf16_bits_to_f64(host_bf16(outs[0]))[rows]
+    assert np.abs(got - ref).max() <= ATTN_ATOL
