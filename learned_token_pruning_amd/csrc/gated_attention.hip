@@ -621,14 +621,16 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
 // The same schedule, but K, V and the key scores go from global memory straight
 // into LDS (buffer loads with the LDS destination), so no staging registers and
 // no LDS store instructions.  Three LDS stages per operand.  In half-step hs
-// the V waves issue the DMA of V tile hs at the start and the K waves that of
-// K tile hs + 2 (with its scores) at the end, each into a stage nobody reads
-// during hs (of the placements measured, this one spreads the per-CU load
-// traffic best: 5-7 % faster than issuing both at the start).  Every wave
-// waits (vmcnt) for its previous half-step's DMAs before the barrier that ends
-// the half-step, so V has about two half-steps to land and K one.  The
-// barriers are plain s_barrier with explicit waits: a workgroup fence would
-// also wait for the DMAs just issued.
+// the group in its softmax phase issues the DMAs of V tile hs and of K tile
+// hs + 2 (with its scores) at the start, each into a stage nobody reads during
+// hs; the MFMA-phase group issues none, so the issue of the DMAs (which can
+// stall while the memory pipeline takes them) overlaps exp2 and VALU work
+// instead of delaying matrix work (2-4 % faster than V waves issuing V at the
+// start of every half-step and K waves K at its end).  A group waits (vmcnt 0)
+// for the DMAs it issued one half-step before at the end of its MFMA phase,
+// so every tile has about two half-steps to land.  The barriers are plain
+// s_barrier with explicit waits: a workgroup fence would also wait for the
+// DMAs just issued.
 //
 // Both tiles are row-major with their 16-byte chunks swizzled per row, for
 // the 256-byte (64-bank) LDS cycle of gfx950.  K: chunk c of row r sits at
@@ -728,17 +730,19 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
   const __amdgpu_buffer_rsrc_t rk = make_rsrc(kb, nrows * row_bytes - (uint32_t)c * D * 2u);
   const __amdgpu_buffer_rsrc_t rv = make_rsrc(vb, nrows * row_bytes - (uint32_t)c * D * 2u);
   const __amdgpu_buffer_rsrc_t rs = make_rsrc(use_bias ? key_score + row0 : key_score, use_bias ? nrows * 4u : 0u);
-  const bool stage_k = grp == 0;  // threads 0-255 stage K and the scores, 256-511 V
+  const bool stage_k = grp == 0;  // threads 0-255 stage the first two K tiles
 
-  // DMA source offsets inside a tile: chunk slot (j 4 + wave) 64 + lane holds row drow[j], chunk dcol[j]
+  // DMA source offsets inside a tile: chunk slot (j 4 + wave) 64 + lane holds row drow[j], chunk dcolk[j] (K)
+  // or dcolv[j] (V); every wave stages both tensors
   int drow[NJ];
-  uint32_t dcol[NJ];
+  uint32_t dcolk[NJ], dcolv[NJ];
 #pragma unroll
   for (int j = 0; j < NJ; ++j) {
     const int p = (j * 4 + wave) * 64 + lane;
     const int r = p / NC;
     drow[j] = r;
-    dcol[j] = (uint32_t)((p % NC) ^ (stage_k ? kswz<D>(r) : vswz<D>(r))) * 16u;
+    dcolk[j] = (uint32_t)((p % NC) ^ kswz<D>(r)) * 16u;
+    dcolv[j] = (uint32_t)((p % NC) ^ vswz<D>(r)) * 16u;
   }
   // byte offset of a tile row in the K/V buffers (gathered: its source row; rows at or past q_end read as zeros)
   auto row_off = [&](int row) -> uint32_t {
@@ -751,13 +755,13 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
       const uint32_t soff = (uint32_t)(tile * kBN) * row_bytes;
 #pragma unroll
       for (int j = 0; j < NJ; ++j)
-        dma16(rk, &sm.k[buf][(j * 4 + wave) * 64 * 8], (uint32_t)drow[j] * row_bytes + dcol[j], soff);
+        dma16(rk, &sm.k[buf][(j * 4 + wave) * 64 * 8], (uint32_t)drow[j] * row_bytes + dcolk[j], soff);
       if (lane < 16) dma4(rs, &sm.s[buf][16 * wave], (uint32_t)(16 * wave + lane) * 4u, (uint32_t)(tile * kBN) * 4u);
     } else {
 #pragma unroll
       for (int j = 0; j < NJ; ++j) {
         const uint32_t ro = row_off(tile * kBN + drow[j]);
-        dma16(rk, &sm.k[buf][(j * 4 + wave) * 64 * 8], ro == kPastRange ? ro : ro + dcol[j], 0u);
+        dma16(rk, &sm.k[buf][(j * 4 + wave) * 64 * 8], ro == kPastRange ? ro : ro + dcolk[j], 0u);
       }
       if (lane < 16) {
         const int row = tile * kBN + 16 * wave + lane;
@@ -771,12 +775,12 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
       const uint32_t soff = (uint32_t)(tile * kBN) * row_bytes;
 #pragma unroll
       for (int j = 0; j < NJ; ++j)
-        dma16(rv, &sm.v[buf][(j * 4 + wave) * 64 * 8], (uint32_t)drow[j] * row_bytes + dcol[j], soff);
+        dma16(rv, &sm.v[buf][(j * 4 + wave) * 64 * 8], (uint32_t)drow[j] * row_bytes + dcolv[j], soff);
     } else {
 #pragma unroll
       for (int j = 0; j < NJ; ++j) {
         const uint32_t ro = row_off(tile * kBN + drow[j]);
-        dma16(rv, &sm.v[buf][(j * 4 + wave) * 64 * 8], ro == kPastRange ? ro : ro + dcol[j], 0u);
+        dma16(rv, &sm.v[buf][(j * 4 + wave) * 64 * 8], ro == kPastRange ? ro : ro + dcolv[j], 0u);
       }
     }
   };
@@ -859,8 +863,11 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
     constexpr int P = decltype(p_)::value;
     const int b1 = b_cur == 2 ? 0 : b_cur + 1;  // (hs + 1) % 3 == (hs - 2) % 3
     const int b2 = b1 == 2 ? 0 : b1 + 1;        // (hs + 2) % 3
-    const bool dma_now = stage_k ? hs + 2 < ntiles : hs < ntiles;
-    if (dma_now && !stage_k) dma_v(hs, b_cur);  // V tile hs at the start of the half-step
+    const bool my_dma = P != grp;  // the group in its softmax phase stages this half-step's tiles
+    if (my_dma) {
+      if (hs < ntiles) dma_v(hs, b_cur);        // V tile hs
+      if (hs + 2 < ntiles) dma_k(hs + 2, b2);   // K tile hs + 2 and its scores
+    }
 
     if (P == grp) {
       const int jp = hs - 2;
@@ -909,18 +916,9 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
         softmax_tile<D>((t0 + js) * kBN, qrow, qw0, n, g, cs, sa, m_run, l_run, o, pf);
     }
 
-    if (dma_now && stage_k) dma_k(hs + 2, b2);  // K tile hs + 2 (and its scores) at the end
-
-    // K tile hs + 1 and V tile hs - 1 (issued one half-step ago) must have landed;
-    // this half-step's DMAs may stay in flight
-    if (dma_now) {
-      if (stage_k)
-        wait_vm<NJ + 1>();
-      else
-        wait_vm<NJ>();
-    } else {
-      wait_vm<0>();
-    }
+    // the MFMA-phase group staged K tile hs + 1 and V tile hs - 1 one half-step ago: they must have landed;
+    // the softmax group's fresh DMAs may stay in flight
+    if (!my_dma) wait_vm<0>();
     lds_barrier();
     b_cur = b1;
   };
