@@ -990,7 +990,8 @@ SplitPlan choose_split(const tg_plan_info& info, int G, int hkv) {
   const int kBM = 128 / G;
   const int nq = (n + kBM - 1) / kBM;
   const int per_head = std::max(1, device_cu_count() / hkv);
-  if (nq > 2 * per_head) return sp;  // enough whole tiles to balance the CUs
+  if (nq > 2 * per_head || nq > 128) return sp;  // enough whole tiles to balance the CUs (the model's search
+                                                 // is quadratic in nq: bounded here)
   static std::mutex mu;
   static std::map<std::tuple<int, int, int>, SplitPlan> cache;
   const auto key = std::make_tuple(n, G, per_head);
