@@ -120,7 +120,10 @@ def test_split_workload_2_full():
 
 @pytest.mark.parametrize("d,hq,hkv,n,bias", [(128, 16, 8, 700, True), (128, 8, 8, 1500, True),
                                              (128, 16, 4, 1200, False), (64, 8, 2, 1000, True),
-                                             (128, 2, 2, 3000, True), (64, 4, 4, 129, False)])
+                                             (128, 2, 2, 3000, True), (64, 4, 4, 129, False),
+                                             # one KV head (every CU serves it): the largest prompt the split
+                                             # model still considers (128 query tiles), and a ragged one
+                                             (128, 4, 1, 4096, True), (64, 2, 1, 2000, False)])
 def test_split_shapes(d, hq, hkv, n, bias):
     import torch
     _say("split attention", d, hq, hkv, n, bias)
