@@ -241,56 +241,89 @@ __device__ __forceinline__ void softmax_tile(int kv0, int qrow, int qw0, int n, 
     }
 }
 
-// Merges the two wave groups (group 1 hands m, l and O^T to group 0 through
-// LDS at xo: 4 waves x (D x 32 + 64) floats), normalises, and stores the bf16
-// output rows (and the natural-log log-sum-exp when lse is given).
+// Merges the two wave groups, normalises, and stores the bf16 output rows
+// (and the natural-log log-sum-exp when lse is given).  Both groups put their
+// (m, l) and the half of O^T the other group finishes into LDS at xo (8 waves
+// x kMergeRec<D> floats); group 0 then finishes dims [0, D/2) and group 1 dims
+// [D/2, D), so each wave moves and stores half the output.
+template <int D>
+constexpr int kMergeRec = D * 16 + 64;  // floats per wave: half of O^T (D/2 x 32), m, l
+
+// The half of O^T the partner group finishes, and this wave's (m, l), into LDS.
+template <int D, bool G0>
+__device__ __forceinline__ void merge_publish(float* xo, int wave, int lane, int g, int l32, const f32x16 (&o)[D / 32],
+                                              float m_run, float l_half) {
+  constexpr int kHalf = D / 64;         // 32-dim tiles per group
+  constexpr int give = G0 ? kHalf : 0;  // first tile of the half the partner finishes
+  float* mine = xo + ((G0 ? 0 : 4) + wave) * kMergeRec<D>;
+#pragma unroll
+  for (int t = 0; t < kHalf; ++t)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) mine[(t * 16 + i) * 64 + lane] = o[give + t][i];
+  if (g == 0) {
+    mine[D * 16 + l32] = m_run;
+    mine[D * 16 + 32 + l32] = l_half;
+  }
+}
+
+// Merges this group's half of the dims with the partner's partial state and stores it.
+template <int D, bool G0>
+__device__ __forceinline__ void merge_finish(const float* xo, int wave, int lane, int g, int l32,
+                                             const f32x16 (&o)[D / 32], float m_run, float l_half, int qrow, int n,
+                                             const tg_segment& seg, int64_t q_stride, int h, int hq,
+                                             float* __restrict__ lse, uint16_t* __restrict__ out) {
+  constexpr int kHalf = D / 64;
+  constexpr int keep = G0 ? 0 : kHalf;  // first tile of the half this group finishes
+  const float* theirs = xo + ((G0 ? 4 : 0) + wave) * kMergeRec<D>;
+  const float mo = theirs[D * 16 + l32];
+  const float lo = theirs[D * 16 + 32 + l32];
+  // group 0's and group 1's partial states, the same in both groups
+  const float m0 = G0 ? m_run : mo, m1 = G0 ? mo : m_run;
+  const float l0 = G0 ? l_half : lo, l1 = G0 ? lo : l_half;
+  const float m = __builtin_fmaxf(m0, m1);
+  const float a0 = m0 == -__builtin_inff() ? 0.0f : __builtin_amdgcn_exp2f(m0 - m);
+  const float a1 = m1 == -__builtin_inff() ? 0.0f : __builtin_amdgcn_exp2f(m1 - m);
+  const float l_all = __builtin_fmaf(l0, a0, l1 * a1);
+  const float inv = 1.0f / l_all;
+  // natural-log log-sum-exp of the row's logits (kept for the backward pass)
+  if (G0 && lse != nullptr && qrow < n && g == 0)
+    lse[((int64_t)seg.kept_start + qrow) * hq + h] = (m + __log2f(l_all)) * 0.6931471805599453f;
+  if (qrow < n) {
+    uint16_t* orow = out + ((int64_t)seg.kept_start + qrow) * q_stride + (int64_t)h * D;
+#pragma unroll
+    for (int t = 0; t < kHalf; ++t) {
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4) {
+        float r[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int i = 4 * q4 + e;
+          const float own = o[keep + t][i];
+          const float other = theirs[(t * 16 + i) * 64 + lane];
+          r[e] = (G0 ? __builtin_fmaf(own, a0, other * a1) : __builtin_fmaf(other, a0, own * a1)) * inv;
+        }
+        *reinterpret_cast<u32x2*>(orow + 32 * (keep + t) + 8 * q4 + 4 * g) = u32x2{pack_bf16(r[0], r[1]),
+                                                                                   pack_bf16(r[2], r[3])};
+      }
+    }
+  }
+}
+
 template <int D>
 __device__ __forceinline__ void merge_and_store(float* xo, int grp, int wave, int lane, int g, int l32,
                                                 const f32x16 (&o)[D / 32], float m_run, float l_run, int qrow, int n,
                                                 const tg_segment& seg, int64_t q_stride, int h, int hq,
                                                 float* __restrict__ lse, uint16_t* __restrict__ out) {
-  float* mine = xo + wave * (D * 32 + 64);
   const float l_half = xor32_sum(l_run);  // both half-waves: same bits
-  if (grp == 1) {
-#pragma unroll
-    for (int dt = 0; dt < D / 32; ++dt)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) mine[(dt * 16 + i) * 64 + lane] = o[dt][i];
-    if (g == 0) {
-      mine[D * 32 + l32] = m_run;
-      mine[D * 32 + 32 + l32] = l_half;
-    }
-  }
+  if (grp == 0)  // uniform per wave
+    merge_publish<D, true>(xo, wave, lane, g, l32, o, m_run, l_half);
+  else
+    merge_publish<D, false>(xo, wave, lane, g, l32, o, m_run, l_half);
   __syncthreads();
-  if (grp == 0) {
-    const float m1 = mine[D * 32 + l32];
-    const float l1 = mine[D * 32 + 32 + l32];
-    const float m = __builtin_fmaxf(m_run, m1);
-    const float a0 = m_run == -__builtin_inff() ? 0.0f : __builtin_amdgcn_exp2f(m_run - m);
-    const float a1 = m1 == -__builtin_inff() ? 0.0f : __builtin_amdgcn_exp2f(m1 - m);
-    const float l_all = l_half * a0 + l1 * a1;
-    const float inv = 1.0f / l_all;
-    // natural-log log-sum-exp of the row's logits (kept for the backward pass)
-    if (lse != nullptr && qrow < n && g == 0)
-      lse[((int64_t)seg.kept_start + qrow) * hq + h] = (m + __log2f(l_all)) * 0.6931471805599453f;
-    if (qrow < n) {
-      uint16_t* orow = out + ((int64_t)seg.kept_start + qrow) * q_stride + (int64_t)h * D;
-#pragma unroll
-      for (int dt = 0; dt < D / 32; ++dt) {
-#pragma unroll
-        for (int q4 = 0; q4 < 4; ++q4) {
-          float r[4];
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const int i = 4 * q4 + e;
-            r[e] = (o[dt][i] * a0 + mine[(dt * 16 + i) * 64 + lane] * a1) * inv;
-          }
-          *reinterpret_cast<u32x2*>(orow + 32 * dt + 8 * q4 + 4 * g) = u32x2{pack_bf16(r[0], r[1]),
-                                                                             pack_bf16(r[2], r[3])};
-        }
-      }
-    }
-  }
+  if (grp == 0)
+    merge_finish<D, true>(xo, wave, lane, g, l32, o, m_run, l_half, qrow, n, seg, q_stride, h, hq, lse, out);
+  else
+    merge_finish<D, false>(xo, wave, lane, g, l32, o, m_run, l_half, qrow, n, seg, q_stride, h, hq, lse, out);
 }
 
 // Epilogue of a split query tile.  The groups merge as in merge_and_store
@@ -429,6 +462,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
   constexpr int kBM = 128 / G;  // query rows per workgroup
   constexpr int kWavesPerHead = 4 / G;
   __shared__ AttnSmem<D> sm;
+  static_assert(8 * kMergeRec<D> * 4 <= (int)sizeof(AttnSmem<D>), "group merge fits in LDS");
   __shared__ int32_t sidx[GATHER ? kMaxGatherRows : 1];  // source rows of the kept rows [0, q_end)
 
   const tg_segment seg = segs[blockIdx.z];
@@ -672,6 +706,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
   constexpr int NC = D / 8;   // 16-byte chunks per row
   constexpr int NJ = NC / 4;  // DMA instructions per staging wave per tile (64 NC chunks over 4 waves)
   __shared__ DmaSmem<D> sm;
+  static_assert(8 * kMergeRec<D> * 4 <= (int)sizeof(DmaSmem<D>), "group merge fits in LDS");
   __shared__ int32_t sidx[GATHER ? kDmaGatherRows : 1];  // source rows of the kept rows [0, q_end)
 
   const tg_segment seg = segs[blockIdx.z];
