@@ -641,7 +641,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
     if (hs + 1 < ntiles + 2) half_step(hs + 1, std::integral_constant<int, 1>());
   }
 
-  // Merge the two groups: group 1 hands (m, l, O^T) to group 0 through LDS.
+  // Merge the two groups through LDS (each finishes half of the head dims).
   merge_and_store<D>(reinterpret_cast<float*>(&sm), grp, wave, lane, g, l32, o, m_run, l_run, qrow, n, seg, q_stride, h,
                      hq, lse, out);
 }
@@ -962,7 +962,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
     if (hs + 1 < ntiles + 2) half_step(hs + 1, std::integral_constant<int, 1>());
   }
 
-  // Merge the two groups: group 1 hands (m, l, O^T) to group 0 through LDS.
+  // Merge the two groups through LDS (each finishes half of the head dims; split tiles also merge across items).
   if (role == 0) {
     merge_and_store<D>(reinterpret_cast<float*>(&sm), grp, wave, lane, g, l32, o, m_run, l_run, qrow, n, seg, q_stride,
                        h, hq, lse, out);

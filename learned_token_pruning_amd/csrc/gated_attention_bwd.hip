@@ -370,7 +370,12 @@ __global__ __launch_bounds__(kDkdvThreads) void bwd_dkdv_kernel(
 // later).  Q and dO chunks are swizzled as in bwd_dq_dma_kernel's K, K and V
 // rows as c ^ (r & 15).  The arithmetic, and its order, is that of
 // bwd_dkdv_kernel, so the results are the same bits.
-__device__ __forceinline__ int dq_swz(int r) { return ((r & 3) << 2) | ((r >> 2) & 3); }
+//
+// rt_swz: chunk swizzle of a row-major tile that is read both by rows and by
+// transposing reads: chunk c of row r sits at c ^ rt_swz(r), which puts the 16
+// rows of a row-read cycle on 16 distinct chunks and the 4 rows of a
+// transposing read on 4 distinct 64-byte groups.
+__device__ __forceinline__ int rt_swz(int r) { return ((r & 3) << 2) | ((r >> 2) & 3); }
 
 constexpr int kDkStages = 5;
 
@@ -446,7 +451,7 @@ __global__ __launch_bounds__(kDkdvThreads) __attribute__((amdgpu_waves_per_eu(2,
   for (int j = 0; j < 2; ++j) {
     const int p = (j * 4 + wave) * 64 + lane;
     const int r = p / 16;
-    doff[j] = (uint32_t)r * q_row_bytes + (uint32_t)((p % 16) ^ dq_swz(r)) * 16u;
+    doff[j] = (uint32_t)r * q_row_bytes + (uint32_t)((p % 16) ^ rt_swz(r)) * 16u;
   }
   auto stage_item = [&](int it, int buf) {
     const int h = c * G + it / nqb, q0 = 32 * (qb_begin + it % nqb);
@@ -472,7 +477,7 @@ __global__ __launch_bounds__(kDkdvThreads) __attribute__((amdgpu_waves_per_eu(2,
   // Q / dO rows (A operands of S and dP): row l32, chunk 2 ks + g.
   uint32_t raddr[D / 16];
 #pragma unroll
-  for (int ks = 0; ks < D / 16; ++ks) raddr[ks] = (uint32_t)(l32 * D + (((2 * ks + g) ^ dq_swz(l32)) * 8));
+  for (int ks = 0; ks < D / 16; ++ks) raddr[ks] = (uint32_t)(l32 * D + (((2 * ks + g) ^ rt_swz(l32)) * 8));
   // Q^T / dO^T (A operands of dK and dV, transposing reads): as bwd_dq_dma_kernel's K^T, rows of a 16-query step.
   uint32_t taddr[2][D / 32];
   {
@@ -483,7 +488,7 @@ __global__ __launch_bounds__(kDkdvThreads) __attribute__((amdgpu_waves_per_eu(2,
 #pragma unroll
       for (int dtile = 0; dtile < D / 32; ++dtile) {
         const int cc = 4 * dtile + 2 * (qg & 1) + ((s2 & 3) >> 1);
-        taddr[hi][dtile] = (uint32_t)(r * D + ((cc ^ dq_swz(r)) * 8) + 4 * (s2 & 1));
+        taddr[hi][dtile] = (uint32_t)(r * D + ((cc ^ rt_swz(r)) * 8) + 4 * (s2 & 1));
       }
     }
   }
@@ -913,7 +918,7 @@ __global__ __launch_bounds__(kDqThreads) __attribute__((amdgpu_waves_per_eu(2, 2
   for (int j = 0; j < NJ; ++j) {
     const int p = (j * 4 + wave) * 64 + lane;
     const int r = p / NC;
-    doff[j] = (uint32_t)r * row_bytes + (uint32_t)((p % NC) ^ dq_swz(r)) * 16u;
+    doff[j] = (uint32_t)r * row_bytes + (uint32_t)((p % NC) ^ rt_swz(r)) * 16u;
   }
   auto dma_k = [&](int tile, int buf) {
     const uint32_t soff = (uint32_t)(tile * kTile) * row_bytes;
@@ -961,7 +966,7 @@ __global__ __launch_bounds__(kDqThreads) __attribute__((amdgpu_waves_per_eu(2, 2
   // K and V rows (A operands of S^T and dP^T): row l32 (+32 for the second half), chunk 2 ks + g.
   uint32_t raddr[D / 16];
 #pragma unroll
-  for (int ks = 0; ks < D / 16; ++ks) raddr[ks] = (uint32_t)(l32 * D + (((2 * ks + g) ^ dq_swz(l32)) * 8));
+  for (int ks = 0; ks < D / 16; ++ks) raddr[ks] = (uint32_t)(l32 * D + (((2 * ks + g) ^ rt_swz(l32)) * 8));
   // K^T (A operand of dQ^T, transposing read): 16-lane group qg covers dims 32 dt + 16 (qg % 2) + 0..15 and
   // keys 4 g + 0..3 (+8 for the upper half of a 16-key step); source lane s points at row 4 g + s / 4 (+8).
   uint32_t taddr[2][D / 32];
@@ -973,7 +978,7 @@ __global__ __launch_bounds__(kDqThreads) __attribute__((amdgpu_waves_per_eu(2, 2
 #pragma unroll
       for (int dtile = 0; dtile < D / 32; ++dtile) {
         const int cc = 4 * dtile + 2 * (qg & 1) + ((s & 3) >> 1);
-        taddr[hi][dtile] = (uint32_t)(r * D + ((cc ^ dq_swz(r)) * 8) + 4 * (s & 1));
+        taddr[hi][dtile] = (uint32_t)(r * D + ((cc ^ rt_swz(r)) * 8) + 4 * (s & 1));
       }
     }
   }
