@@ -243,6 +243,12 @@ int tg_gated_attention_prefill(const void* q, const void* k, const void* v, cons
  *     zero-filled before its first use; every call leaves it reusable (its
  *     counters back at zero).  Calls sharing a workspace must not overlap (use
  *     one stream).  When the size is 0 no tile is split and workspace may be NULL.
+ *   The second half waits for the first half's record a bounded time (about
+ *   0.1 s of polling; a workgroup that has already started only has to store
+ *   it, so the wait normally takes microseconds).  Should that bound ever run
+ *   out (the first half stalled, e.g. preempted), the rows of that tile are
+ *   written as NaN (and NaN log-sum-exp) instead of a merge of a stale record,
+ *   and the workspace must be zero-filled again before its next use.
  * Errors as tg_gated_attention_prefill, and TG_ERR_WORKSPACE when the
  * workspace is missing, misaligned or too small. */
 size_t tg_attention_prefill_workspace_bytes(const tg_plan_info* info, int hq, int hkv, int head_dim);

@@ -399,8 +399,12 @@ __device__ __forceinline__ void merge_split(float* xo, int grp, int wave, int la
     int spins = 0;
     while (__hip_atomic_load(&flags[1], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == 0 && ++spins < kSplitMaxSpins)
       __builtin_amdgcn_s_sleep(1);
+    arrival[1] = spins >= kSplitMaxSpins;
   }
   __syncthreads();
+  // The wait ran out (the other half stalled for ~0.1 s): the record may be stale, so these rows are
+  // written as NaN rather than as a plausible wrong merge, and the flags are left for a fresh zero-fill.
+  const bool expired = arrival[1] != 0;
   if (grp == 0) {
     // both products rounded before the sum (no fused multiply-add), so the two arrival orders give the same bits
 #pragma clang fp contract(off)
@@ -418,8 +422,10 @@ __device__ __forceinline__ void merge_split(float* xo, int grp, int wave, int la
     const float ab = mb == -__builtin_inff() ? 0.0f : __builtin_amdgcn_exp2f(mb - mm);
     const float l_all = l * aa + lb * ab;
     const float inv = 1.0f / l_all;
+    // NaN is chosen on the stored bits: this file is built without NaN semantics for float arithmetic
     if (lse != nullptr && qrow < n && g == 0)
-      lse[((int64_t)seg.kept_start + qrow) * hq + h] = (mm + __log2f(l_all)) * 0.6931471805599453f;
+      reinterpret_cast<uint32_t*>(lse)[((int64_t)seg.kept_start + qrow) * hq + h] =
+          expired ? 0x7fc00000u : __builtin_bit_cast(uint32_t, (mm + __log2f(l_all)) * 0.6931471805599453f);
     if (qrow < n) {
       uint16_t* orow = out + ((int64_t)seg.kept_start + qrow) * q_stride + (int64_t)h * D;
 #pragma unroll
@@ -432,13 +438,13 @@ __device__ __forceinline__ void merge_split(float* xo, int grp, int wave, int la
             const int i = 4 * q4 + e;
             r[e] = (o[dt][i] * aa + ob[dt][i] * ab) * inv;
           }
-          *reinterpret_cast<u32x2*>(orow + 32 * dt + 8 * q4 + 4 * g) = u32x2{pack_bf16(r[0], r[1]),
-                                                                             pack_bf16(r[2], r[3])};
+          *reinterpret_cast<u32x2*>(orow + 32 * dt + 8 * q4 + 4 * g) =
+              expired ? u32x2{0x7fc07fc0u, 0x7fc07fc0u} : u32x2{pack_bf16(r[0], r[1]), pack_bf16(r[2], r[3])};
         }
       }
     }
   }
-  if (threadIdx.x == 0) {
+  if (threadIdx.x == 0 && !expired) {
     __hip_atomic_store(&flags[0], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     __hip_atomic_store(&flags[1], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
