@@ -22,7 +22,8 @@
  * - Device pointers are plain HIP device addresses owned by the caller.  The
  *   library never allocates or frees device memory and never synchronises
  *   the stream: every launch is asynchronous on `stream` (a hipStream_t;
- *   NULL = the legacy default stream).
+ *   NULL = the legacy default stream).  The one exception is
+ *   tg_attention_workspace_status, whose purpose is to read a word back.
  * - Host pointers (marked "host") are read during the call only.
  * - bf16 tensors are IEEE bfloat16 bit patterns (uint16), row-major,
  *   token-major ([tokens, heads, head_dim]).  Scores and parameters are fp32.
@@ -243,15 +244,32 @@ int tg_gated_attention_prefill(const void* q, const void* k, const void* v, cons
  *     zero-filled before its first use; every call leaves it reusable (its
  *     counters back at zero).  Calls sharing a workspace must not overlap (use
  *     one stream).  When the size is 0 no tile is split and workspace may be NULL.
- *   The second half waits for the first half's record a bounded time (about
- *   0.1 s of polling; a workgroup that has already started only has to store
- *   it, so the wait normally takes microseconds).  Should that bound ever run
- *   out (the first half stalled, e.g. preempted), the rows of that tile are
- *   written as NaN (and NaN log-sum-exp) instead of a merge of a stale record,
- *   and the workspace must be zero-filled again before its next use.
+ *   The second half waits for the first half's record a bounded time (2^22
+ *   polls, each a load that bypasses the L2 plus a short sleep: on the order
+ *   of a second; a workgroup that has already started only has to store its
+ *   record, so the wait normally takes microseconds).  The first 4 bytes of
+ *   the workspace are a status word, 0 while the workspace is consistent.
+ *   Should the wait ever run out (the first half stalled, e.g. preempted), or
+ *   should a call find a tile's counters already set when it starts (a
+ *   workspace that was not zero-filled, or left by such a failed call, or
+ *   shared by calls that overlapped), the rows of that tile are written as
+ *   NaN (and NaN log-sum-exp) instead of a merge of a stale record, the status
+ *   word gets bit 1 (counters already set) or bit 2 (wait ran out), and the
+ *   counters are left as they are, so every later call reports the same until
+ *   the caller zero-fills the workspace.  tg_attention_workspace_status reads
+ *   the word.
  * Errors as tg_gated_attention_prefill, and TG_ERR_WORKSPACE when the
  * workspace is missing, misaligned or too small. */
 size_t tg_attention_prefill_workspace_bytes(const tg_plan_info* info, int hq, int hkv, int head_dim);
+
+/* Status word of a split-tile attention workspace (see above): *status = 0
+ * when every call on it merged normally; otherwise bit 1 (a call found
+ * counters already set) and/or bit 2 (a wait ran out), and the outputs of
+ * those calls hold NaN rows.  Unlike every other entry point this one
+ * synchronises `stream` (it copies the word to the host after the work
+ * queued there).  workspace: device, 256-byte aligned, non-NULL; status: host.
+ * Errors: TG_ERR_INVALID_ARG, TG_ERR_NO_DEVICE, TG_ERR_HIP. */
+int tg_attention_workspace_status(const void* workspace, int* status, void* stream);
 int tg_gated_attention_prefill_ws(const void* q, const void* k, const void* v, const float* key_score,
                                   const float* tau, const float* gain, const tg_segment* segs,
                                   const tg_plan_info* info, int hq, int hkv, int head_dim, void* out, void* workspace,

@@ -257,6 +257,21 @@ size_t tg_attention_prefill_workspace_bytes(const tg_plan_info* info, int hq, in
   return tg::attention_prefill_workspace_bytes(*info, hq, hkv, head_dim);
 }
 
+int tg_attention_workspace_status(const void* workspace, int* status, void* stream) {
+  if (!workspace || !status || !aligned(workspace, 256)) return TG_ERR_INVALID_ARG;
+  const int st = check_device();
+  if (st != TG_OK) return st;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  int word = 0;
+  if (hipMemcpyAsync(&word, workspace, sizeof(int), hipMemcpyDeviceToHost, s) != hipSuccess ||
+      hipStreamSynchronize(s) != hipSuccess) {
+    (void)hipGetLastError();
+    return TG_ERR_HIP;
+  }
+  *status = word;
+  return TG_OK;
+}
+
 int tg_gated_attention_prefill_ws(const void* q, const void* k, const void* v, const float* key_score,
                                   const float* tau, const float* gain, const tg_segment* segs,
                                   const tg_plan_info* info, int hq, int hkv, int head_dim, void* out, void* workspace,

@@ -334,19 +334,37 @@ __device__ __forceinline__ void merge_and_store(float* xo, int grp, int wave, in
 // and waits on nothing, so the wait ends; it is also bounded), reads the
 // record from `other`, merges, normalises, stores, and resets both flags for
 // the next launch.  The merge is symmetric (both products rounded before the
-// sum), so the result does not depend on the arrival order.  The record and
-// the flags use device-coherent (agent-scope) accesses, and the record writes
-// complete (vmcnt 0) before the flag: a device-scope fence would instead write
-// back and invalidate the whole L2 of the XCD, evicting the K/V tiles the other
-// workgroups there are reading.
+// sum), so the result does not depend on the arrival order.
+//
+// Ordering (AMDGPU memory model, agent scope, gfx950: one L2 per XCD, not
+// coherent with the others).  Every record and flag access is an agent-scope
+// atomic with relaxed order, which the compiler emits with the sc1 bit: the
+// access bypasses the XCD's L2 and goes to memory, where all XCDs see it.  The
+// publisher waits (vmcnt 0) until its record stores are acknowledged before it
+// stores the flag, so the record is in memory before the flag is; the consumer
+// issues its record loads only after its flag load has returned the raised
+// flag (the loop exit depends on it), and those loads also bypass L2, so they
+// cannot return older data.  That is the release / acquire pair the exchange
+// needs without the L2 write-back and invalidation that agent-scope fences
+// (release / acquire orderings) imply on this chip, which would also evict the
+// K/V tiles of every other workgroup of the XCD (measured: twice as slow).
+//
+// A workspace left inconsistent is detected instead of merged: an arrival
+// count of 2 or more means the counters were not zero when this launch
+// started (a previous wait ran out, or the workspace was not zero-filled);
+// then, and when this call's own wait runs out, the tile's rows (and
+// log-sum-exp) are written as NaN, a bit is set in the status word at the
+// start of the workspace, and the counters are left as they are (every later
+// call sees the same state until the caller zero-fills the workspace).
 constexpr int kSplitMaxSpins = 1 << 22;
+constexpr int kSplitStatusPoisoned = 1, kSplitStatusExpired = 2;
 
 template <int D>
 __device__ __forceinline__ void merge_split(float* xo, int grp, int wave, int lane, int g, int l32,
                                             f32x16 (&o)[D / 32], float m_run, float l_run, int qrow, int n,
                                             const tg_segment& seg, int64_t q_stride, int h, int hq,
                                             float* __restrict__ lse, uint16_t* __restrict__ out, float* mine_rec,
-                                            float* other_rec, int* flags) {
+                                            float* other_rec, int* flags, int* status) {
   constexpr int kRec = D * 32 + 64;
   float* mine = xo + wave * kRec;
   int* arrival = reinterpret_cast<int*>(xo + 4 * kRec);
@@ -377,7 +395,8 @@ __device__ __forceinline__ void merge_split(float* xo, int grp, int wave, int la
   }
   if (threadIdx.x == 0) arrival[0] = atomicAdd(&flags[0], 1);
   __syncthreads();
-  if (arrival[0] == 0) {  // uniform: first half in publishes its record
+  const int arrived = arrival[0];
+  if (arrived == 0) {  // uniform: first half in publishes its record
     if (grp == 0) {
       float* rec = mine_rec + wave * kRec;
 #pragma unroll
@@ -395,16 +414,19 @@ __device__ __forceinline__ void merge_split(float* xo, int grp, int wave, int la
     if (threadIdx.x == 0) __hip_atomic_store(&flags[1], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     return;
   }
-  if (threadIdx.x == 0) {
+  // arrival count 2 or more: the counters were already set when this launch began (poisoned workspace)
+  if (arrived == 1 && threadIdx.x == 0) {
     int spins = 0;
     while (__hip_atomic_load(&flags[1], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == 0 && ++spins < kSplitMaxSpins)
       __builtin_amdgcn_s_sleep(1);
-    arrival[1] = spins >= kSplitMaxSpins;
+    arrival[1] = spins >= kSplitMaxSpins ? kSplitStatusExpired : 0;
   }
   __syncthreads();
-  // The wait ran out (the other half stalled for ~0.1 s): the record may be stale, so these rows are
-  // written as NaN rather than as a plausible wrong merge, and the flags are left for a fresh zero-fill.
-  const bool expired = arrival[1] != 0;
+  // A poisoned workspace or an expired wait: the record may be stale, so these rows are written as NaN
+  // rather than as a plausible wrong merge, the status word records why, and the counters stay as they are.
+  const int bad = arrived == 1 ? arrival[1] : kSplitStatusPoisoned;
+  const bool expired = bad != 0;
+  if (expired && threadIdx.x == 0) atomicOr(status, bad);
   if (grp == 0) {
     // both products rounded before the sum (no fused multiply-add), so the two arrival orders give the same bits
 #pragma clang fp contract(off)
@@ -704,7 +726,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
     const float* __restrict__ key_score, const float* __restrict__ tau, const float* __restrict__ gain,
     const tg_segment* __restrict__ segs, int hq, int hkv, const int32_t* __restrict__ kept_idx, int64_t n_src,
     const int32_t* __restrict__ qpos, float* __restrict__ lse, uint16_t* __restrict__ out, int split_t, int ns_max,
-    int* __restrict__ split_cnt, float* __restrict__ split_part) {
+    int* __restrict__ split_status, int* __restrict__ split_cnt, float* __restrict__ split_part) {
   constexpr bool GATHER = MODE == kGather;
   constexpr bool QTAU = MODE == kQueryTau;
   constexpr int kBM = 128 / G;
@@ -977,7 +999,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
     constexpr int kPart = 4 * (D * 32 + 64);  // floats per half: 4 waves x (O^T, m, l)
     merge_split<D>(reinterpret_cast<float*>(&sm), grp, wave, lane, g, l32, o, m_run, l_run, qrow, n, seg, q_stride, h,
                    hq, lse, out, split_part + ((int64_t)slot * 2 + (role - 1)) * kPart,
-                   split_part + ((int64_t)slot * 2 + (2 - role)) * kPart, split_cnt + 2 * slot);
+                   split_part + ((int64_t)slot * 2 + (2 - role)) * kPart, split_cnt + 2 * slot, split_status);
   }
 }
 
@@ -1072,13 +1094,15 @@ SplitPlan choose_split(const tg_plan_info& info, int G, int hkv) {
   return sp;
 }
 
-// workspace: int flags [n_seg x hkv x ns_max][2] (arrivals, record ready), padded
-// to 256 bytes, then the fp32 records [slot][half][4 waves][D x 32 + 64]
+// workspace: a 256-byte header (the int status word first), int flags
+// [n_seg x hkv x ns_max][2] (arrivals, record ready) padded to 256 bytes, then
+// the fp32 records [slot][half][4 waves][D x 32 + 64]
+constexpr size_t kSplitHeader = 256;
 size_t split_flag_bytes(size_t slots) { return (slots * 8 + 255) / 256 * 256; }
 size_t split_bytes(const SplitPlan& sp, const tg_plan_info& info, int hkv, int D) {
   if (sp.t == 0) return 0;
   const size_t slots = (size_t)info.n_seg * hkv * sp.ns_max;
-  return split_flag_bytes(slots) + slots * 2 * 4 * ((size_t)D * 32 + 64) * 4;
+  return kSplitHeader + split_flag_bytes(slots) + slots * 2 * 4 * ((size_t)D * 32 + 64) * 4;
 }
 
 template <int D, int G>
@@ -1091,12 +1115,14 @@ hipError_t launch_dg(const void* q, const void* k, const void* v, const float* k
   if (ntiles == 0) return hipSuccess;
   SplitPlan sp;
   if (split_ws != nullptr && !(kept_idx != nullptr && info.max_kept_len > kDmaGatherRows)) sp = choose_split(info, G, hkv);
+  int* split_status = nullptr;
   int* split_cnt = nullptr;
   float* split_part = nullptr;
   if (sp.t > 0) {
     const size_t slots = (size_t)info.n_seg * hkv * sp.ns_max;
-    split_cnt = reinterpret_cast<int*>(split_ws);
-    split_part = reinterpret_cast<float*>(reinterpret_cast<char*>(split_ws) + split_flag_bytes(slots));
+    split_status = reinterpret_cast<int*>(split_ws);
+    split_cnt = reinterpret_cast<int*>(reinterpret_cast<char*>(split_ws) + kSplitHeader);
+    split_part = reinterpret_cast<float*>(reinterpret_cast<char*>(split_ws) + kSplitHeader + split_flag_bytes(slots));
     ntiles += sp.ns_max;
   }
   dim3 grid(hkv, ntiles, info.n_seg);
@@ -1106,18 +1132,18 @@ hipError_t launch_dg(const void* q, const void* k, const void* v, const float* k
   auto* ob = reinterpret_cast<uint16_t*>(out);
   if (kept_idx != nullptr && info.max_kept_len <= kDmaGatherRows)
     hipLaunchKernelGGL((gated_attention_dma_kernel<D, G, kGather>), grid, dim3(kThreads), 0, stream, qb, kb, vb, ks,
-                       tau, gain, segs, hq, hkv, kept_idx, n_src, nullptr, lse, ob, sp.t, sp.ns_max, split_cnt,
+                       tau, gain, segs, hq, hkv, kept_idx, n_src, nullptr, lse, ob, sp.t, sp.ns_max, split_status, split_cnt,
                        split_part);
   else if (kept_idx != nullptr)
     hipLaunchKernelGGL((gated_attention_kernel<D, G, kGather>), grid, dim3(kThreads), 0, stream, qb, kb, vb, ks, tau,
                        gain, segs, hq, hkv, kept_idx, n_src, nullptr, lse, ob);
   else if (qpos != nullptr)
     hipLaunchKernelGGL((gated_attention_dma_kernel<D, G, kQueryTau>), grid, dim3(kThreads), 0, stream, qb, kb, vb, ks,
-                       tau, gain, segs, hq, hkv, nullptr, (int64_t)0, qpos, lse, ob, sp.t, sp.ns_max, split_cnt,
+                       tau, gain, segs, hq, hkv, nullptr, (int64_t)0, qpos, lse, ob, sp.t, sp.ns_max, split_status, split_cnt,
                        split_part);
   else
     hipLaunchKernelGGL((gated_attention_dma_kernel<D, G, kCompacted>), grid, dim3(kThreads), 0, stream, qb, kb, vb,
-                       ks, tau, gain, segs, hq, hkv, nullptr, (int64_t)0, nullptr, lse, ob, sp.t, sp.ns_max, split_cnt,
+                       ks, tau, gain, segs, hq, hkv, nullptr, (int64_t)0, nullptr, lse, ob, sp.t, sp.ns_max, split_status, split_cnt,
                        split_part);
   return hipGetLastError();
 }

@@ -32,7 +32,7 @@ STATUS_NAMES = {0: "TG_OK", -1: "TG_ERR_INVALID_ARG", -2: "TG_ERR_UNSUPPORTED", 
 EXPORTS = ("tg_status_string", "tg_abi_version", "tg_plan_segments", "tg_gate_workspace_bytes", "tg_gate_score",
            "tg_gate_packed_w1_bytes", "tg_gate_pack_w1", "tg_gate_score_prepacked",
            "tg_select_workspace_bytes", "tg_select_topk", "tg_compact_kept", "tg_gated_attention_prefill",
-           "tg_attention_prefill_workspace_bytes", "tg_gated_attention_prefill_ws",
+           "tg_attention_prefill_workspace_bytes", "tg_gated_attention_prefill_ws", "tg_attention_workspace_status",
            "tg_gated_attention_prefill_gather_ws", "tg_gated_attention_prefill_query_tau_ws",
            "tg_gated_attention_prefill_gather", "tg_gated_attention_prefill_query_tau",
            "tg_decode_workspace_bytes", "tg_gated_attention_decode", "tg_gated_attention_prefill_lse",
@@ -109,6 +109,8 @@ _lib.tg_gated_attention_prefill_query_tau_ws.argtypes = [_vp, _vp, _vp, _vp, _vp
 _lib.tg_gated_attention_prefill_query_tau.restype = _i32
 _lib.tg_gated_attention_prefill_query_tau.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, ctypes.POINTER(PlanInfo),
                                                       _i32, _i32, _i32, _vp, _vp]
+_lib.tg_attention_workspace_status.restype = _i32
+_lib.tg_attention_workspace_status.argtypes = [_vp, ctypes.POINTER(_i32), _vp]
 _lib.tg_gated_attention_prefill_lse.restype = _i32
 _lib.tg_gated_attention_prefill_lse.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, ctypes.POINTER(PlanInfo), _i32, _i32,
                                                 _i32, _vp, _vp, _vp]
@@ -334,6 +336,16 @@ def attention_prefill_workspace(plan: Plan, hq: int, hkv: int, head_dim: int, de
     """A zero-filled workspace for gated_attention_prefill(..., workspace=)."""
     return torch.zeros(max(attention_prefill_workspace_bytes(plan, hq, hkv, head_dim), 256), dtype=torch.uint8,
                        device=device)
+
+
+def attention_workspace_status(workspace: torch.Tensor, stream=None) -> int:
+    """tg_attention_workspace_status: 0 while every call on the split-tile workspace merged normally; bit 1 if a
+    call found its counters already set, bit 2 if a wait ran out (those calls wrote NaN rows).  Synchronises the
+    stream."""
+    word = _i32(0)
+    _check(_lib.tg_attention_workspace_status(_ptr(workspace), ctypes.byref(word), _stream(stream)),
+           "tg_attention_workspace_status")
+    return int(word.value)
 
 
 def gated_attention_prefill(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, key_score: Optional[torch.Tensor],

@@ -101,11 +101,13 @@ def decoder_layer(x: np.ndarray, positions: np.ndarray, key_score: Optional[np.n
 def pruned_stack(x0: np.ndarray, layers: List[LayerWeights], gate_layer: int, gate_w1: np.ndarray,
                  gate_w2: np.ndarray, seg_start: Sequence[int], doc_begin: Sequence[int], doc_end: Sequence[int],
                  k_budget: Sequence[int], hq: int, hkv: int, dh: int, eps: float = 1e-6, theta: float = 1e6,
-                 gate_eps: float = 1e-6, bf16: bool = True):
+                 gate_eps: float = 1e-6, bf16: bool = True, kept_idx: Optional[np.ndarray] = None):
     """Layers 0 .. gate_layer over every token; the gate on layer
     gate_layer's RMSNorm(h); top-K select; layers above over the kept rows
     (original positions, gated attention).  Returns (y_kept, kept_idx,
-    kept_offsets, scores)."""
+    kept_offsets, scores).  kept_idx, when given, replaces the select's
+    result (a test that must follow another selector's choice at a near-tie
+    of the scores passes it; the offsets are those of the budgets)."""
     n = x0.shape[0]
     pos = np.arange(n)
     full_offs = list(seg_start)
@@ -119,6 +121,10 @@ def pruned_stack(x0: np.ndarray, layers: List[LayerWeights], gate_layer: int, ga
     if bf16:
         s = s.astype(np.float32).astype(np.float64)  # the scores are stored as fp32
     idx, offs = kept_indices(s, seg_start, doc_begin, doc_end, k_budget)
+    if kept_idx is not None:
+        kept_idx = np.asarray(kept_idx, dtype=np.int64)
+        assert kept_idx.shape == idx.shape, "a kept set of the budgets' size"
+        idx = kept_idx
     xk, pk, sk = x[idx], pos[idx], s[idx]
     for li in range(gate_layer + 1, len(layers)):
         xk, _ = decoder_layer(xk, pk, sk, layers[li], offs, hq, hkv, dh, eps, theta, bf16)

@@ -170,10 +170,15 @@ def test_attention_split_workspace():
     if not gpu_available():
         rec = 2 * 4 * (32 * 128 + 64) * 4  # two records of 4 waves x (O^T, m, l) per split tile
         b = nbytes([2112])
-        assert b > 0 and (b - 256 * ((b // rec * 8 + 255) // 256)) % rec == 0
+        # a 256-byte header (status word), the merge counters padded to 256 bytes, then the records
+        assert b > 0 and (b - 256 - 256 * ((b // rec * 8 + 255) // 256)) % rec == 0
         assert nbytes([1000]) > 0
     assert nbytes([300, 700]) == 0 and nbytes([64]) == 0 and nbytes([8192]) == 0
     assert nbytes([2112], hq=16, hkv=6) == 0 and L.tg_attention_prefill_workspace_bytes(None, 16, 8, 128) == 0
+    # the status query validates before touching the device
+    word = ctypes.c_int(0)
+    assert L.tg_attention_workspace_status(None, ctypes.byref(word), None) == -1
+    assert L.tg_attention_workspace_status(FAKE, None, None) == -1
     p = _plan()
     info = ctypes.byref(p.info)
     f = L.tg_gated_attention_prefill_ws

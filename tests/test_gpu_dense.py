@@ -58,6 +58,40 @@ def rel_l2(got, ref):
     return float(np.linalg.norm(got - ref) / np.linalg.norm(ref))
 
 
+def el_err(got, ref):
+    """Largest per-element error in units of the bound b_j = 2^-7 |ref_j| + 2^-8 rms(ref) (about one bf16 step of
+    the element, with a floor for elements near zero); <= 1 means every element is within its bound."""
+    b = 2.0 ** -7 * np.abs(ref) + 2.0 ** -8 * np.sqrt(np.mean(ref * ref))
+    return float(np.max(np.abs(got - ref) / b))
+
+
+# Per-element bounds, in units of el_err's b_j.  One decoder layer stores seven bf16 tensors in a row; the
+# oracle rounds the float64 value of each step, the GPU the fp32 one, so a rounding decision can differ by one
+# bf16 step at every store.  The output y = h + mid W_down carries the step of its own rounding and of h's
+# (residual) directly, and the steps of the earlier stores through sums over >= 2048 products with random
+# signs, which shrink them; LAYER_EL allows four steps.  The stack compounds layers along the residual stream.
+LAYER_EL = 4.0
+STACK_EL = 8.0
+
+
+def near_tie_or_equal(idx, idx_ref, s_ref, seg):
+    """The GPU's kept set equals the oracle's, or differs only at documents whose oracle score is within the
+    gate tolerance of the budget's threshold score (the two score arrays differ by rounding)."""
+    if np.array_equal(idx, idx_ref):
+        return True
+    sym = np.setxor1d(idx, idx_ref)
+    for i in range(len(seg["k_budget"])):
+        a = seg["seg_start"][i]
+        doc = s_ref[a + seg["doc_begin"][i]: a + seg["doc_end"][i]]
+        k = min(seg["k_budget"][i], doc.size)
+        if k == 0 or k == doc.size:
+            continue
+        t = np.sort(doc)[::-1][k - 1]
+        mine = sym[(sym >= a + seg["doc_begin"][i]) & (sym < a + seg["doc_end"][i])]
+        assert np.all(np.abs(s_ref[mine] - t) <= 4e-3 * max(1.0, abs(t))), "kept sets differ beyond near-ties"
+    return False
+
+
 @pytest.mark.parametrize("m,n,k", [(1, 128, 64), (300, 256, 128), (513, 384, 2048), (1000, 4096, 192)])
 def test_gemm_epilogues(m, n, k):
     import torch
@@ -174,7 +208,9 @@ def test_decoder_layer(d, hq, hkv, dh, f, lens, gated):
     y_ref, hn_ref = oracle.decoder_layer(x, pos, s.astype(np.float64) if gated else None, ow, list(offs), hq, hkv,
                                          dh, 1e-6, 1e6)
     e1, e2 = rel_l2(host(hid), y_ref), rel_l2(host(hn), hn_ref)
-    _say(f"rel L2 y {e1:.2e} rmsnorm(h) {e2:.2e}")
+    p1, p2 = el_err(host(hid), y_ref), el_err(host(hn), hn_ref)
+    _say(f"rel L2 y {e1:.2e} rmsnorm(h) {e2:.2e}; per element (bf16 steps) y {p1:.2f} rmsnorm(h) {p2:.2f}")
+    assert p1 <= LAYER_EL and p2 <= LAYER_EL, "per-element bound"
     assert e1 <= 4e-3 and e2 <= 1e-2
 
 
@@ -210,11 +246,16 @@ def test_pruned_stack_matches_oracle():
                                                           dh)
     idx = out["kept"].cpu().numpy().astype(np.int64)
     assert idx.size == idx_ref.size
-    if not np.array_equal(idx, idx_ref):
-        pytest.skip("kept sets differ at a near-tie of the gate scores; stage parity is covered elsewhere")
+    if not near_tie_or_equal(idx, idx_ref, s_ref, seg):
+        # follow the GPU's choice at the near-tie: the oracle stack on the same kept set
+        _say("kept sets differ at a near-tie; comparing on the GPU's kept set")
+        y_ref, _, _, _ = oracle.pruned_stack(x, ows, gl, gw1, gw2.astype(np.float64), seg["seg_start"],
+                                             seg["doc_begin"], seg["doc_end"], seg["k_budget"], hq, hkv, dh,
+                                             kept_idx=idx)
     e = rel_l2(host(out["hidden"]), y_ref)
-    _say(f"stack rel L2 {e:.2e}")
-    assert e <= 2e-2
+    p = el_err(host(out["hidden"]), y_ref)
+    _say(f"stack rel L2 {e:.2e}; per element {p:.2f} bf16 steps")
+    assert p <= STACK_EL and e <= 2e-2
 
 
 def test_pruning_nothing_equals_the_full_stack_bitwise():
@@ -258,11 +299,16 @@ def test_full_width_stack_matches_oracle():
     _say(f"gate scores after two layers: max |d| / rms {e_s:.2e}")
     assert e_s <= 5e-2
     idx = out["kept"].cpu().numpy().astype(np.int64)
-    if not np.array_equal(idx, idx_ref):
-        pytest.skip("kept sets differ at a near-tie of the gate scores; stage parity is covered elsewhere")
+    assert idx.size == idx_ref.size
+    if not near_tie_or_equal(idx, idx_ref, s_ref, seg):
+        _say("kept sets differ at a near-tie; comparing on the GPU's kept set")
+        y_ref, _, _, _ = oracle.pruned_stack(x, ows, gl, gw1, gw2.astype(np.float64), seg["seg_start"],
+                                             seg["doc_begin"], seg["doc_end"], seg["k_budget"], hq, hkv, dh,
+                                             kept_idx=idx)
     e = rel_l2(host(out["hidden"]), y_ref)
-    _say(f"stack rel L2 {e:.2e}")
-    assert e <= 2e-2
+    p = el_err(host(out["hidden"]), y_ref)
+    _say(f"stack rel L2 {e:.2e}; per element {p:.2f} bf16 steps")
+    assert p <= STACK_EL and e <= 2e-2
 
 
 def _check_kept_valid(kept, scores, n, n_doc, k):

@@ -90,7 +90,7 @@ def oracle_gate(L, eps=1e-6, b1=None, b2=0.0):
 # ----------------------------------------------------------------------------- gate
 
 
-@pytest.mark.parametrize("idx", [1, 2])
+@pytest.mark.parametrize("idx", [1, 2, 3])
 def test_gate_workload(idx):
     _say("gate workload", idx)
     L = layer(idx, with_qkv=False)
@@ -362,7 +362,7 @@ def test_attention_workload_2_full():
     check_attention(got, q, k, v, sc, L.tau, L.gain, offs)
 
 
-@pytest.mark.parametrize("kb", [1024, 8192])
+@pytest.mark.parametrize("kb", [1024, 2048, 4096, 8192])
 def test_attention_workload_3_sampled(kb):
     _say("attention workload 3", kb)
     L = layer(3)
@@ -531,21 +531,27 @@ def test_pipeline(idx):
     torch.cuda.synchronize()
 
     s_ref = oracle_gate(L)
-    check_scores(s_gpu.cpu().numpy(), s_ref, doc_mask_of(seg))
+    s_got = s_gpu.cpu().numpy()
+    check_scores(s_got, s_ref, doc_mask_of(seg))
     ref_idx, offs = oracle.kept_indices(s_ref, seg.seg_start, seg.doc_begin, seg.doc_end, seg.k_budget)
     got_idx = idx_gpu.cpu().numpy().astype(np.int64)
+    # the select is exact on the fp32 scores the gate wrote
+    own_idx, _ = oracle.kept_indices(s_got.astype(np.float64), seg.seg_start, seg.doc_begin, seg.doc_end,
+                                     seg.k_budget)
+    assert np.array_equal(got_idx, own_idx), "select differs from the oracle on the GPU's own scores"
     assert got_idx.size == ref_idx.size
     if not np.array_equal(got_idx, ref_idx):
-        # allowed only at near-ties of the oracle scores (GPU and oracle scores differ by rounding)
+        # allowed only at near-ties of the oracle scores (GPU and oracle scores differ by rounding); the later
+        # stages are then checked on the GPU's kept set
         sym = np.setxor1d(got_idx, ref_idx)
         t = np.sort(s_ref[seg.doc_begin[0]:seg.doc_end[0]])[::-1][seg.k_budget[0] - 1]
         assert np.all(np.abs(s_ref[sym] - t) <= 4 * SCORE_RTOL * max(1.0, abs(t))), "kept sets differ beyond near-ties"
-        pytest.skip("kept sets differ at a near-tie; stage parity is covered by the other tests")
-    assert hc.view(torch.int16).cpu().numpy().tobytes() == oracle.compact_rows(L.x.view(np.int16), ref_idx).tobytes()
+        _say("kept sets differ at a near-tie:", sym.size, "tokens; checking the later stages on the GPU's set")
+    assert hc.view(torch.int16).cpu().numpy().tobytes() == oracle.compact_rows(L.x.view(np.int16), got_idx).tobytes()
     got = W.bf16_bits_to_f64(host_bf16(o))
-    q, k, v = (oracle.compact_rows(a, ref_idx) for a in (L.q, L.k, L.v))
+    q, k, v = (oracle.compact_rows(a, got_idx) for a in (L.q, L.k, L.v))
     # the oracle's own scores drive its attention: gate error feeds through the bias (|g| <= 1.5)
-    check_attention(got, q, k, v, oracle.compact_rows(s_ref, ref_idx), L.tau, L.gain, offs)
+    check_attention(got, q, k, v, oracle.compact_rows(s_ref, got_idx), L.tau, L.gain, offs)
 
 
 @pytest.mark.parametrize("gather", [False, True])

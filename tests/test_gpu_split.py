@@ -80,12 +80,14 @@ def oracle_check(got_bits, q, k, v, s, tau, gain, offs, rows=None):
 
 
 def counters_zero(ws, nbytes, d):
-    """The int32 merge flags at the start of the workspace: two per split tile (arrivals, record ready), then
-    two fp32 records of 4 x (32 d + 64) floats per split tile."""
+    """The workspace starts with a 256-byte header (the status word first), then the int32 merge counters, two
+    per split tile (arrivals, record ready), padded to 256 bytes, then two fp32 records of 4 x (32 d + 64) floats
+    per split tile.  True when the status word and every counter are zero."""
     import torch
     torch.cuda.synchronize()
     slots = nbytes // (2 * 4 * (32 * d + 64) * 4)
-    return bool((ws[: 8 * slots].view(torch.int32) == 0).all().item())
+    status = int(ws[:4].view(torch.int32).item())
+    return status == 0 and bool((ws[256: 256 + 8 * slots].view(torch.int32) == 0).all().item())
 
 
 def test_split_workload_2_full():
@@ -242,3 +244,39 @@ def test_split_gather_and_query_tau(d, hq, hkv, n):
                                  s[idx].astype(np.float64), tq, gain.astype(np.float64), offs, rows=rows)
     got = W.bf16_bits_to_f64(host_bf16(outs[0]))[rows]
     assert np.abs(got - ref).max() <= ATTN_ATOL
+
+
+def test_split_poisoned_workspace_is_reported():
+    """A workspace whose merge counters are already set when a call starts (as a wait that ran out would leave
+    them, or a workspace that was not zero-filled) is not merged from: the split tiles' rows come out NaN, the
+    status word reports it (bit 1), no half waits, and every kernel exits normally.  The counters are seeded from
+    the host, so no workgroup is ever stalled.  A zero-filled workspace then works again."""
+    import torch
+    _say("split attention, poisoned workspace")
+    tg = _tg()
+    hq, hkv, d, n = 16, 8, 128, 2112
+    q, k, v, s, tau, gain = random_inputs(31, n, hq, hkv, d)
+    plan = tg.plan_segments([0, n], [0], [0], [0], device="cuda")
+    nbytes = tg.attention_prefill_workspace_bytes(plan, hq, hkv, d)
+    assert nbytes > 0
+    ws = tg.attention_prefill_workspace(plan, hq, hkv, d, "cuda")
+    args = (dev_bf16(q), dev_bf16(k), dev_bf16(v), dev_f32(s), dev_f32(tau), dev_f32(gain), plan)
+    good = tg.gated_attention_prefill(*args, workspace=ws)
+    assert tg.attention_workspace_status(ws) == 0
+    good_bits = good.view(torch.int16).cpu().numpy()
+    slots = nbytes // (2 * 4 * (32 * d + 64) * 4)
+    flags = ws[256: 256 + 8 * slots].view(torch.int32).view(slots, 2)
+    flags[:, 0] = 2
+    flags[:, 1] = 1
+    bad = tg.gated_attention_prefill(*args, workspace=ws)
+    torch.cuda.synchronize()
+    assert tg.attention_workspace_status(ws) & 1
+    bad_bits = bad.view(torch.int16).cpu().numpy()
+    nan_rows = np.isnan(W.bf16_bits_to_f64(bad_bits.view(np.uint16)).reshape(n, -1)).any(axis=1)
+    assert nan_rows.any(), "the split tiles' rows are written as NaN"
+    assert np.array_equal(bad_bits[~nan_rows], good_bits[~nan_rows]), "unsplit tiles unchanged"
+    ws.zero_()
+    again = tg.gated_attention_prefill(*args, workspace=ws)
+    assert tg.attention_workspace_status(ws) == 0
+    assert np.array_equal(again.view(torch.int16).cpu().numpy(), good_bits)
+    assert counters_zero(ws, nbytes, d)

@@ -1,7 +1,10 @@
 """Pins of the oracle's dense decoder stack: the bf16 format definition,
 closed forms and invariances of RMSNorm / RoPE / SiLU, a layer against the
-same layer assembled from torch library routines (float64), and the pruned
-stack reducing to the unpruned stack when nothing is pruned."""
+same layer assembled from torch library routines (float64), the pruned
+stack reducing to the unpruned stack when nothing is pruned, and the pruned
+stack's kept rows equal to a full-length forward that keeps every token at
+its original position and masks the pruned keys out of the attention above
+the gate (with and without the gate bias)."""
 import math
 
 import numpy as np
@@ -141,3 +144,79 @@ def test_pruned_stack_without_pruning_is_the_full_stack():
     # with pruning the kept rows are the selector's and their count is K + question
     y2, idx2, offs2, _ = oracle.pruned_stack(x0, layers, gl, gw1, gw2, [0, 40], [0], [34], [10], hq, hkv, dh)
     assert idx2.size == 16 and y2.shape == (16, d) and np.all(idx2[-6:] == np.arange(34, 40))
+
+
+def _torch_masked_layer(x, pos, w, hq, hkv, dh, eps, theta, seg_id, key_kept, key_score):
+    """One layer over every token (float64 torch routines) where a query row r attends key t only if t <= r in
+    the same prompt and t is kept (every row also sees itself, which only matters for pruned rows, whose outputs
+    are never compared); with key_score the logit gets gain_h * s_t and q.k is scaled by tau_h.  Written
+    independently of the oracle's compaction: no row is moved, the rotary angle is the token's own position."""
+    F = torch.nn.functional
+    t = lambda a: torch.from_numpy(np.asarray(a, dtype=np.float64))
+    X = t(x)
+    m, d = X.shape
+    xn = F.rms_norm(X, (d,), t(w.attn_norm), eps)
+    q = (xn @ t(w.wq).T).reshape(m, hq, dh)
+    k = (xn @ t(w.wk).T).reshape(m, hkv, dh)
+    v = (xn @ t(w.wv).T).reshape(m, hkv, dh)
+    half = dh // 2
+    inv = theta ** (-torch.arange(half, dtype=torch.float64) * 2 / dh)
+    ang = t(pos)[:, None] * inv[None, :]
+    cos = torch.cat([ang.cos(), ang.cos()], -1)[:, None, :]
+    sin = torch.cat([ang.sin(), ang.sin()], -1)[:, None, :]
+    rot = lambda z: torch.cat([-z[..., half:], z[..., :half]], -1)
+    q = q * cos + rot(q) * sin
+    k = k * cos + rot(k) * sin
+    r_ = torch.arange(m)
+    sid = torch.from_numpy(np.asarray(seg_id))
+    vis = (r_[None, :] <= r_[:, None]) & (sid[None, :] == sid[:, None])
+    vis &= torch.from_numpy(np.asarray(key_kept))[None, :] | torch.eye(m, dtype=torch.bool)
+    bias = torch.zeros(hq, m, m, dtype=torch.float64)
+    if key_score is not None:
+        bias += t(w.gain)[:, None, None] * t(key_score)[None, None, :]
+        q = q * t(w.tau)[None, :, None]
+    mask = torch.where(vis[None], bias, torch.tensor(-math.inf, dtype=torch.float64))
+    rep = hq // hkv
+    a = F.scaled_dot_product_attention(q.permute(1, 0, 2), k.repeat_interleave(rep, 1).permute(1, 0, 2).contiguous(),
+                                       v.repeat_interleave(rep, 1).permute(1, 0, 2).contiguous(), attn_mask=mask)
+    h = X + a.permute(1, 0, 2).reshape(m, hq * dh) @ t(w.wo).T
+    hn = F.rms_norm(h, (d,), t(w.mlp_norm), eps)
+    y = h + (F.silu(hn @ t(w.w_gate).T) * (hn @ t(w.w_up).T)) @ t(w.w_down).T
+    return y.numpy(), hn.numpy()
+
+
+@pytest.mark.parametrize("gate_bias", [False, True])
+def test_pruned_stack_equals_masked_full_length_forward(gate_bias):
+    """[reading] §4.1 (three-stage forward; the temperature's p_i is the original position, m_i the kept rank):
+    above the gate, processing only the kept rows at their original positions is the same as processing every
+    token with the pruned keys masked out.  Two prompts, a kept set far from the identity (K well below the
+    document), positions restarting per prompt.  With the gate bias off (g = 0) the gated layers are plain causal
+    attention over the kept keys; with it on, each kept key adds gain_h * s_t.  Using the kept rank instead of the
+    position for the rotary angle, or another token's score as the bias, breaks the equality."""
+    rng = np.random.default_rng(41)
+    d, hq, hkv, dh, f, n_layers, gl = 32, 4, 2, 8, 48, 4, 1
+    layers = [_layer(rng, d, hq, hkv, dh, f, gated=li > gl) for li in range(n_layers)]
+    if not gate_bias:
+        for li in range(gl + 1, n_layers):
+            layers[li].gain = np.zeros(hq)
+    gw1, gw2 = rng.standard_normal((16, d)) * 0.3, rng.standard_normal(16) * 0.5
+    seg_start, doc_begin, doc_end, k_budget = [0, 37, 64], [3, 0], [31, 20], [9, 5]
+    n = seg_start[-1]
+    x0 = rng.standard_normal((n, d))
+    y, idx, offs, s = oracle.pruned_stack(x0, layers, gl, gw1, gw2, seg_start, doc_begin, doc_end, k_budget, hq, hkv,
+                                          dh, bf16=False)
+    # the kept set is a real pruning: neither all tokens nor a prefix, and kept rank != position somewhere
+    assert idx.size == 9 + 9 + 5 + 7
+    pos = np.concatenate([np.arange(seg_start[i + 1] - seg_start[i]) for i in range(2)])
+    seg_id = np.concatenate([np.full(seg_start[i + 1] - seg_start[i], i) for i in range(2)])
+    ranks = np.concatenate([np.arange(offs[i + 1] - offs[i]) for i in range(2)])
+    assert np.any(pos[idx] != ranks)
+    kept = np.zeros(n, bool)
+    kept[idx] = True
+    # full-length forward: every token through every layer, pruned keys masked above the gate
+    x = x0
+    for li in range(n_layers):
+        above = li > gl
+        x, _ = _torch_masked_layer(x, pos, layers[li], hq, hkv, dh, 1e-6, 1e6, seg_id,
+                                   kept if above else np.ones(n, bool), s if above else None)
+    np.testing.assert_allclose(y, x[idx], rtol=1e-10, atol=1e-10)
