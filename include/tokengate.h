@@ -148,6 +148,24 @@ int tg_gate_score_prepacked(const void* x, int64_t ld_x, int d, const void* w1_p
                             const float* w2, float b2, int h, const tg_segment* segs, const tg_plan_info* info,
                             float rms_eps, float* scores, void* workspace, size_t workspace_bytes, void* stream);
 
+/* tg_gate_score_prepacked for callers that cannot allocate device memory
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * allocation): the same arguments without the workspace, the same results
+ * bit for bit.  The per-tile sums of squares go to a fixed scratch array
+ * that the library holds on each GPU it runs on (512 KiB, until the process
+ * ends); nothing is allocated or freed and no allocating routine is called.
+ * The array holds n_seg x ceil(max_doc_len / 64) tiles at most,
+ * tg_gate_noalloc_max_tiles() of them (65536: e.g. one prompt of 4M document
+ * tokens, or 64 prompts of 64K); a plan needing more returns
+ * TG_ERR_WORKSPACE.  All calls on one GPU share that array and nothing in it
+ * needs to start at zero, but calls that overlap on one GPU (other streams,
+ * other threads) race on it and must not be issued.  The first call on each
+ * GPU looks up the address of that GPU's copy (with the GPU current). */
+int tg_gate_score_prepacked_noalloc(const void* x, int64_t ld_x, int d, const void* w1_packed, const float* b1,
+                                    const float* w2, float b2, int h, const tg_segment* segs,
+                                    const tg_plan_info* info, float rms_eps, float* scores, void* stream);
+size_t tg_gate_noalloc_max_tiles(void);
+
 /* ------------------------------------------------------------------------ */
 /* (2) Top-K select                                                          */
 /* ------------------------------------------------------------------------ */

@@ -161,6 +161,31 @@ int tg_gate_score_prepacked(const void* x, int64_t ld_x, int d, const void* w1_p
                                           workspace, reinterpret_cast<hipStream_t>(stream)));
 }
 
+int tg_gate_score_prepacked_noalloc(const void* x, int64_t ld_x, int d, const void* w1_packed, const float* b1,
+                                    const float* w2, float b2, int h, const tg_segment* segs,
+                                    const tg_plan_info* info, float rms_eps, float* scores, void* stream) {
+  int st = check_info(segs, info);
+  if (st != TG_OK) return st;
+  if (!x || !w1_packed || !w2 || !scores || d <= 0 || h <= 0 || ld_x < d) return TG_ERR_INVALID_ARG;
+  if (rms_eps != rms_eps) return TG_ERR_INVALID_ARG;  // NaN
+  if (d % 64 != 0 || d > 65536 || h % 64 != 0 || h > 256 || ld_x % 8 != 0) return TG_ERR_UNSUPPORTED;
+  if (!aligned(x, 16) || !aligned(w1_packed, 16) || !aligned(w2, 16) || (b1 && !aligned(b1, 16)) ||
+      !aligned(scores, 4))
+    return TG_ERR_UNSUPPORTED;
+  if (tg::gate_sumsq_bytes(*info) > tg::gate_scratch_bytes()) return TG_ERR_WORKSPACE;
+  st = check_device();
+  if (st != TG_OK) return st;
+  void* scratch = nullptr;
+  if (tg::gate_scratch(&scratch) != hipSuccess) {
+    (void)hipGetLastError();
+    return TG_ERR_HIP;
+  }
+  return hip_status(tg::launch_gate_score(x, ld_x, d, w1_packed, true, b1, w2, b2, h, segs, *info, rms_eps, scores,
+                                          scratch, reinterpret_cast<hipStream_t>(stream)));
+}
+
+size_t tg_gate_noalloc_max_tiles(void) { return tg::gate_scratch_bytes() / sizeof(double); }
+
 size_t tg_select_workspace_bytes(const tg_plan_info* info) {
   if (info == nullptr || info->n_seg < 1) return 0;
   return tg::select_workspace_bytes(*info);

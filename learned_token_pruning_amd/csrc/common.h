@@ -202,6 +202,11 @@ hipError_t launch_gate_score(const void* x, int64_t ld_x, int d, const void* w1,
                              float rms_eps, float* scores, void* workspace, hipStream_t stream);
 hipError_t launch_gate_pack_w1(const void* w1, int d, int h, void* w1_packed, hipStream_t stream);
 size_t gate_workspace_bytes(const tg_plan_info& info, int d, int h);
+// The prepacked gate's scratch (per-tile sums of squares): bytes needed for a plan, the fixed capacity of the
+// library's own array, and the device address of the current GPU's copy of that array.
+size_t gate_sumsq_bytes(const tg_plan_info& info);
+size_t gate_scratch_bytes();
+hipError_t gate_scratch(void** ptr);
 
 hipError_t launch_select_topk(const float* scores, const tg_segment* segs, const tg_plan_info& info,
                               int32_t* kept_idx, void* workspace, hipStream_t stream);

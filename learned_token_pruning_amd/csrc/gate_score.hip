@@ -20,6 +20,9 @@
 // Kernel 2 (gate_normalize): every block re-reduces its prompt's tile sums
 // in the same fixed order (so all blocks agree bit for bit), then rescales
 // its tokens and writes 0 for non-document tokens.
+#include <atomic>
+#include <mutex>
+
 #include "common.h"
 
 namespace tg {
@@ -361,6 +364,42 @@ hipError_t launch_gate_pack_w1(const void* w1, int d, int h, void* w1_packed, hi
   hipLaunchKernelGGL(pack_w1_kernel, dim3((unsigned)((d / 64) * (h / 32))), dim3(256), 0, stream,
                      reinterpret_cast<const uint16_t*>(w1), d, h, reinterpret_cast<u32x4*>(w1_packed));
   return hipGetLastError();
+}
+
+// Scratch of the entry point that allocates nothing (tg_gate_score_prepacked_noalloc): the per-tile sums of
+// squares live in this fixed array, one copy per GPU, held until the process ends.  Host code never passes the
+// array's name to a kernel (on the host it is only a stand-in): the device address of each GPU's copy is looked
+// up once, with that GPU current, and kept.
+constexpr size_t kGateScratchBytes = (size_t)512 << 10;
+static __device__ __align__(256) double scratch[kGateScratchBytes / sizeof(double)];
+
+namespace {
+constexpr int kScratchDevices = 64;
+std::atomic<void*> g_scratch_ptr[kScratchDevices];
+std::mutex g_scratch_mu;
+}  // namespace
+
+size_t gate_scratch_bytes() { return kGateScratchBytes; }
+size_t gate_sumsq_bytes(const tg_plan_info& info) { return sumsq_bytes(info); }
+
+hipError_t gate_scratch(void** ptr) {
+  *ptr = nullptr;
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kScratchDevices) return hipErrorInvalidDevice;
+  void* p = g_scratch_ptr[dev].load(std::memory_order_acquire);
+  if (p == nullptr) {
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    p = g_scratch_ptr[dev].load(std::memory_order_relaxed);
+    if (p == nullptr) {
+      e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));  // this device's copy (the device is current)
+      if (e != hipSuccess || p == nullptr) return e != hipSuccess ? e : hipErrorInvalidSymbol;
+      g_scratch_ptr[dev].store(p, std::memory_order_release);
+    }
+  }
+  *ptr = p;
+  return hipSuccess;
 }
 
 hipError_t launch_gate_score(const void* x, int64_t ld_x, int d, const void* w1, bool w1_prepacked, const float* b1,

@@ -31,6 +31,7 @@ STATUS_NAMES = {0: "TG_OK", -1: "TG_ERR_INVALID_ARG", -2: "TG_ERR_UNSUPPORTED", 
                 -4: "TG_ERR_NO_DEVICE", -5: "TG_ERR_HIP"}
 EXPORTS = ("tg_status_string", "tg_abi_version", "tg_plan_segments", "tg_gate_workspace_bytes", "tg_gate_score",
            "tg_gate_packed_w1_bytes", "tg_gate_pack_w1", "tg_gate_score_prepacked",
+           "tg_gate_score_prepacked_noalloc", "tg_gate_noalloc_max_tiles",
            "tg_select_workspace_bytes", "tg_select_topk", "tg_compact_kept", "tg_gated_attention_prefill",
            "tg_attention_prefill_workspace_bytes", "tg_gated_attention_prefill_ws", "tg_attention_workspace_status",
            "tg_gated_attention_prefill_gather_ws", "tg_gated_attention_prefill_query_tau_ws",
@@ -89,6 +90,11 @@ _lib.tg_gate_pack_w1.argtypes = [_vp, _i32, _i32, _vp, _vp]
 _lib.tg_gate_score_prepacked.restype = _i32
 _lib.tg_gate_score_prepacked.argtypes = [_vp, _i64, _i32, _vp, _vp, _vp, _f32, _i32, _vp, ctypes.POINTER(PlanInfo), _f32,
                                          _vp, _vp, _sz, _vp]
+_lib.tg_gate_score_prepacked_noalloc.restype = _i32
+_lib.tg_gate_score_prepacked_noalloc.argtypes = [_vp, _i64, _i32, _vp, _vp, _vp, _f32, _i32, _vp,
+                                                 ctypes.POINTER(PlanInfo), _f32, _vp, _vp]
+_lib.tg_gate_noalloc_max_tiles.restype = _sz
+_lib.tg_gate_noalloc_max_tiles.argtypes = []
 _lib.tg_select_workspace_bytes.restype = _sz
 _lib.tg_select_workspace_bytes.argtypes = [ctypes.POINTER(PlanInfo)]
 _lib.tg_select_topk.restype = _i32
@@ -297,6 +303,24 @@ def gate_score_prepacked(x: torch.Tensor, w1_packed: torch.Tensor, h: int, b1: O
                                       _dev_table(plan), ctypes.byref(plan.info), float(rms_eps), _ptr(scores),
                                       _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(stream))
     _check(st, "tg_gate_score_prepacked")
+    return scores
+
+
+def gate_noalloc_max_tiles() -> int:
+    """tg_gate_noalloc_max_tiles: prompts x 64-row document tiles the no-allocation gate supports."""
+    return int(_lib.tg_gate_noalloc_max_tiles())
+
+
+def gate_score_prepacked_noalloc(x: torch.Tensor, w1_packed: torch.Tensor, h: int, b1: Optional[torch.Tensor],
+                                 w2: torch.Tensor, b2: float, plan: Plan, scores: torch.Tensor,
+                                 rms_eps: float = 1e-6, stream=None) -> torch.Tensor:
+    """tg_gate_score_prepacked_noalloc: gate_score_prepacked without a workspace (the library's fixed scratch);
+    the caller passes the output, so nothing is allocated."""
+    d = int(w1_packed.numel() * w1_packed.element_size()) // (2 * h)
+    st = _lib.tg_gate_score_prepacked_noalloc(_ptr(x), x.stride(0), d, _ptr(w1_packed), _ptr(b1), _ptr(w2),
+                                              float(b2), h, _dev_table(plan), ctypes.byref(plan.info),
+                                              float(rms_eps), _ptr(scores), _stream(stream))
+    _check(st, "tg_gate_score_prepacked_noalloc")
     return scores
 
 
