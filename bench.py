@@ -197,33 +197,171 @@ def time_graph(pipe, steps, warmup):
     return (time.perf_counter() - t0) / steps * 1e6
 
 
-def cpu_baseline(layer, k_budget, budget_s=12.0):
-    """The oracle (as it stands) on the same 16K workload, timed on the host cores."""
+def cpu_model():
+    """The host CPU's model name (from /proc/cpuinfo), or None."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
+def cpu_baseline(layer, k_budget, budget_s=12.0, threads=None):
+    """The oracle (as it stands) on the same 16K workload, timed on the host cores (all the BLAS threads the
+    host offers, or `threads`)."""
     import oracle
     from learned_token_pruning_amd import workloads as W
+    from contextlib import nullcontext
     try:
-        from threadpoolctl import threadpool_info
-        threads = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
+        from threadpoolctl import threadpool_info, threadpool_limits
+        ctx = threadpool_limits(threads) if threads else nullcontext()
     except Exception:  # pragma: no cover
-        threads = os.cpu_count() or 1
+        threadpool_info, ctx = None, nullcontext()
     seg = layer.segments.with_budget(k_budget)
     x, w1 = W.bf16_bits_to_f64(layer.x), W.bf16_bits_to_f64(layer.w1)
     q, k, v = (W.bf16_bits_to_f64(a) for a in (layer.q, layer.k, layer.v))
     reps, t_total = 0, 0.0
-    while reps < 3 and t_total < budget_s:
-        t0 = time.perf_counter()
-        s = oracle.gate_scores(x, w1, None, layer.w2.astype(np.float64), 0.0, seg.seg_start, seg.doc_begin,
-                               seg.doc_end)
-        idx, offs = oracle.kept_indices(s, seg.seg_start, seg.doc_begin, seg.doc_end, seg.k_budget)
-        hc, qc, kc, vc, sc = (oracle.compact_rows(a, idx) for a in (x, q, k, v, s))
-        oracle.gated_attention(qc, kc, vc, sc, layer.tau.astype(np.float64), layer.gain.astype(np.float64), offs)
-        t_total += time.perf_counter() - t0
-        reps += 1
+    with ctx:
+        used = (max([p.get("num_threads", 1) for p in threadpool_info()] + [1]) if threadpool_info
+                else (os.cpu_count() or 1))
+        while reps < 3 and t_total < budget_s:
+            t0 = time.perf_counter()
+            s = oracle.gate_scores(x, w1, None, layer.w2.astype(np.float64), 0.0, seg.seg_start, seg.doc_begin,
+                                   seg.doc_end)
+            idx, offs = oracle.kept_indices(s, seg.seg_start, seg.doc_begin, seg.doc_end, seg.k_budget)
+            hc, qc, kc, vc, sc = (oracle.compact_rows(a, idx) for a in (x, q, k, v, s))
+            oracle.gated_attention(qc, kc, vc, sc, layer.tau.astype(np.float64), layer.gain.astype(np.float64), offs)
+            t_total += time.perf_counter() - t0
+            reps += 1
     t = t_total / reps
-    return {"value": seg.n_tokens / t, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
+    return {"value": seg.n_tokens / t, "unit": "tokens/s", "cores": int(used), "kind": "oracle",
+            "cpu_model": cpu_model(), "host_cpus": os.cpu_count(),
             "sample": f"full 16K-token gated layer (gate over {seg.n_doc(0)} documents, select, compaction, "
                       f"attention over {idx.size} kept rows), float64 NumPy, mean of {reps} run(s), "
                       f"{t:.2f} s each"}
+
+
+def events_us(torch, f, reps, warm=3):
+    """Mean time of f() over `reps` back-to-back calls, from events on the current stream."""
+    for _ in range(warm):
+        f()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        f()
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / reps * 1e3
+
+
+def time_k_sweep(torch, tg, reps=50):
+    """The 32K-token layer (32704 documents + 64 question tokens) at every budget K in {1024, 2048, 4096, 8192}:
+    the select on the fp32 mixture scores of that workload (95 % N(0,1), 5 % N(4, 0.5), exact duplicates, ties
+    planted across every K), the compaction of H, Q, K, V and the scores, and the attention over the kept rows
+    (with split query tiles when the prompt is too short to fill the GPU); the gate once (it does not depend on
+    K).  Rooflines: attention against the bf16 MFMA peak, select + compaction against HBM."""
+    from learned_token_pruning_amd import workloads as W
+    dev = torch.device("cuda")
+    L = W.workload(3)
+    seg0 = L.segments
+    s_host = W.mixture_scores(3, seg0, k_marks=(1024, 2048, 4096, 8192))
+    rec = {"workload": "gated layer N=32768 (32704 doc + 64 question), d=2048, gate 2048-256-1, 16 Q / 8 KV heads, "
+                       "head_dim 128; select input: fp32 mixture scores", "by_k": {}}
+    p = Pipeline(L, 1024, torch, tg)
+    rec["gate_us"] = round(events_us(torch, p.stages()[0][1], reps), 2)
+    gf = p.gate_flops()
+    rec["gate_roofline"] = {"bound": "hbm", "achieved": p.gate_bytes() / (rec["gate_us"] * 1e-6) / 1e9,
+                            "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                            "mfma_tflops": gf / (rec["gate_us"] * 1e-6) / 1e12}
+    rec["gate_roofline"]["frac"] = rec["gate_roofline"]["achieved"] / HBM_PEAK_GBS
+    rec["gate_roofline"]["mfma_frac"] = rec["gate_roofline"]["mfma_tflops"] / MFMA_BF16_PEAK_TFLOPS
+    del p
+    s_dev = torch.from_numpy(s_host).to(dev)
+    for kb in (1024, 2048, 4096, 8192):
+        pk = Pipeline(L, kb, torch, tg)
+        pk.scores.copy_(s_dev)  # the select input of this workload
+        st = dict(pk.stages())
+        t_sel = events_us(torch, st["select"], reps)
+        t_cmp = events_us(torch, st["compact"], reps)
+        t_att = events_us(torch, st["attention"], reps)
+        sc_bytes = pk.select_compact_bytes()
+        att = pk.attention_flops() / (t_att * 1e-6) / 1e12
+        sc_gbs = sc_bytes / ((t_sel + t_cmp) * 1e-6) / 1e9
+        rec["by_k"][str(kb)] = {
+            "kept_rows": pk.m, "select_us": round(t_sel, 2), "compact_us": round(t_cmp, 2),
+            "attention_us": round(t_att, 2),
+            "attention_roofline": {"bound": "mfma", "achieved": att, "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                                   "frac": att / MFMA_BF16_PEAK_TFLOPS},
+            "select_plus_compact_roofline": {"bound": "hbm", "achieved": sc_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                                             "frac": sc_gbs / HBM_PEAK_GBS, "bytes": sc_bytes,
+                                             "frac_of_copy_rate": sc_gbs / COPY_GBS if COPY_GBS else None}}
+        log(f"K sweep K={kb}: select {t_sel:.1f} us, compact {t_cmp:.1f} us, attention {t_att:.1f} us "
+            f"({att:.0f} TFLOP/s)")
+        del pk
+        torch.cuda.empty_cache()
+    return rec
+
+
+def time_bias_ratio(torch, tg, reps=50):
+    """The same attention launch with the gate bias (key scores and gains) and without it (key_score = NULL):
+    one prompt of M kept rows, 16 Q / 8 KV heads, head_dim 128, with the temperature in both.  The pages quote
+    1.0-1.1x for the biased call of their FlashAttention-2 kernel on A100."""
+    dev = torch.device("cuda")
+    gen = torch.Generator(device=dev).manual_seed(79)
+    hq, hkv, dh = 16, 8, 128
+    rec = {"workload": "token-gated attention with vs without the key-score bias, one prompt of M kept rows, "
+                       "16 Q / 8 KV heads, head_dim 128"}
+    for m in (2112, 4160):
+        q = torch.randn(m, hq, dh, generator=gen, device=dev).to(torch.bfloat16)
+        k = torch.randn(m, hkv, dh, generator=gen, device=dev).to(torch.bfloat16)
+        v = torch.randn(m, hkv, dh, generator=gen, device=dev).to(torch.bfloat16)
+        sc = torch.randn(m, generator=gen, device=dev)
+        tau = 0.8 + 0.4 * torch.rand(hq, generator=gen, device=dev)
+        gain = 0.5 + torch.rand(hq, generator=gen, device=dev)
+        plan = tg.plan_segments([0, m], [0], [0], [0], device=dev)
+        ws = tg.attention_prefill_workspace(plan, hq, hkv, dh, dev)
+        out = torch.empty_like(q)
+        on, off = [], []
+        for _ in range(3):  # interleaved
+            on.append(events_us(torch, lambda: tg.gated_attention_prefill(q, k, v, sc, tau, gain, plan, out=out,
+                                                                        workspace=ws), reps))
+            off.append(events_us(torch, lambda: tg.gated_attention_prefill(q, k, v, None, tau, None, plan, out=out,
+                                                                         workspace=ws), reps))
+        a, b = float(np.median(on)), float(np.median(off))
+        rec[f"m{m}"] = {"bias_us": round(a, 2), "no_bias_us": round(b, 2), "ratio": a / b}
+        del q, k, v, ws
+    return rec
+
+
+def time_select_sweep(torch, tg, reps=20):
+    """The select alone on batches of many prompts, where it reads enough scores to be bandwidth-bound: 64
+    prompts of 16384 tokens (one workgroup per prompt) and 64 prompts of 131072 tokens (the multi-workgroup
+    path), each prompt 64 question tokens after its document, K = 2048 and 4096; N(0,1) fp32 scores.  Bytes:
+    4 per token read, 4 per kept row written."""
+    dev = torch.device("cuda")
+    gen = torch.Generator(device=dev).manual_seed(80)
+    rec = {"workload": "select over 64-prompt batches, N(0,1) fp32 scores, 64 question tokens per prompt"}
+    for n_tok in (16384, 131072):
+        for kb in (2048, 4096):
+            nseg = 64
+            offs = [i * n_tok for i in range(nseg + 1)]
+            plan = tg.plan_segments(offs, [0] * nseg, [n_tok - 64] * nseg, [kb] * nseg, device=dev)
+            s = torch.randn(n_tok * nseg, generator=gen, device=dev)
+            kept = torch.empty(plan.total_kept, dtype=torch.int32, device=dev)
+            ws = torch.empty(max(tg.select_workspace_bytes(plan), 256), dtype=torch.uint8, device=dev)
+            us = events_us(torch, lambda: tg.select_topk(s, plan, kept_idx=kept, workspace=ws), reps)
+            nbytes = 4 * n_tok * nseg + 4 * plan.total_kept
+            gbs = nbytes / (us * 1e-6) / 1e9
+            rec[f"{nseg}x{n_tok}_k{kb}"] = {"us": round(us, 2), "gbs": gbs, "frac_hbm_peak": gbs / HBM_PEAK_GBS,
+                                            "frac_of_copy_rate": gbs / COPY_GBS if COPY_GBS else None}
+            log(f"select sweep {nseg}x{n_tok} K={kb}: {us:.1f} us, {gbs:.0f} GB/s")
+            del s, kept, ws
+    torch.cuda.empty_cache()
+    return rec
 
 
 def kernel_traffic(kernel_source):
@@ -457,6 +595,22 @@ def time_stack(torch, tg, steps, warmup):
                     MFMA_BF16_PEAK_TFLOPS, "attention_share_of_flops": attn_flops / flops,
                     "peak_device_mem_gib": torch.cuda.max_memory_allocated() / 2 ** 30}
         log(f"stack {key}: {wall * 1e3:.1f} ms/step", ph)
+    # the same pruned forward captured as one graph (all 28 layers, gate, select, compaction) and replayed
+    eager = st.forward(x, plan=plan)
+    graph = st.capture(x, plan)
+    for _ in range(warmup):
+        graph.replay()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        out = graph.replay()
+    torch.cuda.synchronize()
+    wall = (time.perf_counter() - t0) / steps
+    same = bool(torch.equal(out["kept"], eager["kept"]) and
+                torch.equal(out["hidden"].view(torch.int16), eager["hidden"].view(torch.int16)))
+    rec["pruned_graph"] = {"ms": wall * 1e3, "tokens_per_s": n / wall, "equal_to_eager": same}
+    log(f"stack pruned, graph replay: {wall * 1e3:.1f} ms/step (bitwise equal to eager: {same})")
+    del eager, graph, out
     rec["prefill_speedup"] = rec["full"]["ms"] / rec["pruned"]["ms"]
     rec["workload"] = (f"pruned-stack prefill, 28 random-init layers (d 2048, 16 Q / 8 KV heads, head_dim 128, "
                        f"SwiGLU 6144), N={n} ({n - nq} doc + {nq} question), 13 full layers, gate after layer 13, "
@@ -484,6 +638,8 @@ def main():
     ap.add_argument("--no-decode", action="store_true", help="skip the decode-step and backward timings")
     ap.add_argument("--only-decode", action="store_true",
                     help="time only the decode step and the attention backward (profiling)")
+    ap.add_argument("--no-sweeps", action="store_true",
+                    help="skip the 32K K sweep, the bias on/off ratio and the batched select sweep")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="also run one plain 256 MiB device copy (reference for rocprofv3 FETCH_SIZE / WRITE_SIZE)")
     args = ap.parse_args()
@@ -644,6 +800,14 @@ def main():
                   "warmup": 0, "ms_per_step": None, "higher_is_better": True, "scaling": "weak",
                   "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
                   "config": {"workload": "decode step and attention backward only (profiling mode)"}}
+    if not args.only_long and not args.only_decode and result is not None and not args.no_sweeps:
+        log("timing the K sweep of the 32K-token layer")
+        result["n32768_k_sweep"] = time_k_sweep(torch, tg)
+        log("timing attention with and without the gate bias")
+        result["bias_on_off"] = time_bias_ratio(torch, tg)
+        log("timing the batched select sweep")
+        result["select_sweep"] = time_select_sweep(torch, tg)
+
     if not args.no_decode and result is not None:
         log("timing the decode step over pruned and unpruned caches")
         result["decode_b32"] = time_decode(torch, tg)
@@ -657,6 +821,8 @@ def main():
     if not args.no_cpu_baseline and l16 is not None:
         log("timing the CPU oracle on the 16K workload")
         result["cpu_baseline"] = cpu_baseline(l16, 2048)
+        log("timing the CPU oracle on one core")
+        result["cpu_baseline_1core"] = cpu_baseline(l16, 2048, budget_s=25.0, threads=1)
     result["hbm_copy_rate_gbs"] = COPY_GBS
     print(json.dumps(result), flush=True)
 

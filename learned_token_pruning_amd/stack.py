@@ -107,45 +107,115 @@ class PrunedStack:
             self._ws = torch.empty(need, dtype=torch.uint8, device=device)
         return self._ws
 
-    def _layer(self, li, hidden, pos, score, plan, post=None):
+    def _layer(self, li, hidden, pos, score, plan, ws, post=None):
         tg.decoder_layer(hidden, pos, score, plan, self.layers[li].c_struct, self.d, self.hq, self.hkv, self.dh,
-                         self.f, self._workspace(plan.total_kept, hidden.device), self.eps, self.theta, post)
+                         self.f, ws, self.eps, self.theta, post)
+
+    def buffers(self, x: torch.Tensor, plan: StackPlan, prune: bool = True) -> dict:
+        """Every buffer one forward over this batch layout uses (hidden rows, gate input, scores, kept indices,
+        compacted rows, positions and scores, and the workspaces), allocated once: a forward given them
+        allocates nothing, so it can be captured as a graph.  A captured graph keeps its own set (the layer
+        workspace shared by eager forwards may be reallocated later)."""
+        dev = x.device
+        n, m = plan.full.total_kept, plan.pruned.total_kept
+        h = self.gate_w1.shape[0]
+        b = {"hidden": torch.empty_like(x), "gate_in": torch.empty_like(x)}
+        b["layer_ws"] = torch.empty(max(tg.decoder_layer_workspace_bytes(n, self.d, self.hq, self.hkv, self.dh,
+                                                                         self.f), 256), dtype=torch.uint8, device=dev)
+        if prune:
+            b["scores"] = torch.empty(n, dtype=torch.float32, device=dev)
+            b["kept"] = torch.empty(m, dtype=torch.int32, device=dev)
+            b["hk"] = torch.empty((m, self.d), dtype=torch.bfloat16, device=dev)
+            b["pk"] = torch.empty(m, dtype=torch.int32, device=dev)
+            b["sk"] = torch.empty(m, dtype=torch.float32, device=dev)
+            b["gate_ws"] = torch.empty(max(tg.gate_workspace_bytes(plan.pruned, self.d, h), 256), dtype=torch.uint8,
+                                       device=dev)
+            b["select_ws"] = torch.empty(max(tg.select_workspace_bytes(plan.pruned), 256), dtype=torch.uint8,
+                                         device=dev)
+        return b
+
+    def _eager_buffers(self, x: torch.Tensor, plan: StackPlan, prune: bool) -> dict:
+        """Fresh output buffers; the layer workspace is kept between eager calls and grown when needed."""
+        n, m = plan.full.total_kept, plan.pruned.total_kept
+        dev = x.device
+        b = {"hidden": torch.empty_like(x), "gate_in": torch.empty_like(x), "layer_ws": self._workspace(n, dev)}
+        if prune:
+            h = self.gate_w1.shape[0]
+            b.update(scores=torch.empty(n, dtype=torch.float32, device=dev),
+                     kept=torch.empty(m, dtype=torch.int32, device=dev),
+                     hk=torch.empty((m, self.d), dtype=torch.bfloat16, device=dev),
+                     pk=torch.empty(m, dtype=torch.int32, device=dev),
+                     sk=torch.empty(m, dtype=torch.float32, device=dev),
+                     gate_ws=tg._workspace(tg.gate_workspace_bytes(plan.pruned, self.d, h), dev),
+                     select_ws=tg._workspace(tg.select_workspace_bytes(plan.pruned), dev))
+        return b
 
     def forward(self, x: torch.Tensor, seg_start=None, doc_begin=None, doc_end=None, k_budget=None,
-                prune: bool = True, plan: Optional[StackPlan] = None, mark=None) -> dict:
+                prune: bool = True, plan: Optional[StackPlan] = None, mark=None, bufs: Optional[dict] = None) -> dict:
         """x bf16 [N, d] (not modified).  prune=False runs every layer over
         every token.  `plan` (from plan()) saves rebuilding the tables;
         `mark(name)`, if given, is called on the host after the launches of
-        each phase ("lower", "prune", "upper") have been issued."""
+        each phase ("lower", "prune", "upper") have been issued.  `bufs` (from
+        buffers()) makes the forward allocate nothing."""
         dev = x.device
         if plan is None:
             plan = self.plan(seg_start, doc_begin, doc_end, k_budget, dev)
-        full, pos = plan.full, plan.pos
-        hidden = x.clone()
-        gate_in = torch.empty_like(hidden)
+        if bufs is None:
+            bufs = self._eager_buffers(x, plan, prune)
+        full, pos, ws = plan.full, plan.pos, bufs["layer_ws"]
+        hidden, gate_in = bufs["hidden"], bufs["gate_in"]
+        hidden.copy_(x)
         for li in range(self.gate_layer + 1):
-            self._layer(li, hidden, pos, None, full, gate_in if li == self.gate_layer else None)
+            self._layer(li, hidden, pos, None, full, ws, gate_in if li == self.gate_layer else None)
         if mark:
             mark("lower")
         if not prune:
             for li in range(self.gate_layer + 1, len(self.layers)):
-                self._layer(li, hidden, pos, None, full)
+                self._layer(li, hidden, pos, None, full, ws)
             if mark:
                 mark("upper")
             return {"hidden": hidden, "gate_in": gate_in}
         pp = plan.pruned
-        scores = tg.gate_score_prepacked(gate_in, self.gate_w1_packed, self.gate_w1.shape[0], None, self.gate_w2, 0.0,
-                                         pp, rms_eps=self.gate_eps)
-        kept = tg.select_topk(scores, pp)
-        m = pp.total_kept
-        hk = torch.empty((m, self.d), dtype=torch.bfloat16, device=dev)
-        pk = torch.empty(m, dtype=torch.int32, device=dev)
-        sk = torch.empty(m, dtype=torch.float32, device=dev)
+        scores, kept, hk, pk, sk = bufs["scores"], bufs["kept"], bufs["hk"], bufs["pk"], bufs["sk"]
+        tg.gate_score_prepacked(gate_in, self.gate_w1_packed, self.gate_w1.shape[0], None, self.gate_w2, 0.0, pp,
+                                rms_eps=self.gate_eps, scores=scores, workspace=bufs["gate_ws"])
+        tg.select_topk(scores, pp, kept_idx=kept, workspace=bufs["select_ws"])
         tg.compact_kept(kept, [(hidden, hk), (pos, pk), (scores, sk)])
         if mark:
             mark("prune")
         for li in range(self.gate_layer + 1, len(self.layers)):
-            self._layer(li, hk, pk, sk, pp)
+            self._layer(li, hk, pk, sk, pp, ws)
         if mark:
             mark("upper")
         return {"hidden": hk, "kept": kept, "scores": scores, "plan": pp, "gate_in": gate_in}
+
+    def capture(self, x: torch.Tensor, plan: StackPlan, prune: bool = True) -> "StackGraph":
+        """The whole forward over this batch layout (lower layers, gate, select, compaction, upper layers) as one
+        HIP graph: the pages capture the pruned forward as a graph per padded length; here the kept count is
+        known on the host from the budgets, so one graph per layout needs no padding.  Nothing in it allocates,
+        synchronises or memsets (the select's counters are cleared by a kernel)."""
+        bufs = self.buffers(x, plan, prune)
+        side = torch.cuda.Stream(device=x.device)
+        side.wait_stream(torch.cuda.current_stream(x.device))
+        with torch.cuda.stream(side):  # warm the stream (and the library's lazily cached state) before capture
+            out = self.forward(x, plan=plan, prune=prune, bufs=bufs)
+        torch.cuda.current_stream(x.device).wait_stream(side)
+        torch.cuda.synchronize(x.device)
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            out = self.forward(x, plan=plan, prune=prune, bufs=bufs)
+        torch.cuda.synchronize(x.device)
+        return StackGraph(g, out, bufs)
+
+
+@dataclass
+class StackGraph:
+    """A captured forward: replay() runs it again on the input it was captured with (x's storage) and leaves
+    the results in `out` (the buffers of the capture)."""
+    graph: "torch.cuda.CUDAGraph"
+    out: dict
+    bufs: dict
+
+    def replay(self) -> dict:
+        self.graph.replay()
+        return self.out

@@ -353,3 +353,83 @@ def test_stack_at_full_size_properties():
     torch.cuda.synchronize()
     _check_kept_valid(out["kept"].cpu().numpy(), out["scores"].cpu().numpy(), n, n - nq, 4096)
     assert torch.isfinite(out["hidden"].float()).all()
+
+
+def _replays_equal_eager(st, x, plan, graph, xs, check=None):
+    """Replay `graph` once per input in xs (copied into x's storage, the captured input), with an eager forward
+    on fresh buffers and a synchronisation between replays; every replay must equal the eager forward bit for
+    bit (the same kernels on the same data).  check(i, out) runs on each replay's result."""
+    import torch
+    for i, xi in enumerate(xs):
+        x.copy_(xi)
+        ref = st.forward(x.clone(), plan=plan)
+        torch.cuda.synchronize()
+        out = graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out["kept"], ref["kept"]), f"replay {i}: kept rows"
+        assert torch.equal(out["scores"], ref["scores"]), f"replay {i}: gate scores"
+        assert torch.equal(out["hidden"].view(torch.int16), ref["hidden"].view(torch.int16)), f"replay {i}: hidden"
+        if check:
+            check(i, out)
+
+
+def test_stack_graph_replays_match_eager_and_oracle():
+    """The whole pruned forward captured as one graph: three replays, two inputs, against the eager forward
+    (bitwise) and the oracle (per-element bound)."""
+    import torch
+    from learned_token_pruning_amd.stack import PrunedStack
+    _say("pruned stack graph small")
+    tg = _tg()
+    rng = np.random.default_rng(24)
+    d, hq, hkv, dh, f, nl, gl = 256, 4, 2, 64, 512, 6, 2
+    hws, ows, (gw1b, gw1), gw2 = _small_stack(rng, nl, gl, d, hq, hkv, dh, f)
+    seg = dict(seg_start=[0, 500, 640], doc_begin=[10, 0], doc_end=[480, 120], k_budget=[64, 200])
+    xa_b, xa = bf(rng.standard_normal((640, d)))
+    xb_b, xb = bf(rng.standard_normal((640, d)))
+    st = PrunedStack([_device_layer(h) for h in hws], gl, dev(gw1b), torch.from_numpy(gw2).cuda(), d, hq, hkv, dh, f)
+    plan = st.plan(seg["seg_start"], seg["doc_begin"], seg["doc_end"], seg["k_budget"], torch.device("cuda"))
+    x = dev(xa_b)
+    graph = st.capture(x, plan)
+    hosts = {0: xa, 1: xb, 2: xa}
+
+    def against_oracle(i, out):
+        xh = hosts[i]
+        y_ref, idx_ref, _, s_ref = oracle.pruned_stack(xh, ows, gl, gw1, gw2.astype(np.float64), seg["seg_start"],
+                                                       seg["doc_begin"], seg["doc_end"], seg["k_budget"], hq, hkv, dh)
+        idx = out["kept"].cpu().numpy().astype(np.int64)
+        assert idx.size == idx_ref.size
+        if not near_tie_or_equal(idx, idx_ref, s_ref, seg):
+            y_ref, _, _, _ = oracle.pruned_stack(xh, ows, gl, gw1, gw2.astype(np.float64), seg["seg_start"],
+                                                 seg["doc_begin"], seg["doc_end"], seg["k_budget"], hq, hkv, dh,
+                                                 kept_idx=idx)
+        p = el_err(host(out["hidden"]), y_ref)
+        _say(f"replay {i}: per element {p:.2f} bf16 steps")
+        assert p <= STACK_EL
+
+    _replays_equal_eager(st, x, plan, graph, [dev(xa_b), dev(xb_b), dev(xa_b)], against_oracle)
+
+
+def test_stack_graph_long_prompt_replays():
+    """A 40960-token prompt (the multi-workgroup top-K path, whose histogram a kernel clears inside the graph)
+    captured as one graph: three replays with eager work between them equal the eager forward bit for bit."""
+    import torch
+    from learned_token_pruning_amd.stack import PrunedStack, random_layers
+    _say("pruned stack graph 40960")
+    tg = _tg()
+    devc = torch.device("cuda")
+    d, hq, hkv, dh, f, n, nq = 2048, 16, 8, 128, 6144, 40960, 64
+    layers = random_layers(9, 2, 1, d, hq, hkv, dh, f, devc)
+    gen = torch.Generator(device=devc)
+    gen.manual_seed(10)
+    w1 = (torch.randn(256, d, generator=gen, device=devc) * 0.02).to(torch.bfloat16)
+    w2 = torch.randn(256, generator=gen, device=devc) * 0.02
+    xs = [torch.randn(n, d, generator=gen, device=devc).to(torch.bfloat16) for _ in range(2)]
+    st = PrunedStack(layers, 0, w1, w2, d, hq, hkv, dh, f)
+    plan = st.plan([0, n], [0], [n - nq], [4096], devc)
+    x = xs[0].clone()
+    graph = st.capture(x, plan)
+
+    def valid(i, out):
+        _check_kept_valid(out["kept"].cpu().numpy(), out["scores"].cpu().numpy(), n, n - nq, 4096)
+
+    _replays_equal_eager(st, x, plan, graph, [xs[0], xs[1], xs[0]], valid)
