@@ -29,8 +29,15 @@
  *   token-major ([tokens, heads, head_dim]).  Scores and parameters are fp32.
  * - A packed batch of prompts ("segments") is described by a segment table
  *   built on the host with tg_plan_segments() and copied by the caller to the
- *   device; the kernels read the device copy and trust it (build it only
- *   with tg_plan_segments, which validates it).
+ *   device; the host validates the table's totals (tg_plan_info) and sizes
+ *   every grid and buffer from them, and the kernels read the device copy
+ *   (the library cannot read it back without a synchronisation).  Each kernel
+ *   clamps the fields of its entry into those totals (seg_start + seg_len <=
+ *   n_tokens, seg_len <= max_seg_len, the document span inside the prompt and
+ *   at most max_doc_len long, k_eff <= that length, kept_start + kept_len <=
+ *   total_kept, kept_len <= max_kept_len), so a table that disagrees with its
+ *   info gives wrong results, never an access outside the arrays; build it
+ *   with tg_plan_segments, and pass the info returned with it.
  * - Results are deterministic: the same inputs give bit-identical outputs
  *   (fixed-order reductions, integer-only atomics).
  */

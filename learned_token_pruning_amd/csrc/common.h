@@ -138,6 +138,61 @@ __device__ __forceinline__ uint32_t score_key(float f) {
 // at voff + soff into LDS at lds_dst + 16 (or 4) x lane.  Issued in asm so the
 // compiler does not order later LDS reads after it; every consumer waits with
 // an explicit vmcnt (the instruction has no destination registers).
+// A device segment table together with the totals of its plan, which the host validated and sized every
+// grid and buffer from.  Kernels read entries only through at(), which clamps each field into those totals:
+// 0 <= seg_start <= n_tokens, seg_len <= min(max_seg_len, n_tokens - seg_start),
+// 0 <= doc_begin <= doc_end <= seg_len with doc_end - doc_begin <= max_doc_len, 0 <= k_eff <= that length,
+// 0 <= kept_start <= total_kept, kept_len <= min(max_kept_len, total_kept - kept_start).
+// A table that agrees with its info passes unchanged; one that does not yields wrong values, never an access
+// outside the arrays.
+struct SegTable {
+  const tg_segment* p;
+  int32_t n_tokens, total_kept, max_seg_len, max_doc_len, max_kept_len;
+
+  static __host__ __device__ __forceinline__ int32_t clampi(int64_t x, int32_t lo, int32_t hi) {
+    return x < lo ? lo : (x > hi ? hi : (int32_t)x);
+  }
+  // the clamped copy of entry r (host-callable, so the rule can be checked without a device)
+  static __host__ __device__ __forceinline__ tg_segment clamp(const tg_segment& r, int32_t n_tokens,
+                                                              int32_t total_kept, int32_t max_seg_len,
+                                                              int32_t max_doc_len, int32_t max_kept_len) {
+    tg_segment s;
+    s.seg_start = clampi(r.seg_start, 0, n_tokens);
+    s.seg_len = clampi(r.seg_len, 0, n_tokens - s.seg_start < max_seg_len ? n_tokens - s.seg_start : max_seg_len);
+    s.doc_begin = clampi(r.doc_begin, 0, s.seg_len);
+    const int32_t room = s.seg_len - s.doc_begin;
+    s.doc_end = s.doc_begin + clampi((int64_t)r.doc_end - s.doc_begin, 0, room < max_doc_len ? room : max_doc_len);
+    s.k_eff = clampi(r.k_eff, 0, s.doc_end - s.doc_begin);
+    s.kept_start = clampi(r.kept_start, 0, total_kept);
+    const int32_t left = total_kept - s.kept_start;
+    s.kept_len = clampi(r.kept_len, 0, left < max_kept_len ? left : max_kept_len);
+    s.reserved = 0;
+    return s;
+  }
+  __device__ __forceinline__ tg_segment at(int i) const {
+    return clamp(p[i], n_tokens, total_kept, max_seg_len, max_doc_len, max_kept_len);
+  }
+  // at(i) for an index that is the same in every lane (a workgroup's own prompt): the fields stay in
+  // scalar registers, as buffer descriptors and LDS DMA addresses built from them need.
+  __device__ __forceinline__ tg_segment at_uniform(int i) const {
+    tg_segment s = at(i);
+    s.seg_start = __builtin_amdgcn_readfirstlane(s.seg_start);
+    s.seg_len = __builtin_amdgcn_readfirstlane(s.seg_len);
+    s.doc_begin = __builtin_amdgcn_readfirstlane(s.doc_begin);
+    s.doc_end = __builtin_amdgcn_readfirstlane(s.doc_end);
+    s.k_eff = __builtin_amdgcn_readfirstlane(s.k_eff);
+    s.kept_start = __builtin_amdgcn_readfirstlane(s.kept_start);
+    s.kept_len = __builtin_amdgcn_readfirstlane(s.kept_len);
+    return s;
+  }
+};
+
+// info has passed the host checks (n_tokens < 2^31, total_kept <= n_tokens, maxima >= 0).
+inline SegTable seg_table(const tg_segment* p, const tg_plan_info& info) {
+  return SegTable{p, (int32_t)info.n_tokens, (int32_t)info.total_kept, info.max_seg_len, info.max_doc_len,
+                  info.max_kept_len};
+}
+
 __device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, const void* lds_dst, uint32_t voff, uint32_t soff) {
   const uint32_t m0v = (uint32_t)(uintptr_t)TG_LDS(lds_dst);
   asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds" ::"s"(m0v), "v"(voff), "s"(r), "s"(soff)

@@ -100,7 +100,7 @@ __global__ __launch_bounds__(kThreads) void gate_mlp_kernel(const uint16_t* __re
                                                             const u32x4* __restrict__ w1p,
                                                             const float* __restrict__ b1,
                                                             const float* __restrict__ w2, float b2, int h,
-                                                            const tg_segment* __restrict__ segs, int max_tiles,
+                                                            SegTable segs, int max_tiles,
                                                             float* __restrict__ scores,
                                                             double* __restrict__ tile_sumsq) {
   constexpr int BM = 32 * RT;
@@ -115,7 +115,7 @@ __global__ __launch_bounds__(kThreads) void gate_mlp_kernel(const uint16_t* __re
   __shared__ __attribute__((aligned(16))) float w2s[4 * 32 * NCT], b1s[4 * 32 * NCT];  // read in the epilogue
   __shared__ double red2[BM];
 
-  const tg_segment seg = segs[blockIdx.y];
+  const tg_segment seg = segs.at_uniform(blockIdx.y);
   const int n_doc = seg.doc_end - seg.doc_begin;
   const int tile = blockIdx.x;
   if (tile * BM >= n_doc) return;  // uniform across the workgroup
@@ -284,14 +284,14 @@ constexpr int kNormThreads = 256;  // one token per thread
 // 256 partial sums are added pairwise, halving the count each step (the last
 // six steps inside one wave by lane shifts).  Each thread's score load is
 // issued before the reduction, so its latency overlaps it.
-__global__ __launch_bounds__(kNormThreads) void gate_normalize_kernel(const tg_segment* __restrict__ segs,
+__global__ __launch_bounds__(kNormThreads) void gate_normalize_kernel(SegTable segs,
                                                                      int max_tiles, int rows_per_tile,
                                                                      const double* __restrict__ tile_sumsq,
                                                                      float rms_eps, float* __restrict__ scores) {
   __shared__ double red128[128];
   __shared__ double red64[64];
   __shared__ float rho_s;
-  const tg_segment seg = segs[blockIdx.y];
+  const tg_segment seg = segs.at_uniform(blockIdx.y);
   const int t0 = blockIdx.x * kNormThreads;
   if (t0 >= seg.seg_len) return;  // uniform
   const int n_doc = seg.doc_end - seg.doc_begin;
@@ -341,7 +341,7 @@ size_t gate_workspace_bytes(const tg_plan_info& info, int d, int h) {
 
 template <int NCT, int RT, int XB, int S>
 static void launch_mlp(dim3 grid, hipStream_t stream, const uint16_t* xp, int64_t ld_x, int d, const u32x4* wp,
-                       const float* b1, const float* w2, float b2, int h, const tg_segment* segs, int max_tiles,
+                       const float* b1, const float* w2, float b2, int h, SegTable segs, int max_tiles,
                        float* scores, double* ts) {
   hipLaunchKernelGGL((gate_mlp_kernel<NCT, S, RT, XB>), grid, dim3(kThreads), 0, stream, xp, ld_x, d, wp, b1, w2, b2,
                      h, segs, max_tiles, scores, ts);
@@ -349,7 +349,7 @@ static void launch_mlp(dim3 grid, hipStream_t stream, const uint16_t* xp, int64_
 
 template <int NCT>
 static void launch_mlp_d(dim3 grid, hipStream_t stream, const uint16_t* xp, int64_t ld_x, int d, const u32x4* wp,
-                         const float* b1, const float* w2, float b2, int h, const tg_segment* segs, int max_tiles,
+                         const float* b1, const float* w2, float b2, int h, SegTable segs, int max_tiles,
                          float* scores, double* ts) {
   // X stage of 256 columns (512-byte row bursts) when d allows; measured best among 128-1024-byte bursts
   if (d % 256 == 0)
@@ -403,8 +403,9 @@ hipError_t gate_scratch(void** ptr) {
 }
 
 hipError_t launch_gate_score(const void* x, int64_t ld_x, int d, const void* w1, bool w1_prepacked, const float* b1,
-                             const float* w2, float b2, int h, const tg_segment* segs, const tg_plan_info& info,
+                             const float* w2, float b2, int h, const tg_segment* segs_in, const tg_plan_info& info,
                              float rms_eps, float* scores, void* workspace, hipStream_t stream) {
+  const SegTable segs = seg_table(segs_in, info);
   int max_tiles = (info.max_doc_len + kRows - 1) / kRows;  // at the smallest tile height: an upper bound
   if (max_tiles < 1) max_tiles = 1;
   double* ts = reinterpret_cast<double*>(workspace);

@@ -483,7 +483,7 @@ template <int D, int G, int MODE>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void gated_attention_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
     const float* __restrict__ key_score, const float* __restrict__ tau, const float* __restrict__ gain,
-    const tg_segment* __restrict__ segs, int hq, int hkv, const int32_t* __restrict__ kept_idx, int64_t n_src,
+    SegTable segs, int hq, int hkv, const int32_t* __restrict__ kept_idx, int64_t n_src,
     const int32_t* __restrict__ qpos, float* __restrict__ lse, uint16_t* __restrict__ out) {
   constexpr bool GATHER = MODE == kGather;
   constexpr bool QTAU = MODE == kQueryTau;
@@ -493,7 +493,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
   static_assert(8 * kMergeRec<D> * 4 <= (int)sizeof(AttnSmem<D>), "group merge fits in LDS");
   __shared__ int32_t sidx[GATHER ? kMaxGatherRows : 1];  // source rows of the kept rows [0, q_end)
 
-  const tg_segment seg = segs[blockIdx.z];
+  const tg_segment seg = segs.at_uniform(blockIdx.z);
   const int n = seg.kept_len;
   const int q0 = (gridDim.y - 1 - blockIdx.y) * kBM;
   if (q0 >= n) return;  // uniform
@@ -724,7 +724,7 @@ template <int D, int G, int MODE>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void gated_attention_dma_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
     const float* __restrict__ key_score, const float* __restrict__ tau, const float* __restrict__ gain,
-    const tg_segment* __restrict__ segs, int hq, int hkv, const int32_t* __restrict__ kept_idx, int64_t n_src,
+    SegTable segs, int hq, int hkv, const int32_t* __restrict__ kept_idx, int64_t n_src,
     const int32_t* __restrict__ qpos, float* __restrict__ lse, uint16_t* __restrict__ out, int split_t, int ns_max,
     int* __restrict__ split_status, int* __restrict__ split_cnt, float* __restrict__ split_part) {
   constexpr bool GATHER = MODE == kGather;
@@ -737,7 +737,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
   static_assert(8 * kMergeRec<D> * 4 <= (int)sizeof(DmaSmem<D>), "group merge fits in LDS");
   __shared__ int32_t sidx[GATHER ? kDmaGatherRows : 1];  // source rows of the kept rows [0, q_end)
 
-  const tg_segment seg = segs[blockIdx.z];
+  const tg_segment seg = segs.at_uniform(blockIdx.z);
   const int n = seg.kept_len;
   // Work item: query tile qi (kBM rows) and key tiles [t0, t1) of it.  With split_t > 0 every query tile with
   // more than split_t key tiles is split in two items, an owner (key tiles [0, split_t)) and a helper (the rest);
@@ -1107,9 +1107,10 @@ size_t split_bytes(const SplitPlan& sp, const tg_plan_info& info, int hkv, int D
 
 template <int D, int G>
 hipError_t launch_dg(const void* q, const void* k, const void* v, const float* ks, const float* tau,
-                     const float* gain, const tg_segment* segs, const tg_plan_info& info, int hq, int hkv,
+                     const float* gain, const tg_segment* segs_in, const tg_plan_info& info, int hq, int hkv,
                      const int32_t* kept_idx, int64_t n_src, const int32_t* qpos, float* lse, void* out,
                      hipStream_t stream, void* split_ws) {
+  const SegTable segs = seg_table(segs_in, info);
   constexpr int kBM = 128 / G;
   int ntiles = (info.max_kept_len + kBM - 1) / kBM;
   if (ntiles == 0) return hipSuccess;

@@ -116,7 +116,7 @@ template <int D, int G>
 __global__ __launch_bounds__(kDkdvThreads) void bwd_dkdv_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
     const float* __restrict__ key_score, const float* __restrict__ tau, const float* __restrict__ gain,
-    const tg_segment* __restrict__ segs, int hq, int hkv, const uint16_t* __restrict__ dout,
+    SegTable segs, int hq, int hkv, const uint16_t* __restrict__ dout,
     const float* __restrict__ lse, const float* __restrict__ dt, int n_chunks, int qc, float* __restrict__ dk_part,
     float* __restrict__ dv_part, float* __restrict__ ds_part, int64_t total_kept, float* __restrict__ part_g,
     float* __restrict__ part_t) {
@@ -132,7 +132,7 @@ __global__ __launch_bounds__(kDkdvThreads) void bwd_dkdv_kernel(
   __shared__ Smem sm;
   __shared__ float red[8][G][2];
 
-  const tg_segment seg = segs[blockIdx.z];
+  const tg_segment seg = segs.at_uniform(blockIdx.z);
   const int n = seg.kept_len;
   // blockIdx.y = key block x query chunk: the chunk covers query blocks
   // [kb0 / 32 + ci qc, + qc) of the prompt (possibly none: then zero partials)
@@ -391,7 +391,7 @@ template <int G>
 __global__ __launch_bounds__(kDkdvThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void bwd_dkdv_dma_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
     const float* __restrict__ key_score, const float* __restrict__ tau, const float* __restrict__ gain,
-    const tg_segment* __restrict__ segs, int hq, int hkv, const uint16_t* __restrict__ dout,
+    SegTable segs, int hq, int hkv, const uint16_t* __restrict__ dout,
     const float* __restrict__ lse, const float* __restrict__ dt, int n_chunks, int qc, float* __restrict__ dk_part,
     float* __restrict__ dv_part, float* __restrict__ ds_part, int64_t total_kept, float* __restrict__ part_g,
     float* __restrict__ part_t) {
@@ -399,7 +399,7 @@ __global__ __launch_bounds__(kDkdvThreads) __attribute__((amdgpu_waves_per_eu(2,
   __shared__ DkdvSmem sm;
   __shared__ float red[8][G][2];
 
-  const tg_segment seg = segs[blockIdx.z];
+  const tg_segment seg = segs.at_uniform(blockIdx.z);
   const int n = seg.kept_len;
   const int ci = blockIdx.y % n_chunks;
   const int kb0 = (blockIdx.y / n_chunks) * kKeyBlock;
@@ -705,7 +705,7 @@ template <int D, int G>
 __global__ __launch_bounds__(kBwdThreads) void bwd_dq_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
     const float* __restrict__ key_score, const float* __restrict__ tau, const float* __restrict__ gain,
-    const tg_segment* __restrict__ segs, int hq, int hkv, const uint16_t* __restrict__ dout,
+    SegTable segs, int hq, int hkv, const uint16_t* __restrict__ dout,
     const float* __restrict__ lse, const float* __restrict__ dt, float* __restrict__ dq) {
   using KT = KeyTile<D>;
   constexpr int kBM = 128 / G;
@@ -713,7 +713,7 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_dq_kernel(
   __shared__ __attribute__((aligned(16))) uint16_t ks_[kTile * KT::kLd], vs[kTile * KT::kLd], kt[D * KT::tLd];
   __shared__ float sc[kTile];
 
-  const tg_segment seg = segs[blockIdx.z];
+  const tg_segment seg = segs.at_uniform(blockIdx.z);
   const int n = seg.kept_len;
   const int q0 = (gridDim.y - 1 - blockIdx.y) * kBM;
   if (q0 >= n) return;
@@ -877,7 +877,7 @@ template <int G>
 __global__ __launch_bounds__(kDqThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void bwd_dq_dma_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
     const float* __restrict__ key_score, const float* __restrict__ tau, const float* __restrict__ gain,
-    const tg_segment* __restrict__ segs, int hq, int hkv, const uint16_t* __restrict__ dout,
+    SegTable segs, int hq, int hkv, const uint16_t* __restrict__ dout,
     const float* __restrict__ lse, const float* __restrict__ dt, float* __restrict__ dq) {
   constexpr int D = 128;
   constexpr int kBM = 128 / G;
@@ -886,7 +886,7 @@ __global__ __launch_bounds__(kDqThreads) __attribute__((amdgpu_waves_per_eu(2, 2
   constexpr int NJ = NC / 4;  // DMA instructions per staging wave per tile
   __shared__ DqSmem sm;
 
-  const tg_segment seg = segs[blockIdx.z];
+  const tg_segment seg = segs.at_uniform(blockIdx.z);
   const int n = seg.kept_len;
   const int q0 = (gridDim.y - 1 - blockIdx.y) * kBM;
   if (q0 >= n) return;  // uniform
@@ -1154,7 +1154,7 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_reduce_rows_kernel(int n_chun
 }
 
 // dgain / dtau = sum over the workgroup slots that ran, one block per head
-__global__ __launch_bounds__(kBwdThreads) void bwd_reduce_params_kernel(const tg_segment* __restrict__ segs, int n_seg,
+__global__ __launch_bounds__(kBwdThreads) void bwd_reduce_params_kernel(SegTable segs, int n_seg,
                                                                         int slots_per_seg, int n_chunks, int hq,
                                                                         const float* __restrict__ part_g,
                                                                         const float* __restrict__ part_t,
@@ -1166,7 +1166,7 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_reduce_params_kernel(const tg
   const int64_t n_slots = (int64_t)n_seg * slots_per_seg;
   for (int64_t s = tid; s < n_slots; s += kBwdThreads) {
     const int seg_i = (int)(s / slots_per_seg), y = (int)(s % slots_per_seg);
-    if ((y / n_chunks) * kKeyBlock < segs[seg_i].kept_len) {
+    if ((y / n_chunks) * kKeyBlock < segs.at(seg_i).kept_len) {
       sg += part_g[s * hq + h];
       st += part_t[s * hq + h];
     }
@@ -1241,9 +1241,10 @@ BwdWs carve(void* ws, const tg_plan_info& info, int hq, int hkv, int head_dim) {
 
 template <int D, int G>
 hipError_t launch_bwd_dg(const void* q, const void* k, const void* v, const float* ks, const float* tau,
-                         const float* gain, const tg_segment* segs, const tg_plan_info& info, int hq, int hkv,
+                         const float* gain, const tg_segment* segs_in, const tg_plan_info& info, int hq, int hkv,
                          const void* out, const void* dout, const float* lse, float* dq, float* dk, float* dv,
                          float* ds, float* dgain, float* dtau, void* workspace, hipStream_t stream) {
+  const SegTable segs = seg_table(segs_in, info);
   const BwdWs w = carve(workspace, info, hq, hkv, D);
   const BwdGeom geo = bwd_geom(info, hkv);
   auto* qb = reinterpret_cast<const uint16_t*>(q);

@@ -129,11 +129,11 @@ __device__ __forceinline__ void load_chunk(const float* __restrict__ seg_scores,
 
 template <int R>
 __global__ __launch_bounds__(kThreads) void select_topk_kernel(const float* __restrict__ scores,
-                                                               const tg_segment* __restrict__ segs,
+                                                               SegTable segs,
                                                                int32_t* __restrict__ kept_idx) {
   __shared__ SelSmem sm;
   constexpr int kChunk = kThreads * R;
-  const tg_segment seg = segs[blockIdx.x];
+  const tg_segment seg = segs.at_uniform(blockIdx.x);
   if (seg.seg_len <= 0) return;
   const int tid = threadIdx.x;
   const int sub = (tid >> 6) & (kSub - 1);
@@ -328,10 +328,10 @@ __global__ __launch_bounds__(256) void select_zero_kernel(uint32_t* __restrict__
 
 template <int PASS>
 __global__ __launch_bounds__(kMT) void select_hist_kernel(const float* __restrict__ scores,
-                                                          const tg_segment* __restrict__ segs, int n_seg,
+                                                          SegTable segs, int n_seg,
                                                           uint32_t* __restrict__ ws) {
   __shared__ MultiSmem sm;
-  const tg_segment seg = segs[blockIdx.y];
+  const tg_segment seg = segs.at_uniform(blockIdx.y);
   const int n_doc = seg.doc_end - seg.doc_begin;
   if (seg.k_eff <= 0 || seg.k_eff >= n_doc) return;  // no selection to make
   const int t0 = blockIdx.x * kSlice;
@@ -402,10 +402,10 @@ __device__ void multi_threshold(const tg_segment& seg, int n_seg, const uint32_t
 
 // Per slice: tokens kept for sure (non-document or key > T) and ties at T.
 __global__ __launch_bounds__(kMT) void select_count_kernel(const float* __restrict__ scores,
-                                                           const tg_segment* __restrict__ segs, int n_seg,
+                                                           SegTable segs, int n_seg,
                                                            int n_slices, uint32_t* __restrict__ ws) {
   __shared__ MultiSmem sm;
-  const tg_segment seg = segs[blockIdx.y];
+  const tg_segment seg = segs.at_uniform(blockIdx.y);
   const int t0 = blockIdx.x * kSlice;
   if (t0 >= seg.seg_len) return;
   uint32_t thresh, need;
@@ -435,11 +435,11 @@ __global__ __launch_bounds__(kMT) void select_count_kernel(const float* __restri
 }
 
 __global__ __launch_bounds__(kMT) void select_emit_kernel(const float* __restrict__ scores,
-                                                          const tg_segment* __restrict__ segs, int n_seg,
+                                                          SegTable segs, int n_seg,
                                                           int n_slices, const uint32_t* __restrict__ ws,
                                                           int32_t* __restrict__ kept_idx) {
   __shared__ MultiSmem sm;
-  const tg_segment seg = segs[blockIdx.y];
+  const tg_segment seg = segs.at_uniform(blockIdx.y);
   const int s0 = blockIdx.x * kSlice;
   if (s0 >= seg.seg_len) return;
   uint32_t thresh, need;
@@ -509,8 +509,9 @@ size_t select_workspace_bytes(const tg_plan_info& info) {
   return (words * 4 + 255) / 256 * 256;
 }
 
-hipError_t launch_select_topk(const float* scores, const tg_segment* segs, const tg_plan_info& info,
+hipError_t launch_select_topk(const float* scores, const tg_segment* segs_in, const tg_plan_info& info,
                               int32_t* kept_idx, void* workspace, hipStream_t stream) {
+  const SegTable segs = seg_table(segs_in, info);
   if (info.max_seg_len <= 0) return hipSuccess;
   if (!use_multi(info)) {
     if (info.max_seg_len <= kThreads * 16)
