@@ -40,23 +40,9 @@ __device__ __forceinline__ float buf_load4f(__amdgpu_buffer_rsrc_t r, uint32_t v
 // Combine every lane with lane ^ 32 (v_permlane32_swap, no LDS round trip).
 // The swap returns the two halves in both orders, so max / sum of the pair is
 // the same expression, with the same rounding, in both half-waves.
-// max of two or three floats in one instruction.  fmaxf first quiets each operand (one v_max_f32 x, x per
-// operand, as maxNum requires for signalling NaNs); these helpers skip that for operands that cannot be
-// signalling NaNs (products, sums and loads of data the kernels computed; a quiet NaN or -inf behaves as in
-// fmaxf).
-__device__ __forceinline__ float max2f(float a, float b) {
-  float r;
-  asm("v_max_f32 %0, %1, %2" : "=v"(r) : "v"(a), "v"(b));
-  return r;
-}
-__device__ __forceinline__ float max3f(float a, float b, float c) {
-  float r;
-  asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
-  return r;
-}
 __device__ __forceinline__ float xor32_max(float x) {
   const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return max2f(__uint_as_float(r[0]), __uint_as_float(r[1]));
+  return __builtin_fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
 __device__ __forceinline__ float xor32_sum(float x) {
   const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);

@@ -202,15 +202,13 @@ __device__ __forceinline__ void softmax_tile(int kv0, int qrow, int qw0, int n, 
       for (int i = 0; i < 16; ++i)
         if (hf * 32 + 8 * (i / 4) + (i % 4) > lim) sa[hf][i] = -__builtin_inff();
   }
-  // 16 three-input maxima over the lane's 32 logits (masked ones are -inf)
-  float m0 = max3f(sa[0][0], sa[0][1], sa[0][2]);
-  float m1 = max3f(sa[1][0], sa[1][1], sa[1][2]);
+  float m0 = -__builtin_inff(), m1 = -__builtin_inff();
 #pragma unroll
-  for (int i = 3; i < 15; i += 2) {
-    m0 = max3f(m0, sa[0][i], sa[0][i + 1]);
-    m1 = max3f(m1, sa[1][i], sa[1][i + 1]);
+  for (int i = 0; i < 16; i += 2) {
+    m0 = __builtin_fmaxf(m0, __builtin_fmaxf(sa[0][i], sa[0][i + 1]));
+    m1 = __builtin_fmaxf(m1, __builtin_fmaxf(sa[1][i], sa[1][i + 1]));
   }
-  const float x = cs * xor32_max(max3f(m0, m1, max2f(sa[0][15], sa[1][15])));
+  const float x = cs * xor32_max(__builtin_fmaxf(m0, m1));
   // Lazy rescale: the reference point m_run only moves when some row's
   // max exceeds it by more than 2^8 (or on the first visible tile);
   // softmax does not depend on the reference point, and
