@@ -92,7 +92,8 @@ def near_tie_or_equal(idx, idx_ref, s_ref, seg):
     return False
 
 
-@pytest.mark.parametrize("m,n,k", [(1, 128, 64), (300, 256, 128), (513, 384, 2048), (1000, 4096, 192)])
+@pytest.mark.parametrize("m,n,k", [(1, 128, 64), (300, 256, 128), (513, 384, 2048), (1000, 4096, 192), (257, 512, 640),
+                                   (2100, 768, 2048), (4200, 8192, 128)])
 def test_gemm_epilogues(m, n, k):
     import torch
     _say("gemm", m, n, k)
