@@ -676,6 +676,8 @@ def main():
         args.only_long, args.no_long, args.no_stack, args.no_cpu_baseline = True, True, True, True
     elif args.only_stack:
         args.only_long, args.no_long = True, True
+    elif args.only_long:
+        args.no_stack = True
     if args.only_long and not args.only_decode:
         args.no_decode = True
     if not args.only_long:
