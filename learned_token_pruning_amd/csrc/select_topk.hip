@@ -210,20 +210,17 @@ __global__ __launch_bounds__(kThreads) void select_topk_kernel(const float* __re
     }
     uint32_t ed, et, td, tt;
     block_scan2((uint32_t)__builtin_popcount(fd), (uint32_t)__builtin_popcount(ft), ed, et, td, tt, sm);
-    uint32_t rdf = def_base + ed;
-    uint32_t rtie = tie_base + et;
-#pragma unroll
-    for (int i = 0; i < R; ++i) {
-      const bool d = (fd >> i) & 1u;
-      const bool tt_ = (ft >> i) & 1u;
-      const uint32_t taken = rtie < need ? rtie : need;
-      if (d || (tt_ && rtie < need)) {
-        const uint32_t pos = rdf + taken;
-        if (pos < (uint32_t)seg.kept_len) out[pos] = seg.seg_start + t0 + i;
-      }
-      rdf += d;
-      rtie += tt_;
-    }
+    // Ties before this thread: t_before; it keeps its first need - t_before ties (none once the quota is
+    // used up).  Kept tokens then land in index order from row def_before + min(t_before, need) on, so the
+    // j-th kept token of the thread goes to that row + j: one store per kept token, the loop running over
+    // the set bits of the thread's kept mask only.
+    const uint32_t t_before = tie_base + et;
+    uint32_t quota = need > t_before ? need - t_before : 0u;
+    uint32_t kept = fd;
+    for (uint32_t m = ft; m != 0u && quota != 0u; m &= m - 1u, --quota) kept |= m & (0u - m);
+    uint32_t pos = def_base + ed + (t_before < need ? t_before : need);
+    for (uint32_t m = kept; m != 0u; m &= m - 1u, ++pos)
+      if (pos < (uint32_t)seg.kept_len) out[pos] = seg.seg_start + t0 + __builtin_ctz(m);
     def_base += td;
     tie_base += tt;
   }
@@ -478,21 +475,16 @@ __global__ __launch_bounds__(kMT) void select_emit_kernel(const float* __restric
   }
   uint32_t ed, et, td, tt;
   scan256((uint32_t)__builtin_popcount(fd), (uint32_t)__builtin_popcount(ft), ed, et, td, tt, sm);
-  uint32_t rdf = bd + ed;
-  uint32_t rtie = bt + et;
+  // as in select_topk_kernel: the thread keeps its first need - t_before ties, and its kept tokens land in
+  // index order from row def_before + min(t_before, need) on
+  const uint32_t t_before = bt + et;
+  uint32_t quota = need > t_before ? need - t_before : 0u;
+  uint32_t kept = fd;
+  for (uint32_t m = ft; m != 0u && quota != 0u; m &= m - 1u, --quota) kept |= m & (0u - m);
+  uint32_t pos = bd + ed + (t_before < need ? t_before : need);
   int32_t* out = kept_idx + seg.kept_start;
-#pragma unroll
-  for (int i = 0; i < kMPer; ++i) {
-    const bool d = (fd >> i) & 1u;
-    const bool tie = (ft >> i) & 1u;
-    const uint32_t taken = rtie < need ? rtie : need;
-    if (d || (tie && rtie < need)) {
-      const uint32_t pos = rdf + taken;
-      if (pos < (uint32_t)seg.kept_len) out[pos] = seg.seg_start + t0 + i;
-    }
-    rdf += d;
-    rtie += tie;
-  }
+  for (uint32_t m = kept; m != 0u; m &= m - 1u, ++pos)
+    if (pos < (uint32_t)seg.kept_len) out[pos] = seg.seg_start + t0 + __builtin_ctz(m);
 }
 
 }  // namespace
