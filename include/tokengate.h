@@ -110,6 +110,13 @@ typedef struct tg_plan_info {
 int tg_plan_segments(int n_seg, const int32_t* seg_start, const int32_t* doc_begin, const int32_t* doc_end,
                      const int32_t* k_budget, tg_segment* table, tg_plan_info* info);
 
+/* Kept rows of one prompt (host only): min(k, n_doc) + n_other, the size of
+ * S = top-K(document) plus every non-document token ([reading] section 4.1;
+ * the budget "max_kept_prefill_tokens", [news] "如何部署 TokenGate？").  It is
+ * the kept_len that tg_plan_segments writes for the prompt.  Returns -1 for a
+ * negative argument. */
+int64_t tg_kept_count(int64_t n_doc, int64_t n_other, int64_t k);
+
 /* ------------------------------------------------------------------------ */
 /* (1) Gate score                                                            */
 /* ------------------------------------------------------------------------ */

@@ -65,6 +65,11 @@ const char* tg_status_string(int status) {
 
 int tg_abi_version(void) { return TG_ABI_VERSION; }
 
+int64_t tg_kept_count(int64_t n_doc, int64_t n_other, int64_t k) {
+  if (n_doc < 0 || n_other < 0 || k < 0) return -1;
+  return (k < n_doc ? k : n_doc) + n_other;
+}
+
 int tg_plan_segments(int n_seg, const int32_t* seg_start, const int32_t* doc_begin, const int32_t* doc_end,
                      const int32_t* k_budget, tg_segment* table, tg_plan_info* info) {
   if (n_seg < 1 || !seg_start || !doc_begin || !doc_end || !k_budget || !table || !info) return TG_ERR_INVALID_ARG;

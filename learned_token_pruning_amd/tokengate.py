@@ -29,8 +29,8 @@ _lib = ctypes.CDLL(_LIB_PATH, mode=ctypes.RTLD_GLOBAL)
 TG_OK = 0
 STATUS_NAMES = {0: "TG_OK", -1: "TG_ERR_INVALID_ARG", -2: "TG_ERR_UNSUPPORTED", -3: "TG_ERR_WORKSPACE",
                 -4: "TG_ERR_NO_DEVICE", -5: "TG_ERR_HIP"}
-EXPORTS = ("tg_status_string", "tg_abi_version", "tg_plan_segments", "tg_gate_workspace_bytes", "tg_gate_score",
-           "tg_gate_packed_w1_bytes", "tg_gate_pack_w1", "tg_gate_score_prepacked",
+EXPORTS = ("tg_status_string", "tg_abi_version", "tg_plan_segments", "tg_kept_count", "tg_gate_workspace_bytes",
+           "tg_gate_score", "tg_gate_packed_w1_bytes", "tg_gate_pack_w1", "tg_gate_score_prepacked",
            "tg_gate_score_prepacked_noalloc", "tg_gate_noalloc_max_tiles",
            "tg_select_workspace_bytes", "tg_select_topk", "tg_compact_kept", "tg_gated_attention_prefill",
            "tg_attention_prefill_workspace_bytes", "tg_gated_attention_prefill_ws", "tg_attention_workspace_status",
@@ -76,6 +76,8 @@ _sz = ctypes.c_size_t
 _lib.tg_status_string.restype = ctypes.c_char_p
 _lib.tg_status_string.argtypes = [_i32]
 _lib.tg_abi_version.restype = _i32
+_lib.tg_kept_count.restype = _i64
+_lib.tg_kept_count.argtypes = [_i64, _i64, _i64]
 _lib.tg_plan_segments.restype = _i32
 _lib.tg_plan_segments.argtypes = [_i32, _vp, _vp, _vp, _vp, ctypes.POINTER(Segment), ctypes.POINTER(PlanInfo)]
 _lib.tg_gate_workspace_bytes.restype = _sz
@@ -235,6 +237,11 @@ def plan_segments(seg_start: Sequence[int], doc_begin: Sequence[int], doc_end: S
     if device is not None:
         dev = torch.from_numpy(host).to(device)
     return Plan(info=info, table=host, table_dev=dev)
+
+
+def kept_count(n_doc: int, n_other: int, k: int) -> int:
+    """tg_kept_count: min(k, n_doc) + n_other (-1 for a negative argument)."""
+    return int(_lib.tg_kept_count(n_doc, n_other, k))
 
 
 def plan_from(segments, device=None) -> Plan:

@@ -199,6 +199,9 @@ int main(int argc, char** argv) {
   std::mt19937_64 rng(argc > 2 ? std::strtoull(argv[2], nullptr, 10) : 1);
   for (int s = -8; s <= 2; ++s) expect(tg_status_string(s) != nullptr, "status string", s);
   expect(tg_abi_version() == TG_ABI_VERSION, "abi version");
+  expect(tg_kept_count(10, 3, 4) == 7 && tg_kept_count(10, 3, 40) == 13 && tg_kept_count(-1, 0, 0) == -1 &&
+             tg_kept_count(INT64_MAX / 4, INT64_MAX / 4, INT64_MAX) == INT64_MAX / 4 * 2,
+         "kept count");
   for (long it = 0; it < iters; ++it) {
     const int n_seg = 1 + (int)(rng() % 40);
     const int max_len = it % 10 == 0 ? 140000 : (int)(rng() % 5000);

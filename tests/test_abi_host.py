@@ -50,6 +50,17 @@ def test_plan_segments_matches_oracle_counts():
     assert p.info.max_seg_len == max(seg.seg_len(i) for i in range(seg.n_seg))
 
 
+def test_kept_count_matches_oracle_and_plan():
+    rng = np.random.default_rng(4)
+    for _ in range(200):
+        n_doc, n_other, k = (int(v) for v in rng.integers(0, 5000, 3))
+        assert tg.kept_count(n_doc, n_other, k) == oracle.kept_count(n_doc, n_other, k)
+    assert tg.kept_count(10, 3, 0) == 3 and tg.kept_count(10, 3, 99) == 13
+    assert tg.kept_count(-1, 0, 0) == -1 and tg.kept_count(0, -1, 0) == -1 and tg.kept_count(5, 0, -1) == -1
+    p = tg.plan_segments([0, 100, 164], [10, 0], [90, 60], [20, 500])
+    assert p.table[:, 6].tolist() == [tg.kept_count(80, 20, 20), tg.kept_count(60, 4, 500)]
+
+
 @pytest.mark.parametrize("args", [
     ([0, 5], [0], [5], [-1]),       # negative budget
     ([0, 5], [0], [6], [1]),        # span past the prompt
