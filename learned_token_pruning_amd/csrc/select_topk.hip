@@ -240,7 +240,8 @@ __global__ __launch_bounds__(kThreads) void select_topk_kernel(const float* __re
 // kept for sure and how many tie the threshold; the emission kernel turns
 // the counts of the earlier slices into its output offset and the tie quota
 // left for it, then writes its kept indices in index order.
-// Workspace: hist [3][n_seg][2048] u32 | cnt [n_seg][n_slices][2] u32.
+// Workspace: hist [3][n_seg][2048] u32 | cnt [n_seg][n_slices][2] u32 | thr [n_seg][2] u32 (the threshold and
+// tie quota the count kernel derived, for the emission kernel).
 
 constexpr int kSlice = 4096;
 constexpr int kMT = 256;
@@ -407,6 +408,11 @@ __global__ __launch_bounds__(kMT) void select_count_kernel(const float* __restri
   if (t0 >= seg.seg_len) return;
   uint32_t thresh, need;
   multi_threshold(seg, n_seg, ws, sm, thresh, need);
+  if (blockIdx.x == 0 && threadIdx.x == 0) {  // every prompt with tokens has slice 0
+    uint32_t* thr = ws + (int64_t)3 * n_seg * kBins + (int64_t)n_seg * n_slices * 2 + (int64_t)blockIdx.y * 2;
+    thr[0] = thresh;
+    thr[1] = need;
+  }
   const float* ss = scores + seg.seg_start;
   uint32_t nd = 0u, nt = 0u;
 #pragma unroll
@@ -439,8 +445,9 @@ __global__ __launch_bounds__(kMT) void select_emit_kernel(const float* __restric
   const tg_segment seg = segs.at_uniform(blockIdx.y);
   const int s0 = blockIdx.x * kSlice;
   if (s0 >= seg.seg_len) return;
-  uint32_t thresh, need;
-  multi_threshold(seg, n_seg, ws, sm, thresh, need);
+  // the threshold and tie quota the count kernel derived (it ran before this launch, on the same stream)
+  const uint32_t* thr = ws + (int64_t)3 * n_seg * kBins + (int64_t)n_seg * n_slices * 2 + (int64_t)blockIdx.y * 2;
+  const uint32_t thresh = thr[0], need = thr[1];
   // offsets from the earlier slices of this prompt
   const uint32_t* cnt = ws + (int64_t)3 * n_seg * kBins + (int64_t)blockIdx.y * n_slices * 2;
   uint32_t bd = 0u, bt = 0u;
@@ -497,7 +504,7 @@ static int n_slices(const tg_plan_info& info) { return (int)((info.max_seg_len +
 
 size_t select_workspace_bytes(const tg_plan_info& info) {
   if (!use_multi(info)) return 0;  // the one-workgroup kernel keeps its state on chip
-  const size_t words = (size_t)3 * info.n_seg * kBins + (size_t)info.n_seg * n_slices(info) * 2;
+  const size_t words = (size_t)3 * info.n_seg * kBins + (size_t)info.n_seg * n_slices(info) * 2 + (size_t)info.n_seg * 2;
   return (words * 4 + 255) / 256 * 256;
 }
 
