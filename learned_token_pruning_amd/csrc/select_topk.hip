@@ -240,12 +240,16 @@ __global__ __launch_bounds__(kThreads) void select_topk_kernel(const float* __re
 // kept for sure and how many tie the threshold; the emission kernel turns
 // the counts of the earlier slices into its output offset and the tie quota
 // left for it, then writes its kept indices in index order.
-// Workspace: hist [3][n_seg][2048] u32 | cnt [n_seg][n_slices][2] u32 | thr [n_seg][2] u32 (the threshold and
-// tie quota the count kernel derived, for the emission kernel).
+// Workspace: hist [3][n_seg][2048] u32 | state [n_seg][8] u32 | cnt [n_seg][n_slices][2] u32.  state holds, per
+// prompt, the search after pass 0 and after pass 1 (prefix, keys still needed, and whether the chosen bin is
+// kept whole, which ends the search: then prefix and needed are already the threshold and tie quota), written
+// by the first workgroup of the launch that derives it, and the final threshold and tie quota, written by the
+// count kernel; each later launch reads them instead of re-deriving the earlier digits from the histograms.
 
 constexpr int kSlice = 4096;
 constexpr int kMT = 256;
 constexpr int kMPer = kSlice / kMT;  // tokens per thread
+constexpr int kState = 8;            // state words per prompt
 
 struct MultiSmem {
   uint32_t hist[kBins];
@@ -336,14 +340,27 @@ __global__ __launch_bounds__(kMT) void select_hist_kernel(const float* __restric
   if (t0 >= seg.seg_len) return;
   const int tid = threadIdx.x;
   uint32_t* hs = ws + (int64_t)blockIdx.y * kBins;  // + p * n_seg * kBins for pass p
+  uint32_t* state = ws + (int64_t)3 * n_seg * kBins + (int64_t)blockIdx.y * kState;
   uint32_t prefix = 0u, rem = (uint32_t)seg.k_eff;
-  for (int p = 0; p < PASS; ++p) {
+  if (PASS == 2) {  // the search after pass 0, from the previous launch
+    if (state[2] != 0u) return;  // ended at pass 0 (uniform)
+    prefix = state[0];
+    rem = state[1];
+  }
+  if (PASS >= 1) {  // digit of pass PASS - 1, from its completed histogram
+    constexpr int p = PASS - 1;
     int shift;
     uint32_t bins, mask, digit, count;
     pass_shape(p, shift, bins, mask);
     multi_find(hs + (int64_t)p * n_seg * kBins, bins, rem, digit, count, sm);
     prefix |= digit << shift;
-    if (count == rem && prefix != 0u) return;  // that bin is kept whole: no later pass needed (uniform)
+    const bool whole = count == rem && prefix != 0u;  // that bin is kept whole: no later pass needed
+    if (blockIdx.x == 0 && tid == 0) {
+      state[3 * p] = whole ? prefix - 1u : prefix;
+      state[3 * p + 1] = whole ? 0u : rem;
+      state[3 * p + 2] = whole ? 1u : 0u;
+    }
+    if (whole) return;  // uniform
   }
   int shift;
   uint32_t bins, mask;
@@ -378,23 +395,27 @@ __device__ void multi_threshold(const tg_segment& seg, int n_seg, const uint32_t
     thresh = 0u;
     need = 0xffffffffu;
   } else {
-    const uint32_t* hs = ws + (int64_t)blockIdx.y * kBins;
-    uint32_t prefix = 0u, rem = (uint32_t)seg.k_eff;
-    for (int p = 0; p < 3; ++p) {
+    const uint32_t* state = ws + (int64_t)3 * n_seg * kBins + (int64_t)blockIdx.y * kState;
+    if (state[2] != 0u) {  // ended at pass 0
+      thresh = state[0];
+      need = state[1];
+    } else if (state[5] != 0u) {  // ended at pass 1
+      thresh = state[3];
+      need = state[4];
+    } else {  // the last digit, from pass 2's histogram
+      uint32_t prefix = state[3], rem = state[4];
       int shift;
       uint32_t bins, mask, digit, count;
-      pass_shape(p, shift, bins, mask);
-      multi_find(hs + (int64_t)p * n_seg * kBins, bins, rem, digit, count, sm);
+      pass_shape(2, shift, bins, mask);
+      multi_find(ws + (int64_t)blockIdx.y * kBins + (int64_t)2 * n_seg * kBins, bins, rem, digit, count, sm);
       prefix |= digit << shift;
-      if (count == rem && prefix != 0u) {
-        // the found bin is kept whole: the same set as the exact threshold with all its ties
+      if (count == rem && prefix != 0u) {  // the found bin is kept whole: the same set with all its ties
         prefix -= 1u;
         rem = 0u;
-        break;
       }
+      thresh = prefix;
+      need = rem;
     }
-    thresh = prefix;
-    need = rem;
   }
 }
 
@@ -409,9 +430,9 @@ __global__ __launch_bounds__(kMT) void select_count_kernel(const float* __restri
   uint32_t thresh, need;
   multi_threshold(seg, n_seg, ws, sm, thresh, need);
   if (blockIdx.x == 0 && threadIdx.x == 0) {  // every prompt with tokens has slice 0
-    uint32_t* thr = ws + (int64_t)3 * n_seg * kBins + (int64_t)n_seg * n_slices * 2 + (int64_t)blockIdx.y * 2;
-    thr[0] = thresh;
-    thr[1] = need;
+    uint32_t* state = ws + (int64_t)3 * n_seg * kBins + (int64_t)blockIdx.y * kState;
+    state[6] = thresh;
+    state[7] = need;
   }
   const float* ss = scores + seg.seg_start;
   uint32_t nd = 0u, nt = 0u;
@@ -431,7 +452,7 @@ __global__ __launch_bounds__(kMT) void select_count_kernel(const float* __restri
   uint32_t e0, e1, td, tt;
   scan256(nd, nt, e0, e1, td, tt, sm);
   if (threadIdx.x == 0) {
-    uint32_t* cnt = ws + (int64_t)3 * n_seg * kBins + ((int64_t)blockIdx.y * n_slices + blockIdx.x) * 2;
+    uint32_t* cnt = ws + (int64_t)3 * n_seg * kBins + (int64_t)n_seg * kState + ((int64_t)blockIdx.y * n_slices + blockIdx.x) * 2;
     cnt[0] = td;
     cnt[1] = tt;
   }
@@ -446,10 +467,10 @@ __global__ __launch_bounds__(kMT) void select_emit_kernel(const float* __restric
   const int s0 = blockIdx.x * kSlice;
   if (s0 >= seg.seg_len) return;
   // the threshold and tie quota the count kernel derived (it ran before this launch, on the same stream)
-  const uint32_t* thr = ws + (int64_t)3 * n_seg * kBins + (int64_t)n_seg * n_slices * 2 + (int64_t)blockIdx.y * 2;
-  const uint32_t thresh = thr[0], need = thr[1];
+  const uint32_t* state = ws + (int64_t)3 * n_seg * kBins + (int64_t)blockIdx.y * kState;
+  const uint32_t thresh = state[6], need = state[7];
   // offsets from the earlier slices of this prompt
-  const uint32_t* cnt = ws + (int64_t)3 * n_seg * kBins + (int64_t)blockIdx.y * n_slices * 2;
+  const uint32_t* cnt = ws + (int64_t)3 * n_seg * kBins + (int64_t)n_seg * kState + (int64_t)blockIdx.y * n_slices * 2;
   uint32_t bd = 0u, bt = 0u;
   {
     const int j = threadIdx.x;  // one earlier slice per thread (n_slices <= 256 per 1M tokens; looped beyond)
@@ -504,7 +525,7 @@ static int n_slices(const tg_plan_info& info) { return (int)((info.max_seg_len +
 
 size_t select_workspace_bytes(const tg_plan_info& info) {
   if (!use_multi(info)) return 0;  // the one-workgroup kernel keeps its state on chip
-  const size_t words = (size_t)3 * info.n_seg * kBins + (size_t)info.n_seg * n_slices(info) * 2 + (size_t)info.n_seg * 2;
+  const size_t words = (size_t)3 * info.n_seg * kBins + (size_t)info.n_seg * kState + (size_t)info.n_seg * n_slices(info) * 2;
   return (words * 4 + 255) / 256 * 256;
 }
 
