@@ -185,7 +185,7 @@ size_t tg_gate_noalloc_max_tiles(void);
 /* ------------------------------------------------------------------------ */
 
 /* Device workspace (bytes) tg_select_topk needs for this plan: 0 when every
- * prompt has at most 32768 tokens (one workgroup per prompt keeps its state
+ * prompt has at most 16384 tokens (one workgroup per prompt keeps its state
  * on chip; workspace may then be NULL); otherwise room for the radix
  * histograms and per-slice counts of the multi-workgroup path (no initial
  * contents required). */
@@ -203,8 +203,8 @@ size_t tg_select_workspace_bytes(const tg_plan_info* info);
  *     NULL when that size is 0).
  * Exact integer algorithm (radix select on order-preserving 32-bit keys,
  * then an index-ordered scan): identical results on every run.  One launch
- * with one workgroup per prompt up to 32768 tokens; longer prompts use six
- * launches over 4096-token slices (integer atomics only). */
+ * with one workgroup per prompt up to 16384 tokens; longer prompts use six
+ * launches over 512-token slices (integer atomics only). */
 int tg_select_topk(const float* scores, const tg_segment* segs, const tg_plan_info* info, int32_t* kept_idx,
                    void* workspace, size_t workspace_bytes, void* stream);
 

@@ -4,11 +4,10 @@
 // ("TokenGate 与 T2Quant ... 精读", sections 3.1 and 4.1).  Order among document
 // tokens: higher score, then lower index.
 //
-// Prompts of up to 32K tokens: one launch, one 1024-thread workgroup per
-// prompt, keys in registers for all passes (thread t owns R = 16 or 32
-// consecutive tokens).  At that size the cost is latency, so launches, global
-// atomics and fences are avoided.  Longer prompts use the multi-workgroup
-// path below.
+// Prompts of up to 16K tokens: one launch, one 1024-thread workgroup per
+// prompt, keys in registers for all passes (thread t owns R = 16 consecutive
+// tokens).  At that size the cost is latency, so launches, global atomics and
+// fences are avoided.  Longer prompts use the multi-workgroup path below.
 //
 // Scores become order-preserving 32-bit keys (score_key); the K-th largest
 // document key T is found exactly by a three-digit MSB radix select
@@ -228,9 +227,9 @@ __global__ __launch_bounds__(kThreads) void select_topk_kernel(const float* __re
 
 
 // ---------------------------------------------------------------------------
-// Long prompts (more than 32K tokens): the same algorithm spread over many
-// workgroups.  Every prompt is cut into 4096-token slices, one 256-thread
-// workgroup each.  A radix pass accumulates each slice's LDS histogram into a
+// Long prompts (more than 16K tokens): the same algorithm spread over many
+// workgroups.  Every prompt is cut into 512-token slices, one 256-thread
+// workgroup each (so a 131072-token prompt fills the GPU's 256 CUs).  A radix pass accumulates each slice's LDS histogram into a
 // global one with integer atomics (exact, so the result does not depend on
 // the order); the next pass's workgroups all re-derive the chosen digit from
 // it with the same integer scan, so they agree without exchanging anything.
@@ -246,9 +245,10 @@ __global__ __launch_bounds__(kThreads) void select_topk_kernel(const float* __re
 // by the first workgroup of the launch that derives it, and the final threshold and tie quota, written by the
 // count kernel; each later launch reads them instead of re-deriving the earlier digits from the histograms.
 
-constexpr int kSlice = 4096;
+// Slice sizes: 512 tokens while the launch would otherwise have few workgroups (256 for one
+// 131072-token prompt), 4096 for large batches, where more slices only add global atomics.
+constexpr int kSliceSmall = 512, kSliceLarge = 4096;
 constexpr int kMT = 256;
-constexpr int kMPer = kSlice / kMT;  // tokens per thread
 constexpr int kState = 8;            // state words per prompt
 
 struct MultiSmem {
@@ -328,7 +328,7 @@ __global__ __launch_bounds__(256) void select_zero_kernel(uint32_t* __restrict__
   for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256) w[i] = 0u;
 }
 
-template <int PASS>
+template <int PASS, int SLICE>
 __global__ __launch_bounds__(kMT) void select_hist_kernel(const float* __restrict__ scores,
                                                           SegTable segs, int n_seg,
                                                           uint32_t* __restrict__ ws) {
@@ -336,7 +336,7 @@ __global__ __launch_bounds__(kMT) void select_hist_kernel(const float* __restric
   const tg_segment seg = segs.at_uniform(blockIdx.y);
   const int n_doc = seg.doc_end - seg.doc_begin;
   if (seg.k_eff <= 0 || seg.k_eff >= n_doc) return;  // no selection to make
-  const int t0 = blockIdx.x * kSlice;
+  const int t0 = blockIdx.x * SLICE;
   if (t0 >= seg.seg_len) return;
   const int tid = threadIdx.x;
   uint32_t* hs = ws + (int64_t)blockIdx.y * kBins;  // + p * n_seg * kBins for pass p
@@ -369,7 +369,7 @@ __global__ __launch_bounds__(kMT) void select_hist_kernel(const float* __restric
   __syncthreads();
   const float* ss = scores + seg.seg_start;
 #pragma unroll
-  for (int i = 0; i < kMPer; ++i) {
+  for (int i = 0; i < SLICE / kMT; ++i) {
     const int t = t0 + i * kMT + tid;  // coalesced
     if (t < seg.seg_len && t >= seg.doc_begin && t < seg.doc_end) {
       const uint32_t key = score_key(ss[t]);
@@ -420,12 +420,13 @@ __device__ void multi_threshold(const tg_segment& seg, int n_seg, const uint32_t
 }
 
 // Per slice: tokens kept for sure (non-document or key > T) and ties at T.
+template <int SLICE>
 __global__ __launch_bounds__(kMT) void select_count_kernel(const float* __restrict__ scores,
                                                            SegTable segs, int n_seg,
                                                            int n_slices, uint32_t* __restrict__ ws) {
   __shared__ MultiSmem sm;
   const tg_segment seg = segs.at_uniform(blockIdx.y);
-  const int t0 = blockIdx.x * kSlice;
+  const int t0 = blockIdx.x * SLICE;
   if (t0 >= seg.seg_len) return;
   uint32_t thresh, need;
   multi_threshold(seg, n_seg, ws, sm, thresh, need);
@@ -437,7 +438,7 @@ __global__ __launch_bounds__(kMT) void select_count_kernel(const float* __restri
   const float* ss = scores + seg.seg_start;
   uint32_t nd = 0u, nt = 0u;
 #pragma unroll
-  for (int i = 0; i < kMPer; ++i) {
+  for (int i = 0; i < SLICE / kMT; ++i) {
     const int t = t0 + i * kMT + (int)threadIdx.x;
     if (t < seg.seg_len) {
       if (t < seg.doc_begin || t >= seg.doc_end) {
@@ -458,13 +459,14 @@ __global__ __launch_bounds__(kMT) void select_count_kernel(const float* __restri
   }
 }
 
+template <int SLICE>
 __global__ __launch_bounds__(kMT) void select_emit_kernel(const float* __restrict__ scores,
                                                           SegTable segs, int n_seg,
                                                           int n_slices, const uint32_t* __restrict__ ws,
                                                           int32_t* __restrict__ kept_idx) {
   __shared__ MultiSmem sm;
   const tg_segment seg = segs.at_uniform(blockIdx.y);
-  const int s0 = blockIdx.x * kSlice;
+  const int s0 = blockIdx.x * SLICE;
   if (s0 >= seg.seg_len) return;
   // the threshold and tie quota the count kernel derived (it ran before this launch, on the same stream)
   const uint32_t* state = ws + (int64_t)3 * n_seg * kBins + (int64_t)blockIdx.y * kState;
@@ -484,12 +486,12 @@ __global__ __launch_bounds__(kMT) void select_emit_kernel(const float* __restric
   }
   // thread-contiguous ownership for the index-ordered emission
   const float* ss = scores + seg.seg_start;
-  const int t0 = s0 + (int)threadIdx.x * kMPer;
+  const int t0 = s0 + (int)threadIdx.x * (SLICE / kMT);
   uint32_t fd = 0u, ft = 0u;
 #pragma unroll
-  for (int i = 0; i < kMPer; ++i) {
+  for (int i = 0; i < SLICE / kMT; ++i) {
     const int t = t0 + i;
-    if (t < seg.seg_len && t < s0 + kSlice) {
+    if (t < seg.seg_len && t < s0 + SLICE) {
       if (t < seg.doc_begin || t >= seg.doc_end) {
         fd |= 1u << i;
       } else {
@@ -517,11 +519,19 @@ __global__ __launch_bounds__(kMT) void select_emit_kernel(const float* __restric
 
 }  // namespace
 
-// One workgroup per prompt up to 32K tokens (keys resident in registers);
-// past that the six-launch multi-workgroup path is faster.
-static bool use_multi(const tg_plan_info& info) { return info.max_seg_len > kThreads * 32; }
+// One workgroup per prompt up to 16K tokens (keys resident in registers);
+// past that the six-launch multi-workgroup path is faster (measured: 17.2 vs
+// 18.2 us at 24576 tokens, 17.2 vs 20.9 at 32768; 12.2 vs 17.1 at 16384).
+static bool use_multi(const tg_plan_info& info) { return info.max_seg_len > kThreads * 16; }
 
-static int n_slices(const tg_plan_info& info) { return (int)((info.max_seg_len + kSlice - 1) / kSlice); }
+static int slice_of(const tg_plan_info& info) {
+  const int64_t large = (int64_t)info.n_seg * ((info.max_seg_len + kSliceLarge - 1) / kSliceLarge);
+  return large >= 256 ? kSliceLarge : kSliceSmall;
+}
+static int n_slices(const tg_plan_info& info) {
+  const int s = slice_of(info);
+  return (int)((info.max_seg_len + s - 1) / s);
+}
 
 size_t select_workspace_bytes(const tg_plan_info& info) {
   if (!use_multi(info)) return 0;  // the one-workgroup kernel keeps its state on chip
@@ -534,10 +544,7 @@ hipError_t launch_select_topk(const float* scores, const tg_segment* segs_in, co
   const SegTable segs = seg_table(segs_in, info);
   if (info.max_seg_len <= 0) return hipSuccess;
   if (!use_multi(info)) {
-    if (info.max_seg_len <= kThreads * 16)
-      hipLaunchKernelGGL(select_topk_kernel<16>, dim3(info.n_seg), dim3(kThreads), 0, stream, scores, segs, kept_idx);
-    else
-      hipLaunchKernelGGL(select_topk_kernel<32>, dim3(info.n_seg), dim3(kThreads), 0, stream, scores, segs, kept_idx);
+    hipLaunchKernelGGL(select_topk_kernel<16>, dim3(info.n_seg), dim3(kThreads), 0, stream, scores, segs, kept_idx);
     return hipGetLastError();
   }
   uint32_t* ws = static_cast<uint32_t*>(workspace);
@@ -547,11 +554,18 @@ hipError_t launch_select_topk(const float* scores, const tg_segment* segs_in, co
   hipLaunchKernelGGL(select_zero_kernel, dim3((unsigned)((hist_words + 255) / 256 < 1024 ? (hist_words + 255) / 256 : 1024)),
                      dim3(256), 0, stream, ws, hist_words);
   const dim3 grid(ns, n_seg);
-  hipLaunchKernelGGL(select_hist_kernel<0>, grid, dim3(kMT), 0, stream, scores, segs, n_seg, ws);
-  hipLaunchKernelGGL(select_hist_kernel<1>, grid, dim3(kMT), 0, stream, scores, segs, n_seg, ws);
-  hipLaunchKernelGGL(select_hist_kernel<2>, grid, dim3(kMT), 0, stream, scores, segs, n_seg, ws);
-  hipLaunchKernelGGL(select_count_kernel, grid, dim3(kMT), 0, stream, scores, segs, n_seg, ns, ws);
-  hipLaunchKernelGGL(select_emit_kernel, grid, dim3(kMT), 0, stream, scores, segs, n_seg, ns, ws, kept_idx);
+#define TG_SELECT_MULTI(S)                                                                                      \
+  hipLaunchKernelGGL((select_hist_kernel<0, S>), grid, dim3(kMT), 0, stream, scores, segs, n_seg, ws);         \
+  hipLaunchKernelGGL((select_hist_kernel<1, S>), grid, dim3(kMT), 0, stream, scores, segs, n_seg, ws);         \
+  hipLaunchKernelGGL((select_hist_kernel<2, S>), grid, dim3(kMT), 0, stream, scores, segs, n_seg, ws);         \
+  hipLaunchKernelGGL((select_count_kernel<S>), grid, dim3(kMT), 0, stream, scores, segs, n_seg, ns, ws);       \
+  hipLaunchKernelGGL((select_emit_kernel<S>), grid, dim3(kMT), 0, stream, scores, segs, n_seg, ns, ws, kept_idx)
+  if (slice_of(info) == kSliceSmall) {
+    TG_SELECT_MULTI(kSliceSmall);
+  } else {
+    TG_SELECT_MULTI(kSliceLarge);
+  }
+#undef TG_SELECT_MULTI
   return hipGetLastError();
 }
 

@@ -128,7 +128,7 @@ def test_select_validation():
     if ws > 0:
         assert f(FAKE, FAKE, info, FAKE, FAKE, ws - 4, None) == -3
         assert f(FAKE, FAKE, info, FAKE, None, ws, None) == -3
-    # prompts past 32768 tokens take the multi-workgroup path, which needs a workspace
+    # prompts past 16384 tokens take the multi-workgroup path, which needs a workspace
     assert ws == 0
     long = tg.plan_segments([0, 40000, 40100], [0, 0], [39000, 90], [4096, 10])  # 10 slices of 4096
     wl = tg.select_workspace_bytes(long)

@@ -224,8 +224,9 @@ def test_select_all_equal():
 
 @pytest.mark.parametrize("seed", [0, 1, 2, 3, 4, 5])
 def test_select_ragged_segments(seed):
-    """Batches of 40 prompts; seeds 4 and 5 have prompts past 32K tokens, so they
-    run the multi-workgroup path (4096-token slices) next to short prompts."""
+    """Batches of 40 prompts; seeds 3 to 5 have prompts past 16K tokens, so they run the multi-workgroup
+    path next to short prompts: seed 3 on 512-token slices (40 x 5 slices of 4096 tokens would be under 256
+    workgroups), seeds 4 and 5 on 4096-token slices."""
     _say("select ragged", seed)
     rng = np.random.default_rng(100 + seed)
     seg = W.random_segments(rng, 40, [50, 500, 5000, 20000, 70000, 70000][seed])
