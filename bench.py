@@ -163,6 +163,19 @@ def time_pipeline(pipe, steps, warmup):
     return wall / steps * 1e6, gpu_step, per_stage
 
 
+def time_stage_kernels(pipe, reps=20):
+    """Average duration of each stage's kernels: `reps` back-to-back launches of
+    the stage alone between two events on the launch stream (after one whole
+    step, so every stage's inputs are valid; every stage is idempotent).  Unlike
+    the eager per-stage intervals of `time_pipeline`, this leaves out the host's
+    launch gaps between stages."""
+    torch = pipe.torch
+    stages = pipe.stages()
+    for _, f in stages:
+        f()
+    return {name: events_us(torch, f, reps) for name, f in stages}
+
+
 def capture_step(pipe):
     """One step (all stages) captured as a HIP graph on a side stream; every
     buffer is preallocated, and no stage allocates, synchronises or memsets."""
@@ -404,7 +417,8 @@ COPY_GBS = None  # set in main()
 
 
 def stage_rooflines(pipe, st, csrc):
-    """Roofline entry of every stage (algorithmic work / measured time)."""
+    """Roofline entry of every stage: algorithmic work / the stage's kernel time
+    (`time_stage_kernels`)."""
     attn_tflops = pipe.attention_flops() / (st["attention"] * 1e-6) / 1e12
     gate_gbs = pipe.gate_bytes() / (st["gate"] * 1e-6) / 1e9
     compact_gbs = pipe.compact_bytes() / (st["compact"] * 1e-6) / 1e9
@@ -703,9 +717,11 @@ def main():
         _, _, st16t = time_pipeline(p16t, args.steps, args.warmup)
         log("16K: graph replay, per-query temperature", f"{us_qtau:.1f} us/step", st16t)
         del p16t
-        roofs = stage_rooflines(p16, st16, csrc)
-        dominant = max(st16, key=st16.get)
-        sc_gbs = p16.select_compact_bytes() / ((st16["select"] + st16["compact"]) * 1e-6) / 1e9
+        kt16 = time_stage_kernels(p16)
+        log("16K: kernel time per stage (back-to-back launches)", "", kt16)
+        roofs = stage_rooflines(p16, kt16, csrc)
+        dominant = max(kt16, key=kt16.get)
+        sc_gbs = p16.select_compact_bytes() / ((kt16["select"] + kt16["compact"]) * 1e-6) / 1e9
         result = {
             "metric": METRIC,
             "value": p16.n / (us_wall * 1e-6),
@@ -722,10 +738,12 @@ def main():
             "config": {"workload": "gated layer N=16384 (16320 doc + 64 question), d=2048, gate 2048-256-1, "
                                    "K=2048 (M=2112 kept), 16 Q / 8 KV heads, head_dim 128",
                        "global_batch": 1, "seq_len": p16.n, "k_budget": 2048, "kept_rows": p16.m,
-                       "parallelism": "none", "launch": "one HIP graph per step (per-stage times: eager launches)",
+                       "parallelism": "none", "launch": "one HIP graph per step (stages_us: eager launches, host gaps included; "
+                                 "kernel_us and the rooflines: back-to-back launches of each stage)",
                        "gate_weights": "W1 packed into MFMA fragment order once at load"},
             "roofline": dict(roofs[dominant], stage=dominant),
             "stages_us": {k: round(v, 2) for k, v in st16.items()},
+            "kernel_us": {k: round(v, 2) for k, v in kt16.items()},
             "stage_rooflines": roofs,
             "gpu_us_per_step_events": round(us_gpu, 2),
             "eager_us_per_step": round(us_eager, 2),
@@ -748,6 +766,7 @@ def main():
         steps = args.steps if args.only_long else max(10, args.steps // 4)
         us_eager128, us_gpu128, st128 = time_pipeline(p128, steps, max(3, args.warmup // 4))
         us_wall128 = time_graph(p128, steps, max(3, args.warmup // 4))
+        kt128 = time_stage_kernels(p128, reps=10)
         log("128K: eager", f"{us_eager128:.1f} us/step, graph replay {us_wall128:.1f} us/step", st128)
         p128g = Pipeline(l128, 2048, torch, tg, gather=True)
         us_gather128 = time_graph(p128g, steps, max(3, args.warmup // 4))
@@ -759,7 +778,8 @@ def main():
             "eager_us_per_step": round(us_eager128, 2), "launch": "one HIP graph per step",
             "gather_on_load_us_per_step": round(us_gather128, 2),
             "stages_us": {k: round(v, 2) for k, v in st128.items()},
-            "stage_rooflines": stage_rooflines(p128, st128, csrc),
+            "kernel_us": {k: round(v, 2) for k, v in kt128.items()},
+            "stage_rooflines": stage_rooflines(p128, kt128, csrc),
             "peak_device_mem_gib": torch.cuda.max_memory_allocated() / 2 ** 30,
         }
         del p128
@@ -769,13 +789,15 @@ def main():
         p128k = Pipeline(l128, 4096, torch, tg)
         us_eager4k, _, st4k = time_pipeline(p128k, steps, max(3, args.warmup // 4))
         us_wall4k = time_graph(p128k, steps, max(3, args.warmup // 4))
+        kt4k = time_stage_kernels(p128k, reps=10)
         log("128K, K=4096: eager", f"{us_eager4k:.1f} us/step, graph replay {us_wall4k:.1f} us/step", st4k)
         long_rec4k = {
             "workload": "gated layer N=131072 (131008 doc + 64 question), d=2048, K=4096 (M=4160 kept)",
             "tokens_per_s": p128k.n / (us_wall4k * 1e-6), "ms_per_step": us_wall4k / 1e3, "steps": steps,
             "eager_us_per_step": round(us_eager4k, 2), "launch": "one HIP graph per step",
             "stages_us": {k: round(v, 2) for k, v in st4k.items()},
-            "stage_rooflines": stage_rooflines(p128k, st4k, csrc),
+            "kernel_us": {k: round(v, 2) for k, v in kt4k.items()},
+            "stage_rooflines": stage_rooflines(p128k, kt4k, csrc),
             "peak_device_mem_gib": torch.cuda.max_memory_allocated() / 2 ** 30,
         }
         del p128k, l128
