@@ -204,7 +204,8 @@ size_t tg_select_workspace_bytes(const tg_plan_info* info);
  * Exact integer algorithm (radix select on order-preserving 32-bit keys,
  * then an index-ordered scan): identical results on every run.  One launch
  * with one workgroup per prompt up to 16384 tokens; longer prompts use six
- * launches over 512-token slices (integer atomics only). */
+ * launches over 512-token slices, or 4096-token slices when the batch has
+ * enough of them to fill the GPU (integer atomics only). */
 int tg_select_topk(const float* scores, const tg_segment* segs, const tg_plan_info* info, int32_t* kept_idx,
                    void* workspace, size_t workspace_bytes, void* stream);
 
