@@ -245,6 +245,21 @@ def test_select_budget_edges_long(k):
     check_select(s, seg)
 
 
+@pytest.mark.parametrize("n", [16384, 16385, 16896, 16897])
+def test_select_path_boundary(n):
+    """Prompts at the switch from the one-workgroup kernel (up to 16384 tokens) to the multi-workgroup path, with
+    512-token slices that end exactly at the prompt's end (16896) or leave a last slice of one token (16385,
+    16897); budgets at both ends and in the middle, alone and in a batch with a short prompt."""
+    _say("select path boundary", n)
+    for k in (1, 2048, n - 65):
+        seg = W.single_segment(n - 64, 64, k)
+        s = W.mixture_scores(13, seg, k_marks=(2048,))
+        check_select(s, seg)
+    seg = W.Segments([0, n, n + 700], [0, 0], [n - 64, 690], [2048, 100])
+    s = W.mixture_scores(14, seg)
+    check_select(s, seg)
+
+
 def test_select_deterministic():
     _say("select determinism")
     seg = W.single_segment(32704, 64, 2048)
