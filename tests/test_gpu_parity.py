@@ -430,6 +430,44 @@ def test_attention_gather_equals_compacted(d, hq, hkv, lens):
                     rows=np.unique(ref_rows))
 
 
+@pytest.mark.parametrize("d,hq,hkv", [(128, 8, 4), (64, 4, 4)])
+def test_attention_gather_long_prompt(d, hq, hkv):
+    """Gather on load past 8192 kept rows in a prompt (the register-staged kernel, whose row indices fill up to
+    64 KiB of LDS) next to a short prompt: equal to the compacted path (direct-to-LDS kernel) bit for bit, and
+    to the oracle on sampled rows."""
+    import torch
+    _say("attention gather long prompt", d, hq, hkv)
+    tg = _tg()
+    rng = np.random.default_rng(40 + d + hq)
+    lens = [10000, 300]
+    offs = np.concatenate([[0], np.cumsum(lens)])
+    n = int(offs[-1])
+    q = W.f32_to_bf16_bits(rng.standard_normal((n, hq, d)).astype(np.float32))
+    k = W.f32_to_bf16_bits(rng.standard_normal((n, hkv, d)).astype(np.float32))
+    v = W.f32_to_bf16_bits(rng.standard_normal((n, hkv, d)).astype(np.float32))
+    s = rng.standard_normal(n).astype(np.float32)
+    tau = rng.uniform(0.8, 1.2, hq).astype(np.float32)
+    gain = rng.uniform(0.5, 1.5, hq).astype(np.float32)
+    plan = tg.plan_segments(list(offs), [0, 0], [9990, 290], [9000, 50], device="cuda")
+    assert plan.info.max_kept_len > 8192
+    kept = tg.select_topk(dev_f32(s), plan)
+    idx = kept.cpu().numpy().astype(np.int64)
+    qd, kd, vd, sd = dev_bf16(q), dev_bf16(k), dev_bf16(v), dev_f32(s)
+    tt, gg = dev_f32(tau), dev_f32(gain)
+    got_g = tg.gated_attention_prefill_gather(qd, kd, vd, sd, tt, gg, plan, kept)
+    qc, kc, vc, sc = (torch.index_select(t, 0, kept.long()) for t in (qd, kd, vd, sd))
+    got_c = tg.gated_attention_prefill(qc.contiguous(), kc.contiguous(), vc.contiguous(), sc.contiguous(), tt, gg,
+                                       plan)
+    torch.cuda.synchronize()
+    # the two kernels take the same products in the same order: equal bit for bit
+    assert torch.equal(got_g.view(torch.int16), got_c.view(torch.int16))
+    koffs = plan.kept_offsets
+    ref_rows = np.unique(np.concatenate([[0, 1, 8191, 8192, 8193, 9009, 9010, idx.size - 1],
+                                         np.linspace(0, idx.size - 1, 150).astype(np.int64)]))
+    check_attention(W.bf16_bits_to_f64(host_bf16(got_g)), q[idx], k[idx], v[idx], s[idx], tau, gain, koffs,
+                    rows=ref_rows)
+
+
 def run_attention_query_tau(q, k, v, s, sigma, gain, pos, offs, use_bias=True):
     import torch
     tg = _tg()
