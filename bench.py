@@ -210,6 +210,29 @@ def time_graph(pipe, steps, warmup):
     return (time.perf_counter() - t0) / steps * 1e6
 
 
+def time_graph_cold(pipe, steps, flush_bytes=1 << 30):
+    """Per-step time of graph replays that each start with the last-level cache
+    holding none of the step's data: before every replay a 1 GiB buffer (four
+    times the 256 MiB cache) is overwritten, outside the events that time the
+    replay."""
+    torch = pipe.torch
+    g = capture_step(pipe)
+    flush = torch.empty(flush_bytes, dtype=torch.uint8, device="cuda")
+    stream = torch.cuda.current_stream()
+    g.replay()
+    times = []
+    for _ in range(steps):
+        flush.fill_(1)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        g.replay()
+        e1.record(stream)
+        e1.synchronize()
+        times.append(e0.elapsed_time(e1) * 1e3)
+    del flush
+    return float(np.median(times))
+
+
 def cpu_model():
     """The host CPU's model name (from /proc/cpuinfo), or None."""
     try:
@@ -704,6 +727,8 @@ def main():
         log("16K: eager", f"{us_eager:.1f} us/step, events {us_gpu:.1f} us/step", st16)
         us_wall = time_graph(p16, args.steps, args.warmup)
         log("16K: graph replay", f"{us_wall:.1f} us/step")
+        us_cold = time_graph_cold(p16, max(5, args.steps // 4))
+        log("16K: graph replay after a last-level-cache flush", f"{us_cold:.1f} us/step")
         p16g = Pipeline(l16, 2048, torch, tg, gather=True)
         us_gather = time_graph(p16g, args.steps, args.warmup)
         log("16K: graph replay, attention gathering Q/K/V", f"{us_gather:.1f} us/step")
@@ -746,6 +771,7 @@ def main():
             "kernel_us": {k: round(v, 2) for k, v in kt16.items()},
             "stage_rooflines": roofs,
             "gpu_us_per_step_events": round(us_gpu, 2),
+            "cold_cache_us_per_step": round(us_cold, 2),
             "eager_us_per_step": round(us_eager, 2),
             "gather_on_load_us_per_step": round(us_gather, 2),
             "w1_repacked_every_step_us_per_step": round(us_repack, 2),
