@@ -98,10 +98,11 @@ __device__ __forceinline__ void find_digit(SelSmem& sm, uint32_t bins, uint32_t 
   __syncthreads();
 }
 
+// This thread's R tokens of the prompt as keys, and which of them are document tokens.
 template <int R>
-__device__ __forceinline__ void load_chunk(const float* __restrict__ seg_scores, const tg_segment& seg, int base,
-                                           uint32_t (&key)[R], uint32_t& docmask) {
-  const int t0 = base + (int)threadIdx.x * R;
+__device__ __forceinline__ void load_keys(const float* __restrict__ seg_scores, const tg_segment& seg,
+                                          uint32_t (&key)[R], uint32_t& docmask) {
+  const int t0 = (int)threadIdx.x * R;
   docmask = 0u;
   float v[R];
   const bool full = t0 + R <= seg.seg_len;
@@ -131,19 +132,18 @@ __global__ __launch_bounds__(kThreads) void select_topk_kernel(const float* __re
                                                                SegTable segs,
                                                                int32_t* __restrict__ kept_idx) {
   __shared__ SelSmem sm;
-  constexpr int kChunk = kThreads * R;
+  // launched only when every prompt has at most kThreads R tokens (the table entry is clamped to that
+  // maximum), so the whole prompt sits in registers: thread t owns tokens R t .. R t + R - 1
   const tg_segment seg = segs.at_uniform(blockIdx.x);
   if (seg.seg_len <= 0) return;
   const int tid = threadIdx.x;
   const int sub = (tid >> 6) & (kSub - 1);
   const float* ss = scores + seg.seg_start;
   const int n_doc = seg.doc_end - seg.doc_begin;
-  const int n_chunks = (seg.seg_len + kChunk - 1) / kChunk;
-  const bool resident = n_chunks == 1;
 
   uint32_t key[R];
   uint32_t docmask = 0u;
-  if (resident) load_chunk<R>(ss, seg, 0, key, docmask);
+  load_keys<R>(ss, seg, key, docmask);
 
   uint32_t thresh, need;
   if (seg.k_eff <= 0) {
@@ -162,14 +162,10 @@ __global__ __launch_bounds__(kThreads) void select_topk_kernel(const float* __re
       const uint32_t mask = pass == 0 ? 0u : (pass == 1 ? 0xffe00000u : 0xfffffc00u);
       for (int i = tid; i < kSub * kBins; i += kThreads) (&sm.hist[0][0])[i] = 0u;
       __syncthreads();
-#pragma unroll 1
-      for (int c = 0; c < n_chunks; ++c) {
-        if (!resident) load_chunk<R>(ss, seg, c * kChunk, key, docmask);
 #pragma unroll
-        for (int i = 0; i < R; ++i) {
-          if (((docmask >> i) & 1u) && (key[i] & mask) == prefix)
-            atomicAdd(&sm.hist[sub][(key[i] >> shift) & (bins - 1u)], 1u);
-        }
+      for (int i = 0; i < R; ++i) {
+        if (((docmask >> i) & 1u) && (key[i] & mask) == prefix)
+          atomicAdd(&sm.hist[sub][(key[i] >> shift) & (bins - 1u)], 1u);
       }
       __syncthreads();
       find_digit(sm, bins, rem);
@@ -191,38 +187,30 @@ __global__ __launch_bounds__(kThreads) void select_topk_kernel(const float* __re
 
   // Emission in index order.
   int32_t* out = kept_idx + seg.kept_start;
-  uint32_t def_base = 0u, tie_base = 0u;
-#pragma unroll 1
-  for (int c = 0; c < n_chunks; ++c) {
-    if (!resident) load_chunk<R>(ss, seg, c * kChunk, key, docmask);
-    const int t0 = c * kChunk + tid * R;
-    uint32_t fd = 0u, ft = 0u;  // bit i: token t0 + i kept for sure / tie at T
+  const int t0 = tid * R;
+  uint32_t fd = 0u, ft = 0u;  // bit i: token t0 + i kept for sure / tie at T
 #pragma unroll
-    for (int i = 0; i < R; ++i) {
-      const int t = t0 + i;
-      if (t < seg.seg_len) {
-        if (!((docmask >> i) & 1u) || key[i] > thresh)
-          fd |= 1u << i;
-        else if (key[i] == thresh)
-          ft |= 1u << i;
-      }
+  for (int i = 0; i < R; ++i) {
+    const int t = t0 + i;
+    if (t < seg.seg_len) {
+      if (!((docmask >> i) & 1u) || key[i] > thresh)
+        fd |= 1u << i;
+      else if (key[i] == thresh)
+        ft |= 1u << i;
     }
-    uint32_t ed, et, td, tt;
-    block_scan2((uint32_t)__builtin_popcount(fd), (uint32_t)__builtin_popcount(ft), ed, et, td, tt, sm);
-    // Ties before this thread: t_before; it keeps its first need - t_before ties (none once the quota is
-    // used up).  Kept tokens then land in index order from row def_before + min(t_before, need) on, so the
-    // j-th kept token of the thread goes to that row + j: one store per kept token, the loop running over
-    // the set bits of the thread's kept mask only.
-    const uint32_t t_before = tie_base + et;
-    uint32_t quota = need > t_before ? need - t_before : 0u;
-    uint32_t kept = fd;
-    for (uint32_t m = ft; m != 0u && quota != 0u; m &= m - 1u, --quota) kept |= m & (0u - m);
-    uint32_t pos = def_base + ed + (t_before < need ? t_before : need);
-    for (uint32_t m = kept; m != 0u; m &= m - 1u, ++pos)
-      if (pos < (uint32_t)seg.kept_len) out[pos] = seg.seg_start + t0 + __builtin_ctz(m);
-    def_base += td;
-    tie_base += tt;
   }
+  uint32_t ed, et, td, tt;
+  block_scan2((uint32_t)__builtin_popcount(fd), (uint32_t)__builtin_popcount(ft), ed, et, td, tt, sm);
+  // Ties before this thread: et; it keeps its first need - et ties (none once the quota is used up).  Kept
+  // tokens then land in index order from row ed + min(et, need) on, so the j-th kept token of the thread goes
+  // to that row + j: one store per kept token, the loop running over the set bits of the thread's kept mask
+  // only.
+  uint32_t quota = need > et ? need - et : 0u;
+  uint32_t kept = fd;
+  for (uint32_t m = ft; m != 0u && quota != 0u; m &= m - 1u, --quota) kept |= m & (0u - m);
+  uint32_t pos = ed + (et < need ? et : need);
+  for (uint32_t m = kept; m != 0u; m &= m - 1u, ++pos)
+    if (pos < (uint32_t)seg.kept_len) out[pos] = seg.seg_start + t0 + __builtin_ctz(m);
 }
 
 
