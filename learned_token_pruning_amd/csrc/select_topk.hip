@@ -18,6 +18,8 @@
 // key == T is kept while fewer than need = K_eff - #{key > T} ties have been
 // kept before it.  A block-wide exclusive scan gives every kept token its
 // output row, so the output is ascending and identical on every run.
+#include <type_traits>
+
 #include "common.h"
 
 namespace tg {
@@ -67,12 +69,15 @@ __device__ __forceinline__ void block_scan2(uint32_t a, uint32_t b, uint32_t& ea
 }
 
 // Finds the bin (counted from the top) that holds the rem-th largest key.
-// Every thread owns bins/1024 consecutive bins, highest first.
-__device__ __forceinline__ void find_digit(SelSmem& sm, uint32_t bins, uint32_t rem) {
+// Every thread owns BINS/1024 consecutive bins, highest first.
+template <uint32_t BINS>
+__device__ __forceinline__ void find_digit(SelSmem& sm, uint32_t rem) {
+  constexpr uint32_t bins = BINS;
   const int tid = threadIdx.x;
-  const uint32_t per = bins / kThreads;  // 2 or 1
+  constexpr uint32_t per = bins / kThreads;  // 2 or 1
   uint32_t c[2] = {0u, 0u};
   uint32_t sum = 0u;
+#pragma unroll
   for (uint32_t j = 0; j < per; ++j) {
     const uint32_t b = bins - 1u - (tid * per + j);
     uint32_t v = 0u;
@@ -85,6 +90,7 @@ __device__ __forceinline__ void find_digit(SelSmem& sm, uint32_t bins, uint32_t 
   block_scan2(sum, 0u, before, unused, t0, t1, sm);
   if (before < rem && rem <= before + sum) {
     uint32_t acc = before;
+#pragma unroll
     for (uint32_t j = 0; j < per; ++j) {
       if (acc + c[j] >= rem) {
         sm.found_digit = bins - 1u - (tid * per + j);
@@ -155,12 +161,16 @@ __global__ __launch_bounds__(kThreads) void select_topk_kernel(const float* __re
   } else {
     uint32_t prefix = 0u;
     uint32_t rem = (uint32_t)seg.k_eff;
-#pragma unroll 1
-    for (int pass = 0; pass < 3; ++pass) {
-      const int shift = pass == 0 ? 21 : (pass == 1 ? 10 : 0);
-      const uint32_t bins = pass == 2 ? 1024u : 2048u;
-      const uint32_t mask = pass == 0 ? 0u : (pass == 1 ? 0xffe00000u : 0xfffffc00u);
-      for (int i = tid; i < kSub * kBins; i += kThreads) (&sm.hist[0][0])[i] = 0u;
+    // one radix pass with its digit position as constants; true when the search has ended
+    auto pass = [&](auto p_) -> bool {
+      constexpr int P = decltype(p_)::value;
+      constexpr int shift = P == 0 ? 21 : (P == 1 ? 10 : 0);
+      constexpr uint32_t bins = P == 2 ? 1024u : 2048u;
+      constexpr uint32_t mask = P == 0 ? 0u : (P == 1 ? 0xffe00000u : 0xfffffc00u);
+#pragma unroll
+      for (int s = 0; s < kSub; ++s)
+#pragma unroll
+        for (int i = tid; i < (int)bins; i += kThreads) sm.hist[s][i] = 0u;
       __syncthreads();
 #pragma unroll
       for (int i = 0; i < R; ++i) {
@@ -168,7 +178,7 @@ __global__ __launch_bounds__(kThreads) void select_topk_kernel(const float* __re
           atomicAdd(&sm.hist[sub][(key[i] >> shift) & (bins - 1u)], 1u);
       }
       __syncthreads();
-      find_digit(sm, bins, rem);
+      find_digit<bins>(sm, rem);
       prefix |= sm.found_digit << shift;
       rem = sm.found_rem;
       const bool whole_bin = sm.found_cnt == rem && prefix != 0u;
@@ -178,9 +188,11 @@ __global__ __launch_bounds__(kThreads) void select_topk_kernel(const float* __re
         // threshold (its smallest key) with all its ties, so stop here
         prefix -= 1u;
         rem = 0u;
-        break;
       }
-    }
+      return whole_bin;
+    };
+    if (!pass(std::integral_constant<int, 0>()) && !pass(std::integral_constant<int, 1>()))
+      pass(std::integral_constant<int, 2>());
     thresh = prefix;
     need = rem;
   }
