@@ -163,17 +163,44 @@ def time_pipeline(pipe, steps, warmup):
     return wall / steps * 1e6, gpu_step, per_stage
 
 
-def time_stage_kernels(pipe, reps=20):
-    """Average duration of each stage's kernels: `reps` back-to-back launches of
-    the stage alone between two events on the launch stream (after one whole
-    step, so every stage's inputs are valid; every stage is idempotent).  Unlike
-    the eager per-stage intervals of `time_pipeline`, this leaves out the host's
-    launch gaps between stages."""
+def time_stage_kernels(pipe, reps=20, replays=5):
+    """Average duration of each stage's kernels: the stage captured `reps` times
+    in a row in one HIP graph, so its launches run back to back with no host
+    work between them, timed by events around each replay on the launch stream
+    (median of `replays`).  It runs after one whole step, so every stage's inputs
+    are valid (every stage is idempotent).  Unlike the eager per-stage intervals
+    of `time_pipeline`, this leaves out the host's launch gaps."""
     torch = pipe.torch
     stages = pipe.stages()
     for _, f in stages:
         f()
-    return {name: events_us(torch, f, reps) for name, f in stages}
+    torch.cuda.synchronize()
+    out = {}
+    for name, f in stages:
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):  # warm the stream before capture
+            f()
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for _ in range(reps):
+                f()
+        g.replay()
+        torch.cuda.synchronize()
+        stream = torch.cuda.current_stream()
+        ts = []
+        for _ in range(replays):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            g.replay()
+            e1.record(stream)
+            e1.synchronize()
+            ts.append(e0.elapsed_time(e1) / reps * 1e3)
+        out[name] = float(np.median(ts))
+        del g
+    return out
 
 
 def capture_step(pipe):
@@ -764,7 +791,7 @@ def main():
                                    "K=2048 (M=2112 kept), 16 Q / 8 KV heads, head_dim 128",
                        "global_batch": 1, "seq_len": p16.n, "k_budget": 2048, "kept_rows": p16.m,
                        "parallelism": "none", "launch": "one HIP graph per step (stages_us: eager launches, host gaps included; "
-                                 "kernel_us and the rooflines: back-to-back launches of each stage)",
+                                 "kernel_us and the rooflines: each stage repeated back to back inside one graph)",
                        "gate_weights": "W1 packed into MFMA fragment order once at load"},
             "roofline": dict(roofs[dominant], stage=dominant),
             "stages_us": {k: round(v, 2) for k, v in st16.items()},
