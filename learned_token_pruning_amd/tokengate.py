@@ -12,6 +12,7 @@ gate_score, select_topk, compact_kept, gated_attention_prefill.
 from __future__ import annotations
 
 import ctypes
+import math
 import os
 from dataclasses import dataclass
 from typing import List, Optional, Sequence, Tuple
@@ -349,8 +350,7 @@ def compact_kept(kept_idx: torch.Tensor, pairs: Sequence[Tuple[torch.Tensor, tor
     n = len(pairs)
     srcs = (_vp * n)(*[p[0].data_ptr() for p in pairs])
     dsts = (_vp * n)(*[p[1].data_ptr() for p in pairs])
-    rb = (_i64 * n)(*[p[0][0].numel() * p[0].element_size() if p[0].dim() > 1 else p[0].element_size()
-                      for p in pairs])
+    rb = (_i64 * n)(*[math.prod(p[0].shape[1:]) * p[0].element_size() for p in pairs])  # bytes of one row
     ss = (_i64 * n)(*[p[0].stride(0) * p[0].element_size() for p in pairs])
     ds = (_i64 * n)(*[p[1].stride(0) * p[1].element_size() for p in pairs])
     n_src = min(p[0].shape[0] for p in pairs)
