@@ -163,44 +163,17 @@ def time_pipeline(pipe, steps, warmup):
     return wall / steps * 1e6, gpu_step, per_stage
 
 
-def time_stage_kernels(pipe, reps=20, replays=5):
-    """Average duration of each stage's kernels: the stage captured `reps` times
-    in a row in one HIP graph, so its launches run back to back with no host
-    work between them, timed by events around each replay on the launch stream
-    (median of `replays`).  It runs after one whole step, so every stage's inputs
-    are valid (every stage is idempotent).  Unlike the eager per-stage intervals
-    of `time_pipeline`, this leaves out the host's launch gaps."""
+def time_stage_kernels(pipe, reps=20):
+    """Average duration of each stage's kernels (`events_us`: the stage captured
+    `reps` times in a row in one HIP graph, so its launches run back to back with
+    no host work between them), after one whole step so that every stage's
+    inputs are valid (every stage is idempotent).  Unlike the eager per-stage
+    intervals of `time_pipeline`, this leaves out the host's launch gaps."""
     torch = pipe.torch
     stages = pipe.stages()
     for _, f in stages:
         f()
-    torch.cuda.synchronize()
-    out = {}
-    for name, f in stages:
-        side = torch.cuda.Stream()
-        side.wait_stream(torch.cuda.current_stream())
-        with torch.cuda.stream(side):  # warm the stream before capture
-            f()
-        torch.cuda.current_stream().wait_stream(side)
-        torch.cuda.synchronize()
-        g = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(g):
-            for _ in range(reps):
-                f()
-        g.replay()
-        torch.cuda.synchronize()
-        stream = torch.cuda.current_stream()
-        ts = []
-        for _ in range(replays):
-            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            e0.record(stream)
-            g.replay()
-            e1.record(stream)
-            e1.synchronize()
-            ts.append(e0.elapsed_time(e1) / reps * 1e3)
-        out[name] = float(np.median(ts))
-        del g
-    return out
+    return {name: events_us(torch, f, reps) for name, f in stages}
 
 
 def capture_step(pipe):
@@ -308,18 +281,35 @@ def cpu_baseline(layer, k_budget, budget_s=10.0, threads=None):
                       f"{t:.2f} s each"}
 
 
-def events_us(torch, f, reps, warm=3):
-    """Mean time of f() over `reps` back-to-back calls, from events on the current stream."""
-    for _ in range(warm):
-        f()
+def events_us(torch, f, reps, warm=3, replays=5):
+    """Mean time of f(): `reps` calls captured back to back in one HIP graph (no
+    host work between the launches), timed by events around a replay on the
+    current stream; median of `replays` replays.  f must allocate nothing and
+    may be re-run on the same buffers."""
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):  # warm the stream before capture
+        for _ in range(warm):
+            f()
+    torch.cuda.current_stream().wait_stream(side)
     torch.cuda.synchronize()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record()
-    for _ in range(reps):
-        f()
-    e1.record()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for _ in range(reps):
+            f()
+    g.replay()
     torch.cuda.synchronize()
-    return e0.elapsed_time(e1) / reps * 1e3
+    stream = torch.cuda.current_stream()
+    ts = []
+    for _ in range(replays):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        g.replay()
+        e1.record(stream)
+        e1.synchronize()
+        ts.append(e0.elapsed_time(e1) / reps * 1e3)
+    del g
+    return float(np.median(ts))
 
 
 def time_k_sweep(torch, tg, reps=50):
