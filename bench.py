@@ -760,7 +760,7 @@ def main():
         log("16K: graph replay, per-query temperature", f"{us_qtau:.1f} us/step", st16t)
         del p16t
         kt16 = time_stage_kernels(p16)
-        log("16K: kernel time per stage (back-to-back launches)", "", kt16)
+        log("16K: kernel time per stage (repetitions inside one graph)", "", kt16)
         roofs = stage_rooflines(p16, kt16, csrc)
         dominant = max(kt16, key=kt16.get)
         sc_gbs = p16.select_compact_bytes() / ((kt16["select"] + kt16["compact"]) * 1e-6) / 1e9
