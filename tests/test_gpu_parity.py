@@ -608,6 +608,49 @@ def test_pipeline(idx):
     check_attention(got, q, k, v, oracle.compact_rows(s_ref, got_idx), L.tau, L.gain, offs)
 
 
+@pytest.mark.parametrize("kb", [2048, 4096])
+def test_pipeline_workload_4_graph(kb):
+    """The long-context layer at full size (131008 documents + 64 question tokens, d = 2048, 16 Q / 8 KV heads)
+    run as bench.py times it: the whole step captured as one HIP graph and replayed.  Gate scores against the
+    oracle per element; the kept set exactly the oracle's on the GPU's own scores (and the oracle's scores'
+    set up to near-ties); the compacted hidden rows bit for bit; the attention against the oracle on sampled
+    rows of the M = kb + 64 kept rows."""
+    import torch
+    import bench
+    _say("pipeline workload 4 graph", kb)
+    tg = _tg()
+    L = layer(4)
+    pipe = bench.Pipeline(L, kb, torch, tg)
+    g = bench.capture_step(pipe)
+    for t in (pipe.scores, pipe.out, pipe.hc):
+        t.zero_()
+    pipe.kept.fill_(-1)
+    g.replay()
+    torch.cuda.synchronize()
+    seg = pipe.seg
+    s_got = pipe.scores.cpu().numpy()
+    got_idx = pipe.kept.cpu().numpy().astype(np.int64)
+    s_ref = oracle_gate(L)
+    check_scores(s_got, s_ref, doc_mask_of(seg))
+    own_idx, offs = oracle.kept_indices(s_got.astype(np.float64), seg.seg_start, seg.doc_begin, seg.doc_end,
+                                        seg.k_budget)
+    assert np.array_equal(got_idx, own_idx), "select differs from the oracle on the GPU's own scores"
+    ref_idx, _ = oracle.kept_indices(s_ref, seg.seg_start, seg.doc_begin, seg.doc_end, seg.k_budget)
+    if not np.array_equal(got_idx, ref_idx):
+        sym = np.setxor1d(got_idx, ref_idx)
+        t = np.sort(s_ref[seg.doc_begin[0]:seg.doc_end[0]])[::-1][seg.k_budget[0] - 1]
+        assert np.all(np.abs(s_ref[sym] - t) <= 4 * SCORE_RTOL * max(1.0, abs(t))), "kept sets differ beyond near-ties"
+        _say("kept sets differ at a near-tie:", sym.size, "tokens")
+    assert pipe.hc.view(torch.int16).cpu().numpy().tobytes() == oracle.compact_rows(L.x.view(np.int16), got_idx).tobytes()
+    m = got_idx.size
+    assert m == kb + 64
+    rng = np.random.default_rng(kb)
+    rows = np.unique(np.concatenate([[0, 1, 63, 64, m // 2, m - 65, m - 64, m - 2, m - 1], rng.integers(0, m, 60)]))
+    got = W.bf16_bits_to_f64(host_bf16(pipe.out))
+    q, k, v = (oracle.compact_rows(a, got_idx) for a in (L.q, L.k, L.v))
+    check_attention(got, q, k, v, oracle.compact_rows(s_ref, got_idx), L.tau, L.gain, offs, rows=rows)
+
+
 @pytest.mark.parametrize("gather", [False, True])
 def test_pipeline_graph_replays_match_eager(gather):
     """The step captured as a HIP graph (as bench.py times it): every replay,
